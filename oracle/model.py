@@ -1,0 +1,68 @@
+"""Synthetic model and workload inputs for the oracle (test infrastructure only).
+
+Weights and inputs come from the shared seeded generator (``inputs``); this
+module only arranges them the way the oracle's functions take them.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import inputs
+from inputs.configs import (BLOCK_NAMES, MOD_SIGMA, NORM_SIGMA, ROW_SIGMA, TID_FINAL_SCALE,
+                            TID_IMG_IN, TID_MODS, TID_MODS0, TID_PREFIX_X, TID_PROJ_OUT,
+                            TID_TOK, W_SIGMA, block_tid)
+
+from .qi21_oracle import Geometry
+
+
+class SynthModel:
+    """A randomly initialised denoiser of the given ``inputs.ModelSpec``.
+
+    ``block(l)`` regenerates layer l's tensors on demand (a small cache keeps
+    the most recent ones), so a 32-layer model never needs all its weights
+    in memory at once.
+    """
+
+    def __init__(self, spec, cache_layers: int = 2, overrides=None):
+        self.spec = spec
+        self.layers = spec.layers
+        self.geom = Geometry(dim=spec.dim, heads=spec.heads, head_dim=spec.head_dim,
+                             inter=spec.inter, in_ch=spec.in_ch, eps=spec.eps,
+                             axes=tuple(spec.axes), theta=spec.theta)
+        s = spec.seed
+        self.img_in = inputs.host_array(s, TID_IMG_IN, (spec.dim, spec.in_ch), W_SIGMA, bf16=spec.bf16)
+        self.proj_out = inputs.host_array(s, TID_PROJ_OUT, (spec.in_ch, spec.dim), W_SIGMA, bf16=spec.bf16)
+        self.mods0 = inputs.host_array(s, TID_MODS0, (4 * spec.dim,), MOD_SIGMA)
+        self._cache = {}
+        self._order = []
+        self._keep = cache_layers
+        self.overrides = overrides or {}
+
+    def block(self, l: int) -> dict:
+        if l in self._cache:
+            return self._cache[l]
+        spec = self.spec
+        out = {}
+        for j, (name, shape) in enumerate(zip(BLOCK_NAMES, spec.block_shapes())):
+            if name.startswith("norm"):
+                out[name] = inputs.host_array(spec.seed, block_tid(l, j), shape, NORM_SIGMA, mean=1.0)
+            else:
+                out[name] = inputs.host_array(spec.seed, block_tid(l, j), shape, W_SIGMA, bf16=spec.bf16)
+        out.update(self.overrides.get(l, {}))
+        self._cache[l] = out
+        self._order.append(l)
+        while len(self._order) > self._keep:
+            self._cache.pop(self._order.pop(0), None)
+        return out
+
+
+def workload_inputs(w, prefix: int = 0) -> dict:
+    """Prefix rows, tokens, modulation and final scale of workload ``w``."""
+    spec = w.model
+    lp = w.prefix_len(prefix)
+    return {
+        "x_prefix": inputs.host_array(w.prefix_seed(prefix), TID_PREFIX_X, (lp, spec.dim), ROW_SIGMA),
+        "tok": inputs.host_array(w.seed, TID_TOK, (w.n, spec.in_ch), ROW_SIGMA),
+        "mods": inputs.host_array(w.seed, TID_MODS, (4 * spec.dim,), MOD_SIGMA),
+        "final_scale": inputs.host_array(w.seed, TID_FINAL_SCALE, (spec.dim,), MOD_SIGMA),
+    }
