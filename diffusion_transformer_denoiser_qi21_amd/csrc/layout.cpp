@@ -1,0 +1,108 @@
+// Layout helpers of the qi21 C ABI (host only): prefix / target sizes,
+// RoPE positions, the prefix's block-causal visibility and the RoPE tables.
+//
+// Definitions from [QI] (docs.rs cortiq-engine 0.8.4,
+// src/cortiq_engine/qwen_image21.rs): `Qi21Layout` (positions: text rows
+// advance one position on all three axes; an image block keeps the frame
+// at the running position, centres its grid with integer halving and then
+// advances the position by max(h, w)), `prefill` (a text row sees the keys
+// up to itself, an image row up to the end of its image block) and
+// `rope_tables` (float32 frequencies 1/theta^(2i/d) per axis, float32
+// angle, columns frame, row, col).
+#include <cmath>
+#include <vector>
+
+#include "../../include/qi21.h"
+
+namespace {
+int seg_len(const qi21_seg& s) { return s.kind == 0 ? s.h : s.h * s.w; }
+}  // namespace
+
+extern "C" {
+
+int qi21_layout_sizes(const qi21_seg* segs, int nseg, int32_t* lp, int32_t* n) {
+  if (!segs || nseg < 2) return QI21_EINVAL;
+  int64_t total = 0;
+  for (int i = 0; i < nseg; ++i) {
+    const qi21_seg& s = segs[i];
+    if ((s.kind != 0 && s.kind != 1) || s.h < 0 || (s.kind == 1 && s.w < 0)) return QI21_EINVAL;
+    total += seg_len(s);
+  }
+  const qi21_seg& t = segs[nseg - 1];
+  if (t.kind != 1 || t.h <= 0 || t.w <= 0) return QI21_EINVAL;
+  const int64_t nt = seg_len(t);
+  if (total - nt <= 0 || total > (1 << 24)) return QI21_EINVAL;
+  if (lp) *lp = (int32_t)(total - nt);
+  if (n) *n = (int32_t)nt;
+  return QI21_OK;
+}
+
+int qi21_layout_tables(const qi21_seg* segs, int nseg, const int32_t* axes, float theta, int64_t* pos,
+                       uint32_t* vis, float* cos_p, float* sin_p, float* cos_t, float* sin_t) {
+  int32_t lp = 0, n = 0;
+  if (qi21_layout_sizes(segs, nseg, &lp, &n) != QI21_OK || !axes) return QI21_EINVAL;
+  int hd = 0;
+  for (int a = 0; a < 3; ++a) {
+    if (axes[a] <= 0 || axes[a] % 2) return QI21_EINVAL;
+    hd += axes[a];
+  }
+  const int half = hd / 2;
+  const int total = lp + n;
+  std::vector<int64_t> P((size_t)total * 3);
+  std::vector<int> block((size_t)total, -1);
+  int64_t p = 0;
+  int r = 0, id = 0;
+  for (int i = 0; i < nseg; ++i) {
+    const qi21_seg& s = segs[i];
+    if (s.kind == 0) {
+      for (int j = 0; j < s.h; ++j, ++r) {
+        P[3 * r] = P[3 * r + 1] = P[3 * r + 2] = p;
+        ++p;
+      }
+    } else {
+      const int64_t h = s.h, w = s.w;
+      for (int64_t y = 0; y < h; ++y)
+        for (int64_t x = 0; x < w; ++x, ++r) {
+          P[3 * r] = p;
+          P[3 * r + 1] = y - (h - h / 2);
+          P[3 * r + 2] = x - (w - w / 2);
+          block[r] = id;
+        }
+      ++id;
+      p += h > w ? h : w;
+    }
+  }
+  if (pos)
+    for (size_t i = 0; i < P.size(); ++i) pos[i] = P[i];
+  if (vis) {
+    for (int i = 0; i < lp; ++i) {
+      int e = i + 1;
+      if (block[i] >= 0)
+        while (e < lp && block[e] == block[i]) ++e;
+      vis[i] = (uint32_t)e;
+    }
+  }
+  // per-column frequency and axis
+  std::vector<float> freq(half);
+  std::vector<int> axis(half);
+  int j = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int i = 0; i < axes[a] / 2; ++i, ++j) {
+      freq[j] = 1.0f / std::pow(theta, (float)(2 * i) / (float)axes[a]);
+      axis[j] = a;
+    }
+  auto fill = [&](int row0, int rows, float* c, float* s) {
+    if (!c && !s) return;
+    for (int rr = 0; rr < rows; ++rr)
+      for (int k = 0; k < half; ++k) {
+        const float ang = (float)P[3 * (size_t)(row0 + rr) + axis[k]] * freq[k];
+        if (c) c[(size_t)rr * half + k] = std::cos(ang);
+        if (s) s[(size_t)rr * half + k] = std::sin(ang);
+      }
+  };
+  fill(0, lp, cos_p, sin_p);
+  fill(lp, n, cos_t, sin_t);
+  return QI21_OK;
+}
+
+}  // extern "C"

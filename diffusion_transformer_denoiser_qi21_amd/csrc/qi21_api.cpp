@@ -1,0 +1,800 @@
+// Host runtime of the qi21 C ABI: model and weight-plane ownership, the
+// per-prompt programs (prefix K/V caches), argument validation, and the
+// launch sequences of prefill and step.
+//
+// The per-layer launch list follows the device design of [WG] (docs.rs
+// cortiq-engine 0.8.3, src/gpu_wgpu/qi21.rs, `blocks` and `build_prog`) and
+// the block definition of [QI] (cortiq-engine 0.8.4,
+// src/cortiq_engine/qwen_image21.rs, `block_cpu`):
+//   qkv GEMM (xn -> q|k panel, V^T) -> qkrope -> attention -> O GEMM ->
+//   rowop(x += tanh g1 * y; xn = LN(x)(1+s2)) -> gate/up GEMM + SwiGLU ->
+//   down GEMM -> rowop(x += tanh g2 * y; xn = LN(x)(1+s1) for the next block)
+// with the f16 sites scaled by power-of-two range guards that each consumer
+// multiplies back in f32 ([WG] Guards).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <string>
+#include <vector>
+
+#include "../../include/qi21.h"
+#include "../../include/qi21_ops.h"
+#include "qi21_internal.h"
+
+using qi21::f16;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_OK(expr)                                                                          \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess) return fail(QI21_EDEVICE, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+inline float p2(int e) { return std::ldexp(1.0f, e); }
+inline size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
+
+constexpr int NCLASS = 8;
+enum Cls { C_QKV = 0, C_QKROPE, C_FLASH, C_O, C_W13, C_W2, C_ROW, C_IO };
+
+struct Acts {
+  int cap = 0;  // rows, a multiple of 256
+  float* x = nullptr;
+  f16* xn = nullptr;
+  f16* panel = nullptr;  // [cap][2H] q | k
+  f16* vt = nullptr;     // [H][cap] V^T of the pass's own rows
+  f16* att = nullptr;    // [cap][H]
+  float* y = nullptr;    // [cap][H]
+  f16* hid = nullptr;    // [cap][I]
+  float* mods = nullptr; // [4H] tanh-ed modulation of the pass
+  float* out = nullptr;  // [cap][64] velocity before the finite check
+};
+
+struct Prog {
+  uint64_t key = 0;
+  int lp = 0, n = 0, ldc = 0;
+  std::vector<f16*> kc;   // per layer [lp][H] post-RoPE K (scale-free)
+  std::vector<f16*> vtc;  // per layer [H][ldc] V^T (x 2^-qkv)
+  float* rc = nullptr;    // [n][64] target RoPE cos
+  float* rs = nullptr;    // [n][64] target RoPE sin
+};
+
+struct Prof {
+  std::vector<hipEvent_t> ev[NCLASS];
+  size_t used[NCLASS] = {};
+  double ms[NCLASS] = {};
+  int64_t n[NCLASS] = {};
+};
+
+}  // namespace
+
+struct qi21_model {
+  qi21_geom g{};
+  qi21_options o{};
+  int nb = 0;
+  std::vector<f16*> wqkv, wo, w13, w2;
+  std::vector<float*> nq, nk;
+  std::vector<char> set;
+  float* img_in = nullptr;      // [H][64]
+  float* proj_out_t = nullptr;  // [H][64]
+  Acts acts;
+  std::deque<Prog> progs;
+  int* dflag = nullptr;
+  int* hflag = nullptr;  // pinned host
+  size_t bytes = 0;
+  Prof prof;
+};
+
+namespace {
+
+void* dalloc(qi21_model* m, size_t bytes) {
+  if (bytes == 0) bytes = 256;
+  void* p = nullptr;
+  if (m->o.alloc) {
+    p = m->o.alloc(bytes, m->o.alloc_ctx);
+  } else if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    p = nullptr;
+  }
+  if (p) m->bytes += bytes;
+  return p;
+}
+
+void dfree(qi21_model* m, void* p, size_t bytes) {
+  if (!p) return;
+  if (m->o.free)
+    m->o.free(p, m->o.alloc_ctx);
+  else
+    (void)hipFree(p);
+  m->bytes -= std::min(m->bytes, bytes ? bytes : (size_t)256);
+}
+
+size_t acts_bytes(const qi21_geom& g, int cap, size_t* parts) {
+  const size_t H = g.hidden, I = g.inter, c = cap;
+  const size_t p[9] = {c * H * 4, c * H * 2, c * 2 * H * 2, H * c * 2, c * H * 2, c * H * 4, c * I * 2, 4 * H * 4,
+                       c * 64 * 4};
+  size_t t = 0;
+  for (int i = 0; i < 9; ++i) {
+    if (parts) parts[i] = p[i];
+    t += p[i];
+  }
+  return t;
+}
+
+void free_acts(qi21_model* m) {
+  size_t parts[9];
+  acts_bytes(m->g, m->acts.cap, parts);
+  void* ptrs[9] = {m->acts.x, m->acts.xn, m->acts.panel, m->acts.vt, m->acts.att,
+                   m->acts.y, m->acts.hid, m->acts.mods, m->acts.out};
+  for (int i = 0; i < 9; ++i) dfree(m, ptrs[i], parts[i]);
+  m->acts = Acts{};
+}
+
+// Make the shared activations hold at least `rows` rows; zero-filled so
+// padding rows read by GEMM / attention tiles are finite.
+int ensure_acts(qi21_model* m, int rows, hipStream_t s) {
+  if (m->acts.cap >= rows) return QI21_OK;
+  free_acts(m);
+  const int cap = (int)round_up((size_t)rows, 256);
+  size_t parts[9];
+  acts_bytes(m->g, cap, parts);
+  void* p[9];
+  for (int i = 0; i < 9; ++i) {
+    p[i] = dalloc(m, parts[i]);
+    if (!p[i]) {
+      for (int j = 0; j < i; ++j) dfree(m, p[j], parts[j]);
+      return fail(QI21_ENOMEM, "activations for %d rows (%.1f MB) did not fit", rows,
+                  acts_bytes(m->g, cap, nullptr) / 1e6);
+    }
+    HIP_OK(qi21::launch_fill32(p[i], 0u, parts[i] / 4, s));
+  }
+  Acts& a = m->acts;
+  a.cap = cap;
+  a.x = (float*)p[0];
+  a.xn = (f16*)p[1];
+  a.panel = (f16*)p[2];
+  a.vt = (f16*)p[3];
+  a.att = (f16*)p[4];
+  a.y = (float*)p[5];
+  a.hid = (f16*)p[6];
+  a.mods = (float*)p[7];
+  a.out = (float*)p[8];
+  return QI21_OK;
+}
+
+void free_prog(qi21_model* m, Prog& p) {
+  const size_t H = m->g.hidden;
+  for (auto* k : p.kc) dfree(m, k, (size_t)p.lp * H * 2);
+  for (auto* v : p.vtc) dfree(m, v, H * p.ldc * 2);
+  dfree(m, p.rc, (size_t)p.n * 64 * 4);
+  dfree(m, p.rs, (size_t)p.n * 64 * 4);
+  p.kc.clear();
+  p.vtc.clear();
+  p.rc = p.rs = nullptr;
+}
+
+Prog* find_prog(qi21_model* m, uint64_t key) {
+  for (auto& p : m->progs)
+    if (p.key == key) return &p;
+  return nullptr;
+}
+
+// ── profiling: events around each launch of a class ──
+struct Scope {
+  qi21_model* m;
+  int cls;
+  hipStream_t s;
+  hipEvent_t stop = nullptr;
+  Scope(qi21_model* m_, int c, hipStream_t s_) : m(m_), cls(c), s(s_) {
+    if (!((m->o.profile >> cls) & 1)) return;
+    Prof& P = m->prof;
+    const size_t i = P.used[cls] * 2;
+    while (P.ev[cls].size() < i + 2) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return;
+      P.ev[cls].push_back(e);
+    }
+    (void)hipEventRecord(P.ev[cls][i], s);
+    stop = P.ev[cls][i + 1];
+    P.used[cls]++;
+  }
+  ~Scope() {
+    if (stop) (void)hipEventRecord(stop, s);
+  }
+};
+
+void prof_collect(qi21_model* m) {
+  if (!m->o.profile) return;
+  Prof& P = m->prof;
+  for (int c = 0; c < NCLASS; ++c) {
+    for (size_t i = 0; i < P.used[c]; ++i) {
+      float ms = 0.0f;
+      if (hipEventElapsedTime(&ms, P.ev[c][2 * i], P.ev[c][2 * i + 1]) == hipSuccess) P.ms[c] += ms;
+    }
+    P.n[c] += (int64_t)P.used[c];
+    P.used[c] = 0;
+  }
+}
+
+int check_geom(const qi21_geom* g) {
+  if (!g) return fail(QI21_EINVAL, "geometry is NULL");
+  if (g->head_dim != 128 || g->heads < 1 || g->heads * g->head_dim != g->hidden || g->hidden % 128 != 0 ||
+      g->hidden > 8192)
+    return fail(QI21_EUNSUPPORTED,
+                "geometry hidden %d heads %d head_dim %d: the kernels need head_dim 128, heads*128 == hidden, "
+                "hidden %% 128 == 0 and <= 8192",
+                g->hidden, g->heads, g->head_dim);
+  if (g->inter < 64 || g->inter % 64 != 0 || g->in_ch != 64)
+    return fail(QI21_EUNSUPPORTED, "geometry inter %d in_ch %d: the kernels need inter %% 64 == 0 and 64 channels",
+                g->inter, g->in_ch);
+  if (!(g->eps >= 0.0f) || !std::isfinite(g->eps)) return fail(QI21_EINVAL, "eps %g", (double)g->eps);
+  return QI21_OK;
+}
+
+struct Guard {
+  int attn, qkv, ao, ffn, hid;
+};
+Guard guards(const qi21_model* m) {
+  auto c = [](int v) { return std::min(14, std::max(0, v)); };
+  return Guard{c(m->o.shift_attn), c(m->o.shift_qkv), c(m->o.shift_ao), c(m->o.shift_ffn), c(m->o.shift_hid)};
+}
+
+qi21::GemmArgs gemm_args(int M, int N, int K, const f16* A, int lda, const f16* W, void* out, int ldo,
+                         float oscale, float inscale = 1.0f, f16* out2 = nullptr, int ld2 = 0) {
+  qi21::GemmArgs a;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.A = A;
+  a.lda = lda;
+  a.W = W;
+  a.out = out;
+  a.ldo = ldo;
+  a.out2 = out2;
+  a.ld2 = ld2;
+  a.oscale = oscale;
+  a.inscale = inscale;
+  return a;
+}
+
+// One segment of the rows of a pass (one program's rows in a batch).
+struct Seg {
+  int row0, rows;
+  Prog* p;           // step: the program whose cache the rows attend to
+  const float* rc;   // RoPE tables of these rows
+  const float* rs;
+};
+
+// Blocks of one pass over `rows` rows of m->acts.  Prefill: one segment,
+// `pre` receives the caches (keys written by qkrope, V^T by the GEMM), the
+// mask is vis, and the last layer stops after the cache write.  Step: the
+// caches of each segment's program are read.
+int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre, const uint32_t* vis,
+               hipStream_t s) {
+  const qi21_geom& g = m->g;
+  const int H = g.hidden, I = g.inter, nh = g.heads;
+  const Guard gd = guards(m);
+  Acts& a = m->acts;
+  const int tile = m->o.gemm_tile;
+  for (int l = 0; l < m->nb; ++l) {
+    const bool last = l + 1 == m->nb;
+    {  // qkv: panel q|k (x 2^-qkv), V^T to the cache (prefill) or acts.vt
+      Scope sc(m, C_QKV, s);
+      f16* vt = pre ? pre->vtc[l] : a.vt;
+      const int ldv = pre ? pre->ldc : a.cap;
+      HIP_OK(qi21::launch_gemm(qi21::EPI_QKV,
+                               gemm_args(rows, 3 * H, H, a.xn, H, m->wqkv[l], a.panel, 2 * H,
+                                         p2(gd.attn - gd.qkv), 1.0f, vt, ldv),
+                               tile, s));
+    }
+    {  // per-head RMSNorm + RoPE; the norm's eps follows the panel's guard
+      Scope sc(m, C_QKROPE, s);
+      const float eps = g.eps * p2(-2 * gd.qkv);
+      for (const Seg& sg : segs)
+        HIP_OK(qi21::launch_qkrope(sg.rows, nh, a.panel + (size_t)sg.row0 * 2 * H, 2 * H, m->nq[l], m->nk[l], sg.rc,
+                                   sg.rs, eps, pre ? pre->kc[l] : nullptr, H, s));
+    }
+    if (pre && last) break;  // only this layer's K/V leave a prefill
+    {
+      Scope sc(m, C_FLASH, s);
+      for (const Seg& sg : segs) {
+        qi21::FlashArgs f{};
+        f.q = a.panel + (size_t)sg.row0 * 2 * H;
+        f.ldq = 2 * H;
+        f.nq = sg.rows;
+        f.heads = nh;
+        if (pre) {
+          f.k1 = pre->kc[l];
+          f.ldk1 = H;
+          f.vt1 = pre->vtc[l];
+          f.ldvt1 = pre->ldc;
+          f.n1 = pre->lp;
+          f.n2 = 0;
+          f.vis = vis;
+        } else {
+          f.k1 = sg.p->kc[l];
+          f.ldk1 = H;
+          f.vt1 = sg.p->vtc[l];
+          f.ldvt1 = sg.p->ldc;
+          f.n1 = sg.p->lp;
+          f.k2 = a.panel + (size_t)sg.row0 * 2 * H + H;
+          f.ldk2 = 2 * H;
+          f.vt2 = a.vt + sg.row0;
+          f.ldvt2 = a.cap;
+          f.n2 = sg.rows;
+          f.vis = nullptr;
+        }
+        f.out = a.att + (size_t)sg.row0 * H;
+        f.ldo = H;
+        f.oscale = p2(gd.qkv - gd.ao);
+        HIP_OK(qi21::launch_flash(f, s));
+      }
+    }
+    {
+      Scope sc(m, C_O, s);
+      HIP_OK(qi21::launch_gemm(qi21::EPI_F32, gemm_args(rows, H, H, a.att, H, m->wo[l], a.y, H, p2(gd.ao)), tile, s));
+    }
+    {
+      Scope sc(m, C_ROW, s);
+      HIP_OK(qi21::launch_rowop(rows, H, 3, a.x, a.y, a.xn, a.mods, H, 2 * H, g.eps, p2(-gd.ffn), s));
+    }
+    {
+      Scope sc(m, C_W13, s);
+      HIP_OK(qi21::launch_gemm(qi21::EPI_SWIGLU,
+                               gemm_args(rows, 2 * I, H, a.xn, H, m->w13[l], a.hid, I, p2(-gd.hid), p2(gd.ffn)),
+                               tile, s));
+    }
+    {
+      Scope sc(m, C_W2, s);
+      HIP_OK(qi21::launch_gemm(qi21::EPI_F32, gemm_args(rows, H, I, a.hid, I, m->w2[l], a.y, H, p2(gd.hid)), tile, s));
+    }
+    {
+      Scope sc(m, C_ROW, s);
+      if (last)
+        HIP_OK(qi21::launch_rowop(rows, H, 1, a.x, a.y, a.xn, a.mods, 3 * H, 0, g.eps, 1.0f, s));
+      else
+        HIP_OK(qi21::launch_rowop(rows, H, 3, a.x, a.y, a.xn, a.mods, 3 * H, 0, g.eps, p2(-gd.attn), s));
+    }
+  }
+  return QI21_OK;
+}
+
+int sync_stream(hipStream_t s) {
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(QI21_EDEVICE, "stream synchronize: %s", hipGetErrorString(e));
+  return QI21_OK;
+}
+
+}  // namespace
+
+// ───────────────────────────── C ABI ─────────────────────────────
+
+extern "C" {
+
+const char* qi21_last_error(void) { return g_err.c_str(); }
+
+void qi21_default_options(qi21_options* o) {
+  if (!o) return;
+  std::memset(o, 0, sizeof *o);
+  o->shift_attn = 2;
+  o->shift_qkv = 4;
+  o->shift_ao = 4;
+  o->shift_ffn = 2;
+  o->shift_hid = 8;
+  o->max_programs = 2;
+  o->profile = 0;
+  o->gemm_tile = -1;
+}
+
+size_t qi21_model_bytes(const qi21_model* m) { return m ? m->bytes : 0; }
+
+void qi21_model_destroy(qi21_model* m) {
+  if (!m) return;
+  (void)hipDeviceSynchronize();
+  for (auto& p : m->progs) free_prog(m, p);
+  m->progs.clear();
+  free_acts(m);
+  const size_t H = m->g.hidden, I = m->g.inter;
+  for (int l = 0; l < m->nb; ++l) {
+    dfree(m, m->wqkv[l], 3 * H * H * 2);
+    dfree(m, m->wo[l], H * H * 2);
+    dfree(m, m->w13[l], 2 * I * H * 2);
+    dfree(m, m->w2[l], H * I * 2);
+    dfree(m, m->nq[l], 128 * 4);
+    dfree(m, m->nk[l], 128 * 4);
+  }
+  dfree(m, m->img_in, H * 64 * 4);
+  dfree(m, m->proj_out_t, H * 64 * 4);
+  dfree(m, m->dflag, 256);
+  if (m->hflag) (void)hipHostFree(m->hflag);
+  for (int c = 0; c < NCLASS; ++c)
+    for (auto e : m->prof.ev[c]) (void)hipEventDestroy(e);
+  delete m;
+}
+
+int qi21_model_create(const qi21_geom* geom, const qi21_options* opt, int nblocks, const float* img_in,
+                      const float* proj_out, void* stream, qi21_model** out) {
+  g_err.clear();
+  if (!out) return fail(QI21_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = check_geom(geom);
+  if (rc) return rc;
+  if (nblocks < 1 || nblocks > 4096) return fail(QI21_EINVAL, "nblocks %d", nblocks);
+  if (!img_in || !proj_out) return fail(QI21_EINVAL, "img_in / proj_out is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  qi21_model* m = new qi21_model();
+  m->g = *geom;
+  if (opt)
+    m->o = *opt;
+  else
+    qi21_default_options(&m->o);
+  if ((m->o.alloc == nullptr) != (m->o.free == nullptr)) {
+    delete m;
+    return fail(QI21_EINVAL, "alloc and free hooks must be given together");
+  }
+  if (m->o.max_programs < 1) m->o.max_programs = 1;
+  m->nb = nblocks;
+  const size_t H = geom->hidden, I = geom->inter;
+  m->wqkv.assign(nblocks, nullptr);
+  m->wo.assign(nblocks, nullptr);
+  m->w13.assign(nblocks, nullptr);
+  m->w2.assign(nblocks, nullptr);
+  m->nq.assign(nblocks, nullptr);
+  m->nk.assign(nblocks, nullptr);
+  m->set.assign(nblocks, 0);
+  bool ok = true;
+  for (int l = 0; l < nblocks && ok; ++l) {
+    ok = (m->wqkv[l] = (f16*)dalloc(m, 3 * H * H * 2)) && (m->wo[l] = (f16*)dalloc(m, H * H * 2)) &&
+         (m->w13[l] = (f16*)dalloc(m, 2 * I * H * 2)) && (m->w2[l] = (f16*)dalloc(m, H * I * 2)) &&
+         (m->nq[l] = (float*)dalloc(m, 128 * 4)) && (m->nk[l] = (float*)dalloc(m, 128 * 4));
+  }
+  ok = ok && (m->img_in = (float*)dalloc(m, H * 64 * 4)) && (m->proj_out_t = (float*)dalloc(m, H * 64 * 4)) &&
+       (m->dflag = (int*)dalloc(m, 256));
+  if (!ok) {
+    qi21_model_destroy(m);
+    return fail(QI21_ENOMEM, "weight planes for %d blocks (%.2f GB) did not fit", nblocks,
+                (double)nblocks * (4 * H * H + 3 * H * I) * 2 / 1e9);
+  }
+  if (hipHostMalloc((void**)&m->hflag, sizeof(int), hipHostMallocDefault) != hipSuccess) {
+    m->hflag = nullptr;
+    qi21_model_destroy(m);
+    return fail(QI21_ENOMEM, "pinned host flag");
+  }
+  hipError_t e = hipMemcpyAsync(m->img_in, img_in, H * 64 * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = qi21::launch_transpose_f32(64, (int)H, proj_out, m->proj_out_t, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    qi21_model_destroy(m);
+    return fail(QI21_EDEVICE, "model upload: %s", hipGetErrorString(e));
+  }
+  *out = m;
+  return QI21_OK;
+}
+
+int qi21_model_set_block(qi21_model* m, int layer, int w_dtype, const void* const* w, const float* norm_q,
+                         const float* norm_k, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QI21_EINVAL, "model is NULL");
+  if (layer < 0 || layer >= m->nb) return fail(QI21_EINVAL, "layer %d of %d", layer, m->nb);
+  if (w_dtype < QI21_F32 || w_dtype > QI21_F16) return fail(QI21_EINVAL, "weight dtype %d", w_dtype);
+  if (!w || !norm_q || !norm_k) return fail(QI21_EINVAL, "weight pointers are NULL");
+  for (int i = 0; i < 7; ++i)
+    if (!w[i]) return fail(QI21_EINVAL, "weight %d is NULL", i);
+  hipStream_t s = (hipStream_t)stream;
+  const int H = m->g.hidden, I = m->g.inter;
+  // qkv plane rows: q [0, H), k [H, 2H), v [2H, 3H)
+  for (int i = 0; i < 3; ++i) HIP_OK(qi21::launch_plane(w_dtype, w[i], H, H, m->wqkv[layer], H, 0, i * H, s));
+  HIP_OK(qi21::launch_plane(w_dtype, w[3], H, H, m->wo[layer], H, 0, 0, s));
+  // gate/up interleaved by 32 rows: plane rows 64j + r = gate 32j + r, 64j + 32 + r = up 32j + r
+  HIP_OK(qi21::launch_plane(w_dtype, w[4], I, H, m->w13[layer], 32, 64, 0, s));
+  HIP_OK(qi21::launch_plane(w_dtype, w[5], I, H, m->w13[layer], 32, 64, 32, s));
+  HIP_OK(qi21::launch_plane(w_dtype, w[6], H, I, m->w2[layer], H, 0, 0, s));
+  HIP_OK(hipMemcpyAsync(m->nq[layer], norm_q, 128 * 4, hipMemcpyDeviceToDevice, s));
+  HIP_OK(hipMemcpyAsync(m->nk[layer], norm_k, 128 * 4, hipMemcpyDeviceToDevice, s));
+  int rc = sync_stream(s);
+  if (rc) return rc;
+  m->set[layer] = 1;
+  return QI21_OK;
+}
+
+int qi21_prefill(qi21_model* m, uint64_t key, int lp, int n, const float* x, const float* rope_p_cos,
+                 const float* rope_p_sin, const float* rope_t_cos, const float* rope_t_sin, const uint32_t* vis,
+                 const float* mods0, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QI21_EINVAL, "model is NULL");
+  if (lp < 1 || n < 1 || lp > (1 << 20) || n > (1 << 20)) return fail(QI21_EINVAL, "lp %d, n %d", lp, n);
+  if (!x || !rope_p_cos || !rope_p_sin || !rope_t_cos || !rope_t_sin || !vis || !mods0)
+    return fail(QI21_EINVAL, "prefill arguments include NULL");
+  for (int l = 0; l < m->nb; ++l)
+    if (!m->set[l]) return fail(QI21_EINVAL, "block %d has no weights", l);
+  hipStream_t s = (hipStream_t)stream;
+  // the mask the kernel walks: non-decreasing, each row sees >= 1 key
+  std::vector<uint32_t> hv(lp);
+  HIP_OK(hipMemcpyAsync(hv.data(), vis, (size_t)lp * 4, hipMemcpyDeviceToHost, s));
+  int rc = sync_stream(s);
+  if (rc) return rc;
+  for (int i = 0; i < lp; ++i) {
+    if (hv[i] < 1 || hv[i] > (uint32_t)lp)
+      return fail(QI21_EINVAL, "vis[%d] = %u is outside [1, %d]", i, hv[i], lp);
+    if (i && hv[i] < hv[i - 1]) return fail(QI21_EINVAL, "vis is not non-decreasing at row %d", i);
+  }
+  // replace the key, evict the oldest past max_programs
+  for (auto it = m->progs.begin(); it != m->progs.end(); ++it)
+    if (it->key == key) {
+      free_prog(m, *it);
+      m->progs.erase(it);
+      break;
+    }
+  while ((int)m->progs.size() >= m->o.max_programs) {
+    free_prog(m, m->progs.front());
+    m->progs.pop_front();
+  }
+  rc = ensure_acts(m, std::max(lp, n), s);
+  if (rc) return rc;
+  const size_t H = m->g.hidden;
+  Prog p;
+  p.key = key;
+  p.lp = lp;
+  p.n = n;
+  p.ldc = (int)round_up((size_t)lp, 64);
+  bool ok = true;
+  for (int l = 0; l < m->nb && ok; ++l) {
+    f16* k = (f16*)dalloc(m, (size_t)lp * H * 2);
+    f16* v = (f16*)dalloc(m, H * p.ldc * 2);
+    if (k) p.kc.push_back(k);
+    if (v) p.vtc.push_back(v);
+    ok = k && v;
+    if (!ok) {
+      if (k && !v) { dfree(m, k, (size_t)lp * H * 2); p.kc.pop_back(); }
+      if (v && !k) { dfree(m, v, H * p.ldc * 2); p.vtc.pop_back(); }
+    }
+  }
+  ok = ok && (p.rc = (float*)dalloc(m, (size_t)n * 64 * 4)) && (p.rs = (float*)dalloc(m, (size_t)n * 64 * 4));
+  if (!ok) {
+    free_prog(m, p);
+    return fail(QI21_ENOMEM, "prefix cache of %d rows x %d blocks did not fit", lp, m->nb);
+  }
+  for (auto* v : p.vtc) HIP_OK(qi21::launch_fill32(v, 0u, H * p.ldc / 2, s));
+  HIP_OK(hipMemcpyAsync(p.rc, rope_t_cos, (size_t)n * 64 * 4, hipMemcpyDeviceToDevice, s));
+  HIP_OK(hipMemcpyAsync(p.rs, rope_t_sin, (size_t)n * 64 * 4, hipMemcpyDeviceToDevice, s));
+  // the prefix pass
+  Acts& a = m->acts;
+  const Guard gd = guards(m);
+  HIP_OK(qi21::launch_mods((int)H, mods0, a.mods, s));
+  HIP_OK(hipMemcpyAsync(a.x, x, (size_t)lp * H * 4, hipMemcpyDeviceToDevice, s));
+  HIP_OK(qi21::launch_rowop(lp, (int)H, 2, a.x, a.y, a.xn, a.mods, 0, 0, m->g.eps, p2(-gd.attn), s));
+  std::vector<Seg> segs{Seg{0, lp, nullptr, rope_p_cos, rope_p_sin}};
+  rc = run_blocks(m, lp, segs, &p, vis, s);
+  if (rc == QI21_OK) rc = sync_stream(s);
+  prof_collect(m);
+  if (rc) {
+    free_prog(m, p);
+    return rc;
+  }
+  m->progs.push_back(std::move(p));
+  return QI21_OK;
+}
+
+int qi21_step_batch(qi21_model* m, int nprog, const uint64_t* keys, const float* const* xtok, const float* mods,
+                    const float* fs, float* const* out, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QI21_EINVAL, "model is NULL");
+  if (nprog < 1 || nprog > 64 || !keys || !xtok || !out || !mods || !fs)
+    return fail(QI21_EINVAL, "step arguments include NULL or nprog %d", nprog);
+  // each program's rows start at a multiple of 64 of the shared
+  // activations, so its V^T columns stay 16-byte aligned for the attention
+  // kernel; the few gap rows between programs carry finite values nobody reads
+  std::vector<Prog*> ps(nprog);
+  std::vector<int> start(nprog);
+  int rows = 0;
+  for (int i = 0; i < nprog; ++i) {
+    ps[i] = find_prog(m, keys[i]);
+    if (!ps[i]) return fail(QI21_ENOKEY, "no program for key %llu", (unsigned long long)keys[i]);
+    if (!xtok[i] || !out[i]) return fail(QI21_EINVAL, "xtok / out %d is NULL", i);
+    for (int j = 0; j < i; ++j)
+      if (ps[j] == ps[i]) return fail(QI21_EINVAL, "key %llu appears twice", (unsigned long long)keys[i]);
+    start[i] = (int)round_up((size_t)rows, 64);
+    rows = start[i] + ps[i]->n;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  int rc = ensure_acts(m, rows, s);
+  if (rc) return rc;
+  const int H = m->g.hidden;
+  Acts& a = m->acts;
+  const Guard gd = guards(m);
+  std::vector<Seg> segs;
+  {
+    Scope sc(m, C_IO, s);
+    HIP_OK(qi21::launch_fill32(m->dflag, 0u, 1, s));
+    HIP_OK(qi21::launch_mods(H, mods, a.mods, s));
+    for (int i = 0; i < nprog; ++i) {
+      segs.push_back(Seg{start[i], ps[i]->n, ps[i], ps[i]->rc, ps[i]->rs});
+      HIP_OK(qi21::launch_embed(ps[i]->n, H, xtok[i], m->img_in, a.x + (size_t)start[i] * H, s));
+    }
+  }
+  {
+    Scope sc(m, C_ROW, s);
+    HIP_OK(qi21::launch_rowop(rows, H, 2, a.x, a.y, a.xn, a.mods, 0, 0, m->g.eps, p2(-gd.attn), s));
+  }
+  rc = run_blocks(m, rows, segs, nullptr, nullptr, s);
+  if (rc) {
+    (void)hipStreamSynchronize(s);
+    prof_collect(m);
+    return rc;
+  }
+  {
+    Scope sc(m, C_IO, s);
+    HIP_OK(qi21::launch_final(rows, H, a.x, fs, m->proj_out_t, m->g.eps, a.out, m->dflag, s));
+    for (const Seg& sg : segs)
+      HIP_OK(qi21::launch_commit(sg.rows * 64, a.out + (size_t)sg.row0 * 64,
+                                 out[&sg - segs.data()], m->dflag, s));
+    HIP_OK(hipMemcpyAsync(m->hflag, m->dflag, sizeof(int), hipMemcpyDeviceToHost, s));
+  }
+  rc = sync_stream(s);
+  prof_collect(m);
+  if (rc) return rc;
+  if (*m->hflag) return fail(QI21_ENONFINITE, "the step produced a non-finite velocity (a range guard overflowed?)");
+  return QI21_OK;
+}
+
+int qi21_step(qi21_model* m, uint64_t key, const float* xtok, const float* mods, const float* fs, float* out,
+              void* stream) {
+  return qi21_step_batch(m, 1, &key, &xtok, mods, fs, &out, stream);
+}
+
+int qi21_release_key(qi21_model* m, uint64_t key) {
+  g_err.clear();
+  if (!m) return fail(QI21_EINVAL, "model is NULL");
+  for (auto it = m->progs.begin(); it != m->progs.end(); ++it)
+    if (it->key == key) {
+      (void)hipDeviceSynchronize();
+      free_prog(m, *it);
+      m->progs.erase(it);
+      return QI21_OK;
+    }
+  return fail(QI21_ENOKEY, "no program for key %llu", (unsigned long long)key);
+}
+
+int qi21_set_profile(qi21_model* m, int class_mask) {
+  if (!m) return fail(QI21_EINVAL, "model is NULL");
+  m->o.profile = class_mask;
+  return QI21_OK;
+}
+
+int qi21_profile_read(qi21_model* m, double* ms, int64_t* launches) {
+  if (!m || !ms || !launches) return fail(QI21_EINVAL, "NULL argument");
+  for (int c = 0; c < NCLASS; ++c) {
+    ms[c] = m->prof.ms[c];
+    launches[c] = m->prof.n[c];
+    m->prof.ms[c] = 0.0;
+    m->prof.n[c] = 0;
+  }
+  return QI21_OK;
+}
+
+// ───────────────────────────── single-kernel entry points ─────────────────────────────
+
+int qi21_op_gemm(int epi, int M, int N, int K, const void* A, int lda, const void* W, void* out, int ldo, void* out2,
+                 int ld2, float oscale, float inscale, int tile, void* stream) {
+  g_err.clear();
+  if (epi < QI21_EPI_F16 || epi > QI21_EPI_QKV) return fail(QI21_EINVAL, "epilogue %d", epi);
+  if (M < 1 || N < 128 || K < 64 || N % 128 || K % 64 || lda % 8 || lda < K)
+    return fail(QI21_EINVAL, "gemm M %d N %d K %d lda %d (need N %% 128, K %% 64, lda %% 8, lda >= K)", M, N, K, lda);
+  if (!A || !W || !out) return fail(QI21_EINVAL, "gemm pointer is NULL");
+  const int ocols = epi == QI21_EPI_SWIGLU ? N / 2 : epi == QI21_EPI_QKV ? 2 * N / 3 : N;
+  if (ldo < ocols) return fail(QI21_EINVAL, "ldo %d < %d output columns", ldo, ocols);
+  if (epi == QI21_EPI_QKV && ((N / 3) % 128 || N % 3 || !out2 || ld2 % 4 || ld2 < M))
+    return fail(QI21_EINVAL, "qkv epilogue needs N/3 %% 128 == 0, out2, ld2 %% 4 == 0, ld2 >= M");
+  if (tile < -1 || tile > 1 || (tile == 0 && N % 256)) return fail(QI21_EINVAL, "tile %d for N %d", tile, N);
+  qi21::GemmArgs a = gemm_args(M, N, K, (const f16*)A, lda, (const f16*)W, out, ldo, oscale, inscale, (f16*)out2, ld2);
+  HIP_OK(qi21::launch_gemm(epi, a, tile, (hipStream_t)stream));
+  return QI21_OK;
+}
+
+int qi21_op_flash(int nq, int heads, const void* q, int ldq, const void* k1, int ldk1, const void* vt1, int ldvt1,
+                  int n1, const void* k2, int ldk2, const void* vt2, int ldvt2, int n2, const uint32_t* vis, void* out,
+                  int ldo, float oscale, void* stream) {
+  g_err.clear();
+  if (nq < 1 || heads < 1 || n1 < 0 || n2 < 0 || n1 + n2 < 1) return fail(QI21_EINVAL, "flash sizes");
+  if (!q || !out || (n1 && (!k1 || !vt1)) || (n2 && (!k2 || !vt2))) return fail(QI21_EINVAL, "flash pointer NULL");
+  if (ldq % 8 || ldo % 4 || ldq < heads * 128 || ldo < heads * 128) return fail(QI21_EINVAL, "flash ldq / ldo");
+  if (n1 && (ldk1 % 8 || ldvt1 % 8 || ldk1 < heads * 128 || (size_t)ldvt1 < round_up(n1, 64)))
+    return fail(QI21_EINVAL, "flash source 1 leading dimensions");
+  if (n2 && (ldk2 % 8 || ldvt2 % 8 || ldk2 < heads * 128 || (size_t)ldvt2 < round_up(n2, 64)))
+    return fail(QI21_EINVAL, "flash source 2 leading dimensions");
+  qi21::FlashArgs f{};
+  f.q = (const f16*)q;
+  f.ldq = ldq;
+  f.nq = nq;
+  f.heads = heads;
+  f.k1 = (const f16*)k1;
+  f.ldk1 = ldk1;
+  f.vt1 = (const f16*)vt1;
+  f.ldvt1 = ldvt1;
+  f.n1 = n1;
+  f.k2 = (const f16*)k2;
+  f.ldk2 = ldk2;
+  f.vt2 = (const f16*)vt2;
+  f.ldvt2 = ldvt2;
+  f.n2 = n2;
+  f.vis = vis;
+  f.out = (f16*)out;
+  f.ldo = ldo;
+  f.oscale = oscale;
+  HIP_OK(qi21::launch_flash(f, (hipStream_t)stream));
+  return QI21_OK;
+}
+
+int qi21_op_rowop(int rows, int h, int mode, float* x, const float* y, void* xn, const float* mods, int g_off,
+                  int s_off, float eps, float oscale, void* stream) {
+  g_err.clear();
+  if (rows < 1 || h < 4 || h % 4 || h > 8192 || mode < 1 || mode > 3 || g_off % 4 || s_off % 4 || g_off < 0 ||
+      s_off < 0)
+    return fail(QI21_EINVAL, "rowop rows %d h %d mode %d", rows, h, mode);
+  if (!x || !mods || ((mode & 1) && !y) || ((mode & 2) && !xn)) return fail(QI21_EINVAL, "rowop pointer NULL");
+  HIP_OK(qi21::launch_rowop(rows, h, mode, x, y, (f16*)xn, mods, g_off, s_off, eps, oscale, (hipStream_t)stream));
+  return QI21_OK;
+}
+
+int qi21_op_qkrope(int rows, int heads, void* panel, int ldp, const float* norm_q, const float* norm_k,
+                   const float* cos, const float* sin, float eps, void* kdst, int ldk, void* stream) {
+  g_err.clear();
+  if (rows < 1 || heads < 1 || ldp < 2 * heads * 128 || ldp % 2 || (kdst && (ldk < heads * 128 || ldk % 2)))
+    return fail(QI21_EINVAL, "qkrope rows %d heads %d ldp %d", rows, heads, ldp);
+  if (!panel || !norm_q || !norm_k || !cos || !sin) return fail(QI21_EINVAL, "qkrope pointer NULL");
+  HIP_OK(qi21::launch_qkrope(rows, heads, (f16*)panel, ldp, norm_q, norm_k, cos, sin, eps, (f16*)kdst, ldk,
+                             (hipStream_t)stream));
+  return QI21_OK;
+}
+
+int qi21_op_embed(int rows, int h, const float* tok, const float* img_in, float* x, void* stream) {
+  g_err.clear();
+  if (rows < 1 || h < 64 || h % 64 || !tok || !img_in || !x) return fail(QI21_EINVAL, "embed rows %d h %d", rows, h);
+  HIP_OK(qi21::launch_embed(rows, h, tok, img_in, x, (hipStream_t)stream));
+  return QI21_OK;
+}
+
+int qi21_op_final(int rows, int h, const float* x, const float* fs, const float* proj_out_t, float eps, float* out,
+                  int* flag, void* stream) {
+  g_err.clear();
+  if (rows < 1 || h < 256 || h % 256 || !x || !fs || !proj_out_t || !out || !flag)
+    return fail(QI21_EINVAL, "final rows %d h %d", rows, h);
+  HIP_OK(qi21::launch_final(rows, h, x, fs, proj_out_t, eps, out, flag, (hipStream_t)stream));
+  return QI21_OK;
+}
+
+int qi21_op_mods(int h, const float* mods, float* mods_dev, void* stream) {
+  g_err.clear();
+  if (h < 1 || !mods || !mods_dev) return fail(QI21_EINVAL, "mods h %d", h);
+  HIP_OK(qi21::launch_mods(h, mods, mods_dev, (hipStream_t)stream));
+  return QI21_OK;
+}
+
+int qi21_op_plane(int src_dtype, const void* src, int rows, int cols, void* dst, int group, int gstride, int goff,
+                  void* stream) {
+  g_err.clear();
+  if (src_dtype < QI21_F32 || src_dtype > QI21_F16 || rows < 1 || cols < 1 || group < 1 || gstride < 0 || goff < 0 ||
+      !src || !dst)
+    return fail(QI21_EINVAL, "plane arguments");
+  HIP_OK(qi21::launch_plane(src_dtype, src, rows, cols, (f16*)dst, group, gstride, goff, (hipStream_t)stream));
+  return QI21_OK;
+}
+
+}  // extern "C"

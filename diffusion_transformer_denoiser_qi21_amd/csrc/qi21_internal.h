@@ -1,0 +1,101 @@
+// Internal launch interface of the qi21 kernels (gfx950 / CDNA4).
+//
+// Every launcher takes device pointers and a HIP stream and assumes its
+// shape arguments were validated by the caller (qi21_api.cpp checks them
+// on the host before any launch); the comment on each one states what it
+// assumes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qi21 {
+
+typedef _Float16 f16;
+
+enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
+
+// C = A * W^T over f16 operands with f32 accumulation.
+//   A: [M][lda] f16 (K contiguous), W: [N][K] f16 (K contiguous).
+//   EPI_F16:    out f16 [M][ldo] = acc * oscale
+//   EPI_F32:    out f32 [M][ldo] = acc * oscale
+//   EPI_SWIGLU: W is the interleaved gate/up plane (groups of 32 gate rows,
+//               then the 32 matching up rows); out f16 [M][ldo] with N/2
+//               columns = silu(g*inscale) * (u*inscale) * oscale
+//   EPI_QKV:    columns [0, 2H) -> out f16 [M][ldo] (q|k), columns [2H, 3H)
+//               -> out2 f16 transposed, out2[c - 2H][row] with leading
+//               dimension ld2 (V^T), both * oscale; H = N/3.
+// Assumes: N % 128 == 0, K % 64 == 0, M >= 1, 16-byte aligned rows
+// (lda, K multiples of 8), for EPI_QKV N/3 % 128 == 0 and ld2 >= M.
+struct GemmArgs {
+  int M, N, K;
+  const f16* A; int lda;
+  const f16* W;
+  void* out; int ldo;
+  f16* out2; int ld2;
+  float oscale, inscale;
+};
+hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s);
+// the tile a launch would pick (0: 256x256, 1: 128x128, ...)
+int gemm_pick_tile(int M, int N, int K);
+
+// Flash attention, head_dim 128, over up to two key sources.  Keys
+// [0, n1) come from source 1 (K rows k1 + j*ldk1 + h*128, V^T rows
+// vt1 + (h*128 + d)*ldvt1 + j), keys [n1, n1+n2) from source 2 likewise.
+// Query i sees keys j < vis[i] when vis != nullptr (vis non-decreasing,
+// 1 <= vis[i] <= n1 + n2), else all keys.  out f16 [nq][ldo] at column
+// h*128 = softmax(q k^T / sqrt(128)) V * oscale.
+// Assumes: V^T leading dimensions are multiples of 8 and at least
+// round_up(n, 64) with finite (zeroed) padding; K rows 16-byte aligned.
+struct FlashArgs {
+  const f16* q; int ldq; int nq; int heads;
+  const f16* k1; int ldk1; const f16* vt1; int ldvt1; int n1;
+  const f16* k2; int ldk2; const f16* vt2; int ldvt2; int n2;
+  const uint32_t* vis;
+  f16* out; int ldo;
+  float oscale;
+};
+hipError_t launch_flash(const FlashArgs& a, hipStream_t s);
+
+// rowop over `rows` rows of width h (h % 4 == 0, h <= 8192):
+//   mode & 1: x += gate (.) y            (gate = mods + g_off, already tanh-ed)
+//   mode & 2: xn = f16(LN(x) * (1 + mods[s_off + c]) * oscale)
+hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16* xn,
+                        const float* mods, int g_off, int s_off, float eps, float oscale,
+                        hipStream_t s);
+
+// Per-head RMSNorm(w) + interleaved RoPE on the q and k columns of the
+// panel (q at column 0, k at column heads*128, row stride ldp), in place.
+// If kdst != nullptr the normalised k goes to kdst[row][ldk] instead.
+// cos/sin: [rows][64] f32.  eps is the norm's eps (already scaled for the
+// panel's range guard).
+hipError_t launch_qkrope(int rows, int heads, f16* panel, int ldp, const float* norm_q,
+                         const float* norm_k, const float* cosb, const float* sinb, float eps,
+                         f16* kdst, int ldk, hipStream_t s);
+
+// x[r][c] = sum_k tok[r][k] * img_in[c][k], k < 64, f32.  h % 64 == 0.
+hipError_t launch_embed(int rows, int h, const float* tok, const float* img_in, float* x,
+                        hipStream_t s);
+
+// out[r][o] = sum_c (LN(x[r])[c] * fs[c]) * proj_out_t[c][o], o < 64, f32;
+// sets *flag |= 1 when any output is not finite.  h % 256 == 0.
+hipError_t launch_final(int rows, int h, const float* x, const float* fs, const float* proj_out_t,
+                        float eps, float* out, int* flag, hipStream_t s);
+
+// dst[i] = flag == 0 ? src[i] : dst[i], i < count (count % 4 == 0).
+hipError_t launch_commit(int count, const float* src, float* dst, const int* flag, hipStream_t s);
+
+// mods_dev = [s1 | tanh g1 | s2 | tanh g2] from the raw [4h] modulation.
+hipError_t launch_mods(int h, const float* mods, float* mods_dev, hipStream_t s);
+
+// Weight conversion to f16: dst row (r / group) * gstride + goff + r % group
+// (ld = cols) receives source row r.  src_dtype 0 f32, 1 bf16, 2 f16.
+hipError_t launch_plane(int src_dtype, const void* src, int rows, int cols, f16* dst, int group,
+                        int gstride, int goff, hipStream_t s);
+
+// out f32 [cols][rows] = transpose of in f32 [rows][cols]
+hipError_t launch_transpose_f32(int rows, int cols, const float* in, float* out, hipStream_t s);
+
+// fill count 32-bit words with value (a kernel, so it is safe to capture)
+hipError_t launch_fill32(void* p, uint32_t value, size_t count, hipStream_t s);
+
+}  // namespace qi21

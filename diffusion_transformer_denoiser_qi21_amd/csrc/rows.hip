@@ -1,0 +1,326 @@
+// Bandwidth-bound row kernels of the denoiser step: the gated residual +
+// modulated LayerNorm (rowop), the per-head q/k RMSNorm + RoPE (qkrope),
+// the img_in embedding, the final LayerNorm + proj_out, and small helpers
+// (gate tanh, weight-plane conversion, output commit, fill).
+//
+// Access pattern: every row is read with 16-byte (float4 / 8 x f16) or
+// 4-byte-per-lane fully coalesced loads; reductions are wave64 shuffles
+// followed by one LDS exchange between the waves of a block.
+#include "qi21_internal.h"
+
+namespace qi21 {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// sum over a 256-thread block; red must hold 4 floats; all threads get it
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  const float r = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return r;
+}
+
+// ───────────────────────────── rowop ─────────────────────────────
+// One 256-thread block per row; thread t owns the float4 chunks
+// t, t + 256, ... of the row (h/4 chunks, at most 8 per thread).
+template <int MODE>
+__global__ __launch_bounds__(256) void rowop_kernel(int h, float* __restrict__ x, const float* __restrict__ y,
+                                                   f16* __restrict__ xn, const float* __restrict__ mods,
+                                                   int g_off, int s_off, float eps, float oscale) {
+  __shared__ float red[4];
+  const int row = blockIdx.x, t = threadIdx.x;
+  const int nc = h >> 2;
+  float4v* xr = reinterpret_cast<float4v*>(x + (size_t)row * h);
+  float4v v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = t + 256 * j;
+    if (c < nc) {
+      v[j] = xr[c];
+      if (MODE & 1) {
+        const float4v yv = reinterpret_cast<const float4v*>(y + (size_t)row * h)[c];
+        const float4v g = reinterpret_cast<const float4v*>(mods + g_off)[c];
+        v[j] = v[j] + g * yv;
+        xr[c] = v[j];
+      }
+    }
+  }
+  if (!(MODE & 2)) return;
+  float sm = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (t + 256 * j < nc) sm += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
+  const float mean = block_sum256(sm, red) / (float)h;
+  float q = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (t + 256 * j < nc) {
+      const float4v d = v[j] - mean;
+      q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
+    }
+  const float inv = rsqrtf(block_sum256(q, red) / (float)h + eps);
+  half4* xo = reinterpret_cast<half4*>(xn + (size_t)row * h);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = t + 256 * j;
+    if (c < nc) {
+      const float4v s = reinterpret_cast<const float4v*>(mods + s_off)[c];
+      const float4v r = (v[j] - mean) * inv * (1.0f + s) * oscale;
+      xo[c] = half4{(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
+    }
+  }
+}
+
+hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16* xn, const float* mods,
+                        int g_off, int s_off, float eps, float oscale, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  switch (mode) {
+    case 1: hipLaunchKernelGGL(rowop_kernel<1>, dim3(rows), dim3(256), 0, s, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
+    case 2: hipLaunchKernelGGL(rowop_kernel<2>, dim3(rows), dim3(256), 0, s, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
+    case 3: hipLaunchKernelGGL(rowop_kernel<3>, dim3(rows), dim3(256), 0, s, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ───────────────────────────── qkrope ─────────────────────────────
+// One wave per (row, head, q|k); lane l owns the interleaved pair
+// (2l, 2l+1) of the head, which is also RoPE column l.
+__global__ __launch_bounds__(256) void qkrope_kernel(int rows, int heads, f16* __restrict__ panel, int ldp,
+                                                     const float* __restrict__ norm_q,
+                                                     const float* __restrict__ norm_k,
+                                                     const float* __restrict__ cosb,
+                                                     const float* __restrict__ sinb, float eps,
+                                                     f16* __restrict__ kdst, int ldk) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);  // (head, q|k) index
+  const int row = blockIdx.y;
+  if (item >= 2 * heads) return;
+  const bool isk = item >= heads;
+  const int hd = isk ? item - heads : item;
+  const int col = (isk ? heads * 128 : 0) + hd * 128 + 2 * lane;
+  const half2v pv = *reinterpret_cast<const half2v*>(panel + (size_t)row * ldp + col);
+  const float a = (float)pv[0], b = (float)pv[1];
+  const float ss = wave_sum(a * a + b * b);
+  const float inv = rsqrtf(ss * (1.0f / 128.0f) + eps);
+  const float* w = isk ? norm_k : norm_q;
+  const float na = (a * inv) * w[2 * lane], nb = (b * inv) * w[2 * lane + 1];
+  const float c = cosb[(size_t)row * 64 + lane], sn = sinb[(size_t)row * 64 + lane];
+  const half2v r = half2v{(f16)(na * c - nb * sn), (f16)(na * sn + nb * c)};
+  if (isk && kdst)
+    *reinterpret_cast<half2v*>(kdst + (size_t)row * ldk + hd * 128 + 2 * lane) = r;
+  else
+    *reinterpret_cast<half2v*>(panel + (size_t)row * ldp + col) = r;
+}
+
+hipError_t launch_qkrope(int rows, int heads, f16* panel, int ldp, const float* norm_q, const float* norm_k,
+                         const float* cosb, const float* sinb, float eps, f16* kdst, int ldk, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  dim3 grid((2 * heads + 3) / 4, rows);
+  hipLaunchKernelGGL(qkrope_kernel, grid, dim3(256), 0, s, rows, heads, panel, ldp, norm_q, norm_k, cosb, sinb,
+                     eps, kdst, ldk);
+  return hipGetLastError();
+}
+
+// ───────────────────────────── embed ─────────────────────────────
+// Block tile 64 rows x 64 columns, K = 64; tok and img_in tiles in LDS,
+// each thread 4 rows x 4 columns (columns tx, tx+16, tx+32, tx+48).
+__global__ __launch_bounds__(256) void embed_kernel(int rows, int h, const float* __restrict__ tok,
+                                                    const float* __restrict__ w, float* __restrict__ x) {
+  __shared__ float st[64][65];
+  __shared__ float sw[64][65];
+  const int t = threadIdx.x;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  for (int i = t; i < 64 * 64; i += 256) {
+    const int r = i >> 6, k = i & 63;
+    st[r][k] = tok[(size_t)min(r0 + r, rows - 1) * 64 + k];
+    sw[r][k] = w[(size_t)(c0 + r) * 64 + k];
+  }
+  __syncthreads();
+  const int ty = t >> 4, tx = t & 15;
+  float acc[4][4] = {};
+  for (int k = 0; k < 64; ++k) {
+    float av[4], bv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) av[i] = st[ty * 4 + i][k];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = sw[tx + 16 * j][k];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + ty * 4 + i;
+    if (r < rows)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[(size_t)r * h + c0 + tx + 16 * j] = acc[i][j];
+  }
+}
+
+hipError_t launch_embed(int rows, int h, const float* tok, const float* img_in, float* x, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  dim3 grid(h / 64, (rows + 63) / 64);
+  hipLaunchKernelGGL(embed_kernel, grid, dim3(256), 0, s, rows, h, tok, img_in, x);
+  return hipGetLastError();
+}
+
+// ───────────────────────────── final ─────────────────────────────
+// 16 rows per block.  Phase 1: each wave computes mean / inverse std of 4
+// rows.  Phase 2: columns in chunks of 256; the chunk's normalised values
+// (x - mean) * inv * fs go to LDS, then thread (o = t % 64, rows 4*(t/64)..)
+// accumulates over the chunk with proj_out^T rows (coalesced over o).
+__global__ __launch_bounds__(256) void final_kernel(int rows, int h, const float* __restrict__ x,
+                                                    const float* __restrict__ fs,
+                                                    const float* __restrict__ pt, float eps,
+                                                    float* __restrict__ out, int* __restrict__ flag) {
+  __shared__ float xs[16][257];
+  __shared__ float mean_s[16], inv_s[16];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r0 = blockIdx.x * 16;
+  for (int i = 0; i < 4; ++i) {
+    const int rl = wave * 4 + i;
+    const int r = min(r0 + rl, rows - 1);
+    const float* xr = x + (size_t)r * h;
+    float sm = 0.0f;
+    for (int c = lane; c < h; c += 64) sm += xr[c];
+    const float mean = wave_sum(sm) / (float)h;
+    float q = 0.0f;
+    for (int c = lane; c < h; c += 64) {
+      const float d = xr[c] - mean;
+      q += d * d;
+    }
+    const float inv = rsqrtf(wave_sum(q) / (float)h + eps);
+    if (lane == 0) {
+      mean_s[rl] = mean;
+      inv_s[rl] = inv;
+    }
+  }
+  __syncthreads();
+  const int o = t & 63, rg = (t >> 6) * 4;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c0 = 0; c0 < h; c0 += 256) {
+    const float f = fs[c0 + t];
+    for (int rl = 0; rl < 16; ++rl) {
+      const int r = min(r0 + rl, rows - 1);
+      xs[rl][t] = (x[(size_t)r * h + c0 + t] - mean_s[rl]) * inv_s[rl] * f;
+    }
+    __syncthreads();
+    for (int c = 0; c < 256; ++c) {
+      const float p = pt[(size_t)(c0 + c) * 64 + o];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(xs[rg + i][c], p, acc[i]);
+    }
+    __syncthreads();
+  }
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + rg + i;
+    if (r < rows) {
+      out[(size_t)r * 64 + o] = acc[i];
+      bad |= !__builtin_isfinite(acc[i]);
+    }
+  }
+  if (bad) atomicOr(flag, 1);
+}
+
+hipError_t launch_final(int rows, int h, const float* x, const float* fs, const float* proj_out_t, float eps,
+                        float* out, int* flag, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(final_kernel, dim3((rows + 15) / 16), dim3(256), 0, s, rows, h, x, fs, proj_out_t, eps, out,
+                     flag);
+  return hipGetLastError();
+}
+
+// ───────────────────────────── helpers ─────────────────────────────
+__global__ void commit_kernel(int count, const float* __restrict__ src, float* __restrict__ dst,
+                              const int* __restrict__ flag) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (*flag == 0 && i < count / 4)
+    reinterpret_cast<float4v*>(dst)[i] = reinterpret_cast<const float4v*>(src)[i];
+}
+
+hipError_t launch_commit(int count, const float* src, float* dst, const int* flag, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(commit_kernel, dim3((count / 4 + 255) / 256), dim3(256), 0, s, count, src, dst, flag);
+  return hipGetLastError();
+}
+
+__global__ void mods_kernel(int h, const float* __restrict__ m, float* __restrict__ d) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < 4 * h) {
+    const int chunk = i / h;
+    d[i] = (chunk == 1 || chunk == 3) ? tanhf(m[i]) : m[i];
+  }
+}
+
+hipError_t launch_mods(int h, const float* mods, float* mods_dev, hipStream_t s) {
+  hipLaunchKernelGGL(mods_kernel, dim3((4 * h + 255) / 256), dim3(256), 0, s, h, mods, mods_dev);
+  return hipGetLastError();
+}
+
+__global__ void plane_kernel(int src_dtype, const void* __restrict__ src, int rows, int cols, f16* __restrict__ dst,
+                             int group, int gstride, int goff) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)rows * cols) return;
+  const int r = (int)(i / cols), c = (int)(i - (size_t)r * cols);
+  float v;
+  if (src_dtype == 0) {
+    v = reinterpret_cast<const float*>(src)[i];
+  } else if (src_dtype == 1) {
+    const unsigned short b = reinterpret_cast<const unsigned short*>(src)[i];
+    v = __uint_as_float((unsigned)b << 16);
+  } else {
+    v = (float)reinterpret_cast<const f16*>(src)[i];
+  }
+  const int dr = (r / group) * gstride + goff + r % group;
+  dst[(size_t)dr * cols + c] = (f16)v;
+}
+
+hipError_t launch_plane(int src_dtype, const void* src, int rows, int cols, f16* dst, int group, int gstride,
+                        int goff, hipStream_t s) {
+  const size_t n = (size_t)rows * cols;
+  hipLaunchKernelGGL(plane_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src_dtype, src, rows, cols,
+                     dst, group, gstride, goff);
+  return hipGetLastError();
+}
+
+__global__ void transpose_kernel(int rows, int cols, const float* __restrict__ in, float* __restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)rows * cols) return;
+  const int r = (int)(i / cols), c = (int)(i - (size_t)r * cols);
+  out[(size_t)c * rows + r] = in[i];
+}
+
+hipError_t launch_transpose_f32(int rows, int cols, const float* in, float* out, hipStream_t s) {
+  const size_t n = (size_t)rows * cols;
+  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, rows, cols, in, out);
+  return hipGetLastError();
+}
+
+__global__ void fill32_kernel(uint32_t* p, uint32_t v, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill32(void* p, uint32_t value, size_t count, hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill32_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<uint32_t*>(p), value, count);
+  return hipGetLastError();
+}
+
+}  // namespace qi21

@@ -1,0 +1,182 @@
+/* qi21 -- the Qwen-Image-2.1 single-stream denoiser step on AMD MI355X (gfx950).
+ *
+ * A plain C ABI over hand-written HIP kernels.  Sources cited below:
+ *   [QI]  docs.rs, cortiq-engine 0.8.4, src/cortiq_engine/qwen_image21.rs
+ *         (the CPU reference: module doc "Semantics", Qi21Layout, rope_tables,
+ *         block_cpu, prefill, step, step_cpu, target_rope)
+ *   [WG]  docs.rs, cortiq-engine 0.8.3, src/gpu_wgpu/qi21.rs (the device
+ *         contract: module doc, Guards, geom_ok, mods_dev, prefill, step,
+ *         release_key, release)
+ *
+ * Conventions for every call:
+ *   - Array arguments of qi21_model_create, qi21_model_set_block,
+ *     qi21_prefill, qi21_step and qi21_step_batch are DEVICE pointers (HBM of
+ *     the current HIP device), row-major, float32 unless stated; the caller
+ *     owns them and they are only read (or, for `out`, written) during the
+ *     call.  Pointer arrays themselves (w[7], keys, xtok[], out[]) live in
+ *     host memory.  Layout helpers (qi21_layout_*) take host pointers.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  qi21_prefill,
+ *     qi21_step and qi21_step_batch synchronise that stream before returning.
+ *   - Return value: QI21_OK or one of the error codes; on error
+ *     qi21_last_error() (thread-local) explains it.  A call that fails leaves
+ *     no partial result: `out` is written only when the call returns QI21_OK
+ *     ([WG] step: a non-finite velocity is refused and the output untouched).
+ *   - Shape errors and bad masks are found on the host before any device
+ *     work (EINVAL); geometry the kernels do not support gives EUNSUPPORTED;
+ *     allocation failure gives ENOMEM with no state left behind.
+ */
+#ifndef QI21_H
+#define QI21_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  QI21_OK = 0,
+  QI21_EINVAL = 1,       /* bad argument: null pointer, length, mask, layer index */
+  QI21_EUNSUPPORTED = 2, /* geometry outside what the kernels handle */
+  QI21_ENOMEM = 3,       /* device allocation failed (nothing kept) */
+  QI21_ENOKEY = 4,       /* no program for that key */
+  QI21_ENONFINITE = 5,   /* the step produced a non-finite velocity; out untouched */
+  QI21_EDEVICE = 6       /* a HIP call failed */
+};
+
+enum { QI21_F32 = 0, QI21_BF16 = 1, QI21_F16 = 2 };
+
+/* Model geometry ([QI] Qi21Config; [WG] geom_ok).  Supported: head_dim 128,
+ * heads * 128 == hidden, hidden % 128 == 0 and <= 8192, inter % 64 == 0,
+ * in_ch == 64.  eps is the LayerNorm / RMSNorm epsilon (also the final
+ * norm's, [WG] dims). */
+typedef struct {
+  int32_t hidden, heads, head_dim, inter, in_ch;
+  float eps;
+} qi21_geom;
+
+/* Device allocator hook (e.g. a framework's caching allocator).  NULL alloc
+ * = hipMalloc / hipFree.  alloc returns NULL on failure. */
+typedef void* (*qi21_alloc_fn)(size_t bytes, void* ctx);
+typedef void (*qi21_free_fn)(void* ptr, void* ctx);
+
+/* Options ([WG] Guards, knobs).  The five shifts are the power-of-two range
+ * guards of the f16 sites (stored value = x * 2^-shift), each clamped to
+ * 0..14: attention input (2), qkv panel (4), attention output (4), FFN
+ * input (2), SwiGLU hidden (8).  max_programs: prefixes kept at once (2: a
+ * positive and a negative prompt); a new key evicts the oldest.  profile:
+ * bit mask of kernel classes (see qi21_profile_read) whose launches are
+ * bracketed by HIP events on the launch stream; 0 = off. */
+typedef struct {
+  int32_t shift_attn, shift_qkv, shift_ao, shift_ffn, shift_hid;
+  int32_t max_programs;
+  int32_t profile;
+  int32_t gemm_tile; /* -1 = per-shape choice; otherwise a fixed GEMM tile id */
+  qi21_alloc_fn alloc;
+  qi21_free_fn free;
+  void* alloc_ctx;
+} qi21_options;
+
+typedef struct qi21_model qi21_model;
+
+void qi21_default_options(qi21_options* opt);
+
+/* Create a model of `nblocks` blocks.  img_in: [hidden][64]; proj_out:
+ * [64][hidden] (both copied to library-owned f32 buffers).  Weight planes
+ * of all blocks are allocated here (f16, ~ (4 H^2 + 3 H I) * 2 bytes per
+ * block) and filled by qi21_model_set_block.  opt may be NULL (defaults).
+ * Ownership: the model owns every buffer it allocates; destroy releases
+ * them. */
+int qi21_model_create(const qi21_geom* geom, const qi21_options* opt, int nblocks, const float* img_in,
+                      const float* proj_out, void* stream, qi21_model** out);
+
+/* Convert block `layer`'s weights into the model's f16 planes.  w[0..6] =
+ * to_q [H][H], to_k [H][H], to_v [H][H], to_out [H][H], gate [I][H],
+ * up [I][H], down [H][I] ([QI] Qi21Dit tensor names), row-major [out][in],
+ * element type w_dtype (QI21_F32 / QI21_BF16 / QI21_F16).  norm_q, norm_k:
+ * [128] f32.  The inputs may be freed after the call returns (it
+ * synchronises the stream).  Every block must be set before a prefill. */
+int qi21_model_set_block(qi21_model* m, int layer, int w_dtype, const void* const* w, const float* norm_q,
+                         const float* norm_k, void* stream);
+
+/* Prefill ([QI] prefill, [WG] prefill): run the lp prefix rows x [lp][H]
+ * (already embedded) through every block once with the t = 0 modulation
+ * mods0 [4H] (raw: [scale1|gate1|scale2|gate2], gates not yet tanh-ed) and
+ * the visibility mask vis [lp] (uint32, query i sees keys [0, vis[i]);
+ * must be non-decreasing with 1 <= vis[i] <= lp), keeping each layer's
+ * post-RoPE K and V as the program `key`.  rope_p_cos/sin: [lp][64] tables
+ * of the prefix rows; rope_t_cos/sin: [n][64] tables of the n target rows
+ * under this prefix's layout ([QI] target_rope).  A program with the same
+ * key is replaced; past max_programs the oldest is evicted.  Errors:
+ * EINVAL (lengths, mask), ENOMEM, EDEVICE. */
+int qi21_prefill(qi21_model* m, uint64_t key, int lp, int n, const float* x, const float* rope_p_cos,
+                 const float* rope_p_sin, const float* rope_t_cos, const float* rope_t_sin, const uint32_t* vis,
+                 const float* mods0, void* stream);
+
+/* Step ([QI] step / step_cpu, [WG] step): latent tokens xtok [n][64] ->
+ * velocity out [n][64] for program `key`, with the step modulation mods
+ * [4H] (raw, gates tanh-ed inside) and fs [H] = 1 + final_scale.  Every
+ * target row sees the lp cached prefix keys and all n target rows.
+ * Errors: ENOKEY, EINVAL, ENONFINITE (out untouched), EDEVICE. */
+int qi21_step(qi21_model* m, uint64_t key, const float* xtok, const float* mods, const float* fs, float* out,
+              void* stream);
+
+/* Several programs' steps as one batched pass (the classifier-free-guidance
+ * pair of [WG] module doc): the GEMMs and row kernels run over all
+ * programs' rows at once, attention per program against its own prefix.
+ * keys[nprog], xtok[nprog] and out[nprog] are host arrays of device
+ * pointers ([n_k][64] each); mods and fs are shared.  Same errors as
+ * qi21_step; on ENONFINITE no out is written. */
+int qi21_step_batch(qi21_model* m, int nprog, const uint64_t* keys, const float* const* xtok, const float* mods,
+                    const float* fs, float* const* out, void* stream);
+
+/* Drop one program ([WG] release_key).  Returns ENOKEY if absent. */
+int qi21_release_key(qi21_model* m, uint64_t key);
+
+/* Free everything the model holds ([WG] release).  NULL is a no-op. */
+void qi21_model_destroy(qi21_model* m);
+
+/* The last error of the calling thread (empty string if none). */
+const char* qi21_last_error(void);
+
+/* Device bytes the model holds (planes, activations, prefix caches). */
+size_t qi21_model_bytes(const qi21_model* m);
+
+/* Change the profiled class mask of a model (as opt.profile). */
+int qi21_set_profile(qi21_model* m, int class_mask);
+
+/* Profiling (opt.profile != 0): per-class device milliseconds summed over
+ * the steps since the last read, and the number of launches of each
+ * class; classes: 0 qkv GEMM, 1 qkrope, 2 flash, 3 O GEMM, 4 gate/up GEMM,
+ * 5 down GEMM, 6 rowop, 7 embed + final + io.  ms and launches hold 8
+ * entries (host).  The counters are reset. */
+int qi21_profile_read(qi21_model* m, double* ms, int64_t* launches);
+
+/* ── layout helpers (host memory, no device work) ──
+ * A layout is the joint sequence of runs, prefix first, target image last
+ * ([QI] Qi21Layout): kind 0 = text of h rows (w ignored), kind 1 = image
+ * of h x w latent tokens in raster order. */
+typedef struct {
+  int32_t kind, h, w;
+} qi21_seg;
+
+/* Prefix length and target length of a layout; EINVAL unless the last run
+ * is a non-empty image and the prefix is not empty ([QI] validate). */
+int qi21_layout_sizes(const qi21_seg* segs, int nseg, int32_t* lp, int32_t* n);
+
+/* Fill any non-NULL of: pos [total][3] (frame, row, col; [QI] positions),
+ * vis [lp] (block-causal: text row i sees i+1 keys, an image row sees to
+ * the end of its image block; [QI] prefill), cos_p/sin_p [lp][hd/2] and
+ * cos_t/sin_t [n][hd/2] RoPE tables ([QI] rope_tables: per axis of width
+ * d, frequency 1/theta^(2i/d) in float32, angle float32(pos) * frequency,
+ * columns ordered frame, row, col).  axes must be even and sum to head_dim
+ * (hd = axes sum). */
+int qi21_layout_tables(const qi21_seg* segs, int nseg, const int32_t* axes, float theta, int64_t* pos,
+                       uint32_t* vis, float* cos_p, float* sin_p, float* cos_t, float* sin_t);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QI21_H */

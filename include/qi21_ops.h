@@ -1,0 +1,89 @@
+/* qi21 single-kernel entry points.
+ *
+ * Each call runs ONE of the denoiser step's kernels on caller-owned device
+ * buffers, enqueued on `stream` (hipStream_t, NULL = default) without
+ * synchronising, after host-side shape checks (QI21_EINVAL when a shape or
+ * alignment the kernel relies on does not hold; nothing is launched then).
+ * They allocate nothing.  They exist so that each kernel can be checked and
+ * timed alone at the step's real shapes; qi21_step runs the same kernels.
+ * Element types: f16 buffers are IEEE binary16, everything else float32.
+ * Sources as in qi21.h.
+ */
+#ifndef QI21_OPS_H
+#define QI21_OPS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { QI21_EPI_F16 = 0, QI21_EPI_F32 = 1, QI21_EPI_SWIGLU = 2, QI21_EPI_QKV = 3 };
+
+/* out = A W^T ([QI] lin; the four projection sites of [WG] blocks):
+ * A f16 [M][lda] (K contiguous), W f16 [N][K].  Epilogues:
+ *   F16:    out f16 [M][ldo] = acc * oscale
+ *   F32:    out f32 [M][ldo] = acc * oscale
+ *   SWIGLU: W interleaved in groups of 32 gate rows then the matching 32 up
+ *           rows; out f16 [M][ldo], N/2 columns, = silu(g * inscale) *
+ *           (u * inscale) * oscale   ([QI] block_cpu FFN)
+ *   QKV:    columns [0, 2N/3) -> out f16 [M][ldo]; columns [2N/3, N) ->
+ *           out2 f16 transposed: out2[(c - 2N/3) * ld2 + row]; both * oscale
+ * Requires M >= 1, N % 128 == 0, K % 64 == 0, lda % 8 == 0, lda >= K,
+ * ldo >= output columns, for QKV (N/3) % 128 == 0, ld2 % 4 == 0, ld2 >= M.
+ * tile: -1 automatic, 0 = 256x256 (needs N % 256 == 0), 1 = 128x128. */
+int qi21_op_gemm(int epi, int M, int N, int K, const void* A, int lda, const void* W, void* out, int ldo,
+                 void* out2, int ld2, float oscale, float inscale, int tile, void* stream);
+
+/* Attention, head_dim 128 ([QI] attention; [WG] qi_flash): per head h,
+ * out[i][h*128 + d] = oscale * sum_j softmax_j(q_i . k_j / sqrt(128)) v_j[d]
+ * over keys j < min(n1 + n2, vis[i]) (vis == NULL: all keys).  Keys
+ * j < n1 come from k1 [j][ldk1] (column h*128) and V^T vt1 [h*128+d][ldvt1];
+ * keys n1 + j from k2 / vt2 likewise.  q f16 [nq][ldq] at column h*128.
+ * Requires nq >= 1, heads >= 1, n1, n2 >= 0, n1 + n2 >= 1, all leading
+ * dimensions % 8 == 0, ldvt >= round_up(n_src, 64) with finite values in
+ * the padding columns.  vis (device, uint32 [nq]) should be non-decreasing
+ * in [1, n1 + n2]; other values never read out of bounds but give an
+ * undefined (finite) result. */
+int qi21_op_flash(int nq, int heads, const void* q, int ldq, const void* k1, int ldk1, const void* vt1,
+                  int ldvt1, int n1, const void* k2, int ldk2, const void* vt2, int ldvt2, int n2,
+                  const uint32_t* vis, void* out, int ldo, float oscale, void* stream);
+
+/* Row op ([WG] qi_rowop; [QI] gated_add, norm_mod) over rows of width h:
+ * mode bit 0: x += mods[g_off + c] * y  (gate already tanh-ed)
+ * mode bit 1: xn f16 = (LN(x) * (1 + mods[s_off + c])) * oscale
+ * Requires rows >= 1, h % 4 == 0, 4 <= h <= 8192, g_off, s_off % 4 == 0. */
+int qi21_op_rowop(int rows, int h, int mode, float* x, const float* y, void* xn, const float* mods, int g_off,
+                  int s_off, float eps, float oscale, void* stream);
+
+/* Per-head RMSNorm(norm_q | norm_k) then interleaved-pair RoPE on the q
+ * (column 0) and k (column heads*128) parts of panel f16 [rows][ldp], in
+ * place ([QI] qk_norm_rope).  cos, sin: [rows][64].  kdst != NULL: the
+ * normalised k goes to kdst f16 [rows][ldk] instead.  Requires ldp >=
+ * 2*heads*128, ldp % 2 == 0. */
+int qi21_op_qkrope(int rows, int heads, void* panel, int ldp, const float* norm_q, const float* norm_k,
+                   const float* cos, const float* sin, float eps, void* kdst, int ldk, void* stream);
+
+/* x [rows][h] = tok [rows][64] img_in^T, img_in [h][64] ([QI] embed_image).
+ * Requires h % 64 == 0. */
+int qi21_op_embed(int rows, int h, const float* tok, const float* img_in, float* x, void* stream);
+
+/* out [rows][64] = (LN(x) * fs) proj_out^T with proj_out_t = proj_out^T
+ * [h][64] ([QI] step_cpu final layer); *flag |= 1 if any output is not
+ * finite.  Requires h % 256 == 0. */
+int qi21_op_final(int rows, int h, const float* x, const float* fs, const float* proj_out_t, float eps,
+                  float* out, int* flag, void* stream);
+
+/* mods_dev [4h] = [s1 | tanh g1 | s2 | tanh g2] ([WG] mods_dev). */
+int qi21_op_mods(int h, const float* mods, float* mods_dev, void* stream);
+
+/* f16 weight plane: source row r of src [rows][cols] (QI21_F32 / BF16 /
+ * F16) goes to dst row (r / group) * gstride + goff + r % group. */
+int qi21_op_plane(int src_dtype, const void* src, int rows, int cols, void* dst, int group, int gstride,
+                  int goff, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QI21_OPS_H */

@@ -1,0 +1,256 @@
+"""Per-kernel parity of the HIP library against the CPU oracle (needs a GPU).
+
+Every kernel is called through the C ABI (``qi21_op_*``) on seeded inputs
+and compared element by element with the oracle's function on the same
+values: f32 outputs to 1e-5 relative L2, f16 outputs (one rounding to
+binary16) to 2e-3.  Sizes span several tiles with a ragged tail.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import inputs
+from oracle import qi21_oracle as O
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+F16_TOL = 2e-3
+F32_TOL = 1e-5
+
+
+def Q():
+    from diffusion_transformer_denoiser_qi21_amd import qi21
+    return qi21
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def f16_host(seed, tid, shape, sigma):
+    """seeded values rounded to f16, as float32 numpy (exactly what the GPU sees)"""
+    return inputs.host_array(seed, tid, shape, sigma).astype(np.float16).astype(np.float32)
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return t if dtype is None else t.to(dtype)
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ───────────────────────────── GEMM ─────────────────────────────
+
+@pytest.mark.parametrize("tile", [-1, 0, 1])
+@pytest.mark.parametrize("M", [1, 77, 300, 1040])
+@pytest.mark.parametrize("epi", ["f16", "f32", "swiglu", "qkv"])
+def test_gemm_epilogues(epi, M, tile):
+    q = Q()
+    N, K = 768, 512
+    A = f16_host(1, 1, (M, K), 1.0)
+    W = f16_host(1, 2, (N, K), 0.05)
+    oscale, inscale = 0.25, 4.0
+    dA, dW = dev(A, torch.float16), dev(W, torch.float16)
+    if epi in ("f16", "f32"):
+        out = torch.zeros(M, N, device="cuda", dtype=torch.float16 if epi == "f16" else torch.float32)
+        q.qi21_op_gemm(q.QI21_EPI_F16 if epi == "f16" else q.QI21_EPI_F32, M, N, K, dA, K, dW, out, N,
+                       oscale=oscale, tile=tile)
+        sync()
+        want = O.lin(A, W) * np.float32(oscale)
+        assert rel(out.float().cpu().numpy(), want) < (F16_TOL if epi == "f16" else F32_TOL)
+    elif epi == "swiglu":
+        G, U = W[: N // 2], W[N // 2:]
+        w13 = torch.empty(N, K, device="cuda", dtype=torch.float16)
+        q.qi21_op_plane(q.QI21_F32, dev(G), N // 2, K, w13, 32, 64, 0)
+        q.qi21_op_plane(q.QI21_F32, dev(U), N // 2, K, w13, 32, 64, 32)
+        out = torch.zeros(M, N // 2, device="cuda", dtype=torch.float16)
+        q.qi21_op_gemm(q.QI21_EPI_SWIGLU, M, N, K, dA, K, w13, out, N // 2, oscale=oscale, inscale=inscale, tile=tile)
+        sync()
+        g = O.lin(A, G) * np.float32(inscale)
+        u = O.lin(A, U) * np.float32(inscale)
+        want = O.silu(g) * u * np.float32(oscale)
+        assert rel(out.float().cpu().numpy(), want) < F16_TOL
+    else:
+        h = N // 3
+        ld2 = ((M + 63) // 64) * 64
+        out = torch.zeros(M, 2 * h, device="cuda", dtype=torch.float16)
+        vt = torch.zeros(h, ld2, device="cuda", dtype=torch.float16)
+        q.qi21_op_gemm(q.QI21_EPI_QKV, M, N, K, dA, K, dW, out, 2 * h, vt, ld2, oscale=oscale, tile=tile)
+        sync()
+        want = O.lin(A, W) * np.float32(oscale)
+        assert rel(out.float().cpu().numpy(), want[:, :2 * h]) < F16_TOL
+        vtn = vt.float().cpu().numpy()
+        assert rel(vtn[:, :M], want[:, 2 * h:].T) < F16_TOL
+        assert np.all(vtn[:, M:] == 0)  # nothing written past the rows
+
+
+def test_gemm_plane_conversion_exact():
+    q = Q()
+    rows, cols = 96, 128
+    src = inputs.host_array(3, 4, (rows, cols), 0.02, bf16=True)
+    bf = dev(src).to(torch.bfloat16)
+    dst = torch.zeros(2 * rows, cols, device="cuda", dtype=torch.float16)
+    q.qi21_op_plane(q.QI21_BF16, bf, rows, cols, dst, 32, 64, 32)
+    sync()
+    d = dst.cpu()
+    for r in range(rows):
+        assert torch.equal(d[(r // 32) * 64 + 32 + r % 32], bf[r].cpu().half())
+    assert torch.all(d.view(-1, 64, cols)[:, :32] == 0)
+
+
+# ───────────────────────────── flash attention ─────────────────────────────
+
+def _vt(v, ld):
+    """V [n][H] -> V^T [H][ld], zero padding"""
+    out = np.zeros((v.shape[1], ld), np.float32)
+    out[:, :v.shape[0]] = v.T
+    return out
+
+
+@pytest.mark.parametrize("case", ["step", "step_tiny", "step_tiles", "prefill_cond", "prefill_text", "one_key"])
+def test_flash_parity(case):
+    q = Q()
+    heads, hd = 2, 128
+    H = heads * hd
+    vis = None
+    if case == "step":
+        nq, n1, n2 = 300, 18, 300
+    elif case == "step_tiny":
+        nq, n1, n2 = 1, 1, 1
+    elif case == "step_tiles":
+        nq, n1, n2 = 257, 130, 257
+    elif case == "one_key":
+        nq, n1, n2 = 70, 1, 0
+    else:
+        segs = [("text", 22), ("image", 12, 12), ("image", 4, 4)] if case == "prefill_cond" else \
+            [("text", 150), ("image", 2, 2)]
+        lay = O.Layout(segs)
+        vis = O.prefix_visibility(lay)
+        nq, n1, n2 = lay.prefix_len, lay.prefix_len, 0
+    m = n1 + n2
+    qa = f16_host(5, 1, (nq, H), 1.0)
+    k = f16_host(5, 2, (m, H), 1.0)
+    v = f16_host(5, 3, (m, H), 1.0)
+    oscale = 2.0
+    ld1 = ((max(n1, 1) + 63) // 64) * 64
+    ld2 = ((max(n2, 1) + 63) // 64) * 64 + 64
+    k2panel = np.zeros((max(n2, 1), 2 * H), np.float32)  # k at column H of a wider panel
+    k2panel[:n2, H:] = k[n1:]
+    dq = dev(qa, torch.float16)
+    dk1 = dev(k[:n1] if n1 else np.zeros((1, H), np.float32), torch.float16)
+    dvt1 = dev(_vt(v[:n1], ld1), torch.float16)
+    dk2 = dev(k2panel, torch.float16)
+    dvt2 = dev(_vt(v[n1:], ld2), torch.float16)
+    dvis = dev(vis.astype(np.int32)) if vis is not None else None
+    out = torch.zeros(nq, H, device="cuda", dtype=torch.float16)
+    q.qi21_op_flash(nq, heads, dq, H, dk1, H, dvt1, ld1, n1,
+                    dk2.data_ptr() + H * 2 if n2 else None, 2 * H, dvt2 if n2 else None, ld2, n2,
+                    dvis, out, H, oscale)
+    sync()
+    visible = vis if vis is not None else np.full(nq, m, np.int64)
+    want = O.attention(qa, k, v, visible, heads, hd) * np.float32(oscale)
+    assert rel(out.float().cpu().numpy(), want) < F16_TOL
+
+
+# ───────────────────────────── row kernels ─────────────────────────────
+
+@pytest.mark.parametrize("h", [256, 4096])
+@pytest.mark.parametrize("rows", [1, 37, 300])
+@pytest.mark.parametrize("mode", [1, 2, 3])
+def test_rowop_modes(mode, rows, h):
+    q = Q()
+    x = inputs.host_array(7, 1, (rows, h), 1.0)
+    y = inputs.host_array(7, 2, (rows, h), 0.5)
+    mods = inputs.host_array(7, 3, (4 * h,), 0.1)
+    g_off, s_off, eps, oscale = 3 * h, 2 * h, 1e-6, 0.25
+    dx, dy, dm = dev(x), dev(y), dev(mods)
+    xn = torch.zeros(rows, h, device="cuda", dtype=torch.float16)
+    q.qi21_op_rowop(rows, h, mode, dx, dy, xn, dm, g_off, s_off, eps, oscale)
+    sync()
+    xe = O.gated_add(x, y, mods[g_off:g_off + h]) if mode & 1 else x
+    assert rel(dx.cpu().numpy(), xe) < 1e-6
+    if mode & 2:
+        want = O.norm_mod(xe, mods[s_off:s_off + h], eps) * np.float32(oscale)
+        assert rel(xn.float().cpu().numpy(), want) < F16_TOL
+    else:
+        assert torch.all(xn == 0)
+
+
+@pytest.mark.parametrize("kdst", [False, True])
+@pytest.mark.parametrize("rows", [5, 300])
+def test_qkrope(rows, kdst):
+    q = Q()
+    heads, hd = 2, 128
+    H = heads * hd
+    ldp = 2 * H + 64
+    lay = O.Layout([("text", 7), ("image", 17, 18)])
+    pos = lay.positions()[:rows]
+    c, s = O.rope_tables(pos)
+    panel = f16_host(9, 1, (rows, ldp), 1.0 / 16)  # stored values carry 2^-4
+    wq = inputs.host_array(9, 2, (hd,), 0.02, mean=1.0)
+    wk = inputs.host_array(9, 3, (hd,), 0.02, mean=1.0)
+    eps = 1e-6 * 2.0 ** -8
+    dp = dev(panel, torch.float16)
+    kd = torch.zeros(rows, H, device="cuda", dtype=torch.float16) if kdst else None
+    q.qi21_op_qkrope(rows, heads, dp, ldp, dev(wq), dev(wk), dev(c), dev(s), eps, kd, H)
+    sync()
+    got = dp.float().cpu().numpy()
+    wq_ = O.qk_norm_rope(panel[:, :H], wq, c, s, heads, hd, eps)
+    wk_ = O.qk_norm_rope(panel[:, H:2 * H], wk, c, s, heads, hd, eps)
+    assert rel(got[:, :H], wq_) < F16_TOL
+    if kdst:
+        assert rel(kd.float().cpu().numpy(), wk_) < F16_TOL
+        assert np.array_equal(got[:, H:], panel[:, H:])  # k untouched in the panel
+    else:
+        assert rel(got[:, H:2 * H], wk_) < F16_TOL
+        assert np.array_equal(got[:, 2 * H:], panel[:, 2 * H:])
+
+
+@pytest.mark.parametrize("h", [256, 4096])
+@pytest.mark.parametrize("rows", [1, 100, 300])
+def test_embed(rows, h):
+    q = Q()
+    tok = inputs.host_array(11, 1, (rows, 64), 1.0)
+    w = inputs.host_array(11, 2, (h, 64), 0.02)
+    x = torch.zeros(rows, h, device="cuda")
+    q.qi21_op_embed(rows, h, dev(tok), dev(w), x)
+    sync()
+    assert rel(x.cpu().numpy(), O.embed_image(tok, w)) < F32_TOL
+
+
+@pytest.mark.parametrize("h", [256, 4096])
+@pytest.mark.parametrize("rows", [1, 17, 300])
+def test_final_and_nonfinite_flag(rows, h):
+    q = Q()
+    x = inputs.host_array(12, 1, (rows, h), 1.0) * np.float32(3.0) + np.float32(0.5)
+    fs = 1.0 + inputs.host_array(12, 2, (h,), 0.1)
+    po = inputs.host_array(12, 3, (64, h), 0.02)
+    out = torch.zeros(rows, 64, device="cuda")
+    flag = torch.zeros(1, device="cuda", dtype=torch.int32)
+    q.qi21_op_final(rows, h, dev(x), dev(fs), dev(np.ascontiguousarray(po.T)), 1e-6, out, flag)
+    sync()
+    want = O.lin(O.layer_norm(x, 1e-6) * fs, po)  # LN(x) * (1 + final_scale), fs = 1 + final_scale
+    assert rel(out.cpu().numpy(), want) < F32_TOL
+    assert int(flag.item()) == 0
+    x[rows // 2, 3] = np.inf
+    q.qi21_op_final(rows, h, dev(x), dev(fs), dev(np.ascontiguousarray(po.T)), 1e-6, out, flag)
+    sync()
+    assert int(flag.item()) == 1
+
+
+def test_mods_gate_tanh_pages_example():
+    q = Q()
+    h = 3
+    m = (np.arange(12, dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+    out = torch.zeros(12, device="cuda")
+    q.qi21_op_mods(h, dev(m), out)
+    sync()
+    d = out.cpu().numpy()
+    assert np.array_equal(d[:3], m[:3]) and np.array_equal(d[6:9], m[6:9])
+    assert abs(d[4] - math.tanh(0.4)) < 1e-6 and abs(d[11] - math.tanh(1.1)) < 1e-6

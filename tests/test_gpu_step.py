@@ -1,0 +1,185 @@
+"""End-to-end parity of qi21_prefill + qi21_step against the CPU oracle (needs a GPU).
+
+The tiny model (2 blocks, dim 256, f32 weights that the library rounds to
+f16 planes) runs through the C ABI on seeded inputs; its velocity must be
+within 1e-3 relative L2 of the oracle's prefill + step on the same inputs.
+Also: a condition-image prefix (block-causal mask over several key tiles),
+a CFG pair of unequal prefixes as one batched step, determinism, the
+range-guard settings, the non-finite refusal, and the error paths.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import bench
+from inputs import CONFIGS
+from inputs.configs import TINY_MODEL, Workload
+from oracle import SynthModel, workload_inputs
+from oracle import qi21_oracle as O
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+V_TOL = 1e-3
+
+
+def Q():
+    from diffusion_transformer_denoiser_qi21_amd import qi21
+    return qi21
+
+
+def rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+@pytest.fixture(scope="module")
+def tiny_gpu():
+    m = bench.build_model(TINY_MODEL)
+    yield m
+    Q().qi21_model_destroy(m)
+
+
+@pytest.fixture(scope="module")
+def tiny_cpu():
+    return SynthModel(TINY_MODEL)
+
+
+def oracle_v(model, w, prefix=0):
+    d = workload_inputs(w, prefix)
+    lay = O.Layout(w.layout(prefix))
+    pre = O.prefill(model, d["x_prefix"], lay)
+    return O.step(model, pre, d["tok"], d["mods"], d["final_scale"])
+
+
+def gpu_v(m, w, key=1, prefix=0):
+    d = bench.workload_tensors(w, prefix)
+    bench.prefill(m, key, d)
+    out = torch.full((d["n"], 64), 7.0, device="cuda")
+    Q().qi21_step(m, key, d["tok"], d["mods"], d["fs"], out)
+    return out.cpu().numpy(), d
+
+
+def test_tiny_prefill_step_parity(tiny_gpu, tiny_cpu):
+    w = CONFIGS["tiny"]
+    v, _ = gpu_v(tiny_gpu, w)
+    want = oracle_v(tiny_cpu, w)
+    err = rel(v, want)
+    print(f"tiny v rel L2 {err:.3e}")
+    assert err < V_TOL
+
+
+@pytest.mark.parametrize("segs,target", [
+    ((("text", 22), ("image", 12, 12)), (16, 16)),
+    ((("text", 5), ("image", 3, 4), ("text", 2), ("image", 9, 9)), (7, 9)),
+    ((("text", 1),), (1, 1)),
+])
+def test_condition_prefix_parity(tiny_gpu, tiny_cpu, segs, target):
+    w = Workload("t", TINY_MODEL, 33, target, (tuple(segs),))
+    v, _ = gpu_v(tiny_gpu, w, key=2)
+    want = oracle_v(tiny_cpu, w)
+    err = rel(v, want)
+    print(f"{segs} -> {target}: v rel L2 {err:.3e}")
+    assert err < V_TOL
+
+
+def test_cfg_pair_unequal_prefixes_batched(tiny_gpu, tiny_cpu):
+    w = Workload("cfg", TINY_MODEL, 44, (10, 12), ((("text", 18),), (("text", 9), ("image", 2, 3))),
+                 prefix_seeds=(44, 45))
+    q = Q()
+    ds = [bench.workload_tensors(w, p) for p in range(2)]
+    for p in range(2):
+        bench.prefill(tiny_gpu, 10 + p, ds[p])
+    outs = [torch.zeros(d["n"], 64, device="cuda") for d in ds]
+    q.qi21_step_batch(tiny_gpu, [10, 11], [d["tok"] for d in ds], ds[0]["mods"], ds[0]["fs"], outs)
+    for p in range(2):
+        # the oracle's prefix p, with the step inputs of the shared workload
+        d = workload_inputs(w, p)
+        lay = O.Layout(w.layout(p))
+        pre = O.prefill(tiny_cpu, d["x_prefix"], lay)
+        want = O.step(tiny_cpu, pre, d["tok"], d["mods"], d["final_scale"])
+        err = rel(outs[p].cpu().numpy(), want)
+        print(f"cfg prefix {p}: v rel L2 {err:.3e}")
+        assert err < V_TOL
+    # batched == one program at a time
+    single = torch.zeros_like(outs[1])
+    q.qi21_step(tiny_gpu, 11, ds[1]["tok"], ds[1]["mods"], ds[1]["fs"], single)
+    assert rel(single.cpu().numpy(), outs[1].cpu().numpy()) < 1e-6
+
+
+def test_step_is_deterministic(tiny_gpu):
+    w = CONFIGS["tiny"]
+    d = bench.workload_tensors(w)
+    bench.prefill(tiny_gpu, 3, d)
+    a = torch.zeros(d["n"], 64, device="cuda")
+    b = torch.zeros(d["n"], 64, device="cuda")
+    Q().qi21_step(tiny_gpu, 3, d["tok"], d["mods"], d["fs"], a)
+    Q().qi21_step(tiny_gpu, 3, d["tok"], d["mods"], d["fs"], b)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("shifts", [(0, 0, 0, 0, 0), (4, 8, 2, 4, 10)])
+def test_range_guard_settings(tiny_cpu, shifts):
+    q = Q()
+    opt = q.qi21_default_options()
+    opt.shift_attn, opt.shift_qkv, opt.shift_ao, opt.shift_ffn, opt.shift_hid = shifts
+    m = bench.build_model(TINY_MODEL, opt)
+    try:
+        w = CONFIGS["tiny"]
+        v, _ = gpu_v(m, w)
+        assert rel(v, oracle_v(tiny_cpu, w)) < V_TOL
+    finally:
+        q.qi21_model_destroy(m)
+
+
+def test_nonfinite_velocity_is_refused_and_out_untouched(tiny_gpu):
+    q = Q()
+    w = CONFIGS["tiny"]
+    d = bench.workload_tensors(w)
+    bench.prefill(tiny_gpu, 4, d)
+    mods = d["mods"].clone()
+    mods[:TINY_MODEL.dim] = 1e5  # (1 + s1) * LN(x) overflows the f16 attention input
+    out = torch.full((d["n"], 64), 7.0, device="cuda")
+    with pytest.raises(q.Qi21Error) as e:
+        q.qi21_step(tiny_gpu, 4, d["tok"], mods, d["fs"], out)
+    assert e.value.code == q.QI21_ENONFINITE
+    assert torch.all(out == 7.0)
+    # the model still works afterwards
+    q.qi21_step(tiny_gpu, 4, d["tok"], d["mods"], d["fs"], out)
+    assert torch.all(torch.isfinite(out))
+
+
+def test_error_paths_and_eviction(tiny_gpu):
+    q = Q()
+    w = CONFIGS["tiny"]
+    d = bench.workload_tensors(w)
+    out = torch.zeros(d["n"], 64, device="cuda")
+    with pytest.raises(q.Qi21Error) as e:
+        q.qi21_step(tiny_gpu, 999, d["tok"], d["mods"], d["fs"], out)
+    assert e.value.code == q.QI21_ENOKEY
+    for bad in (d["vis"].flip(0), torch.zeros_like(d["vis"]), d["vis"] + 1):
+        dd = dict(d, vis=bad.contiguous())
+        with pytest.raises(q.Qi21Error) as e:
+            bench.prefill(tiny_gpu, 5, dd)
+        assert e.value.code == q.QI21_EINVAL
+    # max_programs = 2: a third prefix evicts the oldest
+    for k in (21, 22, 23):
+        bench.prefill(tiny_gpu, k, d)
+    with pytest.raises(q.Qi21Error) as e:
+        q.qi21_step(tiny_gpu, 21, d["tok"], d["mods"], d["fs"], out)
+    assert e.value.code == q.QI21_ENOKEY
+    q.qi21_step(tiny_gpu, 23, d["tok"], d["mods"], d["fs"], out)
+    q.qi21_release_key(tiny_gpu, 23)
+    with pytest.raises(q.Qi21Error) as e:
+        q.qi21_release_key(tiny_gpu, 23)
+    assert e.value.code == q.QI21_ENOKEY
+    # a model whose blocks were never set refuses to prefill
+    spec = dataclasses.replace(TINY_MODEL, layers=1)
+    m2 = q.qi21_model_create(bench.geom_of(spec), None, 1, torch.zeros(256, 64, device="cuda"),
+                             torch.zeros(64, 256, device="cuda"))
+    try:
+        with pytest.raises(q.Qi21Error) as e:
+            bench.prefill(m2, 1, d)
+        assert e.value.code == q.QI21_EINVAL
+    finally:
+        q.qi21_model_destroy(m2)
