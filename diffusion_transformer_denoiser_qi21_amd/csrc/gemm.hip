@@ -6,17 +6,29 @@
 // which is exactly the layout the MFMA A and B fragments want, so no
 // operand is ever transposed.
 //
-// Block tile BM x BN x 64, 256 threads = 4 waves in a 2 x 2 arrangement,
-// each wave owning a (BM/2) x (BN/2) sub-tile of 32 x 32 MFMA tiles.  The
-// A and B tiles go global -> registers -> LDS, double-buffered so the next
-// k-tile's global loads are in flight while the current one is multiplied;
-// one barrier per k-tile.  LDS rows are 64 halves (8 chunks of 16 bytes);
-// chunk c of row r is stored at slot c ^ (r & 7), so the 16-byte fragment
-// reads of 8 consecutive rows hit 8 different bank groups.
+// Two kernels share the epilogues:
 //
-// Epilogues (fused, from the registers): f16 store, f32 store, the SwiGLU
-// of the interleaved gate/up plane, and the qkv split that writes the v
-// columns transposed (V^T, the layout the attention kernel streams).
+// * gemm_dma_kernel, the large-M kernel: block tile 256 x 256 x 32, 4 waves
+//   (2 x 2) of 128 x 128 each, 4 LDS stages filled by buffer loads that
+//   write straight into LDS (no register staging), so three k-tiles are in
+//   flight while one is multiplied.  A-rows past M come back as zeros from
+//   the buffer resource's range check.  The main loop is branch-free and its
+//   schedule is pinned: each MFMA is paired with one LDS fragment read or one
+//   LDS-bound buffer load, so the single wave of each SIMD keeps its matrix
+//   pipe fed.  One barrier per k-tile, placed after this tile's fragment
+//   reads, when the next tile is resident and this stage may be refilled.
+// * gemm_rs_kernel, the small-M / narrow-N kernel: block tile BM x BN x 64,
+//   global -> registers -> LDS, double-buffered.
+//
+// LDS rows hold the k-slice of one A or W row in 16-byte chunks, XOR-
+// swizzled so the 16-byte fragment reads of 16 consecutive rows fall on 16
+// different bank groups.  Blocks are dealt to the 8 XCDs round-robin; the
+// launch remaps them so each XCD works on a compact 4-row group of tiles
+// (A and W slices shared in that XCD's L2).
+//
+// Epilogues (fused, from the accumulators): f16 store, f32 store, the
+// SwiGLU of the interleaved gate/up plane, and the qkv split that writes
+// the v columns transposed (V^T, the layout the attention kernel streams).
 // Range-guard factors are powers of two folded into oscale / inscale.
 #include "qi21_internal.h"
 
@@ -27,114 +39,46 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+namespace {
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
-  constexpr int BK = 64;
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int AL = BM * 8 / 256;  // 16-byte chunks per thread, A tile
-  constexpr int BL = BN * 8 / 256;  // 16-byte chunks per thread, B tile
-  extern __shared__ u32x4 smem[];   // [2][(BM + BN) * 8]
+// s_waitcnt immediate (gfx9 encoding): vmcnt 6 bits at [3:0] and [15:14],
+// expcnt [6:4], lgkmcnt [11:8]; the maximum of a field means "no wait".
+constexpr int wait_imm(int vm, int lgkm) {
+  return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm & 0xF) << 8);
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_n = a.N / BN;
+// Block -> (tile row, tile column).  Hardware deals block b to XCD b % 8;
+// blocks of one XCD get a contiguous run of tiles, enumerated in groups of
+// 4 tile rows so that the ~32 tiles an XCD runs at once span 4 A panels and
+// 8 W panels instead of 1 and 32.
+__device__ __forceinline__ void tile_of(int M, int N, int BM, int BN, int& tm, int& tn) {
+  const int tiles_n = N / BN, tiles_m = (M + BM - 1) / BM;
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
-  // Blocks are dealt to the 8 XCDs round-robin (block b -> XCD b % 8); remap
-  // so that each XCD works on a contiguous run of tiles, which share their
-  // A row panel in that XCD's L2.
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int tm = bid / tiles_n, tn = bid - tm * tiles_n;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int K = a.K;
-
-  const u32x4* ag[AL];
-  const u32x4* bg[BL];
-  int aslot[AL], bslot[BL];
-#pragma unroll
-  for (int i = 0; i < AL; ++i) {
-    int q = tid + 256 * i, r = q >> 3, c = q & 7;
-    int row = min(m0 + r, a.M - 1);
-    ag[i] = reinterpret_cast<const u32x4*>(a.A + (size_t)row * a.lda + c * 8);
-    aslot[i] = swz(r, c);
+  constexpr int G = 4;
+  if (tiles_m % G == 0) {
+    const int per = G * tiles_n;
+    const int g = bid / per, w = bid - g * per;
+    tm = g * G + w % G;
+    tn = w / G;
+  } else {
+    tm = bid / tiles_n;
+    tn = bid - tm * tiles_n;
   }
-#pragma unroll
-  for (int i = 0; i < BL; ++i) {
-    int q = tid + 256 * i, r = q >> 3, c = q & 7;
-    bg[i] = reinterpret_cast<const u32x4*>(a.W + (size_t)(n0 + r) * K + c * 8);
-    bslot[i] = BM * 8 + swz(r, c);
-  }
+}
 
-  floatx16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  u32x4 ra[AL], rb[BL];
-#pragma unroll
-  for (int i = 0; i < AL; ++i) ra[i] = ag[i][0];
-#pragma unroll
-  for (int i = 0; i < BL; ++i) rb[i] = bg[i][0];
-#pragma unroll
-  for (int i = 0; i < AL; ++i) smem[aslot[i]] = ra[i];
-#pragma unroll
-  for (int i = 0; i < BL; ++i) smem[bslot[i]] = rb[i];
-  __syncthreads();
-
-  const int KT = K / BK;
-  const int arow0 = wm * WM + (lane & 31), brow0 = wn * WN + (lane & 31);
-  const int hsel = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const u32x4* s = smem + cur * (BM + BN) * 8;
-    if (kt + 1 < KT) {
-      const int off = (kt + 1) * (BK / 8);  // in 16-byte units along K
-#pragma unroll
-      for (int i = 0; i < AL; ++i) ra[i] = ag[i][off];
-#pragma unroll
-      for (int i = 0; i < BL; ++i) rb[i] = bg[i][off];
-    }
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + hsel;
-      half8 af[TM], bf[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        u32x4 v = s[swz(arow0 + i * 32, c)];
-        af[i] = __builtin_bit_cast(half8, v);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        u32x4 v = s[BM * 8 + swz(brow0 + j * 32, c)];
-        bf[j] = __builtin_bit_cast(half8, v);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) {
-      u32x4* d = smem + (cur ^ 1) * (BM + BN) * 8;
-#pragma unroll
-      for (int i = 0; i < AL; ++i) d[aslot[i]] = ra[i];
-#pragma unroll
-      for (int i = 0; i < BL; ++i) d[bslot[i]] = rb[i];
-    }
-    __syncthreads();
-  }
-
-  // ── epilogue ── lane (col l%32) holds rows 8g + 4*(l/32) + e of each tile
-  const int rbase = m0 + wm * WM + 4 * hsel;
-  const int cbase = n0 + wn * WN + (lane & 31);
+// Epilogue of one wave's TM x TN grid of 32 x 32 accumulator tiles whose
+// top-left output element is (r0, c0).  MFMA 32x32 accumulator layout: lane
+// l holds column l % 32 and rows 8g + 4(l / 32) + e (g, e = 0..3) in
+// register 4g + e.
+template <int EPI, int TM, int TN>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, floatx16 (&acc)[TM][TN], int r0, int c0, int lane) {
+  const int hsel = lane >> 5, l32 = lane & 31;
+  const int rbase = r0 + 4 * hsel;
+  const int cbase = c0 + l32;
   if constexpr (EPI == EPI_F32 || EPI == EPI_F16) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -154,7 +98,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         }
   } else if constexpr (EPI == EPI_SWIGLU) {
     // tiles (2p, 2p+1) of a wave hold matching gate / up columns
-    const int hc0 = (n0 + wn * WN) / 2 + (lane & 31);
+    const int hc0 = c0 / 2 + l32;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -165,13 +109,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
           if (row < a.M) {
             const float g = acc[i][2 * p][e] * a.inscale;
             const float u = acc[i][2 * p + 1][e] * a.inscale;
-            reinterpret_cast<f16*>(a.out)[(size_t)row * a.ldo + hc0 + p * 32] =
-                (f16)(silu_f(g) * u * a.oscale);
+            reinterpret_cast<f16*>(a.out)[(size_t)row * a.ldo + hc0 + p * 32] = (f16)(silu_f(g) * u * a.oscale);
           }
         }
-  } else {  // EPI_QKV
+  } else {  // EPI_QKV: q | k to the panel, v transposed to out2
     const int two_h = (a.N / 3) * 2;
-    if (n0 < two_h) {
+    if (c0 < two_h) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -180,8 +123,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
           for (int e = 0; e < 16; ++e) {
             const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
             if (row < a.M)
-              reinterpret_cast<f16*>(a.out)[(size_t)row * a.ldo + cbase + j * 32] =
-                  (f16)(acc[i][j][e] * a.oscale);
+              reinterpret_cast<f16*>(a.out)[(size_t)row * a.ldo + cbase + j * 32] = (f16)(acc[i][j][e] * a.oscale);
           }
     } else {
 #pragma unroll
@@ -208,31 +150,267 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   }
 }
 
+// ───────────────────── large-M kernel: 256 x 256 x 32, LDS-direct loads ─────────────────────
+constexpr int DBM = 256, DBN = 256, DBK = 32, DNS = 4;
+constexpr int DSTAGE = (DBM + DBN) * DBK;  // halves per stage
+// LDS rows of DBK = 32 halves: 4 chunks of 16 bytes; chunk c of row r sits
+// at slot c ^ ((r >> 2) & 3).
+__device__ __forceinline__ int dswz(int r) { return (r >> 2) & 3; }
+
+}  // namespace
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) f16 smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_of(a.M, a.N, DBM, DBN, tm, tn);
+  const int m0 = tm * DBM, n0 = tn * DBN;
+  const int K = a.K;
+  // Buffer resources over this block's A rows and W rows; reads of A rows
+  // at or past M fall outside the resource's range and return zeros.
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.A + (size_t)m0 * a.lda), 0, (min(a.M - m0, DBM) - 1) * a.lda * 2 + K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (size_t)n0 * K), 0, DBN * K * 2, 0x00020000);
+  // Load i (0..3) of wave w fills LDS chunk positions (4i + w) * 64 + lane
+  // of the A region and of the W region: row p / 4, slot p % 4.
+  int voa[4], vob[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = (i * 4 + wave) * 64 + lane;
+    const int r = p >> 2, c = (p & 3) ^ dswz(r);
+    voa[i] = (r * a.lda + 8 * c) * 2;
+    vob[i] = (r * K + 8 * c) * 2;
+  }
+  const int KT = K / DBK;
+  // k-tile t -> stage t % DNS; past the last tile the last one is fetched
+  // again into a stage no one reads any more, which keeps the loop free of
+  // branches and the count of loads in flight constant.
+  auto issue = [&](int t) {
+    const int soff = min(t, KT - 1) * DBK * 2;
+    f16* base = smem + (t % DNS) * DSTAGE + wave * 64 * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, base + i * 4 * 64 * 8, 16, voa[i], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, base + DBM * DBK + i * 4 * 64 * 8, 16, vob[i], soff, 0, 0);
+    }
+  };
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  const int hsel = lane >> 5, l32 = lane & 31;
+  half8 af[2][4], bf[2][4];
+  auto frags = [&](int t, int kk, int b) {
+    const f16* sa = smem + (t % DNS) * DSTAGE;
+    const f16* sb = sa + DBM * DBK;
+    const int c = kk * 2 + hsel;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + l32;
+      af[b][i] = *reinterpret_cast<const half8*>(sa + (r * 4 + (c ^ dswz(r))) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn * 128 + j * 32 + l32;
+      bf[b][j] = *reinterpret_cast<const half8*>(sb + (r * 4 + (c ^ dswz(r))) * 8);
+    }
+  };
+  auto mma = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[b][i], bf[b][j], acc[i][j], 0, 0, 0);
+  };
+#pragma unroll
+  for (int t = 0; t < DNS; ++t) issue(t);
+  __builtin_amdgcn_s_waitcnt(wait_imm((DNS - 1) * 8, 15));  // tile 0 landed
+  __builtin_amdgcn_s_barrier();
+  frags(0, 0, 0);
+  for (int t = 0; t < KT - 1; ++t) {
+    frags(t, 1, 1);
+    mma(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // this wave's reads of stage t % DNS are done and tile t + 1 has landed;
+    // after the barrier every wave is past both, so the stage can be refilled
+    __builtin_amdgcn_s_waitcnt(wait_imm((DNS - 2) * 8, 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(t + DNS);
+    frags(t + 1, 0, 0);
+    mma(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load -> LDS
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  frags(KT - 1, 1, 1);
+  mma(0);
+  mma(1);
+  __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));  // no LDS-bound load outlives the block
+  epilogue<EPI, 4, 4>(a, acc, m0 + wm * 128, n0 + wn * 128, lane);
+}
+
+// ───────────────────── small-M kernel: register-staged, BM x BN x 64 ─────────────────────
+namespace {
+__device__ __forceinline__ int swz8(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+}  // namespace
+
 template <int BM, int BN, int EPI>
-static hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
+__global__ __launch_bounds__(256) void gemm_rs_kernel(GemmArgs a) {
+  constexpr int BK = 64;
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int AL = BM * 8 / 256;  // 16-byte chunks per thread, A tile
+  constexpr int BL = BN * 8 / 256;  // 16-byte chunks per thread, B tile
+  extern __shared__ u32x4 smem4[];  // [2][(BM + BN) * 8]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_of(a.M, a.N, BM, BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int K = a.K;
+
+  const u32x4* ag[AL];
+  const u32x4* bg[BL];
+  int aslot[AL], bslot[BL];
+#pragma unroll
+  for (int i = 0; i < AL; ++i) {
+    int q = tid + 256 * i, r = q >> 3, c = q & 7;
+    int row = min(m0 + r, a.M - 1);
+    ag[i] = reinterpret_cast<const u32x4*>(a.A + (size_t)row * a.lda + c * 8);
+    aslot[i] = swz8(r, c);
+  }
+#pragma unroll
+  for (int i = 0; i < BL; ++i) {
+    int q = tid + 256 * i, r = q >> 3, c = q & 7;
+    bg[i] = reinterpret_cast<const u32x4*>(a.W + (size_t)(n0 + r) * K + c * 8);
+    bslot[i] = BM * 8 + swz8(r, c);
+  }
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  u32x4 ra[AL], rb[BL];
+#pragma unroll
+  for (int i = 0; i < AL; ++i) ra[i] = ag[i][0];
+#pragma unroll
+  for (int i = 0; i < BL; ++i) rb[i] = bg[i][0];
+#pragma unroll
+  for (int i = 0; i < AL; ++i) smem4[aslot[i]] = ra[i];
+#pragma unroll
+  for (int i = 0; i < BL; ++i) smem4[bslot[i]] = rb[i];
+  __syncthreads();
+
+  const int KT = K / BK;
+  const int arow0 = wm * WM + (lane & 31), brow0 = wn * WN + (lane & 31);
+  const int hsel = lane >> 5;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    const u32x4* s = smem4 + cur * (BM + BN) * 8;
+    if (kt + 1 < KT) {
+      const int off = (kt + 1) * (BK / 8);  // in 16-byte units along K
+#pragma unroll
+      for (int i = 0; i < AL; ++i) ra[i] = ag[i][off];
+#pragma unroll
+      for (int i = 0; i < BL; ++i) rb[i] = bg[i][off];
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int c = kk * 2 + hsel;
+      half8 af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = __builtin_bit_cast(half8, s[swz8(arow0 + i * 32, c)]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bf[j] = __builtin_bit_cast(half8, s[BM * 8 + swz8(brow0 + j * 32, c)]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) {
+      u32x4* d = smem4 + (cur ^ 1) * (BM + BN) * 8;
+#pragma unroll
+      for (int i = 0; i < AL; ++i) d[aslot[i]] = ra[i];
+#pragma unroll
+      for (int i = 0; i < BL; ++i) d[bslot[i]] = rb[i];
+    }
+    __syncthreads();
+  }
+  epilogue<EPI, TM, TN>(a, acc, m0 + wm * WM, n0 + wn * WN, lane);
+}
+
+namespace {
+
+template <int EPI>
+hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
+  constexpr size_t lds = (size_t)DNS * DSTAGE * 2;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<EPI>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int blocks = ((a.M + DBM - 1) / DBM) * (a.N / DBN);
+  hipLaunchKernelGGL((gemm_dma_kernel<EPI>), dim3(blocks), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int EPI>
+hipError_t launch_rs(const GemmArgs& a, hipStream_t s) {
   constexpr size_t lds = 2 * (BM + BN) * 8 * sizeof(u32x4);
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<BM, BN, EPI>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_rs_kernel<BM, BN, EPI>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int blocks = ((a.M + BM - 1) / BM) * (a.N / BN);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI>), dim3(blocks), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, EPI>), dim3(blocks), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
-int gemm_pick_tile(int M, int N, int K) {
-  (void)K;
-  if (N % 256 == 0 && M >= 2048) return 0;
-  return 1;
+template <int EPI>
+hipError_t launch_epi(const GemmArgs& a, int tile, hipStream_t s) {
+  if (tile == 0) return launch_dma<EPI>(a, s);
+  return launch_rs<128, 128, EPI>(a, s);
 }
 
-template <int EPI>
-static hipError_t launch_epi(const GemmArgs& a, int tile, hipStream_t s) {
-  if (tile == 0) return launch_tile<256, 256, EPI>(a, s);
-  return launch_tile<128, 128, EPI>(a, s);
+}  // namespace
+
+int gemm_pick_tile(int M, int N, int K) {
+  (void)K;
+  if (N % 256 == 0 && M >= 1536) return 0;
+  return 1;
 }
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s) {
