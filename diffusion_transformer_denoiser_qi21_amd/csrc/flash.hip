@@ -16,11 +16,18 @@
 // are lane-local; the two lanes that share a query (l and l ^ 32) exchange
 // their maxima once per key tile and their sums once at the end.
 //
-// Block: 4 waves x 32 queries; key tile 64.  K tile [64][128] and V^T tile
-// [128][64] live in LDS, double-buffered (global -> registers -> LDS, next
-// tile in flight during the current one's MFMAs).  V arrives transposed
-// from HBM (the qkv GEMM epilogue writes V^T), so both tiles load with
-// 16-byte coalesced reads.
+// Block: 4 waves x 32 queries; key tile 64.  The K tile [64][128] and the
+// V^T tile [128][64] of each step are fetched by buffer loads that write
+// straight into LDS (two stages: the next tile is in flight while the
+// current one is multiplied); keys past a source's end read as zeros and
+// are masked.  At most 256 registers per lane, so two blocks share a CU and
+// one block's softmax overlaps the other's MFMAs.
+//
+// Softmax: exp2 with log2(e)/sqrt(128) folded into one FMA, the running
+// maximum updated lazily -- the O^T rescale runs only when some query of
+// the wave sees its maximum grow by more than 2^8 (a wave-uniform branch),
+// so P = 2^(s - m) stays below 2^8 and exact in f16; row sums by v_dot2 on
+// the f16 P that also feeds the P V product.
 #include "qi21_internal.h"
 
 namespace qi21 {
@@ -32,18 +39,35 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 namespace {
-constexpr int BQ = 128;       // queries per block
-constexpr int BKV = 64;       // keys per tile
-constexpr int VT_LD = 17;     // V^T LDS row: 16 units of 8 bytes + 1 pad unit
+constexpr int BQ = 128;   // queries per block
+constexpr int BKV = 64;   // keys per tile
+constexpr int TILE_H = BKV * 128;       // halves in the K tile (and in the V^T tile)
+constexpr int STAGE_H = 2 * TILE_H;     // K tile then V^T tile
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float THR = 8.0f;             // lazy-rescale threshold, log2 units
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// K tile rows: 256 bytes = 16 chunks; chunk c of key row j at slot c ^ (j & 15).
+// V^T tile rows: 128 bytes = 8 chunks; chunk c of dim row d at slot c ^ ((d >> 1) & 7).
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 }  // namespace
 
 template <bool VIS>
-__global__ __launch_bounds__(256) void flash_kernel(FlashArgs a) {
-  __shared__ u32x4 sk[2][BKV * 16];
-  __shared__ u32x2 svt[2][128 * VT_LD];
+__global__ __launch_bounds__(256, 2) void flash_kernel(FlashArgs a) {
+  __shared__ __attribute__((aligned(16))) f16 sm[2 * STAGE_H];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hs = lane >> 5, l32 = lane & 31;
   const int head = blockIdx.y;
   const int q0 = blockIdx.x * BQ;
@@ -52,7 +76,7 @@ __global__ __launch_bounds__(256) void flash_kernel(FlashArgs a) {
   const int qrow = min(myq, a.nq - 1);
   const int ntot = a.n1 + a.n2;
 
-  // Q fragments: dims 16c + 8*hs .. +8 of this lane's query
+  // Q fragments (B operand of S^T = K Q^T): dims 16c + 8*hs .. +8 of this lane's query
   half8 qf[8];
   {
     const f16* qp = a.q + (size_t)qrow * a.ldq + head * 128 + 8 * hs;
@@ -68,34 +92,61 @@ __global__ __launch_bounds__(256) void flash_kernel(FlashArgs a) {
   const int t2 = kmax > a.n1 ? (min(a.n2, kmax - a.n1) + BKV - 1) / BKV : 0;
   const int T = t1 + t2;
 
-  u32x4 rk[4], rv[4];
-  auto load_tile = [&](int t) {
+  // buffer resources of the two sources (this head's columns); K rows past
+  // the source's end fall outside the range and read as zeros
+  __amdgpu_buffer_rsrc_t kr[2], vr[2];
+  int ldk[2], ldv[2];
+  {
+    const f16* kb[2] = {a.k1, a.k2};
+    const f16* vb[2] = {a.vt1, a.vt2};
+    const int ns[2] = {a.n1, a.n2};
+    ldk[0] = a.ldk1;
+    ldk[1] = a.ldk2;
+    ldv[0] = a.ldvt1;
+    ldv[1] = a.ldvt2;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int n = max(ns[s], 1);
+      kr[s] = __builtin_amdgcn_make_buffer_rsrc((void*)(kb[s] + head * 128), 0, (n - 1) * ldk[s] * 2 + 256,
+                                                0x00020000);
+      vr[s] = __builtin_amdgcn_make_buffer_rsrc((void*)(vb[s] + (size_t)head * 128 * ldv[s]), 0, 128 * ldv[s] * 2,
+                                                0x00020000);
+    }
+  }
+  // Load i (0..3) of wave w fills 16-byte LDS positions (4i + w) * 64 + lane
+  // of the K tile (key p / 16, slot p % 16) and of the V^T tile (dim p / 8,
+  // slot p % 8).
+  int kvo[2][4], vvo[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = (i * 4 + wave) * 64 + lane;
+    const int key = p >> 4, ck = (p & 15) ^ (key & 15);
+    const int d = p >> 3, cv = (p & 7) ^ vswz(d);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      kvo[s][i] = key * ldk[s] * 2 + ck * 16;
+      vvo[s][i] = d * ldv[s] * 2 + cv * 16;
+    }
+  }
+  // The key offset of a tile goes into the per-lane offset, which the
+  // buffer range check covers, so keys past a source's end read as zeros
+  // (V^T columns past the end are in range: the leading dimension covers
+  // whole 64-key tiles).
+  auto issue = [&](int t, int stage) {
     const bool s1 = t < t1;
     const int j0 = (s1 ? t : t - t1) * BKV;
-    const int ns = s1 ? a.n1 : a.n2;
-    const f16* kb = s1 ? a.k1 : a.k2;
-    const int ldk = s1 ? a.ldk1 : a.ldk2;
-    const f16* vb = s1 ? a.vt1 : a.vt2;
-    const int ldv = s1 ? a.ldvt1 : a.ldvt2;
+    const int kadd = j0 * (s1 ? ldk[0] : ldk[1]) * 2;
+    const int sv = __builtin_amdgcn_readfirstlane(j0 * 2);
+    f16* base = sm + stage * STAGE_H + wave * 64 * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i;
-      const int key = q >> 4, c = q & 15;
-      const int row = min(j0 + key, ns - 1);
-      rk[i] = *reinterpret_cast<const u32x4*>(kb + (size_t)row * ldk + head * 128 + 8 * c);
-      const int d = q >> 3, cv = q & 7;
-      rv[i] = *reinterpret_cast<const u32x4*>(vb + (size_t)(head * 128 + d) * ldv + j0 + 8 * cv);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i;
-      const int key = q >> 4, c = q & 15;
-      sk[buf][key * 16 + (c ^ (key & 15))] = rk[i];
-      const int d = q >> 3, cv = q & 7;
-      svt[buf][d * VT_LD + 2 * cv] = u32x2{rv[i][0], rv[i][1]};
-      svt[buf][d * VT_LD + 2 * cv + 1] = u32x2{rv[i][2], rv[i][3]};
+      if (s1) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr[0], base + i * 4 * 64 * 8, 16, kvo[0][i] + kadd, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr[0], base + TILE_H + i * 4 * 64 * 8, 16, vvo[0][i], sv, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr[1], base + i * 4 * 64 * 8, 16, kvo[1][i] + kadd, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr[1], base + TILE_H + i * 4 * 64 * 8, 16, vvo[1][i], sv, 0, 0);
+      }
     }
   };
 
@@ -104,17 +155,21 @@ __global__ __launch_bounds__(256) void flash_kernel(FlashArgs a) {
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.0f;
-  float mrun = -INFINITY, lsum = 0.0f;
+  float mused = -INFINITY, lsum = 0.0f;
   const float c2 = LOG2E * 0.08838834764831845f;  // log2(e) / sqrt(128)
+  const float thr_raw = THR / c2;
+  const half2v ones = half2v{(f16)1.0f, (f16)1.0f};
 
-  if (T > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  if (T > 0) issue(0, 0);
   for (int t = 0; t < T; ++t) {
     const int cur = t & 1;
-    if (t + 1 < T) load_tile(t + 1);
+    // tile t resident; every wave is done with tile t - 1, whose stage
+    // receives tile t + 1
+    __builtin_amdgcn_s_waitcnt(0x7 << 4 | 0xF << 8);  // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    if (t + 1 < T) issue(t + 1, cur ^ 1);
+    const f16* sk = sm + cur * STAGE_H;
+    const f16* sv = sk + TILE_H;
 
     // S^T = K Q^T : two 32-key sub-tiles
     floatx16 s[2];
@@ -127,8 +182,8 @@ __global__ __launch_bounds__(256) void flash_kernel(FlashArgs a) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int key = st * 32 + l32;
-        const u32x4 kv = sk[cur][key * 16 + ((2 * c + hs) ^ (key & 15))];
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, kv), qf[c], s[st], 0, 0, 0);
+        const half8 kv = *reinterpret_cast<const half8*>(sk + key * 128 + (((2 * c + hs) ^ (key & 15)) * 8));
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv, qf[c], s[st], 0, 0, 0);
       }
     }
 
@@ -146,56 +201,57 @@ __global__ __launch_bounds__(256) void flash_kernel(FlashArgs a) {
           if (kk >= cnt || gbase + kk >= lim) s[st][e] = -INFINITY;
         }
     }
-    float mx = s[0][0];
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[0][e], s[0][e + 1]));
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[st][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrun, mx);
-    const float msafe = mnew == -INFINITY ? 0.0f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f((mrun - msafe) * c2);
-    const float mc = msafe * c2;
-    mrun = mnew;
-    float ps = 0.0f;
+    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[1][e], s[1][e + 1]));
+    mx = pair_max(mx);
+    if (__any(mx > mused + thr_raw)) {  // wave-uniform: rescale O^T and the sum
+      const float mnew = fmaxf(mused, mx);
+      const float alpha = __builtin_amdgcn_exp2f((mused - mnew) * c2);
+      mused = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+    }
+    const float mc = mused == -INFINITY ? 0.0f : mused * c2;
     half8 pf[2][2];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * u + j], c2, -mc));
-          ps += p;
-          pf[st][u][j] = (f16)p;
+        for (int j = 0; j < 8; j += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * u + j], c2, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * u + j + 1], c2, -mc));
+          const half2v ph = half2v{(f16)p0, (f16)p1};
+          pf[st][u][j] = ph[0];
+          pf[st][u][j + 1] = ph[1];
+          lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
         }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T : the lane's 8 keys of a k-step sit in chunks 4st+2u
+    // and 4st+2u+1 of its dim row, half hs of each
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int unit = 8 * st + 4 * u + hs;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const int row = (32 * d + l32) * VT_LD;
-          const u32x2 lo = svt[cur][row + unit];
-          const u32x2 hi = svt[cur][row + unit + 2];
-          const u32x4 vv = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, vv), pf[st][u], o[d], 0, 0, 0);
+          const int row = 32 * d + l32;
+          const f16* vr0 = sv + row * 64 + hs * 4;
+          const half4 lo = *reinterpret_cast<const half4*>(vr0 + (((4 * st + 2 * u) ^ vswz(row)) * 8));
+          const half4 hi = *reinterpret_cast<const half4*>(vr0 + (((4 * st + 2 * u + 1) ^ vswz(row)) * 8));
+          const half8 vv = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, pf[st][u], o[d], 0, 0, 0);
         }
       }
-
-    if (t + 1 < T) store_tile(cur ^ 1);
-    __syncthreads();
   }
 
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = pair_sum(lsum);
   const float inv = ltot > 0.0f ? a.oscale / ltot : 0.0f;
   if (live) {
     f16* op = a.out + (size_t)myq * a.ldo + head * 128 + 4 * hs;
