@@ -23,6 +23,11 @@
 // are masked.  At most 256 registers per lane, so two blocks share a CU and
 // one block's softmax overlaps the other's MFMAs.
 //
+// V^T rows hold their keys permuted inside each group of 16 (bits 2 and 3
+// of the key index swapped; the qkv GEMM epilogue writes them so), which
+// puts the 8 keys one lane contributes to a P V k-step in one contiguous
+// 16-byte chunk: one conflict-free 16-byte LDS read per fragment.
+//
 // Softmax: exp2 with log2(e)/sqrt(128) folded into one FMA, the running
 // maximum updated lazily -- the O^T rescale runs only when some query of
 // the wave sees its maximum grow by more than 2^8 (a wave-uniform branch),
@@ -115,38 +120,32 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(FlashArgs a) {
   }
   // Load i (0..3) of wave w fills 16-byte LDS positions (4i + w) * 64 + lane
   // of the K tile (key p / 16, slot p % 16) and of the V^T tile (dim p / 8,
-  // slot p % 8).
-  int kvo[2][4], vvo[2][4];
+  // slot p % 8).  The key offset of a tile goes into the per-lane offset,
+  // which the buffer range check covers, so keys past a source's end read
+  // as zeros (V^T columns past the end are in range: the leading dimension
+  // covers whole 64-key tiles).
+  int lkey[4], lck[4], ldim[4], lcv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = (i * 4 + wave) * 64 + lane;
-    const int key = p >> 4, ck = (p & 15) ^ (key & 15);
-    const int d = p >> 3, cv = (p & 7) ^ vswz(d);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      kvo[s][i] = key * ldk[s] * 2 + ck * 16;
-      vvo[s][i] = d * ldv[s] * 2 + cv * 16;
-    }
+    lkey[i] = p >> 4;
+    lck[i] = ((p & 15) ^ (lkey[i] & 15)) * 16;
+    ldim[i] = p >> 3;
+    lcv[i] = ((p & 7) ^ vswz(ldim[i])) * 16;
   }
-  // The key offset of a tile goes into the per-lane offset, which the
-  // buffer range check covers, so keys past a source's end read as zeros
-  // (V^T columns past the end are in range: the leading dimension covers
-  // whole 64-key tiles).
   auto issue = [&](int t, int stage) {
     const bool s1 = t < t1;
     const int j0 = (s1 ? t : t - t1) * BKV;
-    const int kadd = j0 * (s1 ? ldk[0] : ldk[1]) * 2;
+    const int lk2 = (s1 ? ldk[0] : ldk[1]) * 2, lv2 = (s1 ? ldv[0] : ldv[1]) * 2;
+    const __amdgpu_buffer_rsrc_t krs = s1 ? kr[0] : kr[1];
+    const __amdgpu_buffer_rsrc_t vrs = s1 ? vr[0] : vr[1];
     const int sv = __builtin_amdgcn_readfirstlane(j0 * 2);
     f16* base = sm + stage * STAGE_H + wave * 64 * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (s1) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr[0], base + i * 4 * 64 * 8, 16, kvo[0][i] + kadd, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr[0], base + TILE_H + i * 4 * 64 * 8, 16, vvo[0][i], sv, 0, 0);
-      } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr[1], base + i * 4 * 64 * 8, 16, kvo[1][i] + kadd, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr[1], base + TILE_H + i * 4 * 64 * 8, 16, vvo[1][i], sv, 0, 0);
-      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, base + i * 4 * 64 * 8, 16, (j0 + lkey[i]) * lk2 + lck[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, base + TILE_H + i * 4 * 64 * 8, 16, ldim[i] * lv2 + lcv[i], sv, 0,
+                                               0);
     }
   };
 
@@ -187,12 +186,13 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(FlashArgs a) {
       }
     }
 
-    // mask: keys past the source's end, or past vis[i]
+    // mask: keys past the source's end, or past vis[i] (tail tiles and the
+    // prefill only; a wave-uniform branch)
     const bool s1 = t < t1;
     const int j0 = (s1 ? t : t - t1) * BKV;
     const int cnt = min(BKV, (s1 ? a.n1 : a.n2) - j0);
     const int gbase = (s1 ? 0 : a.n1) + j0;
-    if (VIS || cnt < BKV) {
+    if (__builtin_amdgcn_readfirstlane((int)(VIS || cnt < BKV))) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -218,23 +218,26 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(FlashArgs a) {
         for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
     }
     const float mc = mused == -INFINITY ? 0.0f : mused * c2;
+    // P in f16, packed pairwise straight into the B operand registers
     half8 pf[2][2];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u) {
+        u32x4 pk;
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * u + j], c2, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * u + j + 1], c2, -mc));
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * u + 2 * j], c2, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * u + 2 * j + 1], c2, -mc));
           const half2v ph = half2v{(f16)p0, (f16)p1};
-          pf[st][u][j] = ph[0];
-          pf[st][u][j + 1] = ph[1];
           lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
+          pk[j] = __builtin_bit_cast(unsigned int, ph);
         }
+        pf[st][u] = __builtin_bit_cast(half8, pk);
+      }
 
-    // O^T += V^T P^T : the lane's 8 keys of a k-step sit in chunks 4st+2u
-    // and 4st+2u+1 of its dim row, half hs of each
+    // O^T += V^T P^T : the lane's 8 keys of k-step (st, u) are the 16-byte
+    // chunk 4st + 2u + hs of its dim row
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -242,10 +245,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(FlashArgs a) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const int row = 32 * d + l32;
-          const f16* vr0 = sv + row * 64 + hs * 4;
-          const half4 lo = *reinterpret_cast<const half4*>(vr0 + (((4 * st + 2 * u) ^ vswz(row)) * 8));
-          const half4 hi = *reinterpret_cast<const half4*>(vr0 + (((4 * st + 2 * u + 1) ^ vswz(row)) * 8));
-          const half8 vv = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const half8 vv = *reinterpret_cast<const half8*>(sv + row * 64 + (((4 * st + 2 * u + hs) ^ vswz(row)) * 8));
           o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, pf[st][u], o[d], 0, 0, 0);
         }
       }

@@ -70,6 +70,11 @@ __device__ __forceinline__ void tile_of(int M, int N, int BM, int BN, int& tm, i
   }
 }
 
+// Position of key (row) r in a V^T row: bits 2 and 3 of r swapped, which
+// keeps runs of 4 keys contiguous and gathers keys {4h..4h+3, 8+4h..8+4h+3}
+// of every 16 into one 16-byte chunk (the attention kernel's P V operand).
+__device__ __forceinline__ int vt_pos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
 // Epilogue of one wave's TM x TN grid of 32 x 32 accumulator tiles whose
 // top-left output element is (r0, c0).  MFMA 32x32 accumulator layout: lane
 // l holds column l % 32 and rows 8g + 4(l / 32) + e (g, e = 0..3) in
@@ -133,16 +138,17 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, floatx16 (&acc)[TM][
           f16* dst = a.out2 + (size_t)(cbase + j * 32 - two_h) * a.ld2;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int row = rbase + i * 32 + 8 * g;
+            const int row = rbase + i * 32 + 8 * g;  // a multiple of 4
+            const int pos = vt_pos(row);
             half4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = (f16)(acc[i][j][4 * g + e] * a.oscale);
             if (row + 3 < a.M) {
-              *reinterpret_cast<half4*>(dst + row) = v;
+              *reinterpret_cast<half4*>(dst + pos) = v;
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                if (row + e < a.M) dst[row + e] = v[e];
+                if (row + e < a.M) dst[pos + e] = v[e];
             }
           }
         }
@@ -159,22 +165,49 @@ __device__ __forceinline__ int dswz(int r) { return (r >> 2) & 3; }
 
 }  // namespace
 
+// Persistent over tiles: block b runs on XCD b % 8 and walks that XCD's
+// contiguous run of the grouped tile sequence, 32 blocks abreast.  The
+// next tile's first LDS stages are fetched while the current tile's
+// epilogue stores drain.
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) f16 smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  int tm, tn;
-  tile_of(a.M, a.N, DBM, DBN, tm, tn);
-  const int m0 = tm * DBM, n0 = tn * DBN;
+  const int hsel = lane >> 5, l32 = lane & 31;
   const int K = a.K;
-  // Buffer resources over this block's A rows and W rows; reads of A rows
-  // at or past M fall outside the resource's range and return zeros.
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.A + (size_t)m0 * a.lda), 0, (min(a.M - m0, DBM) - 1) * a.lda * 2 + K * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (size_t)n0 * K), 0, DBN * K * 2, 0x00020000);
+  const int KT = K / DBK;
+  const int tiles_n = a.N / DBN, tiles_m = (a.M + DBM - 1) / DBM;
+  const int ntiles = tiles_n * tiles_m;
+  // this block's run of the tile sequence
+  int seq0, seq_end, seq_step;
+  {
+    const int nblk = gridDim.x, b = blockIdx.x;
+    if (nblk < ntiles && (nblk & 7) == 0) {
+      const int per_xcd = nblk >> 3, x = b & 7, li = b >> 3;
+      const int chunk = (ntiles + 7) >> 3;
+      seq0 = x * chunk + li;
+      seq_end = min(ntiles, (x + 1) * chunk);
+      seq_step = per_xcd;
+    } else {
+      seq0 = b;
+      seq_end = b + 1;
+      seq_step = 1;
+    }
+  }
+  auto tile_rc = [&](int sq, int& tm, int& tn) {
+    constexpr int G = 4;
+    if (tiles_m % G == 0) {
+      const int per = G * tiles_n;
+      const int g = sq / per, w = sq - g * per;
+      tm = g * G + w % G;
+      tn = w / G;
+    } else {
+      tm = sq / tiles_n;
+      tn = sq - tm * tiles_n;
+    }
+  };
   // Load i (0..3) of wave w fills LDS chunk positions (4i + w) * 64 + lane
   // of the A region and of the W region: row p / 4, slot p % 4.
   int voa[4], vob[4];
@@ -185,11 +218,19 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs a) {
     voa[i] = (r * a.lda + 8 * c) * 2;
     vob[i] = (r * K + 8 * c) * 2;
   }
-  const int KT = K / DBK;
+  // Buffer resources over a tile's A rows and W rows; A rows at or past M
+  // fall outside the resource's range and return zeros.
+  auto rsrc_a = [&](int m0) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(a.A + (size_t)m0 * a.lda), 0,
+                                             (min(a.M - m0, DBM) - 1) * a.lda * 2 + K * 2, 0x00020000);
+  };
+  auto rsrc_b = [&](int n0) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (size_t)n0 * K), 0, DBN * K * 2, 0x00020000);
+  };
   // k-tile t -> stage t % DNS; past the last tile the last one is fetched
   // again into a stage no one reads any more, which keeps the loop free of
   // branches and the count of loads in flight constant.
-  auto issue = [&](int t) {
+  auto issue = [&](__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int t) {
     const int soff = min(t, KT - 1) * DBK * 2;
     f16* base = smem + (t % DNS) * DSTAGE + wave * 64 * 8;
 #pragma unroll
@@ -199,13 +240,6 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs a) {
     }
   };
   floatx16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  const int hsel = lane >> 5, l32 = lane & 31;
   half8 af[2][4], bf[2][4];
   auto frags = [&](int t, int kk, int b) {
     const f16* sa = smem + (t % DNS) * DSTAGE;
@@ -229,46 +263,78 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs a) {
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[b][i], bf[b][j], acc[i][j], 0, 0, 0);
   };
+
+  int tm, tn;
+  tile_rc(seq0, tm, tn);
 #pragma unroll
-  for (int t = 0; t < DNS; ++t) issue(t);
-  __builtin_amdgcn_s_waitcnt(wait_imm((DNS - 1) * 8, 15));  // tile 0 landed
-  __builtin_amdgcn_s_barrier();
-  frags(0, 0, 0);
-  for (int t = 0; t < KT - 1; ++t) {
-    frags(t, 1, 1);
-    mma(0);
+  for (int t = 0; t < DNS; ++t) issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), t);
+  for (int sq = seq0; sq < seq_end; sq += seq_step) {
+    const int m0 = tm * DBM, n0 = tn * DBN;
+    const __amdgpu_buffer_rsrc_t ra = rsrc_a(m0), rb = rsrc_b(n0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    // k-tile 0 landed.  After an epilogue its stores share the vector
+    // memory counter with these loads, so wait for all of them.
+    if (sq == seq0)
+      __builtin_amdgcn_s_waitcnt(wait_imm((DNS - 1) * 8, 15));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+    __builtin_amdgcn_s_barrier();
+    frags(0, 0, 0);
+    for (int t = 0; t < KT - 1; ++t) {
+      frags(t, 1, 1);
+      mma(0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // this wave's reads of stage t % DNS are done and k-tile t + 1 has
+      // landed; after the barrier every wave is past both, so the stage
+      // can be refilled
+      __builtin_amdgcn_s_waitcnt(wait_imm((DNS - 2) * 8, 0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ra, rb, t + DNS);
+      frags(t + 1, 0, 0);
+      mma(1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load -> LDS
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    frags(KT - 1, 1, 1);
+    mma(0);
+    // every wave's reads of every stage are done (the loads still in
+    // flight only refetch the last k-tile into stages no one reads): the
+    // next tile's first stages can be fetched under the epilogue
     __builtin_amdgcn_sched_barrier(0);
-    // this wave's reads of stage t % DNS are done and tile t + 1 has landed;
-    // after the barrier every wave is past both, so the stage can be refilled
-    __builtin_amdgcn_s_waitcnt(wait_imm((DNS - 2) * 8, 0));
+    __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(t + DNS);
-    frags(t + 1, 0, 0);
+    const int nsq = sq + seq_step;
+    if (nsq < seq_end) {
+      tile_rc(nsq, tm, tn);
+#pragma unroll
+      for (int t = 0; t < DNS; ++t) issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), t);
+    }
     mma(1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load -> LDS
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    epilogue<EPI, 4, 4>(a, acc, m0 + wm * 128, n0 + wn * 128, lane);
   }
-  frags(KT - 1, 1, 1);
-  mma(0);
-  mma(1);
   __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));  // no LDS-bound load outlives the block
-  epilogue<EPI, 4, 4>(a, acc, m0 + wm * 128, n0 + wn * 128, lane);
 }
 
 // ───────────────────── small-M kernel: register-staged, BM x BN x 64 ─────────────────────
@@ -379,7 +445,17 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int blocks = ((a.M + DBM - 1) / DBM) * (a.N / DBN);
+  const int tiles = ((a.M + DBM - 1) / DBM) * (a.N / DBN);
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+      cus = 256;
+    cus &= ~7;
+  }
+  // persistent: one block per CU walks several tiles; fewer tiles than CUs:
+  // one block per tile
+  const int blocks = tiles > cus ? cus : tiles;
   hipLaunchKernelGGL((gemm_dma_kernel<EPI>), dim3(blocks), dim3(256), lds, s, a);
   return hipGetLastError();
 }

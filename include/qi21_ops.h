@@ -28,7 +28,9 @@ enum { QI21_EPI_F16 = 0, QI21_EPI_F32 = 1, QI21_EPI_SWIGLU = 2, QI21_EPI_QKV = 3
  *           rows; out f16 [M][ldo], N/2 columns, = silu(g * inscale) *
  *           (u * inscale) * oscale   ([QI] block_cpu FFN)
  *   QKV:    columns [0, 2N/3) -> out f16 [M][ldo]; columns [2N/3, N) ->
- *           out2 f16 transposed: out2[(c - 2N/3) * ld2 + row]; both * oscale
+ *           out2 f16 transposed, out2[(c - 2N/3) * ld2 + vt_pos(row)], both
+ *           * oscale, where vt_pos swaps bits 2 and 3 of the row index (the
+ *           V^T key order the attention kernel reads, see qi21_op_flash)
  * Requires M >= 1, N % 128 == 0, K % 64 == 0, lda % 8 == 0, lda >= K,
  * ldo >= output columns, for QKV (N/3) % 128 == 0, ld2 % 4 == 0, ld2 >= M.
  * tile: -1 automatic, 0 = 256x256 (needs N % 256 == 0), 1 = 128x128. */
@@ -39,7 +41,9 @@ int qi21_op_gemm(int epi, int M, int N, int K, const void* A, int lda, const voi
  * out[i][h*128 + d] = oscale * sum_j softmax_j(q_i . k_j / sqrt(128)) v_j[d]
  * over keys j < min(n1 + n2, vis[i]) (vis == NULL: all keys).  Keys
  * j < n1 come from k1 [j][ldk1] (column h*128) and V^T vt1 [h*128+d][ldvt1];
- * keys n1 + j from k2 / vt2 likewise.  q f16 [nq][ldq] at column h*128.
+ * keys n1 + j from k2 / vt2 likewise.  In a V^T row, key j of a source sits
+ * at column vt_pos(j) = j with bits 2 and 3 swapped (a permutation inside
+ * each group of 16 keys, as the QKV epilogue of qi21_op_gemm writes it).  q f16 [nq][ldq] at column h*128.
  * Requires nq >= 1, heads >= 1, n1, n2 >= 0, n1 + n2 >= 1, all leading
  * dimensions % 8 == 0, ldvt >= round_up(n_src, 64) with finite values in
  * the padding columns.  vis (device, uint32 [nq]) should be non-decreasing
