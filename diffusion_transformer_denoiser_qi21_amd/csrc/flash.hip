@@ -74,8 +74,23 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(FlashArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hs = lane >> 5, l32 = lane & 31;
-  const int head = blockIdx.y;
-  const int q0 = blockIdx.x * BQ;
+  // Blocks are dealt to the 8 XCDs round-robin (block b -> XCD b % 8).  All
+  // query blocks of a head go to one XCD, so the head's K / V^T tiles are
+  // fetched into that XCD's L2 once and shared by its query blocks.
+  const int nqb = (a.nq + BQ - 1) / BQ;
+  int head, qb;
+  {
+    const int b = blockIdx.x;
+    if ((a.heads & 7) == 0) {
+      const int li = b >> 3;
+      head = (b & 7) + 8 * (li / nqb);
+      qb = li % nqb;
+    } else {
+      head = b / nqb;
+      qb = b % nqb;
+    }
+  }
+  const int q0 = qb * BQ;
   const int myq = q0 + wave * 32 + l32;
   const bool live = myq < a.nq;
   const int qrow = min(myq, a.nq - 1);
@@ -268,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(FlashArgs a) {
 }
 
 hipError_t launch_flash(const FlashArgs& a, hipStream_t s) {
-  dim3 grid((a.nq + BQ - 1) / BQ, a.heads);
+  dim3 grid(((a.nq + BQ - 1) / BQ) * a.heads);
   if (a.vis)
     hipLaunchKernelGGL(flash_kernel<true>, grid, dim3(256), 0, s, a);
   else
