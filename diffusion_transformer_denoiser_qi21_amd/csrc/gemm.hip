@@ -101,7 +101,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, floatx16 (&acc)[TM][
               reinterpret_cast<f16*>(a.out)[(size_t)row * a.ldo + col] = (f16)v;
           }
         }
-  } else if constexpr (EPI == EPI_SWIGLU) {
+  } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU2) {
     // tiles (2p, 2p+1) of a wave hold matching gate / up columns
     const int hc0 = c0 / 2 + l32;
 #pragma unroll
@@ -114,7 +114,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, floatx16 (&acc)[TM][
           if (row < a.M) {
             const float g = acc[i][2 * p][e] * a.inscale;
             const float u = acc[i][2 * p + 1][e] * a.inscale;
-            reinterpret_cast<f16*>(a.out)[(size_t)row * a.ldo + hc0 + p * 32] = (f16)(silu_f(g) * u * a.oscale);
+            const float h = silu_f(g) * u * a.oscale;
+            f16* o = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo + hc0 + p * 32;
+            const f16 hi = (f16)h;
+            o[0] = hi;
+            // the rounding error of hi is exact in f32 (h has 24 significant bits)
+            if constexpr (EPI == EPI_SWIGLU2) o[a.N / 2] = (f16)(h - (float)hi);
           }
         }
   } else {  // EPI_QKV: q | k to the panel, v transposed to out2
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs a) {
     const int p = (i * 4 + wave) * 64 + lane;
     const int r = p >> 2, c = (p & 3) ^ dswz(r);
     voa[i] = (r * a.lda + 8 * c) * 2;
-    vob[i] = (r * K + 8 * c) * 2;
+    vob[i] = (r * a.kw + 8 * c) * 2;
   }
   // Buffer resources over a tile's A rows and W rows; A rows at or past M
   // fall outside the resource's range and return zeros.
@@ -225,18 +230,22 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs a) {
                                              (min(a.M - m0, DBM) - 1) * a.lda * 2 + K * 2, 0x00020000);
   };
   auto rsrc_b = [&](int n0) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (size_t)n0 * K), 0, DBN * K * 2, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (size_t)n0 * a.kw), 0, DBN * a.kw * 2, 0x00020000);
   };
+  // W columns wrap every kw (K is kw or 2 kw)
+  const int KTW = a.kw / DBK;
   // k-tile t -> stage t % DNS; past the last tile the last one is fetched
   // again into a stage no one reads any more, which keeps the loop free of
   // branches and the count of loads in flight constant.
   auto issue = [&](__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int t) {
-    const int soff = min(t, KT - 1) * DBK * 2;
+    const int tt = min(t, KT - 1);
+    const int soff = tt * DBK * 2;
+    const int soffw = (tt >= KTW ? tt - KTW : tt) * DBK * 2;
     f16* base = smem + (t % DNS) * DSTAGE + wave * 64 * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, base + i * 4 * 64 * 8, 16, voa[i], soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, base + DBM * DBK + i * 4 * 64 * 8, 16, vob[i], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, base + DBM * DBK + i * 4 * 64 * 8, 16, vob[i], soffw, 0, 0);
     }
   };
   floatx16 acc[4][4];
@@ -371,7 +380,7 @@ __global__ __launch_bounds__(256) void gemm_rs_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < BL; ++i) {
     int q = tid + 256 * i, r = q >> 3, c = q & 7;
-    bg[i] = reinterpret_cast<const u32x4*>(a.W + (size_t)(n0 + r) * K + c * 8);
+    bg[i] = reinterpret_cast<const u32x4*>(a.W + (size_t)(n0 + r) * a.kw + c * 8);
     bslot[i] = BM * 8 + swz8(r, c);
   }
 
@@ -402,10 +411,11 @@ __global__ __launch_bounds__(256) void gemm_rs_kernel(GemmArgs a) {
     const u32x4* s = smem4 + cur * (BM + BN) * 8;
     if (kt + 1 < KT) {
       const int off = (kt + 1) * (BK / 8);  // in 16-byte units along K
+      const int offw = off >= a.kw / 8 ? off - a.kw / 8 : off;  // W wraps every kw (K is kw or 2 kw)
 #pragma unroll
       for (int i = 0; i < AL; ++i) ra[i] = ag[i][off];
 #pragma unroll
-      for (int i = 0; i < BL; ++i) rb[i] = bg[i][off];
+      for (int i = 0; i < BL; ++i) rb[i] = bg[i][offw];
     }
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
@@ -497,6 +507,7 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s) {
     case EPI_F32: return launch_epi<EPI_F32>(a, tile, s);
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, tile, s);
     case EPI_QKV: return launch_epi<EPI_QKV>(a, tile, s);
+    case EPI_SWIGLU2: return launch_epi<EPI_SWIGLU2>(a, tile, s);
   }
   return hipErrorInvalidValue;
 }

@@ -126,10 +126,11 @@ void dfree(qi21_model* m, void* p, size_t bytes) {
   m->bytes -= std::min(m->bytes, bytes ? bytes : (size_t)256);
 }
 
-size_t acts_bytes(const qi21_geom& g, int cap, size_t* parts) {
-  const size_t H = g.hidden, I = g.inter, c = cap;
-  const size_t p[9] = {c * H * 4, c * H * 2, c * 2 * H * 2, H * c * 2, c * H * 2, c * H * 4, c * I * 2, 4 * H * 4,
-                       c * 64 * 4};
+// pair: the FFN input (in xn) and the SwiGLU hidden are kept as f16 pairs
+size_t acts_bytes(const qi21_geom& g, bool pair, int cap, size_t* parts) {
+  const size_t H = g.hidden, I = g.inter, c = cap, f = pair ? 2 : 1;
+  const size_t p[9] = {c * H * 4, c * H * 2 * f, c * 2 * H * 2, H * c * 2, c * H * 2, c * H * 4, c * I * 2 * f,
+                       4 * H * 4, c * 64 * 4};
   size_t t = 0;
   for (int i = 0; i < 9; ++i) {
     if (parts) parts[i] = p[i];
@@ -140,7 +141,7 @@ size_t acts_bytes(const qi21_geom& g, int cap, size_t* parts) {
 
 void free_acts(qi21_model* m) {
   size_t parts[9];
-  acts_bytes(m->g, m->acts.cap, parts);
+  acts_bytes(m->g, m->o.ffn_pair != 0, m->acts.cap, parts);
   void* ptrs[9] = {m->acts.x, m->acts.xn, m->acts.panel, m->acts.vt, m->acts.att,
                    m->acts.y, m->acts.hid, m->acts.mods, m->acts.out};
   for (int i = 0; i < 9; ++i) dfree(m, ptrs[i], parts[i]);
@@ -154,14 +155,14 @@ int ensure_acts(qi21_model* m, int rows, hipStream_t s) {
   free_acts(m);
   const int cap = (int)round_up((size_t)rows, 256);
   size_t parts[9];
-  acts_bytes(m->g, cap, parts);
+  acts_bytes(m->g, m->o.ffn_pair != 0, cap, parts);
   void* p[9];
   for (int i = 0; i < 9; ++i) {
     p[i] = dalloc(m, parts[i]);
     if (!p[i]) {
       for (int j = 0; j < i; ++j) dfree(m, p[j], parts[j]);
       return fail(QI21_ENOMEM, "activations for %d rows (%.1f MB) did not fit", rows,
-                  acts_bytes(m->g, cap, nullptr) / 1e6);
+                  acts_bytes(m->g, m->o.ffn_pair != 0, cap, nullptr) / 1e6);
     }
     HIP_OK(qi21::launch_fill32(p[i], 0u, parts[i] / 4, s));
   }
@@ -265,6 +266,7 @@ qi21::GemmArgs gemm_args(int M, int N, int K, const f16* A, int lda, const f16* 
   a.A = A;
   a.lda = lda;
   a.W = W;
+  a.kw = K;
   a.out = out;
   a.ldo = ldo;
   a.out2 = out2;
@@ -351,19 +353,25 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
       Scope sc(m, C_O, s);
       HIP_OK(qi21::launch_gemm(qi21::EPI_F32, gemm_args(rows, H, H, a.att, H, m->wo[l], a.y, H, p2(gd.ao)), tile, s));
     }
+    // with ffn_pair the FFN input and the hidden are f16 (hi, lo) pairs in
+    // rows of 2H / 2I and both GEMMs run over K doubled, each W row twice
+    const int pf = m->o.ffn_pair ? 2 : 1;
     {
       Scope sc(m, C_ROW, s);
-      HIP_OK(qi21::launch_rowop(rows, H, 3, a.x, a.y, a.xn, a.mods, H, 2 * H, g.eps, p2(-gd.ffn), s));
+      HIP_OK(qi21::launch_rowop(rows, H, pf == 2 ? 7 : 3, a.x, a.y, a.xn, a.mods, H, 2 * H, g.eps, p2(-gd.ffn), s));
     }
     {
       Scope sc(m, C_W13, s);
-      HIP_OK(qi21::launch_gemm(qi21::EPI_SWIGLU,
-                               gemm_args(rows, 2 * I, H, a.xn, H, m->w13[l], a.hid, I, p2(-gd.hid), p2(gd.ffn)),
-                               tile, s));
+      qi21::GemmArgs ga = gemm_args(rows, 2 * I, pf * H, a.xn, pf * H, m->w13[l], a.hid, pf * I, p2(-gd.hid),
+                                    p2(gd.ffn));
+      ga.kw = H;
+      HIP_OK(qi21::launch_gemm(pf == 2 ? qi21::EPI_SWIGLU2 : qi21::EPI_SWIGLU, ga, tile, s));
     }
     {
       Scope sc(m, C_W2, s);
-      HIP_OK(qi21::launch_gemm(qi21::EPI_F32, gemm_args(rows, H, I, a.hid, I, m->w2[l], a.y, H, p2(gd.hid)), tile, s));
+      qi21::GemmArgs ga = gemm_args(rows, H, pf * I, a.hid, pf * I, m->w2[l], a.y, H, p2(gd.hid));
+      ga.kw = I;
+      HIP_OK(qi21::launch_gemm(qi21::EPI_F32, ga, tile, s));
     }
     {
       Scope sc(m, C_ROW, s);
@@ -401,6 +409,7 @@ void qi21_default_options(qi21_options* o) {
   o->max_programs = 2;
   o->profile = 0;
   o->gemm_tile = -1;
+  o->ffn_pair = 0;
 }
 
 size_t qi21_model_bytes(const qi21_model* m) { return m ? m->bytes : 0; }
@@ -450,6 +459,11 @@ int qi21_model_create(const qi21_geom* geom, const qi21_options* opt, int nblock
     return fail(QI21_EINVAL, "alloc and free hooks must be given together");
   }
   if (m->o.max_programs < 1) m->o.max_programs = 1;
+  if (m->o.ffn_pair != 0 && m->o.ffn_pair != 1) {
+    const int fp = m->o.ffn_pair;
+    delete m;
+    return fail(QI21_EINVAL, "ffn_pair %d (0 or 1)", fp);
+  }
   m->nb = nblocks;
   const size_t H = geom->hidden, I = geom->inter;
   m->wqkv.assign(nblocks, nullptr);
@@ -691,21 +705,38 @@ int qi21_profile_read(qi21_model* m, double* ms, int64_t* launches) {
 
 // ───────────────────────────── single-kernel entry points ─────────────────────────────
 
-int qi21_op_gemm(int epi, int M, int N, int K, const void* A, int lda, const void* W, void* out, int ldo, void* out2,
-                 int ld2, float oscale, float inscale, int tile, void* stream) {
-  g_err.clear();
-  if (epi < QI21_EPI_F16 || epi > QI21_EPI_QKV) return fail(QI21_EINVAL, "epilogue %d", epi);
-  if (M < 1 || N < 128 || K < 64 || N % 128 || K % 64 || lda % 8 || lda < K)
-    return fail(QI21_EINVAL, "gemm M %d N %d K %d lda %d (need N %% 128, K %% 64, lda %% 8, lda >= K)", M, N, K, lda);
+namespace {
+// shared checks of the two GEMM entry points; ka = the columns of A read
+int op_gemm(int epi, int M, int N, int K, int ka, const void* A, int lda, const void* W, void* out, int ldo,
+            void* out2, int ld2, float oscale, float inscale, int tile, void* stream) {
+  if (epi < QI21_EPI_F16 || epi > QI21_EPI_SWIGLU2) return fail(QI21_EINVAL, "epilogue %d", epi);
+  if (M < 1 || N < 128 || K < 64 || N % 128 || K % 64 || lda % 8 || lda < ka)
+    return fail(QI21_EINVAL, "gemm M %d N %d K %d lda %d (need N %% 128, K %% 64, lda %% 8, lda >= %d)", M, N, K, lda,
+                ka);
   if (!A || !W || !out) return fail(QI21_EINVAL, "gemm pointer is NULL");
   const int ocols = epi == QI21_EPI_SWIGLU ? N / 2 : epi == QI21_EPI_QKV ? 2 * N / 3 : N;
   if (ldo < ocols) return fail(QI21_EINVAL, "ldo %d < %d output columns", ldo, ocols);
   if (epi == QI21_EPI_QKV && ((N / 3) % 128 || N % 3 || !out2 || ld2 % 4 || ld2 < M))
     return fail(QI21_EINVAL, "qkv epilogue needs N/3 %% 128 == 0, out2, ld2 %% 4 == 0, ld2 >= M");
   if (tile < -1 || tile > 1 || (tile == 0 && N % 256)) return fail(QI21_EINVAL, "tile %d for N %d", tile, N);
-  qi21::GemmArgs a = gemm_args(M, N, K, (const f16*)A, lda, (const f16*)W, out, ldo, oscale, inscale, (f16*)out2, ld2);
+  qi21::GemmArgs a = gemm_args(M, N, ka, (const f16*)A, lda, (const f16*)W, out, ldo, oscale, inscale, (f16*)out2, ld2);
+  a.kw = K;
   HIP_OK(qi21::launch_gemm(epi, a, tile, (hipStream_t)stream));
   return QI21_OK;
+}
+}  // namespace
+
+int qi21_op_gemm(int epi, int M, int N, int K, const void* A, int lda, const void* W, void* out, int ldo, void* out2,
+                 int ld2, float oscale, float inscale, int tile, void* stream) {
+  g_err.clear();
+  return op_gemm(epi, M, N, K, K, A, lda, W, out, ldo, out2, ld2, oscale, inscale, tile, stream);
+}
+
+int qi21_op_gemm_pair(int epi, int M, int N, int K, const void* A, int lda, const void* W, void* out, int ldo,
+                      float oscale, float inscale, int tile, void* stream) {
+  g_err.clear();
+  if (epi == QI21_EPI_QKV) return fail(QI21_EINVAL, "the pair GEMM has no qkv epilogue");
+  return op_gemm(epi, M, N, K, 2 * K, A, lda, W, out, ldo, nullptr, 0, oscale, inscale, tile, stream);
 }
 
 int qi21_op_flash(int nq, int heads, const void* q, int ldq, const void* k1, int ldk1, const void* vt1, int ldvt1,
@@ -745,7 +776,7 @@ int qi21_op_flash(int nq, int heads, const void* q, int ldq, const void* k1, int
 int qi21_op_rowop(int rows, int h, int mode, float* x, const float* y, void* xn, const float* mods, int g_off,
                   int s_off, float eps, float oscale, void* stream) {
   g_err.clear();
-  if (rows < 1 || h < 4 || h % 4 || h > 8192 || mode < 1 || mode > 3 || g_off % 4 || s_off % 4 || g_off < 0 ||
+  if (rows < 1 || h < 4 || h % 4 || h > 8192 || mode < 1 || mode > 7 || mode == 4 || mode == 5 || g_off % 4 || s_off % 4 || g_off < 0 ||
       s_off < 0)
     return fail(QI21_EINVAL, "rowop rows %d h %d mode %d", rows, h, mode);
   if (!x || !mods || ((mode & 1) && !y) || ((mode & 2) && !xn)) return fail(QI21_EINVAL, "rowop pointer NULL");

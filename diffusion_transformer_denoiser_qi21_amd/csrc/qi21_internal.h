@@ -12,24 +12,29 @@ namespace qi21 {
 
 typedef _Float16 f16;
 
-enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
+enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 4 };
 
 // C = A * W^T over f16 operands with f32 accumulation.
-//   A: [M][lda] f16 (K contiguous), W: [N][K] f16 (K contiguous).
+//   A: [M][lda] f16 (K contiguous), W: [N][kw] f16 (kw contiguous); column
+//   k of A meets column k % kw of W, so with kw = K / 2 an A row holding
+//   [hi | lo] halves of a float operand is multiplied by W twice.
 //   EPI_F16:    out f16 [M][ldo] = acc * oscale
 //   EPI_F32:    out f32 [M][ldo] = acc * oscale
 //   EPI_SWIGLU: W is the interleaved gate/up plane (groups of 32 gate rows,
 //               then the 32 matching up rows); out f16 [M][ldo] with N/2
 //               columns = silu(g*inscale) * (u*inscale) * oscale
+//   EPI_SWIGLU2: as EPI_SWIGLU, the value h written as the pair
+//               out[r][c] = f16(h), out[r][N/2 + c] = f16(h - f16(h))
 //   EPI_QKV:    columns [0, 2H) -> out f16 [M][ldo] (q|k), columns [2H, 3H)
 //               -> out2 f16 transposed, out2[c - 2H][row] with leading
 //               dimension ld2 (V^T), both * oscale; H = N/3.
-// Assumes: N % 128 == 0, K % 64 == 0, M >= 1, 16-byte aligned rows
-// (lda, K multiples of 8), for EPI_QKV N/3 % 128 == 0 and ld2 >= M.
+// Assumes: N % 128 == 0, K % 64 == 0, kw % 64 == 0, K % kw == 0, M >= 1,
+// 16-byte aligned rows (lda a multiple of 8), for EPI_QKV N/3 % 128 == 0
+// and ld2 >= M.
 struct GemmArgs {
   int M, N, K;
   const f16* A; int lda;
-  const f16* W;
+  const f16* W; int kw;
   void* out; int ldo;
   f16* out2; int ld2;
   float oscale, inscale;
@@ -59,6 +64,8 @@ hipError_t launch_flash(const FlashArgs& a, hipStream_t s);
 // rowop over `rows` rows of width h (h % 4 == 0, h <= 8192):
 //   mode & 1: x += gate (.) y            (gate = mods + g_off, already tanh-ed)
 //   mode & 2: xn = f16(LN(x) * (1 + mods[s_off + c]) * oscale)
+//   mode & 4: (with & 2) xn is [rows][2h]: the value v as the pair
+//             xn[r][c] = f16(v), xn[r][h + c] = f16(v - f16(v))
 hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16* xn,
                         const float* mods, int g_off, int s_off, float eps, float oscale,
                         hipStream_t s);

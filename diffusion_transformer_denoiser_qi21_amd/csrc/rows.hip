@@ -70,14 +70,19 @@ __global__ __launch_bounds__(256) void rowop_kernel(int h, float* __restrict__ x
       q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
     }
   const float inv = rsqrtf(block_sum256(q, red) / (float)h + eps);
-  half4* xo = reinterpret_cast<half4*>(xn + (size_t)row * h);
+  half4* xo = reinterpret_cast<half4*>(xn + (size_t)row * ((MODE & 4) ? 2 * h : h));
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int c = t + 256 * j;
     if (c < nc) {
       const float4v s = reinterpret_cast<const float4v*>(mods + s_off)[c];
       const float4v r = (v[j] - mean) * inv * (1.0f + s) * oscale;
-      xo[c] = half4{(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
+      const half4 hi = half4{(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
+      xo[c] = hi;
+      if (MODE & 4) {  // rounding error of hi, exact in f32, as the second half
+        const float4v e = r - float4v{(float)hi[0], (float)hi[1], (float)hi[2], (float)hi[3]};
+        xo[nc + c] = half4{(f16)e[0], (f16)e[1], (f16)e[2], (f16)e[3]};
+      }
     }
   }
 }
@@ -89,6 +94,8 @@ hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16
     case 1: hipLaunchKernelGGL(rowop_kernel<1>, dim3(rows), dim3(256), 0, s, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
     case 2: hipLaunchKernelGGL(rowop_kernel<2>, dim3(rows), dim3(256), 0, s, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
     case 3: hipLaunchKernelGGL(rowop_kernel<3>, dim3(rows), dim3(256), 0, s, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
+    case 6: hipLaunchKernelGGL(rowop_kernel<6>, dim3(rows), dim3(256), 0, s, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
+    case 7: hipLaunchKernelGGL(rowop_kernel<7>, dim3(rows), dim3(256), 0, s, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libqi21.so")
 
 QI21_OK, QI21_EINVAL, QI21_EUNSUPPORTED, QI21_ENOMEM, QI21_ENOKEY, QI21_ENONFINITE, QI21_EDEVICE = range(7)
 QI21_F32, QI21_BF16, QI21_F16 = 0, 1, 2
-QI21_EPI_F16, QI21_EPI_F32, QI21_EPI_SWIGLU, QI21_EPI_QKV = 0, 1, 2, 3
+QI21_EPI_F16, QI21_EPI_F32, QI21_EPI_SWIGLU, QI21_EPI_QKV, QI21_EPI_SWIGLU2 = 0, 1, 2, 3, 4
 PROFILE_CLASSES = ("qkv", "qkrope", "flash", "o", "gate_up", "down", "rowop", "io")
 
 C = ctypes
@@ -43,7 +43,7 @@ FREE_FN = C.CFUNCTYPE(None, vp, vp)
 
 class qi21_options(C.Structure):
     _fields_ = [("shift_attn", i32), ("shift_qkv", i32), ("shift_ao", i32), ("shift_ffn", i32), ("shift_hid", i32),
-                ("max_programs", i32), ("profile", i32), ("gemm_tile", i32),
+                ("max_programs", i32), ("profile", i32), ("gemm_tile", i32), ("ffn_pair", i32),
                 ("alloc", ALLOC_FN), ("free", FREE_FN), ("alloc_ctx", vp)]
 
 
@@ -68,6 +68,8 @@ _SIGS = {
     "qi21_layout_tables": (C.c_int, [C.POINTER(qi21_seg), C.c_int, C.POINTER(i32), f32, vp, vp, vp, vp, vp, vp]),
     "qi21_op_gemm": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, C.c_int, f32, f32,
                                C.c_int, vp]),
+    "qi21_op_gemm_pair": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, f32, f32, C.c_int,
+                                    vp]),
     "qi21_op_flash": (C.c_int, [C.c_int, C.c_int, vp, C.c_int, vp, C.c_int, vp, C.c_int, C.c_int, vp, C.c_int, vp,
                                 C.c_int, C.c_int, vp, vp, C.c_int, f32, vp]),
     "qi21_op_rowop": (C.c_int, [C.c_int, C.c_int, C.c_int, vp, vp, vp, vp, C.c_int, C.c_int, f32, f32, vp]),
@@ -230,6 +232,11 @@ def qi21_layout_tables(segs, axes=(16, 56, 56), theta: float = 10000.0):
 def qi21_op_gemm(epi, M, N, K, A, lda, W, out, ldo, out2=None, ld2=0, oscale=1.0, inscale=1.0, tile=-1, stream=None):
     _check(lib().qi21_op_gemm(epi, M, N, K, _p(A), lda, _p(W), _p(out), ldo, _p(out2), ld2, oscale, inscale, tile,
                               _stream(stream)))
+
+
+def qi21_op_gemm_pair(epi, M, N, K, A, lda, W, out, ldo, oscale=1.0, inscale=1.0, tile=-1, stream=None):
+    _check(lib().qi21_op_gemm_pair(epi, M, N, K, _p(A), lda, _p(W), _p(out), ldo, oscale, inscale, tile,
+                                   _stream(stream)))
 
 
 def qi21_op_flash(nq, heads, q, ldq, k1, ldk1, vt1, ldvt1, n1, k2, ldk2, vt2, ldvt2, n2, vis, out, ldo, oscale=1.0,

@@ -67,12 +67,19 @@ typedef void (*qi21_free_fn)(void* ptr, void* ctx);
  * input (2), SwiGLU hidden (8).  max_programs: prefixes kept at once (2: a
  * positive and a negative prompt); a new key evicts the oldest.  profile:
  * bit mask of kernel classes (see qi21_profile_read) whose launches are
- * bracketed by HIP events on the launch stream; 0 = off. */
+ * bracketed by HIP events on the launch stream; 0 = off.
+ * ffn_pair (not on the pages, whose FFN sites are single f16): 1 keeps the
+ * FFN input and the SwiGLU hidden as f16 (hi, lo) pairs, hi = f16(v), lo =
+ * f16(v - hi), so their storage error falls from about 2^-12 to about 2^-23
+ * of the value (less where lo is subnormal); the gate/up and down GEMMs
+ * then run over twice their K, using each weight row for both halves, which
+ * is 1.75x the step's GEMM work.  0 (default) = single f16. */
 typedef struct {
   int32_t shift_attn, shift_qkv, shift_ao, shift_ffn, shift_hid;
   int32_t max_programs;
   int32_t profile;
   int32_t gemm_tile; /* -1 = per-shape choice; otherwise a fixed GEMM tile id */
+  int32_t ffn_pair;
   qi21_alloc_fn alloc;
   qi21_free_fn free;
   void* alloc_ctx;

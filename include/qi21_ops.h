@@ -18,7 +18,7 @@
 extern "C" {
 #endif
 
-enum { QI21_EPI_F16 = 0, QI21_EPI_F32 = 1, QI21_EPI_SWIGLU = 2, QI21_EPI_QKV = 3 };
+enum { QI21_EPI_F16 = 0, QI21_EPI_F32 = 1, QI21_EPI_SWIGLU = 2, QI21_EPI_QKV = 3, QI21_EPI_SWIGLU2 = 4 };
 
 /* out = A W^T ([QI] lin; the four projection sites of [WG] blocks):
  * A f16 [M][lda] (K contiguous), W f16 [N][K].  Epilogues:
@@ -31,11 +31,22 @@ enum { QI21_EPI_F16 = 0, QI21_EPI_F32 = 1, QI21_EPI_SWIGLU = 2, QI21_EPI_QKV = 3
  *           out2 f16 transposed, out2[(c - 2N/3) * ld2 + vt_pos(row)], both
  *           * oscale, where vt_pos swaps bits 2 and 3 of the row index (the
  *           V^T key order the attention kernel reads, see qi21_op_flash)
+ *   SWIGLU2: as SWIGLU, each hidden value h stored as the f16 pair
+ *           out[r][c] = f16(h), out[r][N/2 + c] = f16(h - f16(h)); ldo >= N
+ *           (the hidden of the ffn_pair option, qi21.h)
  * Requires M >= 1, N % 128 == 0, K % 64 == 0, lda % 8 == 0, lda >= K,
  * ldo >= output columns, for QKV (N/3) % 128 == 0, ld2 % 4 == 0, ld2 >= M.
  * tile: -1 automatic, 0 = 256x256 (needs N % 256 == 0), 1 = 128x128. */
 int qi21_op_gemm(int epi, int M, int N, int K, const void* A, int lda, const void* W, void* out, int ldo,
                  void* out2, int ld2, float oscale, float inscale, int tile, void* stream);
+
+/* The same product with A given as f16 pairs (the ffn_pair option of
+ * qi21.h): A f16 [M][lda], lda >= 2K, holds hi in columns [0, K) and lo in
+ * [K, 2K); out = (A_hi + A_lo) W^T, W f16 [N][K], accumulated in f32 over
+ * both halves (each W row is read for both).  Epilogues F16, F32, SWIGLU,
+ * SWIGLU2 with the requirements above (QKV: EINVAL). */
+int qi21_op_gemm_pair(int epi, int M, int N, int K, const void* A, int lda, const void* W, void* out, int ldo,
+                      float oscale, float inscale, int tile, void* stream);
 
 /* Attention, head_dim 128 ([QI] attention; [WG] qi_flash): per head h,
  * out[i][h*128 + d] = oscale * sum_j softmax_j(q_i . k_j / sqrt(128)) v_j[d]
@@ -56,7 +67,10 @@ int qi21_op_flash(int nq, int heads, const void* q, int ldq, const void* k1, int
 /* Row op ([WG] qi_rowop; [QI] gated_add, norm_mod) over rows of width h:
  * mode bit 0: x += mods[g_off + c] * y  (gate already tanh-ed)
  * mode bit 1: xn f16 = (LN(x) * (1 + mods[s_off + c])) * oscale
- * Requires rows >= 1, h % 4 == 0, 4 <= h <= 8192, g_off, s_off % 4 == 0. */
+ * mode bit 2 (with bit 1): xn is f16 [rows][2h] holding that value v as the
+ *   pair xn[r][c] = f16(v), xn[r][h + c] = f16(v - f16(v)) (ffn_pair, qi21.h)
+ * Requires rows >= 1, mode in {1, 2, 3, 6, 7}, h % 4 == 0, 4 <= h <= 8192,
+ * g_off, s_off % 4 == 0. */
 int qi21_op_rowop(int rows, int h, int mode, float* x, const float* y, void* xn, const float* mods, int g_off,
                   int s_off, float eps, float oscale, void* stream);
 

@@ -26,6 +26,14 @@ which bounds the float32 oracle's own rounding error.
 The oracle has no range guards (the device path's power-of-two scalings of
 its float16 sites are exact in exact arithmetic, [WG] module doc).
 
+``storage="f16"`` additionally rounds, to IEEE binary16, every activation
+the device design stores in float16 ([WG] module doc and ``Acts``: the
+attention input, the q|k|v panel, the normalised and rotated q and k, the
+unnormalised softmax weights P, the attention output, the FFN input and the
+SwiGLU hidden), keeping everything else as above.  It computes what the
+device design computes up to accumulation order, which separates the
+design's own storage error from the kernels' arithmetic.
+
 Parity status: every function here is pinned by a CPU test (worked values
 printed on the pages, closed forms, invariants or brute force).  The
 absolute values of the full-size output have no printed counterpart on the
@@ -158,6 +166,14 @@ def rope_tables(pos: np.ndarray, axes=(16, 56, 56), theta: float = 10000.0):
 # ───────────────────────────── row helpers ─────────────────────────────
 
 
+def store(a: np.ndarray, storage):
+    """Round to the device's float16 storage when ``storage == "f16"`` ([WG] ``Acts``)."""
+    if storage == "f16":
+        return a.astype(np.float16).astype(a.dtype)
+    return a
+
+
+
 def layer_norm(x: np.ndarray, eps: float, dt=F32) -> np.ndarray:
     """Affine-free LayerNorm over the last axis, biased variance ([QI] ``layer_norm_into``).
 
@@ -254,12 +270,15 @@ def qk_norm_rope(a: np.ndarray, w: np.ndarray, cos: np.ndarray, sin: np.ndarray,
 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, visible: np.ndarray,
-              heads: int, hd: int, dt=F32) -> np.ndarray:
+              heads: int, hd: int, dt=F32, storage=None) -> np.ndarray:
     """Masked multi-head attention, all scores materialised ([QI] ``attention``).
 
     Per head: q scaled by 1/sqrt(hd), scores = q k^T (one GEMM), row i keeps
     its first ``visible[i]`` keys (``softmax_prefix``), output = P V.
     ``q`` is ``[n, heads*hd]``, ``k`` and ``v`` ``[m, heads*hd]``.
+    With ``storage="f16"`` the unnormalised weights exp(s - max) are
+    rounded to float16 before P V and their sum ([WG] ``qi_flash``: P in
+    f16, the row sum of the same values).
     """
     n, m = q.shape[0], k.shape[0]
     scale = dt(1.0) / np.sqrt(dt(hd)).astype(dt)
@@ -268,8 +287,15 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, visible: np.ndarray,
         cs = slice(h * hd, (h + 1) * hd)
         qh = (q[:, cs].astype(dt) * scale).astype(dt)
         scores = np.matmul(qh, k[:, cs].astype(dt).T).astype(dt)
-        p = softmax_prefix(scores, visible, dt)
-        out[:, cs] = np.matmul(p, v[:, cs].astype(dt)).astype(dt)
+        if storage == "f16":
+            live = np.arange(m)[None, :] < np.asarray(visible).reshape(n, 1)
+            mx = np.where(live, scores, -np.inf).max(axis=1, keepdims=True)
+            e = store(np.where(live, np.exp((scores - mx).astype(dt)), dt(0.0)).astype(dt), storage)
+            den = e.astype(F64).sum(axis=1, keepdims=True)
+            out[:, cs] = (np.matmul(e, v[:, cs].astype(dt)) / den).astype(dt)
+        else:
+            p = softmax_prefix(scores, visible, dt)
+            out[:, cs] = np.matmul(p, v[:, cs].astype(dt)).astype(dt)
     return out
 
 
@@ -289,7 +315,7 @@ class Geometry:
 
 
 def block(blk: dict, x: np.ndarray, mods: np.ndarray, rope, kv_prefix, visible,
-          g: Geometry, dt=F32):
+          g: Geometry, dt=F32, storage=None):
     """One single-stream block on the query rows ``x`` ([QI] ``block_cpu``; module doc "Semantics").
 
     x += tanh(g1) * O(attn(LN(x)(1+s1))), then x += tanh(g2) * down(silu(gate) * up)
@@ -299,22 +325,23 @@ def block(blk: dict, x: np.ndarray, mods: np.ndarray, rope, kv_prefix, visible,
     rows themselves, post norm and RoPE).
     """
     h = g.dim
+    st = storage
     s1, g1t, s2, g2t = split_mods(mods, h, dt)
-    xn = norm_mod(x, s1, g.eps, dt)
-    q = lin(xn, blk["to_q"], dt)
-    k = lin(xn, blk["to_k"], dt)
-    v = lin(xn, blk["to_v"], dt)
-    q = qk_norm_rope(q, blk["norm_q"], rope[0], rope[1], g.heads, g.head_dim, g.eps, dt)
-    k = qk_norm_rope(k, blk["norm_k"], rope[0], rope[1], g.heads, g.head_dim, g.eps, dt)
+    xn = store(norm_mod(x, s1, g.eps, dt), st)
+    q = store(lin(xn, blk["to_q"], dt), st)
+    k = store(lin(xn, blk["to_k"], dt), st)
+    v = store(lin(xn, blk["to_v"], dt), st)
+    q = store(qk_norm_rope(q, blk["norm_q"], rope[0], rope[1], g.heads, g.head_dim, g.eps, dt), st)
+    k = store(qk_norm_rope(k, blk["norm_k"], rope[0], rope[1], g.heads, g.head_dim, g.eps, dt), st)
     if kv_prefix is not None:
         ka = np.concatenate([kv_prefix[0].astype(dt), k], axis=0)
         va = np.concatenate([kv_prefix[1].astype(dt), v], axis=0)
     else:
         ka, va = k, v
-    att = attention(q, ka, va, visible, g.heads, g.head_dim, dt)
+    att = store(attention(q, ka, va, visible, g.heads, g.head_dim, dt, st), st)
     x = gated_add(x.astype(dt), lin(att, blk["to_out"], dt), g1t, dt)
-    xn = norm_mod(x, s2, g.eps, dt)
-    hid = (silu(lin(xn, blk["gate"], dt), dt) * lin(xn, blk["up"], dt)).astype(dt)
+    xn = store(norm_mod(x, s2, g.eps, dt), st)
+    hid = store((silu(lin(xn, blk["gate"], dt), dt) * lin(xn, blk["up"], dt)).astype(dt), st)
     x = gated_add(x, lin(hid, blk["down"], dt), g2t, dt)
     return x, (k, v)
 
@@ -339,7 +366,8 @@ def target_rope(layout: Layout, g: Geometry):
     return rope_tables(pos[layout.prefix_len:], g.axes, g.theta)
 
 
-def prefill(model, x: np.ndarray, layout: Layout, dt=F32, layers: Optional[int] = None) -> Prefix:
+def prefill(model, x: np.ndarray, layout: Layout, dt=F32, layers: Optional[int] = None,
+            storage=None) -> Prefix:
     """Run the prefix rows through every block once, keeping K/V per layer ([QI] ``prefill``).
 
     ``x`` holds the prefix rows ``[lp, H]`` (already embedded); modulation is
@@ -356,7 +384,7 @@ def prefill(model, x: np.ndarray, layout: Layout, dt=F32, layers: Optional[int] 
     ks, vs = [], []
     x = x.astype(dt)
     for l in range(model.layers if layers is None else layers):
-        x, (k, v) = block(model.block(l), x, model.mods0, rope_p, None, vis, g, dt)
+        x, (k, v) = block(model.block(l), x, model.mods0, rope_p, None, vis, g, dt, storage)
         ks.append(k)
         vs.append(v)
     return Prefix(layout, ks, vs, target_rope(layout, g))
@@ -373,7 +401,7 @@ def final_layer(x: np.ndarray, final_scale: np.ndarray, proj_out: np.ndarray, ep
 
 
 def step(model, prefix: Prefix, tok: np.ndarray, mods: np.ndarray, final_scale: np.ndarray,
-         dt=F32, layers: Optional[int] = None) -> np.ndarray:
+         dt=F32, layers: Optional[int] = None, storage=None) -> np.ndarray:
     """One denoiser call: tokens ``[n, 64]`` -> velocity ``[n, 64]`` ([QI] ``step_cpu``).
 
     Every target row sees all lp + n keys: the cached prefix, then the
@@ -385,7 +413,7 @@ def step(model, prefix: Prefix, tok: np.ndarray, mods: np.ndarray, final_scale: 
     x = embed_image(tok, model.img_in, dt)
     every = np.full(n, lp + n, dtype=np.int64)
     for l in range(model.layers if layers is None else layers):
-        x, _ = block(model.block(l), x, mods, prefix.rope_t, (prefix.k[l], prefix.v[l]), every, g, dt)
+        x, _ = block(model.block(l), x, mods, prefix.rope_t, (prefix.k[l], prefix.v[l]), every, g, dt, storage)
     return final_layer(x, final_scale, model.proj_out, g.eps, dt)
 
 

@@ -71,7 +71,7 @@ def test_layout_vis_block_causal():
 def test_default_options_are_the_pages_guards():
     o = Q.qi21_default_options()
     assert (o.shift_attn, o.shift_qkv, o.shift_ao, o.shift_ffn, o.shift_hid) == (2, 4, 4, 2, 8)
-    assert o.max_programs == 2 and o.gemm_tile == -1
+    assert o.max_programs == 2 and o.gemm_tile == -1 and o.ffn_pair == 0
 
 
 def _geom(**kw):
@@ -112,7 +112,13 @@ def test_op_entry_points_validate_shapes_on_host():
         lambda: Q.qi21_op_flash(0, 1, 1, 128, 1, 128, 1, 64, 10, None, 0, None, 0, 0, None, 1, 128, stream=0),
         lambda: Q.qi21_op_flash(4, 1, 1, 128, 1, 128, 1, 32, 40, None, 0, None, 0, 0, None, 1, 128, stream=0),
         lambda: Q.qi21_op_rowop(4, 4098, 2, 1, 1, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
-        lambda: Q.qi21_op_rowop(4, 256, 4, 1, 1, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop(4, 256, 4, 1, 1, 1, 1, 0, 0, 1e-6, 1.0, stream=0),    # pair bit without the norm
+        lambda: Q.qi21_op_rowop(4, 256, 5, 1, 1, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop(4, 256, 8, 1, 1, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_gemm(5, 16, 128, 64, 1, 64, 1, 1, 128, stream=0),           # no such epilogue
+        lambda: Q.qi21_op_gemm(4, 16, 128, 64, 1, 64, 1, 1, 64, stream=0),            # swiglu2 needs ldo >= N
+        lambda: Q.qi21_op_gemm_pair(1, 16, 128, 64, 1, 100, 1, 1, 128, stream=0),     # lda < 2K
+        lambda: Q.qi21_op_gemm_pair(3, 16, 384, 64, 1, 128, 1, 1, 384, stream=0),     # no qkv pair epilogue
         lambda: Q.qi21_op_qkrope(4, 2, 1, 256, 1, 1, 1, 1, 1e-6, stream=0),
         lambda: Q.qi21_op_embed(4, 100, 1, 1, 1, stream=0),
         lambda: Q.qi21_op_final(4, 100, 1, 1, 1, 1e-6, 1, 1, stream=0),

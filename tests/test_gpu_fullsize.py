@@ -8,6 +8,16 @@ only the rows a sample touches are produced).  End to end, the step's
 velocity at 512^2, 1024^2, with the condition-image prefix and for the CFG
 pair is compared with the oracle's stored output (written by
 ``tests/golden/make_oracle_golden.py`` from the oracle alone).
+
+End-to-end tolerances.  With the FFN input and SwiGLU hidden kept as f16
+pairs (ffn_pair = 1) the velocity is held to the 1e-3 relative L2 bar.
+With every site in single f16 (the default, as on the pages) the error
+after 32 blocks of these N(0, 0.02) weights is the storage's own: the
+oracle run with the same sites rounded to f16 (its ``storage="f16"``
+mode) is itself ~1.8e-3 from the f32 oracle at 512^2, growing as the
+square root of the depth from ~3e-4 per block.  The single-f16 path is
+therefore bounded by 1.5x that storage error, measured on the same
+workload, not by 1e-3.
 """
 import os
 
@@ -177,43 +187,67 @@ def full_model():
     Q().qi21_model_destroy(m)
 
 
-def _golden(name, p=0):
+@pytest.fixture(scope="module")
+def full_model_pair():
+    opt = Q().qi21_default_options()
+    opt.ffn_pair = 1
+    m = bench.build_model(CONFIGS["1024"].model, opt)
+    yield m
+    Q().qi21_model_destroy(m)
+
+
+def _golden(name, p=0, tag=""):
     import glob
-    f = glob.glob(os.path.join(GOLD, f"oracle_v_{name}_p{p}_rows*.npy"))
+    f = glob.glob(os.path.join(GOLD, f"oracle_v_{name}_p{p}{tag}_rows*.npy"))
     if not f:
-        pytest.skip(f"no stored oracle output for {name} (tests/golden/make_oracle_golden.py {name})")
+        pytest.skip(f"no stored oracle output {name}{tag} (tests/golden/make_oracle_golden.py)")
     stride = int(f[0].rsplit("rows", 1)[1].split(".")[0])
     return np.load(f[0]), stride
 
 
-@pytest.mark.parametrize("name", ["512", "1024", "cond"])
-def test_step_full_size_against_oracle(full_model, name):
-    w = CONFIGS[name]
-    want, stride = _golden(name)
+def _step_v(m, w, key, stride):
     d = bench.workload_tensors(w)
-    bench.prefill(full_model, 50, d)
+    bench.prefill(m, key, d)
     out = torch.full((d["n"], 64), 7.0, device="cuda")
-    Q().qi21_step(full_model, 50, d["tok"], d["mods"], d["fs"], out)
-    v = out.cpu().numpy()[::stride]
-    err = rel(v, want)
-    print(f"{name}: v rel L2 vs oracle {err:.3e}")
+    Q().qi21_step(m, key, d["tok"], d["mods"], d["fs"], out)
+    Q().qi21_release_key(m, key)
+    return out.cpu().numpy()[::stride]
+
+
+@pytest.mark.parametrize("name", ["512", "1024", "cond"])
+def test_step_full_size_against_oracle(full_model_pair, name):
+    want, stride = _golden(name)
+    err = rel(_step_v(full_model_pair, CONFIGS[name], 50, stride), want)
+    print(f"{name} (ffn_pair): v rel L2 vs oracle {err:.3e}")
     assert err < V_TOL
-    Q().qi21_release_key(full_model, 50)
 
 
-def test_cfg_pair_full_size_against_oracle(full_model):
+@pytest.mark.parametrize("name", ["512", "1024"])
+def test_step_full_size_single_f16_within_storage_error(full_model, name):
+    want, stride = _golden(name)
+    want16, _ = _golden(name, tag="_f16")
+    storage = rel(want16, want)  # what f16 storage alone costs, per the oracle
+    err = rel(_step_v(full_model, CONFIGS[name], 51, stride), want)
+    print(f"{name} (single f16): v rel L2 vs oracle {err:.3e}; oracle f16-storage error {storage:.3e}")
+    assert storage > V_TOL  # the reason this path has its own bound
+    assert err < 1.5 * storage
+
+
+def test_cfg_pair_full_size_against_oracle(full_model_pair):
     w = CONFIGS["cfg512"]
     wants = [_golden("cfg512", p) for p in range(2)]
     ds = [bench.workload_tensors(w, p) for p in range(2)]
     for p in range(2):
-        bench.prefill(full_model, 60 + p, ds[p])
+        bench.prefill(full_model_pair, 60 + p, ds[p])
     outs = [torch.zeros(d["n"], 64, device="cuda") for d in ds]
-    Q().qi21_step_batch(full_model, [60, 61], [d["tok"] for d in ds], ds[0]["mods"], ds[0]["fs"], outs)
+    Q().qi21_step_batch(full_model_pair, [60, 61], [d["tok"] for d in ds], ds[0]["mods"], ds[0]["fs"], outs)
     for p in range(2):
         want, stride = wants[p]
         err = rel(outs[p].cpu().numpy()[::stride], want)
-        print(f"cfg prefix {p}: v rel L2 vs oracle {err:.3e}")
+        print(f"cfg prefix {p} (ffn_pair): v rel L2 vs oracle {err:.3e}")
         assert err < V_TOL
+    for p in range(2):
+        Q().qi21_release_key(full_model_pair, 60 + p)
 
 
 def test_step_1024_gate_zero_closed_form_and_determinism(full_model):

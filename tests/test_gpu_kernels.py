@@ -99,6 +99,95 @@ def test_gemm_epilogues(epi, M, tile):
         assert np.all(vtn[:, rest] == 0)  # nothing written for rows past M
 
 
+def _pair(a32):
+    """an f32 array as the f16 pair (hi, lo) = (f16(a), f16(a - hi))"""
+    hi = a32.astype(np.float16)
+    lo = (a32 - hi.astype(np.float32)).astype(np.float16)
+    return hi, lo
+
+
+def _check_pair(hi, lo):
+    """lo is at most half an f16 step of hi: hi is the f16 rounding of hi + lo"""
+    hi = np.asarray(hi, np.float16)
+    half_step = np.spacing(np.abs(hi)).astype(np.float32) / 2
+    assert np.all(np.abs(np.asarray(lo, np.float32)) <= half_step)
+
+
+PAIR_TOL = 1e-5  # f32 accumulation; the pair carries ~22 significant bits
+
+
+@pytest.mark.parametrize("tile", [-1, 0, 1])
+@pytest.mark.parametrize("M", [1, 77, 300, 1600])
+@pytest.mark.parametrize("epi", ["f32", "swiglu", "swiglu2"])
+def test_gemm_pair_operand(epi, M, tile):
+    """(A_hi + A_lo) W^T with each W row read for both halves (the ffn_pair
+    GEMMs): within f32 accumulation of the float operand's exact product,
+    where a single f16 operand is ~1e-4 away."""
+    q = Q()
+    N, K = 768, 512
+    A = inputs.host_array(2, 1, (M, K), 1.0)
+    W = f16_host(2, 2, (N, K), 0.05)
+    hi, lo = _pair(A)
+    dA = dev(np.concatenate([hi, lo], axis=1))
+    dW = dev(W, torch.float16)
+    oscale, inscale = 0.25, 4.0
+    A64, W64 = A.astype(np.float64), W.astype(np.float64)
+    if epi == "f32":
+        out = torch.zeros(M, N, device="cuda", dtype=torch.float32)
+        q.qi21_op_gemm_pair(q.QI21_EPI_F32, M, N, K, dA, 2 * K, dW, out, N, oscale=oscale, tile=tile)
+        sync()
+        want = A64 @ W64.T * oscale
+        assert rel(out.cpu().numpy(), want) < PAIR_TOL
+        single = O.lin(hi.astype(np.float32), W) * np.float32(oscale)
+        assert rel(single, want) > 10 * PAIR_TOL  # the lo half matters at this tolerance
+        return
+    G, U = W[: N // 2], W[N // 2:]
+    w13 = torch.empty(N, K, device="cuda", dtype=torch.float16)
+    q.qi21_op_plane(q.QI21_F32, dev(G), N // 2, K, w13, 32, 64, 0)
+    q.qi21_op_plane(q.QI21_F32, dev(U), N // 2, K, w13, 32, 64, 32)
+    g = A64 @ G.astype(np.float64).T * inscale
+    u = A64 @ U.astype(np.float64).T * inscale
+    want = g / (1 + np.exp(-g)) * u * oscale
+    if epi == "swiglu":
+        out = torch.zeros(M, N // 2, device="cuda", dtype=torch.float16)
+        q.qi21_op_gemm_pair(q.QI21_EPI_SWIGLU, M, N, K, dA, 2 * K, w13, out, N // 2, oscale=oscale, inscale=inscale,
+                            tile=tile)
+        sync()
+        assert rel(out.float().cpu().numpy(), want) < F16_TOL
+    else:
+        out = torch.zeros(M, N, device="cuda", dtype=torch.float16)
+        q.qi21_op_gemm_pair(q.QI21_EPI_SWIGLU2, M, N, K, dA, 2 * K, w13, out, N, oscale=oscale, inscale=inscale,
+                            tile=tile)
+        sync()
+        o = out.cpu().numpy()
+        ohi, olo = o[:, : N // 2], o[:, N // 2:]
+        _check_pair(ohi, olo)
+        assert rel(ohi.astype(np.float64) + olo.astype(np.float64), want) < PAIR_TOL
+
+
+@pytest.mark.parametrize("M", [77, 1600])
+def test_gemm_swiglu_pair_output(M):
+    """SWIGLU2 on a single f16 operand: the hidden as an f16 pair equals the
+    f32 epilogue value, hi being its f16 rounding."""
+    q = Q()
+    N, K = 512, 256
+    A = f16_host(4, 1, (M, K), 1.0)
+    W = f16_host(4, 2, (N, K), 0.05)
+    G, U = W[: N // 2], W[N // 2:]
+    w13 = torch.empty(N, K, device="cuda", dtype=torch.float16)
+    q.qi21_op_plane(q.QI21_F32, dev(G), N // 2, K, w13, 32, 64, 0)
+    q.qi21_op_plane(q.QI21_F32, dev(U), N // 2, K, w13, 32, 64, 32)
+    out = torch.zeros(M, N, device="cuda", dtype=torch.float16)
+    q.qi21_op_gemm(q.QI21_EPI_SWIGLU2, M, N, K, dev(A, torch.float16), K, w13, out, N)
+    sync()
+    g = A.astype(np.float64) @ G.astype(np.float64).T
+    u = A.astype(np.float64) @ U.astype(np.float64).T
+    want = g / (1 + np.exp(-g)) * u
+    o = out.cpu().numpy()
+    _check_pair(o[:, : N // 2], o[:, N // 2:])
+    assert rel(o[:, : N // 2].astype(np.float64) + o[:, N // 2:], want) < PAIR_TOL
+
+
 def test_gemm_plane_conversion_exact():
     q = Q()
     rows, cols = 96, 128
@@ -168,6 +257,30 @@ def test_flash_parity(case):
 
 
 # ───────────────────────────── row kernels ─────────────────────────────
+
+@pytest.mark.parametrize("h", [256, 4096])
+@pytest.mark.parametrize("rows", [1, 300])
+@pytest.mark.parametrize("mode", [6, 7])
+def test_rowop_pair_output(mode, rows, h):
+    """mode bit 2: the modulated LayerNorm written as an f16 pair [rows][2h]
+    whose sum is the f32 value (the ffn_pair FFN input)"""
+    q = Q()
+    x = inputs.host_array(8, 1, (rows, h), 1.0)
+    y = inputs.host_array(8, 2, (rows, h), 0.5)
+    mods = inputs.host_array(8, 3, (4 * h,), 0.1)
+    g_off, s_off, eps, oscale = 3 * h, 2 * h, 1e-6, 0.25
+    dx, dy, dm = dev(x), dev(y), dev(mods)
+    xn = torch.zeros(rows, 2 * h, device="cuda", dtype=torch.float16)
+    q.qi21_op_rowop(rows, h, mode, dx, dy, xn, dm, g_off, s_off, eps, oscale)
+    sync()
+    xe = O.gated_add(x, y, mods[g_off:g_off + h]) if mode & 1 else x
+    assert rel(dx.cpu().numpy(), xe) < 1e-6
+    want = O.norm_mod(xe, mods[s_off:s_off + h], eps, dt=np.float64) * oscale
+    o = xn.cpu().numpy()
+    _check_pair(o[:, :h], o[:, h:])
+    assert rel(o[:, :h].astype(np.float64) + o[:, h:], want) < 2e-6
+
+
 
 @pytest.mark.parametrize("h", [256, 4096])
 @pytest.mark.parametrize("rows", [1, 37, 300])

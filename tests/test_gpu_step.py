@@ -132,6 +132,40 @@ def test_range_guard_settings(tiny_cpu, shifts):
         q.qi21_model_destroy(m)
 
 
+def test_ffn_pair_option(tiny_cpu, tiny_gpu):
+    """ffn_pair = 1 (FFN input and hidden as f16 pairs): same result to the
+    bar, on the single step and on a batched CFG pair; no larger error than
+    single f16"""
+    q = Q()
+    opt = q.qi21_default_options()
+    opt.ffn_pair = 1
+    m = bench.build_model(TINY_MODEL, opt)
+    try:
+        w = CONFIGS["tiny"]
+        v, _ = gpu_v(m, w)
+        want = oracle_v(tiny_cpu, w)
+        err = rel(v, want)
+        base = rel(gpu_v(tiny_gpu, w, key=5)[0], want)
+        print(f"tiny v rel L2 ffn_pair {err:.3e}, single f16 {base:.3e}")
+        assert err < V_TOL and err < base
+        ds = [bench.workload_tensors(w) for _ in range(2)]
+        bench.prefill(m, 2, ds[0])
+        outs = [torch.zeros(ds[0]["n"], 64, device="cuda") for _ in range(2)]
+        q.qi21_step_batch(m, [1, 2], [d["tok"] for d in ds], ds[0]["mods"], ds[0]["fs"], outs)
+        for o in outs:
+            assert rel(o.cpu().numpy(), v) < 1e-6
+    finally:
+        q.qi21_model_destroy(m)
+
+
+def test_ffn_pair_option_is_validated():
+    q = Q()
+    opt = q.qi21_default_options()
+    opt.ffn_pair = 2
+    with pytest.raises(q.Qi21Error):
+        bench.build_model(TINY_MODEL, opt)
+
+
 def test_nonfinite_velocity_is_refused_and_out_untouched(tiny_gpu):
     q = Q()
     w = CONFIGS["tiny"]
