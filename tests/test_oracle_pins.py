@@ -415,6 +415,41 @@ def test_f32_oracle_within_bound_of_f64(tiny):
     assert _rel(v32, v64) < 1e-5
 
 
+def test_f16_storage_mode_moves_v_by_rounding_order(tiny):
+    # storage="f16" rounds the device design's f16 sites; on the tiny model
+    # that moves v by f16 rounding's order, never by an O(1) change
+    w, model, d = tiny
+    lay = O.Layout(w.layout())
+    v32 = O.step(model, O.prefill(model, d["x_prefix"], lay), d["tok"], d["mods"], d["final_scale"])
+    p16 = O.prefill(model, d["x_prefix"], lay, storage="f16")
+    v16 = O.step(model, p16, d["tok"], d["mods"], d["final_scale"], storage="f16")
+    assert 1e-5 < _rel(v16, v32) < 5e-3
+
+
+def test_f16_store_is_round_to_nearest_even_binary16():
+    x = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 2.0 ** -24, 2.0 ** -26, 65504.0, 1 / 3], np.float32)
+    got = O.store(x, "f16")
+    want = np.array([1.0, 1 + 2.0 ** -9, 2.0 ** -24, 0.0, 65504.0, 0.333251953125], np.float32)
+    assert np.array_equal(got, want)
+    assert O.store(x, None) is x
+
+
+def test_f16_storage_attention_normalises_by_the_rounded_weights():
+    # with V = 1 the output is the sum of the normalised weights: exactly 1
+    # when the row sum is taken over the same rounded values that multiply V
+    rng = np.random.default_rng(5)
+    n, m, hd = 7, 23, 128
+    q = rng.standard_normal((n, hd)).astype(np.float32)
+    k = rng.standard_normal((m, hd)).astype(np.float32)
+    vis = np.array([1, 3, 5, 9, 12, 20, 23])
+    out = O.attention(q, k, np.ones((m, hd), np.float32), vis, 1, hd, storage="f16")
+    assert np.all(np.abs(out - 1) <= 2 ** -23)
+    # one visible key: the output is that key's value row, exactly
+    v = rng.standard_normal((m, hd)).astype(np.float32)
+    one = O.attention(q, k, v, np.ones(n, int), 1, hd, storage="f16")
+    assert np.array_equal(one, np.broadcast_to(v[0], (n, hd)))
+
+
 def test_softmax_rows_not_flat_on_synthetic_inputs(tiny):
     # the synthetic norm weights (1 + N(0, 0.02)) keep attention peaked
     # enough that the mask matters
