@@ -16,12 +16,16 @@
 // are lane-local; the two lanes that share a query (l and l ^ 32) exchange
 // their maxima once per key tile and their sums once at the end.
 //
-// Block: 4 waves x 32 queries; key tile 64.  The K tile [64][128] and the
-// V^T tile [128][64] of each step are fetched by buffer loads that write
-// straight into LDS (two stages: the next tile is in flight while the
-// current one is multiplied); keys past a source's end read as zeros and
-// are masked.  At most 256 registers per lane, so two blocks share a CU and
-// one block's softmax overlaps the other's MFMAs.
+// Block: NW waves x 32 queries (NW = 8, or 4 for grids too small to fill
+// the chip), key tile 64.  The K tile [64][128] and the V^T tile [128][64]
+// of each step are fetched by buffer loads that write straight into LDS,
+// through a ring of NST stages (4 with 8 waves: 128 KB, one block per CU;
+// 2 with 4 waves: 64 KB, two blocks per CU), so a tile's loads have NST - 1
+// steps to land; keys past a source's end read as zeros and are masked.
+// All 16 K fragments of a step are read from LDS before its first MFMA and
+// the V^T fragments before the softmax, so LDS latency is paid once per
+// phase.  Either way each SIMD holds two waves, whose matrix and vector
+// work interleave.
 //
 // V^T rows hold their keys permuted inside each group of 16 (bits 2 and 3
 // of the key index swapped; the qkv GEMM epilogue writes them so), which
@@ -44,10 +48,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 namespace {
-constexpr int BQ = 128;   // queries per block
 constexpr int BKV = 64;   // keys per tile
-constexpr int TILE_H = BKV * 128;       // halves in the K tile (and in the V^T tile)
-constexpr int STAGE_H = 2 * TILE_H;     // K tile then V^T tile
+constexpr int TILE_B = BKV * 128 * 2;   // bytes of a K tile (and of a V^T tile)
+constexpr int STAGE_B = 2 * TILE_B;     // K tile then V^T tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float THR = 8.0f;             // lazy-rescale threshold, log2 units
 
@@ -67,9 +70,11 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 }  // namespace
 
-template <bool VIS>
-__global__ __launch_bounds__(256, 2) void flash_kernel(FlashArgs a) {
-  __shared__ __attribute__((aligned(16))) f16 sm[2 * STAGE_H];
+template <bool VIS, int NW, int NST>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a) {
+  constexpr int BQ = NW * 32;          // queries per block
+  constexpr int NLD = 16 / NW;         // 16-byte loads per lane per K (and per V^T) tile
+  extern __shared__ __attribute__((aligned(16))) char smb[];  // NST stages of [K tile | V^T tile]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -115,54 +120,62 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(FlashArgs a) {
   // buffer resources of the two sources (this head's columns); K rows past
   // the source's end fall outside the range and read as zeros
   __amdgpu_buffer_rsrc_t kr[2], vr[2];
-  int ldk[2], ldv[2];
+  int lk2[2], lv2[2];
   {
     const f16* kb[2] = {a.k1, a.k2};
     const f16* vb[2] = {a.vt1, a.vt2};
     const int ns[2] = {a.n1, a.n2};
-    ldk[0] = a.ldk1;
-    ldk[1] = a.ldk2;
-    ldv[0] = a.ldvt1;
-    ldv[1] = a.ldvt2;
+    const int ldk[2] = {a.ldk1, a.ldk2}, ldv[2] = {a.ldvt1, a.ldvt2};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int n = max(ns[s], 1);
+      lk2[s] = ldk[s] * 2;
+      lv2[s] = ldv[s] * 2;
       kr[s] = __builtin_amdgcn_make_buffer_rsrc((void*)(kb[s] + head * 128), 0, (n - 1) * ldk[s] * 2 + 256,
                                                 0x00020000);
       vr[s] = __builtin_amdgcn_make_buffer_rsrc((void*)(vb[s] + (size_t)head * 128 * ldv[s]), 0, 128 * ldv[s] * 2,
                                                 0x00020000);
     }
   }
-  // Load i (0..3) of wave w fills 16-byte LDS positions (4i + w) * 64 + lane
-  // of the K tile (key p / 16, slot p % 16) and of the V^T tile (dim p / 8,
-  // slot p % 8).  The key offset of a tile goes into the per-lane offset,
-  // which the buffer range check covers, so keys past a source's end read
-  // as zeros (V^T columns past the end are in range: the leading dimension
-  // covers whole 64-key tiles).
-  int lkey[4], lck[4], ldim[4], lcv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = (i * 4 + wave) * 64 + lane;
-    lkey[i] = p >> 4;
-    lck[i] = ((p & 15) ^ (lkey[i] & 15)) * 16;
-    ldim[i] = p >> 3;
-    lcv[i] = ((p & 7) ^ vswz(ldim[i])) * 16;
-  }
-  auto issue = [&](int t, int stage) {
+  // Load i (0..NLD-1) of wave w fills 16-byte LDS positions p = (NW i + w)
+  // * 64 + lane of the K tile (key p / 16 = 4 NW i + 4w + lane / 16, slot
+  // p % 16) and of the V^T tile (dim p / 8 = 8 NW i + 8w + lane / 8, slot
+  // p % 8); a lane's swizzled chunk is the same for all of them.  The key offset of a tile goes
+  // into the per-lane offset, which the buffer range check covers, so keys
+  // past a source's end read as zeros (V^T columns past the end are in
+  // range: the leading dimension covers whole 64-key tiles, and the tile's
+  // first column goes into the scalar offset).
+  const int lkey0 = 4 * wave + (lane >> 4);
+  const int lck = ((lane & 15) ^ (lkey0 & 15)) * 16;
+  const int ldim0 = 8 * wave + (lane >> 3);
+  const int lcv = ((lane & 7) ^ vswz(ldim0)) * 16;
+  // tile t -> stage t % NST
+  auto issue = [&](int t) {
     const bool s1 = t < t1;
     const int j0 = (s1 ? t : t - t1) * BKV;
-    const int lk2 = (s1 ? ldk[0] : ldk[1]) * 2, lv2 = (s1 ? ldv[0] : ldv[1]) * 2;
+    const int kl2 = s1 ? lk2[0] : lk2[1], vl2 = s1 ? lv2[0] : lv2[1];
     const __amdgpu_buffer_rsrc_t krs = s1 ? kr[0] : kr[1];
     const __amdgpu_buffer_rsrc_t vrs = s1 ? vr[0] : vr[1];
+    const int ko = (j0 + lkey0) * kl2 + lck;
+    const int vo = ldim0 * vl2 + lcv;
     const int sv = __builtin_amdgcn_readfirstlane(j0 * 2);
-    f16* base = sm + stage * STAGE_H + wave * 64 * 8;
+    char* base = smb + (t % NST) * STAGE_B + wave * 64 * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, base + i * 4 * 64 * 8, 16, (j0 + lkey[i]) * lk2 + lck[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, base + TILE_H + i * 4 * 64 * 8, 16, ldim[i] * lv2 + lcv[i], sv, 0,
-                                               0);
+    for (int i = 0; i < NLD; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, base + i * NW * 64 * 16, 16, ko + i * 4 * NW * kl2, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, base + TILE_B + i * NW * 64 * 16, 16, vo + i * 8 * NW * vl2, sv,
+                                               0, 0);
     }
   };
+  // Byte offsets of this lane's LDS fragments inside a tile.  K: key l32
+  // (sub-tile 1 is 32 rows = 8192 bytes further), chunk 2c + hs.  V^T: dim
+  // row l32 (dim block d is 32 rows = 4096 bytes further), chunk 4st + 2u +
+  // hs = 2su + hs.  The swizzles depend on l32 only.
+  int kofs[8], vofs[4];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) kofs[c] = l32 * 256 + (((2 * c + hs) ^ (l32 & 15)) * 16);
+#pragma unroll
+  for (int su = 0; su < 4; ++su) vofs[su] = l32 * 128 + (((2 * su + hs) ^ vswz(l32)) * 16);
 
   floatx16 o[4];
 #pragma unroll
@@ -174,47 +187,68 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(FlashArgs a) {
   const float thr_raw = THR / c2;
   const half2v ones = half2v{(f16)1.0f, (f16)1.0f};
 
-  if (T > 0) issue(0, 0);
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t)
+    if (t < T) issue(t);
   for (int t = 0; t < T; ++t) {
-    const int cur = t & 1;
-    // tile t resident; every wave is done with tile t - 1, whose stage
-    // receives tile t + 1
-    __builtin_amdgcn_s_waitcnt(0x7 << 4 | 0xF << 8);  // vmcnt(0)
+    // tile t resident (the loads of up to NST - 2 later tiles may still be
+    // in flight, 2 NLD per tile); after the barrier every wave is done with
+    // tile t - 1, whose stage receives tile t + NST - 1
+    if (NST == 4 && t + 2 < T)
+      __builtin_amdgcn_s_waitcnt(wait_imm(4 * NLD, 15));
+    else if (NST >= 3 && t + 1 < T)
+      __builtin_amdgcn_s_waitcnt(wait_imm(2 * NLD, 15));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
     __builtin_amdgcn_s_barrier();
-    if (t + 1 < T) issue(t + 1, cur ^ 1);
-    const f16* sk = sm + cur * STAGE_H;
-    const f16* sv = sk + TILE_H;
+    if (t + NST - 1 < T) issue(t + NST - 1);
+    const char* sk = smb + (t % NST) * STAGE_B;
+    const char* sv = sk + TILE_B;
 
     // S^T = K Q^T : two 32-key sub-tiles
+    // all 16 K fragments are read before the first MFMA, so one LDS
+    // latency is paid per tile instead of one per pair of MFMAs
+    half8 kv[16];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) kv[2 * c + st] = *reinterpret_cast<const half8*>(sk + kofs[c] + st * 8192);
     floatx16 s[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[st][e] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int key = st * 32 + l32;
-        const half8 kv = *reinterpret_cast<const half8*>(sk + key * 128 + (((2 * c + hs) ^ (key & 15)) * 8));
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv, qf[c], s[st], 0, 0, 0);
-      }
-    }
+      for (int st = 0; st < 2; ++st) s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv[2 * c + st], qf[c], s[st], 0, 0, 0);
+    // the V^T fragments do not depend on P: their reads are issued now and
+    // land while the softmax runs
+    half8 vv[16];
+#pragma unroll
+    for (int su = 0; su < 4; ++su)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) vv[4 * su + d] = *reinterpret_cast<const half8*>(sv + vofs[su] + d * 4096);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    __builtin_amdgcn_sched_barrier(0);
 
     // mask: keys past the source's end, or past vis[i] (tail tiles and the
-    // prefill only; a wave-uniform branch)
+    // prefill only; a wave-uniform branch).  Element e of sub-tile st is key
+    // st*32 + 8(e/4) + 4hs + e%4 of the tile: its constant part is compared
+    // against one per-lane bound.
     const bool s1 = t < t1;
     const int j0 = (s1 ? t : t - t1) * BKV;
     const int cnt = min(BKV, (s1 ? a.n1 : a.n2) - j0);
     const int gbase = (s1 ? 0 : a.n1) + j0;
     if (__builtin_amdgcn_readfirstlane((int)(VIS || cnt < BKV))) {
+      const int bound = min(cnt, lim - gbase) - 4 * hs;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kk = st * 32 + 8 * (e >> 2) + 4 * hs + (e & 3);
-          if (kk >= cnt || gbase + kk >= lim) s[st][e] = -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e)
+          if (st * 32 + 8 * (e >> 2) + (e & 3) >= bound) s[st][e] = -INFINITY;
     }
     float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
@@ -254,16 +288,10 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(FlashArgs a) {
     // O^T += V^T P^T : the lane's 8 keys of k-step (st, u) are the 16-byte
     // chunk 4st + 2u + hs of its dim row
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int su = 0; su < 4; ++su)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int row = 32 * d + l32;
-          const half8 vv = *reinterpret_cast<const half8*>(sv + row * 64 + (((4 * st + 2 * u + hs) ^ vswz(row)) * 8));
-          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv, pf[st][u], o[d], 0, 0, 0);
-        }
-      }
+      for (int d = 0; d < 4; ++d)
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv[4 * su + d], pf[su >> 1][su & 1], o[d], 0, 0, 0);
   }
 
   const float ltot = pair_sum(lsum);
@@ -282,13 +310,40 @@ __global__ __launch_bounds__(256, 2) void flash_kernel(FlashArgs a) {
   }
 }
 
-hipError_t launch_flash(const FlashArgs& a, hipStream_t s) {
-  dim3 grid(((a.nq + BQ - 1) / BQ) * a.heads);
+namespace {
+template <int NW, int NST>
+hipError_t launch_shape(const FlashArgs& a, hipStream_t s) {
+  constexpr size_t lds = (size_t)NST * STAGE_B;
+  static bool attr = false;
+  if (!attr) {
+    for (const void* f : {reinterpret_cast<const void*>(&flash_kernel<true, NW, NST>),
+                          reinterpret_cast<const void*>(&flash_kernel<false, NW, NST>)}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    attr = true;
+  }
+  dim3 grid(((a.nq + NW * 32 - 1) / (NW * 32)) * a.heads);
   if (a.vis)
-    hipLaunchKernelGGL(flash_kernel<true>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((flash_kernel<true, NW, NST>), grid, dim3(NW * 64), lds, s, a);
   else
-    hipLaunchKernelGGL(flash_kernel<false>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((flash_kernel<false, NW, NST>), grid, dim3(NW * 64), lds, s, a);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_flash(const FlashArgs& a, hipStream_t s) {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+  }
+  // 8-wave blocks (one per CU) once they make at least two rounds over the
+  // chip; smaller grids use 4-wave blocks, two per CU
+  const long blocks8 = (long)((a.nq + 255) / 256) * a.heads;
+  if (blocks8 >= 2L * cus) return launch_shape<8, 4>(a, s);
+  return launch_shape<4, 2>(a, s);
 }
 
 }  // namespace qi21

@@ -43,12 +43,6 @@ namespace {
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
 
-// s_waitcnt immediate (gfx9 encoding): vmcnt 6 bits at [3:0] and [15:14],
-// expcnt [6:4], lgkmcnt [11:8]; the maximum of a field means "no wait".
-constexpr int wait_imm(int vm, int lgkm) {
-  return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm & 0xF) << 8);
-}
-
 // Block -> (tile row, tile column).  Hardware deals block b to XCD b % 8;
 // blocks of one XCD get a contiguous run of tiles, enumerated in groups of
 // 4 tile rows so that the ~32 tiles an XCD runs at once span 4 A panels and

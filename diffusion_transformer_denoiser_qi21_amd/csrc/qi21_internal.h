@@ -12,6 +12,12 @@ namespace qi21 {
 
 typedef _Float16 f16;
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt 6 bits at [3:0] and [15:14],
+// expcnt [6:4], lgkmcnt [11:8]; the maximum of a field means "no wait".
+constexpr int wait_imm(int vm, int lgkm) {
+  return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm & 0xF) << 8);
+}
+
 enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 4 };
 
 // C = A * W^T over f16 operands with f32 accumulation.
