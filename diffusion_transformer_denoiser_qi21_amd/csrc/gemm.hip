@@ -41,7 +41,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
-__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
+// silu through the hardware reciprocal (~1 ulp; the result is stored as f16)
+__device__ __forceinline__ float silu_f(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 // Block -> (tile row, tile column).  Hardware deals block b to XCD b % 8;
 // blocks of one XCD get a contiguous run of tiles, enumerated in groups of
@@ -167,13 +168,18 @@ __device__ __forceinline__ int dswz(int r) { return (r >> 2) & 3; }
 // Persistent over tiles: block b runs on XCD b % 8 and walks that XCD's
 // contiguous run of the grouped tile sequence, 32 blocks abreast.  The
 // next tile's first LDS stages are fetched while the current tile's
-// epilogue stores drain.
-template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs a) {
+// epilogue stores drain.  NW = 4 waves of 128 x 128 (one per SIMD) or 8
+// waves of 128 x 64 (two per SIMD, so one wave's issue stalls, barrier
+// waits and epilogue are covered by the other's MFMAs).
+template <int EPI, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
+  constexpr int TM = 4, TN = NW == 4 ? 4 : 2;  // 32 x 32 tiles per wave
+  constexpr int WTN = TN * 32;                 // wave tile columns
+  constexpr int NL = 16 / NW;                  // 16-byte loads per lane per operand per k-tile
   extern __shared__ __attribute__((aligned(16))) f16 smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
   const int hsel = lane >> 5, l32 = lane & 31;
   const int K = a.K;
   const int KT = K / DBK;
@@ -207,12 +213,14 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs a) {
       tn = sq - tm * tiles_n;
     }
   };
-  // Load i (0..3) of wave w fills LDS chunk positions (4i + w) * 64 + lane
-  // of the A region and of the W region: row p / 4, slot p % 4.
+  // Load i (0..NL-1) of wave w fills LDS chunk positions (NW i + w) * 64 +
+  // lane of the A region and of the W region: row p / 4, slot p % 4.
+  // (fixed size: an array sized by a template-dependent constant and
+  // captured by the lambdas below makes the host pass drop the kernel)
   int voa[4], vob[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = (i * 4 + wave) * 64 + lane;
+  for (int i = 0; i < NL; ++i) {
+    const int p = (i * NW + wave) * 64 + lane;
     const int r = p >> 2, c = (p & 3) ^ dswz(r);
     voa[i] = (r * a.lda + 8 * c) * 2;
     vob[i] = (r * a.kw + 8 * c) * 2;
@@ -237,35 +245,36 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs a) {
     const int soffw = (tt >= KTW ? tt - KTW : tt) * DBK * 2;
     f16* base = smem + (t % DNS) * DSTAGE + wave * 64 * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, base + i * 4 * 64 * 8, 16, voa[i], soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, base + DBM * DBK + i * 4 * 64 * 8, 16, vob[i], soffw, 0, 0);
+    for (int i = 0; i < NL; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, base + i * NW * 64 * 8, 16, voa[i], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, base + DBM * DBK + i * NW * 64 * 8, 16, vob[i], soffw, 0, 0);
     }
   };
-  floatx16 acc[4][4];
-  half8 af[2][4], bf[2][4];
+  floatx16 acc[TM][TN];
+  half8 af[2][TM], bf[2][TN];
   auto frags = [&](int t, int kk, int b) {
     const f16* sa = smem + (t % DNS) * DSTAGE;
     const f16* sb = sa + DBM * DBK;
     const int c = kk * 2 + hsel;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TM; ++i) {
       const int r = wm * 128 + i * 32 + l32;
       af[b][i] = *reinterpret_cast<const half8*>(sa + (r * 4 + (c ^ dswz(r))) * 8);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn * 128 + j * 32 + l32;
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn * WTN + j * 32 + l32;
       bf[b][j] = *reinterpret_cast<const half8*>(sb + (r * 4 + (c ^ dswz(r))) * 8);
     }
   };
   auto mma = [&](int b) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[b][i], bf[b][j], acc[i][j], 0, 0, 0);
   };
+  constexpr int MM = TM * TN, NDS = TM + TN, NVM = 2 * NL;  // per k-step: MFMAs, fragment reads; loads per k-tile
 
   int tm, tn;
   tile_rc(seq0, tm, tn);
@@ -275,15 +284,15 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs a) {
     const int m0 = tm * DBM, n0 = tn * DBN;
     const __amdgpu_buffer_rsrc_t ra = rsrc_a(m0), rb = rsrc_b(n0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     // k-tile 0 landed.  After an epilogue its stores share the vector
     // memory counter with these loads, so wait for all of them.
     if (sq == seq0)
-      __builtin_amdgcn_s_waitcnt(wait_imm((DNS - 1) * 8, 15));
+      __builtin_amdgcn_s_waitcnt(wait_imm((DNS - 1) * NVM, 15));
     else
       __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
     __builtin_amdgcn_s_barrier();
@@ -292,28 +301,28 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs a) {
       frags(t, 1, 1);
       mma(0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NDS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MM - NDS, 0);
       __builtin_amdgcn_sched_barrier(0);
       // this wave's reads of stage t % DNS are done and k-tile t + 1 has
       // landed; after the barrier every wave is past both, so the stage
       // can be refilled
-      __builtin_amdgcn_s_waitcnt(wait_imm((DNS - 2) * 8, 0));
+      __builtin_amdgcn_s_waitcnt(wait_imm((DNS - 2) * NVM, 0));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       issue(ra, rb, t + DNS);
       frags(t + 1, 0, 0);
       mma(1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NVM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load -> LDS
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < MM - NVM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
@@ -335,7 +344,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs a) {
       for (int t = 0; t < DNS; ++t) issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), t);
     }
     mma(1);
-    epilogue<EPI, 4, 4>(a, acc, m0 + wm * 128, n0 + wn * 128, lane);
+    epilogue<EPI, TM, TN>(a, acc, m0 + wm * 128, n0 + wn * WTN, lane);
   }
   __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));  // no LDS-bound load outlives the block
 }
@@ -439,12 +448,12 @@ __global__ __launch_bounds__(256) void gemm_rs_kernel(GemmArgs a) {
 
 namespace {
 
-template <int EPI>
+template <int EPI, int NW>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   constexpr size_t lds = (size_t)DNS * DSTAGE * 2;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<EPI>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<EPI, NW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
@@ -460,7 +469,7 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   // persistent: one block per CU walks several tiles; fewer tiles than CUs:
   // one block per tile
   const int blocks = tiles > cus ? cus : tiles;
-  hipLaunchKernelGGL((gemm_dma_kernel<EPI>), dim3(blocks), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gemm_dma_kernel<EPI, NW>), dim3(blocks), dim3(NW * 64), lds, s, a);
   return hipGetLastError();
 }
 
@@ -481,7 +490,8 @@ hipError_t launch_rs(const GemmArgs& a, hipStream_t s) {
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs& a, int tile, hipStream_t s) {
-  if (tile == 0) return launch_dma<EPI>(a, s);
+  if (tile == 0) return launch_dma<EPI, 4>(a, s);
+  if (tile == 2) return launch_dma<EPI, 8>(a, s);
   return launch_rs<128, 128, EPI>(a, s);
 }
 
@@ -489,13 +499,13 @@ hipError_t launch_epi(const GemmArgs& a, int tile, hipStream_t s) {
 
 int gemm_pick_tile(int M, int N, int K) {
   (void)K;
-  if (N % 256 == 0 && M >= 1536) return 0;
+  if (N % 256 == 0 && M >= 1536) return 2;
   return 1;
 }
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s) {
   if (tile < 0) tile = gemm_pick_tile(a.M, a.N, a.K);
-  if (tile == 0 && a.N % 256 != 0) tile = 1;
+  if ((tile == 0 || tile == 2) && a.N % 256 != 0) tile = 1;
   switch (epi) {
     case EPI_F16: return launch_epi<EPI_F16>(a, tile, s);
     case EPI_F32: return launch_epi<EPI_F32>(a, tile, s);

@@ -718,7 +718,7 @@ int op_gemm(int epi, int M, int N, int K, int ka, const void* A, int lda, const 
   if (ldo < ocols) return fail(QI21_EINVAL, "ldo %d < %d output columns", ldo, ocols);
   if (epi == QI21_EPI_QKV && ((N / 3) % 128 || N % 3 || !out2 || ld2 % 4 || ld2 < M))
     return fail(QI21_EINVAL, "qkv epilogue needs N/3 %% 128 == 0, out2, ld2 %% 4 == 0, ld2 >= M");
-  if (tile < -1 || tile > 1 || (tile == 0 && N % 256)) return fail(QI21_EINVAL, "tile %d for N %d", tile, N);
+  if (tile < -1 || tile > 2 || (tile != 1 && tile != -1 && N % 256)) return fail(QI21_EINVAL, "tile %d for N %d", tile, N);
   qi21::GemmArgs a = gemm_args(M, N, ka, (const f16*)A, lda, (const f16*)W, out, ldo, oscale, inscale, (f16*)out2, ld2);
   a.kw = K;
   HIP_OK(qi21::launch_gemm(epi, a, tile, (hipStream_t)stream));

@@ -54,7 +54,7 @@ def vt_pos(j):
 
 # ───────────────────────────── GEMM ─────────────────────────────
 
-@pytest.mark.parametrize("tile", [-1, 0, 1])
+@pytest.mark.parametrize("tile", [-1, 0, 1, 2])
 @pytest.mark.parametrize("M", [1, 77, 300, 1040])
 @pytest.mark.parametrize("epi", ["f16", "f32", "swiglu", "qkv"])
 def test_gemm_epilogues(epi, M, tile):
@@ -116,7 +116,7 @@ def _check_pair(hi, lo):
 PAIR_TOL = 1e-5  # f32 accumulation; the pair carries ~22 significant bits
 
 
-@pytest.mark.parametrize("tile", [-1, 0, 1])
+@pytest.mark.parametrize("tile", [-1, 0, 1, 2])
 @pytest.mark.parametrize("M", [1, 77, 300, 1600])
 @pytest.mark.parametrize("epi", ["f32", "swiglu", "swiglu2"])
 def test_gemm_pair_operand(epi, M, tile):
