@@ -176,6 +176,21 @@ def recorded_traffic(config: str):
     return rec["traffic_bytes_per_launch"]
 
 
+def copy_calibration(gib: int = 1, reps: int = 5) -> int:
+    """A plain device-to-device copy of a known size, run under rocprofv3
+    --pmc FETCH_SIZE / WRITE_SIZE to scale those counters to bytes."""
+    import torch
+
+    n = gib << 28  # float32 elements
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "reps": reps}))
+    return 0
+
+
 # ───────────────────────────── main ─────────────────────────────
 
 def main(argv=None):

@@ -38,6 +38,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -69,6 +70,63 @@ __device__ __forceinline__ void tile_of(int M, int N, int BM, int BN, int& tm, i
 // keeps runs of 4 keys contiguous and gathers keys {4h..4h+3, 8+4h..8+4h+3}
 // of every 16 into one 16-byte chunk (the attention kernel's P V operand).
 __device__ __forceinline__ int vt_pos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Epilogue of a wave whose output rows [r0, r0 + 32 TM) and columns
+// [c0, c0 + 32 TN) were accumulated with the W fragment as the MFMA's A
+// operand (C^T = W A^T): the 32x32 accumulator layout (lane l holds
+// column l % 32, rows 8g + 4(l / 32) + e in register 4g + e) then gives
+// lane l output row r0 + 32i + l % 32 and the 4 consecutive output columns
+// c0 + 32j + 8g + 4(l / 32) + (0..3) in registers 4g..4g+3, written as one
+// 16-byte (f32) or 8-byte (f16) store.  Requires ldo % 4 == 0.
+template <int EPI, int TM, int TN>
+__device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)[TM][TN], int r0, int c0, int lane) {
+  const int hsel = lane >> 5, l32 = lane & 31;
+  if constexpr (EPI == EPI_F32 || EPI == EPI_F16) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = r0 + i * 32 + l32;
+      if (row < a.M) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const size_t o = (size_t)row * a.ldo + c0 + j * 32 + 8 * g + 4 * hsel;
+            const floatx4 v = floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                      acc[i][j][4 * g + 3]} * a.oscale;
+            if constexpr (EPI == EPI_F32)
+              *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(a.out) + o) = v;
+            else
+              *reinterpret_cast<half4*>(reinterpret_cast<f16*>(a.out) + o) =
+                  half4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+          }
+      }
+    }
+  } else {  // EPI_SWIGLU, EPI_SWIGLU2: tiles (2p, 2p+1) hold matching gate / up columns
+    static_assert(EPI == EPI_SWIGLU || EPI == EPI_SWIGLU2, "row-layout epilogue");
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = r0 + i * 32 + l32;
+      if (row < a.M) {
+#pragma unroll
+        for (int p = 0; p < TN / 2; ++p)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            half4 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float h = silu_f(acc[i][2 * p][4 * g + e] * a.inscale) * (acc[i][2 * p + 1][4 * g + e] * a.inscale) *
+                              a.oscale;
+              hi[e] = (f16)h;
+              lo[e] = (f16)(h - (float)hi[e]);  // exact in f32
+            }
+            f16* op = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo + c0 / 2 + p * 32 + 8 * g + 4 * hsel;
+            *reinterpret_cast<half4*>(op) = hi;
+            if constexpr (EPI == EPI_SWIGLU2) *reinterpret_cast<half4*>(op + a.N / 2) = lo;
+          }
+      }
+    }
+  }
+}
 
 // Epilogue of one wave's TM x TN grid of 32 x 32 accumulator tiles whose
 // top-left output element is (r0, c0).  MFMA 32x32 accumulator layout: lane
@@ -267,12 +325,17 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
       bf[b][j] = *reinterpret_cast<const half8*>(sb + (r * 4 + (c ^ dswz(r))) * 8);
     }
   };
+  // every epilogue but the V^T one stores along output rows: C^T = W A^T
+  constexpr bool ROWS = EPI != EPI_QKV;
   auto mma = [&](int b) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[b][i], bf[b][j], acc[i][j], 0, 0, 0);
+        if constexpr (ROWS)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[b][j], af[b][i], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[b][i], bf[b][j], acc[i][j], 0, 0, 0);
   };
   constexpr int MM = TM * TN, NDS = TM + TN, NVM = 2 * NL;  // per k-step: MFMAs, fragment reads; loads per k-tile
 
@@ -344,7 +407,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
       for (int t = 0; t < DNS; ++t) issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), t);
     }
     mma(1);
-    epilogue<EPI, TM, TN>(a, acc, m0 + wm * 128, n0 + wn * WTN, lane);
+    if constexpr (ROWS)
+      epilogue_rows<EPI, TM, TN>(a, acc, m0 + wm * 128, n0 + wn * WTN, lane);
+    else
+      epilogue<EPI, TM, TN>(a, acc, m0 + wm * 128, n0 + wn * WTN, lane);
   }
   __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));  // no LDS-bound load outlives the block
 }

@@ -710,9 +710,9 @@ namespace {
 int op_gemm(int epi, int M, int N, int K, int ka, const void* A, int lda, const void* W, void* out, int ldo,
             void* out2, int ld2, float oscale, float inscale, int tile, void* stream) {
   if (epi < QI21_EPI_F16 || epi > QI21_EPI_SWIGLU2) return fail(QI21_EINVAL, "epilogue %d", epi);
-  if (M < 1 || N < 128 || K < 64 || N % 128 || K % 64 || lda % 8 || lda < ka)
-    return fail(QI21_EINVAL, "gemm M %d N %d K %d lda %d (need N %% 128, K %% 64, lda %% 8, lda >= %d)", M, N, K, lda,
-                ka);
+  if (M < 1 || N < 128 || K < 64 || N % 128 || K % 64 || lda % 8 || lda < ka || ldo % 4)
+    return fail(QI21_EINVAL, "gemm M %d N %d K %d lda %d ldo %d (need N %% 128, K %% 64, lda %% 8, lda >= %d, ldo %% 4)",
+                M, N, K, lda, ldo, ka);
   if (!A || !W || !out) return fail(QI21_EINVAL, "gemm pointer is NULL");
   const int ocols = epi == QI21_EPI_SWIGLU ? N / 2 : epi == QI21_EPI_QKV ? 2 * N / 3 : N;
   if (ldo < ocols) return fail(QI21_EINVAL, "ldo %d < %d output columns", ldo, ocols);

@@ -35,7 +35,8 @@ enum { QI21_EPI_F16 = 0, QI21_EPI_F32 = 1, QI21_EPI_SWIGLU = 2, QI21_EPI_QKV = 3
  *           out[r][c] = f16(h), out[r][N/2 + c] = f16(h - f16(h)); ldo >= N
  *           (the hidden of the ffn_pair option, qi21.h)
  * Requires M >= 1, N % 128 == 0, K % 64 == 0, lda % 8 == 0, lda >= K,
- * ldo >= output columns, for QKV (N/3) % 128 == 0, ld2 % 4 == 0, ld2 >= M.
+ * ldo >= output columns, ldo % 4 == 0, 16-byte aligned A, W and out, for
+ * QKV (N/3) % 128 == 0, ld2 % 4 == 0, ld2 >= M.
  * tile: -1 automatic, 0 = 256x256 with 4 waves, 2 = 256x256 with 8 waves
  * (both need N % 256 == 0), 1 = 128x128. */
 int qi21_op_gemm(int epi, int M, int N, int K, const void* A, int lda, const void* W, void* out, int ldo,
