@@ -185,29 +185,36 @@ hipError_t launch_embed(int rows, int h, const float* tok, const float* img_in, 
 }
 
 // ───────────────────────────── final ─────────────────────────────
-// 16 rows per block.  Phase 1: each wave computes mean / inverse std of 4
-// rows.  Phase 2: columns in chunks of 256; the chunk's normalised values
-// (x - mean) * inv * fs go to LDS, then thread (o = t % 64, rows 4*(t/64)..)
-// accumulates over the chunk with proj_out^T rows (coalesced over o).
+// 16 rows per block, 4 waves.  Phase 1: wave w computes mean / inverse std
+// of rows 4w..4w+3 (16-byte loads, two passes).  Phase 2: wave w owns the
+// columns [w h/4, (w+1) h/4), taken 64 at a time: the chunk's normalised
+// values (x - mean) * inv * fs of the 16 rows go to the wave's LDS area
+// ([16][64]), then lane o accumulates the 16 rows over the chunk against
+// proj_out^T rows (coalesced over o), four columns per broadcast 16-byte
+// LDS read.  Phase 3: the four waves' partial sums are added through LDS.
 __global__ __launch_bounds__(256) void final_kernel(int rows, int h, const float* __restrict__ x,
                                                     const float* __restrict__ fs,
                                                     const float* __restrict__ pt, float eps,
                                                     float* __restrict__ out, int* __restrict__ flag) {
-  __shared__ float xs[16][257];
+  __shared__ __attribute__((aligned(16))) float xs[4][16][64];
+  __shared__ float part[4][16][64];
   __shared__ float mean_s[16], inv_s[16];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int r0 = blockIdx.x * 16;
+  const int h4 = h >> 2;
   for (int i = 0; i < 4; ++i) {
     const int rl = wave * 4 + i;
-    const int r = min(r0 + rl, rows - 1);
-    const float* xr = x + (size_t)r * h;
+    const float4v* xr = reinterpret_cast<const float4v*>(x + (size_t)min(r0 + rl, rows - 1) * h);
     float sm = 0.0f;
-    for (int c = lane; c < h; c += 64) sm += xr[c];
+    for (int c = lane; c < h4; c += 64) {
+      const float4v v = xr[c];
+      sm += (v[0] + v[1]) + (v[2] + v[3]);
+    }
     const float mean = wave_sum(sm) / (float)h;
     float q = 0.0f;
-    for (int c = lane; c < h; c += 64) {
-      const float d = xr[c] - mean;
-      q += d * d;
+    for (int c = lane; c < h4; c += 64) {
+      const float4v d = xr[c] - mean;
+      q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
     }
     const float inv = rsqrtf(wave_sum(q) / (float)h + eps);
     if (lane == 0) {
@@ -216,29 +223,39 @@ __global__ __launch_bounds__(256) void final_kernel(int rows, int h, const float
     }
   }
   __syncthreads();
-  const int o = t & 63, rg = (t >> 6) * 4;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int c0 = 0; c0 < h; c0 += 256) {
-    const float f = fs[c0 + t];
-    for (int rl = 0; rl < 16; ++rl) {
-      const int r = min(r0 + rl, rows - 1);
-      xs[rl][t] = (x[(size_t)r * h + c0 + t] - mean_s[rl]) * inv_s[rl] * f;
-    }
-    __syncthreads();
-    for (int c = 0; c < 256; ++c) {
-      const float p = pt[(size_t)(c0 + c) * 64 + o];
+  float acc[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(xs[rg + i][c], p, acc[i]);
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  const int cw = wave * (h >> 2);  // this wave's first column
+  for (int cc = 0; cc < (h >> 2); cc += 64) {
+    const int c = cw + cc + lane;
+    const float f = fs[c];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      xs[wave][r][lane] = (x[(size_t)min(r0 + r, rows - 1) * h + c] - mean_s[r]) * inv_s[r] * f;
+    __syncthreads();
+    const float* pc = pt + (size_t)(cw + cc) * 64 + lane;
+    for (int j = 0; j < 64; j += 4) {
+      const float p0 = pc[(j + 0) * 64], p1 = pc[(j + 1) * 64], p2 = pc[(j + 2) * 64], p3 = pc[(j + 3) * 64];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float4v xv = *reinterpret_cast<const float4v*>(&xs[wave][r][j]);
+        acc[r] = __builtin_fmaf(xv[0], p0, __builtin_fmaf(xv[1], p1, __builtin_fmaf(xv[2], p2, __builtin_fmaf(xv[3], p3, acc[r]))));
+      }
     }
     __syncthreads();
   }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part[wave][r][lane] = acc[r];
+  __syncthreads();
   bool bad = false;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = r0 + rg + i;
+    const int rl = wave * 4 + i, r = r0 + rl;
+    const float v = (part[0][rl][lane] + part[1][rl][lane]) + (part[2][rl][lane] + part[3][rl][lane]);
     if (r < rows) {
-      out[(size_t)r * 64 + o] = acc[i];
-      bad |= !__builtin_isfinite(acc[i]);
+      out[(size_t)r * 64 + lane] = v;
+      bad |= !__builtin_isfinite(v);
     }
   }
   if (bad) atomicOr(flag, 1);
