@@ -39,6 +39,7 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -98,6 +99,73 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
             else
               *reinterpret_cast<half4*>(reinterpret_cast<f16*>(a.out) + o) =
                   half4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+          }
+      }
+    }
+  } else if constexpr (EPI == EPI_QKROPE) {
+    // the wave's TN = 4 column tiles are one 128-column head (c0 % 128 == 0);
+    // lanes l and l ^ 32 hold the two halves of a row
+    static_assert(TN == 4, "a wave spans one head");
+    const int H = a.N / 2;
+    const bool isk = c0 >= H;
+    const float* nw = isk ? a.nk : a.nq;
+    f16* dst = isk ? a.kout + (c0 - H) : reinterpret_cast<f16*>(a.out) + c0;
+    const int ld = isk ? a.ldk : a.ldo;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = r0 + i * 32 + l32;
+      float ss = 0.0f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ss = __builtin_fmaf(acc[i][j][e], acc[i][j][e], ss);
+      {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+        ss = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      }
+      const float inv = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
+      if (row < a.M) {
+        const float* cr = a.rcos + (size_t)row * 64;
+        const float* sr = a.rsin + (size_t)row * 64;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d = j * 32 + 8 * g + 4 * hsel;  // dims d .. d+3: pairs d/2, d/2 + 1
+            const floatx4 w = *reinterpret_cast<const floatx4*>(nw + d);
+            const floatx2 cs = *reinterpret_cast<const floatx2*>(cr + d / 2);
+            const floatx2 sn = *reinterpret_cast<const floatx2*>(sr + d / 2);
+            const float a0 = (acc[i][j][4 * g] * inv) * w[0], b0 = (acc[i][j][4 * g + 1] * inv) * w[1];
+            const float a1 = (acc[i][j][4 * g + 2] * inv) * w[2], b1 = (acc[i][j][4 * g + 3] * inv) * w[3];
+            *reinterpret_cast<half4*>(dst + (size_t)row * ld + d) =
+                half4{(f16)(a0 * cs[0] - b0 * sn[0]), (f16)(a0 * sn[0] + b0 * cs[0]), (f16)(a1 * cs[1] - b1 * sn[1]),
+                      (f16)(a1 * sn[1] + b1 * cs[1])};
+          }
+      }
+    }
+  } else if constexpr (EPI == EPI_VT) {
+    // output rows are V dims, columns are keys: key c goes to vt_pos(c),
+    // which keeps aligned runs of 4 together
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = r0 + i * 32 + l32;
+      if (row < a.M) {
+        f16* orow = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = c0 + j * 32 + 8 * g + 4 * hsel;
+            half4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (f16)(acc[i][j][4 * g + e] * a.oscale);
+            if (c + 3 < a.nvalid) {
+              *reinterpret_cast<half4*>(orow + vt_pos(c)) = v;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (c + e < a.nvalid) orow[vt_pos(c) + e] = v[e];
+            }
           }
       }
     }
@@ -231,13 +299,17 @@ __device__ __forceinline__ int dswz(int r) { return (r >> 2) & 3; }
 // waits and epilogue are covered by the other's MFMAs).
 template <int EPI, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
-  constexpr int TM = 4, TN = NW == 4 ? 4 : 2;  // 32 x 32 tiles per wave
-  constexpr int WTN = TN * 32;                 // wave tile columns
+  // 32 x 32 tiles per wave: 4 x 4 with 4 waves; 4 x 2 with 8, except the
+  // q/k-norm epilogue, whose waves span whole 128-column heads (2 x 4)
+  constexpr int TM = (NW == 8 && EPI == EPI_QKROPE) ? 2 : 4;
+  constexpr int TN = (NW == 4 || EPI == EPI_QKROPE) ? 4 : 2;
+  constexpr int WTM = TM * 32, WTN = TN * 32;  // wave tile
+  constexpr int NCOL = DBN / WTN;              // waves across the block's columns
   constexpr int NL = 16 / NW;                  // 16-byte loads per lane per operand per k-tile
   extern __shared__ __attribute__((aligned(16))) f16 smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
+  const int wm = wave / NCOL, wn = wave % NCOL;
   const int hsel = lane >> 5, l32 = lane & 31;
   const int K = a.K;
   const int KT = K / DBK;
@@ -316,7 +388,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
     const int c = kk * 2 + hsel;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int r = wm * 128 + i * 32 + l32;
+      const int r = wm * WTM + i * 32 + l32;
       af[b][i] = *reinterpret_cast<const half8*>(sa + (r * 4 + (c ^ dswz(r))) * 8);
     }
 #pragma unroll
@@ -408,9 +480,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
     }
     mma(1);
     if constexpr (ROWS)
-      epilogue_rows<EPI, TM, TN>(a, acc, m0 + wm * 128, n0 + wn * WTN, lane);
+      epilogue_rows<EPI, TM, TN>(a, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
     else
-      epilogue<EPI, TM, TN>(a, acc, m0 + wm * 128, n0 + wn * WTN, lane);
+      epilogue<EPI, TM, TN>(a, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
   }
   __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));  // no LDS-bound load outlives the block
 }
@@ -578,6 +650,14 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s) {
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, tile, s);
     case EPI_QKV: return launch_epi<EPI_QKV>(a, tile, s);
     case EPI_SWIGLU2: return launch_epi<EPI_SWIGLU2>(a, tile, s);
+    case EPI_QKROPE:
+      if (tile == 0) return launch_dma<EPI_QKROPE, 4>(a, s);
+      if (tile == 2) return launch_dma<EPI_QKROPE, 8>(a, s);
+      return hipErrorInvalidValue;
+    case EPI_VT:
+      if (tile == 0) return launch_dma<EPI_VT, 4>(a, s);
+      if (tile == 2) return launch_dma<EPI_VT, 8>(a, s);
+      return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }

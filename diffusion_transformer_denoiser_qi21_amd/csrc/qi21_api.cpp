@@ -65,6 +65,8 @@ struct Acts {
   f16* hid = nullptr;    // [cap][I]
   float* mods = nullptr; // [4H] tanh-ed modulation of the pass
   float* out = nullptr;  // [cap][64] velocity before the finite check
+  float* rc = nullptr;   // [cap][64] RoPE cos / sin of the pass's rows when
+  float* rs = nullptr;   // they come from several programs
 };
 
 struct Prog {
@@ -129,10 +131,10 @@ void dfree(qi21_model* m, void* p, size_t bytes) {
 // pair: the FFN input (in xn) and the SwiGLU hidden are kept as f16 pairs
 size_t acts_bytes(const qi21_geom& g, bool pair, int cap, size_t* parts) {
   const size_t H = g.hidden, I = g.inter, c = cap, f = pair ? 2 : 1;
-  const size_t p[9] = {c * H * 4, c * H * 2 * f, c * 2 * H * 2, H * c * 2, c * H * 2, c * H * 4, c * I * 2 * f,
-                       4 * H * 4, c * 64 * 4};
+  const size_t p[11] = {c * H * 4, c * H * 2 * f, c * 2 * H * 2, H * c * 2, c * H * 2, c * H * 4, c * I * 2 * f,
+                        4 * H * 4, c * 64 * 4, c * 64 * 4, c * 64 * 4};
   size_t t = 0;
-  for (int i = 0; i < 9; ++i) {
+  for (int i = 0; i < 11; ++i) {
     if (parts) parts[i] = p[i];
     t += p[i];
   }
@@ -140,11 +142,11 @@ size_t acts_bytes(const qi21_geom& g, bool pair, int cap, size_t* parts) {
 }
 
 void free_acts(qi21_model* m) {
-  size_t parts[9];
+  size_t parts[11];
   acts_bytes(m->g, m->o.ffn_pair != 0, m->acts.cap, parts);
-  void* ptrs[9] = {m->acts.x, m->acts.xn, m->acts.panel, m->acts.vt, m->acts.att,
-                   m->acts.y, m->acts.hid, m->acts.mods, m->acts.out};
-  for (int i = 0; i < 9; ++i) dfree(m, ptrs[i], parts[i]);
+  void* ptrs[11] = {m->acts.x, m->acts.xn, m->acts.panel, m->acts.vt, m->acts.att, m->acts.y,
+                    m->acts.hid, m->acts.mods, m->acts.out, m->acts.rc, m->acts.rs};
+  for (int i = 0; i < 11; ++i) dfree(m, ptrs[i], parts[i]);
   m->acts = Acts{};
 }
 
@@ -154,10 +156,10 @@ int ensure_acts(qi21_model* m, int rows, hipStream_t s) {
   if (m->acts.cap >= rows) return QI21_OK;
   free_acts(m);
   const int cap = (int)round_up((size_t)rows, 256);
-  size_t parts[9];
+  size_t parts[11];
   acts_bytes(m->g, m->o.ffn_pair != 0, cap, parts);
-  void* p[9];
-  for (int i = 0; i < 9; ++i) {
+  void* p[11];
+  for (int i = 0; i < 11; ++i) {
     p[i] = dalloc(m, parts[i]);
     if (!p[i]) {
       for (int j = 0; j < i; ++j) dfree(m, p[j], parts[j]);
@@ -177,6 +179,8 @@ int ensure_acts(qi21_model* m, int rows, hipStream_t s) {
   a.hid = (f16*)p[6];
   a.mods = (float*)p[7];
   a.out = (float*)p[8];
+  a.rc = (float*)p[9];
+  a.rs = (float*)p[10];
   return QI21_OK;
 }
 
@@ -295,23 +299,58 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
   const Guard gd = guards(m);
   Acts& a = m->acts;
   const int tile = m->o.gemm_tile;
+  // With the large-M GEMM the per-head q/k RMSNorm + RoPE runs in the q|k
+  // GEMM's epilogue and V^T comes from its own GEMM (Wv times the rows);
+  // otherwise the qkv GEMM writes q|k and V^T and qkrope follows.
+  const int tile_qk = tile >= 0 ? tile : qi21::gemm_pick_tile(rows, 2 * H, H);
+  const bool fused = tile_qk == 0 || tile_qk == 2;
+  const float* rcos = segs[0].rc;
+  const float* rsin = segs[0].rs;
+  if (fused && (segs.size() > 1 || segs[0].row0 != 0)) {  // one table for all rows of the pass
+    for (const Seg& sg : segs) {
+      HIP_OK(hipMemcpyAsync(a.rc + (size_t)sg.row0 * 64, sg.rc, (size_t)sg.rows * 64 * 4, hipMemcpyDeviceToDevice, s));
+      HIP_OK(hipMemcpyAsync(a.rs + (size_t)sg.row0 * 64, sg.rs, (size_t)sg.rows * 64 * 4, hipMemcpyDeviceToDevice, s));
+    }
+    rcos = a.rc;
+    rsin = a.rs;
+  }
   for (int l = 0; l < m->nb; ++l) {
     const bool last = l + 1 == m->nb;
-    {  // qkv: panel q|k (x 2^-qkv), V^T to the cache (prefill) or acts.vt
+    f16* vt = pre ? pre->vtc[l] : a.vt;
+    const int ldv = pre ? pre->ldc : a.cap;
+    if (fused) {
       Scope sc(m, C_QKV, s);
-      f16* vt = pre ? pre->vtc[l] : a.vt;
-      const int ldv = pre ? pre->ldc : a.cap;
-      HIP_OK(qi21::launch_gemm(qi21::EPI_QKV,
-                               gemm_args(rows, 3 * H, H, a.xn, H, m->wqkv[l], a.panel, 2 * H,
-                                         p2(gd.attn - gd.qkv), 1.0f, vt, ldv),
-                               tile, s));
-    }
-    {  // per-head RMSNorm + RoPE; the norm's eps follows the panel's guard
-      Scope sc(m, C_QKROPE, s);
-      const float eps = g.eps * p2(-2 * gd.qkv);
-      for (const Seg& sg : segs)
-        HIP_OK(qi21::launch_qkrope(sg.rows, nh, a.panel + (size_t)sg.row0 * 2 * H, 2 * H, m->nq[l], m->nk[l], sg.rc,
-                                   sg.rs, eps, pre ? pre->kc[l] : nullptr, H, s));
+      // q|k: normalised and rotated in the epilogue (scale-free); the
+      // accumulators carry 2^-attn, so the norm's eps does too
+      qi21::GemmArgs qk = gemm_args(rows, 2 * H, H, a.xn, H, m->wqkv[l], a.panel, 2 * H, 1.0f);
+      qk.nq = m->nq[l];
+      qk.nk = m->nk[l];
+      qk.rcos = rcos;
+      qk.rsin = rsin;
+      qk.eps = g.eps * p2(-2 * gd.attn);
+      qk.kout = pre ? pre->kc[l] : a.panel + H;
+      qk.ldk = pre ? H : 2 * H;
+      HIP_OK(qi21::launch_gemm(qi21::EPI_QKROPE, qk, tile_qk, s));
+      // V^T = Wv xn^T (x 2^-qkv) over the rows padded to whole tiles
+      qi21::GemmArgs v = gemm_args(H, (int)round_up((size_t)rows, 256), H, m->wqkv[l] + (size_t)2 * H * H, H, a.xn,
+                                   vt, ldv, p2(gd.attn - gd.qkv));
+      v.nvalid = rows;
+      HIP_OK(qi21::launch_gemm(qi21::EPI_VT, v, tile_qk, s));
+    } else {
+      {  // qkv: panel q|k (x 2^-qkv), V^T to the cache (prefill) or acts.vt
+        Scope sc(m, C_QKV, s);
+        HIP_OK(qi21::launch_gemm(qi21::EPI_QKV,
+                                 gemm_args(rows, 3 * H, H, a.xn, H, m->wqkv[l], a.panel, 2 * H,
+                                           p2(gd.attn - gd.qkv), 1.0f, vt, ldv),
+                                 tile, s));
+      }
+      {  // per-head RMSNorm + RoPE; the norm's eps follows the panel's guard
+        Scope sc(m, C_QKROPE, s);
+        const float eps = g.eps * p2(-2 * gd.qkv);
+        for (const Seg& sg : segs)
+          HIP_OK(qi21::launch_qkrope(sg.rows, nh, a.panel + (size_t)sg.row0 * 2 * H, 2 * H, m->nq[l], m->nk[l], sg.rc,
+                                     sg.rs, eps, pre ? pre->kc[l] : nullptr, H, s));
+      }
     }
     if (pre && last) break;  // only this layer's K/V leave a prefill
     {
@@ -737,6 +776,41 @@ int qi21_op_gemm_pair(int epi, int M, int N, int K, const void* A, int lda, cons
   g_err.clear();
   if (epi == QI21_EPI_QKV) return fail(QI21_EINVAL, "the pair GEMM has no qkv epilogue");
   return op_gemm(epi, M, N, K, 2 * K, A, lda, W, out, ldo, nullptr, 0, oscale, inscale, tile, stream);
+}
+
+int qi21_op_qk_gemm(int M, int H, const void* A, int lda, const void* W, void* q_out, int ldq, void* k_out, int ldk,
+                    const float* norm_q, const float* norm_k, const float* cos, const float* sin, float eps, int tile,
+                    void* stream) {
+  g_err.clear();
+  if (M < 1 || H < 128 || H % 128 || lda % 8 || lda < H || ldq % 4 || ldk % 4 || ldq < H || ldk < H)
+    return fail(QI21_EINVAL, "qk gemm M %d H %d lda %d ldq %d ldk %d", M, H, lda, ldq, ldk);
+  if (!A || !W || !q_out || !k_out || !norm_q || !norm_k || !cos || !sin) return fail(QI21_EINVAL, "qk gemm pointer NULL");
+  if (tile == -1) tile = 2;
+  if (tile != 0 && tile != 2) return fail(QI21_EINVAL, "qk gemm tile %d (0 or 2)", tile);
+  qi21::GemmArgs a = gemm_args(M, 2 * H, H, (const f16*)A, lda, (const f16*)W, q_out, ldq, 1.0f);
+  a.nq = norm_q;
+  a.nk = norm_k;
+  a.rcos = cos;
+  a.rsin = sin;
+  a.eps = eps;
+  a.kout = (f16*)k_out;
+  a.ldk = ldk;
+  HIP_OK(qi21::launch_gemm(qi21::EPI_QKROPE, a, tile, (hipStream_t)stream));
+  return QI21_OK;
+}
+
+int qi21_op_vt_gemm(int H, int nkeys, int K, const void* Wv, int lda, const void* X, void* out, int ldo, float oscale,
+                    int tile, void* stream) {
+  g_err.clear();
+  if (H < 1 || nkeys < 1 || K < 64 || K % 64 || lda % 8 || lda < K || ldo % 4 || (size_t)ldo < round_up(nkeys, 16))
+    return fail(QI21_EINVAL, "vt gemm H %d nkeys %d K %d lda %d ldo %d", H, nkeys, K, lda, ldo);
+  if (!Wv || !X || !out) return fail(QI21_EINVAL, "vt gemm pointer NULL");
+  if (tile == -1) tile = 2;
+  if (tile != 0 && tile != 2) return fail(QI21_EINVAL, "vt gemm tile %d (0 or 2)", tile);
+  qi21::GemmArgs a = gemm_args(H, (int)round_up(nkeys, 256), K, (const f16*)Wv, lda, (const f16*)X, out, ldo, oscale);
+  a.nvalid = nkeys;
+  HIP_OK(qi21::launch_gemm(qi21::EPI_VT, a, tile, (hipStream_t)stream));
+  return QI21_OK;
 }
 
 int qi21_op_flash(int nq, int heads, const void* q, int ldq, const void* k1, int ldk1, const void* vt1, int ldvt1,

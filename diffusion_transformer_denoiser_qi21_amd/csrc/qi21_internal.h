@@ -18,7 +18,7 @@ constexpr int wait_imm(int vm, int lgkm) {
   return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm & 0xF) << 8);
 }
 
-enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 4 };
+enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 4, EPI_QKROPE = 5, EPI_VT = 6 };
 
 // C = A * W^T over f16 operands with f32 accumulation.
 //   A: [M][lda] f16 (K contiguous), W: [N][kw] f16 (kw contiguous); column
@@ -31,6 +31,15 @@ enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 
 //               columns = silu(g*inscale) * (u*inscale) * oscale
 //   EPI_SWIGLU2: as EPI_SWIGLU, the value h written as the pair
 //               out[r][c] = f16(h), out[r][N/2 + c] = f16(h - f16(h))
+//   EPI_QKROPE: N = 2H, W = the q then k projection rows; per row and
+//               128-column head: RMSNorm of the accumulators (weights nq for
+//               q heads, nk for k heads, eps in the accumulators' scale),
+//               then interleaved-pair RoPE with rcos / rsin [M][64]; q heads
+//               to out f16 [M][ldo], k heads to kout f16 [M][ldk] (column
+//               c - H).  Large-M kernels only (tile 0 / 2).
+//   EPI_VT:     out f16 [M][ldo] = acc * oscale with output column c stored at
+//               vt_pos(c) and only columns c < nvalid (V^T from Wv and the
+//               rows as the W operand).  Large-M kernels only.
 //   EPI_QKV:    columns [0, 2H) -> out f16 [M][ldo] (q|k), columns [2H, 3H)
 //               -> out2 f16 transposed, out2[c - 2H][row] with leading
 //               dimension ld2 (V^T), both * oscale; H = N/3.
@@ -44,6 +53,13 @@ struct GemmArgs {
   void* out; int ldo;
   f16* out2; int ld2;
   float oscale, inscale;
+  // EPI_QKROPE
+  const float* nq = nullptr; const float* nk = nullptr;
+  const float* rcos = nullptr; const float* rsin = nullptr;
+  float eps = 0.0f;
+  f16* kout = nullptr; int ldk = 0;
+  // EPI_VT
+  int nvalid = 0;
 };
 hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s);
 // the tile a launch would pick (0: 256x256, 1: 128x128, ...)

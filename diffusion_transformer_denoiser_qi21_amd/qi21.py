@@ -70,6 +70,9 @@ _SIGS = {
                                C.c_int, vp]),
     "qi21_op_gemm_pair": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, f32, f32, C.c_int,
                                     vp]),
+    "qi21_op_qk_gemm": (C.c_int, [C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, C.c_int, vp, vp, vp, vp, f32,
+                                  C.c_int, vp]),
+    "qi21_op_vt_gemm": (C.c_int, [C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, f32, C.c_int, vp]),
     "qi21_op_flash": (C.c_int, [C.c_int, C.c_int, vp, C.c_int, vp, C.c_int, vp, C.c_int, C.c_int, vp, C.c_int, vp,
                                 C.c_int, C.c_int, vp, vp, C.c_int, f32, vp]),
     "qi21_op_rowop": (C.c_int, [C.c_int, C.c_int, C.c_int, vp, vp, vp, vp, C.c_int, C.c_int, f32, f32, vp]),
@@ -237,6 +240,15 @@ def qi21_op_gemm(epi, M, N, K, A, lda, W, out, ldo, out2=None, ld2=0, oscale=1.0
 def qi21_op_gemm_pair(epi, M, N, K, A, lda, W, out, ldo, oscale=1.0, inscale=1.0, tile=-1, stream=None):
     _check(lib().qi21_op_gemm_pair(epi, M, N, K, _p(A), lda, _p(W), _p(out), ldo, oscale, inscale, tile,
                                    _stream(stream)))
+
+
+def qi21_op_qk_gemm(M, H, A, lda, W, q_out, ldq, k_out, ldk, norm_q, norm_k, cos, sin, eps, tile=-1, stream=None):
+    _check(lib().qi21_op_qk_gemm(M, H, _p(A), lda, _p(W), _p(q_out), ldq, _p(k_out), ldk, _p(norm_q), _p(norm_k),
+                                 _p(cos), _p(sin), eps, tile, _stream(stream)))
+
+
+def qi21_op_vt_gemm(H, nkeys, K, Wv, lda, X, out, ldo, oscale=1.0, tile=-1, stream=None):
+    _check(lib().qi21_op_vt_gemm(H, nkeys, K, _p(Wv), lda, _p(X), _p(out), ldo, oscale, tile, _stream(stream)))
 
 
 def qi21_op_flash(nq, heads, q, ldq, k1, ldk1, vt1, ldvt1, n1, k2, ldk2, vt2, ldvt2, n2, vis, out, ldo, oscale=1.0,

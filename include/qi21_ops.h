@@ -50,6 +50,32 @@ int qi21_op_gemm(int epi, int M, int N, int K, const void* A, int lda, const voi
 int qi21_op_gemm_pair(int epi, int M, int N, int K, const void* A, int lda, const void* W, void* out, int ldo,
                       float oscale, float inscale, int tile, void* stream);
 
+/* The q|k projection with the per-head RMSNorm + RoPE in its epilogue
+ * ([QI] block_cpu, qk_norm_rope: the fused form of the QKV GEMM's q|k
+ * columns followed by qi21_op_qkrope).  A f16 [M][lda] (H columns), W f16
+ * [2H][H] = to_q rows then to_k rows.  For every row and 128-column head
+ * the f32 accumulators a are normalised, a * rsqrt(mean(a^2) + eps) *
+ * norm_q / norm_k [128] (eps in the accumulators' scale), then pairs
+ * (2j, 2j+1) are rotated by cos / sin [M][64] (row-major, column j); q
+ * heads go to q_out f16 [M][ldq], k heads to k_out f16 [M][ldk], both at
+ * column head*128.  Requires M >= 1, H % 128 == 0, lda % 8 == 0, lda >= H,
+ * ldq, ldk >= H and % 4 == 0, 16-byte aligned pointers.  tile: -1 or 2 (8
+ * waves), 0 (4 waves). */
+int qi21_op_qk_gemm(int M, int H, const void* A, int lda, const void* W, void* q_out, int ldq, void* k_out, int ldk,
+                    const float* norm_q, const float* norm_k, const float* cos, const float* sin, float eps, int tile,
+                    void* stream);
+
+/* V^T of nkeys rows: out[d][vt_pos(j)] = oscale * sum_k Wv[d][k] X[j][k]
+ * for d < H, j < nkeys, where vt_pos swaps bits 2 and 3 of j (the key
+ * order qi21_op_flash reads); other columns are not written.  Wv f16
+ * [H][lda], X f16 rows of K columns (row stride K); X must hold
+ * round_up(nkeys, 256) readable rows (the kernel reads whole 256-row
+ * tiles, and rows past nkeys only feed unwritten columns).  Requires
+ * K % 64 == 0, lda % 8 == 0, lda >= K, ldo % 4 == 0, ldo >=
+ * round_up(nkeys, 16).  tile: -1 or 2, or 0. */
+int qi21_op_vt_gemm(int H, int nkeys, int K, const void* Wv, int lda, const void* X, void* out, int ldo, float oscale,
+                    int tile, void* stream);
+
 /* Attention, head_dim 128 ([QI] attention; [WG] qi_flash): per head h,
  * out[i][h*128 + d] = oscale * sum_j softmax_j(q_i . k_j / sqrt(128)) v_j[d]
  * over keys j < min(n1 + n2, vis[i]) (vis == NULL: all keys).  Keys

@@ -334,6 +334,58 @@ def test_qkrope(rows, kdst):
         assert np.array_equal(got[:, 2 * H:], panel[:, 2 * H:])
 
 
+@pytest.mark.parametrize("tile", [0, 2])
+@pytest.mark.parametrize("M", [1, 77, 300, 1600])
+def test_qk_gemm_fused_norm_rope(M, tile):
+    """q|k projection with the per-head RMSNorm + RoPE in the epilogue vs
+    the oracle's lin then qk_norm_rope on the same f16 inputs"""
+    q = Q()
+    heads, hd = 2, 128
+    H = heads * hd
+    lay = O.Layout([("text", 7), ("image", 40, 41)])
+    pos = lay.positions()[:M]
+    c, s = O.rope_tables(pos)
+    A = f16_host(10, 1, (M, H), 0.25)  # the attention input carries 2^-2
+    W = f16_host(10, 2, (2 * H, H), 0.05)
+    wq = inputs.host_array(10, 3, (hd,), 0.02, mean=1.0)
+    wk = inputs.host_array(10, 4, (hd,), 0.02, mean=1.0)
+    eps = 1e-6 * 2.0 ** -4
+    ldq, ldk = H + 64, H
+    qo = torch.zeros(M, ldq, device="cuda", dtype=torch.float16)
+    ko = torch.zeros(M, ldk, device="cuda", dtype=torch.float16)
+    q.qi21_op_qk_gemm(M, H, dev(A, torch.float16), H, dev(W, torch.float16), qo, ldq, ko, ldk, dev(wq), dev(wk),
+                      dev(c), dev(s), eps, tile)
+    sync()
+    want_q = O.qk_norm_rope(O.lin(A, W[:H]), wq, c, s, heads, hd, eps)
+    want_k = O.qk_norm_rope(O.lin(A, W[H:]), wk, c, s, heads, hd, eps)
+    got_q = qo.float().cpu().numpy()
+    assert rel(got_q[:, :H], want_q) < F16_TOL
+    assert rel(ko.float().cpu().numpy(), want_k) < F16_TOL
+    assert np.all(got_q[:, H:] == 0)  # nothing past the q heads
+
+
+@pytest.mark.parametrize("tile", [0, 2])
+@pytest.mark.parametrize("nkeys", [1, 18, 300, 4118])
+def test_vt_gemm_key_order_and_bound(nkeys, tile):
+    """V^T = Wv X^T with key j at vt_pos(j), only keys < nkeys written"""
+    q = Q()
+    H, K = 384, 256
+    rows = ((nkeys + 255) // 256) * 256
+    X = np.zeros((rows, K), np.float32)
+    X[:nkeys] = f16_host(11, 1, (nkeys, K), 1.0)
+    Wv = f16_host(11, 2, (H, K), 0.05)
+    ldo = ((nkeys + 63) // 64) * 64 + 8
+    out = torch.zeros(H, ldo, device="cuda", dtype=torch.float16)
+    q.qi21_op_vt_gemm(H, nkeys, K, dev(Wv, torch.float16), K, dev(X, torch.float16), out, ldo, 0.5, tile)
+    sync()
+    got = out.float().cpu().numpy()
+    want = (O.lin(X[:nkeys], Wv) * np.float32(0.5)).T
+    cols = vt_pos(np.arange(nkeys))
+    assert rel(got[:, cols], want) < F16_TOL
+    rest = np.setdiff1d(np.arange(ldo), cols)
+    assert np.all(got[:, rest] == 0)
+
+
 @pytest.mark.parametrize("h", [256, 4096])
 @pytest.mark.parametrize("rows", [1, 100, 300])
 def test_embed(rows, h):
