@@ -82,7 +82,26 @@ __device__ __forceinline__ int vt_pos(int r) { return (r & ~12) | ((r & 4) << 1)
 template <int EPI, int TM, int TN>
 __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)[TM][TN], int r0, int c0, int lane) {
   const int hsel = lane >> 5, l32 = lane & 31;
-  if constexpr (EPI == EPI_F32 || EPI == EPI_F16) {
+  if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = r0 + i * 32 + l32;
+      if (row < a.M) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = c0 + j * 32 + 8 * g + 4 * hsel;
+            floatx4* xp = reinterpret_cast<floatx4*>(reinterpret_cast<float*>(a.out) + (size_t)row * a.ldo + c);
+            const floatx4 gt = *reinterpret_cast<const floatx4*>(a.gate + c);
+            floatx4 x = *xp;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(gt[e], acc[i][j][4 * g + e] * a.oscale, x[e]);
+            *xp = x;
+          }
+      }
+    }
+  } else if constexpr (EPI == EPI_F32 || EPI == EPI_F16) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int row = r0 + i * 32 + l32;
@@ -205,7 +224,22 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, floatx16 (&acc)[TM][
   const int hsel = lane >> 5, l32 = lane & 31;
   const int rbase = r0 + 4 * hsel;
   const int cbase = c0 + l32;
-  if constexpr (EPI == EPI_F32 || EPI == EPI_F16) {
+  if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const float gt = a.gate[cbase + j * 32];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
+          if (row < a.M) {
+            float* xp = reinterpret_cast<float*>(a.out) + (size_t)row * a.ldo + cbase + j * 32;
+            *xp = __builtin_fmaf(gt, acc[i][j][e] * a.oscale, *xp);
+          }
+        }
+    }
+  } else if constexpr (EPI == EPI_F32 || EPI == EPI_F16) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -650,6 +684,7 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s) {
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, tile, s);
     case EPI_QKV: return launch_epi<EPI_QKV>(a, tile, s);
     case EPI_SWIGLU2: return launch_epi<EPI_SWIGLU2>(a, tile, s);
+    case EPI_RESID: return launch_epi<EPI_RESID>(a, tile, s);
     case EPI_QKROPE:
       if (tile == 0) return launch_dma<EPI_QKROPE, 4>(a, s);
       if (tile == 2) return launch_dma<EPI_QKROPE, 8>(a, s);

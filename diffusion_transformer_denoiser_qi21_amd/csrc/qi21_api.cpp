@@ -61,7 +61,6 @@ struct Acts {
   f16* panel = nullptr;  // [cap][2H] q | k
   f16* vt = nullptr;     // [H][cap] V^T of the pass's own rows
   f16* att = nullptr;    // [cap][H]
-  float* y = nullptr;    // [cap][H]
   f16* hid = nullptr;    // [cap][I]
   float* mods = nullptr; // [4H] tanh-ed modulation of the pass
   float* out = nullptr;  // [cap][64] velocity before the finite check
@@ -131,7 +130,8 @@ void dfree(qi21_model* m, void* p, size_t bytes) {
 // pair: the FFN input (in xn) and the SwiGLU hidden are kept as f16 pairs
 size_t acts_bytes(const qi21_geom& g, bool pair, int cap, size_t* parts) {
   const size_t H = g.hidden, I = g.inter, c = cap, f = pair ? 2 : 1;
-  const size_t p[11] = {c * H * 4, c * H * 2 * f, c * 2 * H * 2, H * c * 2, c * H * 2, c * H * 4, c * I * 2 * f,
+  // slot 5 is empty: the gated residuals run in the O / down GEMM epilogues
+  const size_t p[11] = {c * H * 4, c * H * 2 * f, c * 2 * H * 2, H * c * 2, c * H * 2, 0, c * I * 2 * f,
                         4 * H * 4, c * 64 * 4, c * 64 * 4, c * 64 * 4};
   size_t t = 0;
   for (int i = 0; i < 11; ++i) {
@@ -144,7 +144,7 @@ size_t acts_bytes(const qi21_geom& g, bool pair, int cap, size_t* parts) {
 void free_acts(qi21_model* m) {
   size_t parts[11];
   acts_bytes(m->g, m->o.ffn_pair != 0, m->acts.cap, parts);
-  void* ptrs[11] = {m->acts.x, m->acts.xn, m->acts.panel, m->acts.vt, m->acts.att, m->acts.y,
+  void* ptrs[11] = {m->acts.x, m->acts.xn, m->acts.panel, m->acts.vt, m->acts.att, nullptr,
                     m->acts.hid, m->acts.mods, m->acts.out, m->acts.rc, m->acts.rs};
   for (int i = 0; i < 11; ++i) dfree(m, ptrs[i], parts[i]);
   m->acts = Acts{};
@@ -160,6 +160,10 @@ int ensure_acts(qi21_model* m, int rows, hipStream_t s) {
   acts_bytes(m->g, m->o.ffn_pair != 0, cap, parts);
   void* p[11];
   for (int i = 0; i < 11; ++i) {
+    if (!parts[i]) {
+      p[i] = nullptr;
+      continue;
+    }
     p[i] = dalloc(m, parts[i]);
     if (!p[i]) {
       for (int j = 0; j < i; ++j) dfree(m, p[j], parts[j]);
@@ -175,7 +179,6 @@ int ensure_acts(qi21_model* m, int rows, hipStream_t s) {
   a.panel = (f16*)p[2];
   a.vt = (f16*)p[3];
   a.att = (f16*)p[4];
-  a.y = (float*)p[5];
   a.hid = (f16*)p[6];
   a.mods = (float*)p[7];
   a.out = (float*)p[8];
@@ -388,16 +391,18 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
         HIP_OK(qi21::launch_flash(f, s));
       }
     }
-    {
+    {  // x += tanh(g1) (att Wo^T) in the O GEMM's epilogue
       Scope sc(m, C_O, s);
-      HIP_OK(qi21::launch_gemm(qi21::EPI_F32, gemm_args(rows, H, H, a.att, H, m->wo[l], a.y, H, p2(gd.ao)), tile, s));
+      qi21::GemmArgs o = gemm_args(rows, H, H, a.att, H, m->wo[l], a.x, H, p2(gd.ao));
+      o.gate = a.mods + H;
+      HIP_OK(qi21::launch_gemm(qi21::EPI_RESID, o, tile, s));
     }
     // with ffn_pair the FFN input and the hidden are f16 (hi, lo) pairs in
     // rows of 2H / 2I and both GEMMs run over K doubled, each W row twice
     const int pf = m->o.ffn_pair ? 2 : 1;
-    {
+    {  // xn = LN(x)(1 + s2)
       Scope sc(m, C_ROW, s);
-      HIP_OK(qi21::launch_rowop(rows, H, pf == 2 ? 7 : 3, a.x, a.y, a.xn, a.mods, H, 2 * H, g.eps, p2(-gd.ffn), s));
+      HIP_OK(qi21::launch_rowop(rows, H, pf == 2 ? 6 : 2, a.x, nullptr, a.xn, a.mods, 0, 2 * H, g.eps, p2(-gd.ffn), s));
     }
     {
       Scope sc(m, C_W13, s);
@@ -406,18 +411,16 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
       ga.kw = H;
       HIP_OK(qi21::launch_gemm(pf == 2 ? qi21::EPI_SWIGLU2 : qi21::EPI_SWIGLU, ga, tile, s));
     }
-    {
+    {  // x += tanh(g2) (hid W2^T) in the down GEMM's epilogue
       Scope sc(m, C_W2, s);
-      qi21::GemmArgs ga = gemm_args(rows, H, pf * I, a.hid, pf * I, m->w2[l], a.y, H, p2(gd.hid));
+      qi21::GemmArgs ga = gemm_args(rows, H, pf * I, a.hid, pf * I, m->w2[l], a.x, H, p2(gd.hid));
       ga.kw = I;
-      HIP_OK(qi21::launch_gemm(qi21::EPI_F32, ga, tile, s));
+      ga.gate = a.mods + 3 * H;
+      HIP_OK(qi21::launch_gemm(qi21::EPI_RESID, ga, tile, s));
     }
-    {
+    if (!last) {  // the next block's xn = LN(x)(1 + s1)
       Scope sc(m, C_ROW, s);
-      if (last)
-        HIP_OK(qi21::launch_rowop(rows, H, 1, a.x, a.y, a.xn, a.mods, 3 * H, 0, g.eps, 1.0f, s));
-      else
-        HIP_OK(qi21::launch_rowop(rows, H, 3, a.x, a.y, a.xn, a.mods, 3 * H, 0, g.eps, p2(-gd.attn), s));
+      HIP_OK(qi21::launch_rowop(rows, H, 2, a.x, nullptr, a.xn, a.mods, 0, 0, g.eps, p2(-gd.attn), s));
     }
   }
   return QI21_OK;
@@ -632,7 +635,7 @@ int qi21_prefill(qi21_model* m, uint64_t key, int lp, int n, const float* x, con
   const Guard gd = guards(m);
   HIP_OK(qi21::launch_mods((int)H, mods0, a.mods, s));
   HIP_OK(hipMemcpyAsync(a.x, x, (size_t)lp * H * 4, hipMemcpyDeviceToDevice, s));
-  HIP_OK(qi21::launch_rowop(lp, (int)H, 2, a.x, a.y, a.xn, a.mods, 0, 0, m->g.eps, p2(-gd.attn), s));
+  HIP_OK(qi21::launch_rowop(lp, (int)H, 2, a.x, nullptr, a.xn, a.mods, 0, 0, m->g.eps, p2(-gd.attn), s));
   std::vector<Seg> segs{Seg{0, lp, nullptr, rope_p_cos, rope_p_sin}};
   rc = run_blocks(m, lp, segs, &p, vis, s);
   if (rc == QI21_OK) rc = sync_stream(s);
@@ -684,7 +687,7 @@ int qi21_step_batch(qi21_model* m, int nprog, const uint64_t* keys, const float*
   }
   {
     Scope sc(m, C_ROW, s);
-    HIP_OK(qi21::launch_rowop(rows, H, 2, a.x, a.y, a.xn, a.mods, 0, 0, m->g.eps, p2(-gd.attn), s));
+    HIP_OK(qi21::launch_rowop(rows, H, 2, a.x, nullptr, a.xn, a.mods, 0, 0, m->g.eps, p2(-gd.attn), s));
   }
   rc = run_blocks(m, rows, segs, nullptr, nullptr, s);
   if (rc) {
@@ -776,6 +779,22 @@ int qi21_op_gemm_pair(int epi, int M, int N, int K, const void* A, int lda, cons
   g_err.clear();
   if (epi == QI21_EPI_QKV) return fail(QI21_EINVAL, "the pair GEMM has no qkv epilogue");
   return op_gemm(epi, M, N, K, 2 * K, A, lda, W, out, ldo, nullptr, 0, oscale, inscale, tile, stream);
+}
+
+int qi21_op_gemm_resid(int M, int N, int K, int kw, const void* A, int lda, const void* W, float* x, int ldx,
+                       const float* gate, float oscale, int tile, void* stream) {
+  g_err.clear();
+  if (kw < 64 || kw % 64 || (K != kw && K != 2 * kw)) return fail(QI21_EINVAL, "resid gemm K %d kw %d", K, kw);
+  if (!gate) return fail(QI21_EINVAL, "resid gemm gate is NULL");
+  if (M < 1 || N < 128 || N % 128 || lda % 8 || lda < K || ldx % 4 || ldx < N)
+    return fail(QI21_EINVAL, "resid gemm M %d N %d lda %d ldx %d", M, N, lda, ldx);
+  if (!A || !W || !x) return fail(QI21_EINVAL, "resid gemm pointer is NULL");
+  if (tile < -1 || tile > 2 || (tile != 1 && tile != -1 && N % 256)) return fail(QI21_EINVAL, "tile %d for N %d", tile, N);
+  qi21::GemmArgs a = gemm_args(M, N, K, (const f16*)A, lda, (const f16*)W, x, ldx, oscale);
+  a.kw = kw;
+  a.gate = gate;
+  HIP_OK(qi21::launch_gemm(qi21::EPI_RESID, a, tile, (hipStream_t)stream));
+  return QI21_OK;
 }
 
 int qi21_op_qk_gemm(int M, int H, const void* A, int lda, const void* W, void* q_out, int ldq, void* k_out, int ldk,

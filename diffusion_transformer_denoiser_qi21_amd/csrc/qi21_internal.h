@@ -18,7 +18,8 @@ constexpr int wait_imm(int vm, int lgkm) {
   return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm & 0xF) << 8);
 }
 
-enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 4, EPI_QKROPE = 5, EPI_VT = 6 };
+enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 4, EPI_QKROPE = 5, EPI_VT = 6,
+           EPI_RESID = 7 };
 
 // C = A * W^T over f16 operands with f32 accumulation.
 //   A: [M][lda] f16 (K contiguous), W: [N][kw] f16 (kw contiguous); column
@@ -40,6 +41,8 @@ enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 
 //   EPI_VT:     out f16 [M][ldo] = acc * oscale with output column c stored at
 //               vt_pos(c) and only columns c < nvalid (V^T from Wv and the
 //               rows as the W operand).  Large-M kernels only.
+//   EPI_RESID:  out f32 [M][ldo] += gate[c] * acc * oscale (the gated residual
+//               of a block's branch, x += tanh(g) y, in place)
 //   EPI_QKV:    columns [0, 2H) -> out f16 [M][ldo] (q|k), columns [2H, 3H)
 //               -> out2 f16 transposed, out2[c - 2H][row] with leading
 //               dimension ld2 (V^T), both * oscale; H = N/3.
@@ -60,6 +63,8 @@ struct GemmArgs {
   f16* kout = nullptr; int ldk = 0;
   // EPI_VT
   int nvalid = 0;
+  // EPI_RESID
+  const float* gate = nullptr;
 };
 hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s);
 // the tile a launch would pick (0: 256x256, 1: 128x128, ...)

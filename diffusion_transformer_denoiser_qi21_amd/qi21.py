@@ -70,6 +70,8 @@ _SIGS = {
                                C.c_int, vp]),
     "qi21_op_gemm_pair": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, f32, f32, C.c_int,
                                     vp]),
+    "qi21_op_gemm_resid": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, f32,
+                                     C.c_int, vp]),
     "qi21_op_qk_gemm": (C.c_int, [C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, C.c_int, vp, vp, vp, vp, f32,
                                   C.c_int, vp]),
     "qi21_op_vt_gemm": (C.c_int, [C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, f32, C.c_int, vp]),
@@ -240,6 +242,11 @@ def qi21_op_gemm(epi, M, N, K, A, lda, W, out, ldo, out2=None, ld2=0, oscale=1.0
 def qi21_op_gemm_pair(epi, M, N, K, A, lda, W, out, ldo, oscale=1.0, inscale=1.0, tile=-1, stream=None):
     _check(lib().qi21_op_gemm_pair(epi, M, N, K, _p(A), lda, _p(W), _p(out), ldo, oscale, inscale, tile,
                                    _stream(stream)))
+
+
+def qi21_op_gemm_resid(M, N, K, kw, A, lda, W, x, ldx, gate, oscale=1.0, tile=-1, stream=None):
+    _check(lib().qi21_op_gemm_resid(M, N, K, kw, _p(A), lda, _p(W), _p(x), ldx, _p(gate), oscale, tile,
+                                    _stream(stream)))
 
 
 def qi21_op_qk_gemm(M, H, A, lda, W, q_out, ldq, k_out, ldk, norm_q, norm_k, cos, sin, eps, tile=-1, stream=None):

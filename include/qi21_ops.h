@@ -50,6 +50,16 @@ int qi21_op_gemm(int epi, int M, int N, int K, const void* A, int lda, const voi
 int qi21_op_gemm_pair(int epi, int M, int N, int K, const void* A, int lda, const void* W, void* out, int ldo,
                       float oscale, float inscale, int tile, void* stream);
 
+/* The gated residual of a block branch in the GEMM's epilogue ([QI]
+ * gated_add): x f32 [M][ldx] += gate[c] * oscale * sum_k A[m][k] W[c][k % kw]
+ * in place, for c < N.  A f16 [M][lda] with K columns read; W f16 [N][kw];
+ * K == kw, or K == 2 kw for an A of f16 (hi, lo) pairs (the ffn_pair option
+ * of qi21.h).  gate f32 [N], already tanh-ed.  Requires M >= 1, N % 128 ==
+ * 0, kw % 64 == 0, lda % 8 == 0, lda >= K, ldx % 4 == 0, ldx >= N.  tile as
+ * qi21_op_gemm. */
+int qi21_op_gemm_resid(int M, int N, int K, int kw, const void* A, int lda, const void* W, float* x, int ldx,
+                       const float* gate, float oscale, int tile, void* stream);
+
 /* The q|k projection with the per-head RMSNorm + RoPE in its epilogue
  * ([QI] block_cpu, qk_norm_rope: the fused form of the QKV GEMM's q|k
  * columns followed by qi21_op_qkrope).  A f16 [M][lda] (H columns), W f16

@@ -334,6 +334,32 @@ def test_qkrope(rows, kdst):
         assert np.array_equal(got[:, 2 * H:], panel[:, 2 * H:])
 
 
+@pytest.mark.parametrize("pair", [False, True])
+@pytest.mark.parametrize("tile", [-1, 0, 1, 2])
+@pytest.mark.parametrize("M", [1, 77, 1600])
+def test_gemm_gated_residual(M, tile, pair):
+    """x += gate * (A W^T) * oscale in the GEMM epilogue ([QI] gated_add)"""
+    q = Q()
+    N, K = 768, 512
+    x = inputs.host_array(12, 1, (M, N), 1.0)
+    gate = np.tanh(inputs.host_array(12, 2, (N,), 0.1)).astype(np.float32)
+    W = f16_host(12, 3, (N, K), 0.05)
+    if pair:
+        A32 = inputs.host_array(12, 4, (M, K), 1.0)
+        hi, lo = _pair(A32)
+        A = np.concatenate([hi, lo], axis=1)
+        prod = A32.astype(np.float64) @ W.astype(np.float64).T
+    else:
+        A = f16_host(12, 4, (M, K), 1.0)
+        prod = A.astype(np.float64) @ W.astype(np.float64).T
+    dx = dev(x)
+    q.qi21_op_gemm_resid(M, N, A.shape[1], K, dev(A, torch.float16), A.shape[1], dev(W, torch.float16), dx, N,
+                         dev(gate), 0.5, tile)
+    sync()
+    want = x.astype(np.float64) + gate.astype(np.float64) * prod * 0.5
+    assert rel(dx.cpu().numpy(), want) < (PAIR_TOL if pair else F32_TOL * 10)
+
+
 @pytest.mark.parametrize("tile", [0, 2])
 @pytest.mark.parametrize("M", [1, 77, 300, 1600])
 def test_qk_gemm_fused_norm_rope(M, tile):
