@@ -25,6 +25,10 @@ from typing import List, Tuple
 BLOCK_NAMES = ("to_q", "to_k", "to_v", "to_out", "gate", "up", "down", "norm_q", "norm_k")
 TID_IMG_IN, TID_PROJ_OUT, TID_MODS0 = 1, 2, 3
 TID_PREFIX_X, TID_TOK, TID_MODS, TID_FINAL_SCALE = 10, 11, 12, 13
+# time path (temb MLP, shared modulation, final-norm scale) and the txt_in front
+TID_T_LIN1, TID_T_LIN2, TID_MODULATION, TID_NORM_OUT = 20, 21, 22, 23
+TID_TXT_NORM, TID_TXT_IN1, TID_TXT_IN2, TID_TXT_FEATS = 24, 25, 26, 27
+TEMB_IN = 256  # the sinusoidal timestep embedding's width (128 cos + 128 sin)
 W_SIGMA, NORM_SIGMA, ROW_SIGMA, MOD_SIGMA = 0.02, 0.02, 1.0, 0.1
 
 

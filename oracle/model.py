@@ -8,9 +8,9 @@ from __future__ import annotations
 import numpy as np
 
 import inputs
-from inputs.configs import (BLOCK_NAMES, MOD_SIGMA, NORM_SIGMA, ROW_SIGMA, TID_FINAL_SCALE,
-                            TID_IMG_IN, TID_MODS, TID_MODS0, TID_PREFIX_X, TID_PROJ_OUT,
-                            TID_TOK, W_SIGMA, block_tid)
+from inputs.configs import (BLOCK_NAMES, MOD_SIGMA, NORM_SIGMA, ROW_SIGMA, TEMB_IN, TID_FINAL_SCALE,
+                            TID_IMG_IN, TID_MODS, TID_MODS0, TID_MODULATION, TID_NORM_OUT, TID_PREFIX_X,
+                            TID_PROJ_OUT, TID_T_LIN1, TID_T_LIN2, TID_TOK, W_SIGMA, block_tid)
 
 from .qi21_oracle import Geometry
 
@@ -37,6 +37,17 @@ class SynthModel:
         self._order = []
         self._keep = cache_layers
         self.overrides = overrides or {}
+
+    def time(self) -> dict:
+        """The time path's weights ([QI] ``Qi21Dit``: ``t_lin1`` [dim][256],
+        ``t_lin2`` [dim][dim], ``modulation`` [4 dim][dim], ``norm_out``
+        [dim][dim]; bias-free), drawn like the other matrices."""
+        if getattr(self, "_time", None) is None:
+            sp, s = self.spec, self.spec.seed
+            shapes = {"t_lin1": (TID_T_LIN1, (sp.dim, TEMB_IN)), "t_lin2": (TID_T_LIN2, (sp.dim, sp.dim)),
+                      "modulation": (TID_MODULATION, (4 * sp.dim, sp.dim)), "norm_out": (TID_NORM_OUT, (sp.dim, sp.dim))}
+            self._time = {k: inputs.host_array(s, tid, shape, W_SIGMA, bf16=sp.bf16) for k, (tid, shape) in shapes.items()}
+        return self._time
 
     def block(self, l: int) -> dict:
         if l in self._cache:

@@ -417,6 +417,61 @@ def step(model, prefix: Prefix, tok: np.ndarray, mods: np.ndarray, final_scale: 
     return final_layer(x, final_scale, model.proj_out, g.eps, dt)
 
 
+# ───────────────────────────── time path and sampler ─────────────────────────────
+
+
+def timestep_embedding(t: float) -> np.ndarray:
+    """Sinusoidal embedding of the model time t in [0, 1] ([QI] ``Qi21Dit::temb``).
+
+    ts = 1000 t; frequency i = exp(-ln(10000) i / 128) for i < 128; the
+    cosines of ts * frequency, then the sines.  Every step in float32, as on
+    the host path.
+    """
+    half = 128
+    ts = F32(1000.0) * F32(t)
+    i = np.arange(half, dtype=F32)
+    f = np.exp((-np.log(F32(10000.0))) * i / F32(half)).astype(F32)
+    a = (ts * f).astype(F32)
+    return np.concatenate([np.cos(a), np.sin(a)]).astype(F32)
+
+
+def lin_row(w: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """One vector through a small bias-free projection ``w [out][in]`` with
+    float64 accumulation, rounded to float32 ([QI] ``lin_row``)."""
+    return (np.asarray(w, F64) @ np.asarray(x, F64)).astype(F32)
+
+
+def time_mods(tw: dict, t: float):
+    """The shared block modulation and the final-norm scale of one time
+    ([QI] ``Qi21Dit::temb`` and ``Qi21Dit::mods``).
+
+    temb = t_lin2 silu(t_lin1 e(t)); s = silu(temb); returns
+    (modulation s [4 dim] = raw [s1|g1|s2|g2], norm_out s [dim] = final_scale).
+    """
+    e = timestep_embedding(t)
+    h = silu(lin_row(tw["t_lin1"], e))
+    s = silu(lin_row(tw["t_lin2"], h))
+    return lin_row(tw["modulation"], s), lin_row(tw["norm_out"], s)
+
+
+def sample(model, prefix: Prefix, tok: np.ndarray, schedule, storage=None) -> np.ndarray:
+    """A flow-matching Euler sampler over the cached prefix ([WG] module doc:
+    a 40-step ``imagine`` calls the step once per time).
+
+    Reading (the pages give no schedule or update rule): for k < len - 1,
+    v = step(x, mods(t_k)), x <- x + (t_{k+1} - t_k) v, with the difference
+    taken in float32 between the float32 times.
+    """
+    x = np.asarray(tok, F32)
+    tw = model.time()
+    ts = np.asarray(schedule, F32)
+    for k in range(len(ts) - 1):
+        mods, fsc = time_mods(tw, float(ts[k]))
+        v = step(model, prefix, x, mods, fsc, storage=storage)
+        x = (x + (ts[k + 1] - ts[k]) * v).astype(F32)
+    return x
+
+
 def joint_forward(model, x_prefix: np.ndarray, tok: np.ndarray, layout: Layout, mods: np.ndarray,
                   final_scale: np.ndarray, dt=F32, layers: Optional[int] = None):
     """The whole joint sequence [prefix; target] in one pass, no cache ([QI] module doc "Semantics").

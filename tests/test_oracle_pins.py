@@ -495,3 +495,66 @@ def test_modulation_chunks_route_to_their_branch(tiny):
     m_s1 = m.copy()
     m_s1[:h] += rnd
     assert _rel(_one_block(model, x, m_s1)[0] - x, base - x) > 1e-3
+
+
+# ───────────────────────────── time path and sampler ─────────────────────────────
+
+def test_timestep_embedding_hand_values():
+    # t = 0: every cosine 1, every sine 0; ts = 1000 t = 1 makes the first
+    # frequency (exactly 1) give cos 1, sin 1; the last frequency is
+    # 10000^(-127/128); cosines come first
+    e0 = O.timestep_embedding(0.0)
+    assert np.array_equal(e0[:128], np.ones(128, np.float32)) and np.array_equal(e0[128:], np.zeros(128, np.float32))
+    e = O.timestep_embedding(0.001)
+    assert e.shape == (256,) and e.dtype == np.float32
+    assert abs(e[0] - math.cos(1.0)) < 1e-6 and abs(e[128] - math.sin(1.0)) < 1e-6
+    f127 = 10000.0 ** (-127 / 128)
+    assert abs(e[127] - math.cos(1.0 * f127)) < 1e-6 and abs(e[255] - math.sin(1.0 * f127)) < 1e-6
+    e7 = O.timestep_embedding(0.7)
+    for i in (0, 5, 64, 127):
+        a = 700.0 * 10000.0 ** (-i / 128)
+        assert abs(e7[i] - math.cos(a)) < 2e-4 * max(1.0, a / 100) and abs(e7[128 + i] - math.sin(a)) < 2e-4 * max(1.0, a / 100)
+
+
+def test_lin_row_accumulates_in_f64():
+    # 1e8 + 1 - 1e8 is lost in float32 accumulation, kept in float64
+    w = np.array([[1e8, 1.0, -1e8], [2.0, 3.0, 4.0]], np.float32)
+    x = np.array([1.0, 1.0, 1.0], np.float32)
+    assert np.array_equal(O.lin_row(w, x), np.array([1.0, 9.0], np.float32))
+
+
+def test_time_mods_structure(tiny):
+    _, model, _ = tiny
+    tw = dict(model.time())
+    mods, fs = O.time_mods(tw, 0.37)
+    assert mods.shape == (4 * model.geom.dim,) and fs.shape == (model.geom.dim,)
+    # linear in the last projections, which see the same silu(temb)
+    t2 = dict(tw, modulation=tw["modulation"] * 2, norm_out=tw["norm_out"] * 4)
+    m2, f2 = O.time_mods(t2, 0.37)
+    assert np.array_equal(m2, mods * 2) and np.array_equal(f2, fs * 4)
+    # a zero first layer: silu(0) = 0 feeds the second, temb = 0, so s = 0
+    z = dict(tw, t_lin1=np.zeros_like(tw["t_lin1"]))
+    mz, fz = O.time_mods(z, 0.37)
+    assert not np.any(mz) and not np.any(fz)
+    # the time matters
+    m3, _ = O.time_mods(tw, 0.9)
+    assert _rel(m3, mods) > 1e-3
+
+
+def test_sampler_steps(tiny):
+    w, model, d = tiny
+    lay = O.Layout(w.layout())
+    pre = O.prefill(model, d["x_prefix"], lay)
+    tok = d["tok"]
+    # no time elapses: no change
+    assert np.array_equal(O.sample(model, pre, tok, [0.6, 0.6]), tok)
+    # one step is x + (t1 - t0) v with v the step at the modulation of t0
+    mods, fs = O.time_mods(model.time(), 0.6)
+    v = O.step(model, pre, tok, mods, fs)
+    one = O.sample(model, pre, tok, [0.6, 0.35])
+    assert np.array_equal(one, (tok + (np.float32(0.35) - np.float32(0.6)) * v).astype(np.float32))
+    # two steps start the second from the first's result
+    two = O.sample(model, pre, tok, [0.6, 0.35, 0.1])
+    m2, f2 = O.time_mods(model.time(), 0.35)
+    v2 = O.step(model, pre, one, m2, f2)
+    assert np.array_equal(two, (one + (np.float32(0.1) - np.float32(0.35)) * v2).astype(np.float32))
