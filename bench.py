@@ -50,8 +50,9 @@ def geom_of(spec):
                        in_ch=spec.in_ch, eps=spec.eps)
 
 
-def build_model(spec, opt=None, device="cuda"):
-    """A qi21 model holding the seeded synthetic weights of ``spec``."""
+def build_model(spec, opt=None, device="cuda", time_path=False):
+    """A qi21 model holding the seeded synthetic weights of ``spec`` (and,
+    with ``time_path``, the time path's)."""
     import torch
     from diffusion_transformer_denoiser_qi21_amd import qi21 as Q
 
@@ -69,6 +70,14 @@ def build_model(spec, opt=None, device="cuda"):
                 ws.append(inputs.device_tensor(s, block_tid(l, j), shape, W_SIGMA, bf16=spec.bf16, device=device))
         Q.qi21_model_set_block(m, l, None, ws[:7], ws[7], ws[8])
         del ws
+    if time_path:
+        from inputs.configs import TEMB_IN, TID_MODULATION, TID_NORM_OUT, TID_T_LIN1, TID_T_LIN2
+        d = spec.dim
+        tw = [inputs.device_tensor(s, tid, shape, W_SIGMA, bf16=spec.bf16, device=device)
+              for tid, shape in ((TID_T_LIN1, (d, TEMB_IN)), (TID_T_LIN2, (d, d)), (TID_MODULATION, (4 * d, d)),
+                                 (TID_NORM_OUT, (d, d)))]
+        Q.qi21_model_set_time(m, None, *tw)
+        del tw
     torch.cuda.synchronize()
     return m
 

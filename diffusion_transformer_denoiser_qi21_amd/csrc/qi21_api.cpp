@@ -99,6 +99,13 @@ struct qi21_model {
   std::deque<Prog> progs;
   int* dflag = nullptr;
   int* hflag = nullptr;  // pinned host
+  // time path (qi21_model_set_time): f32 t_lin1 [H][256], t_lin2 [H][H],
+  // modulation [4H][H], norm_out [H][H]; work 256 + 2H; the last time's
+  // mods [4H] and fs [H]
+  float* tw[4] = {nullptr, nullptr, nullptr, nullptr};
+  float* twork = nullptr;
+  float* tmods = nullptr;
+  float* tfs = nullptr;
   size_t bytes = 0;
   Prof prof;
 };
@@ -196,6 +203,24 @@ void free_prog(qi21_model* m, Prog& p) {
   p.kc.clear();
   p.vtc.clear();
   p.rc = p.rs = nullptr;
+}
+
+size_t time_floats(const qi21_geom& g, int i) {
+  const size_t H = g.hidden;
+  const size_t n[4] = {H * 256, H * H, 4 * H * H, H * H};
+  return n[i];
+}
+
+void free_time(qi21_model* m) {
+  for (int i = 0; i < 4; ++i) {
+    dfree(m, m->tw[i], time_floats(m->g, i) * 4);
+    m->tw[i] = nullptr;
+  }
+  const size_t H = m->g.hidden;
+  dfree(m, m->twork, (256 + 2 * H) * 4);
+  dfree(m, m->tmods, 4 * H * 4);
+  dfree(m, m->tfs, H * 4);
+  m->twork = m->tmods = m->tfs = nullptr;
 }
 
 Prog* find_prog(qi21_model* m, uint64_t key) {
@@ -473,6 +498,7 @@ void qi21_model_destroy(qi21_model* m) {
   }
   dfree(m, m->img_in, H * 64 * 4);
   dfree(m, m->proj_out_t, H * 64 * 4);
+  free_time(m);
   dfree(m, m->dflag, 256);
   if (m->hflag) (void)hipHostFree(m->hflag);
   for (int c = 0; c < NCLASS; ++c)
@@ -713,6 +739,75 @@ int qi21_step_batch(qi21_model* m, int nprog, const uint64_t* keys, const float*
 int qi21_step(qi21_model* m, uint64_t key, const float* xtok, const float* mods, const float* fs, float* out,
               void* stream) {
   return qi21_step_batch(m, 1, &key, &xtok, mods, fs, &out, stream);
+}
+
+int qi21_model_set_time(qi21_model* m, int w_dtype, const void* t_lin1, const void* t_lin2, const void* modulation,
+                        const void* norm_out, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QI21_EINVAL, "model is NULL");
+  if (w_dtype < QI21_F32 || w_dtype > QI21_F16) return fail(QI21_EINVAL, "w_dtype %d", w_dtype);
+  const void* src[4] = {t_lin1, t_lin2, modulation, norm_out};
+  for (int i = 0; i < 4; ++i)
+    if (!src[i]) return fail(QI21_EINVAL, "time weight %d is NULL", i);
+  hipStream_t s = (hipStream_t)stream;
+  const size_t H = m->g.hidden;
+  if (!m->tw[0]) {
+    for (int i = 0; i < 4; ++i) m->tw[i] = (float*)dalloc(m, time_floats(m->g, i) * 4);
+    m->twork = (float*)dalloc(m, (256 + 2 * H) * 4);
+    m->tmods = (float*)dalloc(m, 4 * H * 4);
+    m->tfs = (float*)dalloc(m, H * 4);
+    if (!m->tw[0] || !m->tw[1] || !m->tw[2] || !m->tw[3] || !m->twork || !m->tmods || !m->tfs) {
+      free_time(m);
+      return fail(QI21_ENOMEM, "time-path weights did not fit");
+    }
+  }
+  for (int i = 0; i < 4; ++i) HIP_OK(qi21::launch_to_f32(w_dtype, src[i], time_floats(m->g, i), m->tw[i], s));
+  return sync_stream(s);
+}
+
+int qi21_time_mods(qi21_model* m, float t, float* mods, float* fs, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QI21_EINVAL, "model is NULL");
+  if (!m->tw[0]) return fail(QI21_EINVAL, "no time-path weights (qi21_model_set_time)");
+  if (!mods || !fs) return fail(QI21_EINVAL, "mods / fs is NULL");
+  if (!std::isfinite(t)) return fail(QI21_EINVAL, "time is not finite");
+  HIP_OK(qi21::launch_time_mods(m->g.hidden, t, m->tw[0], m->tw[1], m->tw[2], m->tw[3], m->twork, mods, fs,
+                                (hipStream_t)stream));
+  return QI21_OK;
+}
+
+int qi21_step_t(qi21_model* m, uint64_t key, const float* xtok, float t, float* out, void* stream) {
+  int rc = qi21_time_mods(m, t, m ? m->tmods : nullptr, m ? m->tfs : nullptr, stream);
+  if (rc) return rc;
+  return qi21_step(m, key, xtok, m->tmods, m->tfs, out, stream);
+}
+
+int qi21_sample(qi21_model* m, uint64_t key, float* x, int nsteps, const float* t, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QI21_EINVAL, "model is NULL");
+  if (nsteps < 0 || (nsteps > 0 && (!t || !x))) return fail(QI21_EINVAL, "sample: nsteps %d, t or x NULL", nsteps);
+  if (!m->tw[0]) return fail(QI21_EINVAL, "no time-path weights (qi21_model_set_time)");
+  Prog* p = find_prog(m, key);
+  if (!p) return fail(QI21_ENOKEY, "no program for key %llu", (unsigned long long)key);
+  for (int k = 0; k <= nsteps; ++k)
+    if (!std::isfinite(t[k])) return fail(QI21_EINVAL, "time %d is not finite", k);
+  if (nsteps == 0) return QI21_OK;
+  const size_t nv = (size_t)p->n * 64;
+  float* v = (float*)dalloc(m, nv * 4);
+  if (!v) return fail(QI21_ENOMEM, "sampler velocity buffer");
+  int rc = QI21_OK;
+  hipStream_t s = (hipStream_t)stream;
+  for (int k = 0; k < nsteps && rc == QI21_OK; ++k) {
+    rc = qi21_step_t(m, key, x, t[k], v, stream);  // synchronises; x is untouched on failure
+    if (rc == QI21_OK) {
+      hipError_t e = qi21::launch_axpy((int)nv, t[k + 1] - t[k], v, x, s);
+      if (e != hipSuccess) rc = fail(QI21_EDEVICE, "sampler update: %s", hipGetErrorString(e));
+    }
+  }
+  if (rc == QI21_OK) rc = sync_stream(s);
+  (void)hipStreamSynchronize(s);
+  dfree(m, v, nv * 4);
+  return rc;
 }
 
 int qi21_release_key(qi21_model* m, uint64_t key) {

@@ -129,6 +129,19 @@ hipError_t launch_plane(int src_dtype, const void* src, int rows, int cols, f16*
 // out f32 [cols][rows] = transpose of in f32 [rows][cols]
 hipError_t launch_transpose_f32(int rows, int cols, const float* in, float* out, hipStream_t s);
 
+// The time path ([QI] Qi21Dit::temb / mods): mods [4h] (raw [s1|g1|s2|g2])
+// and fs [h] = 1 + final_scale of model time t, from f32 weights t_lin1
+// [h][256], t_lin2 [h][h], modulation [4h][h], norm_out [h][h]; work holds
+// 256 + 2h floats.  h % 4 == 0.
+hipError_t launch_time_mods(int h, float t, const float* t_lin1, const float* t_lin2, const float* modulation,
+                            const float* norm_out, float* work, float* mods, float* fs, hipStream_t s);
+
+// x[i] += dt v[i], i < n (product and sum rounded separately)
+hipError_t launch_axpy(int n, float dt, const float* v, float* x, hipStream_t s);
+
+// dst f32 [n] = src (src_dtype 0 f32, 1 bf16, 2 f16)
+hipError_t launch_to_f32(int src_dtype, const void* src, size_t n, float* dst, hipStream_t s);
+
 // fill count 32-bit words with value (a kernel, so it is safe to capture)
 hipError_t launch_fill32(void* p, uint32_t value, size_t count, hipStream_t s);
 

@@ -59,6 +59,10 @@ _SIGS = {
     "qi21_step": (C.c_int, [vp, u64, vp, vp, vp, vp, vp]),
     "qi21_step_batch": (C.c_int, [vp, C.c_int, C.POINTER(u64), C.POINTER(vp), vp, vp, C.POINTER(vp), vp]),
     "qi21_release_key": (C.c_int, [vp, u64]),
+    "qi21_model_set_time": (C.c_int, [vp, C.c_int, vp, vp, vp, vp, vp]),
+    "qi21_time_mods": (C.c_int, [vp, f32, vp, vp, vp]),
+    "qi21_step_t": (C.c_int, [vp, u64, vp, f32, vp, vp]),
+    "qi21_sample": (C.c_int, [vp, u64, vp, C.c_int, C.POINTER(f32), vp]),
     "qi21_model_destroy": (None, [vp]),
     "qi21_last_error": (C.c_char_p, []),
     "qi21_model_bytes": (C.c_size_t, [vp]),
@@ -177,6 +181,26 @@ def qi21_step_batch(m, keys: Sequence[int], xtok: Sequence, mods, fs, out: Seque
     n = len(keys)
     _check(lib().qi21_step_batch(m, n, (u64 * n)(*[int(k) for k in keys]), (vp * n)(*[_p(t) for t in xtok]),
                                  _p(mods), _p(fs), (vp * n)(*[_p(t) for t in out]), _stream(stream)))
+
+
+def qi21_model_set_time(m, w_dtype: Optional[int], t_lin1, t_lin2, modulation, norm_out, stream=None):
+    ws = (t_lin1, t_lin2, modulation, norm_out)
+    dt = _wdtype(t_lin1) if w_dtype is None else w_dtype
+    _check(lib().qi21_model_set_time(m, dt, *[_p(w) for w in ws], _stream(stream)))
+
+
+def qi21_time_mods(m, t: float, mods, fs, stream=None):
+    _check(lib().qi21_time_mods(m, float(t), _p(mods), _p(fs), _stream(stream)))
+
+
+def qi21_step_t(m, key: int, xtok, t: float, out, stream=None):
+    _check(lib().qi21_step_t(m, key, _p(xtok), float(t), _p(out), _stream(stream)))
+
+
+def qi21_sample(m, key: int, x, times: Sequence[float], stream=None):
+    n = len(times) - 1
+    arr = (f32 * max(1, len(times)))(*[float(v) for v in times])
+    _check(lib().qi21_sample(m, key, _p(x), n, arr, _stream(stream)))
 
 
 def qi21_release_key(m, key: int):

@@ -138,6 +138,36 @@ int qi21_step(qi21_model* m, uint64_t key, const float* xtok, const float* mods,
 int qi21_step_batch(qi21_model* m, int nprog, const uint64_t* keys, const float* const* xtok, const float* mods,
                     const float* fs, float* const* out, void* stream);
 
+/* Time-path weights ([QI] Qi21Dit: time_text_embed.timestep_embedder
+ * linear_1 [H][256] and linear_2 [H][H], modulation [4H][H], norm_out
+ * [H][H]; row-major [out][in], bias-free), element type w_dtype, kept as f32
+ * copies (about 28 H^2 bytes).  Needed by qi21_time_mods, qi21_step_t and
+ * qi21_sample.  The inputs may be freed after the call (it synchronises).
+ * Errors: EINVAL, ENOMEM, EDEVICE. */
+int qi21_model_set_time(qi21_model* m, int w_dtype, const void* t_lin1, const void* t_lin2, const void* modulation,
+                        const void* norm_out, void* stream);
+
+/* The modulation of model time t on the device ([QI] Qi21Dit::temb and
+ * Qi21Dit::mods): e = [cos(1000 t f_i) | sin(1000 t f_i)], f_i =
+ * exp(-ln(10000) i / 128), i < 128; temb = linear_2 silu(linear_1 e);
+ * mods [4H] = modulation silu(temb) (raw: [s1|g1|s2|g2]); fs [H] = 1 +
+ * norm_out silu(temb), the final scale as qi21_step takes it.  Float64
+ * partial sums in the projections.  Enqueued on stream, no
+ * synchronisation. */
+int qi21_time_mods(qi21_model* m, float t, float* mods, float* fs, void* stream);
+
+/* qi21_step with the modulation of time t computed on the device. */
+int qi21_step_t(qi21_model* m, uint64_t key, const float* xtok, float t, float* out, void* stream);
+
+/* A flow-matching Euler sampler over program key ([WG] module doc: an
+ * imagine call runs the step once per time; the update rule is not on the
+ * pages, and this is the plainest reading): x [n][64] (device, in place)
+ * goes through the times t[0..nsteps] (host array): for each k, v =
+ * qi21_step_t(x, t[k]), x += (t[k+1] - t[k]) v.  One upload per prompt:
+ * only x and the times cross from the host.  Errors as qi21_step; on
+ * ENONFINITE at step k, x holds the state after step k - 1. */
+int qi21_sample(qi21_model* m, uint64_t key, float* x, int nsteps, const float* t, void* stream);
+
 /* Drop one program ([WG] release_key).  Returns ENOKEY if absent. */
 int qi21_release_key(qi21_model* m, uint64_t key);
 

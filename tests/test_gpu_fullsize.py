@@ -275,3 +275,21 @@ def test_step_1024_gate_zero_closed_form_and_determinism(full_model):
     want = O.final_layer(O.embed_image(tok, img_in), fsc, proj_out, spec.eps)
     assert rel(a.cpu().numpy()[rows], want) < V_TOL
     Q().qi21_release_key(full_model, 70)
+
+
+def test_time_mods_full_size():
+    # the full model's time path (bf16 weights widened to f32, f64 sums)
+    from oracle import SynthModel
+    spec = CONFIGS["1024"].model
+    q = Q()
+    m = bench.build_model(spec, time_path=True)
+    try:
+        mods = torch.zeros(4 * spec.dim, device="cuda")
+        fs = torch.zeros(spec.dim, device="cuda")
+        q.qi21_time_mods(m, 0.81, mods, fs)
+        torch.cuda.synchronize()
+        want_m, want_f = O.time_mods(SynthModel(spec, cache_layers=0).time(), 0.81)
+        assert rel(mods.cpu().numpy(), want_m) < 1e-5
+        assert rel(fs.cpu().numpy(), 1.0 + want_f) < 1e-6
+    finally:
+        q.qi21_model_destroy(m)

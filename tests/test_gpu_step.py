@@ -217,3 +217,73 @@ def test_error_paths_and_eviction(tiny_gpu):
         assert e.value.code == q.QI21_EINVAL
     finally:
         q.qi21_model_destroy(m2)
+
+
+# ───────────────────────────── time path and sampler ─────────────────────────────
+
+@pytest.fixture(scope="module")
+def tiny_time():
+    m = bench.build_model(TINY_MODEL, time_path=True)
+    yield m
+    Q().qi21_model_destroy(m)
+
+
+@pytest.mark.parametrize("t", [0.0, 0.37, 1.0])
+def test_time_mods_match_oracle(tiny_time, tiny_cpu, t):
+    q = Q()
+    h = TINY_MODEL.dim
+    mods = torch.zeros(4 * h, device="cuda")
+    fs = torch.zeros(h, device="cuda")
+    q.qi21_time_mods(tiny_time, t, mods, fs)
+    torch.cuda.synchronize()
+    want_m, want_f = O.time_mods(tiny_cpu.time(), t)
+    assert rel(mods.cpu().numpy(), want_m) < 1e-5
+    assert rel(fs.cpu().numpy(), 1.0 + want_f) < 1e-6
+
+
+def test_step_t_against_oracle(tiny_time, tiny_cpu):
+    w = CONFIGS["tiny"]
+    d = bench.workload_tensors(w)
+    bench.prefill(tiny_time, 7, d)
+    out = torch.zeros(d["n"], 64, device="cuda")
+    Q().qi21_step_t(tiny_time, 7, d["tok"], 0.55, out)
+    dd = workload_inputs(w)
+    pre = O.prefill(tiny_cpu, dd["x_prefix"], O.Layout(w.layout()))
+    mods, fsc = O.time_mods(tiny_cpu.time(), 0.55)
+    err = rel(out.cpu().numpy(), O.step(tiny_cpu, pre, dd["tok"], mods, fsc))
+    print(f"step_t v rel L2 {err:.3e}")
+    assert err < V_TOL
+
+
+def test_sampler_against_oracle(tiny_time, tiny_cpu):
+    w = CONFIGS["tiny"]
+    d = bench.workload_tensors(w)
+    bench.prefill(tiny_time, 8, d)
+    times = [1.0, 0.75, 0.5, 0.25]
+    x = d["tok"].clone()
+    Q().qi21_sample(tiny_time, 8, x, times)
+    dd = workload_inputs(w)
+    pre = O.prefill(tiny_cpu, dd["x_prefix"], O.Layout(w.layout()))
+    want = O.sample(tiny_cpu, pre, dd["tok"], times)
+    err = rel(x.cpu().numpy(), want)
+    print(f"3-step sample rel L2 {err:.3e}")
+    assert err < V_TOL
+    # no time elapses, x unchanged; zero steps are a no-op
+    y = d["tok"].clone()
+    Q().qi21_sample(tiny_time, 8, y, [0.4, 0.4])
+    Q().qi21_sample(tiny_time, 8, y, [0.4])
+    assert torch.equal(y, d["tok"])
+
+
+def test_time_path_errors(tiny_gpu, tiny_time):
+    q = Q()
+    x = torch.zeros(256, 64, device="cuda")
+    bench.prefill(tiny_gpu, 9, bench.workload_tensors(CONFIGS["tiny"]))
+    with pytest.raises(q.Qi21Error) as e:  # no time weights in this model
+        q.qi21_sample(tiny_gpu, 9, x, [1.0, 0.5])
+    assert e.value.code == q.QI21_EINVAL
+    with pytest.raises(q.Qi21Error) as e:
+        q.qi21_sample(tiny_time, 12345, x, [1.0, 0.5])
+    assert e.value.code == q.QI21_ENOKEY
+    with pytest.raises(q.Qi21Error):
+        q.qi21_time_mods(tiny_time, float("nan"), x, x)
