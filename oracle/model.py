@@ -10,7 +10,8 @@ import numpy as np
 import inputs
 from inputs.configs import (BLOCK_NAMES, MOD_SIGMA, NORM_SIGMA, ROW_SIGMA, TEMB_IN, TID_FINAL_SCALE,
                             TID_IMG_IN, TID_MODS, TID_MODS0, TID_MODULATION, TID_NORM_OUT, TID_PREFIX_X,
-                            TID_PROJ_OUT, TID_T_LIN1, TID_T_LIN2, TID_TOK, W_SIGMA, block_tid)
+                            TID_PROJ_OUT, TID_T_LIN1, TID_T_LIN2, TID_TOK, TID_TXT_IN1, TID_TXT_IN2,
+                            TID_TXT_NORM, W_SIGMA, block_tid)
 
 from .qi21_oracle import Geometry
 
@@ -48,6 +49,20 @@ class SynthModel:
                       "modulation": (TID_MODULATION, (4 * sp.dim, sp.dim)), "norm_out": (TID_NORM_OUT, (sp.dim, sp.dim))}
             self._time = {k: inputs.host_array(s, tid, shape, W_SIGMA, bf16=sp.bf16) for k, (tid, shape) in shapes.items()}
         return self._time
+
+    def txt(self) -> dict:
+        """The txt_in front's weights ([QI] ``Qi21Dit``: ``txt_norm``
+        [context_in] (zero-centred: the norm multiplies by w + 1),
+        ``txt_in1`` [dim][context_in], ``txt_in2`` [dim][dim]; bias-free);
+        context_in = dim here."""
+        if getattr(self, "_txt", None) is None:
+            sp, s = self.spec, self.spec.seed
+            self._txt = {
+                "txt_norm": inputs.host_array(s, TID_TXT_NORM, (sp.dim,), NORM_SIGMA),
+                "txt_in1": inputs.host_array(s, TID_TXT_IN1, (sp.dim, sp.dim), W_SIGMA, bf16=sp.bf16),
+                "txt_in2": inputs.host_array(s, TID_TXT_IN2, (sp.dim, sp.dim), W_SIGMA, bf16=sp.bf16),
+            }
+        return self._txt
 
     def block(self, l: int) -> dict:
         if l in self._cache:

@@ -472,6 +472,32 @@ def sample(model, prefix: Prefix, tok: np.ndarray, schedule, storage=None) -> np
     return x
 
 
+# ───────────────────────────── txt_in front ─────────────────────────────
+
+
+def gelu_tanh(v: np.ndarray) -> np.ndarray:
+    """The tanh approximation of GELU, evaluated in float64 and rounded to
+    float32 ([QI] ``gelu_tanh``)."""
+    x = np.asarray(v, F64)
+    return (0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x * x * x)))).astype(F32)
+
+
+def embed_text(feats: np.ndarray, txt_norm: np.ndarray, txt_in1: np.ndarray, txt_in2: np.ndarray,
+               eps: float) -> np.ndarray:
+    """Text features ``[n, context_in]`` -> prefix rows ``[n, dim]`` ([QI] ``Qi21Dit::embed_text``).
+
+    Per row: RMSNorm with a float64 sum of squares and a zero-centred
+    weight, f32(v / sqrt(mean(v^2) + eps)) * (w + 1); then txt_in1, the tanh
+    GELU, and txt_in2 (bias-free, float32-accumulated projections).
+    """
+    x = np.asarray(feats, F32)
+    ms = (x.astype(F64) ** 2).sum(axis=1, keepdims=True) / x.shape[1]
+    inv = 1.0 / np.sqrt(ms + eps)
+    xn = ((x.astype(F64) * inv).astype(F32) * (np.asarray(txt_norm, F32) + F32(1.0))).astype(F32)
+    h = gelu_tanh(lin(xn, txt_in1))
+    return lin(h, txt_in2)
+
+
 def joint_forward(model, x_prefix: np.ndarray, tok: np.ndarray, layout: Layout, mods: np.ndarray,
                   final_scale: np.ndarray, dt=F32, layers: Optional[int] = None):
     """The whole joint sequence [prefix; target] in one pass, no cache ([QI] module doc "Semantics").

@@ -558,3 +558,33 @@ def test_sampler_steps(tiny):
     m2, f2 = O.time_mods(model.time(), 0.35)
     v2 = O.step(model, pre, one, m2, f2)
     assert np.array_equal(two, (one + (np.float32(0.1) - np.float32(0.35)) * v2).astype(np.float32))
+
+
+# ───────────────────────────── txt_in front ─────────────────────────────
+
+def test_gelu_tanh_values():
+    g = O.gelu_tanh(np.array([0.0, 1.0, -1.0, 3.0, -6.0], np.float32))
+    # 0.5 x (1 + tanh(sqrt(2/pi)(x + 0.044715 x^3))) by hand
+    want = [0.0, 0.8411919906, -0.1588080094, 2.9963625, -0.0]
+    assert np.allclose(g, want, rtol=0, atol=2e-7)
+
+
+def test_embed_text_norm_and_structure():
+    rng = np.random.default_rng(3)
+    n, c, d = 5, 64, 48
+    feats = rng.standard_normal((n, c)).astype(np.float32)
+    w0 = np.zeros(c, np.float32)
+    eye = np.eye(d, c, dtype=np.float32)
+    ident = np.eye(d, dtype=np.float32)
+    # zero-centred weight 0 scales by 1; identity projections expose
+    # gelu(rms-normalised features), whose mean square is 1 before the gelu
+    out = O.embed_text(feats, w0, eye, ident, 1e-6)
+    xn = feats / np.sqrt((feats.astype(np.float64) ** 2).mean(axis=1, keepdims=True) + 1e-6)
+    assert np.allclose(out, O.gelu_tanh(xn[:, :d]), rtol=0, atol=1e-6)
+    # a constant row normalises to +-1; the weight w scales it by (w + 1)
+    const = np.full((1, c), -7.0, np.float32)
+    w = np.full(c, 0.5, np.float32)
+    o2 = O.embed_text(const, w, eye, ident, 0.0)
+    assert np.allclose(o2, O.gelu_tanh(np.full((1, d), -1.5, np.float32)), rtol=0, atol=1e-7)
+    # scale invariance of the norm (eps = 0): features x 8 give the same rows
+    assert np.array_equal(O.embed_text(feats * 8, w0, eye, ident, 0.0), O.embed_text(feats, w0, eye, ident, 0.0))
