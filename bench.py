@@ -50,9 +50,9 @@ def geom_of(spec):
                        in_ch=spec.in_ch, eps=spec.eps)
 
 
-def build_model(spec, opt=None, device="cuda", time_path=False):
+def build_model(spec, opt=None, device="cuda", time_path=False, txt_in=False):
     """A qi21 model holding the seeded synthetic weights of ``spec`` (and,
-    with ``time_path``, the time path's)."""
+    with ``time_path`` / ``txt_in``, those of the time path / text front)."""
     import torch
     from diffusion_transformer_denoiser_qi21_amd import qi21 as Q
 
@@ -78,6 +78,12 @@ def build_model(spec, opt=None, device="cuda", time_path=False):
                                  (TID_NORM_OUT, (d, d)))]
         Q.qi21_model_set_time(m, None, *tw)
         del tw
+    if txt_in:
+        from inputs.configs import TID_TXT_IN1, TID_TXT_IN2, TID_TXT_NORM
+        d = spec.dim
+        Q.qi21_model_set_txt_in(m, d, None, inputs.device_tensor(s, TID_TXT_NORM, (d,), NORM_SIGMA, device=device),
+                                inputs.device_tensor(s, TID_TXT_IN1, (d, d), W_SIGMA, bf16=spec.bf16, device=device),
+                                inputs.device_tensor(s, TID_TXT_IN2, (d, d), W_SIGMA, bf16=spec.bf16, device=device))
     torch.cuda.synchronize()
     return m
 

@@ -46,6 +46,11 @@ namespace {
 // silu through the hardware reciprocal (~1 ulp; the result is stored as f16)
 __device__ __forceinline__ float silu_f(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
+// the tanh approximation of GELU (stored as f16)
+__device__ __forceinline__ float gelu_f(float v) {
+  return 0.5f * v * (1.0f + tanhf(0.7978845608028654f * (v + 0.044715f * v * v * v)));
+}
+
 // Block -> (tile row, tile column).  Hardware deals block b to XCD b % 8;
 // blocks of one XCD get a contiguous run of tiles, enumerated in groups of
 // 4 tile rows so that the ~32 tiles an XCD runs at once span 4 A panels and
@@ -101,7 +106,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
           }
       }
     }
-  } else if constexpr (EPI == EPI_F32 || EPI == EPI_F16) {
+  } else if constexpr (EPI == EPI_F32 || EPI == EPI_F16 || EPI == EPI_GELU) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int row = r0 + i * 32 + l32;
@@ -111,8 +116,12 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const size_t o = (size_t)row * a.ldo + c0 + j * 32 + 8 * g + 4 * hsel;
-            const floatx4 v = floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                      acc[i][j][4 * g + 3]} * a.oscale;
+            floatx4 v = floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+            if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e] * a.inscale);
+            }
+            v = v * a.oscale;
             if constexpr (EPI == EPI_F32)
               *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(a.out) + o) = v;
             else
@@ -239,7 +248,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, floatx16 (&acc)[TM][
           }
         }
     }
-  } else if constexpr (EPI == EPI_F32 || EPI == EPI_F16) {
+  } else if constexpr (EPI == EPI_F32 || EPI == EPI_F16 || EPI == EPI_GELU) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -249,7 +258,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, floatx16 (&acc)[TM][
           const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
           const int col = cbase + j * 32;
           if (row < a.M) {
-            const float v = acc[i][j][e] * a.oscale;
+            const float v = (EPI == EPI_GELU ? gelu_f(acc[i][j][e] * a.inscale) : acc[i][j][e]) * a.oscale;
             if constexpr (EPI == EPI_F32)
               reinterpret_cast<float*>(a.out)[(size_t)row * a.ldo + col] = v;
             else
@@ -685,6 +694,7 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s) {
     case EPI_QKV: return launch_epi<EPI_QKV>(a, tile, s);
     case EPI_SWIGLU2: return launch_epi<EPI_SWIGLU2>(a, tile, s);
     case EPI_RESID: return launch_epi<EPI_RESID>(a, tile, s);
+    case EPI_GELU: return launch_epi<EPI_GELU>(a, tile, s);
     case EPI_QKROPE:
       if (tile == 0) return launch_dma<EPI_QKROPE, 4>(a, s);
       if (tile == 2) return launch_dma<EPI_QKROPE, 8>(a, s);

@@ -106,6 +106,14 @@ struct qi21_model {
   float* twork = nullptr;
   float* tmods = nullptr;
   float* tfs = nullptr;
+  // txt_in front (qi21_model_set_txt_in): norm weight f32 [cin], f16 planes
+  // txt_in1 [H][cin] and txt_in2 [H][H]; row buffers for txt_cap rows
+  int txt_cin = 0, txt_cap = 0;
+  float* txt_norm = nullptr;
+  f16* txt_w1 = nullptr;
+  f16* txt_w2 = nullptr;
+  f16* txt_xn = nullptr;  // [txt_cap][cin]
+  f16* txt_h = nullptr;   // [txt_cap][H]
   size_t bytes = 0;
   Prof prof;
 };
@@ -221,6 +229,25 @@ void free_time(qi21_model* m) {
   dfree(m, m->tmods, 4 * H * 4);
   dfree(m, m->tfs, H * 4);
   m->twork = m->tmods = m->tfs = nullptr;
+}
+
+void free_txt_rows(qi21_model* m) {
+  const size_t H = m->g.hidden;
+  dfree(m, m->txt_xn, (size_t)m->txt_cap * m->txt_cin * 2);
+  dfree(m, m->txt_h, (size_t)m->txt_cap * H * 2);
+  m->txt_xn = m->txt_h = nullptr;
+  m->txt_cap = 0;
+}
+
+void free_txt(qi21_model* m) {
+  free_txt_rows(m);
+  const size_t H = m->g.hidden, c = m->txt_cin;
+  dfree(m, m->txt_norm, c * 4);
+  dfree(m, m->txt_w1, H * c * 2);
+  dfree(m, m->txt_w2, H * H * 2);
+  m->txt_norm = nullptr;
+  m->txt_w1 = m->txt_w2 = nullptr;
+  m->txt_cin = 0;
 }
 
 Prog* find_prog(qi21_model* m, uint64_t key) {
@@ -499,6 +526,7 @@ void qi21_model_destroy(qi21_model* m) {
   dfree(m, m->img_in, H * 64 * 4);
   dfree(m, m->proj_out_t, H * 64 * 4);
   free_time(m);
+  free_txt(m);
   dfree(m, m->dflag, 256);
   if (m->hflag) (void)hipHostFree(m->hflag);
   for (int c = 0; c < NCLASS; ++c)
@@ -808,6 +836,61 @@ int qi21_sample(qi21_model* m, uint64_t key, float* x, int nsteps, const float* 
   (void)hipStreamSynchronize(s);
   dfree(m, v, nv * 4);
   return rc;
+}
+
+int qi21_model_set_txt_in(qi21_model* m, int context_in, int w_dtype, const float* txt_norm, const void* txt_in1,
+                          const void* txt_in2, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QI21_EINVAL, "model is NULL");
+  if (context_in < 64 || context_in % 64 || context_in > 8192)
+    return fail(QI21_EINVAL, "context_in %d (a multiple of 64, at most 8192)", context_in);
+  if (w_dtype < QI21_F32 || w_dtype > QI21_F16) return fail(QI21_EINVAL, "w_dtype %d", w_dtype);
+  if (!txt_norm || !txt_in1 || !txt_in2) return fail(QI21_EINVAL, "txt_in weight is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  const size_t H = m->g.hidden, c = context_in;
+  if (m->txt_cin != context_in) {
+    free_txt(m);
+    m->txt_cin = context_in;
+    m->txt_norm = (float*)dalloc(m, c * 4);
+    m->txt_w1 = (f16*)dalloc(m, H * c * 2);
+    m->txt_w2 = (f16*)dalloc(m, H * H * 2);
+    if (!m->txt_norm || !m->txt_w1 || !m->txt_w2) {
+      free_txt(m);
+      return fail(QI21_ENOMEM, "txt_in weights did not fit");
+    }
+  }
+  HIP_OK(hipMemcpyAsync(m->txt_norm, txt_norm, c * 4, hipMemcpyDeviceToDevice, s));
+  HIP_OK(qi21::launch_plane(w_dtype, txt_in1, (int)H, (int)c, m->txt_w1, (int)H, 0, 0, s));
+  HIP_OK(qi21::launch_plane(w_dtype, txt_in2, (int)H, (int)H, m->txt_w2, (int)H, 0, 0, s));
+  return sync_stream(s);
+}
+
+int qi21_txt_in(qi21_model* m, int n, const float* feats, float* out, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QI21_EINVAL, "model is NULL");
+  if (!m->txt_cin) return fail(QI21_EINVAL, "no txt_in weights (qi21_model_set_txt_in)");
+  if (n < 1 || !feats || !out) return fail(QI21_EINVAL, "txt_in: n %d, feats or out NULL", n);
+  hipStream_t s = (hipStream_t)stream;
+  const int H = m->g.hidden, c = m->txt_cin;
+  if (m->txt_cap < n) {
+    HIP_OK(hipStreamSynchronize(s));  // earlier calls may still use the buffers
+    free_txt_rows(m);
+    const int cap = (int)round_up((size_t)n, 256);
+    m->txt_xn = (f16*)dalloc(m, (size_t)cap * c * 2);
+    m->txt_h = (f16*)dalloc(m, (size_t)cap * H * 2);
+    if (!m->txt_xn || !m->txt_h) {
+      free_txt_rows(m);
+      return fail(QI21_ENOMEM, "txt_in rows for %d rows", n);
+    }
+    m->txt_cap = cap;
+  }
+  HIP_OK(qi21::launch_txtnorm(n, c, feats, m->txt_norm, m->g.eps, m->txt_xn, s));
+  const int tile = m->o.gemm_tile;
+  qi21::GemmArgs g1 = gemm_args(n, H, c, m->txt_xn, c, m->txt_w1, m->txt_h, H, 1.0f);
+  HIP_OK(qi21::launch_gemm(qi21::EPI_GELU, g1, tile, s));
+  qi21::GemmArgs g2 = gemm_args(n, H, H, m->txt_h, H, m->txt_w2, out, H, 1.0f);
+  HIP_OK(qi21::launch_gemm(qi21::EPI_F32, g2, tile, s));
+  return QI21_OK;
 }
 
 int qi21_release_key(qi21_model* m, uint64_t key) {

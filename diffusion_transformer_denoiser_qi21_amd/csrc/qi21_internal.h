@@ -19,7 +19,7 @@ constexpr int wait_imm(int vm, int lgkm) {
 }
 
 enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 4, EPI_QKROPE = 5, EPI_VT = 6,
-           EPI_RESID = 7 };
+           EPI_RESID = 7, EPI_GELU = 8 };
 
 // C = A * W^T over f16 operands with f32 accumulation.
 //   A: [M][lda] f16 (K contiguous), W: [N][kw] f16 (kw contiguous); column
@@ -41,6 +41,7 @@ enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 
 //   EPI_VT:     out f16 [M][ldo] = acc * oscale with output column c stored at
 //               vt_pos(c) and only columns c < nvalid (V^T from Wv and the
 //               rows as the W operand).  Large-M kernels only.
+//   EPI_GELU:   out f16 [M][ldo] = gelu_tanh(acc * inscale) * oscale
 //   EPI_RESID:  out f32 [M][ldo] += gate[c] * acc * oscale (the gated residual
 //               of a block's branch, x += tanh(g) y, in place)
 //   EPI_QKV:    columns [0, 2H) -> out f16 [M][ldo] (q|k), columns [2H, 3H)
@@ -96,6 +97,10 @@ hipError_t launch_flash(const FlashArgs& a, hipStream_t s);
 hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16* xn,
                         const float* mods, int g_off, int s_off, float eps, float oscale,
                         hipStream_t s);
+
+// txt_in norm over rows of width c (c % 4 == 0, c <= 8192): xn f16 =
+// f32(v / sqrt(mean(v^2) + eps)) * (w + 1), float64 sum of squares
+hipError_t launch_txtnorm(int rows, int c, const float* feats, const float* w, float eps, f16* xn, hipStream_t s);
 
 // Per-head RMSNorm(w) + interleaved RoPE on the q and k columns of the
 // panel (q at column 0, k at column heads*128, row stride ldp), in place.

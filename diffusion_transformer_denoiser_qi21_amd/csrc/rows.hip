@@ -101,6 +101,51 @@ hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16
   return hipGetLastError();
 }
 
+// ───────────────────────────── txt_in norm ─────────────────────────────
+// One 256-thread block per text row of width c (c % 4 == 0, c <= 8192):
+// xn = f16(f32(v / sqrt(mean(v^2) + eps)) * (w + 1)), the sum of squares
+// and the scaling in float64 ([QI] embed_text).
+__global__ __launch_bounds__(256) void txtnorm_kernel(int c, const float* __restrict__ feats,
+                                                      const float* __restrict__ w, float eps, f16* __restrict__ xn) {
+  __shared__ double red[4];
+  const int row = blockIdx.x, t = threadIdx.x;
+  const int nc = c >> 2;
+  const float4v* fr = reinterpret_cast<const float4v*>(feats + (size_t)row * c);
+  float4v v[8];
+  double ss = 0.0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = t + 256 * j;
+    if (k < nc) {
+      v[j] = fr[k];
+      ss += ((double)v[j][0] * v[j][0] + (double)v[j][1] * v[j][1]) + ((double)v[j][2] * v[j][2] + (double)v[j][3] * v[j][3]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  const double inv = 1.0 / sqrt((red[0] + red[1] + red[2] + red[3]) / (double)c + (double)eps);
+  half4* xo = reinterpret_cast<half4*>(xn + (size_t)row * c);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = t + 256 * j;
+    if (k < nc) {
+      const float4v wv = reinterpret_cast<const float4v*>(w)[k];
+      half4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (f16)((float)((double)v[j][e] * inv) * (wv[e] + 1.0f));
+      xo[k] = o;
+    }
+  }
+}
+
+hipError_t launch_txtnorm(int rows, int c, const float* feats, const float* w, float eps, f16* xn, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(txtnorm_kernel, dim3(rows), dim3(256), 0, s, c, feats, w, eps, xn);
+  return hipGetLastError();
+}
+
 // ───────────────────────────── qkrope ─────────────────────────────
 // One wave per (row, head, q|k); lane l owns the interleaved pair
 // (2l, 2l+1) of the head, which is also RoPE column l.

@@ -60,6 +60,8 @@ _SIGS = {
     "qi21_step_batch": (C.c_int, [vp, C.c_int, C.POINTER(u64), C.POINTER(vp), vp, vp, C.POINTER(vp), vp]),
     "qi21_release_key": (C.c_int, [vp, u64]),
     "qi21_model_set_time": (C.c_int, [vp, C.c_int, vp, vp, vp, vp, vp]),
+    "qi21_model_set_txt_in": (C.c_int, [vp, C.c_int, C.c_int, vp, vp, vp, vp]),
+    "qi21_txt_in": (C.c_int, [vp, C.c_int, vp, vp, vp]),
     "qi21_time_mods": (C.c_int, [vp, f32, vp, vp, vp]),
     "qi21_step_t": (C.c_int, [vp, u64, vp, f32, vp, vp]),
     "qi21_sample": (C.c_int, [vp, u64, vp, C.c_int, C.POINTER(f32), vp]),
@@ -187,6 +189,15 @@ def qi21_model_set_time(m, w_dtype: Optional[int], t_lin1, t_lin2, modulation, n
     ws = (t_lin1, t_lin2, modulation, norm_out)
     dt = _wdtype(t_lin1) if w_dtype is None else w_dtype
     _check(lib().qi21_model_set_time(m, dt, *[_p(w) for w in ws], _stream(stream)))
+
+
+def qi21_model_set_txt_in(m, context_in: int, w_dtype: Optional[int], txt_norm, txt_in1, txt_in2, stream=None):
+    dt = _wdtype(txt_in1) if w_dtype is None else w_dtype
+    _check(lib().qi21_model_set_txt_in(m, context_in, dt, _p(txt_norm), _p(txt_in1), _p(txt_in2), _stream(stream)))
+
+
+def qi21_txt_in(m, n: int, feats, out, stream=None):
+    _check(lib().qi21_txt_in(m, n, _p(feats), _p(out), _stream(stream)))
 
 
 def qi21_time_mods(m, t: float, mods, fs, stream=None):

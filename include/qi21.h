@@ -138,6 +138,23 @@ int qi21_step(qi21_model* m, uint64_t key, const float* xtok, const float* mods,
 int qi21_step_batch(qi21_model* m, int nprog, const uint64_t* keys, const float* const* xtok, const float* mods,
                     const float* fs, float* const* out, void* stream);
 
+/* txt_in weights ([QI] Qi21Dit: txt_in.text_norm [context_in] f32, a
+ * zero-centred RMSNorm weight; txt_in.in_layer [H][context_in] and
+ * txt_in.out_layer [H][H] of element type w_dtype, row-major [out][in],
+ * bias-free; the projections are kept as f16 planes).  context_in % 64 ==
+ * 0, at most 8192.  The inputs may be freed after the call (it
+ * synchronises).  Errors: EINVAL, ENOMEM, EDEVICE. */
+int qi21_model_set_txt_in(qi21_model* m, int context_in, int w_dtype, const float* txt_norm, const void* txt_in1,
+                          const void* txt_in2, void* stream);
+
+/* Text features -> prefix rows on the device ([QI] Qi21Dit::embed_text):
+ * feats f32 [n][context_in] -> out f32 [n][H] = txt_in2 gelu_tanh(txt_in1
+ * xn), xn = (v / sqrt(mean(v^2) + eps)) * (w + 1) per row (float64 sum of
+ * squares; xn and the GELU output are stored as f16).  out feeds
+ * qi21_prefill as the text rows.  Enqueued on stream; out is ready when the
+ * stream is. */
+int qi21_txt_in(qi21_model* m, int n, const float* feats, float* out, void* stream);
+
 /* Time-path weights ([QI] Qi21Dit: time_text_embed.timestep_embedder
  * linear_1 [H][256] and linear_2 [H][H], modulation [4H][H], norm_out
  * [H][H]; row-major [out][in], bias-free), element type w_dtype, kept as f32

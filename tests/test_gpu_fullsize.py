@@ -293,3 +293,22 @@ def test_time_mods_full_size():
         assert rel(fs.cpu().numpy(), 1.0 + want_f) < 1e-6
     finally:
         q.qi21_model_destroy(m)
+
+
+def test_txt_in_full_size():
+    from oracle import SynthModel
+    from inputs.configs import TID_TXT_FEATS
+    spec = CONFIGS["1024"].model
+    q = Q()
+    m = bench.build_model(spec, txt_in=True)
+    try:
+        n = 22
+        f = inputs.host_array(5, TID_TXT_FEATS, (n, spec.dim), 1.0)
+        out = torch.zeros(n, spec.dim, device="cuda")
+        q.qi21_txt_in(m, n, torch.from_numpy(f).cuda(), out)
+        torch.cuda.synchronize()
+        t = SynthModel(spec, cache_layers=0).txt()
+        want = O.embed_text(f, t["txt_norm"], t["txt_in1"], t["txt_in2"], spec.eps)
+        assert rel(out.cpu().numpy(), want) < 2e-3
+    finally:
+        q.qi21_model_destroy(m)

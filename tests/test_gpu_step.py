@@ -287,3 +287,59 @@ def test_time_path_errors(tiny_gpu, tiny_time):
     assert e.value.code == q.QI21_ENOKEY
     with pytest.raises(q.Qi21Error):
         q.qi21_time_mods(tiny_time, float("nan"), x, x)
+
+
+# ───────────────────────────── txt_in front ─────────────────────────────
+
+@pytest.fixture(scope="module")
+def tiny_txt():
+    m = bench.build_model(TINY_MODEL, txt_in=True)
+    yield m
+    Q().qi21_model_destroy(m)
+
+
+def _feats(n, c, seed=5):
+    import inputs
+    from inputs.configs import TID_TXT_FEATS
+    return inputs.host_array(seed, TID_TXT_FEATS, (n, c), 1.0)
+
+
+@pytest.mark.parametrize("n", [1, 18, 22, 300])
+def test_txt_in_matches_oracle(tiny_txt, tiny_cpu, n):
+    h = TINY_MODEL.dim
+    f = _feats(n, h)
+    out = torch.full((n, h), 7.0, device="cuda")
+    Q().qi21_txt_in(tiny_txt, n, torch.from_numpy(f).cuda(), out)
+    torch.cuda.synchronize()
+    t = tiny_cpu.txt()
+    want = O.embed_text(f, t["txt_norm"], t["txt_in1"], t["txt_in2"], TINY_MODEL.eps)
+    err = rel(out.cpu().numpy(), want)
+    print(f"txt_in n {n}: rel L2 {err:.3e}")
+    assert err < 2e-3  # the normalised features and the GELU output are f16
+
+
+def test_txt_in_feeds_prefill(tiny_txt, tiny_cpu):
+    # a text-only prefix whose rows come from txt_in, then a step
+    w = CONFIGS["tiny"]
+    d = bench.workload_tensors(w)
+    f = _feats(d["lp"], TINY_MODEL.dim, seed=6)
+    Q().qi21_txt_in(tiny_txt, d["lp"], torch.from_numpy(f).cuda(), d["x"])
+    bench.prefill(tiny_txt, 4, d)
+    out = torch.zeros(d["n"], 64, device="cuda")
+    Q().qi21_step(tiny_txt, 4, d["tok"], d["mods"], d["fs"], out)
+    dd = workload_inputs(w)
+    t = tiny_cpu.txt()
+    xp = O.embed_text(f, t["txt_norm"], t["txt_in1"], t["txt_in2"], TINY_MODEL.eps)
+    pre = O.prefill(tiny_cpu, xp, O.Layout(w.layout()))
+    want = O.step(tiny_cpu, pre, dd["tok"], dd["mods"], dd["final_scale"])
+    err = rel(out.cpu().numpy(), want)
+    print(f"txt_in prefix -> step: v rel L2 {err:.3e}")
+    assert err < V_TOL
+
+
+def test_txt_in_requires_weights(tiny_gpu):
+    q = Q()
+    z = torch.zeros(4, 256, device="cuda")
+    with pytest.raises(q.Qi21Error) as e:
+        q.qi21_txt_in(tiny_gpu, 4, z, z)
+    assert e.value.code == q.QI21_EINVAL
