@@ -678,10 +678,20 @@ hipError_t launch_epi(const GemmArgs& a, int tile, hipStream_t s) {
 
 }  // namespace
 
+// 256 x 256 tiles (8 waves) when their rounds over the CUs are at least 85%
+// full; otherwise the smaller 128 x 128 tiles keep more CUs busy
 int gemm_pick_tile(int M, int N, int K) {
   (void)K;
-  if (N % 256 == 0 && M >= 1536) return 2;
-  return 1;
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+  }
+  if (N % 256 != 0) return 1;
+  const long tiles = (long)((M + 255) / 256) * (N / 256);
+  const long rounds = (tiles + cus - 1) / cus;
+  return tiles * 100 >= rounds * cus * 85 ? 2 : 1;
 }
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s) {
