@@ -221,7 +221,7 @@ def main(argv=None):
     if args.copy_calibration:
         return copy_calibration()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
+        print(json.dumps({"error": "this library runs on one GPU; --gpus above 1 is not supported "
                                    "(the row-sharded multi-GPU step is described in DESIGN.md, not built)"}))
         return 2
 
