@@ -32,20 +32,22 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 }
 
 // ───────────────────────────── rowop ─────────────────────────────
-// One 256-thread block per row; thread t owns the float4 chunks
-// t, t + 256, ... of the row (h/4 chunks, at most 8 per thread).
-template <int MODE>
-__global__ __launch_bounds__(256) void rowop_kernel(int h, float* __restrict__ x, const float* __restrict__ y,
+// One wave per row, four rows per 256-thread block; lane l owns the float4
+// chunks l, l + 64, ... of the row (h/4 chunks, at most NJ per lane), so
+// both reductions are wave shuffles and no block barrier is needed.
+template <int MODE, int NJ>
+__global__ __launch_bounds__(256) void rowop_kernel(int rows, int h, float* __restrict__ x, const float* __restrict__ y,
                                                    f16* __restrict__ xn, const float* __restrict__ mods,
                                                    int g_off, int s_off, float eps, float oscale) {
-  __shared__ float red[4];
-  const int row = blockIdx.x, t = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
   const int nc = h >> 2;
   float4v* xr = reinterpret_cast<float4v*>(x + (size_t)row * h);
-  float4v v[8];
+  float4v v[NJ];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int c = t + 256 * j;
+  for (int j = 0; j < NJ; ++j) {
+    const int c = lane + 64 * j;
     if (c < nc) {
       v[j] = xr[c];
       if (MODE & 1) {
@@ -59,21 +61,21 @@ __global__ __launch_bounds__(256) void rowop_kernel(int h, float* __restrict__ x
   if (!(MODE & 2)) return;
   float sm = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (t + 256 * j < nc) sm += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
-  const float mean = block_sum256(sm, red) / (float)h;
+  for (int j = 0; j < NJ; ++j)
+    if (lane + 64 * j < nc) sm += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
+  const float mean = wave_sum(sm) / (float)h;
   float q = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (t + 256 * j < nc) {
+  for (int j = 0; j < NJ; ++j)
+    if (lane + 64 * j < nc) {
       const float4v d = v[j] - mean;
       q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
     }
-  const float inv = rsqrtf(block_sum256(q, red) / (float)h + eps);
+  const float inv = rsqrtf(wave_sum(q) / (float)h + eps);
   half4* xo = reinterpret_cast<half4*>(xn + (size_t)row * ((MODE & 4) ? 2 * h : h));
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int c = t + 256 * j;
+  for (int j = 0; j < NJ; ++j) {
+    const int c = lane + 64 * j;
     if (c < nc) {
       const float4v s = reinterpret_cast<const float4v*>(mods + s_off)[c];
       const float4v r = (v[j] - mean) * inv * (1.0f + s) * oscale;
@@ -87,18 +89,29 @@ __global__ __launch_bounds__(256) void rowop_kernel(int h, float* __restrict__ x
   }
 }
 
-hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16* xn, const float* mods,
-                        int g_off, int s_off, float eps, float oscale, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
+namespace {
+template <int NJ>
+hipError_t launch_rowop_nj(int rows, int h, int mode, float* x, const float* y, f16* xn, const float* mods,
+                           int g_off, int s_off, float eps, float oscale, hipStream_t s) {
+  const dim3 grid((rows + 3) / 4), block(256);
   switch (mode) {
-    case 1: hipLaunchKernelGGL(rowop_kernel<1>, dim3(rows), dim3(256), 0, s, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
-    case 2: hipLaunchKernelGGL(rowop_kernel<2>, dim3(rows), dim3(256), 0, s, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
-    case 3: hipLaunchKernelGGL(rowop_kernel<3>, dim3(rows), dim3(256), 0, s, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
-    case 6: hipLaunchKernelGGL(rowop_kernel<6>, dim3(rows), dim3(256), 0, s, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
-    case 7: hipLaunchKernelGGL(rowop_kernel<7>, dim3(rows), dim3(256), 0, s, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
+    case 1: hipLaunchKernelGGL((rowop_kernel<1, NJ>), grid, block, 0, s, rows, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
+    case 2: hipLaunchKernelGGL((rowop_kernel<2, NJ>), grid, block, 0, s, rows, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
+    case 3: hipLaunchKernelGGL((rowop_kernel<3, NJ>), grid, block, 0, s, rows, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
+    case 6: hipLaunchKernelGGL((rowop_kernel<6, NJ>), grid, block, 0, s, rows, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
+    case 7: hipLaunchKernelGGL((rowop_kernel<7, NJ>), grid, block, 0, s, rows, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16* xn, const float* mods,
+                        int g_off, int s_off, float eps, float oscale, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (h <= 1024) return launch_rowop_nj<4>(rows, h, mode, x, y, xn, mods, g_off, s_off, eps, oscale, s);
+  if (h <= 4096) return launch_rowop_nj<16>(rows, h, mode, x, y, xn, mods, g_off, s_off, eps, oscale, s);
+  return launch_rowop_nj<32>(rows, h, mode, x, y, xn, mods, g_off, s_off, eps, oscale, s);
 }
 
 // ───────────────────────────── txt_in norm ─────────────────────────────
