@@ -8,15 +8,17 @@
 //
 // Two kernels share the epilogues:
 //
-// * gemm_dma_kernel, the large-M kernel: block tile 256 x 256 x 32, 4 waves
-//   (2 x 2) of 128 x 128 each, 4 LDS stages filled by buffer loads that
-//   write straight into LDS (no register staging), so three k-tiles are in
-//   flight while one is multiplied.  A-rows past M come back as zeros from
-//   the buffer resource's range check.  The main loop is branch-free and its
-//   schedule is pinned: each MFMA is paired with one LDS fragment read or one
-//   LDS-bound buffer load, so the single wave of each SIMD keeps its matrix
-//   pipe fed.  One barrier per k-tile, placed after this tile's fragment
-//   reads, when the next tile is resident and this stage may be refilled.
+// * gemm_dma_kernel, the large-M kernel: block tile 256 x 256 x 64, 8 waves
+//   of 128 x 64 (two per SIMD; a 4-wave form of 128 x 128 is kept), 2 LDS
+//   stages filled by buffer loads that write straight into LDS (no register
+//   staging).  Each load reads 8 whole 128-byte rows, which the L2 -> CU
+//   path serves about 1.4x faster than 16 half rows.  A-rows past M come
+//   back as zeros from the buffer resource's range check.  The main loop is
+//   branch-free and its schedule is pinned: each MFMA is paired with at most
+//   one LDS fragment read and one LDS-bound buffer load.  One barrier per
+//   k-tile, after its third k-step's fragment reads: the next k-tile is then
+//   resident and this stage may be refilled; the refill is spread over the
+//   fourth k-step and the first k-step of the next k-tile.
 // * gemm_rs_kernel, the small-M / narrow-N kernel: block tile BM x BN x 64,
 //   global -> registers -> LDS, double-buffered.
 //
@@ -325,12 +327,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, floatx16 (&acc)[TM][
   }
 }
 
-// ───────────────────── large-M kernel: 256 x 256 x 32, LDS-direct loads ─────────────────────
-constexpr int DBM = 256, DBN = 256, DBK = 32, DNS = 4;
+// ───────────────────── large-M kernel: 256 x 256 x 64, LDS-direct loads ─────────────────────
+constexpr int DBM = 256, DBN = 256, DBK = 64, DNS = 2;
 constexpr int DSTAGE = (DBM + DBN) * DBK;  // halves per stage
-// LDS rows of DBK = 32 halves: 4 chunks of 16 bytes; chunk c of row r sits
-// at slot c ^ ((r >> 2) & 3).
-__device__ __forceinline__ int dswz(int r) { return (r >> 2) & 3; }
+// LDS rows of DBK = 64 halves: 8 chunks of 16 bytes; chunk c of row r sits
+// at slot c ^ ((r >> 1) & 7), so the 16 rows a fragment read serves at once
+// cover all 64 banks.
+__device__ __forceinline__ int dswz(int r) { return (r >> 1) & 7; }
 
 }  // namespace
 
@@ -348,7 +351,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
   constexpr int TN = (NW == 4 || EPI == EPI_QKROPE) ? 4 : 2;
   constexpr int WTM = TM * 32, WTN = TN * 32;  // wave tile
   constexpr int NCOL = DBN / WTN;              // waves across the block's columns
-  constexpr int NL = 16 / NW;                  // 16-byte loads per lane per operand per k-tile
+  constexpr int NL = 32 / NW;                  // 16-byte loads per lane per operand per k-tile
   extern __shared__ __attribute__((aligned(16))) f16 smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -387,14 +390,15 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
     }
   };
   // Load i (0..NL-1) of wave w fills LDS chunk positions (NW i + w) * 64 +
-  // lane of the A region and of the W region: row p / 4, slot p % 4.
+  // lane of the A region and of the W region: row p / 8, slot p % 8, so one
+  // load reads 8 whole 128-byte rows.
   // (fixed size: an array sized by a template-dependent constant and
   // captured by the lambdas below makes the host pass drop the kernel)
-  int voa[4], vob[4];
+  int voa[8], vob[8];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int p = (i * NW + wave) * 64 + lane;
-    const int r = p >> 2, c = (p & 3) ^ dswz(r);
+    const int r = p >> 3, c = (p & 7) ^ dswz(r);
     voa[i] = (r * a.lda + 8 * c) * 2;
     vob[i] = (r * a.kw + 8 * c) * 2;
   }
@@ -412,13 +416,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
   // k-tile t -> stage t % DNS; past the last tile the last one is fetched
   // again into a stage no one reads any more, which keeps the loop free of
   // branches and the count of loads in flight constant.
-  auto issue = [&](__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int t) {
+  // Loads i0..i1-1 of each operand for k-tile t.
+  auto issue = [&](__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int t, int i0, int i1) {
     const int tt = min(t, KT - 1);
     const int soff = tt * DBK * 2;
     const int soffw = (tt >= KTW ? tt - KTW : tt) * DBK * 2;
     f16* base = smem + (t % DNS) * DSTAGE + wave * 64 * 8;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
+    for (int i = i0; i < i1; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, base + i * NW * 64 * 8, 16, voa[i], soff, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, base + DBM * DBK + i * NW * 64 * 8, 16, vob[i], soffw, 0, 0);
     }
@@ -432,12 +437,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = wm * WTM + i * 32 + l32;
-      af[b][i] = *reinterpret_cast<const half8*>(sa + (r * 4 + (c ^ dswz(r))) * 8);
+      af[b][i] = *reinterpret_cast<const half8*>(sa + (r * 8 + (c ^ dswz(r))) * 8);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int r = wn * WTN + j * 32 + l32;
-      bf[b][j] = *reinterpret_cast<const half8*>(sb + (r * 4 + (c ^ dswz(r))) * 8);
+      bf[b][j] = *reinterpret_cast<const half8*>(sb + (r * 8 + (c ^ dswz(r))) * 8);
     }
   };
   // every epilogue but the V^T one stores along output rows: C^T = W A^T
@@ -452,12 +457,32 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
         else
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[b][i], bf[b][j], acc[i][j], 0, 0, 0);
   };
-  constexpr int MM = TM * TN, NDS = TM + TN, NVM = 2 * NL;  // per k-step: MFMAs, fragment reads; loads per k-tile
+  // per k-step: MFMAs, fragment reads; loads per operand issued in the last
+  // k-step of a k-tile (the rest go out in the first k-step of the next)
+  constexpr int MM = TM * TN, NDS = TM + TN, NVM = 2 * NL, L3 = NL / 2;
+  // one k-step of MFMAs on fragment buffer b with the reads of the next
+  // k-step's fragments into the other buffer
+  // Pins a k-step's order: each MFMA followed by up to one LDS-bound load
+  // (nv of them in all) and one fragment read.
+  auto pin = [&](int nv) {
+#pragma unroll
+    for (int i = 0; i < MM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
+      if (i < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load -> LDS
+      if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto kstep = [&](int t, int kk, int b) {
+    frags(t, kk + 1, b ^ 1);
+    mma(b);
+    pin(0);
+  };
 
   int tm, tn;
   tile_rc(seq0, tm, tn);
-#pragma unroll
-  for (int t = 0; t < DNS; ++t) issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), t);
+  issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), 0, 0, NL);
+  issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), 1, 0, L3);
   for (int sq = seq0; sq < seq_end; sq += seq_step) {
     const int m0 = tm * DBM, n0 = tn * DBN;
     const __amdgpu_buffer_rsrc_t ra = rsrc_a(m0), rb = rsrc_b(n0);
@@ -470,56 +495,49 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
     // k-tile 0 landed.  After an epilogue its stores share the vector
     // memory counter with these loads, so wait for all of them.
     if (sq == seq0)
-      __builtin_amdgcn_s_waitcnt(wait_imm((DNS - 1) * NVM, 15));
+      __builtin_amdgcn_s_waitcnt(wait_imm(2 * L3, 15));
     else
       __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
     __builtin_amdgcn_s_barrier();
     frags(0, 0, 0);
     for (int t = 0; t < KT - 1; ++t) {
+      // k-step 0, with the second part of k-tile t + 1's loads
       frags(t, 1, 1);
+      issue(ra, rb, t + 1, L3, NL);
       mma(0);
-#pragma unroll
-      for (int i = 0; i < NDS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, MM - NDS, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      // this wave's reads of stage t % DNS are done and k-tile t + 1 has
+      pin(2 * (NL - L3));
+      kstep(t, 1, 1);
+      kstep(t, 2, 0);
+      // this wave's reads of stage t % 2 are done and k-tile t + 1 has
       // landed; after the barrier every wave is past both, so the stage
-      // can be refilled
-      __builtin_amdgcn_s_waitcnt(wait_imm((DNS - 2) * NVM, 0));
+      // can be refilled with k-tile t + 2
+      __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      issue(ra, rb, t + DNS);
+      issue(ra, rb, t + 2, 0, L3);
       frags(t + 1, 0, 0);
       mma(1);
-#pragma unroll
-      for (int i = 0; i < NVM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load -> LDS
-      }
-#pragma unroll
-      for (int i = 0; i < MM - NVM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      pin(2 * L3);
     }
+    // the last k-tile; the second part of the (refetched, unread) k-tile
+    // after it keeps the load count of every k-tile the same
     frags(KT - 1, 1, 1);
+    issue(ra, rb, KT, L3, NL);
     mma(0);
+    pin(2 * (NL - L3));
+    kstep(KT - 1, 1, 1);
+    kstep(KT - 1, 2, 0);
     // every wave's reads of every stage are done (the loads still in
-    // flight only refetch the last k-tile into stages no one reads): the
-    // next tile's first stages can be fetched under the epilogue
-    __builtin_amdgcn_sched_barrier(0);
+    // flight only refetch the last k-tile into a stage no one reads any
+    // more): the next tile's first k-tiles can be fetched under the epilogue
     __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     const int nsq = sq + seq_step;
     if (nsq < seq_end) {
       tile_rc(nsq, tm, tn);
-#pragma unroll
-      for (int t = 0; t < DNS; ++t) issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), t);
+      issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), 0, 0, NL);
+      issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), 1, 0, L3);
     }
     mma(1);
     if constexpr (ROWS)
