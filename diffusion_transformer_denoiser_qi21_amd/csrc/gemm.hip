@@ -389,18 +389,20 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
       tn = sq - tm * tiles_n;
     }
   };
-  // Load i (0..NL-1) of wave w fills LDS chunk positions (NW i + w) * 64 +
-  // lane of the A region and of the W region: row p / 8, slot p % 8, so one
-  // load reads 8 whole 128-byte rows.
+  // Load i (0..NL-1) of wave w fills LDS chunk positions p = (NL w + i) * 64
+  // + lane of the A region and of the W region: row p / 8, slot p % 8, so
+  // one load reads 8 whole 128-byte rows.
   // (fixed size: an array sized by a template-dependent constant and
   // captured by the lambdas below makes the host pass drop the kernel)
   int voa[8], vob[8];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int p = (i * NW + wave) * 64 + lane;
+    const int p = (wave * NL + i) * 64 + lane;
     const int r = p >> 3, c = (p & 7) ^ dswz(r);
-    voa[i] = (r * a.lda + 8 * c) * 2;
-    vob[i] = (r * a.kw + 8 * c) * 2;
+    // the instruction offset (i % 4) KiB moves the LDS and the global
+    // address alike; the global part is taken back here
+    voa[i] = (r * a.lda + 8 * c) * 2 - (i & 3) * 1024;
+    vob[i] = (r * a.kw + 8 * c) * 2 - (i & 3) * 1024;
   }
   // Buffer resources over a tile's A rows and W rows; A rows at or past M
   // fall outside the resource's range and return zeros.
@@ -413,76 +415,79 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
   };
   // W columns wrap every kw (K is kw or 2 kw)
   const int KTW = a.kw / DBK;
-  // k-tile t -> stage t % DNS; past the last tile the last one is fetched
-  // again into a stage no one reads any more, which keeps the loop free of
-  // branches and the count of loads in flight constant.
-  // Loads i0..i1-1 of each operand for k-tile t.
-  auto issue = [&](__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int t, int i0, int i1) {
-    const int tt = min(t, KT - 1);
-    const int soff = tt * DBK * 2;
-    const int soffw = (tt >= KTW ? tt - KTW : tt) * DBK * 2;
-    f16* base = smem + (t % DNS) * DSTAGE + wave * 64 * 8;
-#pragma unroll
-    for (int i = i0; i < i1; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, base + i * NW * 64 * 8, 16, voa[i], soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, base + DBM * DBK + i * NW * 64 * 8, 16, vob[i], soffw, 0, 0);
+  // Load q (0 .. 2 NL - 1) of k-tile t into stage st: A-operand load q for
+  // q < NL, W-operand load q - NL above.  Loads 4j .. 4j+3 of an operand
+  // share one LDS base (M0) and differ in the instruction offset.
+  auto load1 = [&](__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int st, int t, int q) {
+    const bool w = q >= NL;
+    const int i = w ? q - NL : q;
+    f16* base = smem + st * DSTAGE + (w ? DBM * DBK : 0) + (wave * NL + (i & ~3)) * 64 * 8;
+    const __amdgpu_buffer_rsrc_t r = w ? rb : ra;
+    const int vo = w ? vob[i] : voa[i];
+    const int so = (w && t >= KTW ? t - KTW : t) * DBK * 2;
+    switch (i & 3) {  // (the offset must be an immediate)
+      case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base, 16, vo, so, 0, 0); break;
+      case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base, 16, vo, so, 1024, 0); break;
+      case 2: __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base, 16, vo, so, 2048, 0); break;
+      default: __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base, 16, vo, so, 3072, 0); break;
     }
   };
   floatx16 acc[TM][TN];
   half8 af[2][TM], bf[2][TN];
-  auto frags = [&](int t, int kk, int b) {
+  // Fragment read r of k-step kk of k-tile t into buffer b, in the order the
+  // MFMAs below consume them: A 0, W 0 .. TN-1, A 1 .. TM-1.
+  auto read1 = [&](int t, int kk, int b, int r) {
     const f16* sa = smem + (t % DNS) * DSTAGE;
-    const f16* sb = sa + DBM * DBK;
     const int c = kk * 2 + hsel;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int r = wm * WTM + i * 32 + l32;
-      af[b][i] = *reinterpret_cast<const half8*>(sa + (r * 8 + (c ^ dswz(r))) * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int r = wn * WTN + j * 32 + l32;
-      bf[b][j] = *reinterpret_cast<const half8*>(sb + (r * 8 + (c ^ dswz(r))) * 8);
+    if (r == 0 || r > TN) {
+      const int i = r == 0 ? 0 : r - TN;
+      const int row = wm * WTM + i * 32 + l32;
+      af[b][i] = *reinterpret_cast<const half8*>(sa + (row * 8 + (c ^ dswz(row))) * 8);
+    } else {
+      const int j = r - 1;
+      const int row = wn * WTN + j * 32 + l32;
+      bf[b][j] = *reinterpret_cast<const half8*>(sa + DBM * DBK + (row * 8 + (c ^ dswz(row))) * 8);
     }
   };
   // every epilogue but the V^T one stores along output rows: C^T = W A^T
   constexpr bool ROWS = EPI != EPI_QKV;
-  auto mma = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        if constexpr (ROWS)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[b][j], af[b][i], acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[b][i], bf[b][j], acc[i][j], 0, 0, 0);
+  auto mfma1 = [&](int b, int k) {
+    const int i = k / TN, j = k % TN;
+    if constexpr (ROWS)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[b][j], af[b][i], acc[i][j], 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[b][i], bf[b][j], acc[i][j], 0, 0, 0);
   };
-  // per k-step: MFMAs, fragment reads; loads per operand issued in the last
-  // k-step of a k-tile (the rest go out in the first k-step of the next)
-  constexpr int MM = TM * TN, NDS = TM + TN, NVM = 2 * NL, L3 = NL / 2;
-  // one k-step of MFMAs on fragment buffer b with the reads of the next
-  // k-step's fragments into the other buffer
-  // Pins a k-step's order: each MFMA followed by up to one LDS-bound load
-  // (nv of them in all) and one fragment read.
-  auto pin = [&](int nv) {
+  constexpr int MM = TM * TN, NDS = TM + TN, NQ = 2 * NL;
+  // A k-tile's NQ loads go out over three k-steps: [0, Q1) in the last
+  // k-step of the k-tile two before, [Q1, Q2) and [Q2, NQ) in the first two
+  // of the k-tile before.
+  constexpr int Q1 = (NQ + 2) / 3, Q2 = Q1 + (NQ - Q1 + 1) / 2;
+  // One k-step in a fixed order: MFMA k on fragment buffer b, then load
+  // q0 + k of k-tile tl while below q1, then fragment read k of k-step kk
+  // of k-tile t into buffer b ^ 1 when rd.
+  auto step = [&](int b, bool rd, int t, int kk, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int tl,
+                  int q0, int q1) {
 #pragma unroll
-    for (int i = 0; i < MM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
-      if (i < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load -> LDS
-      if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    for (int k = 0; k < MM; ++k) {
+      mfma1(b, k);
+      if (q0 + k < q1) load1(ra, rb, tl & 1, tl, q0 + k);
+      if (rd && k < NDS) read1(t, kk, b ^ 1, k);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
-  auto kstep = [&](int t, int kk, int b) {
-    frags(t, kk + 1, b ^ 1);
-    mma(b);
-    pin(0);
+  // k-tile 0 and the first part of k-tile 1 of the tile at (tm, tn)
+  auto prologue = [&](int tm, int tn) {
+    const __amdgpu_buffer_rsrc_t ra = rsrc_a(tm * DBM), rb = rsrc_b(tn * DBN);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) load1(ra, rb, 0, 0, q);
+#pragma unroll
+    for (int q = 0; q < Q1; ++q) load1(ra, rb, 1, min(1, KT - 1), q);
   };
 
   int tm, tn;
   tile_rc(seq0, tm, tn);
-  issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), 0, 0, NL);
-  issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), 1, 0, L3);
+  prologue(tm, tn);
   for (int sq = seq0; sq < seq_end; sq += seq_step) {
     const int m0 = tm * DBM, n0 = tn * DBN;
     const __amdgpu_buffer_rsrc_t ra = rsrc_a(m0), rb = rsrc_b(n0);
@@ -495,51 +500,43 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
     // k-tile 0 landed.  After an epilogue its stores share the vector
     // memory counter with these loads, so wait for all of them.
     if (sq == seq0)
-      __builtin_amdgcn_s_waitcnt(wait_imm(2 * L3, 15));
+      __builtin_amdgcn_s_waitcnt(wait_imm(Q1, 15));
     else
       __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
     __builtin_amdgcn_s_barrier();
-    frags(0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < NDS; ++r) read1(0, 0, 0, r);
+    __builtin_amdgcn_sched_barrier(0);
+    // (with KT = 1 the prologue's k-tile 1 is k-tile 0 again, in the stage
+    // no one reads, and the loop below does not run)
     for (int t = 0; t < KT - 1; ++t) {
-      // k-step 0, with the second part of k-tile t + 1's loads
-      frags(t, 1, 1);
-      issue(ra, rb, t + 1, L3, NL);
-      mma(0);
-      pin(2 * (NL - L3));
-      kstep(t, 1, 1);
-      kstep(t, 2, 0);
+      step(0, true, t, 1, ra, rb, t + 1, Q1, Q2);
+      step(1, true, t, 2, ra, rb, t + 1, Q2, NQ);
+      step(0, true, t, 3, ra, rb, 0, 0, 0);
       // this wave's reads of stage t % 2 are done and k-tile t + 1 has
       // landed; after the barrier every wave is past both, so the stage
-      // can be refilled with k-tile t + 2
+      // can take the first part of k-tile t + 2 (past the last k-tile:
+      // k-tile 0 again, into a stage no one reads any more)
       __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      issue(ra, rb, t + 2, 0, L3);
-      frags(t + 1, 0, 0);
-      mma(1);
-      pin(2 * L3);
+      step(1, true, t + 1, 0, ra, rb, t + 2 < KT ? t + 2 : t, 0, Q1);
     }
-    // the last k-tile; the second part of the (refetched, unread) k-tile
-    // after it keeps the load count of every k-tile the same
-    frags(KT - 1, 1, 1);
-    issue(ra, rb, KT, L3, NL);
-    mma(0);
-    pin(2 * (NL - L3));
-    kstep(KT - 1, 1, 1);
-    kstep(KT - 1, 2, 0);
-    // every wave's reads of every stage are done (the loads still in
-    // flight only refetch the last k-tile into a stage no one reads any
-    // more): the next tile's first k-tiles can be fetched under the epilogue
+    // the last k-tile
+    step(0, true, KT - 1, 1, ra, rb, 0, 0, 0);
+    step(1, true, KT - 1, 2, ra, rb, 0, 0, 0);
+    step(0, true, KT - 1, 3, ra, rb, 0, 0, 0);
+    // every wave's reads of every stage are done and no load is in flight:
+    // the next tile's first k-tiles can be fetched under the epilogue
     __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     const int nsq = sq + seq_step;
     if (nsq < seq_end) {
       tile_rc(nsq, tm, tn);
-      issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), 0, 0, NL);
-      issue(rsrc_a(tm * DBM), rsrc_b(tn * DBN), 1, 0, L3);
+      prologue(tm, tn);
     }
-    mma(1);
+    step(1, false, 0, 0, ra, rb, 0, 0, 0);
     if constexpr (ROWS)
       epilogue_rows<EPI, TM, TN>(a, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
     else
@@ -696,8 +693,11 @@ hipError_t launch_epi(const GemmArgs& a, int tile, hipStream_t s) {
 
 }  // namespace
 
-// 256 x 256 tiles (8 waves) when their rounds over the CUs are at least 85%
-// full; otherwise the smaller 128 x 128 tiles keep more CUs busy
+// 256 x 256 tiles when their rounds over the CUs are at least 85% full,
+// otherwise the smaller 128 x 128 tiles keep more CUs busy.  Of the two
+// 256 x 256 forms the 4-wave one is taken: on the 1024^2 step it measured
+// 1.7% faster than the 8-wave one (58.66 against 59.69 ms, interleaved),
+// its gain coming from the long gate/up and down GEMMs.
 int gemm_pick_tile(int M, int N, int K) {
   (void)K;
   static int cus = 0;
@@ -709,7 +709,7 @@ int gemm_pick_tile(int M, int N, int K) {
   if (N % 256 != 0) return 1;
   const long tiles = (long)((M + 255) / 256) * (N / 256);
   const long rounds = (tiles + cus - 1) / cus;
-  return tiles * 100 >= rounds * cus * 85 ? 2 : 1;
+  return tiles * 100 >= rounds * cus * 85 ? 0 : 1;
 }
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s) {

@@ -982,7 +982,7 @@ int qi21_op_qk_gemm(int M, int H, const void* A, int lda, const void* W, void* q
   if (M < 1 || H < 128 || H % 128 || lda % 8 || lda < H || ldq % 4 || ldk % 4 || ldq < H || ldk < H)
     return fail(QI21_EINVAL, "qk gemm M %d H %d lda %d ldq %d ldk %d", M, H, lda, ldq, ldk);
   if (!A || !W || !q_out || !k_out || !norm_q || !norm_k || !cos || !sin) return fail(QI21_EINVAL, "qk gemm pointer NULL");
-  if (tile == -1) tile = 2;
+  if (tile == -1) tile = 0;
   if (tile != 0 && tile != 2) return fail(QI21_EINVAL, "qk gemm tile %d (0 or 2)", tile);
   qi21::GemmArgs a = gemm_args(M, 2 * H, H, (const f16*)A, lda, (const f16*)W, q_out, ldq, 1.0f);
   a.nq = norm_q;
@@ -1002,7 +1002,7 @@ int qi21_op_vt_gemm(int H, int nkeys, int K, const void* Wv, int lda, const void
   if (H < 1 || nkeys < 1 || K < 64 || K % 64 || lda % 8 || lda < K || ldo % 4 || (size_t)ldo < round_up(nkeys, 16))
     return fail(QI21_EINVAL, "vt gemm H %d nkeys %d K %d lda %d ldo %d", H, nkeys, K, lda, ldo);
   if (!Wv || !X || !out) return fail(QI21_EINVAL, "vt gemm pointer NULL");
-  if (tile == -1) tile = 2;
+  if (tile == -1) tile = 0;
   if (tile != 0 && tile != 2) return fail(QI21_EINVAL, "vt gemm tile %d (0 or 2)", tile);
   qi21::GemmArgs a = gemm_args(H, (int)round_up(nkeys, 256), K, (const f16*)Wv, lda, (const f16*)X, out, ldo, oscale);
   a.nvalid = nkeys;

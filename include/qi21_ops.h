@@ -69,8 +69,8 @@ int qi21_op_gemm_resid(int M, int N, int K, int kw, const void* A, int lda, cons
  * (2j, 2j+1) are rotated by cos / sin [M][64] (row-major, column j); q
  * heads go to q_out f16 [M][ldq], k heads to k_out f16 [M][ldk], both at
  * column head*128.  Requires M >= 1, H % 128 == 0, lda % 8 == 0, lda >= H,
- * ldq, ldk >= H and % 4 == 0, 16-byte aligned pointers.  tile: -1 or 2 (8
- * waves), 0 (4 waves). */
+ * ldq, ldk >= H and % 4 == 0, 16-byte aligned pointers.  tile: -1 or 0 (4
+ * waves), 2 (8 waves). */
 int qi21_op_qk_gemm(int M, int H, const void* A, int lda, const void* W, void* q_out, int ldq, void* k_out, int ldk,
                     const float* norm_q, const float* norm_k, const float* cos, const float* sin, float eps, int tile,
                     void* stream);
@@ -82,7 +82,7 @@ int qi21_op_qk_gemm(int M, int H, const void* A, int lda, const void* W, void* q
  * round_up(nkeys, 256) readable rows (the kernel reads whole 256-row
  * tiles, and rows past nkeys only feed unwritten columns).  Requires
  * K % 64 == 0, lda % 8 == 0, lda >= K, ldo % 4 == 0, ldo >=
- * round_up(nkeys, 16).  tile: -1 or 2, or 0. */
+ * round_up(nkeys, 16).  tile: -1 or 0 (4 waves), 2 (8 waves). */
 int qi21_op_vt_gemm(int H, int nkeys, int K, const void* Wv, int lda, const void* X, void* out, int ldo, float oscale,
                     int tile, void* stream);
 
