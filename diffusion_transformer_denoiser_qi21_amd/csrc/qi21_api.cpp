@@ -94,7 +94,7 @@ struct qi21_model {
   std::vector<float*> nq, nk;
   std::vector<char> set;
   float* img_in = nullptr;      // [H][64]
-  float* proj_out_t = nullptr;  // [H][64]
+  float* proj_out = nullptr;  // [64][H]
   Acts acts;
   std::deque<Prog> progs;
   int* dflag = nullptr;
@@ -524,7 +524,7 @@ void qi21_model_destroy(qi21_model* m) {
     dfree(m, m->nk[l], 128 * 4);
   }
   dfree(m, m->img_in, H * 64 * 4);
-  dfree(m, m->proj_out_t, H * 64 * 4);
+  dfree(m, m->proj_out, H * 64 * 4);
   free_time(m);
   free_txt(m);
   dfree(m, m->dflag, 256);
@@ -575,7 +575,7 @@ int qi21_model_create(const qi21_geom* geom, const qi21_options* opt, int nblock
          (m->w13[l] = (f16*)dalloc(m, 2 * I * H * 2)) && (m->w2[l] = (f16*)dalloc(m, H * I * 2)) &&
          (m->nq[l] = (float*)dalloc(m, 128 * 4)) && (m->nk[l] = (float*)dalloc(m, 128 * 4));
   }
-  ok = ok && (m->img_in = (float*)dalloc(m, H * 64 * 4)) && (m->proj_out_t = (float*)dalloc(m, H * 64 * 4)) &&
+  ok = ok && (m->img_in = (float*)dalloc(m, H * 64 * 4)) && (m->proj_out = (float*)dalloc(m, H * 64 * 4)) &&
        (m->dflag = (int*)dalloc(m, 256));
   if (!ok) {
     qi21_model_destroy(m);
@@ -588,7 +588,7 @@ int qi21_model_create(const qi21_geom* geom, const qi21_options* opt, int nblock
     return fail(QI21_ENOMEM, "pinned host flag");
   }
   hipError_t e = hipMemcpyAsync(m->img_in, img_in, H * 64 * 4, hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess) e = qi21::launch_transpose_f32(64, (int)H, proj_out, m->proj_out_t, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(m->proj_out, proj_out, H * 64 * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     qi21_model_destroy(m);
@@ -751,7 +751,7 @@ int qi21_step_batch(qi21_model* m, int nprog, const uint64_t* keys, const float*
   }
   {
     Scope sc(m, C_IO, s);
-    HIP_OK(qi21::launch_final(rows, H, a.x, fs, m->proj_out_t, m->g.eps, a.out, m->dflag, s));
+    HIP_OK(qi21::launch_final(rows, H, a.x, fs, m->proj_out, m->g.eps, a.out, m->dflag, s));
     for (const Seg& sg : segs)
       HIP_OK(qi21::launch_commit(sg.rows * 64, a.out + (size_t)sg.row0 * 64,
                                  out[&sg - segs.data()], m->dflag, s));
@@ -1073,12 +1073,12 @@ int qi21_op_embed(int rows, int h, const float* tok, const float* img_in, float*
   return QI21_OK;
 }
 
-int qi21_op_final(int rows, int h, const float* x, const float* fs, const float* proj_out_t, float eps, float* out,
+int qi21_op_final(int rows, int h, const float* x, const float* fs, const float* proj_out, float eps, float* out,
                   int* flag, void* stream) {
   g_err.clear();
-  if (rows < 1 || h < 256 || h % 256 || !x || !fs || !proj_out_t || !out || !flag)
+  if (rows < 1 || h < 256 || h % 256 || !x || !fs || !proj_out || !out || !flag)
     return fail(QI21_EINVAL, "final rows %d h %d", rows, h);
-  HIP_OK(qi21::launch_final(rows, h, x, fs, proj_out_t, eps, out, flag, (hipStream_t)stream));
+  HIP_OK(qi21::launch_final(rows, h, x, fs, proj_out, eps, out, flag, (hipStream_t)stream));
   return QI21_OK;
 }
 

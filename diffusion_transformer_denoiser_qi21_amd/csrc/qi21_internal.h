@@ -115,9 +115,9 @@ hipError_t launch_qkrope(int rows, int heads, f16* panel, int ldp, const float* 
 hipError_t launch_embed(int rows, int h, const float* tok, const float* img_in, float* x,
                         hipStream_t s);
 
-// out[r][o] = sum_c (LN(x[r])[c] * fs[c]) * proj_out_t[c][o], o < 64, f32;
+// out[r][o] = sum_c (LN(x[r])[c] * fs[c]) * proj_out[o][c], o < 64, f32;
 // sets *flag |= 1 when any output is not finite.  h % 256 == 0.
-hipError_t launch_final(int rows, int h, const float* x, const float* fs, const float* proj_out_t,
+hipError_t launch_final(int rows, int h, const float* x, const float* fs, const float* proj_out,
                         float eps, float* out, int* flag, hipStream_t s);
 
 // dst[i] = flag == 0 ? src[i] : dst[i], i < count (count % 4 == 0).
@@ -130,9 +130,6 @@ hipError_t launch_mods(int h, const float* mods, float* mods_dev, hipStream_t s)
 // (ld = cols) receives source row r.  src_dtype 0 f32, 1 bf16, 2 f16.
 hipError_t launch_plane(int src_dtype, const void* src, int rows, int cols, f16* dst, int group,
                         int gstride, int goff, hipStream_t s);
-
-// out f32 [cols][rows] = transpose of in f32 [rows][cols]
-hipError_t launch_transpose_f32(int rows, int cols, const float* in, float* out, hipStream_t s);
 
 // The time path ([QI] Qi21Dit::temb / mods): mods [4h] (raw [s1|g1|s2|g2])
 // and fs [h] = 1 + final_scale of model time t, from f32 weights t_lin1

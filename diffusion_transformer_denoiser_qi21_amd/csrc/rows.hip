@@ -13,6 +13,7 @@ namespace qi21 {
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -243,87 +244,127 @@ hipError_t launch_embed(int rows, int h, const float* tok, const float* img_in, 
 }
 
 // ───────────────────────────── final ─────────────────────────────
-// 16 rows per block, 4 waves.  Phase 1: wave w computes mean / inverse std
-// of rows 4w..4w+3 (16-byte loads, two passes).  Phase 2: wave w owns the
-// columns [w h/4, (w+1) h/4), taken 64 at a time: the chunk's normalised
-// values (x - mean) * inv * fs of the 16 rows go to the wave's LDS area
-// ([16][64]), then lane o accumulates the 16 rows over the chunk against
-// proj_out^T rows (coalesced over o), four columns per broadcast 16-byte
-// LDS read.  Phase 3: the four waves' partial sums are added through LDS.
-__global__ __launch_bounds__(256) void final_kernel(int rows, int h, const float* __restrict__ x,
-                                                    const float* __restrict__ fs,
-                                                    const float* __restrict__ pt, float eps,
-                                                    float* __restrict__ out, int* __restrict__ flag) {
-  __shared__ __attribute__((aligned(16))) float xs[4][16][64];
-  __shared__ float part[4][16][64];
+// out[r][o] = sum_c LN(x[r])[c] fs[c] W[o][c] for the 64 outputs o, W the
+// proj_out weight [64][h].  A block takes 16 rows with 16 waves.  Phase 1:
+// wave w finds mean and inverse std of row w in one pass of sums shifted by
+// the row's first element (the shift keeps the variance free of
+// cancellation when the mean is large).  Phase 2: wave w contracts the
+// sixteenth [w h/16, (w+1) h/16) of the c range on v_mfma_f32_16x16x4_f32.
+// For a 16-wide c-slice at c0, lane l (row l % 16, quarter q = l / 16) holds
+// the normalised x[row][c0 + 4q .. +3] and W[16 nb + l % 16][c0 + 4q .. +3]
+// for the four 16-column blocks nb of o; MFMA j pairs element j of both, so
+// the four MFMAs of a slice cover its 16 c once each.  Loads run one to two
+// slices ahead of the MFMAs.  Phase 3: the 16 partial 16 x 64 tiles are summed
+// through LDS.
+namespace {
+struct FinalSlice {
+  float4v x, f, w[4];
+};
+}  // namespace
+
+// (amdgpu_waves_per_eu: the scheduler may keep 128 registers per lane, so the
+// loads run ahead instead of being moved next to their use)
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void final_kernel(int rows, int h, const float* __restrict__ x,
+                                                     const float* __restrict__ fs, const float* __restrict__ w,
+                                                     float eps, float* __restrict__ out, int* __restrict__ flag) {
+  constexpr int NWV = 16;
+  __shared__ float part[NWV][16][64];
   __shared__ float mean_s[16], inv_s[16];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int r0 = blockIdx.x * 16;
-  const int h4 = h >> 2;
-  for (int i = 0; i < 4; ++i) {
-    const int rl = wave * 4 + i;
-    const float4v* xr = reinterpret_cast<const float4v*>(x + (size_t)min(r0 + rl, rows - 1) * h);
-    float sm = 0.0f;
-    for (int c = lane; c < h4; c += 64) {
-      const float4v v = xr[c];
-      sm += (v[0] + v[1]) + (v[2] + v[3]);
-    }
-    const float mean = wave_sum(sm) / (float)h;
-    float q = 0.0f;
-    for (int c = lane; c < h4; c += 64) {
-      const float4v d = xr[c] - mean;
-      q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
-    }
-    const float inv = rsqrtf(wave_sum(q) / (float)h + eps);
-    if (lane == 0) {
-      mean_s[rl] = mean;
-      inv_s[rl] = inv;
-    }
-  }
-  __syncthreads();
-  float acc[16];
+  {
+    const float* xrow = x + (size_t)min(r0 + wave, rows - 1) * h;
+    const float4v* xr = reinterpret_cast<const float4v*>(xrow);
+    const float shift = xrow[0];
+    float s1 = 0.0f, s2 = 0.0f;
+    // four loads in flight per lane (h / 4 is a multiple of 64, so the
+    // bound is the same for the whole wave; lanes past it add zeros)
+    for (int c0 = 0; c0 < (h >> 2); c0 += 256) {
+      float4v v[4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-  const int cw = wave * (h >> 2);  // this wave's first column
-  for (int cc = 0; cc < (h >> 2); cc += 64) {
-    const int c = cw + cc + lane;
-    const float f = fs[c];
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + 64 * j + lane;
+        v[j] = c < (h >> 2) ? xr[c] : float4v{shift, shift, shift, shift};
+      }
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      xs[wave][r][lane] = (x[(size_t)min(r0 + r, rows - 1) * h + c] - mean_s[r]) * inv_s[r] * f;
-    __syncthreads();
-    const float* pc = pt + (size_t)(cw + cc) * 64 + lane;
-    for (int j = 0; j < 64; j += 4) {
-      const float p0 = pc[(j + 0) * 64], p1 = pc[(j + 1) * 64], p2 = pc[(j + 2) * 64], p3 = pc[(j + 3) * 64];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float4v xv = *reinterpret_cast<const float4v*>(&xs[wave][r][j]);
-        acc[r] = __builtin_fmaf(xv[0], p0, __builtin_fmaf(xv[1], p1, __builtin_fmaf(xv[2], p2, __builtin_fmaf(xv[3], p3, acc[r]))));
+      for (int j = 0; j < 4; ++j) {
+        const float4v d = v[j] - shift;
+        s1 += (d[0] + d[1]) + (d[2] + d[3]);
+        s2 += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
       }
     }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) part[wave][r][lane] = acc[r];
-  __syncthreads();
-  bool bad = false;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rl = wave * 4 + i, r = r0 + rl;
-    const float v = (part[0][rl][lane] + part[1][rl][lane]) + (part[2][rl][lane] + part[3][rl][lane]);
-    if (r < rows) {
-      out[(size_t)r * 64 + lane] = v;
-      bad |= !__builtin_isfinite(v);
+    const float m1 = wave_sum(s1) / (float)h;
+    const float var = fmaxf(wave_sum(s2) / (float)h - m1 * m1, 0.0f);
+    if (lane == 0) {
+      mean_s[wave] = shift + m1;
+      inv_s[wave] = rsqrtf(var + eps);
     }
   }
-  if (bad) atomicOr(flag, 1);
+  __syncthreads();
+  const int rl = lane & 15, q = lane >> 4;
+  const float mean = mean_s[rl], inv = inv_s[rl];
+  // Buffer loads (an intrinsic, not a plain load, so the compiler does not
+  // fold the two buffers' loads back into one load next to the MFMAs).
+  // Rows of the block past the end read as zeros and are not stored.
+  const auto rx = __builtin_amdgcn_make_buffer_rsrc((void*)(x + (size_t)r0 * h), 0, min(rows - r0, 16) * h * 4,
+                                                    0x00020000);
+  const auto rf = __builtin_amdgcn_make_buffer_rsrc((void*)fs, 0, h * 4, 0x00020000);
+  const auto rw = __builtin_amdgcn_make_buffer_rsrc((void*)w, 0, 64 * h * 4, 0x00020000);
+  const int xo = (rl * h + 4 * q) * 4, fo = 4 * q * 4, wo = (rl * h + 4 * q) * 4, wnb = 16 * h * 4;
+  const int cq = h / NWV, cb = wave * cq, ce = cb + cq;
+  auto ld = [&](__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(float4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  };
+  auto fetch = [&](int c, FinalSlice& sl) {
+    c = min(c, ce - 16) * 4;  // past the end: the last slice again
+    sl.x = ld(rx, xo + c);
+    sl.f = ld(rf, fo + c);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) sl.w[nb] = ld(rw, wo + nb * wnb + c);
+  };
+  floatx4 acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  auto mma = [&](const FinalSlice& sl) {
+    const float4v av = (sl.x - mean) * inv * sl.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], sl.w[nb][j], acc[nb], 0, 0, 0);
+  };
+  // two slices in flight: each buffer is refilled right after its MFMAs
+  // (cq is a multiple of 16; an odd count of slices skips the last sb)
+  FinalSlice sa, sb;
+  fetch(cb, sa);
+  fetch(cb + 16, sb);
+  for (int c0 = cb; c0 < ce; c0 += 32) {
+    mma(sa);
+    fetch(c0 + 32, sa);
+    if (c0 + 16 < ce) {
+      mma(sb);
+      fetch(c0 + 48, sb);
+    }
+  }
+  // lane l holds rows 4q .. 4q+3 of column l % 16 of each 16-column block
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[wave][4 * q + i][nb * 16 + rl] = acc[nb][i];
+  __syncthreads();
+  const int r = t >> 6, o = t & 63;  // one output per thread
+  float v = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NWV; ++k) v += part[k][r][o];
+  if (r0 + r < rows) {
+    out[(size_t)(r0 + r) * 64 + o] = v;
+    if (!__builtin_isfinite(v)) atomicOr(flag, 1);
+  }
 }
 
-hipError_t launch_final(int rows, int h, const float* x, const float* fs, const float* proj_out_t, float eps,
-                        float* out, int* flag, hipStream_t s) {
+hipError_t launch_final(int rows, int h, const float* x, const float* fs, const float* proj_out, float eps, float* out,
+                        int* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(final_kernel, dim3((rows + 15) / 16), dim3(256), 0, s, rows, h, x, fs, proj_out_t, eps, out,
-                     flag);
+  hipLaunchKernelGGL(final_kernel, dim3((rows + 15) / 16), dim3(1024), 0, s, rows, h, x, fs, proj_out, eps, out, flag);
   return hipGetLastError();
 }
 
@@ -377,19 +418,6 @@ hipError_t launch_plane(int src_dtype, const void* src, int rows, int cols, f16*
   const size_t n = (size_t)rows * cols;
   hipLaunchKernelGGL(plane_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src_dtype, src, rows, cols,
                      dst, group, gstride, goff);
-  return hipGetLastError();
-}
-
-__global__ void transpose_kernel(int rows, int cols, const float* __restrict__ in, float* __restrict__ out) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (size_t)rows * cols) return;
-  const int r = (int)(i / cols), c = (int)(i - (size_t)r * cols);
-  out[(size_t)c * rows + r] = in[i];
-}
-
-hipError_t launch_transpose_f32(int rows, int cols, const float* in, float* out, hipStream_t s) {
-  const size_t n = (size_t)rows * cols;
-  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, rows, cols, in, out);
   return hipGetLastError();
 }
 

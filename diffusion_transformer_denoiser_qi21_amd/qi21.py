@@ -313,8 +313,8 @@ def qi21_op_embed(rows, h, tok, img_in, x, stream=None):
     _check(lib().qi21_op_embed(rows, h, _p(tok), _p(img_in), _p(x), _stream(stream)))
 
 
-def qi21_op_final(rows, h, x, fs, proj_out_t, eps, out, flag, stream=None):
-    _check(lib().qi21_op_final(rows, h, _p(x), _p(fs), _p(proj_out_t), eps, _p(out), _p(flag), _stream(stream)))
+def qi21_op_final(rows, h, x, fs, proj_out, eps, out, flag, stream=None):
+    _check(lib().qi21_op_final(rows, h, _p(x), _p(fs), _p(proj_out), eps, _p(out), _p(flag), _stream(stream)))
 
 
 def qi21_op_mods(h, mods, mods_dev, stream=None):

@@ -124,10 +124,10 @@ int qi21_op_qkrope(int rows, int heads, void* panel, int ldp, const float* norm_
  * Requires h % 64 == 0. */
 int qi21_op_embed(int rows, int h, const float* tok, const float* img_in, float* x, void* stream);
 
-/* out [rows][64] = (LN(x) * fs) proj_out^T with proj_out_t = proj_out^T
- * [h][64] ([QI] step_cpu final layer); *flag |= 1 if any output is not
- * finite.  Requires h % 256 == 0. */
-int qi21_op_final(int rows, int h, const float* x, const float* fs, const float* proj_out_t, float eps,
+/* out [rows][64] = (LN(x) * fs) proj_out^T, proj_out the Linear weight
+ * [64][h] (f32, row-major) ([QI] step_cpu final layer); *flag |= 1 if any
+ * output is not finite.  Requires h % 256 == 0. */
+int qi21_op_final(int rows, int h, const float* x, const float* fs, const float* proj_out, float eps,
                   float* out, int* flag, void* stream);
 
 /* mods_dev [4h] = [s1 | tanh g1 | s2 | tanh g2] ([WG] mods_dev). */

@@ -426,20 +426,23 @@ def test_embed(rows, h):
 
 @pytest.mark.parametrize("h", [256, 4096])
 @pytest.mark.parametrize("rows", [1, 17, 300])
-def test_final_and_nonfinite_flag(rows, h):
+@pytest.mark.parametrize("offset", [0.5, 200.0])
+def test_final_and_nonfinite_flag(rows, h, offset):
+    """The final layer against the oracle; a large common offset of the rows
+    checks that the LayerNorm statistics do not cancel."""
     q = Q()
-    x = inputs.host_array(12, 1, (rows, h), 1.0) * np.float32(3.0) + np.float32(0.5)
+    x = inputs.host_array(12, 1, (rows, h), 1.0) * np.float32(3.0) + np.float32(offset)
     fs = 1.0 + inputs.host_array(12, 2, (h,), 0.1)
     po = inputs.host_array(12, 3, (64, h), 0.02)
     out = torch.zeros(rows, 64, device="cuda")
     flag = torch.zeros(1, device="cuda", dtype=torch.int32)
-    q.qi21_op_final(rows, h, dev(x), dev(fs), dev(np.ascontiguousarray(po.T)), 1e-6, out, flag)
+    q.qi21_op_final(rows, h, dev(x), dev(fs), dev(po), 1e-6, out, flag)
     sync()
     want = O.lin(O.layer_norm(x, 1e-6) * fs, po)  # LN(x) * (1 + final_scale), fs = 1 + final_scale
     assert rel(out.cpu().numpy(), want) < F32_TOL
     assert int(flag.item()) == 0
     x[rows // 2, 3] = np.inf
-    q.qi21_op_final(rows, h, dev(x), dev(fs), dev(np.ascontiguousarray(po.T)), 1e-6, out, flag)
+    q.qi21_op_final(rows, h, dev(x), dev(fs), dev(po), 1e-6, out, flag)
     sync()
     assert int(flag.item()) == 1
 
