@@ -360,6 +360,33 @@ def test_gemm_gated_residual(M, tile, pair):
     assert rel(dx.cpu().numpy(), want) < (PAIR_TOL if pair else F32_TOL * 10)
 
 
+@pytest.mark.parametrize("tile", [0, 1, 2])
+@pytest.mark.parametrize("K", [64, 128, 192, 320, 4160])
+def test_gemm_k_depths(K, tile):
+    """Depths of one, two, an odd number and many 64-wide k-tiles: the
+    two-stage pipeline's first, last and refetched k-tiles (f32 store), and
+    the pair form whose W columns wrap after kw = K (2K columns of A)."""
+    q = Q()
+    M, N = 300, 512
+    A = f16_host(13, 1, (M, K), 1.0)
+    W = f16_host(13, 2, (N, K), 0.05)
+    out = torch.zeros(M, N, device="cuda", dtype=torch.float32)
+    q.qi21_op_gemm(q.QI21_EPI_F32, M, N, K, dev(A, torch.float16), K, dev(W, torch.float16), out, N, tile=tile)
+    sync()
+    assert rel(out.cpu().numpy(), O.lin(A, W)) < F32_TOL * 10
+    A32 = inputs.host_array(13, 3, (M, K), 1.0)
+    hi, lo = _pair(A32)
+    Ap = np.concatenate([hi, lo], axis=1)
+    x = np.zeros((M, N), np.float32)
+    gate = np.ones(N, np.float32)
+    dx = dev(x)
+    q.qi21_op_gemm_resid(M, N, 2 * K, K, dev(Ap, torch.float16), 2 * K, dev(W, torch.float16), dx, N, dev(gate), 1.0,
+                         tile)
+    sync()
+    want = A32.astype(np.float64) @ W.astype(np.float64).T
+    assert rel(dx.cpu().numpy(), want) < PAIR_TOL
+
+
 @pytest.mark.parametrize("tile", [0, 2])
 @pytest.mark.parametrize("M", [1, 77, 300, 1600])
 def test_qk_gemm_fused_norm_rope(M, tile):
