@@ -34,6 +34,8 @@
 // Range-guard factors are powers of two folded into oscale / inscale.
 #include "qi21_internal.h"
 
+#include <algorithm>
+
 namespace qi21 {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -87,7 +89,8 @@ __device__ __forceinline__ int vt_pos(int r) { return (r & ~12) | ((r & 4) << 1)
 // c0 + 32j + 8g + 4(l / 32) + (0..3) in registers 4g..4g+3, written as one
 // 16-byte (f32) or 8-byte (f16) store.  Requires ldo % 4 == 0.
 template <int EPI, int TM, int TN>
-__device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)[TM][TN], int r0, int c0, int lane) {
+__device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)[TM][TN], int r0, int c0, int lane,
+                                              size_t obase = 0) {
   const int hsel = lane >> 5, l32 = lane & 31;
   if constexpr (EPI == EPI_RESID) {
 #pragma unroll
@@ -117,7 +120,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
         for (int j = 0; j < TN; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const size_t o = (size_t)row * a.ldo + c0 + j * 32 + 8 * g + 4 * hsel;
+            const size_t o = obase + (size_t)row * a.ldo + c0 + j * 32 + 8 * g + 4 * hsel;
             floatx4 v = floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
             if constexpr (EPI == EPI_GELU) {
 #pragma unroll
@@ -358,18 +361,18 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
   const int wm = wave / NCOL, wn = wave % NCOL;
   const int hsel = lane >> 5, l32 = lane & 31;
   const int K = a.K;
-  const int KT = K / DBK;
+  const int KT = K / DBK / a.ksplit;  // k-tiles per work unit
   const int tiles_n = a.N / DBN, tiles_m = (a.M + DBM - 1) / DBM;
-  const int ntiles = tiles_n * tiles_m;
+  const int ntiles = tiles_n * tiles_m, nunits = ntiles * a.ksplit;
   // this block's run of the tile sequence
   int seq0, seq_end, seq_step;
   {
     const int nblk = gridDim.x, b = blockIdx.x;
-    if (nblk < ntiles && (nblk & 7) == 0) {
+    if (nblk < nunits && (nblk & 7) == 0) {
       const int per_xcd = nblk >> 3, x = b & 7, li = b >> 3;
-      const int chunk = (ntiles + 7) >> 3;
+      const int chunk = (nunits + 7) >> 3;
       seq0 = x * chunk + li;
-      seq_end = min(ntiles, (x + 1) * chunk);
+      seq_end = min(nunits, (x + 1) * chunk);
       seq_step = per_xcd;
     } else {
       seq0 = b;
@@ -377,7 +380,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
       seq_step = 1;
     }
   }
-  auto tile_rc = [&](int sq, int& tm, int& tn) {
+  // work unit sq -> tile (tm, tn) and its first k-tile kt0
+  auto tile_rc = [&](int sq, int& tm, int& tn, int& kt0) {
+    kt0 = (sq / ntiles) * KT;
+    sq %= ntiles;
     constexpr int G = 4;
     if (tiles_m % G == 0) {
       const int per = G * tiles_n;
@@ -415,10 +421,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
   };
   // W columns wrap every kw (K is kw or 2 kw)
   const int KTW = a.kw / DBK;
+  int kt0 = 0;  // the current work unit's first k-tile
   // Load q (0 .. 2 NL - 1) of k-tile t into stage st: A-operand load q for
   // q < NL, W-operand load q - NL above.  Loads 4j .. 4j+3 of an operand
   // share one LDS base (M0) and differ in the instruction offset.
   auto load1 = [&](__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int st, int t, int q) {
+    // (t is the global k-tile)
     const bool w = q >= NL;
     const int i = w ? q - NL : q;
     f16* base = smem + st * DSTAGE + (w ? DBM * DBK : 0) + (wave * NL + (i & ~3)) * 64 * 8;
@@ -471,25 +479,26 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
 #pragma unroll
     for (int k = 0; k < MM; ++k) {
       mfma1(b, k);
-      if (q0 + k < q1) load1(ra, rb, tl & 1, tl, q0 + k);
+      if (q0 + k < q1) load1(ra, rb, tl & 1, kt0 + tl, q0 + k);
       if (rd && k < NDS) read1(t, kk, b ^ 1, k);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // k-tile 0 and the first part of k-tile 1 of the tile at (tm, tn)
-  auto prologue = [&](int tm, int tn) {
+  // k-tile 0 and the first part of k-tile 1 of the unit at (tm, tn, kt0)
+  auto prologue = [&](int tm, int tn, int kt0) {
     const __amdgpu_buffer_rsrc_t ra = rsrc_a(tm * DBM), rb = rsrc_b(tn * DBN);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) load1(ra, rb, 0, 0, q);
+    for (int q = 0; q < NQ; ++q) load1(ra, rb, 0, kt0, q);
 #pragma unroll
-    for (int q = 0; q < Q1; ++q) load1(ra, rb, 1, min(1, KT - 1), q);
+    for (int q = 0; q < Q1; ++q) load1(ra, rb, 1, kt0 + min(1, KT - 1), q);
   };
 
   int tm, tn;
-  tile_rc(seq0, tm, tn);
-  prologue(tm, tn);
+  tile_rc(seq0, tm, tn, kt0);
+  prologue(tm, tn, kt0);
   for (int sq = seq0; sq < seq_end; sq += seq_step) {
     const int m0 = tm * DBM, n0 = tn * DBN;
+    const size_t obase = (size_t)(kt0 / KT) * a.pstride;  // partial plane of a split unit
     const __amdgpu_buffer_rsrc_t ra = rsrc_a(m0), rb = rsrc_b(n0);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -533,12 +542,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     const int nsq = sq + seq_step;
     if (nsq < seq_end) {
-      tile_rc(nsq, tm, tn);
-      prologue(tm, tn);
+      tile_rc(nsq, tm, tn, kt0);
+      prologue(tm, tn, kt0);
     }
     step(1, false, 0, 0, ra, rb, 0, 0, 0);
     if constexpr (ROWS)
-      epilogue_rows<EPI, TM, TN>(a, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
+      epilogue_rows<EPI, TM, TN>(a, acc, m0 + wm * WTM, n0 + wn * WTN, lane, obase);
     else
       epilogue<EPI, TM, TN>(a, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
   }
@@ -654,7 +663,7 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int tiles = ((a.M + DBM - 1) / DBM) * (a.N / DBN);
+  const int tiles = ((a.M + DBM - 1) / DBM) * (a.N / DBN) * a.ksplit;
   static int cus = 0;
   if (!cus) {
     int dev = 0;
@@ -718,7 +727,32 @@ int gemm_pick_tile(int M, int N, int K) {
   return t256 * 140 * r128 >= t128 * 100 * r256 ? 0 : 1;
 }
 
+// Split over K where the whole tiles of a 256 x 256 launch fill less than
+// half the CUs and the 128 x 128 kernel would be picked: at 1024 rows the
+// down GEMM (64 tiles of 256 x 256) runs as 256 work units of a quarter of
+// K each, at the 256 x 256 kernel's rate, and the row pass that follows
+// adds the partial products.  Needs at least 512 rows (two 256-row tiles).
+int gemm_split_count(int M, int N, int K, int maxs) {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+  }
+  if (M < 512 || N % 256 != 0 || K % 64 != 0 || gemm_pick_tile(M, N, K) != 1) return 1;
+  const long t = (long)((M + 255) / 256) * (N / 256);
+  if (2 * t > cus) return 1;
+  int sp = (int)std::min<long>(cus / t, maxs);
+  while (sp > 1 && (K / 64) % sp != 0) --sp;
+  return std::max(sp, 1);
+}
+
 hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s) {
+  if (a.ksplit > 1) {  // split units: 256 x 256 f32 partial products only
+    if (epi != EPI_F32 || (tile != 0 && tile != 2) || a.N % 256 != 0 || (a.K / 64) % a.ksplit != 0)
+      return hipErrorInvalidValue;
+    return tile == 2 ? launch_dma<EPI_F32, 8>(a, s) : launch_dma<EPI_F32, 4>(a, s);
+  }
   if (tile < 0) tile = gemm_pick_tile(a.M, a.N, a.K);
   if ((tile == 0 || tile == 2) && a.N % 256 != 0) tile = 1;
   switch (epi) {

@@ -62,6 +62,7 @@ struct Acts {
   f16* vt = nullptr;     // [H][cap] V^T of the pass's own rows
   f16* att = nullptr;    // [cap][H]
   f16* hid = nullptr;    // [cap][I]
+  float* part = nullptr; // [4 min(cap, 2048)][H] partial products of a down GEMM split over K
   float* mods = nullptr; // [4H] tanh-ed modulation of the pass
   float* out = nullptr;  // [cap][64] velocity before the finite check
   float* rc = nullptr;   // [cap][64] RoPE cos / sin of the pass's rows when
@@ -145,9 +146,10 @@ void dfree(qi21_model* m, void* p, size_t bytes) {
 // pair: the FFN input (in xn) and the SwiGLU hidden are kept as f16 pairs
 size_t acts_bytes(const qi21_geom& g, bool pair, int cap, size_t* parts) {
   const size_t H = g.hidden, I = g.inter, c = cap, f = pair ? 2 : 1;
-  // slot 5 is empty: the gated residuals run in the O / down GEMM epilogues
-  const size_t p[11] = {c * H * 4, c * H * 2 * f, c * 2 * H * 2, H * c * 2, c * H * 2, 0, c * I * 2 * f,
-                        4 * H * 4, c * 64 * 4, c * 64 * 4, c * 64 * 4};
+  // slot 5: the partial products of a down GEMM split over K (4 planes of
+  // up to 2048 rows; split GEMMs only run at fewer than 2048 rows)
+  const size_t p[11] = {c * H * 4, c * H * 2 * f, c * 2 * H * 2, H * c * 2, c * H * 2, 4 * std::min<size_t>(c, 2048) * H * 4,
+                        c * I * 2 * f, 4 * H * 4, c * 64 * 4, c * 64 * 4, c * 64 * 4};
   size_t t = 0;
   for (int i = 0; i < 11; ++i) {
     if (parts) parts[i] = p[i];
@@ -159,7 +161,7 @@ size_t acts_bytes(const qi21_geom& g, bool pair, int cap, size_t* parts) {
 void free_acts(qi21_model* m) {
   size_t parts[11];
   acts_bytes(m->g, m->o.ffn_pair != 0, m->acts.cap, parts);
-  void* ptrs[11] = {m->acts.x, m->acts.xn, m->acts.panel, m->acts.vt, m->acts.att, nullptr,
+  void* ptrs[11] = {m->acts.x, m->acts.xn, m->acts.panel, m->acts.vt, m->acts.att, m->acts.part,
                     m->acts.hid, m->acts.mods, m->acts.out, m->acts.rc, m->acts.rs};
   for (int i = 0; i < 11; ++i) dfree(m, ptrs[i], parts[i]);
   m->acts = Acts{};
@@ -194,6 +196,7 @@ int ensure_acts(qi21_model* m, int rows, hipStream_t s) {
   a.panel = (f16*)p[2];
   a.vt = (f16*)p[3];
   a.att = (f16*)p[4];
+  a.part = (float*)p[5];
   a.hid = (f16*)p[6];
   a.mods = (float*)p[7];
   a.out = (float*)p[8];
@@ -463,16 +466,36 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
       ga.kw = H;
       HIP_OK(qi21::launch_gemm(pf == 2 ? qi21::EPI_SWIGLU2 : qi21::EPI_SWIGLU, ga, tile, s));
     }
-    {  // x += tanh(g2) (hid W2^T) in the down GEMM's epilogue
-      Scope sc(m, C_W2, s);
-      qi21::GemmArgs ga = gemm_args(rows, H, pf * I, a.hid, pf * I, m->w2[l], a.x, H, p2(gd.hid));
-      ga.kw = I;
-      ga.gate = a.mods + 3 * H;
-      HIP_OK(qi21::launch_gemm(qi21::EPI_RESID, ga, tile, s));
-    }
-    if (!last) {  // the next block's xn = LN(x)(1 + s1)
+    // Where whole 256 x 256 tiles would leave most CUs idle (512 to 2047
+    // rows), the down GEMM runs split over K into partial products and the
+    // row pass adds them: x += tanh(g2) sum_p part_p, then (but in the
+    // last block) the next block's xn = LN(x)(1 + s1).  Otherwise the
+    // gated residual runs in the GEMM's epilogue.
+    const int sp = tile < 0 ? qi21::gemm_split_count(rows, H, pf * I, 4) : 1;
+    if (sp > 1 && (size_t)sp * rows <= 4 * std::min<size_t>(a.cap, 2048)) {
+      {
+        Scope sc(m, C_W2, s);
+        qi21::GemmArgs ga = gemm_args(rows, H, pf * I, a.hid, pf * I, m->w2[l], a.part, H, p2(gd.hid));
+        ga.kw = I;
+        ga.ksplit = sp;
+        ga.pstride = (size_t)rows * H;
+        HIP_OK(qi21::launch_gemm(qi21::EPI_F32, ga, 0, s));
+      }
       Scope sc(m, C_ROW, s);
-      HIP_OK(qi21::launch_rowop(rows, H, 2, a.x, nullptr, a.xn, a.mods, 0, 0, g.eps, p2(-gd.attn), s));
+      HIP_OK(qi21::launch_rowop(rows, H, last ? 1 : 3, a.x, a.part, a.xn, a.mods, 3 * H, 0, g.eps, p2(-gd.attn), s,
+                                sp, (size_t)rows * H));
+    } else {
+      {  // x += tanh(g2) (hid W2^T) in the down GEMM's epilogue
+        Scope sc(m, C_W2, s);
+        qi21::GemmArgs ga = gemm_args(rows, H, pf * I, a.hid, pf * I, m->w2[l], a.x, H, p2(gd.hid));
+        ga.kw = I;
+        ga.gate = a.mods + 3 * H;
+        HIP_OK(qi21::launch_gemm(qi21::EPI_RESID, ga, tile, s));
+      }
+      if (!last) {  // the next block's xn = LN(x)(1 + s1)
+        Scope sc(m, C_ROW, s);
+        HIP_OK(qi21::launch_rowop(rows, H, 2, a.x, nullptr, a.xn, a.mods, 0, 0, g.eps, p2(-gd.attn), s));
+      }
     }
   }
   return QI21_OK;
@@ -975,6 +998,24 @@ int qi21_op_gemm_resid(int M, int N, int K, int kw, const void* A, int lda, cons
   return QI21_OK;
 }
 
+int qi21_op_gemm_split(int M, int N, int K, int kw, const void* A, int lda, const void* W, float* part, int ksplit,
+                       float oscale, int tile, void* stream) {
+  g_err.clear();
+  if (ksplit < 1 || ksplit > 8) return fail(QI21_EINVAL, "split gemm ksplit %d (1..8)", ksplit);
+  if (kw < 64 || kw % 64 || (K != kw && K != 2 * kw) || K % (64 * ksplit))
+    return fail(QI21_EINVAL, "split gemm K %d kw %d ksplit %d", K, kw, ksplit);
+  if (M < 1 || N < 256 || N % 256 || lda % 8 || lda < K) return fail(QI21_EINVAL, "split gemm M %d N %d lda %d", M, N, lda);
+  if (!A || !W || !part) return fail(QI21_EINVAL, "split gemm pointer is NULL");
+  if (tile == -1) tile = 0;
+  if (tile != 0 && tile != 2) return fail(QI21_EINVAL, "split gemm tile %d (0 or 2)", tile);
+  qi21::GemmArgs a = gemm_args(M, N, K, (const f16*)A, lda, (const f16*)W, part, N, oscale);
+  a.kw = kw;
+  a.ksplit = ksplit;
+  a.pstride = (size_t)M * N;
+  HIP_OK(qi21::launch_gemm(qi21::EPI_F32, a, tile, (hipStream_t)stream));
+  return QI21_OK;
+}
+
 int qi21_op_qk_gemm(int M, int H, const void* A, int lda, const void* W, void* q_out, int ldq, void* k_out, int ldk,
                     const float* norm_q, const float* norm_k, const float* cos, const float* sin, float eps, int tile,
                     void* stream) {
@@ -1052,6 +1093,20 @@ int qi21_op_rowop(int rows, int h, int mode, float* x, const float* y, void* xn,
     return fail(QI21_EINVAL, "rowop rows %d h %d mode %d", rows, h, mode);
   if (!x || !mods || ((mode & 1) && !y) || ((mode & 2) && !xn)) return fail(QI21_EINVAL, "rowop pointer NULL");
   HIP_OK(qi21::launch_rowop(rows, h, mode, x, y, (f16*)xn, mods, g_off, s_off, eps, oscale, (hipStream_t)stream));
+  return QI21_OK;
+}
+
+int qi21_op_rowop_parts(int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride, void* xn,
+                        const float* mods, int g_off, int s_off, float eps, float oscale, void* stream) {
+  g_err.clear();
+  if (nparts < 1 || nparts > 8 || (nparts > 1 && pstride < (size_t)rows * h))
+    return fail(QI21_EINVAL, "rowop nparts %d pstride %zu", nparts, pstride);
+  if (rows < 1 || h < 4 || h % 4 || h > 8192 || mode < 1 || mode > 7 || mode == 4 || mode == 5 || g_off % 4 || s_off % 4 || g_off < 0 ||
+      s_off < 0)
+    return fail(QI21_EINVAL, "rowop rows %d h %d mode %d", rows, h, mode);
+  if (!x || !mods || ((mode & 1) && !y) || ((mode & 2) && !xn)) return fail(QI21_EINVAL, "rowop pointer NULL");
+  HIP_OK(qi21::launch_rowop(rows, h, mode, x, y, (f16*)xn, mods, g_off, s_off, eps, oscale, (hipStream_t)stream,
+                            nparts, pstride));
   return QI21_OK;
 }
 

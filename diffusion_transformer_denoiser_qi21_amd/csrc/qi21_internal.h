@@ -66,6 +66,11 @@ struct GemmArgs {
   int nvalid = 0;
   // EPI_RESID
   const float* gate = nullptr;
+  // split over K (256 x 256 kernels, EPI_F32 only): work unit u covers tile
+  // u % tiles over k-tiles [(u / tiles) KT / ksplit, ...) and writes its
+  // partial product to out + (u / tiles) * pstride (floats)
+  int ksplit = 1;
+  size_t pstride = 0;
 };
 hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s);
 // the tile a launch would pick (0: 256x256, 1: 128x128, ...)
@@ -90,13 +95,18 @@ struct FlashArgs {
 hipError_t launch_flash(const FlashArgs& a, hipStream_t s);
 
 // rowop over `rows` rows of width h (h % 4 == 0, h <= 8192):
-//   mode & 1: x += gate (.) y            (gate = mods + g_off, already tanh-ed)
+//   mode & 1: x += gate (.) y            (gate = mods + g_off, already tanh-ed;
+//             y = the sum of nparts planes [rows][h] pstride floats apart)
 //   mode & 2: xn = f16(LN(x) * (1 + mods[s_off + c]) * oscale)
 //   mode & 4: (with & 2) xn is [rows][2h]: the value v as the pair
 //             xn[r][c] = f16(v), xn[r][h + c] = f16(v - f16(v))
 hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16* xn,
                         const float* mods, int g_off, int s_off, float eps, float oscale,
-                        hipStream_t s);
+                        hipStream_t s, int nparts = 1, size_t pstride = 0);
+// How many K splits a 256 x 256 GEMM of this shape should run with so its
+// work units fill the CUs where whole tiles would not (1: no split); at
+// most maxs, and K / 64 divisible by it.
+int gemm_split_count(int M, int N, int K, int maxs);
 
 // txt_in norm over rows of width c (c % 4 == 0, c <= 8192): xn f16 =
 // f32(v / sqrt(mean(v^2) + eps)) * (w + 1), float64 sum of squares

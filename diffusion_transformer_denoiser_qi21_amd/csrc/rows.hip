@@ -35,11 +35,14 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // ───────────────────────────── rowop ─────────────────────────────
 // One wave per row, four rows per 256-thread block; lane l owns the float4
 // chunks l, l + 64, ... of the row (h/4 chunks, at most NJ per lane), so
-// both reductions are wave shuffles and no block barrier is needed.
+// both reductions are wave shuffles and no block barrier is needed.  y is
+// the sum of nparts planes pstride floats apart (the partial products of a
+// GEMM split over K), added in plane order.
 template <int MODE, int NJ>
 __global__ __launch_bounds__(256) void rowop_kernel(int rows, int h, float* __restrict__ x, const float* __restrict__ y,
-                                                   f16* __restrict__ xn, const float* __restrict__ mods,
-                                                   int g_off, int s_off, float eps, float oscale) {
+                                                   int nparts, size_t pstride, f16* __restrict__ xn,
+                                                   const float* __restrict__ mods, int g_off, int s_off, float eps,
+                                                   float oscale) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -52,7 +55,8 @@ __global__ __launch_bounds__(256) void rowop_kernel(int rows, int h, float* __re
     if (c < nc) {
       v[j] = xr[c];
       if (MODE & 1) {
-        const float4v yv = reinterpret_cast<const float4v*>(y + (size_t)row * h)[c];
+        float4v yv = reinterpret_cast<const float4v*>(y + (size_t)row * h)[c];
+        for (int p = 1; p < nparts; ++p) yv += reinterpret_cast<const float4v*>(y + p * pstride + (size_t)row * h)[c];
         const float4v g = reinterpret_cast<const float4v*>(mods + g_off)[c];
         v[j] = v[j] + g * yv;
         xr[c] = v[j];
@@ -92,15 +96,15 @@ __global__ __launch_bounds__(256) void rowop_kernel(int rows, int h, float* __re
 
 namespace {
 template <int NJ>
-hipError_t launch_rowop_nj(int rows, int h, int mode, float* x, const float* y, f16* xn, const float* mods,
-                           int g_off, int s_off, float eps, float oscale, hipStream_t s) {
+hipError_t launch_rowop_nj(int rows, int h, int mode, float* x, const float* y, int np, size_t ps, f16* xn,
+                           const float* mods, int g_off, int s_off, float eps, float oscale, hipStream_t s) {
   const dim3 grid((rows + 3) / 4), block(256);
   switch (mode) {
-    case 1: hipLaunchKernelGGL((rowop_kernel<1, NJ>), grid, block, 0, s, rows, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
-    case 2: hipLaunchKernelGGL((rowop_kernel<2, NJ>), grid, block, 0, s, rows, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
-    case 3: hipLaunchKernelGGL((rowop_kernel<3, NJ>), grid, block, 0, s, rows, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
-    case 6: hipLaunchKernelGGL((rowop_kernel<6, NJ>), grid, block, 0, s, rows, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
-    case 7: hipLaunchKernelGGL((rowop_kernel<7, NJ>), grid, block, 0, s, rows, h, x, y, xn, mods, g_off, s_off, eps, oscale); break;
+    case 1: hipLaunchKernelGGL((rowop_kernel<1, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
+    case 2: hipLaunchKernelGGL((rowop_kernel<2, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
+    case 3: hipLaunchKernelGGL((rowop_kernel<3, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
+    case 6: hipLaunchKernelGGL((rowop_kernel<6, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
+    case 7: hipLaunchKernelGGL((rowop_kernel<7, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -108,11 +112,12 @@ hipError_t launch_rowop_nj(int rows, int h, int mode, float* x, const float* y, 
 }  // namespace
 
 hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16* xn, const float* mods,
-                        int g_off, int s_off, float eps, float oscale, hipStream_t s) {
+                        int g_off, int s_off, float eps, float oscale, hipStream_t s, int nparts, size_t pstride) {
   if (rows <= 0) return hipSuccess;
-  if (h <= 1024) return launch_rowop_nj<4>(rows, h, mode, x, y, xn, mods, g_off, s_off, eps, oscale, s);
-  if (h <= 4096) return launch_rowop_nj<16>(rows, h, mode, x, y, xn, mods, g_off, s_off, eps, oscale, s);
-  return launch_rowop_nj<32>(rows, h, mode, x, y, xn, mods, g_off, s_off, eps, oscale, s);
+  if (h <= 1024) return launch_rowop_nj<4>(rows, h, mode, x, y, nparts, pstride, xn, mods, g_off, s_off, eps, oscale, s);
+  if (h <= 4096)
+    return launch_rowop_nj<16>(rows, h, mode, x, y, nparts, pstride, xn, mods, g_off, s_off, eps, oscale, s);
+  return launch_rowop_nj<32>(rows, h, mode, x, y, nparts, pstride, xn, mods, g_off, s_off, eps, oscale, s);
 }
 
 // ───────────────────────────── txt_in norm ─────────────────────────────

@@ -76,6 +76,10 @@ _SIGS = {
                                C.c_int, vp]),
     "qi21_op_gemm_pair": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, f32, f32, C.c_int,
                                     vp]),
+    "qi21_op_gemm_split": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, f32, C.c_int,
+                                     vp]),
+    "qi21_op_rowop_parts": (C.c_int, [C.c_int, C.c_int, C.c_int, vp, vp, C.c_int, C.c_size_t, vp, vp, C.c_int,
+                                      C.c_int, f32, f32, vp]),
     "qi21_op_gemm_resid": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, f32,
                                      C.c_int, vp]),
     "qi21_op_qk_gemm": (C.c_int, [C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, C.c_int, vp, vp, vp, vp, f32,
@@ -297,6 +301,15 @@ def qi21_op_flash(nq, heads, q, ldq, k1, ldk1, vt1, ldvt1, n1, k2, ldk2, vt2, ld
                   stream=None):
     _check(lib().qi21_op_flash(nq, heads, _p(q), ldq, _p(k1), ldk1, _p(vt1), ldvt1, n1, _p(k2), ldk2, _p(vt2), ldvt2,
                                n2, _p(vis), _p(out), ldo, oscale, _stream(stream)))
+
+
+def qi21_op_gemm_split(M, N, K, kw, A, lda, W, part, ksplit, oscale=1.0, tile=-1, stream=None):
+    _check(lib().qi21_op_gemm_split(M, N, K, kw, _p(A), lda, _p(W), _p(part), ksplit, oscale, tile, _stream(stream)))
+
+
+def qi21_op_rowop_parts(rows, h, mode, x, y, nparts, pstride, xn, mods, g_off, s_off, eps, oscale, stream=None):
+    _check(lib().qi21_op_rowop_parts(rows, h, mode, _p(x), _p(y), nparts, pstride, _p(xn), _p(mods), g_off, s_off,
+                                     eps, oscale, _stream(stream)))
 
 
 def qi21_op_rowop(rows, h, mode, x, y, xn, mods, g_off, s_off, eps, oscale, stream=None):

@@ -12,6 +12,7 @@
 #ifndef QI21_OPS_H
 #define QI21_OPS_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -59,6 +60,17 @@ int qi21_op_gemm_pair(int epi, int M, int N, int K, const void* A, int lda, cons
  * qi21_op_gemm. */
 int qi21_op_gemm_resid(int M, int N, int K, int kw, const void* A, int lda, const void* W, float* x, int ldx,
                        const float* gate, float oscale, int tile, void* stream);
+
+/* A GEMM split over K, for shapes whose whole tiles would leave most CUs
+ * idle: part f32 [ksplit][M][N] with part[p][m][c] = oscale * sum over k
+ * in [p K/ksplit, (p+1) K/ksplit) of A[m][k] W[c][k % kw]; the sum of the
+ * planes is the product (qi21_op_rowop_parts adds them into a gated
+ * residual).  A f16 [M][lda], W f16 [N][kw], K == kw or 2 kw as for
+ * qi21_op_gemm_resid.  Requires M >= 1, N % 256 == 0, 1 <= ksplit <= 8,
+ * K % (64 ksplit) == 0, kw % 64 == 0, lda % 8 == 0, lda >= K, 16-byte
+ * aligned pointers.  tile: -1 or 0 (4 waves), 2 (8 waves). */
+int qi21_op_gemm_split(int M, int N, int K, int kw, const void* A, int lda, const void* W, float* part, int ksplit,
+                       float oscale, int tile, void* stream);
 
 /* The q|k projection with the per-head RMSNorm + RoPE in its epilogue
  * ([QI] block_cpu, qk_norm_rope: the fused form of the QKV GEMM's q|k
@@ -111,6 +123,13 @@ int qi21_op_flash(int nq, int heads, const void* q, int ldq, const void* k1, int
  * g_off, s_off % 4 == 0. */
 int qi21_op_rowop(int rows, int h, int mode, float* x, const float* y, void* xn, const float* mods, int g_off,
                   int s_off, float eps, float oscale, void* stream);
+
+/* qi21_op_rowop with y the sum of nparts planes [rows][h] pstride floats
+ * apart, added in plane order (the partial products of qi21_op_gemm_split).
+ * Requires 1 <= nparts <= 8 and, for nparts > 1, pstride >= rows * h;
+ * otherwise as qi21_op_rowop. */
+int qi21_op_rowop_parts(int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride, void* xn,
+                        const float* mods, int g_off, int s_off, float eps, float oscale, void* stream);
 
 /* Per-head RMSNorm(norm_q | norm_k) then interleaved-pair RoPE on the q
  * (column 0) and k (column heads*128) parts of panel f16 [rows][ldp], in

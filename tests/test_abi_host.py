@@ -126,6 +126,12 @@ def test_op_entry_points_validate_shapes_on_host():
         lambda: Q.qi21_op_qkrope(4, 2, 1, 256, 1, 1, 1, 1, 1e-6, stream=0),
         lambda: Q.qi21_op_embed(4, 100, 1, 1, 1, stream=0),
         lambda: Q.qi21_op_final(4, 100, 1, 1, 1, 1e-6, 1, 1, stream=0),
+        lambda: Q.qi21_op_gemm_split(16, 256, 192, 192, 1, 192, 1, 1, 2, stream=0),     # K % (64 ksplit)
+        lambda: Q.qi21_op_gemm_split(16, 256, 256, 256, 1, 256, 1, 1, 9, stream=0),     # ksplit > 8
+        lambda: Q.qi21_op_gemm_split(16, 128, 256, 256, 1, 256, 1, 1, 2, stream=0),     # N % 256
+        lambda: Q.qi21_op_gemm_split(16, 256, 256, 256, 1, 256, 1, 1, 2, tile=1, stream=0),
+        lambda: Q.qi21_op_rowop_parts(4, 256, 3, 1, 1, 0, 1024, 1, 1, 0, 0, 1e-6, 1.0, stream=0),  # nparts 0
+        lambda: Q.qi21_op_rowop_parts(4, 256, 3, 1, 1, 2, 1000, 1, 1, 0, 0, 1e-6, 1.0, stream=0),  # planes overlap
     ]
     for c in cases:
         with pytest.raises(Q.Qi21Error) as e:

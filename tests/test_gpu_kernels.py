@@ -388,6 +388,65 @@ def test_gemm_k_depths(K, tile):
 
 
 @pytest.mark.parametrize("tile", [0, 2])
+@pytest.mark.parametrize("ksplit,K", [(2, 256), (3, 576), (4, 4352), (4, 1024)])
+@pytest.mark.parametrize("M", [1, 300, 1024])
+def test_gemm_split_partials(M, ksplit, K, tile):
+    """Each partial plane is the product over its quarter (third, half) of K;
+    the planes add up to the whole product.  The pair form (A of K columns,
+    W rows of kw = K / 2, each read twice) splits the same way."""
+    q = Q()
+    N = 512
+    A = f16_host(14, 1, (M, K), 1.0)
+    W = f16_host(14, 2, (N, K), 0.05)
+    part = torch.zeros(ksplit, M, N, device="cuda")
+    q.qi21_op_gemm_split(M, N, K, K, dev(A, torch.float16), K, dev(W, torch.float16), part, ksplit, 0.5, tile)
+    sync()
+    ks = K // ksplit
+    got = part.cpu().numpy()
+    for p in range(ksplit):
+        want = O.lin(A[:, p * ks:(p + 1) * ks], W[:, p * ks:(p + 1) * ks]) * np.float32(0.5)
+        assert rel(got[p], want) < F32_TOL * 10
+    assert rel(got.sum(axis=0), O.lin(A, W) * np.float32(0.5)) < F32_TOL * 10
+    if K % (128 * ksplit) == 0:
+        kw = K // 2
+        Wp = W[:, :kw]
+        part.zero_()
+        q.qi21_op_gemm_split(M, N, K, kw, dev(A, torch.float16), K, dev(Wp, torch.float16), part, ksplit, 1.0, tile)
+        sync()
+        want = A[:, :kw].astype(np.float64) @ Wp.astype(np.float64).T + A[:, kw:].astype(np.float64) @ Wp.astype(np.float64).T
+        assert rel(part.cpu().numpy().sum(axis=0), want) < F32_TOL * 10
+
+
+@pytest.mark.parametrize("nparts", [1, 2, 4])
+@pytest.mark.parametrize("mode", [1, 3, 7])
+def test_rowop_adds_partial_planes(mode, nparts):
+    """x += gate * (sum of the planes, in order), then the modulated LayerNorm
+    (and its f16 pair for mode 7), against the same computation in numpy."""
+    q = Q()
+    rows, h = 37, 4096
+    x = inputs.host_array(15, 1, (rows, h), 1.0)
+    y = inputs.host_array(15, 2, (nparts, rows + 3, h), 1.0)  # planes rows + 3 rows apart
+    mods = inputs.host_array(15, 3, (4 * h,), 0.1)
+    g_off, s_off, eps, oscale = 3 * h, 0, 1e-6, 0.25
+    dx, xn = dev(x), torch.zeros(rows, 2 * h if mode & 4 else h, device="cuda", dtype=torch.float16)
+    q.qi21_op_rowop_parts(rows, h, mode, dx, dev(y), nparts, (rows + 3) * h, xn, dev(mods), g_off, s_off, eps, oscale)
+    sync()
+    ysum = y[0, :rows].copy()
+    for p in range(1, nparts):
+        ysum = ysum + y[p, :rows]
+    xw = x + mods[g_off:g_off + h] * ysum
+    assert rel(dx.cpu().numpy(), xw) < F32_TOL
+    if mode & 2:
+        v = O.layer_norm(xw, eps) * (1.0 + mods[s_off:s_off + h]) * np.float32(oscale)
+        got = xn.float().cpu().numpy()
+        if mode & 4:
+            got = got[:, :h] + got[:, h:]
+            assert rel(got, v) < F32_TOL
+        else:
+            assert rel(got, v) < F16_TOL
+
+
+@pytest.mark.parametrize("tile", [0, 2])
 @pytest.mark.parametrize("M", [1, 77, 300, 1600])
 def test_qk_gemm_fused_norm_rope(M, tile):
     """q|k projection with the per-head RMSNorm + RoPE in the epilogue vs
