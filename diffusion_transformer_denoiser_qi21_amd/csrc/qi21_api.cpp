@@ -446,18 +446,35 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
         HIP_OK(qi21::launch_flash(f, s));
       }
     }
-    {  // x += tanh(g1) (att Wo^T) in the O GEMM's epilogue
-      Scope sc(m, C_O, s);
-      qi21::GemmArgs o = gemm_args(rows, H, H, a.att, H, m->wo[l], a.x, H, p2(gd.ao));
-      o.gate = a.mods + H;
-      HIP_OK(qi21::launch_gemm(qi21::EPI_RESID, o, tile, s));
-    }
     // with ffn_pair the FFN input and the hidden are f16 (hi, lo) pairs in
     // rows of 2H / 2I and both GEMMs run over K doubled, each W row twice
     const int pf = m->o.ffn_pair ? 2 : 1;
-    {  // xn = LN(x)(1 + s2)
-      Scope sc(m, C_ROW, s);
-      HIP_OK(qi21::launch_rowop(rows, H, pf == 2 ? 6 : 2, a.x, nullptr, a.xn, a.mods, 0, 2 * H, g.eps, p2(-gd.ffn), s));
+    // the O GEMM split over K like the down GEMM below, or with the gated
+    // residual in its epilogue
+    const int spo = tile < 0 ? qi21::gemm_split_count(rows, H, H, 4) : 1;
+    if (spo > 1 && (size_t)spo * rows <= 4 * std::min<size_t>(a.cap, 2048)) {
+      {
+        Scope sc(m, C_O, s);
+        qi21::GemmArgs o = gemm_args(rows, H, H, a.att, H, m->wo[l], a.part, H, p2(gd.ao));
+        o.ksplit = spo;
+        o.pstride = (size_t)rows * H;
+        HIP_OK(qi21::launch_gemm(qi21::EPI_F32, o, 0, s));
+      }
+      Scope sc(m, C_ROW, s);  // x += tanh(g1) sum_p part_p; xn = LN(x)(1 + s2)
+      HIP_OK(qi21::launch_rowop(rows, H, pf == 2 ? 7 : 3, a.x, a.part, a.xn, a.mods, H, 2 * H, g.eps, p2(-gd.ffn), s,
+                                spo, (size_t)rows * H));
+    } else {
+      {  // x += tanh(g1) (att Wo^T) in the O GEMM's epilogue
+        Scope sc(m, C_O, s);
+        qi21::GemmArgs o = gemm_args(rows, H, H, a.att, H, m->wo[l], a.x, H, p2(gd.ao));
+        o.gate = a.mods + H;
+        HIP_OK(qi21::launch_gemm(qi21::EPI_RESID, o, tile, s));
+      }
+      {  // xn = LN(x)(1 + s2)
+        Scope sc(m, C_ROW, s);
+        HIP_OK(qi21::launch_rowop(rows, H, pf == 2 ? 6 : 2, a.x, nullptr, a.xn, a.mods, 0, 2 * H, g.eps, p2(-gd.ffn),
+                                  s));
+      }
     }
     {
       Scope sc(m, C_W13, s);
