@@ -340,10 +340,11 @@ __device__ __forceinline__ int dswz(int r) { return (r >> 1) & 7; }
 
 }  // namespace
 
-// Persistent over tiles: block b runs on XCD b % 8 and walks that XCD's
-// contiguous run of the grouped tile sequence, 32 blocks abreast.  The
-// next tile's first LDS stages are fetched while the current tile's
-// epilogue stores drain.  NW = 4 waves of 128 x 128 (one per SIMD) or 8
+// Persistent over work units (a tile, or with ksplit > 1 a tile's share of
+// the k-tiles; units of one share come first): block b runs on XCD b % 8
+// and walks that XCD's contiguous run of the grouped unit sequence, 32
+// blocks abreast.  The next unit's first k-tiles are fetched while the
+// current unit's epilogue stores drain.  NW = 4 waves of 128 x 128 (one per SIMD) or 8
 // waves of 128 x 64 (two per SIMD, so one wave's issue stalls, barrier
 // waits and epilogue are covered by the other's MFMAs).
 template <int EPI, int NW>
