@@ -304,6 +304,36 @@ def test_rowop_modes(mode, rows, h):
         assert torch.all(xn == 0)
 
 
+@pytest.mark.parametrize("rows,h,mode", [(2048, 4096, 3), (2049, 4096, 3), (2049, 4096, 2), (5, 8192, 3),
+                                         (5, 2052, 7), (3000, 2048, 1), (64, 2044, 3)])
+def test_rowop_row_forms(rows, h, mode):
+    """Both row-pass forms and the choice between them: one block per row for
+    wide rows, one wave per row for narrower rows and for long passes with a
+    residual (more than 2048 rows); widths that are not a multiple of the
+    block's 1024-float stride leave threads with partial chunk sets."""
+    q = Q()
+    x = inputs.host_array(16, 1, (rows, h), 1.0)
+    y = inputs.host_array(16, 2, (rows, h), 0.5)
+    mods = inputs.host_array(16, 3, (4 * h,), 0.1)
+    g_off, s_off, eps, oscale = 3 * h, 2 * h, 1e-6, 0.25
+    dx, dy, dm = dev(x), dev(y), dev(mods)
+    xn = torch.zeros(rows, 2 * h if mode & 4 else h, device="cuda", dtype=torch.float16)
+    q.qi21_op_rowop(rows, h, mode, dx, dy, xn, dm, g_off, s_off, eps, oscale)
+    sync()
+    xe = O.gated_add(x, y, mods[g_off:g_off + h]) if mode & 1 else x
+    assert rel(dx.cpu().numpy(), xe) < 1e-6
+    if mode & 2:
+        want = O.norm_mod(xe, mods[s_off:s_off + h], eps, dt=np.float64) * oscale
+        o = xn.float().cpu().numpy()
+        if mode & 4:
+            _check_pair(xn[:, :h].cpu().numpy(), xn[:, h:].cpu().numpy())
+            assert rel(o[:, :h].astype(np.float64) + o[:, h:], want) < 2e-6
+        else:
+            assert rel(o, want) < F16_TOL
+    else:
+        assert torch.all(xn == 0)
+
+
 @pytest.mark.parametrize("kdst", [False, True])
 @pytest.mark.parametrize("rows", [5, 300])
 def test_qkrope(rows, kdst):
