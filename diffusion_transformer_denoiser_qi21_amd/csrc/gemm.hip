@@ -158,16 +158,16 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
       }
       const float inv = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
       if (row < a.M) {
-        const float* cr = a.rcos + (size_t)row * 64;
-        const float* sr = a.rsin + (size_t)row * 64;
+        // the row's packed table: cos and sin of the lane's two pairs in one 16-byte load
+        const float* tr = a.rope + (size_t)row * 128;
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int d = j * 32 + 8 * g + 4 * hsel;  // dims d .. d+3: pairs d/2, d/2 + 1
             const floatx4 w = *reinterpret_cast<const floatx4*>(nw + d);
-            const floatx2 cs = *reinterpret_cast<const floatx2*>(cr + d / 2);
-            const floatx2 sn = *reinterpret_cast<const floatx2*>(sr + d / 2);
+            const floatx4 t = *reinterpret_cast<const floatx4*>(tr + d);  // cos d/2, d/2+1, sin d/2, d/2+1
+            const floatx2 cs = floatx2{t[0], t[1]}, sn = floatx2{t[2], t[3]};
             const float a0 = (acc[i][j][4 * g] * inv) * w[0], b0 = (acc[i][j][4 * g + 1] * inv) * w[1];
             const float a1 = (acc[i][j][4 * g + 2] * inv) * w[2], b1 = (acc[i][j][4 * g + 3] * inv) * w[3];
             *reinterpret_cast<half4*>(dst + (size_t)row * ld + d) =

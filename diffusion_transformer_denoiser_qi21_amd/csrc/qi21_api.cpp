@@ -65,8 +65,8 @@ struct Acts {
   float* part = nullptr; // [4 min(cap, 2048)][H] partial products of a down GEMM split over K
   float* mods = nullptr; // [4H] tanh-ed modulation of the pass
   float* out = nullptr;  // [cap][64] velocity before the finite check
-  float* rc = nullptr;   // [cap][64] RoPE cos / sin of the pass's rows when
-  float* rs = nullptr;   // they come from several programs
+  float* rcs = nullptr;  // [cap][128] packed RoPE table of the pass's rows when
+                         // they come from several programs, or of a prefill
 };
 
 struct Prog {
@@ -76,6 +76,7 @@ struct Prog {
   std::vector<f16*> vtc;  // per layer [H][ldc] V^T (x 2^-qkv)
   float* rc = nullptr;    // [n][64] target RoPE cos
   float* rs = nullptr;    // [n][64] target RoPE sin
+  float* rcs = nullptr;   // [n][128] the same, packed for the q|k GEMM epilogue
 };
 
 struct Prof {
@@ -148,10 +149,10 @@ size_t acts_bytes(const qi21_geom& g, bool pair, int cap, size_t* parts) {
   const size_t H = g.hidden, I = g.inter, c = cap, f = pair ? 2 : 1;
   // slot 5: the partial products of a down GEMM split over K (4 planes of
   // up to 2048 rows; split GEMMs only run at fewer than 2048 rows)
-  const size_t p[11] = {c * H * 4, c * H * 2 * f, c * 2 * H * 2, H * c * 2, c * H * 2, 4 * std::min<size_t>(c, 2048) * H * 4,
-                        c * I * 2 * f, 4 * H * 4, c * 64 * 4, c * 64 * 4, c * 64 * 4};
+  const size_t p[10] = {c * H * 4, c * H * 2 * f, c * 2 * H * 2, H * c * 2, c * H * 2, 4 * std::min<size_t>(c, 2048) * H * 4,
+                        c * I * 2 * f, 4 * H * 4, c * 64 * 4, c * 128 * 4};
   size_t t = 0;
-  for (int i = 0; i < 11; ++i) {
+  for (int i = 0; i < 10; ++i) {
     if (parts) parts[i] = p[i];
     t += p[i];
   }
@@ -159,11 +160,11 @@ size_t acts_bytes(const qi21_geom& g, bool pair, int cap, size_t* parts) {
 }
 
 void free_acts(qi21_model* m) {
-  size_t parts[11];
+  size_t parts[10];
   acts_bytes(m->g, m->o.ffn_pair != 0, m->acts.cap, parts);
-  void* ptrs[11] = {m->acts.x, m->acts.xn, m->acts.panel, m->acts.vt, m->acts.att, m->acts.part,
-                    m->acts.hid, m->acts.mods, m->acts.out, m->acts.rc, m->acts.rs};
-  for (int i = 0; i < 11; ++i) dfree(m, ptrs[i], parts[i]);
+  void* ptrs[10] = {m->acts.x, m->acts.xn, m->acts.panel, m->acts.vt, m->acts.att, m->acts.part,
+                    m->acts.hid, m->acts.mods, m->acts.out, m->acts.rcs};
+  for (int i = 0; i < 10; ++i) dfree(m, ptrs[i], parts[i]);
   m->acts = Acts{};
 }
 
@@ -173,10 +174,10 @@ int ensure_acts(qi21_model* m, int rows, hipStream_t s) {
   if (m->acts.cap >= rows) return QI21_OK;
   free_acts(m);
   const int cap = (int)round_up((size_t)rows, 256);
-  size_t parts[11];
+  size_t parts[10];
   acts_bytes(m->g, m->o.ffn_pair != 0, cap, parts);
-  void* p[11];
-  for (int i = 0; i < 11; ++i) {
+  void* p[10];
+  for (int i = 0; i < 10; ++i) {
     if (!parts[i]) {
       p[i] = nullptr;
       continue;
@@ -200,8 +201,7 @@ int ensure_acts(qi21_model* m, int rows, hipStream_t s) {
   a.hid = (f16*)p[6];
   a.mods = (float*)p[7];
   a.out = (float*)p[8];
-  a.rc = (float*)p[9];
-  a.rs = (float*)p[10];
+  a.rcs = (float*)p[9];
   return QI21_OK;
 }
 
@@ -211,9 +211,10 @@ void free_prog(qi21_model* m, Prog& p) {
   for (auto* v : p.vtc) dfree(m, v, H * p.ldc * 2);
   dfree(m, p.rc, (size_t)p.n * 64 * 4);
   dfree(m, p.rs, (size_t)p.n * 64 * 4);
+  dfree(m, p.rcs, (size_t)p.n * 128 * 4);
   p.kc.clear();
   p.vtc.clear();
-  p.rc = p.rs = nullptr;
+  p.rc = p.rs = p.rcs = nullptr;
 }
 
 size_t time_floats(const qi21_geom& g, int i) {
@@ -344,6 +345,7 @@ struct Seg {
   Prog* p;           // step: the program whose cache the rows attend to
   const float* rc;   // RoPE tables of these rows
   const float* rs;
+  const float* rcs;  // the same, packed ([rows][128], launch_rope_pack)
 };
 
 // Blocks of one pass over `rows` rows of m->acts.  Prefill: one segment,
@@ -362,15 +364,12 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
   // otherwise the qkv GEMM writes q|k and V^T and qkrope follows.
   const int tile_qk = tile >= 0 ? tile : qi21::gemm_pick_tile(rows, 2 * H, H);
   const bool fused = tile_qk == 0 || tile_qk == 2;
-  const float* rcos = segs[0].rc;
-  const float* rsin = segs[0].rs;
+  const float* rope = segs[0].rcs;
   if (fused && (segs.size() > 1 || segs[0].row0 != 0)) {  // one table for all rows of the pass
-    for (const Seg& sg : segs) {
-      HIP_OK(hipMemcpyAsync(a.rc + (size_t)sg.row0 * 64, sg.rc, (size_t)sg.rows * 64 * 4, hipMemcpyDeviceToDevice, s));
-      HIP_OK(hipMemcpyAsync(a.rs + (size_t)sg.row0 * 64, sg.rs, (size_t)sg.rows * 64 * 4, hipMemcpyDeviceToDevice, s));
-    }
-    rcos = a.rc;
-    rsin = a.rs;
+    for (const Seg& sg : segs)
+      HIP_OK(hipMemcpyAsync(a.rcs + (size_t)sg.row0 * 128, sg.rcs, (size_t)sg.rows * 128 * 4, hipMemcpyDeviceToDevice,
+                            s));
+    rope = a.rcs;
   }
   for (int l = 0; l < m->nb; ++l) {
     const bool last = l + 1 == m->nb;
@@ -383,8 +382,7 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
       qi21::GemmArgs qk = gemm_args(rows, 2 * H, H, a.xn, H, m->wqkv[l], a.panel, 2 * H, 1.0f);
       qk.nq = m->nq[l];
       qk.nk = m->nk[l];
-      qk.rcos = rcos;
-      qk.rsin = rsin;
+      qk.rope = rope;
       qk.eps = g.eps * p2(-2 * gd.attn);
       qk.kout = pre ? pre->kc[l] : a.panel + H;
       qk.ldk = pre ? H : 2 * H;
@@ -716,7 +714,8 @@ int qi21_prefill(qi21_model* m, uint64_t key, int lp, int n, const float* x, con
       if (v && !k) { dfree(m, v, H * p.ldc * 2); p.vtc.pop_back(); }
     }
   }
-  ok = ok && (p.rc = (float*)dalloc(m, (size_t)n * 64 * 4)) && (p.rs = (float*)dalloc(m, (size_t)n * 64 * 4));
+  ok = ok && (p.rc = (float*)dalloc(m, (size_t)n * 64 * 4)) && (p.rs = (float*)dalloc(m, (size_t)n * 64 * 4)) &&
+       (p.rcs = (float*)dalloc(m, (size_t)n * 128 * 4));
   if (!ok) {
     free_prog(m, p);
     return fail(QI21_ENOMEM, "prefix cache of %d rows x %d blocks did not fit", lp, m->nb);
@@ -724,13 +723,15 @@ int qi21_prefill(qi21_model* m, uint64_t key, int lp, int n, const float* x, con
   for (auto* v : p.vtc) HIP_OK(qi21::launch_fill32(v, 0u, H * p.ldc / 2, s));
   HIP_OK(hipMemcpyAsync(p.rc, rope_t_cos, (size_t)n * 64 * 4, hipMemcpyDeviceToDevice, s));
   HIP_OK(hipMemcpyAsync(p.rs, rope_t_sin, (size_t)n * 64 * 4, hipMemcpyDeviceToDevice, s));
+  HIP_OK(qi21::launch_rope_pack(n, rope_t_cos, rope_t_sin, p.rcs, s));
   // the prefix pass
   Acts& a = m->acts;
   const Guard gd = guards(m);
   HIP_OK(qi21::launch_mods((int)H, mods0, a.mods, s));
   HIP_OK(hipMemcpyAsync(a.x, x, (size_t)lp * H * 4, hipMemcpyDeviceToDevice, s));
   HIP_OK(qi21::launch_rowop(lp, (int)H, 2, a.x, nullptr, a.xn, a.mods, 0, 0, m->g.eps, p2(-gd.attn), s));
-  std::vector<Seg> segs{Seg{0, lp, nullptr, rope_p_cos, rope_p_sin}};
+  HIP_OK(qi21::launch_rope_pack(lp, rope_p_cos, rope_p_sin, a.rcs, s));
+  std::vector<Seg> segs{Seg{0, lp, nullptr, rope_p_cos, rope_p_sin, a.rcs}};
   rc = run_blocks(m, lp, segs, &p, vis, s);
   if (rc == QI21_OK) rc = sync_stream(s);
   prof_collect(m);
@@ -775,7 +776,7 @@ int qi21_step_batch(qi21_model* m, int nprog, const uint64_t* keys, const float*
     HIP_OK(qi21::launch_fill32(m->dflag, 0u, 1, s));
     HIP_OK(qi21::launch_mods(H, mods, a.mods, s));
     for (int i = 0; i < nprog; ++i) {
-      segs.push_back(Seg{start[i], ps[i]->n, ps[i], ps[i]->rc, ps[i]->rs});
+      segs.push_back(Seg{start[i], ps[i]->n, ps[i], ps[i]->rc, ps[i]->rs, ps[i]->rcs});
       HIP_OK(qi21::launch_embed(ps[i]->n, H, xtok[i], m->img_in, a.x + (size_t)start[i] * H, s));
     }
   }
@@ -1033,20 +1034,26 @@ int qi21_op_gemm_split(int M, int N, int K, int kw, const void* A, int lda, cons
   return QI21_OK;
 }
 
+int qi21_op_rope_pack(int n, const float* cos, const float* sin, float* out, void* stream) {
+  g_err.clear();
+  if (n < 1) return fail(QI21_EINVAL, "rope pack n %d", n);
+  if (!cos || !sin || !out) return fail(QI21_EINVAL, "rope pack pointer NULL");
+  HIP_OK(qi21::launch_rope_pack(n, cos, sin, out, (hipStream_t)stream));
+  return QI21_OK;
+}
+
 int qi21_op_qk_gemm(int M, int H, const void* A, int lda, const void* W, void* q_out, int ldq, void* k_out, int ldk,
-                    const float* norm_q, const float* norm_k, const float* cos, const float* sin, float eps, int tile,
-                    void* stream) {
+                    const float* norm_q, const float* norm_k, const float* rope, float eps, int tile, void* stream) {
   g_err.clear();
   if (M < 1 || H < 128 || H % 128 || lda % 8 || lda < H || ldq % 4 || ldk % 4 || ldq < H || ldk < H)
     return fail(QI21_EINVAL, "qk gemm M %d H %d lda %d ldq %d ldk %d", M, H, lda, ldq, ldk);
-  if (!A || !W || !q_out || !k_out || !norm_q || !norm_k || !cos || !sin) return fail(QI21_EINVAL, "qk gemm pointer NULL");
+  if (!A || !W || !q_out || !k_out || !norm_q || !norm_k || !rope) return fail(QI21_EINVAL, "qk gemm pointer NULL");
   if (tile == -1) tile = 0;
   if (tile != 0 && tile != 2) return fail(QI21_EINVAL, "qk gemm tile %d (0 or 2)", tile);
   qi21::GemmArgs a = gemm_args(M, 2 * H, H, (const f16*)A, lda, (const f16*)W, q_out, ldq, 1.0f);
   a.nq = norm_q;
   a.nk = norm_k;
-  a.rcos = cos;
-  a.rsin = sin;
+  a.rope = rope;
   a.eps = eps;
   a.kout = (f16*)k_out;
   a.ldk = ldk;

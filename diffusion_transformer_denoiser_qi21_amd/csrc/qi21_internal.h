@@ -35,7 +35,8 @@ enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 
 //   EPI_QKROPE: N = 2H, W = the q then k projection rows; per row and
 //               128-column head: RMSNorm of the accumulators (weights nq for
 //               q heads, nk for k heads, eps in the accumulators' scale),
-//               then interleaved-pair RoPE with rcos / rsin [M][64]; q heads
+//               then interleaved-pair RoPE with the packed table rope
+//               [M][128] (launch_rope_pack); q heads
 //               to out f16 [M][ldo], k heads to kout f16 [M][ldk] (column
 //               c - H).  Large-M kernels only (tile 0 / 2).
 //   EPI_VT:     out f16 [M][ldo] = acc * oscale with output column c stored at
@@ -59,7 +60,7 @@ struct GemmArgs {
   float oscale, inscale;
   // EPI_QKROPE
   const float* nq = nullptr; const float* nk = nullptr;
-  const float* rcos = nullptr; const float* rsin = nullptr;
+  const float* rope = nullptr;  // [M][128]: per two pairs (2m, 2m+1): cos 2m, cos 2m+1, sin 2m, sin 2m+1
   float eps = 0.0f;
   f16* kout = nullptr; int ldk = 0;
   // EPI_VT
@@ -156,5 +157,9 @@ hipError_t launch_to_f32(int src_dtype, const void* src, size_t n, float* dst, h
 
 // fill count 32-bit words with value (a kernel, so it is safe to capture)
 hipError_t launch_fill32(void* p, uint32_t value, size_t count, hipStream_t s);
+// RoPE tables cos / sin [n][64] packed into out [n][128] for the q|k GEMM
+// epilogue: out[r][4m + (0, 1, 2, 3)] = cos[r][2m], cos[r][2m + 1],
+// sin[r][2m], sin[r][2m + 1]
+hipError_t launch_rope_pack(int n, const float* cos, const float* sin, float* out, hipStream_t s);
 
 }  // namespace qi21

@@ -14,6 +14,7 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -221,6 +222,27 @@ hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16
   if (h <= 4096)
     return launch_rowop_wide<4>(rows, h, mode, x, y, nparts, pstride, xn, mods, g_off, s_off, eps, oscale, s);
   return launch_rowop_wide<8>(rows, h, mode, x, y, nparts, pstride, xn, mods, g_off, s_off, eps, oscale, s);
+}
+
+// ───────────────────────────── RoPE table packing ─────────────────────────────
+// One thread per float4 of the packed table: out[r][4m ..] = cos[r][2m],
+// cos[r][2m + 1], sin[r][2m], sin[r][2m + 1], so the q|k epilogue reads the
+// cos and sin of two adjacent pairs in one 16-byte load.
+__global__ __launch_bounds__(256) void rope_pack_kernel(int n, const float* __restrict__ cosb,
+                                                        const float* __restrict__ sinb, float* __restrict__ out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;  // (row, m)
+  if (i >= (long)n * 32) return;
+  const long r = i >> 5;
+  const int mm = (int)(i & 31);
+  const floatx2 c = *reinterpret_cast<const floatx2*>(cosb + r * 64 + 2 * mm);
+  const floatx2 s = *reinterpret_cast<const floatx2*>(sinb + r * 64 + 2 * mm);
+  *reinterpret_cast<float4v*>(out + r * 128 + 4 * mm) = float4v{c[0], c[1], s[0], s[1]};
+}
+
+hipError_t launch_rope_pack(int n, const float* cos, const float* sin, float* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_pack_kernel, dim3((unsigned)(((long)n * 32 + 255) / 256)), dim3(256), 0, s, n, cos, sin, out);
+  return hipGetLastError();
 }
 
 // ───────────────────────────── txt_in norm ─────────────────────────────

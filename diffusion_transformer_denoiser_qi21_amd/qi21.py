@@ -82,8 +82,9 @@ _SIGS = {
                                       C.c_int, f32, f32, vp]),
     "qi21_op_gemm_resid": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, f32,
                                      C.c_int, vp]),
-    "qi21_op_qk_gemm": (C.c_int, [C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, C.c_int, vp, vp, vp, vp, f32,
+    "qi21_op_qk_gemm": (C.c_int, [C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, C.c_int, vp, vp, vp, f32,
                                   C.c_int, vp]),
+    "qi21_op_rope_pack": (C.c_int, [C.c_int, vp, vp, vp, vp]),
     "qi21_op_vt_gemm": (C.c_int, [C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, f32, C.c_int, vp]),
     "qi21_op_flash": (C.c_int, [C.c_int, C.c_int, vp, C.c_int, vp, C.c_int, vp, C.c_int, C.c_int, vp, C.c_int, vp,
                                 C.c_int, C.c_int, vp, vp, C.c_int, f32, vp]),
@@ -288,9 +289,13 @@ def qi21_op_gemm_resid(M, N, K, kw, A, lda, W, x, ldx, gate, oscale=1.0, tile=-1
                                     _stream(stream)))
 
 
-def qi21_op_qk_gemm(M, H, A, lda, W, q_out, ldq, k_out, ldk, norm_q, norm_k, cos, sin, eps, tile=-1, stream=None):
+def qi21_op_qk_gemm(M, H, A, lda, W, q_out, ldq, k_out, ldk, norm_q, norm_k, rope, eps, tile=-1, stream=None):
     _check(lib().qi21_op_qk_gemm(M, H, _p(A), lda, _p(W), _p(q_out), ldq, _p(k_out), ldk, _p(norm_q), _p(norm_k),
-                                 _p(cos), _p(sin), eps, tile, _stream(stream)))
+                                 _p(rope), eps, tile, _stream(stream)))
+
+
+def qi21_op_rope_pack(n, cos, sin, out, stream=None):
+    _check(lib().qi21_op_rope_pack(n, _p(cos), _p(sin), _p(out), _stream(stream)))
 
 
 def qi21_op_vt_gemm(H, nkeys, K, Wv, lda, X, out, ldo, oscale=1.0, tile=-1, stream=None):

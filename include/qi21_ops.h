@@ -78,14 +78,22 @@ int qi21_op_gemm_split(int M, int N, int K, int kw, const void* A, int lda, cons
  * [2H][H] = to_q rows then to_k rows.  For every row and 128-column head
  * the f32 accumulators a are normalised, a * rsqrt(mean(a^2) + eps) *
  * norm_q / norm_k [128] (eps in the accumulators' scale), then pairs
- * (2j, 2j+1) are rotated by cos / sin [M][64] (row-major, column j); q
- * heads go to q_out f16 [M][ldq], k heads to k_out f16 [M][ldk], both at
- * column head*128.  Requires M >= 1, H % 128 == 0, lda % 8 == 0, lda >= H,
- * ldq, ldk >= H and % 4 == 0, 16-byte aligned pointers.  tile: -1 or 0 (4
+ * (2j, 2j+1) are rotated by the RoPE cos / sin of row r, read from the
+ * packed table rope f32 [M][128] that qi21_op_rope_pack writes; q heads go
+ * to q_out f16 [M][ldq], k heads to k_out f16 [M][ldk], both at column
+ * head*128.  Requires M >= 1, H % 128 == 0, lda % 8 == 0, lda >= H, ldq,
+ * ldk >= H and % 4 == 0, 16-byte aligned pointers.  tile: -1 or 0 (4
  * waves), 2 (8 waves). */
 int qi21_op_qk_gemm(int M, int H, const void* A, int lda, const void* W, void* q_out, int ldq, void* k_out, int ldk,
-                    const float* norm_q, const float* norm_k, const float* cos, const float* sin, float eps, int tile,
-                    void* stream);
+                    const float* norm_q, const float* norm_k, const float* rope, float eps, int tile, void* stream);
+
+/* The RoPE tables of n rows ([QI] rope_tables: cos, sin f32 [n][64],
+ * row-major, column j = pair (2j, 2j+1)) packed for qi21_op_qk_gemm:
+ * out f32 [n][128] with out[r][4m + 0..3] = cos[r][2m], cos[r][2m+1],
+ * sin[r][2m], sin[r][2m+1], so the epilogue reads the cos and sin of two
+ * adjacent pairs in one 16-byte load.  All three are device pointers,
+ * 8-byte aligned (out 16-byte).  Requires n >= 1; EINVAL otherwise. */
+int qi21_op_rope_pack(int n, const float* cos, const float* sin, float* out, void* stream);
 
 /* V^T of nkeys rows: out[d][vt_pos(j)] = oscale * sum_k Wv[d][k] X[j][k]
  * for d < H, j < nkeys, where vt_pos swaps bits 2 and 3 of j (the key

@@ -119,8 +119,11 @@ def test_op_entry_points_validate_shapes_on_host():
         lambda: Q.qi21_op_gemm(4, 16, 128, 64, 1, 64, 1, 1, 64, stream=0),            # swiglu2 needs ldo >= N
         lambda: Q.qi21_op_gemm_pair(1, 16, 128, 64, 1, 100, 1, 1, 128, stream=0),     # lda < 2K
         lambda: Q.qi21_op_gemm_pair(3, 16, 384, 64, 1, 128, 1, 1, 384, stream=0),     # no qkv pair epilogue
-        lambda: Q.qi21_op_qk_gemm(16, 200, 1, 256, 1, 1, 256, 1, 256, 1, 1, 1, 1, 1e-6, stream=0),  # H % 128
-        lambda: Q.qi21_op_qk_gemm(16, 256, 1, 256, 1, 1, 256, 1, 256, 1, 1, 1, 1, 1e-6, tile=1, stream=0),
+        lambda: Q.qi21_op_qk_gemm(16, 200, 1, 256, 1, 1, 256, 1, 256, 1, 1, 1, 1e-6, stream=0),  # H % 128
+        lambda: Q.qi21_op_qk_gemm(16, 256, 1, 256, 1, 1, 256, 1, 256, 1, 1, 1, 1e-6, tile=1, stream=0),
+        lambda: Q.qi21_op_qk_gemm(16, 256, 1, 256, 1, 1, 256, 1, 256, 1, 1, None, 1e-6, stream=0),  # no table
+        lambda: Q.qi21_op_rope_pack(0, 1, 1, 1, stream=0),
+        lambda: Q.qi21_op_rope_pack(4, 1, None, 1, stream=0),
         lambda: Q.qi21_op_vt_gemm(256, 100, 256, 1, 256, 1, 1, 100, stream=0),        # ldo < round_up(n, 16)
         lambda: Q.qi21_op_vt_gemm(256, 100, 100, 1, 256, 1, 1, 112, stream=0),        # K % 64
         lambda: Q.qi21_op_qkrope(4, 2, 1, 256, 1, 1, 1, 1, 1e-6, stream=0),

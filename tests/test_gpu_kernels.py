@@ -304,6 +304,21 @@ def test_rowop_modes(mode, rows, h):
         assert torch.all(xn == 0)
 
 
+@pytest.mark.parametrize("n", [1, 5, 4118])
+def test_rope_pack_layout(n):
+    """The packed RoPE table holds, per row and pair couple m, cos 2m, cos
+    2m+1, sin 2m, sin 2m+1: bit-exact copies of the separate tables."""
+    q = Q()
+    c = inputs.host_array(17, 1, (n, 64), 1.0)
+    s = inputs.host_array(17, 2, (n, 64), 1.0)
+    out = torch.full((n, 128), float("nan"), device="cuda")
+    q.qi21_op_rope_pack(n, dev(c), dev(s), out)
+    sync()
+    o = out.cpu().numpy().reshape(n, 32, 4)
+    assert np.array_equal(o[:, :, 0], c[:, 0::2]) and np.array_equal(o[:, :, 1], c[:, 1::2])
+    assert np.array_equal(o[:, :, 2], s[:, 0::2]) and np.array_equal(o[:, :, 3], s[:, 1::2])
+
+
 @pytest.mark.parametrize("rows,h,mode", [(2048, 4096, 3), (2049, 4096, 3), (2049, 4096, 2), (5, 8192, 3),
                                          (5, 2052, 7), (3000, 2048, 1), (64, 2044, 3)])
 def test_rowop_row_forms(rows, h, mode):
@@ -495,8 +510,10 @@ def test_qk_gemm_fused_norm_rope(M, tile):
     ldq, ldk = H + 64, H
     qo = torch.zeros(M, ldq, device="cuda", dtype=torch.float16)
     ko = torch.zeros(M, ldk, device="cuda", dtype=torch.float16)
+    rope = torch.empty(M, 128, device="cuda")
+    q.qi21_op_rope_pack(M, dev(c), dev(s), rope)
     q.qi21_op_qk_gemm(M, H, dev(A, torch.float16), H, dev(W, torch.float16), qo, ldq, ko, ldk, dev(wq), dev(wk),
-                      dev(c), dev(s), eps, tile)
+                      rope, eps, tile)
     sync()
     want_q = O.qk_norm_rope(O.lin(A, W[:H]), wq, c, s, heads, hd, eps)
     want_k = O.qk_norm_rope(O.lin(A, W[H:]), wk, c, s, heads, hd, eps)
