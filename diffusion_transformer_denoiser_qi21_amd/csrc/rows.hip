@@ -1,7 +1,8 @@
 // Bandwidth-bound row kernels of the denoiser step: the gated residual +
 // modulated LayerNorm (rowop), the per-head q/k RMSNorm + RoPE (qkrope),
 // the img_in embedding, the final LayerNorm + proj_out, and small helpers
-// (gate tanh, weight-plane conversion, output commit, fill).
+// (gate tanh, weight-plane conversion, RoPE table packing, output commit,
+// fill).
 //
 // Access pattern: every row is read with 16-byte (float4 / 8 x f16) or
 // 4-byte-per-lane fully coalesced loads; reductions are wave64 shuffles

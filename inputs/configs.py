@@ -109,4 +109,7 @@ CONFIGS = {
     "cfg512": Workload("cfg512", FULL_MODEL, 7, (32, 32), ((("text", 18),), (("text", 18),)),
                        prefix_seeds=(7, 8),
                        note="CFG pair at 512^2: two Text(18) prefixes (seeds 7, 8), shared tokens and modulation"),
+    "ragged": Workload("ragged", FULL_MODEL, 4087, (61, 67), ((("text", 37),),),
+                       note="parity case: 4087 target rows (ragged last tile of every GEMM and attention key "
+                            "tile) behind a Text(37) prefix"),
 }

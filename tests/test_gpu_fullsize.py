@@ -214,8 +214,11 @@ def _step_v(m, w, key, stride):
     return out.cpu().numpy()[::stride]
 
 
-@pytest.mark.parametrize("name", ["512", "1024", "cond"])
+@pytest.mark.parametrize("name", ["512", "1024", "cond", "ragged"])
 def test_step_full_size_against_oracle(full_model_pair, name):
+    # ragged: 4087 target rows behind 37 prefix rows, so the last row tile of
+    # every GEMM, the last V^T columns and the last key tile of attention are
+    # partial on the large-pass path (fused q|k epilogue, block-per-row pass)
     want, stride = _golden(name)
     err = rel(_step_v(full_model_pair, CONFIGS[name], 50, stride), want)
     print(f"{name} (ffn_pair): v rel L2 vs oracle {err:.3e}")
