@@ -222,7 +222,7 @@ def main(argv=None):
         return copy_calibration()
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU; --gpus above 1 is not supported "
-                                   "(the row-sharded multi-GPU step is described in DESIGN.md, not built)"}))
+                                   "(a step sharded by target rows over several GPUs is not built)"}))
         return 2
 
     import torch
