@@ -176,7 +176,9 @@ __global__ __launch_bounds__(256) void rownorm2_kernel(int rows, int h, const fl
   }
 }
 
-template <int MODE, int NJ>
+// NP > 0: the number of planes of y, known at compile time (1 to 4); 0:
+// nparts at run time.
+template <int MODE, int NJ, int NP>
 __global__ __launch_bounds__(256) void rowop_wide_kernel(int rows, int h, float* __restrict__ x,
                                                          const float* __restrict__ y, int nparts, size_t pstride,
                                                          f16* __restrict__ xn, const float* __restrict__ mods,
@@ -200,12 +202,32 @@ __global__ __launch_bounds__(256) void rowop_wide_kernel(int rows, int h, float*
       const int c = t + 256 * j;
       if (c < nc) yv[j] = yr[c];
     }
-    for (int p = 1; p < nparts; ++p) {
-      const float4v* yp = reinterpret_cast<const float4v*>(y + p * pstride + (size_t)row * h);
+    if (NP > 0) {
+      // a known plane count: every plane's loads go out before the first
+      // add (the sum stays in plane order)
+      float4v yq[NP > 1 ? NP - 1 : 1][NJ];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int c = t + 256 * j;
-        if (c < nc) yv[j] += yp[c];
+      for (int p = 1; p < NP; ++p) {
+        const float4v* yp = reinterpret_cast<const float4v*>(y + p * pstride + (size_t)row * h);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int c = t + 256 * j;
+          if (c < nc) yq[p - 1][j] = yp[c];
+        }
+      }
+#pragma unroll
+      for (int p = 1; p < NP; ++p)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          if (t + 256 * j < nc) yv[j] += yq[p - 1][j];
+    } else {
+      for (int p = 1; p < nparts; ++p) {
+        const float4v* yp = reinterpret_cast<const float4v*>(y + p * pstride + (size_t)row * h);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int c = t + 256 * j;
+          if (c < nc) yv[j] += yp[c];
+        }
       }
     }
 #pragma unroll
@@ -250,19 +272,33 @@ __global__ __launch_bounds__(256) void rowop_wide_kernel(int rows, int h, float*
 }
 
 namespace {
-template <int NJ>
-hipError_t launch_rowop_wide(int rows, int h, int mode, float* x, const float* y, int np, size_t ps, f16* xn,
-                             const float* mods, int g_off, int s_off, float eps, float oscale, hipStream_t s) {
+template <int NJ, int NP>
+hipError_t launch_rowop_wide_np(int rows, int h, int mode, float* x, const float* y, int np, size_t ps, f16* xn,
+                                const float* mods, int g_off, int s_off, float eps, float oscale, hipStream_t s) {
   const dim3 grid(rows), block(256);
   switch (mode) {
-    case 1: hipLaunchKernelGGL((rowop_wide_kernel<1, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
-    case 2: hipLaunchKernelGGL((rowop_wide_kernel<2, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
-    case 3: hipLaunchKernelGGL((rowop_wide_kernel<3, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
-    case 6: hipLaunchKernelGGL((rowop_wide_kernel<6, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
-    case 7: hipLaunchKernelGGL((rowop_wide_kernel<7, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
+    case 1: hipLaunchKernelGGL((rowop_wide_kernel<1, NJ, NP>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
+    case 2: hipLaunchKernelGGL((rowop_wide_kernel<2, NJ, NP>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
+    case 3: hipLaunchKernelGGL((rowop_wide_kernel<3, NJ, NP>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
+    case 6: hipLaunchKernelGGL((rowop_wide_kernel<6, NJ, NP>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
+    case 7: hipLaunchKernelGGL((rowop_wide_kernel<7, NJ, NP>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int NJ>
+hipError_t launch_rowop_wide(int rows, int h, int mode, float* x, const float* y, int np, size_t ps, f16* xn,
+                             const float* mods, int g_off, int s_off, float eps, float oscale, hipStream_t s) {
+  // three or four planes with every plane's loads issued up front (1024
+  // rows x 4096: 22.1 against 23.6 us with four planes, 16.5 against 21.1
+  // with three); one or two planes with the plane loop, which measured
+  // faster there (2048 rows, two planes: 31.0 against 36.7 us)
+  if ((mode & 1) && np == 3)
+    return launch_rowop_wide_np<NJ, 3>(rows, h, mode, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale, s);
+  if ((mode & 1) && np == 4)
+    return launch_rowop_wide_np<NJ, 4>(rows, h, mode, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale, s);
+  return launch_rowop_wide_np<NJ, 0>(rows, h, mode, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale, s);
 }
 }  // namespace
 

@@ -462,7 +462,7 @@ def test_gemm_split_partials(M, ksplit, K, tile):
         assert rel(part.cpu().numpy().sum(axis=0), want) < F32_TOL * 10
 
 
-@pytest.mark.parametrize("nparts", [1, 2, 4])
+@pytest.mark.parametrize("nparts", [1, 2, 3, 4])
 @pytest.mark.parametrize("mode", [1, 3, 7])
 def test_rowop_adds_partial_planes(mode, nparts):
     """x += gate * (sum of the planes, in order), then the modulated LayerNorm
