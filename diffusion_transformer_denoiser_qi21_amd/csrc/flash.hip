@@ -17,7 +17,8 @@
 // their maxima once per key tile and their sums once at the end.
 //
 // Block: NW waves x 32 queries (NW = 8, or 4 for grids too small to fill
-// the chip), key tile 64.  The K tile [64][128] and the V^T tile [128][64]
+// the chip; grids of at most one round of 128-query blocks use the
+// key-split form below), key tile 64.  The K tile [64][128] and the V^T tile [128][64]
 // of each step are fetched by buffer loads that write straight into LDS,
 // through a ring of NST stages (4 with 8 waves: 128 KB, one block per CU;
 // 2 with 4 waves: 64 KB, two blocks per CU), so a tile's loads have NST - 1
@@ -310,6 +311,246 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a) {
   }
 }
 
+// The key-split form for grids too small to give each SIMD two waves
+// (1024 queries x 32 heads: 1024 waves of 32 queries).  A block of 8 waves
+// takes 128 queries: waves w and w + 4 own the same 32 queries, wave group
+// g = w / 4 the key tiles t = 2s + g of step s.  Each step the block's 8
+// waves fetch the step's two tiles (one per group) into a 4-stage ring, one
+// step ahead.  At the end group 1 hands its unnormalised output, running
+// maximum and partial sums to group 0 through LDS, and group 0 merges them
+// (both rescaled to the larger maximum) and stores the result.
+template <bool VIS>
+__global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a) {
+  constexpr int NW = 8, NST = 4;
+  constexpr int BQ = 128;       // queries per block
+  constexpr int NLD = 16 / NW;  // 16-byte loads per lane per K (and per V^T) tile
+  extern __shared__ __attribute__((aligned(16))) char smb[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, qw = wave & 3;
+  const int hs = lane >> 5, l32 = lane & 31;
+  const int nqb = (a.nq + BQ - 1) / BQ;
+  int head, qb;
+  {
+    const int b = blockIdx.x;
+    if ((a.heads & 7) == 0) {
+      const int li = b >> 3;
+      head = (b & 7) + 8 * (li / nqb);
+      qb = li % nqb;
+    } else {
+      head = b / nqb;
+      qb = b % nqb;
+    }
+  }
+  const int q0 = qb * BQ;
+  const int myq = q0 + qw * 32 + l32;
+  const bool live = myq < a.nq;
+  const int qrow = min(myq, a.nq - 1);
+  const int ntot = a.n1 + a.n2;
+
+  half8 qf[8];
+  {
+    const f16* qp = a.q + (size_t)qrow * a.ldq + head * 128 + 8 * hs;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const half8*>(qp + 16 * c);
+  }
+  int lim = ntot, kmax = ntot;
+  if (VIS) {
+    lim = min(ntot, (int)a.vis[qrow]);
+    kmax = min(ntot, (int)a.vis[min(q0 + BQ, a.nq) - 1]);
+  }
+  const int t1 = (min(a.n1, kmax) + BKV - 1) / BKV;
+  const int t2 = kmax > a.n1 ? (min(a.n2, kmax - a.n1) + BKV - 1) / BKV : 0;
+  const int T = t1 + t2;
+  const int S = (T + 1) / 2;  // steps of two tiles
+
+  __amdgpu_buffer_rsrc_t kr[2], vr[2];
+  int lk2[2], lv2[2];
+  {
+    const f16* kb[2] = {a.k1, a.k2};
+    const f16* vb[2] = {a.vt1, a.vt2};
+    const int ns[2] = {a.n1, a.n2};
+    const int ldk[2] = {a.ldk1, a.ldk2}, ldv[2] = {a.ldvt1, a.ldvt2};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int n = max(ns[s], 1);
+      lk2[s] = ldk[s] * 2;
+      lv2[s] = ldv[s] * 2;
+      kr[s] = __builtin_amdgcn_make_buffer_rsrc((void*)(kb[s] + head * 128), 0, (n - 1) * ldk[s] * 2 + 256,
+                                                0x00020000);
+      vr[s] = __builtin_amdgcn_make_buffer_rsrc((void*)(vb[s] + (size_t)head * 128 * ldv[s]), 0, 128 * ldv[s] * 2,
+                                                0x00020000);
+    }
+  }
+  // tile t into stage t % NST by all 8 waves, as in flash_kernel with NW = 8
+  const int lkey0 = 4 * wave + (lane >> 4);
+  const int lck = ((lane & 15) ^ (lkey0 & 15)) * 16;
+  const int ldim0 = 8 * wave + (lane >> 3);
+  const int lcv = ((lane & 7) ^ vswz(ldim0)) * 16;
+  auto issue = [&](int t) {
+    const bool s1 = t < t1;
+    const int j0 = (s1 ? t : t - t1) * BKV;
+    const int kl2 = s1 ? lk2[0] : lk2[1], vl2 = s1 ? lv2[0] : lv2[1];
+    const __amdgpu_buffer_rsrc_t krs = s1 ? kr[0] : kr[1];
+    const __amdgpu_buffer_rsrc_t vrs = s1 ? vr[0] : vr[1];
+    const int ko = (j0 + lkey0) * kl2 + lck;
+    const int vo = ldim0 * vl2 + lcv;
+    const int sv = __builtin_amdgcn_readfirstlane(j0 * 2);
+    char* base = smb + (t % NST) * STAGE_B + wave * 64 * 16;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, base + i * NW * 64 * 16, 16, ko + i * 4 * NW * kl2, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, base + TILE_B + i * NW * 64 * 16, 16, vo + i * 8 * NW * vl2, sv,
+                                               0, 0);
+    }
+  };
+  int kofs[8], vofs[4];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) kofs[c] = l32 * 256 + (((2 * c + hs) ^ (l32 & 15)) * 16);
+#pragma unroll
+  for (int su = 0; su < 4; ++su) vofs[su] = l32 * 128 + (((2 * su + hs) ^ vswz(l32)) * 16);
+
+  floatx16 o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[d][e] = 0.0f;
+  float mused = -INFINITY, lsum = 0.0f;
+  const float c2 = LOG2E * 0.08838834764831845f;  // log2(e) / sqrt(128)
+  const float thr_raw = THR / c2;
+  const half2v ones = half2v{(f16)1.0f, (f16)1.0f};
+
+  // step 0's tiles
+  if (0 < T) issue(0);
+  if (1 < T) issue(1);
+  for (int s = 0; s < S; ++s) {
+    // this step's two tiles have landed; after the barrier every wave is
+    // done with step s - 1, whose stages receive step s + 1
+    __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+    __builtin_amdgcn_s_barrier();
+    if (2 * s + 2 < T) issue(2 * s + 2);
+    if (2 * s + 3 < T) issue(2 * s + 3);
+    const int t = 2 * s + grp;
+    if (t < T) {  // (wave-uniform; a group without a tile in the last step only keeps the barriers)
+      const char* sk = smb + (t % NST) * STAGE_B;
+      const char* sv = sk + TILE_B;
+      half8 kv[16];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) kv[2 * c + st] = *reinterpret_cast<const half8*>(sk + kofs[c] + st * 8192);
+      floatx16 sc[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[st][e] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+          sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv[2 * c + st], qf[c], sc[st], 0, 0, 0);
+      half8 vv[16];
+#pragma unroll
+      for (int su = 0; su < 4; ++su)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) vv[4 * su + d] = *reinterpret_cast<const half8*>(sv + vofs[su] + d * 4096);
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool s1 = t < t1;
+      const int j0 = (s1 ? t : t - t1) * BKV;
+      const int cnt = min(BKV, (s1 ? a.n1 : a.n2) - j0);
+      const int gbase = (s1 ? 0 : a.n1) + j0;
+      if (__builtin_amdgcn_readfirstlane((int)(VIS || cnt < BKV))) {
+        const int bound = min(cnt, lim - gbase) - 4 * hs;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (st * 32 + 8 * (e >> 2) + (e & 3) >= bound) sc[st][e] = -INFINITY;
+      }
+      float mx = fmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+      for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sc[0][e], sc[0][e + 1]));
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sc[1][e], sc[1][e + 1]));
+      mx = pair_max(mx);
+      if (__any(mx > mused + thr_raw)) {
+        // (a lane whose keys so far were all masked -- group 1 starts at tile
+        // 1, past what an early prefix query sees -- still has mused = -inf
+        // and nothing accumulated: alpha 0, never (-inf) - (-inf))
+        const float mnew = fmaxf(mused, mx);
+        const float alpha = mused == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mused - mnew) * c2);
+        mused = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+      }
+      const float mc = mused == -INFINITY ? 0.0f : mused * c2;
+      half8 pf[2][2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          u32x4 pk;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[st][8 * u + 2 * j], c2, -mc));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[st][8 * u + 2 * j + 1], c2, -mc));
+            const half2v ph = half2v{(f16)p0, (f16)p1};
+            lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
+            pk[j] = __builtin_bit_cast(unsigned int, ph);
+          }
+          pf[st][u] = __builtin_bit_cast(half8, pk);
+        }
+#pragma unroll
+      for (int su = 0; su < 4; ++su)
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vv[4 * su + d], pf[su >> 1][su & 1], o[d], 0, 0, 0);
+    }
+  }
+  // merge: group 1's (o, mused, lsum) per lane through LDS (the ring is free
+  // once every wave is past this barrier)
+  __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(smb) + (size_t)(qw * 64 + lane) * 66;  // [4 waves][64 lanes][64 + 2]
+  if (grp == 1) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xo[d * 16 + e] = o[d][e];
+    xo[64] = mused;
+    xo[65] = lsum;
+  }
+  __syncthreads();
+  if (grp == 0) {
+    const float m1 = xo[64], l1 = xo[65];
+    const float m = fmaxf(mused, m1);
+    const float a0 = mused == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mused - m) * c2);
+    const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m1 - m) * c2);
+    const float ltot = pair_sum(lsum * a0 + l1 * a1);
+    const float inv = ltot > 0.0f ? a.oscale / ltot : 0.0f;
+    if (live) {
+      f16* op = a.out + (size_t)myq * a.ldo + head * 128 + 4 * hs;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          half4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = (f16)((o[d][4 * g + e] * a0 + xo[d * 16 + 4 * g + e] * a1) * inv);
+          *reinterpret_cast<half4*>(op + 32 * d + 8 * g) = v;
+        }
+    }
+  }
+}
+
 namespace {
 template <int NW, int NST>
 hipError_t launch_shape(const FlashArgs& a, hipStream_t s) {
@@ -330,6 +571,24 @@ hipError_t launch_shape(const FlashArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((flash_kernel<false, NW, NST>), grid, dim3(NW * 64), lds, s, a);
   return hipGetLastError();
 }
+hipError_t launch_split(const FlashArgs& a, hipStream_t s) {
+  constexpr size_t lds = (size_t)4 * STAGE_B;
+  static bool attr = false;
+  if (!attr) {
+    for (const void* f : {reinterpret_cast<const void*>(&flash_split_kernel<true>),
+                          reinterpret_cast<const void*>(&flash_split_kernel<false>)}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    attr = true;
+  }
+  dim3 grid(((a.nq + 127) / 128) * a.heads);
+  if (a.vis)
+    hipLaunchKernelGGL((flash_split_kernel<true>), grid, dim3(512), lds, s, a);
+  else
+    hipLaunchKernelGGL((flash_split_kernel<false>), grid, dim3(512), lds, s, a);
+  return hipGetLastError();
+}
 }  // namespace
 
 hipError_t launch_flash(const FlashArgs& a, hipStream_t s) {
@@ -343,6 +602,10 @@ hipError_t launch_flash(const FlashArgs& a, hipStream_t s) {
   // chip; smaller grids use 4-wave blocks, two per CU
   const long blocks8 = (long)((a.nq + 255) / 256) * a.heads;
   if (blocks8 >= 2L * cus) return launch_shape<8, 4>(a, s);
+  // one round or less of 128-query blocks: split each block's keys over two
+  // wave groups (two waves per SIMD instead of one)
+  const long blocks_split = (long)((a.nq + 127) / 128) * a.heads;
+  if (blocks_split <= cus) return launch_split(a, s);
   return launch_shape<4, 2>(a, s);
 }
 
