@@ -72,7 +72,12 @@ __device__ __forceinline__ float pair_sum(float x) {
 }  // namespace
 
 template <bool VIS, int NW, int NST>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a) {
+__global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a0, FlashArgs a1, int nb0) {
+  // blocks [0, nb0) work on segment a0, the rest on a1 (one launch for the
+  // rows of two programs, each attending to its own keys)
+  const bool seg1 = (int)blockIdx.x >= nb0;
+  const FlashArgs& a = seg1 ? a1 : a0;
+  const int bid = (int)blockIdx.x - (seg1 ? nb0 : 0);
   constexpr int BQ = NW * 32;          // queries per block
   constexpr int NLD = 16 / NW;         // 16-byte loads per lane per K (and per V^T) tile
   extern __shared__ __attribute__((aligned(16))) char smb[];  // NST stages of [K tile | V^T tile]
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a) {
   const int nqb = (a.nq + BQ - 1) / BQ;
   int head, qb;
   {
-    const int b = blockIdx.x;
+    const int b = bid;
     if ((a.heads & 7) == 0) {
       const int li = b >> 3;
       head = (b & 7) + 8 * (li / nqb);
@@ -320,7 +325,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a) {
 // maximum and partial sums to group 0 through LDS, and group 0 merges them
 // (both rescaled to the larger maximum) and stores the result.
 template <bool VIS>
-__global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a) {
+__global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a0, FlashArgs a1, int nb0) {
+  // blocks [0, nb0) work on segment a0, the rest on a1 (one launch for the
+  // rows of two programs, each attending to its own keys)
+  const bool seg1 = (int)blockIdx.x >= nb0;
+  const FlashArgs& a = seg1 ? a1 : a0;
+  const int bid = (int)blockIdx.x - (seg1 ? nb0 : 0);
   constexpr int NW = 8, NST = 4;
   constexpr int BQ = 128;       // queries per block
   constexpr int NLD = 16 / NW;  // 16-byte loads per lane per K (and per V^T) tile
@@ -333,7 +343,7 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a) {
   const int nqb = (a.nq + BQ - 1) / BQ;
   int head, qb;
   {
-    const int b = blockIdx.x;
+    const int b = bid;
     if ((a.heads & 7) == 0) {
       const int li = b >> 3;
       head = (b & 7) + 8 * (li / nqb);
@@ -552,8 +562,11 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a) {
 }
 
 namespace {
+// Blocks of `bq` queries over the heads of one segment.
+long seg_blocks(const FlashArgs& a, int bq) { return (long)((a.nq + bq - 1) / bq) * a.heads; }
+
 template <int NW, int NST>
-hipError_t launch_shape(const FlashArgs& a, hipStream_t s) {
+hipError_t launch_shape(const FlashArgs& a0, const FlashArgs& a1, int nseg, hipStream_t s) {
   constexpr size_t lds = (size_t)NST * STAGE_B;
   static bool attr = false;
   if (!attr) {
@@ -564,14 +577,15 @@ hipError_t launch_shape(const FlashArgs& a, hipStream_t s) {
     }
     attr = true;
   }
-  dim3 grid(((a.nq + NW * 32 - 1) / (NW * 32)) * a.heads);
-  if (a.vis)
-    hipLaunchKernelGGL((flash_kernel<true, NW, NST>), grid, dim3(NW * 64), lds, s, a);
+  const int nb0 = (int)seg_blocks(a0, NW * 32);
+  dim3 grid(nb0 + (nseg > 1 ? (int)seg_blocks(a1, NW * 32) : 0));
+  if (a0.vis)
+    hipLaunchKernelGGL((flash_kernel<true, NW, NST>), grid, dim3(NW * 64), lds, s, a0, a1, nb0);
   else
-    hipLaunchKernelGGL((flash_kernel<false, NW, NST>), grid, dim3(NW * 64), lds, s, a);
+    hipLaunchKernelGGL((flash_kernel<false, NW, NST>), grid, dim3(NW * 64), lds, s, a0, a1, nb0);
   return hipGetLastError();
 }
-hipError_t launch_split(const FlashArgs& a, hipStream_t s) {
+hipError_t launch_split(const FlashArgs& a0, const FlashArgs& a1, int nseg, hipStream_t s) {
   constexpr size_t lds = (size_t)4 * STAGE_B;
   static bool attr = false;
   if (!attr) {
@@ -582,31 +596,54 @@ hipError_t launch_split(const FlashArgs& a, hipStream_t s) {
     }
     attr = true;
   }
-  dim3 grid(((a.nq + 127) / 128) * a.heads);
-  if (a.vis)
-    hipLaunchKernelGGL((flash_split_kernel<true>), grid, dim3(512), lds, s, a);
+  const int nb0 = (int)seg_blocks(a0, 128);
+  dim3 grid(nb0 + (nseg > 1 ? (int)seg_blocks(a1, 128) : 0));
+  if (a0.vis)
+    hipLaunchKernelGGL((flash_split_kernel<true>), grid, dim3(512), lds, s, a0, a1, nb0);
   else
-    hipLaunchKernelGGL((flash_split_kernel<false>), grid, dim3(512), lds, s, a);
+    hipLaunchKernelGGL((flash_split_kernel<false>), grid, dim3(512), lds, s, a0, a1, nb0);
   return hipGetLastError();
 }
-}  // namespace
 
-hipError_t launch_flash(const FlashArgs& a, hipStream_t s) {
+// One launch over one or two segments (both with or both without vis).
+hipError_t launch_segs(const FlashArgs& a0, const FlashArgs& a1, int nseg, hipStream_t s) {
   static int cus = 0;
   if (!cus) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
   }
+  const long blocks8 = seg_blocks(a0, 256) + (nseg > 1 ? seg_blocks(a1, 256) : 0);
+  const long blocks_split = seg_blocks(a0, 128) + (nseg > 1 ? seg_blocks(a1, 128) : 0);
   // 8-wave blocks (one per CU) once they make at least two rounds over the
-  // chip; smaller grids use 4-wave blocks, two per CU
-  const long blocks8 = (long)((a.nq + 255) / 256) * a.heads;
-  if (blocks8 >= 2L * cus) return launch_shape<8, 4>(a, s);
+  // chip
+  if (blocks8 >= 2L * cus) return launch_shape<8, 4>(a0, a1, nseg, s);
   // one round or less of 128-query blocks: split each block's keys over two
   // wave groups (two waves per SIMD instead of one)
-  const long blocks_split = (long)((a.nq + 127) / 128) * a.heads;
-  if (blocks_split <= cus) return launch_split(a, s);
-  return launch_shape<4, 2>(a, s);
+  if (blocks_split <= cus) return launch_split(a0, a1, nseg, s);
+  // otherwise 4-wave blocks, two per CU
+  return launch_shape<4, 2>(a0, a1, nseg, s);
+}
+}  // namespace
+
+hipError_t launch_flash(const FlashArgs& a, hipStream_t s) { return launch_segs(a, a, 1, s); }
+
+hipError_t launch_flash(const FlashArgs* segs, int nseg, hipStream_t s) {
+  // pairs of segments share a launch (the grid is sized from their
+  // combined blocks); a pair that mixes masked and unmasked segments runs
+  // as two launches
+  for (int i = 0; i < nseg; i += 2) {
+    hipError_t e;
+    if (i + 1 < nseg && !segs[i].vis == !segs[i + 1].vis)
+      e = launch_segs(segs[i], segs[i + 1], 2, s);
+    else if (i + 1 < nseg) {
+      e = launch_segs(segs[i], segs[i], 1, s);
+      if (e == hipSuccess) e = launch_segs(segs[i + 1], segs[i + 1], 1, s);
+    } else
+      e = launch_segs(segs[i], segs[i], 1, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace qi21

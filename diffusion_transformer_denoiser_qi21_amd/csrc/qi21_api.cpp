@@ -411,6 +411,7 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
     if (pre && last) break;  // only this layer's K/V leave a prefill
     {
       Scope sc(m, C_FLASH, s);
+      std::vector<qi21::FlashArgs> fa;
       for (const Seg& sg : segs) {
         qi21::FlashArgs f{};
         f.q = a.panel + (size_t)sg.row0 * 2 * H;
@@ -441,8 +442,9 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
         f.out = a.att + (size_t)sg.row0 * H;
         f.ldo = H;
         f.oscale = p2(gd.qkv - gd.ao);
-        HIP_OK(qi21::launch_flash(f, s));
+        fa.push_back(f);
       }
+      HIP_OK(qi21::launch_flash(fa.data(), (int)fa.size(), s));
     }
     // with ffn_pair the FFN input and the hidden are f16 (hi, lo) pairs in
     // rows of 2H / 2I and both GEMMs run over K doubled, each W row twice

@@ -94,6 +94,10 @@ struct FlashArgs {
   float oscale;
 };
 hipError_t launch_flash(const FlashArgs& a, hipStream_t s);
+// The segments' blocks in launches of two segments each (the rows of two
+// programs, each attending to its own keys; combined grids fill the CUs
+// where one program's rows would not).
+hipError_t launch_flash(const FlashArgs* segs, int nseg, hipStream_t s);
 
 // rowop over `rows` rows of width h (h % 4 == 0, h <= 8192):
 //   mode & 1: x += gate (.) y            (gate = mods + g_off, already tanh-ed;

@@ -107,6 +107,51 @@ def test_cfg_pair_unequal_prefixes_batched(tiny_gpu, tiny_cpu):
     assert rel(single.cpu().numpy(), outs[1].cpu().numpy()) < 1e-6
 
 
+@pytest.fixture(scope="module")
+def wide_gpu():
+    """One block at the full width (32 heads of 128), so the attention grids
+    reach the sizes at which the launch forms change."""
+    from inputs.configs import FULL_MODEL
+    m = bench.build_model(dataclasses.replace(FULL_MODEL, layers=1))
+    yield m
+    Q().qi21_model_destroy(m)
+
+
+@pytest.fixture(scope="module")
+def wide_cpu():
+    from inputs.configs import FULL_MODEL
+    return SynthModel(dataclasses.replace(FULL_MODEL, layers=1))
+
+
+# Target rows per program -> the attention form of the two programs' shared
+# launch on 256 CUs: 512 -> key-split blocks, 1024 -> 4-wave blocks, 2048 ->
+# 8-wave blocks (while each program alone would take the key-split, key-split
+# and 4-wave forms).
+@pytest.mark.parametrize("target", [(16, 32), (32, 32), (32, 64)])
+def test_cfg_pair_shared_attention_launch(wide_gpu, wide_cpu, target):
+    """The two programs' rows in one attention launch, against the oracle's
+    step of each program (unequal prefixes, so the second segment's key
+    count differs from the first's)."""
+    from inputs.configs import FULL_MODEL
+    w = Workload("cfgw", dataclasses.replace(FULL_MODEL, layers=1), 51, target,
+                 ((("text", 18),), (("text", 7), ("image", 2, 2))), prefix_seeds=(51, 52))
+    q = Q()
+    ds = [bench.workload_tensors(w, p) for p in range(2)]
+    for p in range(2):
+        bench.prefill(wide_gpu, 20 + p, ds[p])
+    outs = [torch.zeros(d["n"], 64, device="cuda") for d in ds]
+    q.qi21_step_batch(wide_gpu, [20, 21], [d["tok"] for d in ds], ds[0]["mods"], ds[0]["fs"], outs)
+    for p in range(2):
+        got = outs[p].cpu().numpy()
+        assert np.isfinite(got).all()
+        err = rel(got, oracle_v(wide_cpu, w, p))
+        single = torch.zeros_like(outs[p])
+        q.qi21_step(wide_gpu, 20 + p, ds[p]["tok"], ds[p]["mods"], ds[p]["fs"], single)
+        print(f"{target} program {p}: v rel L2 {err:.3e} (alone vs batched "
+              f"{rel(single.cpu().numpy(), got):.3e})")
+        assert err < V_TOL
+
+
 def test_step_is_deterministic(tiny_gpu):
     w = CONFIGS["tiny"]
     d = bench.workload_tensors(w)
