@@ -105,7 +105,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a0, Fl
   const int myq = q0 + wave * 32 + l32;
   const bool live = myq < a.nq;
   const int qrow = min(myq, a.nq - 1);
-  const int ntot = a.n1 + a.n2;
+  // n1 / n2 as opaque scalars: the loop's mask reads them from registers.
+  // A reload of the kernel argument there would leave a scalar load in
+  // flight at the loop's first LDS reads, and the LDS wait before the
+  // first MFMA would then have to drain every read, not just the first.
+  int n1 = a.n1, n2 = a.n2;
+  asm volatile("" : "+s"(n1), "+s"(n2));
+  const int ntot = n1 + n2;
 
   // Q fragments (B operand of S^T = K Q^T): dims 16c + 8*hs .. +8 of this lane's query
   half8 qf[8];
@@ -119,8 +125,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a0, Fl
     lim = min(ntot, (int)a.vis[qrow]);
     kmax = min(ntot, (int)a.vis[min(q0 + BQ, a.nq) - 1]);
   }
-  const int t1 = (min(a.n1, kmax) + BKV - 1) / BKV;
-  const int t2 = kmax > a.n1 ? (min(a.n2, kmax - a.n1) + BKV - 1) / BKV : 0;
+  const int t1 = (min(n1, kmax) + BKV - 1) / BKV;
+  const int t2 = kmax > n1 ? (min(n2, kmax - n1) + BKV - 1) / BKV : 0;
   const int T = t1 + t2;
 
   // buffer resources of the two sources (this head's columns); K rows past
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a0, Fl
   {
     const f16* kb[2] = {a.k1, a.k2};
     const f16* vb[2] = {a.vt1, a.vt2};
-    const int ns[2] = {a.n1, a.n2};
+    const int ns[2] = {n1, n2};
     const int ldk[2] = {a.ldk1, a.ldk2}, ldv[2] = {a.ldvt1, a.ldvt2};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -246,8 +252,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a0, Fl
     // against one per-lane bound.
     const bool s1 = t < t1;
     const int j0 = (s1 ? t : t - t1) * BKV;
-    const int cnt = min(BKV, (s1 ? a.n1 : a.n2) - j0);
-    const int gbase = (s1 ? 0 : a.n1) + j0;
+    const int cnt = min(BKV, (s1 ? n1 : n2) - j0);
+    const int gbase = (s1 ? 0 : n1) + j0;
     if (__builtin_amdgcn_readfirstlane((int)(VIS || cnt < BKV))) {
       const int bound = min(cnt, lim - gbase) - 4 * hs;
 #pragma unroll
@@ -357,7 +363,13 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a0, Flash
   const int myq = q0 + qw * 32 + l32;
   const bool live = myq < a.nq;
   const int qrow = min(myq, a.nq - 1);
-  const int ntot = a.n1 + a.n2;
+  // n1 / n2 as opaque scalars: the loop's mask reads them from registers.
+  // A reload of the kernel argument there would leave a scalar load in
+  // flight at the loop's first LDS reads, and the LDS wait before the
+  // first MFMA would then have to drain every read, not just the first.
+  int n1 = a.n1, n2 = a.n2;
+  asm volatile("" : "+s"(n1), "+s"(n2));
+  const int ntot = n1 + n2;
 
   half8 qf[8];
   {
@@ -370,8 +382,8 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a0, Flash
     lim = min(ntot, (int)a.vis[qrow]);
     kmax = min(ntot, (int)a.vis[min(q0 + BQ, a.nq) - 1]);
   }
-  const int t1 = (min(a.n1, kmax) + BKV - 1) / BKV;
-  const int t2 = kmax > a.n1 ? (min(a.n2, kmax - a.n1) + BKV - 1) / BKV : 0;
+  const int t1 = (min(n1, kmax) + BKV - 1) / BKV;
+  const int t2 = kmax > n1 ? (min(n2, kmax - n1) + BKV - 1) / BKV : 0;
   const int T = t1 + t2;
   const int S = (T + 1) / 2;  // steps of two tiles
 
@@ -380,7 +392,7 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a0, Flash
   {
     const f16* kb[2] = {a.k1, a.k2};
     const f16* vb[2] = {a.vt1, a.vt2};
-    const int ns[2] = {a.n1, a.n2};
+    const int ns[2] = {n1, n2};
     const int ldk[2] = {a.ldk1, a.ldk2}, ldv[2] = {a.ldvt1, a.ldvt2};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -471,8 +483,8 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a0, Flash
       __builtin_amdgcn_sched_barrier(0);
       const bool s1 = t < t1;
       const int j0 = (s1 ? t : t - t1) * BKV;
-      const int cnt = min(BKV, (s1 ? a.n1 : a.n2) - j0);
-      const int gbase = (s1 ? 0 : a.n1) + j0;
+      const int cnt = min(BKV, (s1 ? n1 : n2) - j0);
+      const int gbase = (s1 ? 0 : n1) + j0;
       if (__builtin_amdgcn_readfirstlane((int)(VIS || cnt < BKV))) {
         const int bound = min(cnt, lim - gbase) - 4 * hs;
 #pragma unroll
