@@ -61,6 +61,25 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 // V^T tile rows: 128 bytes = 8 chunks; chunk c of dim row d at slot c ^ ((d >> 1) & 7).
 __device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 
+// Maximum of a lane's 32 scores (two 16-element sub-tiles): one chain of
+// 3-input maxima per sub-tile, 16 instructions plus one to join them (the
+// compiler's own tree takes 24).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float lane_max(const floatx16 (&s)[2]) {
+  float m[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    m[st] = max3f(s[st][0], s[st][1], s[st][2]);
+#pragma unroll
+    for (int e = 3; e < 15; e += 2) m[st] = max3f(m[st], s[st][e], s[st][e + 1]);
+    m[st] = fmaxf(m[st], s[st][15]);
+  }
+  return fmaxf(m[0], m[1]);
+}
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -262,11 +281,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a0, Fl
         for (int e = 0; e < 16; ++e)
           if (st * 32 + 8 * (e >> 2) + (e & 3) >= bound) s[st][e] = -INFINITY;
     }
-    float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-    for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[0][e], s[0][e + 1]));
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[1][e], s[1][e + 1]));
+    float mx = lane_max(s);
     mx = pair_max(mx);
     if (__any(mx > mused + thr_raw)) {  // wave-uniform: rescale O^T and the sum
       const float mnew = fmaxf(mused, mx);
@@ -493,11 +508,7 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a0, Flash
           for (int e = 0; e < 16; ++e)
             if (st * 32 + 8 * (e >> 2) + (e & 3) >= bound) sc[st][e] = -INFINITY;
       }
-      float mx = fmaxf(sc[0][0], sc[0][1]);
-#pragma unroll
-      for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sc[0][e], sc[0][e + 1]));
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sc[1][e], sc[1][e + 1]));
+      float mx = lane_max(sc);
       mx = pair_max(mx);
       if (__any(mx > mused + thr_raw)) {
         // (a lane whose keys so far were all masked -- group 1 starts at tile
