@@ -1,7 +1,8 @@
 // Flash attention of the denoiser step and prefill (head_dim 128).
 //
 // Computes, per head, softmax(q k^T / sqrt(128)) v with the online
-// softmax, keys streamed from two sources: the per-layer prefix cache and
+// softmax, from q given in log2 units (q log2(e) / sqrt(128), the scale the
+// q producers apply through their norm weights), keys streamed from two sources: the per-layer prefix cache and
 // the pass's own rows.  Query i may be limited to keys [0, vis[i]) (the
 // prefill's block-causal mask, a non-decreasing leading run); a block walks
 // only the key tiles its last live query sees.
@@ -33,11 +34,13 @@
 // puts the 8 keys one lane contributes to a P V k-step in one contiguous
 // 16-byte chunk: one conflict-free 16-byte LDS read per fragment.
 //
-// Softmax: exp2 with log2(e)/sqrt(128) folded into one FMA, the running
-// maximum updated lazily -- the O^T rescale runs only when some query of
-// the wave sees its maximum grow by more than 2^8 (a wave-uniform branch),
-// so P = 2^(s - m) stays below 2^8 and exact in f16; row sums by v_dot2 on
-// the f16 P that also feeds the P V product.
+// Softmax: S^T is already the base-2 exponent, and the S^T accumulators
+// are seeded with minus the running maximum m, so P = exp2 of them with no
+// further arithmetic.  m is updated lazily -- the rescale of O^T and of the
+// sum, and the shift of the tile's scores, run only when some query of the
+// wave sees its maximum grow by more than 2^8 (a wave-uniform branch), so
+// P = 2^(s - m) stays below 2^8 and exact in f16; row sums by v_dot2 on the
+// f16 P that also feeds the P V product.
 #include "qi21_internal.h"
 
 namespace qi21 {
@@ -52,7 +55,6 @@ namespace {
 constexpr int BKV = 64;   // keys per tile
 constexpr int TILE_B = BKV * 128 * 2;   // bytes of a K tile (and of a V^T tile)
 constexpr int STAGE_B = 2 * TILE_B;     // K tile then V^T tile
-constexpr float LOG2E = 1.4426950408889634f;
 constexpr float THR = 8.0f;             // lazy-rescale threshold, log2 units
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -79,6 +81,32 @@ __device__ __forceinline__ float lane_max(const floatx16 (&s)[2]) {
     m[st] = fmaxf(m[st], s[st][15]);
   }
   return fmaxf(m[0], m[1]);
+}
+// The lazy rescale of one lane: mx is the maximum of the tile's S^T - base.
+// The running maximum moves to mnew (the larger of the old one and this
+// tile's); O^T and the sum are scaled by 2^(mused - mnew) (0 while mused =
+// -inf), the tile's scores are shifted to S^T - mnew, and nb / thr follow.
+// A lane that has seen no key yet (mnew = -inf) keeps base 0, thr = -inf and
+// its -inf scores.
+__device__ __forceinline__ void rebase(floatx16 (&s)[2], float mx, float& mused, float& base, float& thr,
+                                       floatx16& nb, float& lsum, floatx16 (&o)[4]) {
+  const float mnew = fmaxf(mused, mx + base);
+  const float alpha = mused == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mused - mnew);
+  const float shift = mnew == -INFINITY ? 0.0f : mnew - base;
+  mused = mnew;
+  base = mnew == -INFINITY ? 0.0f : mnew;
+  thr = mnew == -INFINITY ? -INFINITY : THR;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) nb[e] = -base;
+  lsum *= alpha;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[st][e] -= shift;
 }
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -213,9 +241,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a0, Fl
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.0f;
-  float mused = -INFINITY, lsum = 0.0f;
-  const float c2 = LOG2E * 0.08838834764831845f;  // log2(e) / sqrt(128)
-  const float thr_raw = THR / c2;
+  // Q arrives in log2 units (q log2(e) / sqrt(128)), so S^T is the base-2
+  // exponent itself.  The S^T accumulators are seeded with nb = -base, where
+  // base is the running maximum mused (0 while that is -inf): they leave
+  // the MFMAs as S^T - mused and P = exp2 of them.  thr is the lazy-rescale
+  // threshold on that difference (-inf until a lane has seen a key).
+  float mused = -INFINITY, lsum = 0.0f, base = 0.0f, thr = -INFINITY;
+  floatx16 nb;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) nb[e] = 0.0f;
   const half2v ones = half2v{(f16)1.0f, (f16)1.0f};
 
 #pragma unroll
@@ -246,11 +280,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a0, Fl
       for (int st = 0; st < 2; ++st) kv[2 * c + st] = *reinterpret_cast<const half8*>(sk + kofs[c] + st * 8192);
     floatx16 s[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < 2; ++st) s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv[st], qf[0], nb, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[st][e] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 1; c < 8; ++c)
 #pragma unroll
       for (int st = 0; st < 2; ++st) s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv[2 * c + st], qf[c], s[st], 0, 0, 0);
     // the V^T fragments do not depend on P: their reads are issued now and
@@ -281,19 +313,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a0, Fl
         for (int e = 0; e < 16; ++e)
           if (st * 32 + 8 * (e >> 2) + (e & 3) >= bound) s[st][e] = -INFINITY;
     }
-    float mx = lane_max(s);
-    mx = pair_max(mx);
-    if (__any(mx > mused + thr_raw)) {  // wave-uniform: rescale O^T and the sum
-      const float mnew = fmaxf(mused, mx);
-      const float alpha = __builtin_amdgcn_exp2f((mused - mnew) * c2);
-      mused = mnew;
-      lsum *= alpha;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
+    const float mx = pair_max(lane_max(s));  // of S^T - base
+    if (__any(mx > thr)) {  // wave-uniform: move the reference maximum
+      rebase(s, mx, mused, base, thr, nb, lsum, o);
     }
-    const float mc = mused == -INFINITY ? 0.0f : mused * c2;
     // P in f16, packed pairwise straight into the B operand registers
     half8 pf[2][2];
 #pragma unroll
@@ -303,8 +326,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a0, Fl
         u32x4 pk;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * u + 2 * j], c2, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * u + 2 * j + 1], c2, -mc));
+          const float p0 = __builtin_amdgcn_exp2f(s[st][8 * u + 2 * j]);
+          const float p1 = __builtin_amdgcn_exp2f(s[st][8 * u + 2 * j + 1]);
           const half2v ph = half2v{(f16)p0, (f16)p1};
           lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
           pk[j] = __builtin_bit_cast(unsigned int, ph);
@@ -453,9 +476,11 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a0, Flash
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[d][e] = 0.0f;
-  float mused = -INFINITY, lsum = 0.0f;
-  const float c2 = LOG2E * 0.08838834764831845f;  // log2(e) / sqrt(128)
-  const float thr_raw = THR / c2;
+  // scores in log2 units, seeded with nb = -base as in flash_kernel
+  float mused = -INFINITY, lsum = 0.0f, base = 0.0f, thr = -INFINITY;
+  floatx16 nb;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) nb[e] = 0.0f;
   const half2v ones = half2v{(f16)1.0f, (f16)1.0f};
 
   // step 0's tiles
@@ -479,11 +504,9 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a0, Flash
         for (int st = 0; st < 2; ++st) kv[2 * c + st] = *reinterpret_cast<const half8*>(sk + kofs[c] + st * 8192);
       floatx16 sc[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st) sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv[st], qf[0], nb, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sc[st][e] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
+      for (int c = 1; c < 8; ++c)
 #pragma unroll
         for (int st = 0; st < 2; ++st)
           sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kv[2 * c + st], qf[c], sc[st], 0, 0, 0);
@@ -508,22 +531,11 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a0, Flash
           for (int e = 0; e < 16; ++e)
             if (st * 32 + 8 * (e >> 2) + (e & 3) >= bound) sc[st][e] = -INFINITY;
       }
-      float mx = lane_max(sc);
-      mx = pair_max(mx);
-      if (__any(mx > mused + thr_raw)) {
-        // (a lane whose keys so far were all masked -- group 1 starts at tile
-        // 1, past what an early prefix query sees -- still has mused = -inf
-        // and nothing accumulated: alpha 0, never (-inf) - (-inf))
-        const float mnew = fmaxf(mused, mx);
-        const float alpha = mused == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mused - mnew) * c2);
-        mused = mnew;
-        lsum *= alpha;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
-      }
-      const float mc = mused == -INFINITY ? 0.0f : mused * c2;
+      const float mx = pair_max(lane_max(sc));
+      // (a lane whose keys so far were all masked -- group 1 starts at tile
+      // 1, past what an early prefix query sees -- still has mused = -inf
+      // and nothing accumulated; rebase keeps it so)
+      if (__any(mx > thr)) rebase(sc, mx, mused, base, thr, nb, lsum, o);
       half8 pf[2][2];
 #pragma unroll
       for (int st = 0; st < 2; ++st)
@@ -532,8 +544,8 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a0, Flash
           u32x4 pk;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[st][8 * u + 2 * j], c2, -mc));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[st][8 * u + 2 * j + 1], c2, -mc));
+            const float p0 = __builtin_amdgcn_exp2f(sc[st][8 * u + 2 * j]);
+            const float p1 = __builtin_amdgcn_exp2f(sc[st][8 * u + 2 * j + 1]);
             const half2v ph = half2v{(f16)p0, (f16)p1};
             lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
             pk[j] = __builtin_bit_cast(unsigned int, ph);
@@ -564,8 +576,8 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a0, Flash
   if (grp == 0) {
     const float m1 = xo[64], l1 = xo[65];
     const float m = fmaxf(mused, m1);
-    const float a0 = mused == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mused - m) * c2);
-    const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m1 - m) * c2);
+    const float a0 = mused == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mused - m);
+    const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
     const float ltot = pair_sum(lsum * a0 + l1 * a1);
     const float inv = ltot > 0.0f ? a.oscale / ltot : 0.0f;
     if (live) {

@@ -656,7 +656,9 @@ int qi21_model_set_block(qi21_model* m, int layer, int w_dtype, const void* cons
   HIP_OK(qi21::launch_plane(w_dtype, w[4], I, H, m->w13[layer], 32, 64, 0, s));
   HIP_OK(qi21::launch_plane(w_dtype, w[5], I, H, m->w13[layer], 32, 64, 32, s));
   HIP_OK(qi21::launch_plane(w_dtype, w[6], H, I, m->w2[layer], H, 0, 0, s));
-  HIP_OK(hipMemcpyAsync(m->nq[layer], norm_q, 128 * 4, hipMemcpyDeviceToDevice, s));
+  // the q norm weights carry the softmax's log2(e) / sqrt(128), so every q
+  // the block produces is in the base-2 units the attention kernels take
+  HIP_OK(qi21::launch_scale(128, norm_q, (float)(1.4426950408889634 / 11.313708498984761), m->nq[layer], s));
   HIP_OK(hipMemcpyAsync(m->nk[layer], norm_k, 128 * 4, hipMemcpyDeviceToDevice, s));
   int rc = sync_stream(s);
   if (rc) return rc;

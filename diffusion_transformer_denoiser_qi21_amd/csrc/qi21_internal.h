@@ -161,6 +161,8 @@ hipError_t launch_to_f32(int src_dtype, const void* src, size_t n, float* dst, h
 
 // fill count 32-bit words with value (a kernel, so it is safe to capture)
 hipError_t launch_fill32(void* p, uint32_t value, size_t count, hipStream_t s);
+// dst[i] = src[i] * f, i < n (device pointers; in place allowed)
+hipError_t launch_scale(int n, const float* src, float f, float* dst, hipStream_t s);
 // RoPE tables cos / sin [n][64] packed into out [n][128] for the q|k GEMM
 // epilogue: out[r][4m + (0, 1, 2, 3)] = cos[r][2m], cos[r][2m + 1],
 // sin[r][2m], sin[r][2m + 1]

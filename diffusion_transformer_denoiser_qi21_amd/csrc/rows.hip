@@ -675,6 +675,17 @@ __global__ void fill32_kernel(uint32_t* p, uint32_t v, size_t n) {
   if (i < n) p[i] = v;
 }
 
+__global__ void scale_kernel(int n, const float* __restrict__ src, float f, float* __restrict__ dst) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src[i] * f;
+}
+
+hipError_t launch_scale(int n, const float* src, float f, float* dst, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scale_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, src, f, dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill32(void* p, uint32_t value, size_t count, hipStream_t s) {
   if (count == 0) return hipSuccess;
   hipLaunchKernelGGL(fill32_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s,

@@ -112,7 +112,11 @@ int qi21_op_vt_gemm(int H, int nkeys, int K, const void* Wv, int lda, const void
  * j < n1 come from k1 [j][ldk1] (column h*128) and V^T vt1 [h*128+d][ldvt1];
  * keys n1 + j from k2 / vt2 likewise.  In a V^T row, key j of a source sits
  * at column vt_pos(j) = j with bits 2 and 3 swapped (a permutation inside
- * each group of 16 keys, as the QKV epilogue of qi21_op_gemm writes it).  q f16 [nq][ldq] at column h*128.
+ * each group of 16 keys, as the QKV epilogue of qi21_op_gemm writes it).
+ * q f16 [nq][ldq] at column h*128 holds q_i in base-2 units, q_i * log2(e)
+ * / sqrt(128): the score's exponent of 2 is then q_i . k_j itself (the
+ * model's q norm weights carry that factor, so the q that qi21_op_qk_gemm /
+ * qi21_op_qkrope produce with them arrives so scaled).
  * Requires nq >= 1, heads >= 1, n1, n2 >= 0, n1 + n2 >= 1, all leading
  * dimensions % 8 == 0, ldvt >= round_up(n_src, 64) with finite values in
  * the padding columns.  vis (device, uint32 [nq]) should be non-decreasing

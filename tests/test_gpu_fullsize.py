@@ -137,7 +137,9 @@ def test_flash_full_shape_sampled(case):
         nq, n1, n2 = lay.prefix_len, lay.prefix_len, 0
     m = n1 + n2
     seed = 7000 + nq
-    qd = dev_f16(seed, 1, (nq, H), 1.0)
+    # q in the kernel's base-2 units: f16 of (f16 q) * f32(log2(e) / sqrt(128))
+    ql2 = np.log2(np.e) / np.sqrt(128.0)
+    qd = (dev_f16(seed, 1, (nq, H), 1.0).float() * float(np.float32(ql2))).half()
     kd = dev_f16(seed, 2, (m, H), 1.0)
     vd = dev_f16(seed, 3, (m, H), 1.0)
     ld1 = (n1 + 63) // 64 * 64
@@ -151,7 +153,8 @@ def test_flash_full_shape_sampled(case):
     torch.cuda.synchronize()
     rng = np.random.default_rng(nq)
     rows = np.sort(np.concatenate([rng.choice(nq, 24, replace=False), [0, 5, 21, 22, nq - 1]]))
-    qh = host_rows_f16(seed, 1, H, rows, 1.0)
+    qh = (host_rows_f16(seed, 1, H, rows, 1.0).astype(np.float32) * np.float32(ql2)).astype(np.float16)
+    qh = qh.astype(np.float64) / ql2
     kh = inputs.host_array(seed, 2, (m, H), 1.0).astype(np.float16).astype(np.float32)
     vh = inputs.host_array(seed, 3, (m, H), 1.0).astype(np.float16).astype(np.float32)
     visible = vis[rows] if vis is not None else np.full(len(rows), m, np.int64)

@@ -204,6 +204,9 @@ def test_gemm_plane_conversion_exact():
 
 # ───────────────────────────── flash attention ─────────────────────────────
 
+QL2 = np.log2(np.e) / np.sqrt(128.0)  # the attention kernels take q * QL2
+
+
 def _vt(v, ld):
     """V [n][H] -> V^T [H][ld] in the attention kernel's key order, zero padding"""
     out = np.zeros((v.shape[1], ld), np.float32)
@@ -232,7 +235,11 @@ def test_flash_parity(case):
         vis = O.prefix_visibility(lay)
         nq, n1, n2 = lay.prefix_len, lay.prefix_len, 0
     m = n1 + n2
+    # q in the kernel's base-2 units (f16 of q log2(e) / sqrt(128)); the
+    # oracle gets the q that stands for
     qa = f16_host(5, 1, (nq, H), 1.0)
+    ql = (qa * np.float32(QL2)).astype(np.float16)
+    qa = ql.astype(np.float64) / QL2
     k = f16_host(5, 2, (m, H), 1.0)
     v = f16_host(5, 3, (m, H), 1.0)
     oscale = 2.0
@@ -240,7 +247,7 @@ def test_flash_parity(case):
     ld2 = ((max(n2, 1) + 63) // 64) * 64 + 64
     k2panel = np.zeros((max(n2, 1), 2 * H), np.float32)  # k at column H of a wider panel
     k2panel[:n2, H:] = k[n1:]
-    dq = dev(qa, torch.float16)
+    dq = dev(ql)
     dk1 = dev(k[:n1] if n1 else np.zeros((1, H), np.float32), torch.float16)
     dvt1 = dev(_vt(v[:n1], ld1), torch.float16)
     dk2 = dev(k2panel, torch.float16)
