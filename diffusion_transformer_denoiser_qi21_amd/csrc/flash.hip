@@ -131,6 +131,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a0, Fl
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // With 8 waves the two waves of a SIMD (w and w + 4) take its issue slots
+  // in a fixed order, waves 0-3 first: the lower wave runs each step's
+  // phases ahead of its partner, so one's matrix phase meets the other's
+  // vector phase instead of both contending for the same unit.
+  if (NW == 8 && wave < 4) __builtin_amdgcn_s_setprio(1);
   const int hs = lane >> 5, l32 = lane & 31;
   // Blocks are dealt to the 8 XCDs round-robin (block b -> XCD b % 8).  All
   // query blocks of a head go to one XCD, so the head's K / V^T tiles are
@@ -382,6 +387,8 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a0, Flash
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // group 0 first in the issue order (as in flash_kernel)
+  if (wave < 4) __builtin_amdgcn_s_setprio(1);
   const int grp = wave >> 2, qw = wave & 3;
   const int hs = lane >> 5, l32 = lane & 31;
   const int nqb = (a.nq + BQ - 1) / BQ;
