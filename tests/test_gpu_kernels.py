@@ -263,6 +263,47 @@ def test_flash_parity(case):
     assert rel(out.float().cpu().numpy(), want) < F16_TOL
 
 
+# 32 heads; on 256 CUs 96 queries run as key-split blocks, 2048 as 4-wave
+# blocks and 4096 as 8-wave blocks
+@pytest.mark.parametrize("nq", [96, 2048, 4096])
+@pytest.mark.parametrize("order", ["growing", "shrinking", "masked_start"])
+def test_flash_lazy_rescale_paths(order, nq):
+    """Key scales that make a query's maximum grow by far more than the lazy
+    rescale threshold from tile to tile (a rescale at every tile), shrink
+    (later tiles underflow against the first), or a block-causal start where
+    the first visible keys are few: the running-maximum bookkeeping of the
+    base-2 scores against the oracle's softmax, in each launch form."""
+    q = Q()
+    heads, hd = 32, 128
+    H = heads * hd
+    n1 = 333
+    qa = f16_host(6, 1, (nq, H), 1.0)
+    ql = (qa * np.float32(QL2)).astype(np.float16)
+    qe = ql.astype(np.float64) / QL2
+    k = inputs.host_array(6, 2, (n1, H), 1.0)
+    j = np.arange(n1, dtype=np.float64)[:, None]
+    if order == "growing":
+        k = k * (0.05 + j / 12.0)        # maxima grow by ~2^10 per tile
+    elif order == "shrinking":
+        k = k * (30.0 / (1.0 + j / 8.0))  # the first tile dominates
+    k = k.astype(np.float16).astype(np.float32)
+    v = f16_host(6, 3, (n1, H), 1.0)
+    vis = None
+    if order == "masked_start":
+        vis = np.minimum(1 + np.arange(nq) * 4, n1).astype(np.int64)  # 1, 5, 9, ... keys
+    ld1 = ((n1 + 63) // 64) * 64
+    out = torch.zeros(nq, H, device="cuda", dtype=torch.float16)
+    dvis = dev(vis.astype(np.int32)) if vis is not None else None
+    q.qi21_op_flash(nq, heads, dev(ql), H, dev(k, torch.float16), H, dev(_vt(v, ld1), torch.float16), ld1, n1,
+                    None, 0, None, 0, 0, dvis, out, H, 1.0)
+    sync()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    visible = vis if vis is not None else np.full(nq, n1, np.int64)
+    want = O.attention(qe, k, v, visible, heads, hd)
+    assert rel(got, want) < F16_TOL
+
+
 # ───────────────────────────── row kernels ─────────────────────────────
 
 @pytest.mark.parametrize("h", [256, 4096])
