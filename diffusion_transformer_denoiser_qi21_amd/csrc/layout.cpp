@@ -1,14 +1,17 @@
 // Layout helpers of the qi21 C ABI (host only): prefix / target sizes,
 // RoPE positions, the prefix's block-causal visibility and the RoPE tables.
 //
-// Definitions from [QI] (docs.rs cortiq-engine 0.8.4,
-// src/cortiq_engine/qwen_image21.rs): `Qi21Layout` (positions: text rows
-// advance one position on all three axes; an image block keeps the frame
-// at the running position, centres its grid with integer halving and then
-// advances the position by max(h, w)), `prefill` (a text row sees the keys
-// up to itself, an image row up to the end of its image block) and
-// `rope_tables` (float32 frequencies 1/theta^(2i/d) per axis, float32
-// angle, columns frame, row, col).
+// Following [QI] (docs.rs cortiq-engine 0.8.4,
+// src/cortiq_engine/qwen_image21.rs), items `Qi21Layout`, `prefill` and
+// `rope_tables`.  Each row gets a (frame, row, col) position from a running
+// counter p: a text row takes (p, p, p) and bumps p by one; an image of
+// h x w tokens puts all its tokens on frame p, with the grid shifted so
+// that row r sits at r - (h - h/2) and column c at c - (w - w/2) (integer
+// division), after which p grows by max(h, w).  In a prefill, text row i
+// attends to keys 0..i and an image row to every key up to the last row of
+// its own image.  The tables use float32 frequencies 1/theta^(2i/d) for
+// each axis of width d and a float32 angle, with the axes laid out frame,
+// row, col.
 #include <cmath>
 #include <vector>
 

@@ -83,7 +83,7 @@ class Layout:
         """The last run is a non-empty image, and the prefix is not empty ([QI] ``validate``)."""
         last = self.segs[-1] if self.segs else None
         if last is None or last[0] != "image" or last[1] <= 0 or last[2] <= 0:
-            raise ValueError("the layout must end with a non-empty target image block")
+            raise ValueError("invalid layout: its last run has to be an image of at least one row and one column")
         if self.prefix_len == 0:
             raise ValueError("the prompt prefix is empty")
 

@@ -541,6 +541,30 @@ def test_time_mods_structure(tiny):
     assert _rel(m3, mods) > 1e-3
 
 
+def test_time_mods_hand_values():
+    # A two-wide time path whose values are worked out by hand at t = 0, where
+    # e = [cos 0 ...| sin 0 ...] = [1]*128 + [0]*128 ([QI] Qi21Dit::temb,
+    # Qi21Dit::mods).  t_lin1 reads e[0] with weights -3 and 2, so its output
+    # is (-3, 2) and h = silu of it = (-0.14227762, 1.76159416); t_lin2 =
+    # diag(1, -4) gives temb = (-0.14227762, -7.04637662); the second silu
+    # gives s = (-0.06608660, -0.00612894); modulation and norm_out are small
+    # integer matrices applied to s.  Dropping either silu, or moving the
+    # second one before t_lin2, changes s by more than 100x somewhere.
+    t_lin1 = np.zeros((2, 256), np.float32)
+    t_lin1[0, 0], t_lin1[1, 0] = -3.0, 2.0
+    tw = {
+        "t_lin1": t_lin1,
+        "t_lin2": np.array([[1.0, 0.0], [0.0, -4.0]], np.float32),
+        "modulation": np.array([[1, 0], [0, 1], [2, 0], [0, -1], [1, 1], [0, 0], [-1, 0], [0, 3]], np.float32),
+        "norm_out": np.array([[0, 1], [1, 0]], np.float32),
+    }
+    s0, s1 = -0.06608659926223291, -0.006128941176595901
+    mods, fs = O.time_mods(tw, 0.0)
+    want_m = [s0, s1, 2 * s0, -s1, s0 + s1, 0.0, -s0, 3 * s1]
+    assert np.allclose(mods, want_m, rtol=2e-6, atol=1e-9)
+    assert np.allclose(fs, [s1, s0], rtol=2e-6, atol=1e-9)
+
+
 def test_sampler_steps(tiny):
     w, model, d = tiny
     lay = O.Layout(w.layout())
@@ -588,3 +612,23 @@ def test_embed_text_norm_and_structure():
     assert np.allclose(o2, O.gelu_tanh(np.full((1, d), -1.5, np.float32)), rtol=0, atol=1e-7)
     # scale invariance of the norm (eps = 0): features x 8 give the same rows
     assert np.array_equal(O.embed_text(feats * 8, w0, eye, ident, 0.0), O.embed_text(feats, w0, eye, ident, 0.0))
+
+
+def test_embed_text_gelu_sits_between_the_projections():
+    # [QI] Qi21Dit::embed_text: txt_in1, then the tanh GELU, then txt_in2.
+    # Row 0 (constant -7) normalises to -1 and the weight w = 0.5 scales it
+    # to (-1.5, -1.5); row 1 (3, -3) becomes (1.5, -1.5).  txt_in1 =
+    # diag(2, 1) gives (-3, -1.5) and (3, -1.5); the GELU gives (gelu(-3),
+    # gelu(-1.5)) and (gelu(3), gelu(-1.5)); txt_in2 doubles and swaps the
+    # two columns: (2 gelu(-1.5), 2 gelu(-3)) = (-0.20085685, -0.00727478)
+    # and (2 gelu(-1.5), 2 gelu(3)) = (-0.20085685, 5.99272522).  The GELU
+    # before txt_in1 gives 2 gelu(-1.5) * 2 in column 1 of row 0; after
+    # txt_in2 it gives gelu(-3) in column 0; a transposed txt_in2 or txt_in1
+    # swaps the columns.
+    feats = np.array([[-7.0, -7.0], [3.0, -3.0]], np.float32)
+    w = np.full(2, 0.5, np.float32)
+    d21 = np.diag([2.0, 1.0]).astype(np.float32)
+    swap2 = np.array([[0.0, 2.0], [2.0, 0.0]], np.float32)
+    out = O.embed_text(feats, w, d21, swap2, 0.0)
+    want = np.array([[-0.20085684603953413, -0.007274784163545989], [-0.20085684603953413, 5.992725215836454]])
+    assert np.allclose(out, want, rtol=1e-6, atol=1e-7)
