@@ -10,10 +10,18 @@ qkrope, attention, O GEMM, rowop, gate/up GEMM + SwiGLU, down GEMM, rowop]
 prefilled once before the timed region.  Weights are random (seeded,
 bf16, N(0, 0.02)) with the full model's shapes; inputs are synthetic.
 
+The FFN input and the SwiGLU hidden are stored in the lo8 form by default
+(f16 plus a scaled e4m3 residual, ``--ffn lo8``), the configuration whose
+velocity the tests hold to 1e-3 of the oracle; ``--ffn f16`` times the
+pages' single-f16 design and ``--ffn pair`` the f16-pair form.
+
 Prints ONE JSON line: s/step (the metric), TFLOP/s and the fraction of the
-f16 MFMA peak, the dominant kernel's roofline (gate/up GEMM, timed with HIP
-events on the launch stream inside the timed region) and the CPU oracle's
-time on a bounded sample of the same workload.
+f16 MFMA peak (algorithmic FLOP of the method: the residual products of
+the lo8 form are not counted), the dominant kernel's roofline (gate/up
+GEMM, timed with HIP events on the launch stream inside the timed region),
+every site's MFMA fraction from a separate profiled pass after the timed
+region, and the CPU oracle's time on a bounded sample of the same
+workload.
 
 This module also holds the GPU-side workload builders the GPU tests use.
 """
@@ -170,7 +178,13 @@ def cpu_baseline(w, min_s=10.0):
     except Exception:
         pass
     assert np.all(np.isfinite(v))
-    return {"value": est, "unit": "s/step", "cores": threads, "kind": "oracle",
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return {"value": est, "unit": "s/step", "cores": threads, "cpu_model": cpu, "kind": "oracle",
             "sample": f"{blocks_done} of {spec.layers} blocks of the {w.name} step ({n} target rows vs {lp + n} keys) "
                       f"timed {t_blocks:.1f} s on the host, plus embed and final {t_io:.2f} s; blocks scaled "
                       f"x{spec.layers / blocks_done:.2f}"}
@@ -214,6 +228,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="1024", choices=sorted(k for k in CONFIGS if k != "tiny"))
+    ap.add_argument("--ffn", default="lo8", choices=("lo8", "pair", "f16"),
+                    help="storage of the FFN input and hidden (lo8: f16 + scaled e4m3 residual; the default)")
+    ap.add_argument("--site-steps", type=int, default=3,
+                    help="steps of the untimed pass that times every site with HIP events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (the scale for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -235,6 +253,7 @@ def main(argv=None):
     props = torch.cuda.get_device_properties(dev)
     t_build = time.perf_counter()
     opt = Q.qi21_default_options()
+    opt.ffn_mode = {"f16": Q.QI21_FFN_F16, "pair": Q.QI21_FFN_PAIR, "lo8": Q.QI21_FFN_LO8}[args.ffn]
     m = build_model(spec, opt)
     t_build = time.perf_counter() - t_build
     nprog = len(w.prefixes)
@@ -268,6 +287,14 @@ def main(argv=None):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_cls, n_cls = Q.qi21_profile_read(m)
+    # every site's launches bracketed by events, after the timed region
+    site_ms, site_n = None, None
+    if args.site_steps > 0:
+        Q.qi21_set_profile(m, (1 << 0) | (1 << 2) | (1 << 3) | (1 << 4) | (1 << 5))
+        for _ in range(args.site_steps):
+            one_step()
+        torch.cuda.synchronize()
+        site_ms, site_n = Q.qi21_profile_read(m)
     Q.qi21_set_profile(m, 0)
     sec = elapsed / args.steps
     flops = sum(step_flops(spec, d["n"], d["lp"])[0] for d in ds)
@@ -277,6 +304,34 @@ def main(argv=None):
     rows_total = sum(d["n"] for d in ds)
     w13_flop = 2.0 * rows_total * 2 * spec.inter * spec.dim
     w13_tf = w13_flop / (w13_launch_ms / 1e3) / 1e12 if w13_launch_ms > 0 else 0.0
+    sites = None
+    if site_ms is not None:
+        h, i = spec.dim, spec.inter
+        keys_rows = sum(d["n"] * (d["lp"] + d["n"]) for d in ds)
+        per_launch = {  # algorithmic FLOP of one launch (one block) of each site
+            "qkv": (0, 2.0 * rows_total * 3 * h * h), "attention": (2, 4.0 * keys_rows * h),
+            "o": (3, 2.0 * rows_total * h * h), "gate_up": (4, 2.0 * rows_total * 2 * i * h),
+            "down": (5, 2.0 * rows_total * i * h)}
+        sites = {}
+        g_ms = g_fl = 0.0
+        for name, (c, fl) in per_launch.items():
+            if site_n[c] == 0:
+                continue
+            ms = site_ms[c] / site_n[c]
+            tf = fl / (ms / 1e3) / 1e12
+            sites[name] = {"launch_ms": ms, "tflops": tf, "frac": tf / PEAK_F16_TFLOPS, "launches": int(site_n[c])}
+            if name != "attention":
+                g_ms += site_ms[c]
+                g_fl += fl * site_n[c]
+        if g_ms > 0:
+            tf = g_fl / (g_ms / 1e3) / 1e12
+            sites["all_gemms"] = {"ms_per_step": g_ms / args.site_steps, "tflops": tf, "frac": tf / PEAK_F16_TFLOPS}
+        sites["note"] = (f"HIP events around every launch of each site over {args.site_steps} untimed steps after the "
+                         "timed region; algorithmic FLOP (lo8 residual products not counted)")
+    # the lo8 form runs its FFN GEMMs over 1.5x their K in MFMA cycles (the
+    # residual k-tiles on the fp8 MFMA at twice the f16 rate): the fraction
+    # of the peak of that instruction mix, for context
+    mix = 1.5 if args.ffn == "lo8" else 2.0 if args.ffn == "pair" else 1.0
     line = {
         "metric": "denoiser step s/call + TFLOP/s (% f16 MFMA peak) at 1024^2, 32 blocks",
         "value": sec,
@@ -288,17 +343,20 @@ def main(argv=None):
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": (sec / PAGES_STEP_S[args.config]) if (args.config in PAGES_STEP_S and nprog == 1) else None,
-        "dtype": "f16",
+        "dtype": {"lo8": "f16+e4m3", "pair": "f16", "f16": "f16"}[args.ffn],
         "data": "synthetic (seeded N(0,0.02) bf16 weights of the full 32-block dim-4096 model; N(0,1) rows)",
         "config": {"workload": w.note, "blocks": spec.layers, "dim": spec.dim, "heads": spec.heads,
-                   "mlp_hidden": spec.inter, "target_rows": rows_total, "prefix_rows": lp, "programs": nprog},
+                   "mlp_hidden": spec.inter, "target_rows": rows_total, "prefix_rows": lp, "programs": nprog,
+                   "ffn_storage": args.ffn},
         "tflops_per_s": tflops,
         "pct_f16_peak": 100.0 * tflops / PEAK_F16_TFLOPS,
         "step_tflop": flops / 1e12,
         "roofline": {"bound": "mfma", "kernel": "gate/up GEMM + SwiGLU", "achieved": w13_tf,
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": w13_tf / PEAK_F16_TFLOPS,
                      "traffic": recorded_traffic(args.config), "launch_ms": w13_launch_ms,
-                     "launches": int(n_cls[4]), "algorithmic_flop": w13_flop},
+                     "launches": int(n_cls[4]), "algorithmic_flop": w13_flop,
+                     "mfma_mix_frac": w13_tf * mix / PEAK_F16_TFLOPS},
+        "sites": sites,
         "device": props.name,
         "build_s": round(t_build, 1),
         "prefill_s": round(t_pre, 3),

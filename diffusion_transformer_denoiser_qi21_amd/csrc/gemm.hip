@@ -33,6 +33,7 @@
 // the v columns transposed (V^T, the layout the attention kernel streams).
 // Range-guard factors are powers of two folded into oscale / inscale.
 #include "qi21_internal.h"
+#include "lo8.h"
 
 #include <algorithm>
 
@@ -44,6 +45,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 namespace {
 
@@ -178,7 +180,12 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
     }
   } else if constexpr (EPI == EPI_VT) {
     // output rows are V dims, columns are keys: key c goes to vt_pos(c),
-    // which keeps aligned runs of 4 together
+    // which keeps aligned runs of 4 together.  Columns from nvalid up to
+    // the leading dimension (whole groups of 16, within which vt_pos
+    // permutes) get zeros: the attention kernel reads whole 64-key tiles
+    // and multiplies the columns past the keys by P = 0, which must not
+    // meet a stale non-finite value.
+    const int cz = a.ldo & ~15;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int row = r0 + i * 32 + l32;
@@ -194,12 +201,57 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
             for (int e = 0; e < 4; ++e) v[e] = (f16)(acc[i][j][4 * g + e] * a.oscale);
             if (c + 3 < a.nvalid) {
               *reinterpret_cast<half4*>(orow + vt_pos(c)) = v;
-            } else {
+            } else if (c < cz) {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                if (c + e < a.nvalid) orow[vt_pos(c) + e] = v[e];
+                if (c + e >= a.nvalid) v[e] = (f16)0.0f;
+              *reinterpret_cast<half4*>(orow + vt_pos(c)) = v;
             }
           }
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU8) {
+    // the wave's 4 column tiles are 64 hidden columns, one scale block per
+    // row: lanes l and l ^ 32 hold its two halves
+    static_assert(TN == 4, "a wave spans one 64-column scale block");
+    const int hc = c0 / 2;  // first hidden column of the wave
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = r0 + i * 32 + l32;
+      half4 hi[2][4];
+      floatx4 lo[2][4];
+      float mx = 0.0f;
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float h = silu_f(acc[i][2 * p][4 * g + e] * a.inscale) * (acc[i][2 * p + 1][4 * g + e] * a.inscale) *
+                            a.oscale;
+            hi[p][g][e] = (f16)h;
+            lo[p][g][e] = h - (float)hi[p][g][e];  // exact in f32
+            mx = fmaxf(mx, fabsf(lo[p][g][e]));
+          }
+      {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      }
+      const int ex = lo8_exp(mx);
+      const float inv = __builtin_ldexpf(1.0f, -ex);
+      if (row < a.M) {
+        f16* orow = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo;
+        uint8_t* brow = reinterpret_cast<uint8_t*>(orow);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = hc + p * 32 + 8 * g + 4 * hsel;
+            *reinterpret_cast<half4*>(orow + lo8_hi_at(c)) = hi[p][g];
+            const floatx4 v = lo[p][g] * inv;
+            *reinterpret_cast<unsigned*>(brow + lo8_lo_at(c)) = pack_e4m3(v[0], v[1], v[2], v[3]);
+          }
+        if (hsel == 0) a.osc[(size_t)row * a.ldos + hc / 64] = (uint8_t)(ex + 127);
       }
     }
   } else {  // EPI_SWIGLU, EPI_SWIGLU2: tiles (2p, 2p+1) hold matching gate / up columns
@@ -305,6 +357,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, floatx16 (&acc)[TM][
               reinterpret_cast<f16*>(a.out)[(size_t)row * a.ldo + cbase + j * 32] = (f16)(acc[i][j][e] * a.oscale);
           }
     } else {
+      // keys from M up to the leading dimension (whole groups of 16) get
+      // zeros, as in the V^T epilogue above
+      const int rz = a.ld2 & ~15;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -319,10 +374,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, floatx16 (&acc)[TM][
             for (int e = 0; e < 4; ++e) v[e] = (f16)(acc[i][j][4 * g + e] * a.oscale);
             if (row + 3 < a.M) {
               *reinterpret_cast<half4*>(dst + pos) = v;
-            } else {
+            } else if (row < rz) {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                if (row + e < a.M) dst[pos + e] = v[e];
+                if (row + e >= a.M) v[e] = (f16)0.0f;
+              *reinterpret_cast<half4*>(dst + pos) = v;
             }
           }
         }
@@ -347,7 +403,17 @@ __device__ __forceinline__ int dswz(int r) { return (r >> 1) & 7; }
 // current unit's epilogue stores drain.  NW = 4 waves of 128 x 128 (one per SIMD) or 8
 // waves of 128 x 64 (two per SIMD, so one wave's issue stalls, barrier
 // waits and epilogue are covered by the other's MFMAs).
-template <int EPI, int NW>
+//
+// LO8 (the lo8 row form of GemmArgs): every third k-tile holds the fp8
+// residuals of the 128 columns the two before it hold as halves.  The
+// loads do not change (a k-tile is 128 bytes of each row either way); an
+// fp8 k-tile is two k-steps of 64 columns, each a 32-byte fragment per
+// lane and one scaled 32x32x64 MFMA per 32 x 32 tile, which takes as long
+// as two f16 k-steps.  A unit runs whole groups of three k-tiles in one
+// branch-free loop, so the accumulators stay in AGPRs.  Scales: the W
+// rows' are fixed over a unit; the A rows' two bytes of a group are read
+// at its first k-tile.
+template <int EPI, int NW, bool LO8 = false>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
   // 32 x 32 tiles per wave: 4 x 4 with 4 waves; 4 x 2 with 8, except the
   // q/k-norm epilogue, whose waves span whole 128-column heads (2 x 4)
@@ -356,13 +422,15 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
   constexpr int WTM = TM * 32, WTN = TN * 32;  // wave tile
   constexpr int NCOL = DBN / WTN;              // waves across the block's columns
   constexpr int NL = 32 / NW;                  // 16-byte loads per lane per operand per k-tile
+  static_assert(!LO8 || (NW == 4 && EPI != EPI_QKV), "fp8 k-tiles: 4-wave row-layout kernels");
   extern __shared__ __attribute__((aligned(16))) f16 smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / NCOL, wn = wave % NCOL;
   const int hsel = lane >> 5, l32 = lane & 31;
   const int K = a.K;
-  const int KT = K / DBK / a.ksplit;  // k-tiles per work unit
+  const int KT = K / DBK / a.ksplit;  // k-tiles per work unit (LO8: a multiple of 3)
+  const int ldw = a.ldw ? a.ldw : a.kw;
   const int tiles_n = a.N / DBN, tiles_m = (a.M + DBM - 1) / DBM;
   const int ntiles = tiles_n * tiles_m, nunits = ntiles * a.ksplit;
   // this block's run of the tile sequence
@@ -409,7 +477,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
     // the instruction offset (i % 4) KiB moves the LDS and the global
     // address alike; the global part is taken back here
     voa[i] = (r * a.lda + 8 * c) * 2 - (i & 3) * 1024;
-    vob[i] = (r * a.kw + 8 * c) * 2 - (i & 3) * 1024;
+    vob[i] = (r * ldw + 8 * c) * 2 - (i & 3) * 1024;
   }
   // Buffer resources over a tile's A rows and W rows; A rows at or past M
   // fall outside the resource's range and return zeros.
@@ -418,7 +486,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
                                              (min(a.M - m0, DBM) - 1) * a.lda * 2 + K * 2, 0x00020000);
   };
   auto rsrc_b = [&](int n0) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (size_t)n0 * a.kw), 0, DBN * a.kw * 2, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (size_t)n0 * ldw), 0, DBN * ldw * 2, 0x00020000);
   };
   // W columns wrap every kw (K is kw or 2 kw)
   const int KTW = a.kw / DBK;
@@ -458,6 +526,23 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
       bf[b][j] = *reinterpret_cast<const half8*>(sa + DBM * DBK + (row * 8 + (c ^ dswz(row))) * 8);
     }
   };
+  // fp8 fragments: 32 bytes per lane (chunks 4 kk + 2 hsel and the next),
+  // read in the same order, one fragment (two 16-byte reads) per call
+  i32x8 af8[2][TM], bf8[2][TN];
+  auto read8 = [&](int t, int kk, int b, int r) {
+    const f16* sa = smem + (t % DNS) * DSTAGE;
+    const int c = kk * 4 + 2 * hsel;
+    const bool isa = r == 0 || r > TN;
+    const int row = isa ? wm * WTM + (r == 0 ? 0 : r - TN) * 32 + l32 : wn * WTN + (r - 1) * 32 + l32;
+    const f16* base = sa + (isa ? 0 : DBM * DBK) + row * 64;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + (c ^ dswz(row)) * 8);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + ((c + 1) ^ dswz(row)) * 8);
+    const i32x8 v = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    if (isa)
+      af8[b][r == 0 ? 0 : r - TN] = v;
+    else
+      bf8[b][r - 1] = v;
+  };
   // every epilogue but the V^T one stores along output rows: C^T = W A^T
   constexpr bool ROWS = EPI != EPI_QKV;
   auto mfma1 = [&](int b, int k) {
@@ -467,21 +552,51 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
     else
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[b][i], bf[b][j], acc[i][j], 0, 0, 0);
   };
+  // scales of the fp8 k-tiles: the W rows' (per unit) and, per A row, the
+  // two bytes of the current group's k-steps
+  int wsc[TN], asc[TM];
+  auto mfma8 = [&](int b, int k, int kk) {
+    const int i = k / TN, j = k % TN;
+    if (kk == 0)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf8[b][j], af8[b][i], acc[i][j], 0, 0, 0, wsc[j], 0,
+                                                                  asc[i]);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf8[b][j], af8[b][i], acc[i][j], 0, 0, 0, wsc[j], 1,
+                                                                  asc[i]);
+  };
   constexpr int MM = TM * TN, NDS = TM + TN, NQ = 2 * NL;
   // A k-tile's NQ loads go out over three k-steps: [0, Q1) in the last
   // k-step of the k-tile two before, [Q1, Q2) and [Q2, NQ) in the first two
-  // of the k-tile before.
+  // of the k-tile before.  (Before an fp8 k-tile's barrier there is one
+  // k-step: [Q1, NQ) go out in it.)
   constexpr int Q1 = (NQ + 2) / 3, Q2 = Q1 + (NQ - Q1 + 1) / 2;
   // One k-step in a fixed order: MFMA k on fragment buffer b, then load
   // q0 + k of k-tile tl while below q1, then fragment read k of k-step kk
-  // of k-tile t into buffer b ^ 1 when rd.
+  // of k-tile t into buffer b ^ 1 when rd (with rd8: an fp8 fragment of
+  // k-step kk of k-tile t into fp8 buffer 0 instead).
   auto step = [&](int b, bool rd, int t, int kk, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int tl,
-                  int q0, int q1) {
+                  int q0, int q1, bool rd8 = false) {
 #pragma unroll
     for (int k = 0; k < MM; ++k) {
       mfma1(b, k);
       if (q0 + k < q1) load1(ra, rb, tl & 1, kt0 + tl, q0 + k);
-      if (rd && k < NDS) read1(t, kk, b ^ 1, k);
+      if (rd && !rd8 && k < NDS) read1(t, kk, b ^ 1, k);
+      if constexpr (LO8)
+        if (rd8 && k < NDS) read8(t, kk, 0, k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // An fp8 k-step: MFMA k (k-step kk8 of its k-tile) on fp8 buffer b8,
+  // loads as above, then fragment read k of k-step kk of k-tile t: into
+  // fp8 buffer 1 (rd8) or f16 buffer 0 (rd16).
+  auto step8 = [&](int b8, int kk8, bool rd8, bool rd16, int t, int kk, __amdgpu_buffer_rsrc_t ra,
+                   __amdgpu_buffer_rsrc_t rb, int tl, int q0, int q1) {
+#pragma unroll
+    for (int k = 0; k < MM; ++k) {
+      mfma8(b8, k, kk8);
+      if (q0 + k < q1) load1(ra, rb, tl & 1, kt0 + tl, q0 + k);
+      if (rd8 && k < NDS) read8(t, kk, 1, k);
+      if (rd16 && k < NDS) read1(t, kk, 0, k);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -492,6 +607,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
     for (int q = 0; q < NQ; ++q) load1(ra, rb, 0, kt0, q);
 #pragma unroll
     for (int q = 0; q < Q1; ++q) load1(ra, rb, 1, kt0 + min(1, KT - 1), q);
+  };
+  // the wait for, and the barrier after, a k-tile's reads and the next
+  // k-tile's loads
+  auto sync_tile = [&]() {
+    __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   int tm, tn;
@@ -507,46 +629,107 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    // k-tile 0 landed.  After an epilogue its stores share the vector
-    // memory counter with these loads, so wait for all of them.
-    if (sq == seq0)
-      __builtin_amdgcn_s_waitcnt(wait_imm(Q1, 15));
-    else
-      __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
-    __builtin_amdgcn_s_barrier();
+    if constexpr (LO8) {
+      // A scales: rows past M read as zero (so do their A rows)
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.asc + (size_t)m0 * a.lds), 0, min(a.M - m0, DBM) * a.lds, 0x00020000);
+      // the A scale bytes of the group at unit-local k-tile t (its k-steps
+      // 2 g and 2 g + 1, g the global group)
+      auto load_asc = [&](int t) {
+        const int g = (kt0 + t) / 3;
 #pragma unroll
-    for (int r = 0; r < NDS; ++r) read1(0, 0, 0, r);
-    __builtin_amdgcn_sched_barrier(0);
-    // (with KT = 1 the prologue's k-tile 1 is k-tile 0 again, in the stage
-    // no one reads, and the loop below does not run)
-    for (int t = 0; t < KT - 1; ++t) {
-      step(0, true, t, 1, ra, rb, t + 1, Q1, Q2);
-      step(1, true, t, 2, ra, rb, t + 1, Q2, NQ);
-      step(0, true, t, 3, ra, rb, 0, 0, 0);
-      // this wave's reads of stage t % 2 are done and k-tile t + 1 has
-      // landed; after the barrier every wave is past both, so the stage
-      // can take the first part of k-tile t + 2 (past the last k-tile:
-      // k-tile 0 again, into a stage no one reads any more)
-      __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
+        for (int i = 0; i < TM; ++i)
+          asc[i] = (int)__builtin_amdgcn_raw_buffer_load_b16(rs, (wm * WTM + i * 32 + l32) * a.lds + 2 * g, 0, 0);
+      };
+#pragma unroll
+      for (int j = 0; j < TN; ++j) wsc[j] = a.wsc[n0 + wn * WTN + j * 32 + l32];
+      load_asc(0);
+      if (sq == seq0)
+        __builtin_amdgcn_s_waitcnt(wait_imm(Q1, 15));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
       __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int r = 0; r < NDS; ++r) read1(0, 0, 0, r);
       __builtin_amdgcn_sched_barrier(0);
-      step(1, true, t + 1, 0, ra, rb, t + 2 < KT ? t + 2 : t, 0, Q1);
+      // groups (f16, f16, fp8) of k-tiles t, t + 1, t + 2; the next group's
+      // A scales are fetched after this group's fp8 MFMAs are issued
+      for (int t = 0; t < KT - 3; t += 3) {
+        step(0, true, t, 1, ra, rb, t + 1, Q1, Q2);
+        step(1, true, t, 2, ra, rb, t + 1, Q2, NQ);
+        step(0, true, t, 3, ra, rb, 0, 0, 0);
+        sync_tile();
+        step(1, true, t + 1, 0, ra, rb, t + 2, 0, Q1);
+        step(0, true, t + 1, 1, ra, rb, t + 2, Q1, Q2);
+        step(1, true, t + 1, 2, ra, rb, t + 2, Q2, NQ);
+        step(0, true, t + 1, 3, ra, rb, 0, 0, 0);
+        sync_tile();
+        step(1, false, t + 2, 0, ra, rb, t + 3, 0, Q1, true);
+        step8(0, 0, true, false, t + 2, 1, ra, rb, t + 3, Q1, NQ);
+        sync_tile();
+        step8(1, 1, false, true, t + 3, 0, ra, rb, t + 4, 0, Q1);
+        load_asc(t + 3);
+      }
+      // the last group
+      {
+        const int t = KT - 3;
+        step(0, true, t, 1, ra, rb, t + 1, Q1, Q2);
+        step(1, true, t, 2, ra, rb, t + 1, Q2, NQ);
+        step(0, true, t, 3, ra, rb, 0, 0, 0);
+        sync_tile();
+        step(1, true, t + 1, 0, ra, rb, t + 2, 0, Q1);
+        step(0, true, t + 1, 1, ra, rb, t + 2, Q1, Q2);
+        step(1, true, t + 1, 2, ra, rb, t + 2, Q2, NQ);
+        step(0, true, t + 1, 3, ra, rb, 0, 0, 0);
+        sync_tile();
+        step(1, false, t + 2, 0, ra, rb, 0, 0, 0, true);
+        step8(0, 0, true, false, t + 2, 1, ra, rb, 0, 0, 0);
+        sync_tile();
+        const int nsq = sq + seq_step;
+        if (nsq < seq_end) {
+          tile_rc(nsq, tm, tn, kt0);
+          prologue(tm, tn, kt0);
+        }
+        step8(1, 1, false, false, 0, 0, ra, rb, 0, 0, 0);
+      }
+    } else {
+      // k-tile 0 landed.  After an epilogue its stores share the vector
+      // memory counter with these loads, so wait for all of them.
+      if (sq == seq0)
+        __builtin_amdgcn_s_waitcnt(wait_imm(Q1, 15));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int r = 0; r < NDS; ++r) read1(0, 0, 0, r);
+      __builtin_amdgcn_sched_barrier(0);
+      // (with KT = 1 the prologue's k-tile 1 is k-tile 0 again, in the stage
+      // no one reads, and the loop below does not run)
+      for (int t = 0; t < KT - 1; ++t) {
+        step(0, true, t, 1, ra, rb, t + 1, Q1, Q2);
+        step(1, true, t, 2, ra, rb, t + 1, Q2, NQ);
+        step(0, true, t, 3, ra, rb, 0, 0, 0);
+        // this wave's reads of stage t % 2 are done and k-tile t + 1 has
+        // landed; after the barrier every wave is past both, so the stage
+        // can take the first part of k-tile t + 2 (past the last k-tile:
+        // k-tile 0 again, into a stage no one reads any more)
+        sync_tile();
+        step(1, true, t + 1, 0, ra, rb, t + 2 < KT ? t + 2 : t, 0, Q1);
+      }
+      // the last k-tile
+      step(0, true, KT - 1, 1, ra, rb, 0, 0, 0);
+      step(1, true, KT - 1, 2, ra, rb, 0, 0, 0);
+      step(0, true, KT - 1, 3, ra, rb, 0, 0, 0);
+      // every wave's reads of every stage are done and no load is in flight:
+      // the next tile's first k-tiles can be fetched under the epilogue
+      sync_tile();
+      const int nsq = sq + seq_step;
+      if (nsq < seq_end) {
+        tile_rc(nsq, tm, tn, kt0);
+        prologue(tm, tn, kt0);
+      }
+      step(1, false, 0, 0, ra, rb, 0, 0, 0);
     }
-    // the last k-tile
-    step(0, true, KT - 1, 1, ra, rb, 0, 0, 0);
-    step(1, true, KT - 1, 2, ra, rb, 0, 0, 0);
-    step(0, true, KT - 1, 3, ra, rb, 0, 0, 0);
-    // every wave's reads of every stage are done and no load is in flight:
-    // the next tile's first k-tiles can be fetched under the epilogue
-    __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    const int nsq = sq + seq_step;
-    if (nsq < seq_end) {
-      tile_rc(nsq, tm, tn, kt0);
-      prologue(tm, tn, kt0);
-    }
-    step(1, false, 0, 0, ra, rb, 0, 0, 0);
     if constexpr (ROWS)
       epilogue_rows<EPI, TM, TN>(a, acc, m0 + wm * WTM, n0 + wn * WTN, lane, obase);
     else
@@ -654,12 +837,12 @@ __global__ __launch_bounds__(256) void gemm_rs_kernel(GemmArgs a) {
 
 namespace {
 
-template <int EPI, int NW>
+template <int EPI, int NW, bool LO8 = false>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   constexpr size_t lds = (size_t)DNS * DSTAGE * 2;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<EPI, NW>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<EPI, NW, LO8>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
@@ -675,7 +858,7 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   // persistent: one block per CU walks several tiles; fewer tiles than CUs:
   // one block per tile
   const int blocks = tiles > cus ? cus : tiles;
-  hipLaunchKernelGGL((gemm_dma_kernel<EPI, NW>), dim3(blocks), dim3(NW * 64), lds, s, a);
+  hipLaunchKernelGGL((gemm_dma_kernel<EPI, NW, LO8>), dim3(blocks), dim3(NW * 64), lds, s, a);
   return hipGetLastError();
 }
 
@@ -749,6 +932,22 @@ int gemm_split_count(int M, int N, int K, int maxs) {
 }
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s) {
+  if (a.kt8 < a.K / 64) {  // fp8 k-tiles: the 4-wave 256 x 256 kernel
+    if (a.kt8 != 2 || a.N % 256 != 0 || !a.asc || !a.wsc || a.lds % 2 != 0 || (tile != 0 && tile != -1) ||
+        (a.K / 64) % (3 * a.ksplit) != 0)
+      return hipErrorInvalidValue;
+    if (a.ksplit > 1) return epi == EPI_F32 ? launch_dma<EPI_F32, 4, true>(a, s) : hipErrorInvalidValue;
+    switch (epi) {
+      case EPI_F32: return launch_dma<EPI_F32, 4, true>(a, s);
+      case EPI_RESID: return launch_dma<EPI_RESID, 4, true>(a, s);
+      case EPI_SWIGLU8: return launch_dma<EPI_SWIGLU8, 4, true>(a, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (epi == EPI_SWIGLU8) {
+    if (a.N % 256 != 0 || (tile != 0 && tile != -1) || a.ksplit != 1) return hipErrorInvalidValue;
+    return launch_dma<EPI_SWIGLU8, 4>(a, s);
+  }
   if (a.ksplit > 1) {  // split units: 256 x 256 f32 partial products only
     if (epi != EPI_F32 || (tile != 0 && tile != 2) || a.N % 256 != 0 || (a.K / 64) % a.ksplit != 0)
       return hipErrorInvalidValue;

@@ -61,12 +61,14 @@ struct Acts {
   f16* panel = nullptr;  // [cap][2H] q | k
   f16* vt = nullptr;     // [H][cap] V^T of the pass's own rows
   f16* att = nullptr;    // [cap][H]
-  f16* hid = nullptr;    // [cap][I]
+  f16* hid = nullptr;    // [cap][I] (pair: [cap][2I]; lo8: rows of 3I bytes)
   float* part = nullptr; // [4 min(cap, 2048)][H] partial products of a down GEMM split over K
   float* mods = nullptr; // [4H] tanh-ed modulation of the pass
   float* out = nullptr;  // [cap][64] velocity before the finite check
   float* rcs = nullptr;  // [cap][128] packed RoPE table of the pass's rows when
                          // they come from several programs, or of a prefill
+  uint8_t* xsc = nullptr;  // lo8: [cap][H / 64] scales of the FFN input's residuals
+  uint8_t* hsc = nullptr;  // lo8: [cap][I / 64] scales of the hidden's residuals
 };
 
 struct Prog {
@@ -93,6 +95,7 @@ struct qi21_model {
   qi21_options o{};
   int nb = 0;
   std::vector<f16*> wqkv, wo, w13, w2;
+  std::vector<uint8_t*> w13s, w2s;  // lo8: per-row scales of the W13 / W2 residual bytes
   std::vector<float*> nq, nk;
   std::vector<char> set;
   float* img_in = nullptr;      // [H][64]
@@ -144,15 +147,22 @@ void dfree(qi21_model* m, void* p, size_t bytes) {
   m->bytes -= std::min(m->bytes, bytes ? bytes : (size_t)256);
 }
 
-// pair: the FFN input (in xn) and the SwiGLU hidden are kept as f16 pairs
-size_t acts_bytes(const qi21_geom& g, bool pair, int cap, size_t* parts) {
-  const size_t H = g.hidden, I = g.inter, c = cap, f = pair ? 2 : 1;
+constexpr int NACT = 12;
+
+// Bytes of the FFN input's and the hidden's rows per column: 2 (single
+// f16), 4 (f16 pairs), 3 (lo8: f16 plus an fp8 residual)
+size_t ffn_row_bytes(int mode) { return mode == QI21_FFN_PAIR ? 4 : mode == QI21_FFN_LO8 ? 3 : 2; }
+
+size_t acts_bytes(const qi21_geom& g, int ffn_mode, int cap, size_t* parts) {
+  const size_t H = g.hidden, I = g.inter, c = cap, f = ffn_row_bytes(ffn_mode);
+  const bool lo8 = ffn_mode == QI21_FFN_LO8;
   // slot 5: the partial products of a down GEMM split over K (4 planes of
   // up to 2048 rows; split GEMMs only run at fewer than 2048 rows)
-  const size_t p[10] = {c * H * 4, c * H * 2 * f, c * 2 * H * 2, H * c * 2, c * H * 2, 4 * std::min<size_t>(c, 2048) * H * 4,
-                        c * I * 2 * f, 4 * H * 4, c * 64 * 4, c * 128 * 4};
+  const size_t p[NACT] = {c * H * 4, c * H * std::max<size_t>(f, 2), c * 2 * H * 2, H * c * 2, c * H * 2,
+                          4 * std::min<size_t>(c, 2048) * H * 4, c * I * f, 4 * H * 4, c * 64 * 4, c * 128 * 4,
+                          lo8 ? c * H / 64 : 0, lo8 ? c * I / 64 : 0};
   size_t t = 0;
-  for (int i = 0; i < 10; ++i) {
+  for (int i = 0; i < NACT; ++i) {
     if (parts) parts[i] = p[i];
     t += p[i];
   }
@@ -160,11 +170,11 @@ size_t acts_bytes(const qi21_geom& g, bool pair, int cap, size_t* parts) {
 }
 
 void free_acts(qi21_model* m) {
-  size_t parts[10];
-  acts_bytes(m->g, m->o.ffn_pair != 0, m->acts.cap, parts);
-  void* ptrs[10] = {m->acts.x, m->acts.xn, m->acts.panel, m->acts.vt, m->acts.att, m->acts.part,
-                    m->acts.hid, m->acts.mods, m->acts.out, m->acts.rcs};
-  for (int i = 0; i < 10; ++i) dfree(m, ptrs[i], parts[i]);
+  size_t parts[NACT];
+  acts_bytes(m->g, m->o.ffn_mode, m->acts.cap, parts);
+  void* ptrs[NACT] = {m->acts.x,   m->acts.xn,   m->acts.panel, m->acts.vt,  m->acts.att, m->acts.part,
+                      m->acts.hid, m->acts.mods, m->acts.out,   m->acts.rcs, m->acts.xsc, m->acts.hsc};
+  for (int i = 0; i < NACT; ++i) dfree(m, ptrs[i], parts[i]);
   m->acts = Acts{};
 }
 
@@ -174,10 +184,10 @@ int ensure_acts(qi21_model* m, int rows, hipStream_t s) {
   if (m->acts.cap >= rows) return QI21_OK;
   free_acts(m);
   const int cap = (int)round_up((size_t)rows, 256);
-  size_t parts[10];
-  acts_bytes(m->g, m->o.ffn_pair != 0, cap, parts);
-  void* p[10];
-  for (int i = 0; i < 10; ++i) {
+  size_t parts[NACT];
+  acts_bytes(m->g, m->o.ffn_mode, cap, parts);
+  void* p[NACT];
+  for (int i = 0; i < NACT; ++i) {
     if (!parts[i]) {
       p[i] = nullptr;
       continue;
@@ -186,7 +196,7 @@ int ensure_acts(qi21_model* m, int rows, hipStream_t s) {
     if (!p[i]) {
       for (int j = 0; j < i; ++j) dfree(m, p[j], parts[j]);
       return fail(QI21_ENOMEM, "activations for %d rows (%.1f MB) did not fit", rows,
-                  acts_bytes(m->g, m->o.ffn_pair != 0, cap, nullptr) / 1e6);
+                  acts_bytes(m->g, m->o.ffn_mode, cap, nullptr) / 1e6);
     }
     HIP_OK(qi21::launch_fill32(p[i], 0u, parts[i] / 4, s));
   }
@@ -202,6 +212,8 @@ int ensure_acts(qi21_model* m, int rows, hipStream_t s) {
   a.mods = (float*)p[7];
   a.out = (float*)p[8];
   a.rcs = (float*)p[9];
+  a.xsc = (uint8_t*)p[10];
+  a.hsc = (uint8_t*)p[11];
   return QI21_OK;
 }
 
@@ -446,9 +458,22 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
       }
       HIP_OK(qi21::launch_flash(fa.data(), (int)fa.size(), s));
     }
-    // with ffn_pair the FFN input and the hidden are f16 (hi, lo) pairs in
-    // rows of 2H / 2I and both GEMMs run over K doubled, each W row twice
-    const int pf = m->o.ffn_pair ? 2 : 1;
+    // The FFN input (in xn) and the hidden: single f16; f16 (hi, lo) pairs
+    // in rows of 2H / 2I, both FFN GEMMs then running over K doubled with
+    // each W row read twice; or lo8 (f16 plus scaled fp8 residuals, rows
+    // of 3H / 3I bytes, with the weight planes in the same form).
+    const int fm = m->o.ffn_mode;
+    const bool lo8 = fm == QI21_FFN_LO8;
+    const int pf = fm == QI21_FFN_PAIR ? 2 : 1;
+    const int ffn_bits = fm == QI21_FFN_PAIR ? 4 : lo8 ? 8 : 0;  // the FFN-input row pass's mode bits
+    const int kx = lo8 ? 3 * H / 2 : pf * H;                    // the FFN input's row, in halves
+    const int kh = lo8 ? 3 * I / 2 : pf * I;                    // the hidden's row, in halves
+    auto ffn_lo8 = [&](qi21::GemmArgs& ga, const uint8_t* asc, int lds, const uint8_t* wsc) {
+      ga.kt8 = 2;
+      ga.asc = asc;
+      ga.lds = lds;
+      ga.wsc = wsc;
+    };
     // the O GEMM split over K like the down GEMM below, or with the gated
     // residual in its epilogue
     const int spo = tile < 0 ? qi21::gemm_split_count(rows, H, H, 4) : 1;
@@ -461,8 +486,8 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
         HIP_OK(qi21::launch_gemm(qi21::EPI_F32, o, 0, s));
       }
       Scope sc(m, C_ROW, s);  // x += tanh(g1) sum_p part_p; xn = LN(x)(1 + s2)
-      HIP_OK(qi21::launch_rowop(rows, H, pf == 2 ? 7 : 3, a.x, a.part, a.xn, a.mods, H, 2 * H, g.eps, p2(-gd.ffn), s,
-                                spo, (size_t)rows * H));
+      HIP_OK(qi21::launch_rowop(rows, H, 3 | ffn_bits, a.x, a.part, a.xn, a.mods, H, 2 * H, g.eps, p2(-gd.ffn), s,
+                                spo, (size_t)rows * H, a.xsc));
     } else {
       {  // x += tanh(g1) (att Wo^T) in the O GEMM's epilogue
         Scope sc(m, C_O, s);
@@ -472,28 +497,38 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
       }
       {  // xn = LN(x)(1 + s2)
         Scope sc(m, C_ROW, s);
-        HIP_OK(qi21::launch_rowop(rows, H, pf == 2 ? 6 : 2, a.x, nullptr, a.xn, a.mods, 0, 2 * H, g.eps, p2(-gd.ffn),
-                                  s));
+        HIP_OK(qi21::launch_rowop(rows, H, 2 | ffn_bits, a.x, nullptr, a.xn, a.mods, 0, 2 * H, g.eps, p2(-gd.ffn), s,
+                                  1, 0, a.xsc));
       }
     }
     {
       Scope sc(m, C_W13, s);
-      qi21::GemmArgs ga = gemm_args(rows, 2 * I, pf * H, a.xn, pf * H, m->w13[l], a.hid, pf * I, p2(-gd.hid),
-                                    p2(gd.ffn));
-      ga.kw = H;
-      HIP_OK(qi21::launch_gemm(pf == 2 ? qi21::EPI_SWIGLU2 : qi21::EPI_SWIGLU, ga, tile, s));
+      qi21::GemmArgs ga = gemm_args(rows, 2 * I, kx, a.xn, kx, m->w13[l], a.hid, kh, p2(-gd.hid), p2(gd.ffn));
+      if (lo8) {
+        ffn_lo8(ga, a.xsc, H / 64, m->w13s[l]);
+        ga.osc = a.hsc;
+        ga.ldos = I / 64;
+        HIP_OK(qi21::launch_gemm(qi21::EPI_SWIGLU8, ga, 0, s));
+      } else {
+        ga.kw = H;
+        HIP_OK(qi21::launch_gemm(pf == 2 ? qi21::EPI_SWIGLU2 : qi21::EPI_SWIGLU, ga, tile, s));
+      }
     }
     // Where whole 256 x 256 tiles would leave most CUs idle (512 to 2047
     // rows), the down GEMM runs split over K into partial products and the
     // row pass adds them: x += tanh(g2) sum_p part_p, then (but in the
     // last block) the next block's xn = LN(x)(1 + s1).  Otherwise the
-    // gated residual runs in the GEMM's epilogue.
-    const int sp = tile < 0 ? qi21::gemm_split_count(rows, H, pf * I, 4) : 1;
+    // gated residual runs in the GEMM's epilogue.  (lo8: the split falls
+    // on whole groups of 128 columns, so the count must divide I / 128.)
+    const int sp = tile < 0 ? qi21::gemm_split_count(rows, H, lo8 ? I / 2 : pf * I, 4) : 1;
     if (sp > 1 && (size_t)sp * rows <= 4 * std::min<size_t>(a.cap, 2048)) {
       {
         Scope sc(m, C_W2, s);
-        qi21::GemmArgs ga = gemm_args(rows, H, pf * I, a.hid, pf * I, m->w2[l], a.part, H, p2(gd.hid));
-        ga.kw = I;
+        qi21::GemmArgs ga = gemm_args(rows, H, kh, a.hid, kh, m->w2[l], a.part, H, p2(gd.hid));
+        if (lo8)
+          ffn_lo8(ga, a.hsc, I / 64, m->w2s[l]);
+        else
+          ga.kw = I;
         ga.ksplit = sp;
         ga.pstride = (size_t)rows * H;
         HIP_OK(qi21::launch_gemm(qi21::EPI_F32, ga, 0, s));
@@ -504,10 +539,13 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
     } else {
       {  // x += tanh(g2) (hid W2^T) in the down GEMM's epilogue
         Scope sc(m, C_W2, s);
-        qi21::GemmArgs ga = gemm_args(rows, H, pf * I, a.hid, pf * I, m->w2[l], a.x, H, p2(gd.hid));
-        ga.kw = I;
+        qi21::GemmArgs ga = gemm_args(rows, H, kh, a.hid, kh, m->w2[l], a.x, H, p2(gd.hid));
         ga.gate = a.mods + 3 * H;
-        HIP_OK(qi21::launch_gemm(qi21::EPI_RESID, ga, tile, s));
+        if (lo8)
+          ffn_lo8(ga, a.hsc, I / 64, m->w2s[l]);
+        else
+          ga.kw = I;
+        HIP_OK(qi21::launch_gemm(qi21::EPI_RESID, ga, lo8 ? 0 : tile, s));
       }
       if (!last) {  // the next block's xn = LN(x)(1 + s1)
         Scope sc(m, C_ROW, s);
@@ -543,7 +581,7 @@ void qi21_default_options(qi21_options* o) {
   o->max_programs = 2;
   o->profile = 0;
   o->gemm_tile = -1;
-  o->ffn_pair = 0;
+  o->ffn_mode = QI21_FFN_F16;
 }
 
 size_t qi21_model_bytes(const qi21_model* m) { return m ? m->bytes : 0; }
@@ -554,14 +592,16 @@ void qi21_model_destroy(qi21_model* m) {
   for (auto& p : m->progs) free_prog(m, p);
   m->progs.clear();
   free_acts(m);
-  const size_t H = m->g.hidden, I = m->g.inter;
+  const size_t H = m->g.hidden, I = m->g.inter, fb = ffn_row_bytes(m->o.ffn_mode == QI21_FFN_LO8 ? QI21_FFN_LO8 : 0);
   for (int l = 0; l < m->nb; ++l) {
     dfree(m, m->wqkv[l], 3 * H * H * 2);
     dfree(m, m->wo[l], H * H * 2);
-    dfree(m, m->w13[l], 2 * I * H * 2);
-    dfree(m, m->w2[l], H * I * 2);
+    dfree(m, m->w13[l], 2 * I * H * fb);
+    dfree(m, m->w2[l], H * I * fb);
     dfree(m, m->nq[l], 128 * 4);
     dfree(m, m->nk[l], 128 * 4);
+    if (l < (int)m->w13s.size()) dfree(m, m->w13s[l], 2 * I);
+    if (l < (int)m->w2s.size()) dfree(m, m->w2s[l], H);
   }
   dfree(m, m->img_in, H * 64 * 4);
   dfree(m, m->proj_out, H * 64 * 4);
@@ -595,13 +635,20 @@ int qi21_model_create(const qi21_geom* geom, const qi21_options* opt, int nblock
     return fail(QI21_EINVAL, "alloc and free hooks must be given together");
   }
   if (m->o.max_programs < 1) m->o.max_programs = 1;
-  if (m->o.ffn_pair != 0 && m->o.ffn_pair != 1) {
-    const int fp = m->o.ffn_pair;
+  if (m->o.ffn_mode < QI21_FFN_F16 || m->o.ffn_mode > QI21_FFN_LO8) {
+    const int fm = m->o.ffn_mode;
     delete m;
-    return fail(QI21_EINVAL, "ffn_pair %d (0 or 1)", fp);
+    return fail(QI21_EINVAL, "ffn_mode %d (0, 1 or 2)", fm);
+  }
+  if (m->o.ffn_mode == QI21_FFN_LO8 && (geom->hidden % 256 != 0 || geom->inter % 128 != 0)) {
+    delete m;
+    return fail(QI21_EUNSUPPORTED, "ffn_mode lo8 needs hidden %% 256 == 0 and inter %% 128 == 0 (hidden %d, inter %d)",
+                geom->hidden, geom->inter);
   }
   m->nb = nblocks;
   const size_t H = geom->hidden, I = geom->inter;
+  const bool lo8 = m->o.ffn_mode == QI21_FFN_LO8;
+  const size_t fb = ffn_row_bytes(lo8 ? QI21_FFN_LO8 : 0);  // bytes per FFN plane column
   m->wqkv.assign(nblocks, nullptr);
   m->wo.assign(nblocks, nullptr);
   m->w13.assign(nblocks, nullptr);
@@ -609,18 +656,23 @@ int qi21_model_create(const qi21_geom* geom, const qi21_options* opt, int nblock
   m->nq.assign(nblocks, nullptr);
   m->nk.assign(nblocks, nullptr);
   m->set.assign(nblocks, 0);
+  if (lo8) {
+    m->w13s.assign(nblocks, nullptr);
+    m->w2s.assign(nblocks, nullptr);
+  }
   bool ok = true;
   for (int l = 0; l < nblocks && ok; ++l) {
     ok = (m->wqkv[l] = (f16*)dalloc(m, 3 * H * H * 2)) && (m->wo[l] = (f16*)dalloc(m, H * H * 2)) &&
-         (m->w13[l] = (f16*)dalloc(m, 2 * I * H * 2)) && (m->w2[l] = (f16*)dalloc(m, H * I * 2)) &&
+         (m->w13[l] = (f16*)dalloc(m, 2 * I * H * fb)) && (m->w2[l] = (f16*)dalloc(m, H * I * fb)) &&
          (m->nq[l] = (float*)dalloc(m, 128 * 4)) && (m->nk[l] = (float*)dalloc(m, 128 * 4));
+    if (ok && lo8) ok = (m->w13s[l] = (uint8_t*)dalloc(m, 2 * I)) && (m->w2s[l] = (uint8_t*)dalloc(m, H));
   }
   ok = ok && (m->img_in = (float*)dalloc(m, H * 64 * 4)) && (m->proj_out = (float*)dalloc(m, H * 64 * 4)) &&
        (m->dflag = (int*)dalloc(m, 256));
   if (!ok) {
     qi21_model_destroy(m);
     return fail(QI21_ENOMEM, "weight planes for %d blocks (%.2f GB) did not fit", nblocks,
-                (double)nblocks * (4 * H * H + 3 * H * I) * 2 / 1e9);
+                (double)nblocks * (8 * H * H + 3 * H * I * fb) / 1e9);
   }
   if (hipHostMalloc((void**)&m->hflag, sizeof(int), hipHostMallocDefault) != hipSuccess) {
     m->hflag = nullptr;
@@ -652,10 +704,18 @@ int qi21_model_set_block(qi21_model* m, int layer, int w_dtype, const void* cons
   // qkv plane rows: q [0, H), k [H, 2H), v [2H, 3H)
   for (int i = 0; i < 3; ++i) HIP_OK(qi21::launch_plane(w_dtype, w[i], H, H, m->wqkv[layer], H, 0, i * H, s));
   HIP_OK(qi21::launch_plane(w_dtype, w[3], H, H, m->wo[layer], H, 0, 0, s));
-  // gate/up interleaved by 32 rows: plane rows 64j + r = gate 32j + r, 64j + 32 + r = up 32j + r
-  HIP_OK(qi21::launch_plane(w_dtype, w[4], I, H, m->w13[layer], 32, 64, 0, s));
-  HIP_OK(qi21::launch_plane(w_dtype, w[5], I, H, m->w13[layer], 32, 64, 32, s));
-  HIP_OK(qi21::launch_plane(w_dtype, w[6], H, I, m->w2[layer], H, 0, 0, s));
+  // gate/up interleaved by 32 rows: plane rows 64j + r = gate 32j + r, 64j + 32 + r = up 32j + r;
+  // lo8: both FFN planes in the lo8 row form, their fp8 residual bytes and
+  // per-row scales derived from the f16 values
+  const bool lo8 = m->o.ffn_mode == QI21_FFN_LO8;
+  const int ld13 = lo8 ? 3 * H / 2 : H, ld2 = lo8 ? 3 * I / 2 : I;
+  HIP_OK(qi21::launch_plane(w_dtype, w[4], I, H, m->w13[layer], 32, 64, 0, s, ld13, lo8));
+  HIP_OK(qi21::launch_plane(w_dtype, w[5], I, H, m->w13[layer], 32, 64, 32, s, ld13, lo8));
+  HIP_OK(qi21::launch_plane(w_dtype, w[6], H, I, m->w2[layer], H, 0, 0, s, ld2, lo8));
+  if (lo8) {
+    HIP_OK(qi21::launch_plane8(2 * I, H, m->w13[layer], ld13, m->w13s[layer], s));
+    HIP_OK(qi21::launch_plane8(H, I, m->w2[layer], ld2, m->w2s[layer], s));
+  }
   // the q norm weights carry the softmax's log2(e) / sqrt(128), so every q
   // the block produces is in the base-2 units the attention kernels take
   HIP_OK(qi21::launch_scale(128, norm_q, (float)(1.4426950408889634 / 11.313708498984761), m->nq[layer], s));
@@ -755,7 +815,11 @@ int qi21_step_batch(qi21_model* m, int nprog, const uint64_t* keys, const float*
     return fail(QI21_EINVAL, "step arguments include NULL or nprog %d", nprog);
   // each program's rows start at a multiple of 64 of the shared
   // activations, so its V^T columns stay 16-byte aligned for the attention
-  // kernel; the few gap rows between programs carry finite values nobody reads
+  // kernel.  The gap rows between programs are zeroed in x and in the
+  // attention output each call, so they stay exactly zero through every
+  // block; the attention kernel reads their V^T columns (with P = 0) as the
+  // padding of the program before, so they must be finite even after a
+  // refused non-finite step left anything behind in the activations.
   std::vector<Prog*> ps(nprog);
   std::vector<int> start(nprog);
   int rows = 0;
@@ -782,6 +846,11 @@ int qi21_step_batch(qi21_model* m, int nprog, const uint64_t* keys, const float*
     for (int i = 0; i < nprog; ++i) {
       segs.push_back(Seg{start[i], ps[i]->n, ps[i], ps[i]->rc, ps[i]->rs, ps[i]->rcs});
       HIP_OK(qi21::launch_embed(ps[i]->n, H, xtok[i], m->img_in, a.x + (size_t)start[i] * H, s));
+      if (i > 0) {
+        const size_t g0 = (size_t)start[i - 1] + ps[i - 1]->n, gn = (size_t)start[i] - g0;
+        HIP_OK(qi21::launch_fill32(a.x + g0 * H, 0u, gn * H, s));
+        HIP_OK(qi21::launch_fill32(a.att + g0 * H, 0u, gn * H / 2, s));
+      }
     }
   }
   {
@@ -1113,28 +1182,98 @@ int qi21_op_flash(int nq, int heads, const void* q, int ldq, const void* k1, int
   return QI21_OK;
 }
 
-int qi21_op_rowop(int rows, int h, int mode, float* x, const float* y, void* xn, const float* mods, int g_off,
-                  int s_off, float eps, float oscale, void* stream) {
-  g_err.clear();
-  if (rows < 1 || h < 4 || h % 4 || h > 8192 || mode < 1 || mode > 7 || mode == 4 || mode == 5 || g_off % 4 || s_off % 4 || g_off < 0 ||
-      s_off < 0)
+namespace {
+// shared checks of the row-op entry points; lo8: the FFN-input form
+int op_rowop(int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride, void* xn, int ldxn,
+             uint8_t* xsc, const float* mods, int g_off, int s_off, float eps, float oscale, void* stream, bool lo8) {
+  if (nparts < 1 || nparts > 8 || (nparts > 1 && pstride < (size_t)rows * h))
+    return fail(QI21_EINVAL, "rowop nparts %d pstride %zu", nparts, pstride);
+  const bool mode_ok = lo8 ? (mode == 2 || mode == 3) : (mode >= 1 && mode <= 7 && mode != 4 && mode != 5);
+  if (rows < 1 || h < 4 || h % 4 || h > 8192 || !mode_ok || g_off % 4 || s_off % 4 || g_off < 0 || s_off < 0)
     return fail(QI21_EINVAL, "rowop rows %d h %d mode %d", rows, h, mode);
-  if (!x || !mods || ((mode & 1) && !y) || ((mode & 2) && !xn)) return fail(QI21_EINVAL, "rowop pointer NULL");
-  HIP_OK(qi21::launch_rowop(rows, h, mode, x, y, (f16*)xn, mods, g_off, s_off, eps, oscale, (hipStream_t)stream));
+  if (!x || !mods || ((mode & 1) && !y) || ((mode & 2) && !xn) || (lo8 && !xsc))
+    return fail(QI21_EINVAL, "rowop pointer NULL");
+  if (lo8 && h % 128) return fail(QI21_EINVAL, "rowop lo8 h %d (a multiple of 128)", h);
+  // the row stride xn needs: h, 2h for the pair form, 1.5h for lo8 (in halves)
+  const long need = lo8 ? 3L * h / 2 : (mode & 4) ? 2L * h : h;
+  if ((mode & 2) && (ldxn < need || ldxn % 4))
+    return fail(QI21_EINVAL, "rowop ldxn %d (at least %ld halves for mode %d, a multiple of 4)", ldxn, need, mode);
+  HIP_OK(qi21::launch_rowop(rows, h, lo8 ? mode | 8 : mode, x, y, (f16*)xn, mods, g_off, s_off, eps, oscale,
+                            (hipStream_t)stream, nparts, pstride, xsc, (mode & 2) ? ldxn : h));
   return QI21_OK;
+}
+}  // namespace
+
+int qi21_op_rowop(int rows, int h, int mode, float* x, const float* y, void* xn, int ldxn, const float* mods,
+                  int g_off, int s_off, float eps, float oscale, void* stream) {
+  g_err.clear();
+  return op_rowop(rows, h, mode, x, y, 1, 0, xn, ldxn, nullptr, mods, g_off, s_off, eps, oscale, stream, false);
 }
 
 int qi21_op_rowop_parts(int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride, void* xn,
-                        const float* mods, int g_off, int s_off, float eps, float oscale, void* stream) {
+                        int ldxn, const float* mods, int g_off, int s_off, float eps, float oscale, void* stream) {
   g_err.clear();
-  if (nparts < 1 || nparts > 8 || (nparts > 1 && pstride < (size_t)rows * h))
-    return fail(QI21_EINVAL, "rowop nparts %d pstride %zu", nparts, pstride);
-  if (rows < 1 || h < 4 || h % 4 || h > 8192 || mode < 1 || mode > 7 || mode == 4 || mode == 5 || g_off % 4 || s_off % 4 || g_off < 0 ||
-      s_off < 0)
-    return fail(QI21_EINVAL, "rowop rows %d h %d mode %d", rows, h, mode);
-  if (!x || !mods || ((mode & 1) && !y) || ((mode & 2) && !xn)) return fail(QI21_EINVAL, "rowop pointer NULL");
-  HIP_OK(qi21::launch_rowop(rows, h, mode, x, y, (f16*)xn, mods, g_off, s_off, eps, oscale, (hipStream_t)stream,
-                            nparts, pstride));
+  return op_rowop(rows, h, mode, x, y, nparts, pstride, xn, ldxn, nullptr, mods, g_off, s_off, eps, oscale, stream,
+                  false);
+}
+
+int qi21_op_rowop_lo8(int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride, void* xn,
+                      int ldxn, uint8_t* xsc, const float* mods, int g_off, int s_off, float eps, float oscale,
+                      void* stream) {
+  g_err.clear();
+  return op_rowop(rows, h, mode, x, y, nparts, pstride, xn, ldxn, xsc, mods, g_off, s_off, eps, oscale, stream, true);
+}
+
+int qi21_op_gemm_lo8(int epi, int M, int N, int K, const void* A, int lda, const uint8_t* asc, int lds, const void* W,
+                     int ldw, const uint8_t* wsc, void* out, int ldo, const float* gate, uint8_t* osc, int ldos,
+                     int ksplit, float oscale, float inscale, void* stream) {
+  g_err.clear();
+  if (epi != QI21_EPI_F32 && epi != QI21_EPI_RESID && epi != QI21_EPI_SWIGLU8)
+    return fail(QI21_EINVAL, "lo8 gemm epilogue %d (F32, RESID or SWIGLU8)", epi);
+  if (M < 1 || N < 256 || N % 256 || K < 128 || K % 128 || lda % 8 || ldw % 8 || lda < 3 * K / 2 || ldw < 3 * K / 2 ||
+      lds < K / 64 || lds % 2)
+    return fail(QI21_EINVAL,
+                "lo8 gemm M %d N %d K %d lda %d ldw %d lds %d (need N %% 256, K %% 128, lda and ldw >= 1.5 K and %% 8, "
+                "lds >= K / 64 and even)",
+                M, N, K, lda, ldw, lds);
+  if (!A || !W || !asc || !wsc || !out) return fail(QI21_EINVAL, "lo8 gemm pointer is NULL");
+  if (ksplit < 1 || ksplit > 8 || (K / 128) % ksplit || (ksplit > 1 && epi != QI21_EPI_F32))
+    return fail(QI21_EINVAL, "lo8 gemm ksplit %d (1..8, dividing K / 128; F32 only)", ksplit);
+  if (epi == QI21_EPI_RESID && (!gate || ldo < N || ldo % 4)) return fail(QI21_EINVAL, "lo8 gemm resid gate / ldo %d", ldo);
+  if (epi == QI21_EPI_F32 && (ldo < N || ldo % 4 || (ksplit > 1 && ldo != N)))
+    return fail(QI21_EINVAL, "lo8 gemm f32 ldo %d (>= N, % 4; = N when split)", ldo);
+  if (epi == QI21_EPI_SWIGLU8 && (!osc || ldo < 3 * N / 4 || ldo % 4 || ldos < N / 128 || (N / 2) % 128))
+    return fail(QI21_EINVAL, "lo8 gemm swiglu8 ldo %d (>= 0.75 N, % 4), osc, ldos %d (>= N / 128)", ldo, ldos);
+  qi21::GemmArgs a = gemm_args(M, N, 3 * K / 2, (const f16*)A, lda, (const f16*)W, out, ldo, oscale, inscale);
+  a.ldw = ldw;
+  a.kt8 = 2;
+  a.asc = asc;
+  a.lds = lds;
+  a.wsc = wsc;
+  a.gate = gate;
+  a.osc = osc;
+  a.ldos = ldos;
+  a.ksplit = ksplit;
+  a.pstride = (size_t)M * N;
+  HIP_OK(qi21::launch_gemm(epi, a, 0, (hipStream_t)stream));
+  return QI21_OK;
+}
+
+int qi21_op_plane_lo8(int src_dtype, const void* src, int rows, int cols, void* dst, int ld, int group, int gstride,
+                      int goff, void* stream) {
+  g_err.clear();
+  if (src_dtype < QI21_F32 || src_dtype > QI21_F16 || rows < 1 || cols < 128 || cols % 128 || ld < 3 * cols / 2 ||
+      ld % 4 || group < 1 || gstride < 0 || goff < 0 || !src || !dst)
+    return fail(QI21_EINVAL, "lo8 plane arguments (cols %% 128, ld >= 1.5 cols and %% 4)");
+  HIP_OK(qi21::launch_plane(src_dtype, src, rows, cols, (f16*)dst, group, gstride, goff, (hipStream_t)stream, ld, true));
+  return QI21_OK;
+}
+
+int qi21_op_plane8(int rows, int cols, void* plane, int ld, uint8_t* sc, void* stream) {
+  g_err.clear();
+  if (rows < 1 || cols < 128 || cols % 128 || ld < 3 * cols / 2 || ld % 4 || !plane || !sc)
+    return fail(QI21_EINVAL, "plane8 rows %d cols %d ld %d", rows, cols, ld);
+  HIP_OK(qi21::launch_plane8(rows, cols, (f16*)plane, ld, sc, (hipStream_t)stream));
   return QI21_OK;
 }
 

@@ -8,6 +8,7 @@
 // 4-byte-per-lane fully coalesced loads; reductions are wave64 shuffles
 // followed by one LDS exchange between the waves of a block.
 #include "qi21_internal.h"
+#include "lo8.h"
 
 namespace qi21 {
 
@@ -34,6 +35,27 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
   return r;
 }
 
+// mode & 8 of the row ops: chunk c (float4 c of the row, 4c .. 4c+3) of
+// the value r written in the lo8 row form (lo8.h) to row bytes xb; the
+// 16 lanes holding one 64-column block (consecutive lanes, whole groups
+// active or not) share its scale, which the first of them stores
+__device__ __forceinline__ void lo8_store(bool act, int c, float4v r, uint8_t* __restrict__ xb,
+                                          uint8_t* __restrict__ scrow) {
+  const half4 hi = half4{(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
+  const float4v lo = r - float4v{(float)hi[0], (float)hi[1], (float)hi[2], (float)hi[3]};  // exact in f32
+  float mx = act ? fmaxf(fmaxf(fabsf(lo[0]), fabsf(lo[1])), fmaxf(fabsf(lo[2]), fabsf(lo[3]))) : 0.0f;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const int ex = lo8_exp(mx);
+  if (act) {
+    const int e0 = 4 * c;
+    *reinterpret_cast<half4*>(xb + 2 * lo8_hi_at(e0)) = hi;
+    const float4v v = lo * __builtin_ldexpf(1.0f, -ex);
+    *reinterpret_cast<unsigned*>(xb + lo8_lo_at(e0)) = pack_e4m3(v[0], v[1], v[2], v[3]);
+    if ((c & 15) == 0) scrow[e0 >> 6] = (uint8_t)(ex + 127);
+  }
+}
+
 // ───────────────────────────── rowop ─────────────────────────────
 // One wave per row, four rows per 256-thread block; lane l owns the float4
 // chunks l, l + 64, ... of the row (h/4 chunks, at most NJ per lane), so
@@ -42,9 +64,9 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // GEMM split over K), added in plane order.
 template <int MODE, int NJ>
 __global__ __launch_bounds__(256) void rowop_kernel(int rows, int h, float* __restrict__ x, const float* __restrict__ y,
-                                                   int nparts, size_t pstride, f16* __restrict__ xn,
+                                                   int nparts, size_t pstride, f16* __restrict__ xn, int ldxn,
                                                    const float* __restrict__ mods, int g_off, int s_off, float eps,
-                                                   float oscale) {
+                                                   float oscale, uint8_t* __restrict__ xsc) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -79,7 +101,19 @@ __global__ __launch_bounds__(256) void rowop_kernel(int rows, int h, float* __re
       q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
     }
   const float inv = rsqrtf(wave_sum(q) / (float)h + eps);
-  half4* xo = reinterpret_cast<half4*>(xn + (size_t)row * ((MODE & 4) ? 2 * h : h));
+  if constexpr ((MODE & 8) != 0) {
+    uint8_t* xb = reinterpret_cast<uint8_t*>(xn + (size_t)row * ldxn);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = lane + 64 * j;
+      const bool act = c < nc;
+      float4v r = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+      if (act) r = (v[j] - mean) * inv * (1.0f + reinterpret_cast<const float4v*>(mods + s_off)[c]) * oscale;
+      lo8_store(act, c, r, xb, xsc + (size_t)row * (h >> 6));
+    }
+    return;
+  }
+  half4* xo = reinterpret_cast<half4*>(xn + (size_t)row * ldxn);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int c = lane + 64 * j;
@@ -109,7 +143,7 @@ __global__ __launch_bounds__(256) void rowop_kernel(int rows, int h, float* __re
 // written once.
 template <int NJ>
 __global__ __launch_bounds__(256) void rownorm2_kernel(int rows, int h, const float* __restrict__ x,
-                                                       f16* __restrict__ xn, const float* __restrict__ mods,
+                                                       f16* __restrict__ xn, int ldxn, const float* __restrict__ mods,
                                                        int s_off, float eps, float oscale) {
   __shared__ float red[2][4];
   const int t = threadIdx.x, w = t >> 6;
@@ -163,7 +197,7 @@ __global__ __launch_bounds__(256) void rownorm2_kernel(int rows, int h, const fl
   for (int k = 0; k < 2; ++k) {
     if (k == 1 && !two) break;
     const float inv = rsqrtf((red[k][0] + red[k][1] + red[k][2] + red[k][3]) / (float)h + eps);
-    half4* xo = reinterpret_cast<half4*>(xn + (size_t)(r0 + k) * h);
+    half4* xo = reinterpret_cast<half4*>(xn + (size_t)(r0 + k) * ldxn);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int c = t + 256 * j;
@@ -181,8 +215,9 @@ __global__ __launch_bounds__(256) void rownorm2_kernel(int rows, int h, const fl
 template <int MODE, int NJ, int NP>
 __global__ __launch_bounds__(256) void rowop_wide_kernel(int rows, int h, float* __restrict__ x,
                                                          const float* __restrict__ y, int nparts, size_t pstride,
-                                                         f16* __restrict__ xn, const float* __restrict__ mods,
-                                                         int g_off, int s_off, float eps, float oscale) {
+                                                         f16* __restrict__ xn, int ldxn, const float* __restrict__ mods,
+                                                         int g_off, int s_off, float eps, float oscale,
+                                                         uint8_t* __restrict__ xsc) {
   __shared__ float red[4];
   const int t = threadIdx.x;
   const int row = blockIdx.x;
@@ -254,7 +289,19 @@ __global__ __launch_bounds__(256) void rowop_wide_kernel(int rows, int h, float*
       q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
     }
   const float inv = rsqrtf(block_sum256(q, red) / (float)h + eps);
-  half4* xo = reinterpret_cast<half4*>(xn + (size_t)row * ((MODE & 4) ? 2 * h : h));
+  if constexpr ((MODE & 8) != 0) {
+    uint8_t* xb = reinterpret_cast<uint8_t*>(xn + (size_t)row * ldxn);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = t + 256 * j;
+      const bool act = c < nc;
+      float4v r = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+      if (act) r = (v[j] - mean) * inv * (1.0f + reinterpret_cast<const float4v*>(mods + s_off)[c]) * oscale;
+      lo8_store(act, c, r, xb, xsc + (size_t)row * (h >> 6));
+    }
+    return;
+  }
+  half4* xo = reinterpret_cast<half4*>(xn + (size_t)row * ldxn);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int c = t + 256 * j;
@@ -272,16 +319,20 @@ __global__ __launch_bounds__(256) void rowop_wide_kernel(int rows, int h, float*
 }
 
 namespace {
+#define QI21_ROWOP_ARGS rows, h, x, y, np, ps, xn, ldxn, mods, g_off, s_off, eps, oscale, xsc
 template <int NJ, int NP>
 hipError_t launch_rowop_wide_np(int rows, int h, int mode, float* x, const float* y, int np, size_t ps, f16* xn,
-                                const float* mods, int g_off, int s_off, float eps, float oscale, hipStream_t s) {
+                                int ldxn, const float* mods, int g_off, int s_off, float eps, float oscale, uint8_t* xsc,
+                                hipStream_t s) {
   const dim3 grid(rows), block(256);
   switch (mode) {
-    case 1: hipLaunchKernelGGL((rowop_wide_kernel<1, NJ, NP>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
-    case 2: hipLaunchKernelGGL((rowop_wide_kernel<2, NJ, NP>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
-    case 3: hipLaunchKernelGGL((rowop_wide_kernel<3, NJ, NP>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
-    case 6: hipLaunchKernelGGL((rowop_wide_kernel<6, NJ, NP>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
-    case 7: hipLaunchKernelGGL((rowop_wide_kernel<7, NJ, NP>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
+    case 1: hipLaunchKernelGGL((rowop_wide_kernel<1, NJ, NP>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 2: hipLaunchKernelGGL((rowop_wide_kernel<2, NJ, NP>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 3: hipLaunchKernelGGL((rowop_wide_kernel<3, NJ, NP>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 6: hipLaunchKernelGGL((rowop_wide_kernel<6, NJ, NP>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 7: hipLaunchKernelGGL((rowop_wide_kernel<7, NJ, NP>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 10: hipLaunchKernelGGL((rowop_wide_kernel<10, NJ, NP>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 11: hipLaunchKernelGGL((rowop_wide_kernel<11, NJ, NP>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -289,58 +340,67 @@ hipError_t launch_rowop_wide_np(int rows, int h, int mode, float* x, const float
 
 template <int NJ>
 hipError_t launch_rowop_wide(int rows, int h, int mode, float* x, const float* y, int np, size_t ps, f16* xn,
-                             const float* mods, int g_off, int s_off, float eps, float oscale, hipStream_t s) {
+                             int ldxn, const float* mods, int g_off, int s_off, float eps, float oscale, uint8_t* xsc,
+                             hipStream_t s) {
   // three or four planes with every plane's loads issued up front (1024
   // rows x 4096: 22.1 against 23.6 us with four planes, 16.5 against 21.1
   // with three); one or two planes with the plane loop, which measured
   // faster there (2048 rows, two planes: 31.0 against 36.7 us)
-  if ((mode & 1) && np == 3)
-    return launch_rowop_wide_np<NJ, 3>(rows, h, mode, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale, s);
-  if ((mode & 1) && np == 4)
-    return launch_rowop_wide_np<NJ, 4>(rows, h, mode, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale, s);
-  return launch_rowop_wide_np<NJ, 0>(rows, h, mode, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale, s);
+#define QI21_WIDE_ARGS rows, h, mode, x, y, np, ps, xn, ldxn, mods, g_off, s_off, eps, oscale, xsc, s
+  if ((mode & 1) && np == 3) return launch_rowop_wide_np<NJ, 3>(QI21_WIDE_ARGS);
+  if ((mode & 1) && np == 4) return launch_rowop_wide_np<NJ, 4>(QI21_WIDE_ARGS);
+  return launch_rowop_wide_np<NJ, 0>(QI21_WIDE_ARGS);
+#undef QI21_WIDE_ARGS
 }
 }  // namespace
 
 namespace {
 template <int NJ>
 hipError_t launch_rowop_nj(int rows, int h, int mode, float* x, const float* y, int np, size_t ps, f16* xn,
-                           const float* mods, int g_off, int s_off, float eps, float oscale, hipStream_t s) {
+                           int ldxn, const float* mods, int g_off, int s_off, float eps, float oscale, uint8_t* xsc,
+                           hipStream_t s) {
   const dim3 grid((rows + 3) / 4), block(256);
   switch (mode) {
-    case 1: hipLaunchKernelGGL((rowop_kernel<1, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
-    case 2: hipLaunchKernelGGL((rowop_kernel<2, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
-    case 3: hipLaunchKernelGGL((rowop_kernel<3, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
-    case 6: hipLaunchKernelGGL((rowop_kernel<6, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
-    case 7: hipLaunchKernelGGL((rowop_kernel<7, NJ>), grid, block, 0, s, rows, h, x, y, np, ps, xn, mods, g_off, s_off, eps, oscale); break;
+    case 1: hipLaunchKernelGGL((rowop_kernel<1, NJ>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 2: hipLaunchKernelGGL((rowop_kernel<2, NJ>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 3: hipLaunchKernelGGL((rowop_kernel<3, NJ>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 6: hipLaunchKernelGGL((rowop_kernel<6, NJ>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 7: hipLaunchKernelGGL((rowop_kernel<7, NJ>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 10: hipLaunchKernelGGL((rowop_kernel<10, NJ>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 11: hipLaunchKernelGGL((rowop_kernel<11, NJ>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
+#undef QI21_ROWOP_ARGS
 }  // namespace
 
 hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16* xn, const float* mods,
-                        int g_off, int s_off, float eps, float oscale, hipStream_t s, int nparts, size_t pstride) {
+                        int g_off, int s_off, float eps, float oscale, hipStream_t s, int nparts, size_t pstride,
+                        uint8_t* xsc, int ldxn) {
   if (rows <= 0) return hipSuccess;
-  if (h <= 1024) return launch_rowop_nj<4>(rows, h, mode, x, y, nparts, pstride, xn, mods, g_off, s_off, eps, oscale, s);
+  if ((mode & 8) && (!xsc || h % 128 != 0 || (mode & 4) || !(mode & 2))) return hipErrorInvalidValue;
+  if (!ldxn) ldxn = (mode & 4) ? 2 * h : (mode & 8) ? 3 * h / 2 : h;
+#define QI21_LAUNCH_ARGS rows, h, mode, x, y, nparts, pstride, xn, ldxn, mods, g_off, s_off, eps, oscale, xsc, s
+  if (h <= 1024) return launch_rowop_nj<4>(QI21_LAUNCH_ARGS);
   // the block-per-row form for wide rows, except on long passes that also
   // add a residual: there the one-wave-per-row form streamed faster
   // (4096 rows x 4096: 41 against 47 us; without the residual 19 against
   // 23 us for the block form, and 24 against 27 us on 1024 rows with four
   // planes)
-  if (h < 2048 || (h <= 4096 && (mode & 1) && rows > 2048))
-    return launch_rowop_nj<16>(rows, h, mode, x, y, nparts, pstride, xn, mods, g_off, s_off, eps, oscale, s);
+  if (h < 2048 || (h <= 4096 && (mode & 1) && rows > 2048)) return launch_rowop_nj<16>(QI21_LAUNCH_ARGS);
   if (h <= 4096) {
     // the LayerNorm passes of long steps: two rows per block (4096 rows: 17.0
     // against 19.5 us; even at 16384 rows, 0.3 us slower at 1024)
     if (mode == 2 && rows > 2048) {
-      hipLaunchKernelGGL(rownorm2_kernel<4>, dim3((rows + 1) / 2), dim3(256), 0, s, rows, h, x, xn, mods, s_off, eps,
-                         oscale);
+      hipLaunchKernelGGL(rownorm2_kernel<4>, dim3((rows + 1) / 2), dim3(256), 0, s, rows, h, x, xn, ldxn, mods, s_off,
+                         eps, oscale);
       return hipGetLastError();
     }
-    return launch_rowop_wide<4>(rows, h, mode, x, y, nparts, pstride, xn, mods, g_off, s_off, eps, oscale, s);
+    return launch_rowop_wide<4>(QI21_LAUNCH_ARGS);
   }
-  return launch_rowop_wide<8>(rows, h, mode, x, y, nparts, pstride, xn, mods, g_off, s_off, eps, oscale, s);
+  return launch_rowop_wide<8>(QI21_LAUNCH_ARGS);
+#undef QI21_LAUNCH_ARGS
 }
 
 // ───────────────────────────── RoPE table packing ─────────────────────────────
@@ -645,7 +705,7 @@ hipError_t launch_mods(int h, const float* mods, float* mods_dev, hipStream_t s)
 }
 
 __global__ void plane_kernel(int src_dtype, const void* __restrict__ src, int rows, int cols, f16* __restrict__ dst,
-                             int group, int gstride, int goff) {
+                             int group, int gstride, int goff, int ldd, int lo8) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (size_t)rows * cols) return;
   const int r = (int)(i / cols), c = (int)(i - (size_t)r * cols);
@@ -659,14 +719,51 @@ __global__ void plane_kernel(int src_dtype, const void* __restrict__ src, int ro
     v = (float)reinterpret_cast<const f16*>(src)[i];
   }
   const int dr = (r / group) * gstride + goff + r % group;
-  dst[(size_t)dr * cols + c] = (f16)v;
+  dst[(size_t)dr * ldd + (lo8 ? lo8_hi_at(c) : c)] = (f16)v;
 }
 
 hipError_t launch_plane(int src_dtype, const void* src, int rows, int cols, f16* dst, int group, int gstride,
-                        int goff, hipStream_t s) {
+                        int goff, hipStream_t s, int ldd, bool lo8) {
   const size_t n = (size_t)rows * cols;
+  if (lo8 && cols % 128 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(plane_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src_dtype, src, rows, cols,
-                     dst, group, gstride, goff);
+                     dst, group, gstride, goff, ldd ? ldd : cols, lo8 ? 1 : 0);
+  return hipGetLastError();
+}
+
+// One 256-thread block per row of a lo8 weight plane: the row's largest
+// |w| over its f16 values (a block max), then every residual byte =
+// e4m3(w 2^-e) and the row's E8M0 scale.
+__global__ __launch_bounds__(256) void plane8_kernel(int cols, f16* __restrict__ plane, int ld,
+                                                     uint8_t* __restrict__ sc) {
+  __shared__ float red[4];
+  const int row = blockIdx.x, t = threadIdx.x;
+  f16* pr = plane + (size_t)row * ld;
+  uint8_t* pb = reinterpret_cast<uint8_t*>(pr);
+  float mx = 0.0f;
+  for (int c = 4 * t; c < cols; c += 1024) {
+    const half4 w = *reinterpret_cast<const half4*>(pr + lo8_hi_at(c));
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf((float)w[0]), fabsf((float)w[1])), fmaxf(fabsf((float)w[2]), fabsf((float)w[3]))));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((t & 63) == 0) red[t >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int ex = lo8_exp(mx);
+  const float inv = __builtin_ldexpf(1.0f, -ex);
+  for (int c = 4 * t; c < cols; c += 1024) {
+    const half4 w = *reinterpret_cast<const half4*>(pr + lo8_hi_at(c));
+    *reinterpret_cast<unsigned*>(pb + lo8_lo_at(c)) =
+        pack_e4m3((float)w[0] * inv, (float)w[1] * inv, (float)w[2] * inv, (float)w[3] * inv);
+  }
+  if (t == 0) sc[row] = (uint8_t)(ex + 127);
+}
+
+hipError_t launch_plane8(int rows, int cols, f16* plane, int ld, uint8_t* sc, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (cols % 128 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(plane8_kernel, dim3(rows), dim3(256), 0, s, cols, plane, ld, sc);
   return hipGetLastError();
 }
 

@@ -68,18 +68,28 @@ typedef void (*qi21_free_fn)(void* ptr, void* ctx);
  * positive and a negative prompt); a new key evicts the oldest.  profile:
  * bit mask of kernel classes (see qi21_profile_read) whose launches are
  * bracketed by HIP events on the launch stream; 0 = off.
- * ffn_pair (not on the pages, whose FFN sites are single f16): 1 keeps the
- * FFN input and the SwiGLU hidden as f16 (hi, lo) pairs, hi = f16(v), lo =
- * f16(v - hi), so their storage error falls from about 2^-12 to about 2^-23
- * of the value (less where lo is subnormal); the gate/up and down GEMMs
- * then run over twice their K, using each weight row for both halves, which
- * is 1.75x the step's GEMM work.  0 (default) = single f16. */
+ * ffn_mode (not on the pages, whose FFN sites are single f16) sets how the
+ * FFN input and the SwiGLU hidden are stored:
+ *   QI21_FFN_F16 (0, default): single f16, as on the pages; storage error
+ *     about 2^-12 of the value at each of the two sites.
+ *   QI21_FFN_PAIR (1): f16 (hi, lo) pairs, hi = f16(v), lo = f16(v - hi);
+ *     storage error about 2^-23; the gate/up and down GEMMs run over twice
+ *     their K, each weight row read for both halves (1.75x the step's
+ *     GEMM work).
+ *   QI21_FFN_LO8 (2): hi = f16(v) plus the residual v - hi in fp8 (OCP
+ *     e4m3) scaled by a power of two per 64 columns; the two FFN weight
+ *     planes carry an fp8 copy of each row (scaled per row) next to the
+ *     f16 one, and the residual products run on gfx950's scaled fp8 MFMA
+ *     (1.35x the step's GEMM work in MFMA cycles).  Storage error about
+ *     2^-16 of the value.  Needs hidden % 256 == 0 and inter % 128 == 0
+ *     (EUNSUPPORTED otherwise). */
+enum { QI21_FFN_F16 = 0, QI21_FFN_PAIR = 1, QI21_FFN_LO8 = 2 };
 typedef struct {
   int32_t shift_attn, shift_qkv, shift_ao, shift_ffn, shift_hid;
   int32_t max_programs;
   int32_t profile;
   int32_t gemm_tile; /* -1 = per-shape choice; otherwise a fixed GEMM tile id */
-  int32_t ffn_pair;
+  int32_t ffn_mode;  /* QI21_FFN_F16 / QI21_FFN_PAIR / QI21_FFN_LO8, see above */
   qi21_alloc_fn alloc;
   qi21_free_fn free;
   void* alloc_ctx;

@@ -19,7 +19,8 @@
 extern "C" {
 #endif
 
-enum { QI21_EPI_F16 = 0, QI21_EPI_F32 = 1, QI21_EPI_SWIGLU = 2, QI21_EPI_QKV = 3, QI21_EPI_SWIGLU2 = 4 };
+enum { QI21_EPI_F16 = 0, QI21_EPI_F32 = 1, QI21_EPI_SWIGLU = 2, QI21_EPI_QKV = 3, QI21_EPI_SWIGLU2 = 4,
+       QI21_EPI_RESID = 7, QI21_EPI_SWIGLU8 = 9 };
 
 /* out = A W^T ([QI] lin; the four projection sites of [WG] blocks):
  * A f16 [M][lda] (K contiguous), W f16 [N][K].  Epilogues:
@@ -34,7 +35,7 @@ enum { QI21_EPI_F16 = 0, QI21_EPI_F32 = 1, QI21_EPI_SWIGLU = 2, QI21_EPI_QKV = 3
  *           V^T key order the attention kernel reads, see qi21_op_flash)
  *   SWIGLU2: as SWIGLU, each hidden value h stored as the f16 pair
  *           out[r][c] = f16(h), out[r][N/2 + c] = f16(h - f16(h)); ldo >= N
- *           (the hidden of the ffn_pair option, qi21.h)
+ *           (the hidden of the QI21_FFN_PAIR option, qi21.h)
  * Requires M >= 1, N % 128 == 0, K % 64 == 0, lda % 8 == 0, lda >= K,
  * ldo >= output columns, ldo % 4 == 0, 16-byte aligned A, W and out, for
  * QKV (N/3) % 128 == 0, ld2 % 4 == 0, ld2 >= M.
@@ -43,7 +44,7 @@ enum { QI21_EPI_F16 = 0, QI21_EPI_F32 = 1, QI21_EPI_SWIGLU = 2, QI21_EPI_QKV = 3
 int qi21_op_gemm(int epi, int M, int N, int K, const void* A, int lda, const void* W, void* out, int ldo,
                  void* out2, int ld2, float oscale, float inscale, int tile, void* stream);
 
-/* The same product with A given as f16 pairs (the ffn_pair option of
+/* The same product with A given as f16 pairs (the QI21_FFN_PAIR option of
  * qi21.h): A f16 [M][lda], lda >= 2K, holds hi in columns [0, K) and lo in
  * [K, 2K); out = (A_hi + A_lo) W^T, W f16 [N][K], accumulated in f32 over
  * both halves (each W row is read for both).  Epilogues F16, F32, SWIGLU,
@@ -54,7 +55,7 @@ int qi21_op_gemm_pair(int epi, int M, int N, int K, const void* A, int lda, cons
 /* The gated residual of a block branch in the GEMM's epilogue ([QI]
  * gated_add): x f32 [M][ldx] += gate[c] * oscale * sum_k A[m][k] W[c][k % kw]
  * in place, for c < N.  A f16 [M][lda] with K columns read; W f16 [N][kw];
- * K == kw, or K == 2 kw for an A of f16 (hi, lo) pairs (the ffn_pair option
+ * K == kw, or K == 2 kw for an A of f16 (hi, lo) pairs (the QI21_FFN_PAIR option
  * of qi21.h).  gate f32 [N], already tanh-ed.  Requires M >= 1, N % 128 ==
  * 0, kw % 64 == 0, lda % 8 == 0, lda >= K, ldx % 4 == 0, ldx >= N.  tile as
  * qi21_op_gemm. */
@@ -128,20 +129,78 @@ int qi21_op_flash(int nq, int heads, const void* q, int ldq, const void* k1, int
 
 /* Row op ([WG] qi_rowop; [QI] gated_add, norm_mod) over rows of width h:
  * mode bit 0: x += mods[g_off + c] * y  (gate already tanh-ed)
- * mode bit 1: xn f16 = (LN(x) * (1 + mods[s_off + c])) * oscale
- * mode bit 2 (with bit 1): xn is f16 [rows][2h] holding that value v as the
- *   pair xn[r][c] = f16(v), xn[r][h + c] = f16(v - f16(v)) (ffn_pair, qi21.h)
+ * mode bit 1: xn f16 [rows][ldxn] = (LN(x) * (1 + mods[s_off + c])) * oscale
+ * mode bit 2 (with bit 1): that value v as the pair xn[r][c] = f16(v),
+ *   xn[r][h + c] = f16(v - f16(v)) (QI21_FFN_PAIR, qi21.h)
+ * ldxn is xn's row stride in halves: at least h (2h with bit 2) and a
+ * multiple of 4; the row op writes columns [0, h) (with bit 2: [0, 2h)) of
+ * each row and nothing else (ldxn is ignored without bit 1).
  * Requires rows >= 1, mode in {1, 2, 3, 6, 7}, h % 4 == 0, 4 <= h <= 8192,
- * g_off, s_off % 4 == 0. */
-int qi21_op_rowop(int rows, int h, int mode, float* x, const float* y, void* xn, const float* mods, int g_off,
-                  int s_off, float eps, float oscale, void* stream);
+ * g_off, s_off % 4 == 0; EINVAL otherwise, before any launch. */
+int qi21_op_rowop(int rows, int h, int mode, float* x, const float* y, void* xn, int ldxn, const float* mods,
+                  int g_off, int s_off, float eps, float oscale, void* stream);
 
 /* qi21_op_rowop with y the sum of nparts planes [rows][h] pstride floats
  * apart, added in plane order (the partial products of qi21_op_gemm_split).
  * Requires 1 <= nparts <= 8 and, for nparts > 1, pstride >= rows * h;
  * otherwise as qi21_op_rowop. */
 int qi21_op_rowop_parts(int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride, void* xn,
-                        const float* mods, int g_off, int s_off, float eps, float oscale, void* stream);
+                        int ldxn, const float* mods, int g_off, int s_off, float eps, float oscale, void* stream);
+
+/* The lo8 operand form (QI21_FFN_LO8, qi21.h).  Columns are grouped by
+ * 128: group g of a row takes 384 bytes, 128 halves (halves offset 192 g +
+ * c % 128) and then 128 fp8 bytes in OCP e4m3 (byte offset 384 g + 256 +
+ * c % 128).  Scales are E8M0 bytes b, the factor 2^(b - 127), chosen so
+ * that a block's largest |value| / factor lies in [128, 256).
+ *   Activation rows: the halves hold hi = f16(v) and the bytes the
+ *   residual (v - hi) / factor, one scale per row and 64 columns; the row
+ *   represents hi + e4m3 * factor, about 2^-16 of v from v.
+ *   Weight rows: the halves hold the weight w in f16 and the bytes an fp8
+ *   copy w / factor, one scale per row. */
+/* qi21_op_rowop_parts writing xn in the lo8 form: mode 2 or 3 (bits 0 and
+ * 1 as above), h % 128 == 0, xn rows of ldxn halves (ldxn >= 1.5 h, % 4),
+ * and one scale per row and 64 columns in xsc [rows][h / 64] (row stride
+ * h / 64 bytes).  Otherwise as qi21_op_rowop_parts. */
+int qi21_op_rowop_lo8(int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride, void* xn,
+                      int ldxn, uint8_t* xsc, const float* mods, int g_off, int s_off, float eps, float oscale,
+                      void* stream);
+
+/* out = A W^T over operands in the lo8 form ([QI] lin, the FFN sites of
+ * [WG] blocks, with the QI21_FFN_LO8 storage of qi21.h): A holds M
+ * activation rows of lda halves, W N weight rows of ldw halves, each with
+ * K columns in the lo8 form (lda, ldw >= 1.5 K, % 8); asc [M][lds] bytes
+ * are A's scales per row and 64 columns, wsc [N] W's per row.  Computes,
+ * in f32 on f16 and scaled fp8 MFMAs,
+ *   acc[m][n] = sum_k hiA[m][k] w[n][k] + sum_k resA[m][k] w8[n][k]
+ * with resA and w8 the scaled fp8 values (the residual meets the weight's
+ * fp8 copy).  Epilogues:
+ *   F32:     out f32 [M][ldo] = acc * oscale; with ksplit > 1 out is
+ *            [ksplit][M][N] (ldo == N) of partial products over the column
+ *            ranges [p K / ksplit, (p + 1) K / ksplit) (K / 128 % ksplit == 0)
+ *   RESID:   out f32 [M][ldo] += gate[c] * acc * oscale, in place
+ *   SWIGLU8: W the interleaved gate/up plane (see SWIGLU); the hidden h =
+ *            silu(g * inscale) * (u * inscale) * oscale of N/2 columns to
+ *            out as activation rows in the lo8 form (rows of ldo halves,
+ *            ldo >= 0.75 N) with scales osc [M][ldos] (ldos >= N / 128)
+ * Requires M >= 1, N % 256 == 0, K % 128 == 0, lds >= K / 64 and even,
+ * 16-byte aligned A, W, out.  Runs the 256 x 256 4-wave kernel. */
+int qi21_op_gemm_lo8(int epi, int M, int N, int K, const void* A, int lda, const uint8_t* asc, int lds, const void* W,
+                     int ldw, const uint8_t* wsc, void* out, int ldo, const float* gate, uint8_t* osc, int ldos,
+                     int ksplit, float oscale, float inscale, void* stream);
+
+/* The f16 part of a lo8 weight plane: source row r of src [rows][cols]
+ * (QI21_F32 / BF16 / F16) goes to dst row (r / group) * gstride + goff +
+ * r % group (rows of ld halves, ld >= 1.5 cols, % 4), its values at their
+ * lo8 positions; the residual bytes are left for qi21_op_plane8.
+ * cols % 128 == 0. */
+int qi21_op_plane_lo8(int src_dtype, const void* src, int rows, int cols, void* dst, int ld, int group, int gstride,
+                      int goff, void* stream);
+
+/* The fp8 part of a lo8 weight plane whose f16 values are set: for each of
+ * the rows, e per row such that the row's largest |w| 2^-e lies in [128,
+ * 256); byte of column c = e4m3(w_c 2^-e) and sc[r] = e + 127.
+ * cols % 128 == 0, ld >= 1.5 cols, % 4. */
+int qi21_op_plane8(int rows, int cols, void* plane, int ld, uint8_t* sc, void* stream);
 
 /* Per-head RMSNorm(norm_q | norm_k) then interleaved-pair RoPE on the q
  * (column 0) and k (column heads*128) parts of panel f16 [rows][ldp], in

@@ -26,7 +26,7 @@ from oracle import SynthModel, workload_inputs  # noqa: E402
 from oracle import qi21_oracle as O  # noqa: E402
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-STRIDE = {"512": 1, "1024": 4, "cond": 4, "cfg512": 2, "2048": 16, "ragged": 4}
+STRIDE = {"512": 1, "1024": 1, "cond": 4, "cfg512": 2, "2048": 16, "ragged": 4}
 
 
 def golden_path(name: str, prefix: int = 0, storage=None) -> str:

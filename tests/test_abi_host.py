@@ -71,7 +71,7 @@ def test_layout_vis_block_causal():
 def test_default_options_are_the_pages_guards():
     o = Q.qi21_default_options()
     assert (o.shift_attn, o.shift_qkv, o.shift_ao, o.shift_ffn, o.shift_hid) == (2, 4, 4, 2, 8)
-    assert o.max_programs == 2 and o.gemm_tile == -1 and o.ffn_pair == 0
+    assert o.max_programs == 2 and o.gemm_tile == -1 and o.ffn_mode == 0
 
 
 def _geom(**kw):
@@ -102,6 +102,26 @@ def test_model_create_refuses_null_and_block_count():
     assert e.value.code == Q.QI21_EINVAL
 
 
+def test_model_create_refuses_bad_ffn_mode_before_device_work():
+    # the option is checked, and lo8's geometry bounds, before any allocation
+    opt = Q.qi21_default_options()
+    opt.ffn_mode = 3
+    with pytest.raises(Q.Qi21Error) as e:
+        Q.qi21_model_create(_geom(), opt, 2, 1, 1, stream=0)
+    assert e.value.code == Q.QI21_EINVAL
+    opt.ffn_mode = Q.QI21_FFN_LO8
+    g = _geom()
+    g.hidden, g.heads = 384, 3  # hidden % 256 != 0
+    with pytest.raises(Q.Qi21Error) as e:
+        Q.qi21_model_create(g, opt, 2, 1, 1, stream=0)
+    assert e.value.code == Q.QI21_EUNSUPPORTED
+    g = _geom()
+    g.inter = 704  # inter % 128 != 0
+    with pytest.raises(Q.Qi21Error) as e:
+        Q.qi21_model_create(g, opt, 2, 1, 1, stream=0)
+    assert e.value.code == Q.QI21_EUNSUPPORTED
+
+
 def test_op_entry_points_validate_shapes_on_host():
     cases = [
         lambda: Q.qi21_op_gemm(0, 16, 100, 64, 1, 64, 1, 1, 100, stream=0),        # N % 128
@@ -111,10 +131,10 @@ def test_op_entry_points_validate_shapes_on_host():
         lambda: Q.qi21_op_gemm(0, 16, 128, 64, 1, 64, 1, 1, 128, tile=0, stream=0),   # 256 tile, N % 256
         lambda: Q.qi21_op_flash(0, 1, 1, 128, 1, 128, 1, 64, 10, None, 0, None, 0, 0, None, 1, 128, stream=0),
         lambda: Q.qi21_op_flash(4, 1, 1, 128, 1, 128, 1, 32, 40, None, 0, None, 0, 0, None, 1, 128, stream=0),
-        lambda: Q.qi21_op_rowop(4, 4098, 2, 1, 1, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
-        lambda: Q.qi21_op_rowop(4, 256, 4, 1, 1, 1, 1, 0, 0, 1e-6, 1.0, stream=0),    # pair bit without the norm
-        lambda: Q.qi21_op_rowop(4, 256, 5, 1, 1, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
-        lambda: Q.qi21_op_rowop(4, 256, 8, 1, 1, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop(4, 4098, 2, 1, 1, 1, 4100, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop(4, 256, 4, 1, 1, 1, 512, 1, 0, 0, 1e-6, 1.0, stream=0),    # pair bit without the norm
+        lambda: Q.qi21_op_rowop(4, 256, 5, 1, 1, 1, 512, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop(4, 256, 8, 1, 1, 1, 256, 1, 0, 0, 1e-6, 1.0, stream=0),
         lambda: Q.qi21_op_gemm(5, 16, 128, 64, 1, 64, 1, 1, 128, stream=0),           # no such epilogue
         lambda: Q.qi21_op_gemm(4, 16, 128, 64, 1, 64, 1, 1, 64, stream=0),            # swiglu2 needs ldo >= N
         lambda: Q.qi21_op_gemm_pair(1, 16, 128, 64, 1, 100, 1, 1, 128, stream=0),     # lda < 2K
@@ -133,8 +153,32 @@ def test_op_entry_points_validate_shapes_on_host():
         lambda: Q.qi21_op_gemm_split(16, 256, 256, 256, 1, 256, 1, 1, 9, stream=0),     # ksplit > 8
         lambda: Q.qi21_op_gemm_split(16, 128, 256, 256, 1, 256, 1, 1, 2, stream=0),     # N % 256
         lambda: Q.qi21_op_gemm_split(16, 256, 256, 256, 1, 256, 1, 1, 2, tile=1, stream=0),
-        lambda: Q.qi21_op_rowop_parts(4, 256, 3, 1, 1, 0, 1024, 1, 1, 0, 0, 1e-6, 1.0, stream=0),  # nparts 0
-        lambda: Q.qi21_op_rowop_parts(4, 256, 3, 1, 1, 2, 1000, 1, 1, 0, 0, 1e-6, 1.0, stream=0),  # planes overlap
+        lambda: Q.qi21_op_rowop_parts(4, 256, 3, 1, 1, 0, 1024, 1, 256, 1, 0, 0, 1e-6, 1.0, stream=0),  # nparts 0
+        lambda: Q.qi21_op_rowop_parts(4, 256, 3, 1, 1, 2, 1000, 1, 256, 1, 0, 0, 1e-6, 1.0, stream=0),  # planes overlap
+        # the xn row stride: at least h, 2h with the pair bit, a multiple of 4
+        lambda: Q.qi21_op_rowop(4, 256, 2, 1, 1, 1, 252, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop(4, 256, 6, 1, 1, 1, 256, 1, 0, 0, 1e-6, 1.0, stream=0),    # pair rows into [rows][h]
+        lambda: Q.qi21_op_rowop(4, 256, 2, 1, 1, 1, 258, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop_parts(4, 256, 7, 1, 1, 2, 1024, 1, 500, 1, 0, 0, 1e-6, 1.0, stream=0),
+        # the lo8 row op: h % 128, ldxn >= 1.5 h, scales, modes 2 / 3 only
+        lambda: Q.qi21_op_rowop_lo8(4, 192, 2, 1, 1, 1, 0, 1, 288, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop_lo8(4, 256, 2, 1, 1, 1, 0, 1, 380, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop_lo8(4, 256, 2, 1, 1, 1, 0, 1, 384, None, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop_lo8(4, 256, 6, 1, 1, 1, 0, 1, 512, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
+        # the lo8 GEMM: K % 128, N % 256, lda / ldw >= 1.5 K, scale strides, split, epilogue arguments
+        lambda: Q.qi21_op_gemm_lo8(1, 16, 256, 192, 1, 288, 1, 4, 1, 288, 1, 1, 256, stream=0),
+        lambda: Q.qi21_op_gemm_lo8(1, 16, 128, 256, 1, 384, 1, 4, 1, 384, 1, 1, 128, stream=0),
+        lambda: Q.qi21_op_gemm_lo8(1, 16, 256, 256, 1, 256, 1, 4, 1, 384, 1, 1, 256, stream=0),
+        lambda: Q.qi21_op_gemm_lo8(1, 16, 256, 256, 1, 384, 1, 3, 1, 384, 1, 1, 256, stream=0),
+        lambda: Q.qi21_op_gemm_lo8(1, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 1, 256, ksplit=3, stream=0),
+        lambda: Q.qi21_op_gemm_lo8(7, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 1, 256, stream=0),       # no gate
+        lambda: Q.qi21_op_gemm_lo8(9, 16, 512, 256, 1, 384, 1, 4, 1, 384, 1, 1, 384, stream=0),       # no osc
+        lambda: Q.qi21_op_gemm_lo8(0, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 1, 256, stream=0),       # F16
+        lambda: Q.qi21_op_gemm_lo8(7, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 1, 256, gate=1, ksplit=2, stream=0),
+        lambda: Q.qi21_op_plane_lo8(0, 1, 16, 192, 1, 288, 16, 0, 0, stream=0),
+        lambda: Q.qi21_op_plane_lo8(0, 1, 16, 256, 1, 256, 16, 0, 0, stream=0),
+        lambda: Q.qi21_op_plane8(16, 256, 1, 380, 1, stream=0),
+        lambda: Q.qi21_op_plane8(16, 256, 1, 384, None, stream=0),
     ]
     for c in cases:
         with pytest.raises(Q.Qi21Error) as e:

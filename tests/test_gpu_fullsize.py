@@ -9,14 +9,17 @@ velocity at 512^2, 1024^2, with the condition-image prefix and for the CFG
 pair is compared with the oracle's stored output (written by
 ``tests/golden/make_oracle_golden.py`` from the oracle alone).
 
-End-to-end tolerances.  With the FFN input and SwiGLU hidden kept as f16
-pairs (ffn_pair = 1) the velocity is held to the 1e-3 relative L2 bar.
-With every site in single f16 (the default, as on the pages) the error
-after 32 blocks of these N(0, 0.02) weights is the storage's own: the
-oracle run with the same sites rounded to f16 (its ``storage="f16"``
-mode) is itself ~1.8e-3 from the f32 oracle at 512^2, growing as the
-square root of the depth from ~3e-4 per block.  The single-f16 path is
-therefore bounded by 1.5x that storage error, measured on the same
+End-to-end tolerances.  The benchmark's configuration keeps the FFN input
+and SwiGLU hidden in the lo8 form (QI21_FFN_LO8: f16 plus a scaled fp8
+residual); it, and the f16-pair form (QI21_FFN_PAIR), are held to the 1e-3
+relative L2 bar on v, and every target row compared to 3e-3 relative L2
+over its 64 channels (a row-local fault a few times the bar fails it even
+where the global figure hides it).  With every site in single f16 (the
+pages' design) the error after 32 blocks of these N(0, 0.02) weights is
+the storage's own: the oracle run with the same sites rounded to f16 (its
+``storage="f16"`` mode) is itself ~1.8e-3 from the f32 oracle at 512^2,
+growing as the square root of the depth from ~3e-4 per block.  That path
+is therefore bounded by 1.5x that storage error, measured on the same
 workload, not by 1e-3.
 """
 import os
@@ -169,7 +172,7 @@ def test_rowop_full_shape_sampled():
     y = inputs.device_tensor(31, 2, (rows, h), 0.5)
     mods = inputs.device_tensor(31, 3, (4 * h,), 0.1)
     xn = torch.empty(rows, h, device="cuda", dtype=torch.float16)
-    q.qi21_op_rowop(rows, h, 3, x, y, xn, mods, 3 * h, 0, 1e-6, 0.25)
+    q.qi21_op_rowop(rows, h, 3, x, y, xn, h, mods, 3 * h, 0, 1e-6, 0.25)
     torch.cuda.synchronize()
     sample = np.sort(np.random.default_rng(3).choice(rows, 32, replace=False))
     xh = np.stack([inputs.host_array(31, 1, (h,), 1.0, start=int(r) * h) for r in sample])
@@ -183,18 +186,34 @@ def test_rowop_full_shape_sampled():
 
 # ───────────────────────────── end to end ─────────────────────────────
 
+ROW_TOL = 3e-3
+
+
+def _full(opt_mode=None):
+    q = Q()
+    opt = q.qi21_default_options()
+    if opt_mode is not None:
+        opt.ffn_mode = opt_mode
+    return bench.build_model(CONFIGS["1024"].model, opt)
+
+
 @pytest.fixture(scope="module")
 def full_model():
-    m = bench.build_model(CONFIGS["1024"].model)
+    m = _full()
     yield m
     Q().qi21_model_destroy(m)
 
 
 @pytest.fixture(scope="module")
 def full_model_pair():
-    opt = Q().qi21_default_options()
-    opt.ffn_pair = 1
-    m = bench.build_model(CONFIGS["1024"].model, opt)
+    m = _full(Q().QI21_FFN_PAIR)
+    yield m
+    Q().qi21_model_destroy(m)
+
+
+@pytest.fixture(scope="module")
+def full_model_lo8():
+    m = _full(Q().QI21_FFN_LO8)
     yield m
     Q().qi21_model_destroy(m)
 
@@ -217,43 +236,56 @@ def _step_v(m, w, key, stride):
     return out.cpu().numpy()[::stride]
 
 
-@pytest.mark.parametrize("name", ["512", "1024", "cond", "ragged"])
-def test_step_full_size_against_oracle(full_model_pair, name):
-    # ragged: 4087 target rows behind 37 prefix rows, so the last row tile of
-    # every GEMM, the last V^T columns and the last key tile of attention are
-    # partial on the large-pass path (fused q|k epilogue, block-per-row pass)
-    want, stride = _golden(name)
-    err = rel(_step_v(full_model_pair, CONFIGS[name], 50, stride), want)
-    print(f"{name} (ffn_pair): v rel L2 vs oracle {err:.3e}")
+def _check_v(got, want, label):
+    err = rel(got, want)
+    g, w = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    rows = np.linalg.norm(g - w, axis=1) / np.linalg.norm(w, axis=1)
+    print(f"{label}: v rel L2 vs oracle {err:.3e}, worst row {rows.max():.3e} (row {int(rows.argmax())})")
     assert err < V_TOL
+    assert rows.max() < ROW_TOL
+
+
+@pytest.mark.parametrize("name", ["512", "1024", "cond", "ragged", "2048"])
+def test_step_full_size_lo8_against_oracle(full_model_lo8, name):
+    # the configuration bench.py times.  ragged: 4087 target rows behind 37
+    # prefix rows, so the last row tile of every GEMM, the last V^T columns
+    # and the last key tile of attention are partial on the large-pass path
+    want, stride = _golden(name)
+    _check_v(_step_v(full_model_lo8, CONFIGS[name], 52, stride), want, f"{name} (lo8)")
+
+
+@pytest.mark.parametrize("name", ["512", "1024", "cond", "ragged"])
+def test_step_full_size_pair_against_oracle(full_model_pair, name):
+    want, stride = _golden(name)
+    _check_v(_step_v(full_model_pair, CONFIGS[name], 50, stride), want, f"{name} (pair)")
 
 
 @pytest.mark.parametrize("name", ["512", "1024"])
 def test_step_full_size_single_f16_within_storage_error(full_model, name):
     want, stride = _golden(name)
-    want16, _ = _golden(name, tag="_f16")
-    storage = rel(want16, want)  # what f16 storage alone costs, per the oracle
+    want16, stride16 = _golden(name, tag="_f16")
+    storage = rel(want16, want[::stride16 // stride])  # what f16 storage alone costs, per the oracle
     err = rel(_step_v(full_model, CONFIGS[name], 51, stride), want)
     print(f"{name} (single f16): v rel L2 vs oracle {err:.3e}; oracle f16-storage error {storage:.3e}")
     assert storage > V_TOL  # the reason this path has its own bound
     assert err < 1.5 * storage
 
 
-def test_cfg_pair_full_size_against_oracle(full_model_pair):
+@pytest.mark.parametrize("mode", ["lo8", "pair"])
+def test_cfg_pair_full_size_against_oracle(request, mode):
+    m = request.getfixturevalue("full_model_lo8" if mode == "lo8" else "full_model_pair")
     w = CONFIGS["cfg512"]
     wants = [_golden("cfg512", p) for p in range(2)]
     ds = [bench.workload_tensors(w, p) for p in range(2)]
     for p in range(2):
-        bench.prefill(full_model_pair, 60 + p, ds[p])
+        bench.prefill(m, 60 + p, ds[p])
     outs = [torch.zeros(d["n"], 64, device="cuda") for d in ds]
-    Q().qi21_step_batch(full_model_pair, [60, 61], [d["tok"] for d in ds], ds[0]["mods"], ds[0]["fs"], outs)
+    Q().qi21_step_batch(m, [60, 61], [d["tok"] for d in ds], ds[0]["mods"], ds[0]["fs"], outs)
     for p in range(2):
         want, stride = wants[p]
-        err = rel(outs[p].cpu().numpy()[::stride], want)
-        print(f"cfg prefix {p} (ffn_pair): v rel L2 vs oracle {err:.3e}")
-        assert err < V_TOL
+        _check_v(outs[p].cpu().numpy()[::stride], want, f"cfg prefix {p} ({mode})")
     for p in range(2):
-        Q().qi21_release_key(full_model_pair, 60 + p)
+        Q().qi21_release_key(m, 60 + p)
 
 
 def test_step_1024_gate_zero_closed_form_and_determinism(full_model):

@@ -120,7 +120,7 @@ PAIR_TOL = 1e-5  # f32 accumulation; the pair carries ~22 significant bits
 @pytest.mark.parametrize("M", [1, 77, 300, 1600])
 @pytest.mark.parametrize("epi", ["f32", "swiglu", "swiglu2"])
 def test_gemm_pair_operand(epi, M, tile):
-    """(A_hi + A_lo) W^T with each W row read for both halves (the ffn_pair
+    """(A_hi + A_lo) W^T with each W row read for both halves (the QI21_FFN_PAIR
     GEMMs): within f32 accumulation of the float operand's exact product,
     where a single f16 operand is ~1e-4 away."""
     q = Q()
@@ -311,7 +311,7 @@ def test_flash_lazy_rescale_paths(order, nq):
 @pytest.mark.parametrize("mode", [6, 7])
 def test_rowop_pair_output(mode, rows, h):
     """mode bit 2: the modulated LayerNorm written as an f16 pair [rows][2h]
-    whose sum is the f32 value (the ffn_pair FFN input)"""
+    whose sum is the f32 value (the QI21_FFN_PAIR FFN input)"""
     q = Q()
     x = inputs.host_array(8, 1, (rows, h), 1.0)
     y = inputs.host_array(8, 2, (rows, h), 0.5)
@@ -319,7 +319,7 @@ def test_rowop_pair_output(mode, rows, h):
     g_off, s_off, eps, oscale = 3 * h, 2 * h, 1e-6, 0.25
     dx, dy, dm = dev(x), dev(y), dev(mods)
     xn = torch.zeros(rows, 2 * h, device="cuda", dtype=torch.float16)
-    q.qi21_op_rowop(rows, h, mode, dx, dy, xn, dm, g_off, s_off, eps, oscale)
+    q.qi21_op_rowop(rows, h, mode, dx, dy, xn, xn.shape[1], dm, g_off, s_off, eps, oscale)
     sync()
     xe = O.gated_add(x, y, mods[g_off:g_off + h]) if mode & 1 else x
     assert rel(dx.cpu().numpy(), xe) < 1e-6
@@ -341,7 +341,7 @@ def test_rowop_modes(mode, rows, h):
     g_off, s_off, eps, oscale = 3 * h, 2 * h, 1e-6, 0.25
     dx, dy, dm = dev(x), dev(y), dev(mods)
     xn = torch.zeros(rows, h, device="cuda", dtype=torch.float16)
-    q.qi21_op_rowop(rows, h, mode, dx, dy, xn, dm, g_off, s_off, eps, oscale)
+    q.qi21_op_rowop(rows, h, mode, dx, dy, xn, xn.shape[1], dm, g_off, s_off, eps, oscale)
     sync()
     xe = O.gated_add(x, y, mods[g_off:g_off + h]) if mode & 1 else x
     assert rel(dx.cpu().numpy(), xe) < 1e-6
@@ -381,7 +381,7 @@ def test_rowop_row_forms(rows, h, mode):
     g_off, s_off, eps, oscale = 3 * h, 2 * h, 1e-6, 0.25
     dx, dy, dm = dev(x), dev(y), dev(mods)
     xn = torch.zeros(rows, 2 * h if mode & 4 else h, device="cuda", dtype=torch.float16)
-    q.qi21_op_rowop(rows, h, mode, dx, dy, xn, dm, g_off, s_off, eps, oscale)
+    q.qi21_op_rowop(rows, h, mode, dx, dy, xn, xn.shape[1], dm, g_off, s_off, eps, oscale)
     sync()
     xe = O.gated_add(x, y, mods[g_off:g_off + h]) if mode & 1 else x
     assert rel(dx.cpu().numpy(), xe) < 1e-6
@@ -522,7 +522,7 @@ def test_rowop_adds_partial_planes(mode, nparts):
     mods = inputs.host_array(15, 3, (4 * h,), 0.1)
     g_off, s_off, eps, oscale = 3 * h, 0, 1e-6, 0.25
     dx, xn = dev(x), torch.zeros(rows, 2 * h if mode & 4 else h, device="cuda", dtype=torch.float16)
-    q.qi21_op_rowop_parts(rows, h, mode, dx, dev(y), nparts, (rows + 3) * h, xn, dev(mods), g_off, s_off, eps, oscale)
+    q.qi21_op_rowop_parts(rows, h, mode, dx, dev(y), nparts, (rows + 3) * h, xn, xn.shape[1], dev(mods), g_off, s_off, eps, oscale)
     sync()
     ysum = y[0, :rows].copy()
     for p in range(1, nparts):

@@ -177,13 +177,14 @@ def test_range_guard_settings(tiny_cpu, shifts):
         q.qi21_model_destroy(m)
 
 
-def test_ffn_pair_option(tiny_cpu, tiny_gpu):
-    """ffn_pair = 1 (FFN input and hidden as f16 pairs): same result to the
-    bar, on the single step and on a batched CFG pair; no larger error than
-    single f16"""
+@pytest.mark.parametrize("mode", ["pair", "lo8"])
+def test_ffn_mode_option(tiny_cpu, tiny_gpu, mode):
+    """ffn_mode PAIR (FFN input and hidden as f16 pairs) and LO8 (f16 plus
+    a scaled fp8 residual): the result to the bar, on the single step and
+    on a batched CFG pair, and no larger error than single f16"""
     q = Q()
     opt = q.qi21_default_options()
-    opt.ffn_pair = 1
+    opt.ffn_mode = q.QI21_FFN_PAIR if mode == "pair" else q.QI21_FFN_LO8
     m = bench.build_model(TINY_MODEL, opt)
     try:
         w = CONFIGS["tiny"]
@@ -191,7 +192,7 @@ def test_ffn_pair_option(tiny_cpu, tiny_gpu):
         want = oracle_v(tiny_cpu, w)
         err = rel(v, want)
         base = rel(gpu_v(tiny_gpu, w, key=5)[0], want)
-        print(f"tiny v rel L2 ffn_pair {err:.3e}, single f16 {base:.3e}")
+        print(f"tiny v rel L2 ffn_mode {mode} {err:.3e}, single f16 {base:.3e}")
         assert err < V_TOL and err < base
         ds = [bench.workload_tensors(w) for _ in range(2)]
         bench.prefill(m, 2, ds[0])
@@ -201,14 +202,6 @@ def test_ffn_pair_option(tiny_cpu, tiny_gpu):
             assert rel(o.cpu().numpy(), v) < 1e-6
     finally:
         q.qi21_model_destroy(m)
-
-
-def test_ffn_pair_option_is_validated():
-    q = Q()
-    opt = q.qi21_default_options()
-    opt.ffn_pair = 2
-    with pytest.raises(q.Qi21Error):
-        bench.build_model(TINY_MODEL, opt)
 
 
 def test_nonfinite_velocity_is_refused_and_out_untouched(tiny_gpu):
@@ -226,6 +219,43 @@ def test_nonfinite_velocity_is_refused_and_out_untouched(tiny_gpu):
     # the model still works afterwards
     q.qi21_step(tiny_gpu, 4, d["tok"], d["mods"], d["fs"], out)
     assert torch.all(torch.isfinite(out))
+
+
+def test_batched_step_after_a_refused_nonfinite_step(tiny_gpu, tiny_cpu):
+    """A refused non-finite step leaves non-finite values behind in the
+    shared activations.  A later batched step whose programs leave gap rows
+    between them (target 120 rows: the second program starts at row 128)
+    and V^T padding past the last key (248 rows in a 256-row pass) reads
+    both with zero weight, so they must have been rewritten: the step is
+    finite and matches the oracle ([WG] step refuses a non-finite velocity
+    and the program stays usable)."""
+    q = Q()
+    w0 = CONFIGS["tiny"]
+    d0 = bench.workload_tensors(w0)
+    bench.prefill(tiny_gpu, 20, d0)
+    mods = d0["mods"].clone()
+    mods[:TINY_MODEL.dim] = 1e5  # (1 + s1) * LN(x) overflows the f16 attention input
+    out = torch.zeros(d0["n"], 64, device="cuda")
+    with pytest.raises(q.Qi21Error) as e:
+        q.qi21_step(tiny_gpu, 20, d0["tok"], mods, d0["fs"], out)
+    assert e.value.code == q.QI21_ENONFINITE
+    q.qi21_release_key(tiny_gpu, 20)
+    w = Workload("cfg", TINY_MODEL, 44, (10, 12), ((("text", 18),), (("text", 9), ("image", 2, 3))),
+                 prefix_seeds=(44, 45))
+    ds = [bench.workload_tensors(w, p) for p in range(2)]
+    for p in range(2):
+        bench.prefill(tiny_gpu, 21 + p, ds[p])
+    outs = [torch.zeros(d["n"], 64, device="cuda") for d in ds]
+    q.qi21_step_batch(tiny_gpu, [21, 22], [d["tok"] for d in ds], ds[0]["mods"], ds[0]["fs"], outs)
+    for p in range(2):
+        d = workload_inputs(w, p)
+        pre = O.prefill(tiny_cpu, d["x_prefix"], O.Layout(w.layout(p)))
+        want = O.step(tiny_cpu, pre, d["tok"], d["mods"], d["final_scale"])
+        got = outs[p].cpu().numpy()
+        assert np.isfinite(got).all()
+        assert rel(got, want) < V_TOL
+    for p in range(2):
+        q.qi21_release_key(tiny_gpu, 21 + p)
 
 
 def test_error_paths_and_eviction(tiny_gpu):
