@@ -33,7 +33,7 @@
 // the v columns transposed (V^T, the layout the attention kernel streams).
 // Range-guard factors are powers of two folded into oscale / inscale.
 #include "qi21_internal.h"
-#include "lo8.h"
+#include "lores.h"
 
 #include <algorithm>
 
@@ -254,6 +254,52 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
         if (hsel == 0) a.osc[(size_t)row * a.ldos + hc / 64] = (uint8_t)(ex + 127);
       }
     }
+  } else if constexpr (EPI == EPI_SWIGLU4) {
+    // the wave's 4 column tiles are 64 hidden columns, two 32-column scale
+    // blocks p per row: lanes l and l ^ 32 hold the two halves of each
+    static_assert(TN == 4, "a wave spans two 32-column scale blocks");
+    const int hc = c0 / 2;  // first hidden column of the wave
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = r0 + i * 32 + l32;
+      half4 hi[2][4];
+      floatx4 lo[2][4];
+      float mx[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float h = silu_f(acc[i][2 * p][4 * g + e] * a.inscale) * (acc[i][2 * p + 1][4 * g + e] * a.inscale) *
+                            a.oscale;
+            hi[p][g][e] = (f16)h;
+            lo[p][g][e] = h - (float)hi[p][g][e];  // exact in f32
+            mx[p] = fmaxf(mx[p], fabsf(lo[p][g][e]));
+          }
+      int ex[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[p]), __float_as_uint(mx[p]), false, false);
+        ex[p] = lo4_exp(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+      }
+      if (row < a.M) {
+        f16* orow = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo;
+        uint8_t* brow = reinterpret_cast<uint8_t*>(orow);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const float inv = __builtin_ldexpf(1.0f, -ex[p]);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = hc + p * 32 + 8 * g + 4 * hsel;
+            *reinterpret_cast<half4*>(orow + lo4_hi_at(c)) = hi[p][g];
+            const floatx4 v = lo[p][g] * inv;
+            *reinterpret_cast<uint16_t*>(brow + lo4_lo_at(c)) = (uint16_t)pack_e2m1(v[0], v[1], v[2], v[3]);
+          }
+          if (hsel == 0) a.osc[(size_t)row * a.ldos + lo4_sc_at(hc + p * 32)] = (uint8_t)(ex[p] + 127);
+        }
+      }
+    }
   } else {  // EPI_SWIGLU, EPI_SWIGLU2: tiles (2p, 2p+1) hold matching gate / up columns
     static_assert(EPI == EPI_SWIGLU || EPI == EPI_SWIGLU2, "row-layout epilogue");
 #pragma unroll
@@ -413,8 +459,9 @@ __device__ __forceinline__ int dswz(int r) { return (r >> 1) & 7; }
 // branch-free loop, so the accumulators stay in AGPRs.  Scales: the W
 // rows' are fixed over a unit; the A rows' two bytes of a group are read
 // at its first k-tile.
-template <int EPI, int NW, bool LO8 = false>
+template <int EPI, int NW, int LO = 0>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
+  constexpr bool LO8 = LO == 8, LO4 = LO == 4;
   // 32 x 32 tiles per wave: 4 x 4 with 4 waves; 4 x 2 with 8, except the
   // q/k-norm epilogue, whose waves span whole 128-column heads (2 x 4)
   constexpr int TM = (NW == 8 && EPI == EPI_QKROPE) ? 2 : 4;
@@ -422,7 +469,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
   constexpr int WTM = TM * 32, WTN = TN * 32;  // wave tile
   constexpr int NCOL = DBN / WTN;              // waves across the block's columns
   constexpr int NL = 32 / NW;                  // 16-byte loads per lane per operand per k-tile
-  static_assert(!LO8 || (NW == 4 && EPI != EPI_QKV), "fp8 k-tiles: 4-wave row-layout kernels");
+  static_assert(LO == 0 || (NW == 4 && EPI != EPI_QKV), "residual k-tiles: 4-wave row-layout kernels");
   extern __shared__ __attribute__((aligned(16))) f16 smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -552,9 +599,24 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
     else
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[b][i], bf[b][j], acc[i][j], 0, 0, 0);
   };
-  // scales of the fp8 k-tiles: the W rows' (per unit) and, per A row, the
-  // two bytes of the current group's k-steps
+  // scales of the residual k-tiles: lo8, the W rows' (per unit) and, per A
+  // row, the two bytes of the current group's k-steps; lo4, per W row and
+  // per A row the dword of the current group's four k-steps (lane half h)
   int wsc[TN], asc[TM];
+  // an fp4 MFMA of k-step kk (the scale byte kk of each dword)
+  auto mfma4 = [&](int b, int k, int kk) {
+    const int i = k / TN, j = k % TN;
+    const i32x8 wv = __builtin_bit_cast(i32x8, __builtin_shufflevector(__builtin_bit_cast(u32x4, bf[b][j]),
+                                                                       u32x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7));
+    const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(__builtin_bit_cast(u32x4, af[b][i]),
+                                                                       u32x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7));
+    switch (kk) {  // (the byte selects must be immediates)
+      case 0: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 4, 4, 0, wsc[j], 0, asc[i]); break;
+      case 1: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 4, 4, 1, wsc[j], 1, asc[i]); break;
+      case 2: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 4, 4, 2, wsc[j], 2, asc[i]); break;
+      default: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 4, 4, 3, wsc[j], 3, asc[i]); break;
+    }
+  };
   auto mfma8 = [&](int b, int k, int kk) {
     const int i = k / TN, j = k % TN;
     if (kk == 0)
@@ -583,6 +645,21 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
       if (rd && !rd8 && k < NDS) read1(t, kk, b ^ 1, k);
       if constexpr (LO8)
         if (rd8 && k < NDS) read8(t, kk, 0, k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // lo4: a k-step of either kind (fp4 = the group's residual k-tile, whose
+  // MFMAs take k-step mk's scale bytes), otherwise as step
+  auto step4 = [&](bool fp4, int mk, int b, bool rd, int t, int kk, __amdgpu_buffer_rsrc_t ra,
+                   __amdgpu_buffer_rsrc_t rb, int tl, int q0, int q1) {
+#pragma unroll
+    for (int k = 0; k < MM; ++k) {
+      if (fp4)
+        mfma4(b, k, mk);
+      else
+        mfma1(b, k);
+      if (q0 + k < q1) load1(ra, rb, tl & 1, kt0 + tl, q0 + k);
+      if (rd && k < NDS) read1(t, kk, b ^ 1, k);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -691,6 +768,70 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
           prologue(tm, tn, kt0);
         }
         step8(1, 1, false, false, 0, 0, ra, rb, 0, 0, 0);
+      }
+    } else if constexpr (LO4) {
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.asc + (size_t)m0 * a.lds), 0, min(a.M - m0, DBM) * a.lds, 0x00020000);
+      // the scale dwords of the group at unit-local k-tile t: its fp4
+      // k-tile's four k-steps for this lane half, per A row and per W row
+      auto load_sc = [&](int t) {
+        const int o = ((kt0 + t) / 5) * 8 + 4 * hsel;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          asc[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, (wm * WTM + i * 32 + l32) * a.lds + o, 0, 0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          wsc[j] = *reinterpret_cast<const int*>(a.wsc + (size_t)(n0 + wn * WTN + j * 32 + l32) * a.ldws + o);
+      };
+      load_sc(0);
+      if (sq == seq0)
+        __builtin_amdgcn_s_waitcnt(wait_imm(Q1, 15));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int r = 0; r < NDS; ++r) read1(0, 0, 0, r);
+      __builtin_amdgcn_sched_barrier(0);
+      // one k-tile of either kind whose last k-step reads the next k-tile's
+      // first fragments (loads of k-tiles t + 1 and t + 2 as in the plain loop)
+      auto tile4 = [&](bool fp4, int t) {
+        step4(fp4, 0, 0, true, t, 1, ra, rb, t + 1, Q1, Q2);
+        step4(fp4, 1, 1, true, t, 2, ra, rb, t + 1, Q2, NQ);
+        step4(fp4, 2, 0, true, t, 3, ra, rb, 0, 0, 0);
+        sync_tile();
+        step4(fp4, 3, 1, true, t + 1, 0, ra, rb, t + 2, 0, Q1);
+      };
+      // groups (f16 x 4, fp4) of k-tiles t .. t + 4; the next group's scales
+      // are fetched once its fp4 MFMAs are issued
+      for (int t = 0; t < KT - 5; t += 5) {
+        tile4(false, t);
+        tile4(false, t + 1);
+        tile4(false, t + 2);
+        tile4(false, t + 3);
+        tile4(true, t + 4);
+        load_sc(t + 5);
+      }
+      // the last group
+      {
+        const int t = KT - 5;
+        tile4(false, t);
+        tile4(false, t + 1);
+        tile4(false, t + 2);
+        step4(false, 0, 0, true, t + 3, 1, ra, rb, t + 4, Q1, Q2);
+        step4(false, 1, 1, true, t + 3, 2, ra, rb, t + 4, Q2, NQ);
+        step4(false, 2, 0, true, t + 3, 3, ra, rb, 0, 0, 0);
+        sync_tile();
+        step4(false, 3, 1, true, t + 4, 0, ra, rb, 0, 0, 0);
+        step4(true, 0, 0, true, t + 4, 1, ra, rb, 0, 0, 0);
+        step4(true, 1, 1, true, t + 4, 2, ra, rb, 0, 0, 0);
+        step4(true, 2, 0, true, t + 4, 3, ra, rb, 0, 0, 0);
+        sync_tile();
+        const int nsq = sq + seq_step;
+        if (nsq < seq_end) {
+          tile_rc(nsq, tm, tn, kt0);
+          prologue(tm, tn, kt0);
+        }
+        step4(true, 3, 1, false, 0, 0, ra, rb, 0, 0, 0);
       }
     } else {
       // k-tile 0 landed.  After an epilogue its stores share the vector
@@ -837,12 +978,12 @@ __global__ __launch_bounds__(256) void gemm_rs_kernel(GemmArgs a) {
 
 namespace {
 
-template <int EPI, int NW, bool LO8 = false>
+template <int EPI, int NW, int LO = 0>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   constexpr size_t lds = (size_t)DNS * DSTAGE * 2;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<EPI, NW, LO8>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<EPI, NW, LO>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
@@ -858,7 +999,7 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   // persistent: one block per CU walks several tiles; fewer tiles than CUs:
   // one block per tile
   const int blocks = tiles > cus ? cus : tiles;
-  hipLaunchKernelGGL((gemm_dma_kernel<EPI, NW, LO8>), dim3(blocks), dim3(NW * 64), lds, s, a);
+  hipLaunchKernelGGL((gemm_dma_kernel<EPI, NW, LO>), dim3(blocks), dim3(NW * 64), lds, s, a);
   return hipGetLastError();
 }
 
@@ -932,18 +1073,29 @@ int gemm_split_count(int M, int N, int K, int maxs) {
 }
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, int tile, hipStream_t s) {
-  if (a.kt8 < a.K / 64) {  // fp8 k-tiles: the 4-wave 256 x 256 kernel
-    if (a.kt8 != 2 || a.N % 256 != 0 || !a.asc || !a.wsc || a.lds % 2 != 0 || (tile != 0 && tile != -1) ||
-        (a.K / 64) % (3 * a.ksplit) != 0)
+  if (a.lo == 8 || a.lo == 4) {  // residual k-tiles: the 4-wave 256 x 256 kernel
+    const int group = a.lo == 8 ? 3 : 5;  // k-tiles per group of columns
+    if (a.N % 256 != 0 || !a.asc || !a.wsc || (tile != 0 && tile != -1) || (a.K / 64) % (group * a.ksplit) != 0 ||
+        (a.lo == 8 ? a.lds % 2 != 0 : (a.lds % 4 != 0 || a.ldws % 4 != 0)))
       return hipErrorInvalidValue;
-    if (a.ksplit > 1) return epi == EPI_F32 ? launch_dma<EPI_F32, 4, true>(a, s) : hipErrorInvalidValue;
+    if (a.lo == 8) {
+      if (a.ksplit > 1) return epi == EPI_F32 ? launch_dma<EPI_F32, 4, 8>(a, s) : hipErrorInvalidValue;
+      switch (epi) {
+        case EPI_F32: return launch_dma<EPI_F32, 4, 8>(a, s);
+        case EPI_RESID: return launch_dma<EPI_RESID, 4, 8>(a, s);
+        case EPI_SWIGLU8: return launch_dma<EPI_SWIGLU8, 4, 8>(a, s);
+      }
+      return hipErrorInvalidValue;
+    }
+    if (a.ksplit > 1) return epi == EPI_F32 ? launch_dma<EPI_F32, 4, 4>(a, s) : hipErrorInvalidValue;
     switch (epi) {
-      case EPI_F32: return launch_dma<EPI_F32, 4, true>(a, s);
-      case EPI_RESID: return launch_dma<EPI_RESID, 4, true>(a, s);
-      case EPI_SWIGLU8: return launch_dma<EPI_SWIGLU8, 4, true>(a, s);
+      case EPI_F32: return launch_dma<EPI_F32, 4, 4>(a, s);
+      case EPI_RESID: return launch_dma<EPI_RESID, 4, 4>(a, s);
+      case EPI_SWIGLU4: return launch_dma<EPI_SWIGLU4, 4, 4>(a, s);
     }
     return hipErrorInvalidValue;
   }
+  if (a.lo != 0) return hipErrorInvalidValue;
   if (epi == EPI_SWIGLU8) {
     if (a.N % 256 != 0 || (tile != 0 && tile != -1) || a.ksplit != 1) return hipErrorInvalidValue;
     return launch_dma<EPI_SWIGLU8, 4>(a, s);

@@ -67,8 +67,8 @@ struct Acts {
   float* out = nullptr;  // [cap][64] velocity before the finite check
   float* rcs = nullptr;  // [cap][128] packed RoPE table of the pass's rows when
                          // they come from several programs, or of a prefill
-  uint8_t* xsc = nullptr;  // lo8: [cap][H / 64] scales of the FFN input's residuals
-  uint8_t* hsc = nullptr;  // lo8: [cap][I / 64] scales of the hidden's residuals
+  uint8_t* xsc = nullptr;  // lo8 / lo4: [cap][H / 64 or H / 32] scales of the FFN input's residuals
+  uint8_t* hsc = nullptr;  // lo8 / lo4: [cap][I / 64 or I / 32] scales of the hidden's residuals
 };
 
 struct Prog {
@@ -95,7 +95,7 @@ struct qi21_model {
   qi21_options o{};
   int nb = 0;
   std::vector<f16*> wqkv, wo, w13, w2;
-  std::vector<uint8_t*> w13s, w2s;  // lo8: per-row scales of the W13 / W2 residual bytes
+  std::vector<uint8_t*> w13s, w2s;  // lo8: per-row scales of the W13 / W2 fp8 copies; lo4: per row and 32 columns
   std::vector<float*> nq, nk;
   std::vector<char> set;
   float* img_in = nullptr;      // [H][64]
@@ -149,18 +149,23 @@ void dfree(qi21_model* m, void* p, size_t bytes) {
 
 constexpr int NACT = 12;
 
-// Bytes of the FFN input's and the hidden's rows per column: 2 (single
-// f16), 4 (f16 pairs), 3 (lo8: f16 plus an fp8 residual)
-size_t ffn_row_bytes(int mode) { return mode == QI21_FFN_PAIR ? 4 : mode == QI21_FFN_LO8 ? 3 : 2; }
+// Half-bytes per column of the FFN input's and the hidden's rows: 4
+// (single f16), 8 (f16 pairs), 6 (lo8: f16 plus an fp8 residual), 5 (lo4:
+// f16 plus an fp4 residual); likewise for the FFN weight planes (f16, lo8
+// or lo4)
+size_t ffn_row_nibbles(int mode) {
+  return mode == QI21_FFN_PAIR ? 8 : mode == QI21_FFN_LO8 ? 6 : mode == QI21_FFN_LO4 ? 5 : 4;
+}
+// scale bytes per row of a residual activation of w columns
+size_t ffn_scale_bytes(int mode, size_t w) { return mode == QI21_FFN_LO8 ? w / 64 : mode == QI21_FFN_LO4 ? w / 32 : 0; }
 
 size_t acts_bytes(const qi21_geom& g, int ffn_mode, int cap, size_t* parts) {
-  const size_t H = g.hidden, I = g.inter, c = cap, f = ffn_row_bytes(ffn_mode);
-  const bool lo8 = ffn_mode == QI21_FFN_LO8;
+  const size_t H = g.hidden, I = g.inter, c = cap, f = ffn_row_nibbles(ffn_mode);
   // slot 5: the partial products of a down GEMM split over K (4 planes of
   // up to 2048 rows; split GEMMs only run at fewer than 2048 rows)
-  const size_t p[NACT] = {c * H * 4, c * H * std::max<size_t>(f, 2), c * 2 * H * 2, H * c * 2, c * H * 2,
-                          4 * std::min<size_t>(c, 2048) * H * 4, c * I * f, 4 * H * 4, c * 64 * 4, c * 128 * 4,
-                          lo8 ? c * H / 64 : 0, lo8 ? c * I / 64 : 0};
+  const size_t p[NACT] = {c * H * 4, c * H * f / 2, c * 2 * H * 2, H * c * 2, c * H * 2,
+                          4 * std::min<size_t>(c, 2048) * H * 4, c * I * f / 2, 4 * H * 4, c * 64 * 4, c * 128 * 4,
+                          c * ffn_scale_bytes(ffn_mode, H), c * ffn_scale_bytes(ffn_mode, I)};
   size_t t = 0;
   for (int i = 0; i < NACT; ++i) {
     if (parts) parts[i] = p[i];
@@ -463,16 +468,18 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
     // each W row read twice; or lo8 (f16 plus scaled fp8 residuals, rows
     // of 3H / 3I bytes, with the weight planes in the same form).
     const int fm = m->o.ffn_mode;
-    const bool lo8 = fm == QI21_FFN_LO8;
+    const bool lo8 = fm == QI21_FFN_LO8, lo4 = fm == QI21_FFN_LO4, lo = lo8 || lo4;
     const int pf = fm == QI21_FFN_PAIR ? 2 : 1;
-    const int ffn_bits = fm == QI21_FFN_PAIR ? 4 : lo8 ? 8 : 0;  // the FFN-input row pass's mode bits
-    const int kx = lo8 ? 3 * H / 2 : pf * H;                    // the FFN input's row, in halves
-    const int kh = lo8 ? 3 * I / 2 : pf * I;                    // the hidden's row, in halves
-    auto ffn_lo8 = [&](qi21::GemmArgs& ga, const uint8_t* asc, int lds, const uint8_t* wsc) {
-      ga.kt8 = 2;
+    const int ffn_bits = fm == QI21_FFN_PAIR ? 4 : lo8 ? 8 : lo4 ? 16 : 0;  // the FFN-input row pass's mode bits
+    const int kx = lo8 ? 3 * H / 2 : lo4 ? 5 * H / 4 : pf * H;          // the FFN input's row, in halves
+    const int kh = lo8 ? 3 * I / 2 : lo4 ? 5 * I / 4 : pf * I;          // the hidden's row, in halves
+    const int sx = lo8 ? H / 64 : H / 32, sh = lo8 ? I / 64 : I / 32;  // their scale bytes per row
+    auto ffn_lo = [&](qi21::GemmArgs& ga, const uint8_t* asc, int lds, const uint8_t* wsc, int ldws) {
+      ga.lo = lo8 ? 8 : 4;
       ga.asc = asc;
       ga.lds = lds;
       ga.wsc = wsc;
+      ga.ldws = ldws;
     };
     // the O GEMM split over K like the down GEMM below, or with the gated
     // residual in its epilogue
@@ -504,11 +511,11 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
     {
       Scope sc(m, C_W13, s);
       qi21::GemmArgs ga = gemm_args(rows, 2 * I, kx, a.xn, kx, m->w13[l], a.hid, kh, p2(-gd.hid), p2(gd.ffn));
-      if (lo8) {
-        ffn_lo8(ga, a.xsc, H / 64, m->w13s[l]);
+      if (lo) {
+        ffn_lo(ga, a.xsc, sx, m->w13s[l], lo4 ? H / 32 : 0);
         ga.osc = a.hsc;
-        ga.ldos = I / 64;
-        HIP_OK(qi21::launch_gemm(qi21::EPI_SWIGLU8, ga, 0, s));
+        ga.ldos = sh;
+        HIP_OK(qi21::launch_gemm(lo8 ? qi21::EPI_SWIGLU8 : qi21::EPI_SWIGLU4, ga, 0, s));
       } else {
         ga.kw = H;
         HIP_OK(qi21::launch_gemm(pf == 2 ? qi21::EPI_SWIGLU2 : qi21::EPI_SWIGLU, ga, tile, s));
@@ -518,15 +525,16 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
     // rows), the down GEMM runs split over K into partial products and the
     // row pass adds them: x += tanh(g2) sum_p part_p, then (but in the
     // last block) the next block's xn = LN(x)(1 + s1).  Otherwise the
-    // gated residual runs in the GEMM's epilogue.  (lo8: the split falls
-    // on whole groups of 128 columns, so the count must divide I / 128.)
-    const int sp = tile < 0 ? qi21::gemm_split_count(rows, H, lo8 ? I / 2 : pf * I, 4) : 1;
+    // gated residual runs in the GEMM's epilogue.  (lo8 / lo4: the split
+    // falls on whole groups of 128 / 256 columns, so the count must divide
+    // I / 128 / I / 256; gemm_split_count sees the K with that many k-tiles.)
+    const int sp = tile < 0 ? qi21::gemm_split_count(rows, H, lo8 ? I / 2 : lo4 ? I / 4 : pf * I, 4) : 1;
     if (sp > 1 && (size_t)sp * rows <= 4 * std::min<size_t>(a.cap, 2048)) {
       {
         Scope sc(m, C_W2, s);
         qi21::GemmArgs ga = gemm_args(rows, H, kh, a.hid, kh, m->w2[l], a.part, H, p2(gd.hid));
-        if (lo8)
-          ffn_lo8(ga, a.hsc, I / 64, m->w2s[l]);
+        if (lo)
+          ffn_lo(ga, a.hsc, sh, m->w2s[l], lo4 ? I / 32 : 0);
         else
           ga.kw = I;
         ga.ksplit = sp;
@@ -541,11 +549,11 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
         Scope sc(m, C_W2, s);
         qi21::GemmArgs ga = gemm_args(rows, H, kh, a.hid, kh, m->w2[l], a.x, H, p2(gd.hid));
         ga.gate = a.mods + 3 * H;
-        if (lo8)
-          ffn_lo8(ga, a.hsc, I / 64, m->w2s[l]);
+        if (lo)
+          ffn_lo(ga, a.hsc, sh, m->w2s[l], lo4 ? I / 32 : 0);
         else
           ga.kw = I;
-        HIP_OK(qi21::launch_gemm(qi21::EPI_RESID, ga, lo8 ? 0 : tile, s));
+        HIP_OK(qi21::launch_gemm(qi21::EPI_RESID, ga, lo ? 0 : tile, s));
       }
       if (!last) {  // the next block's xn = LN(x)(1 + s1)
         Scope sc(m, C_ROW, s);
@@ -592,16 +600,18 @@ void qi21_model_destroy(qi21_model* m) {
   for (auto& p : m->progs) free_prog(m, p);
   m->progs.clear();
   free_acts(m);
-  const size_t H = m->g.hidden, I = m->g.inter, fb = ffn_row_bytes(m->o.ffn_mode == QI21_FFN_LO8 ? QI21_FFN_LO8 : 0);
+  const size_t H = m->g.hidden, I = m->g.inter;
+  const int pm = m->o.ffn_mode == QI21_FFN_PAIR ? QI21_FFN_F16 : m->o.ffn_mode;  // the planes' form
+  const size_t fb = ffn_row_nibbles(pm);
   for (int l = 0; l < m->nb; ++l) {
     dfree(m, m->wqkv[l], 3 * H * H * 2);
     dfree(m, m->wo[l], H * H * 2);
-    dfree(m, m->w13[l], 2 * I * H * fb);
-    dfree(m, m->w2[l], H * I * fb);
+    dfree(m, m->w13[l], 2 * I * H * fb / 2);
+    dfree(m, m->w2[l], H * I * fb / 2);
     dfree(m, m->nq[l], 128 * 4);
     dfree(m, m->nk[l], 128 * 4);
-    if (l < (int)m->w13s.size()) dfree(m, m->w13s[l], 2 * I);
-    if (l < (int)m->w2s.size()) dfree(m, m->w2s[l], H);
+    if (l < (int)m->w13s.size()) dfree(m, m->w13s[l], pm == QI21_FFN_LO4 ? 2 * I * H / 32 : 2 * I);
+    if (l < (int)m->w2s.size()) dfree(m, m->w2s[l], pm == QI21_FFN_LO4 ? H * I / 32 : H);
   }
   dfree(m, m->img_in, H * 64 * 4);
   dfree(m, m->proj_out, H * 64 * 4);
@@ -635,20 +645,23 @@ int qi21_model_create(const qi21_geom* geom, const qi21_options* opt, int nblock
     return fail(QI21_EINVAL, "alloc and free hooks must be given together");
   }
   if (m->o.max_programs < 1) m->o.max_programs = 1;
-  if (m->o.ffn_mode < QI21_FFN_F16 || m->o.ffn_mode > QI21_FFN_LO8) {
+  if (m->o.ffn_mode < QI21_FFN_F16 || m->o.ffn_mode > QI21_FFN_LO4) {
     const int fm = m->o.ffn_mode;
     delete m;
-    return fail(QI21_EINVAL, "ffn_mode %d (0, 1 or 2)", fm);
+    return fail(QI21_EINVAL, "ffn_mode %d (0 to 3)", fm);
   }
-  if (m->o.ffn_mode == QI21_FFN_LO8 && (geom->hidden % 256 != 0 || geom->inter % 128 != 0)) {
+  if ((m->o.ffn_mode == QI21_FFN_LO8 && (geom->hidden % 256 != 0 || geom->inter % 128 != 0)) ||
+      (m->o.ffn_mode == QI21_FFN_LO4 && (geom->hidden % 256 != 0 || geom->inter % 256 != 0))) {
+    const int fm = m->o.ffn_mode;
     delete m;
-    return fail(QI21_EUNSUPPORTED, "ffn_mode lo8 needs hidden %% 256 == 0 and inter %% 128 == 0 (hidden %d, inter %d)",
-                geom->hidden, geom->inter);
+    return fail(QI21_EUNSUPPORTED, "ffn_mode %s needs hidden %% 256 == 0 and inter %% %d == 0 (hidden %d, inter %d)",
+                fm == QI21_FFN_LO8 ? "lo8" : "lo4", fm == QI21_FFN_LO8 ? 128 : 256, geom->hidden, geom->inter);
   }
   m->nb = nblocks;
   const size_t H = geom->hidden, I = geom->inter;
-  const bool lo8 = m->o.ffn_mode == QI21_FFN_LO8;
-  const size_t fb = ffn_row_bytes(lo8 ? QI21_FFN_LO8 : 0);  // bytes per FFN plane column
+  const int pm = m->o.ffn_mode == QI21_FFN_PAIR ? QI21_FFN_F16 : m->o.ffn_mode;  // the FFN planes' form
+  const bool lop = pm == QI21_FFN_LO8 || pm == QI21_FFN_LO4;
+  const size_t fb = ffn_row_nibbles(pm);  // half-bytes per FFN plane column
   m->wqkv.assign(nblocks, nullptr);
   m->wo.assign(nblocks, nullptr);
   m->w13.assign(nblocks, nullptr);
@@ -656,23 +669,24 @@ int qi21_model_create(const qi21_geom* geom, const qi21_options* opt, int nblock
   m->nq.assign(nblocks, nullptr);
   m->nk.assign(nblocks, nullptr);
   m->set.assign(nblocks, 0);
-  if (lo8) {
+  if (lop) {
     m->w13s.assign(nblocks, nullptr);
     m->w2s.assign(nblocks, nullptr);
   }
+  const size_t s13 = pm == QI21_FFN_LO4 ? 2 * I * H / 32 : 2 * I, s2 = pm == QI21_FFN_LO4 ? H * I / 32 : H;
   bool ok = true;
   for (int l = 0; l < nblocks && ok; ++l) {
     ok = (m->wqkv[l] = (f16*)dalloc(m, 3 * H * H * 2)) && (m->wo[l] = (f16*)dalloc(m, H * H * 2)) &&
-         (m->w13[l] = (f16*)dalloc(m, 2 * I * H * fb)) && (m->w2[l] = (f16*)dalloc(m, H * I * fb)) &&
+         (m->w13[l] = (f16*)dalloc(m, 2 * I * H * fb / 2)) && (m->w2[l] = (f16*)dalloc(m, H * I * fb / 2)) &&
          (m->nq[l] = (float*)dalloc(m, 128 * 4)) && (m->nk[l] = (float*)dalloc(m, 128 * 4));
-    if (ok && lo8) ok = (m->w13s[l] = (uint8_t*)dalloc(m, 2 * I)) && (m->w2s[l] = (uint8_t*)dalloc(m, H));
+    if (ok && lop) ok = (m->w13s[l] = (uint8_t*)dalloc(m, s13)) && (m->w2s[l] = (uint8_t*)dalloc(m, s2));
   }
   ok = ok && (m->img_in = (float*)dalloc(m, H * 64 * 4)) && (m->proj_out = (float*)dalloc(m, H * 64 * 4)) &&
        (m->dflag = (int*)dalloc(m, 256));
   if (!ok) {
     qi21_model_destroy(m);
     return fail(QI21_ENOMEM, "weight planes for %d blocks (%.2f GB) did not fit", nblocks,
-                (double)nblocks * (8 * H * H + 3 * H * I * fb) / 1e9);
+                (double)nblocks * (8 * H * H + 3 * H * I * fb / 2) / 1e9);
   }
   if (hipHostMalloc((void**)&m->hflag, sizeof(int), hipHostMallocDefault) != hipSuccess) {
     m->hflag = nullptr;
@@ -707,14 +721,19 @@ int qi21_model_set_block(qi21_model* m, int layer, int w_dtype, const void* cons
   // gate/up interleaved by 32 rows: plane rows 64j + r = gate 32j + r, 64j + 32 + r = up 32j + r;
   // lo8: both FFN planes in the lo8 row form, their fp8 residual bytes and
   // per-row scales derived from the f16 values
-  const bool lo8 = m->o.ffn_mode == QI21_FFN_LO8;
-  const int ld13 = lo8 ? 3 * H / 2 : H, ld2 = lo8 ? 3 * I / 2 : I;
-  HIP_OK(qi21::launch_plane(w_dtype, w[4], I, H, m->w13[layer], 32, 64, 0, s, ld13, lo8));
-  HIP_OK(qi21::launch_plane(w_dtype, w[5], I, H, m->w13[layer], 32, 64, 32, s, ld13, lo8));
-  HIP_OK(qi21::launch_plane(w_dtype, w[6], H, I, m->w2[layer], H, 0, 0, s, ld2, lo8));
+  const bool lo8 = m->o.ffn_mode == QI21_FFN_LO8, lo4 = m->o.ffn_mode == QI21_FFN_LO4;
+  const int lo = lo8 ? 8 : lo4 ? 4 : 0;
+  const int ld13 = lo8 ? 3 * H / 2 : lo4 ? 5 * H / 4 : H, ld2 = lo8 ? 3 * I / 2 : lo4 ? 5 * I / 4 : I;
+  HIP_OK(qi21::launch_plane(w_dtype, w[4], I, H, m->w13[layer], 32, 64, 0, s, ld13, lo));
+  HIP_OK(qi21::launch_plane(w_dtype, w[5], I, H, m->w13[layer], 32, 64, 32, s, ld13, lo));
+  HIP_OK(qi21::launch_plane(w_dtype, w[6], H, I, m->w2[layer], H, 0, 0, s, ld2, lo));
   if (lo8) {
     HIP_OK(qi21::launch_plane8(2 * I, H, m->w13[layer], ld13, m->w13s[layer], s));
     HIP_OK(qi21::launch_plane8(H, I, m->w2[layer], ld2, m->w2s[layer], s));
+  }
+  if (lo4) {
+    HIP_OK(qi21::launch_plane4(2 * I, H, m->w13[layer], ld13, m->w13s[layer], H / 32, s));
+    HIP_OK(qi21::launch_plane4(H, I, m->w2[layer], ld2, m->w2s[layer], I / 32, s));
   }
   // the q norm weights carry the softmax's log2(e) / sqrt(128), so every q
   // the block produces is in the base-2 units the attention kernels take
@@ -1183,23 +1202,28 @@ int qi21_op_flash(int nq, int heads, const void* q, int ldq, const void* k1, int
 }
 
 namespace {
-// shared checks of the row-op entry points; lo8: the FFN-input form
+// shared checks of the row-op entry points; fmt: QI21_FFN_LO8 / LO4 for
+// the residual FFN-input forms, 0 for the f16 forms
 int op_rowop(int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride, void* xn, int ldxn,
-             uint8_t* xsc, const float* mods, int g_off, int s_off, float eps, float oscale, void* stream, bool lo8) {
+             uint8_t* xsc, const float* mods, int g_off, int s_off, float eps, float oscale, void* stream, int fmt) {
   if (nparts < 1 || nparts > 8 || (nparts > 1 && pstride < (size_t)rows * h))
     return fail(QI21_EINVAL, "rowop nparts %d pstride %zu", nparts, pstride);
-  const bool mode_ok = lo8 ? (mode == 2 || mode == 3) : (mode >= 1 && mode <= 7 && mode != 4 && mode != 5);
+  const bool lo = fmt == QI21_FFN_LO8 || fmt == QI21_FFN_LO4;
+  if (fmt != 0 && !lo) return fail(QI21_EINVAL, "rowop format %d (QI21_FFN_LO8 or QI21_FFN_LO4)", fmt);
+  const bool mode_ok = lo ? (mode == 2 || mode == 3) : (mode >= 1 && mode <= 7 && mode != 4 && mode != 5);
   if (rows < 1 || h < 4 || h % 4 || h > 8192 || !mode_ok || g_off % 4 || s_off % 4 || g_off < 0 || s_off < 0)
     return fail(QI21_EINVAL, "rowop rows %d h %d mode %d", rows, h, mode);
-  if (!x || !mods || ((mode & 1) && !y) || ((mode & 2) && !xn) || (lo8 && !xsc))
+  if (!x || !mods || ((mode & 1) && !y) || ((mode & 2) && !xn) || (lo && !xsc))
     return fail(QI21_EINVAL, "rowop pointer NULL");
-  if (lo8 && h % 128) return fail(QI21_EINVAL, "rowop lo8 h %d (a multiple of 128)", h);
-  // the row stride xn needs: h, 2h for the pair form, 1.5h for lo8 (in halves)
-  const long need = lo8 ? 3L * h / 2 : (mode & 4) ? 2L * h : h;
+  const int hm = fmt == QI21_FFN_LO4 ? 256 : 128;
+  if (lo && h % hm) return fail(QI21_EINVAL, "rowop %s h %d (a multiple of %d)", fmt == QI21_FFN_LO8 ? "lo8" : "lo4", h, hm);
+  // the row stride xn needs: h, 2h for the pair form, 1.5h (lo8) or 1.25h (lo4), in halves
+  const long need = fmt == QI21_FFN_LO8 ? 3L * h / 2 : fmt == QI21_FFN_LO4 ? 5L * h / 4 : (mode & 4) ? 2L * h : h;
   if ((mode & 2) && (ldxn < need || ldxn % 4))
     return fail(QI21_EINVAL, "rowop ldxn %d (at least %ld halves for mode %d, a multiple of 4)", ldxn, need, mode);
-  HIP_OK(qi21::launch_rowop(rows, h, lo8 ? mode | 8 : mode, x, y, (f16*)xn, mods, g_off, s_off, eps, oscale,
-                            (hipStream_t)stream, nparts, pstride, xsc, (mode & 2) ? ldxn : h));
+  const int bits = fmt == QI21_FFN_LO8 ? 8 : fmt == QI21_FFN_LO4 ? 16 : 0;
+  HIP_OK(qi21::launch_rowop(rows, h, mode | bits, x, y, (f16*)xn, mods, g_off, s_off, eps, oscale, (hipStream_t)stream,
+                            nparts, pstride, xsc, (mode & 2) ? ldxn : h));
   return QI21_OK;
 }
 }  // namespace
@@ -1207,49 +1231,58 @@ int op_rowop(int rows, int h, int mode, float* x, const float* y, int nparts, si
 int qi21_op_rowop(int rows, int h, int mode, float* x, const float* y, void* xn, int ldxn, const float* mods,
                   int g_off, int s_off, float eps, float oscale, void* stream) {
   g_err.clear();
-  return op_rowop(rows, h, mode, x, y, 1, 0, xn, ldxn, nullptr, mods, g_off, s_off, eps, oscale, stream, false);
+  return op_rowop(rows, h, mode, x, y, 1, 0, xn, ldxn, nullptr, mods, g_off, s_off, eps, oscale, stream, 0);
 }
 
 int qi21_op_rowop_parts(int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride, void* xn,
                         int ldxn, const float* mods, int g_off, int s_off, float eps, float oscale, void* stream) {
   g_err.clear();
-  return op_rowop(rows, h, mode, x, y, nparts, pstride, xn, ldxn, nullptr, mods, g_off, s_off, eps, oscale, stream,
-                  false);
+  return op_rowop(rows, h, mode, x, y, nparts, pstride, xn, ldxn, nullptr, mods, g_off, s_off, eps, oscale, stream, 0);
 }
 
-int qi21_op_rowop_lo8(int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride, void* xn,
-                      int ldxn, uint8_t* xsc, const float* mods, int g_off, int s_off, float eps, float oscale,
-                      void* stream) {
+int qi21_op_rowop_lo(int fmt, int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride,
+                     void* xn, int ldxn, uint8_t* xsc, const float* mods, int g_off, int s_off, float eps,
+                     float oscale, void* stream) {
   g_err.clear();
-  return op_rowop(rows, h, mode, x, y, nparts, pstride, xn, ldxn, xsc, mods, g_off, s_off, eps, oscale, stream, true);
+  if (fmt != QI21_FFN_LO8 && fmt != QI21_FFN_LO4) return fail(QI21_EINVAL, "rowop format %d", fmt);
+  return op_rowop(rows, h, mode, x, y, nparts, pstride, xn, ldxn, xsc, mods, g_off, s_off, eps, oscale, stream, fmt);
 }
 
-int qi21_op_gemm_lo8(int epi, int M, int N, int K, const void* A, int lda, const uint8_t* asc, int lds, const void* W,
-                     int ldw, const uint8_t* wsc, void* out, int ldo, const float* gate, uint8_t* osc, int ldos,
-                     int ksplit, float oscale, float inscale, void* stream) {
+int qi21_op_gemm_lo(int fmt, int epi, int M, int N, int K, const void* A, int lda, const uint8_t* asc, int lds,
+                    const void* W, int ldw, const uint8_t* wsc, int ldws, void* out, int ldo, const float* gate,
+                    uint8_t* osc, int ldos, int ksplit, float oscale, float inscale, void* stream) {
   g_err.clear();
-  if (epi != QI21_EPI_F32 && epi != QI21_EPI_RESID && epi != QI21_EPI_SWIGLU8)
-    return fail(QI21_EINVAL, "lo8 gemm epilogue %d (F32, RESID or SWIGLU8)", epi);
-  if (M < 1 || N < 256 || N % 256 || K < 128 || K % 128 || lda % 8 || ldw % 8 || lda < 3 * K / 2 || ldw < 3 * K / 2 ||
-      lds < K / 64 || lds % 2)
+  const bool l8 = fmt == QI21_FFN_LO8;
+  if (!l8 && fmt != QI21_FFN_LO4) return fail(QI21_EINVAL, "gemm format %d (QI21_FFN_LO8 or QI21_FFN_LO4)", fmt);
+  const int sw = l8 ? QI21_EPI_SWIGLU8 : QI21_EPI_SWIGLU4;
+  if (epi != QI21_EPI_F32 && epi != QI21_EPI_RESID && epi != sw)
+    return fail(QI21_EINVAL, "residual gemm epilogue %d (F32, RESID or the format's SWIGLU)", epi);
+  const int g = l8 ? 128 : 256;                    // columns per group
+  const long krow = l8 ? 3L * K / 2 : 5L * K / 4;  // halves per row
+  const int blk = l8 ? 64 : 32;                    // activation scale block
+  if (M < 1 || N < 256 || N % 256 || K < g || K % g || lda % 8 || ldw % 8 || lda < krow || ldw < krow ||
+      lds < K / blk || lds % (l8 ? 2 : 4) || (!l8 && (ldws < K / 32 || ldws % 4)))
     return fail(QI21_EINVAL,
-                "lo8 gemm M %d N %d K %d lda %d ldw %d lds %d (need N %% 256, K %% 128, lda and ldw >= 1.5 K and %% 8, "
-                "lds >= K / 64 and even)",
-                M, N, K, lda, ldw, lds);
-  if (!A || !W || !asc || !wsc || !out) return fail(QI21_EINVAL, "lo8 gemm pointer is NULL");
-  if (ksplit < 1 || ksplit > 8 || (K / 128) % ksplit || (ksplit > 1 && epi != QI21_EPI_F32))
-    return fail(QI21_EINVAL, "lo8 gemm ksplit %d (1..8, dividing K / 128; F32 only)", ksplit);
-  if (epi == QI21_EPI_RESID && (!gate || ldo < N || ldo % 4)) return fail(QI21_EINVAL, "lo8 gemm resid gate / ldo %d", ldo);
+                "residual gemm M %d N %d K %d lda %d ldw %d lds %d ldws %d (need N %% 256, K %% %d, lda and ldw >= %ld "
+                "and %% 8, lds >= K / %d, W scales per 32 columns for lo4)",
+                M, N, K, lda, ldw, lds, ldws, g, krow, blk);
+  if (!A || !W || !asc || !wsc || !out) return fail(QI21_EINVAL, "residual gemm pointer is NULL");
+  if (ksplit < 1 || ksplit > 8 || (K / g) % ksplit || (ksplit > 1 && epi != QI21_EPI_F32))
+    return fail(QI21_EINVAL, "residual gemm ksplit %d (1..8, dividing K / %d; F32 only)", ksplit, g);
+  if (epi == QI21_EPI_RESID && (!gate || ldo < N || ldo % 4)) return fail(QI21_EINVAL, "residual gemm resid gate / ldo %d", ldo);
   if (epi == QI21_EPI_F32 && (ldo < N || ldo % 4 || (ksplit > 1 && ldo != N)))
-    return fail(QI21_EINVAL, "lo8 gemm f32 ldo %d (>= N, % 4; = N when split)", ldo);
-  if (epi == QI21_EPI_SWIGLU8 && (!osc || ldo < 3 * N / 4 || ldo % 4 || ldos < N / 128 || (N / 2) % 128))
-    return fail(QI21_EINVAL, "lo8 gemm swiglu8 ldo %d (>= 0.75 N, % 4), osc, ldos %d (>= N / 128)", ldo, ldos);
-  qi21::GemmArgs a = gemm_args(M, N, 3 * K / 2, (const f16*)A, lda, (const f16*)W, out, ldo, oscale, inscale);
+    return fail(QI21_EINVAL, "residual gemm f32 ldo %d (>= N, %% 4; = N when split)", ldo);
+  const long hrow = l8 ? 3L * N / 4 : 5L * N / 8;  // halves of an output row of N/2 columns
+  if (epi == sw && (!osc || ldo < hrow || ldo % 4 || ldos < (N / 2) / blk || (N / 2) % g))
+    return fail(QI21_EINVAL, "residual gemm swiglu ldo %d (>= %ld, %% 4), osc, ldos %d (>= %d)", ldo, hrow, ldos,
+                (N / 2) / blk);
+  qi21::GemmArgs a = gemm_args(M, N, (int)krow, (const f16*)A, lda, (const f16*)W, out, ldo, oscale, inscale);
   a.ldw = ldw;
-  a.kt8 = 2;
+  a.lo = l8 ? 8 : 4;
   a.asc = asc;
   a.lds = lds;
   a.wsc = wsc;
+  a.ldws = l8 ? 0 : ldws;
   a.gate = gate;
   a.osc = osc;
   a.ldos = ldos;
@@ -1259,21 +1292,33 @@ int qi21_op_gemm_lo8(int epi, int M, int N, int K, const void* A, int lda, const
   return QI21_OK;
 }
 
-int qi21_op_plane_lo8(int src_dtype, const void* src, int rows, int cols, void* dst, int ld, int group, int gstride,
-                      int goff, void* stream) {
+int qi21_op_plane_lo(int fmt, int src_dtype, const void* src, int rows, int cols, void* dst, int ld, int group,
+                     int gstride, int goff, void* stream) {
   g_err.clear();
-  if (src_dtype < QI21_F32 || src_dtype > QI21_F16 || rows < 1 || cols < 128 || cols % 128 || ld < 3 * cols / 2 ||
-      ld % 4 || group < 1 || gstride < 0 || goff < 0 || !src || !dst)
-    return fail(QI21_EINVAL, "lo8 plane arguments (cols %% 128, ld >= 1.5 cols and %% 4)");
-  HIP_OK(qi21::launch_plane(src_dtype, src, rows, cols, (f16*)dst, group, gstride, goff, (hipStream_t)stream, ld, true));
+  const bool l8 = fmt == QI21_FFN_LO8;
+  if (!l8 && fmt != QI21_FFN_LO4) return fail(QI21_EINVAL, "plane format %d", fmt);
+  const int g = l8 ? 128 : 256;
+  const long need = l8 ? 3L * cols / 2 : 5L * cols / 4;
+  if (src_dtype < QI21_F32 || src_dtype > QI21_F16 || rows < 1 || cols < g || cols % g || ld < need || ld % 4 ||
+      group < 1 || gstride < 0 || goff < 0 || !src || !dst)
+    return fail(QI21_EINVAL, "residual plane arguments (cols %% %d, ld >= %ld and %% 4)", g, need);
+  HIP_OK(qi21::launch_plane(src_dtype, src, rows, cols, (f16*)dst, group, gstride, goff, (hipStream_t)stream, ld,
+                            l8 ? 8 : 4));
   return QI21_OK;
 }
 
-int qi21_op_plane8(int rows, int cols, void* plane, int ld, uint8_t* sc, void* stream) {
+int qi21_op_plane_lo_fill(int fmt, int rows, int cols, void* plane, int ld, uint8_t* sc, int ldsc, void* stream) {
   g_err.clear();
-  if (rows < 1 || cols < 128 || cols % 128 || ld < 3 * cols / 2 || ld % 4 || !plane || !sc)
-    return fail(QI21_EINVAL, "plane8 rows %d cols %d ld %d", rows, cols, ld);
-  HIP_OK(qi21::launch_plane8(rows, cols, (f16*)plane, ld, sc, (hipStream_t)stream));
+  const bool l8 = fmt == QI21_FFN_LO8;
+  if (!l8 && fmt != QI21_FFN_LO4) return fail(QI21_EINVAL, "plane format %d", fmt);
+  const int g = l8 ? 128 : 256;
+  const long need = l8 ? 3L * cols / 2 : 5L * cols / 4;
+  if (rows < 1 || cols < g || cols % g || ld < need || ld % 4 || !plane || !sc || (!l8 && ldsc < cols / 32))
+    return fail(QI21_EINVAL, "residual plane fill rows %d cols %d ld %d ldsc %d", rows, cols, ld, ldsc);
+  if (l8)
+    HIP_OK(qi21::launch_plane8(rows, cols, (f16*)plane, ld, sc, (hipStream_t)stream));
+  else
+    HIP_OK(qi21::launch_plane4(rows, cols, (f16*)plane, ld, sc, ldsc, (hipStream_t)stream));
   return QI21_OK;
 }
 

@@ -19,7 +19,7 @@ constexpr int wait_imm(int vm, int lgkm) {
 }
 
 enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 4, EPI_QKROPE = 5, EPI_VT = 6,
-           EPI_RESID = 7, EPI_GELU = 8, EPI_SWIGLU8 = 9 };
+           EPI_RESID = 7, EPI_GELU = 8, EPI_SWIGLU8 = 9, EPI_SWIGLU4 = 10 };
 
 // C = A * W^T over f16 operands with f32 accumulation.
 //   A: [M][lda] f16 (K contiguous), W: [N][kw] f16 (kw contiguous); column
@@ -32,11 +32,11 @@ enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 
 //               columns = silu(g*inscale) * (u*inscale) * oscale
 //   EPI_SWIGLU2: as EPI_SWIGLU, the value h written as the pair
 //               out[r][c] = f16(h), out[r][N/2 + c] = f16(h - f16(h))
-//   EPI_SWIGLU8: as EPI_SWIGLU, h written in the lo8 row form (lo8.h):
-//               out row r (ldo halves) holds f16(h) and e4m3((h - f16(h))
-//               2^-e) of its N/2 columns, grouped by 128, with e per (row,
-//               64-column block) in osc[r * ldos + c / 64].  Large-M 4-wave
-//               kernel only.
+//   EPI_SWIGLU8 / EPI_SWIGLU4: as EPI_SWIGLU, h written in the lo8 / lo4
+//               row form (lores.h): out row r (ldo halves) holds f16(h) and
+//               the scaled residuals of its N/2 columns, with the scales in
+//               osc[r * ldos + ...] (per 64 columns / per 32 in the lo4
+//               order).  Large-M 4-wave kernel only.
 //   EPI_QKROPE: N = 2H, W = the q then k projection rows; per row and
 //               128-column head: RMSNorm of the accumulators (weights nq for
 //               q heads, nk for k heads, eps in the accumulators' scale),
@@ -53,13 +53,15 @@ enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 
 //   EPI_QKV:    columns [0, 2H) -> out f16 [M][ldo] (q|k), columns [2H, 3H)
 //               -> out2 f16 transposed, out2[c - 2H][row] with leading
 //               dimension ld2 (V^T), both * oscale; H = N/3.
-// lo8 operands (kt8 = 2; large-M 4-wave kernel, row-layout epilogues): A
-// and W rows are in the lo8 row form (lo8.h), K counting the halves of the
-// whole row (1.5 times the columns), so of every three k-tiles the first
-// two are f16 and the third their e4m3 residuals, multiplied on the scaled
-// fp8 MFMA.  A's residuals of row r, columns [64 g, 64 g + 64) are scaled
-// by 2^(b - 127), b = asc[r * lds + g]; W row n's by 2^(b - 127), b =
-// wsc[n].  kw = K (no wrap), ldw the W row stride.
+// Residual operands (lo = 8 or 4; large-M 4-wave kernel, row-layout
+// epilogues): A and W rows are in the lo8 / lo4 row form (lores.h), K
+// counting the halves of the whole row (1.5 / 1.25 times the columns), so
+// of every 3 / 5 k-tiles the last holds the residuals of the columns the
+// others hold as halves, multiplied on the scaled fp8 / fp4 MFMA.  Scales:
+// lo8, A row r's residuals of columns [64 g, 64 g + 64) by asc[r * lds +
+// g], W row n's by wsc[n]; lo4, per row and 32 columns in the lo4 order,
+// asc[r * lds + ...] and wsc[n * ldws + ...].  kw = K (no wrap), ldw the
+// W row stride.
 // Assumes: N % 128 == 0, K % 64 == 0, kw % 64 == 0, K % kw == 0, M >= 1,
 // 16-byte aligned rows (lda a multiple of 8), for EPI_QKV N/3 % 128 == 0
 // and ld2 >= M.
@@ -68,10 +70,10 @@ struct GemmArgs {
   const f16* A; int lda;
   const f16* W; int kw;
   int ldw = 0;  // W row stride in halves (0: kw)
-  // lo8 (see above): 2 (every third k-tile is fp8), or a large value: none
-  int kt8 = 1 << 30;
+  // residual operands (see above): 0 none, 8 lo8, 4 lo4
+  int lo = 0;
   const uint8_t* asc = nullptr; int lds = 0;
-  const uint8_t* wsc = nullptr;
+  const uint8_t* wsc = nullptr; int ldws = 0;
   // EPI_SWIGLU8 output scales
   uint8_t* osc = nullptr; int ldos = 0;
   void* out; int ldo;
@@ -125,9 +127,12 @@ hipError_t launch_flash(const FlashArgs* segs, int nseg, hipStream_t s);
 //   mode & 4: (with & 2) xn is [rows][2h]: the value v as the pair
 //             xn[r][c] = f16(v), xn[r][h + c] = f16(v - f16(v))
 //   mode & 8: (with & 2, not with & 4) xn rows of 3h bytes in the lo8 row
-//             form (lo8.h): f16(v) and e4m3((v - f16(v)) 2^-e), e per 64
+//             form (lores.h): f16(v) and e4m3((v - f16(v)) 2^-e), e per 64
 //             columns in xsc[r * (h / 64) + c / 64] (E8M0); h % 128 == 0
-// ldxn: xn's row stride in halves (0: h, 2h or 1.5h as the mode implies;
+//   mode & 16: (with & 2 only) the lo4 row form, rows of 2.5h bytes, e per
+//             32 columns in xsc[r * (h / 32) + ...] in the lo4 order;
+//             h % 256 == 0
+// ldxn: xn's row stride in halves (0: h, 2h, 1.5h or 1.25h as the mode implies;
 // otherwise at least that, and a multiple of 4)
 hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16* xn,
                         const float* mods, int g_off, int s_off, float eps, float oscale,
@@ -167,10 +172,16 @@ hipError_t launch_mods(int h, const float* mods, float* mods_dev, hipStream_t s)
 
 // Weight conversion to f16: dst row (r / group) * gstride + goff + r % group
 // (ld = cols) receives source row r.  src_dtype 0 f32, 1 bf16, 2 f16.
-// ldd: dst row stride in halves (0: cols); lo8: dst rows in the lo8 row
-// form (f16 values at their lo8.h positions; cols % 128 == 0).
+// ldd: dst row stride in halves (0: cols); lo = 8 / 4: dst rows in the
+// lo8 / lo4 row form (f16 values at their lores.h positions; cols % 128 /
+// 256 == 0).
 hipError_t launch_plane(int src_dtype, const void* src, int rows, int cols, f16* dst, int group,
-                        int gstride, int goff, hipStream_t s, int ldd = 0, bool lo8 = false);
+                        int gstride, int goff, hipStream_t s, int ldd = 0, int lo = 0);
+// The fp4 part of a lo4 weight plane whose f16 values are set: per row and
+// 32-column block, e with the block's largest |w| 2^-e <= 6 (the smallest
+// such), the residual nibbles e2m1(w 2^-e) and the scale byte e + 127 at
+// sc[r * ldsc + ...] in the lo4 order.  cols % 256 == 0.
+hipError_t launch_plane4(int rows, int cols, f16* plane, int ld, uint8_t* sc, int ldsc, hipStream_t s);
 // The fp8 part of a lo8 weight plane (rows of ld halves in the lo8 row
 // form whose f16 values are set): each row's residual bytes become
 // e4m3(w 2^-e), w the f16 value, e per row such that the row's largest

@@ -8,7 +8,7 @@
 // 4-byte-per-lane fully coalesced loads; reductions are wave64 shuffles
 // followed by one LDS exchange between the waves of a block.
 #include "qi21_internal.h"
-#include "lo8.h"
+#include "lores.h"
 
 namespace qi21 {
 
@@ -36,7 +36,7 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 }
 
 // mode & 8 of the row ops: chunk c (float4 c of the row, 4c .. 4c+3) of
-// the value r written in the lo8 row form (lo8.h) to row bytes xb; the
+// the value r written in the lo8 row form (lores.h) to row bytes xb; the
 // 16 lanes holding one 64-column block (consecutive lanes, whole groups
 // active or not) share its scale, which the first of them stores
 __device__ __forceinline__ void lo8_store(bool act, int c, float4v r, uint8_t* __restrict__ xb,
@@ -53,6 +53,25 @@ __device__ __forceinline__ void lo8_store(bool act, int c, float4v r, uint8_t* _
     const float4v v = lo * __builtin_ldexpf(1.0f, -ex);
     *reinterpret_cast<unsigned*>(xb + lo8_lo_at(e0)) = pack_e4m3(v[0], v[1], v[2], v[3]);
     if ((c & 15) == 0) scrow[e0 >> 6] = (uint8_t)(ex + 127);
+  }
+}
+
+// mode & 16: the same in the lo4 row form, the 8 lanes of a 32-column
+// block sharing its scale
+__device__ __forceinline__ void lo4_store(bool act, int c, float4v r, uint8_t* __restrict__ xb,
+                                          uint8_t* __restrict__ scrow) {
+  const half4 hi = half4{(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
+  const float4v lo = r - float4v{(float)hi[0], (float)hi[1], (float)hi[2], (float)hi[3]};  // exact in f32
+  float mx = act ? fmaxf(fmaxf(fabsf(lo[0]), fabsf(lo[1])), fmaxf(fabsf(lo[2]), fabsf(lo[3]))) : 0.0f;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const int ex = lo4_exp(mx);
+  if (act) {
+    const int e0 = 4 * c;
+    *reinterpret_cast<half4*>(xb + 2 * lo4_hi_at(e0)) = hi;
+    const float4v v = lo * __builtin_ldexpf(1.0f, -ex);
+    *reinterpret_cast<uint16_t*>(xb + lo4_lo_at(e0)) = (uint16_t)pack_e2m1(v[0], v[1], v[2], v[3]);
+    if ((c & 7) == 0) scrow[lo4_sc_at(e0)] = (uint8_t)(ex + 127);
   }
 }
 
@@ -101,7 +120,7 @@ __global__ __launch_bounds__(256) void rowop_kernel(int rows, int h, float* __re
       q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
     }
   const float inv = rsqrtf(wave_sum(q) / (float)h + eps);
-  if constexpr ((MODE & 8) != 0) {
+  if constexpr ((MODE & 24) != 0) {
     uint8_t* xb = reinterpret_cast<uint8_t*>(xn + (size_t)row * ldxn);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -109,7 +128,10 @@ __global__ __launch_bounds__(256) void rowop_kernel(int rows, int h, float* __re
       const bool act = c < nc;
       float4v r = float4v{0.0f, 0.0f, 0.0f, 0.0f};
       if (act) r = (v[j] - mean) * inv * (1.0f + reinterpret_cast<const float4v*>(mods + s_off)[c]) * oscale;
-      lo8_store(act, c, r, xb, xsc + (size_t)row * (h >> 6));
+      if constexpr ((MODE & 8) != 0)
+        lo8_store(act, c, r, xb, xsc + (size_t)row * (h >> 6));
+      else
+        lo4_store(act, c, r, xb, xsc + (size_t)row * (h >> 5));
     }
     return;
   }
@@ -289,7 +311,7 @@ __global__ __launch_bounds__(256) void rowop_wide_kernel(int rows, int h, float*
       q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
     }
   const float inv = rsqrtf(block_sum256(q, red) / (float)h + eps);
-  if constexpr ((MODE & 8) != 0) {
+  if constexpr ((MODE & 24) != 0) {
     uint8_t* xb = reinterpret_cast<uint8_t*>(xn + (size_t)row * ldxn);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -297,7 +319,10 @@ __global__ __launch_bounds__(256) void rowop_wide_kernel(int rows, int h, float*
       const bool act = c < nc;
       float4v r = float4v{0.0f, 0.0f, 0.0f, 0.0f};
       if (act) r = (v[j] - mean) * inv * (1.0f + reinterpret_cast<const float4v*>(mods + s_off)[c]) * oscale;
-      lo8_store(act, c, r, xb, xsc + (size_t)row * (h >> 6));
+      if constexpr ((MODE & 8) != 0)
+        lo8_store(act, c, r, xb, xsc + (size_t)row * (h >> 6));
+      else
+        lo4_store(act, c, r, xb, xsc + (size_t)row * (h >> 5));
     }
     return;
   }
@@ -333,6 +358,8 @@ hipError_t launch_rowop_wide_np(int rows, int h, int mode, float* x, const float
     case 7: hipLaunchKernelGGL((rowop_wide_kernel<7, NJ, NP>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
     case 10: hipLaunchKernelGGL((rowop_wide_kernel<10, NJ, NP>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
     case 11: hipLaunchKernelGGL((rowop_wide_kernel<11, NJ, NP>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 18: hipLaunchKernelGGL((rowop_wide_kernel<18, NJ, NP>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 19: hipLaunchKernelGGL((rowop_wide_kernel<19, NJ, NP>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -368,6 +395,8 @@ hipError_t launch_rowop_nj(int rows, int h, int mode, float* x, const float* y, 
     case 7: hipLaunchKernelGGL((rowop_kernel<7, NJ>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
     case 10: hipLaunchKernelGGL((rowop_kernel<10, NJ>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
     case 11: hipLaunchKernelGGL((rowop_kernel<11, NJ>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 18: hipLaunchKernelGGL((rowop_kernel<18, NJ>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
+    case 19: hipLaunchKernelGGL((rowop_kernel<19, NJ>), grid, block, 0, s, QI21_ROWOP_ARGS); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -379,8 +408,9 @@ hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16
                         int g_off, int s_off, float eps, float oscale, hipStream_t s, int nparts, size_t pstride,
                         uint8_t* xsc, int ldxn) {
   if (rows <= 0) return hipSuccess;
-  if ((mode & 8) && (!xsc || h % 128 != 0 || (mode & 4) || !(mode & 2))) return hipErrorInvalidValue;
-  if (!ldxn) ldxn = (mode & 4) ? 2 * h : (mode & 8) ? 3 * h / 2 : h;
+  if ((mode & 8) && (!xsc || h % 128 != 0 || (mode & 20) || !(mode & 2))) return hipErrorInvalidValue;
+  if ((mode & 16) && (!xsc || h % 256 != 0 || (mode & 12) || !(mode & 2))) return hipErrorInvalidValue;
+  if (!ldxn) ldxn = (mode & 4) ? 2 * h : (mode & 8) ? 3 * h / 2 : (mode & 16) ? 5 * h / 4 : h;
 #define QI21_LAUNCH_ARGS rows, h, mode, x, y, nparts, pstride, xn, ldxn, mods, g_off, s_off, eps, oscale, xsc, s
   if (h <= 1024) return launch_rowop_nj<4>(QI21_LAUNCH_ARGS);
   // the block-per-row form for wide rows, except on long passes that also
@@ -705,7 +735,7 @@ hipError_t launch_mods(int h, const float* mods, float* mods_dev, hipStream_t s)
 }
 
 __global__ void plane_kernel(int src_dtype, const void* __restrict__ src, int rows, int cols, f16* __restrict__ dst,
-                             int group, int gstride, int goff, int ldd, int lo8) {
+                             int group, int gstride, int goff, int ldd, int lo) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (size_t)rows * cols) return;
   const int r = (int)(i / cols), c = (int)(i - (size_t)r * cols);
@@ -719,15 +749,16 @@ __global__ void plane_kernel(int src_dtype, const void* __restrict__ src, int ro
     v = (float)reinterpret_cast<const f16*>(src)[i];
   }
   const int dr = (r / group) * gstride + goff + r % group;
-  dst[(size_t)dr * ldd + (lo8 ? lo8_hi_at(c) : c)] = (f16)v;
+  dst[(size_t)dr * ldd + (lo == 8 ? lo8_hi_at(c) : lo == 4 ? lo4_hi_at(c) : c)] = (f16)v;
 }
 
 hipError_t launch_plane(int src_dtype, const void* src, int rows, int cols, f16* dst, int group, int gstride,
-                        int goff, hipStream_t s, int ldd, bool lo8) {
+                        int goff, hipStream_t s, int ldd, int lo) {
   const size_t n = (size_t)rows * cols;
-  if (lo8 && cols % 128 != 0) return hipErrorInvalidValue;
+  if ((lo == 8 && cols % 128 != 0) || (lo == 4 && cols % 256 != 0) || (lo != 0 && lo != 8 && lo != 4))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(plane_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src_dtype, src, rows, cols,
-                     dst, group, gstride, goff, ldd ? ldd : cols, lo8 ? 1 : 0);
+                     dst, group, gstride, goff, ldd ? ldd : cols, lo);
   return hipGetLastError();
 }
 
@@ -758,6 +789,41 @@ __global__ __launch_bounds__(256) void plane8_kernel(int cols, f16* __restrict__
         pack_e4m3((float)w[0] * inv, (float)w[1] * inv, (float)w[2] * inv, (float)w[3] * inv);
   }
   if (t == 0) sc[row] = (uint8_t)(ex + 127);
+}
+
+// One 256-thread block per row of a lo4 weight plane: per 32-column block
+// (8 consecutive threads) the largest |w| of its f16 values, then the
+// block's e2m1 copy w 2^-e and its E8M0 scale in the lo4 order.
+__global__ __launch_bounds__(256) void plane4_kernel(int cols, f16* __restrict__ plane, int ld,
+                                                     uint8_t* __restrict__ sc, int ldsc) {
+  const int row = blockIdx.x, t = threadIdx.x;
+  f16* pr = plane + (size_t)row * ld;
+  uint8_t* pb = reinterpret_cast<uint8_t*>(pr);
+  uint8_t* sr = sc + (size_t)row * ldsc;
+  for (int c0 = 0; c0 < cols; c0 += 1024) {
+    // (cols % 256 == 0: whole waves are active or not)
+    const int c = c0 + 4 * t;
+    const bool act = c < cols;
+    half4 w = half4{(f16)0.0f, (f16)0.0f, (f16)0.0f, (f16)0.0f};
+    if (act) w = *reinterpret_cast<const half4*>(pr + lo4_hi_at(c));
+    float mx = fmaxf(fmaxf(fabsf((float)w[0]), fabsf((float)w[1])), fmaxf(fabsf((float)w[2]), fabsf((float)w[3])));
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const int ex = lo4_exp(mx);
+    if (act) {
+      const float inv = __builtin_ldexpf(1.0f, -ex);
+      *reinterpret_cast<uint16_t*>(pb + lo4_lo_at(c)) =
+          (uint16_t)pack_e2m1((float)w[0] * inv, (float)w[1] * inv, (float)w[2] * inv, (float)w[3] * inv);
+      if ((t & 7) == 0) sr[lo4_sc_at(c)] = (uint8_t)(ex + 127);
+    }
+  }
+}
+
+hipError_t launch_plane4(int rows, int cols, f16* plane, int ld, uint8_t* sc, int ldsc, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (cols % 256 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(plane4_kernel, dim3(rows), dim3(256), 0, s, cols, plane, ld, sc, ldsc);
+  return hipGetLastError();
 }
 
 hipError_t launch_plane8(int rows, int cols, f16* plane, int ld, uint8_t* sc, hipStream_t s) {

@@ -21,8 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libqi21.so")
 QI21_OK, QI21_EINVAL, QI21_EUNSUPPORTED, QI21_ENOMEM, QI21_ENOKEY, QI21_ENONFINITE, QI21_EDEVICE = range(7)
 QI21_F32, QI21_BF16, QI21_F16 = 0, 1, 2
 QI21_EPI_F16, QI21_EPI_F32, QI21_EPI_SWIGLU, QI21_EPI_QKV, QI21_EPI_SWIGLU2 = 0, 1, 2, 3, 4
-QI21_EPI_RESID, QI21_EPI_SWIGLU8 = 7, 9
-QI21_FFN_F16, QI21_FFN_PAIR, QI21_FFN_LO8 = 0, 1, 2
+QI21_EPI_RESID, QI21_EPI_SWIGLU8, QI21_EPI_SWIGLU4 = 7, 9, 10
+QI21_FFN_F16, QI21_FFN_PAIR, QI21_FFN_LO8, QI21_FFN_LO4 = 0, 1, 2, 3
 PROFILE_CLASSES = ("qkv", "qkrope", "flash", "o", "gate_up", "down", "rowop", "io")
 
 C = ctypes
@@ -82,12 +82,13 @@ _SIGS = {
                                      vp]),
     "qi21_op_rowop_parts": (C.c_int, [C.c_int, C.c_int, C.c_int, vp, vp, C.c_int, C.c_size_t, vp, C.c_int, vp,
                                       C.c_int, C.c_int, f32, f32, vp]),
-    "qi21_op_rowop_lo8": (C.c_int, [C.c_int, C.c_int, C.c_int, vp, vp, C.c_int, C.c_size_t, vp, C.c_int, vp, vp,
-                                    C.c_int, C.c_int, f32, f32, vp]),
-    "qi21_op_gemm_lo8": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, C.c_int, vp, C.c_int, vp, vp,
-                                   C.c_int, vp, vp, C.c_int, C.c_int, f32, f32, vp]),
-    "qi21_op_plane_lo8": (C.c_int, [C.c_int, vp, C.c_int, C.c_int, vp, C.c_int, C.c_int, C.c_int, C.c_int, vp]),
-    "qi21_op_plane8": (C.c_int, [C.c_int, C.c_int, vp, C.c_int, vp, vp]),
+    "qi21_op_rowop_lo": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, vp, C.c_int, C.c_size_t, vp, C.c_int, vp,
+                                   vp, C.c_int, C.c_int, f32, f32, vp]),
+    "qi21_op_gemm_lo": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, C.c_int, vp, C.c_int,
+                                  vp, C.c_int, vp, C.c_int, vp, vp, C.c_int, C.c_int, f32, f32, vp]),
+    "qi21_op_plane_lo": (C.c_int, [C.c_int, C.c_int, vp, C.c_int, C.c_int, vp, C.c_int, C.c_int, C.c_int, C.c_int,
+                                   vp]),
+    "qi21_op_plane_lo_fill": (C.c_int, [C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, C.c_int, vp]),
     "qi21_op_gemm_resid": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, f32,
                                      C.c_int, vp]),
     "qi21_op_qk_gemm": (C.c_int, [C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, C.c_int, vp, vp, vp, f32,
@@ -331,25 +332,25 @@ def qi21_op_rowop(rows, h, mode, x, y, xn, ldxn, mods, g_off, s_off, eps, oscale
                                _stream(stream)))
 
 
-def qi21_op_rowop_lo8(rows, h, mode, x, y, nparts, pstride, xn, ldxn, xsc, mods, g_off, s_off, eps, oscale,
-                      stream=None):
-    _check(lib().qi21_op_rowop_lo8(rows, h, mode, _p(x), _p(y), nparts, pstride, _p(xn), ldxn, _p(xsc), _p(mods),
-                                   g_off, s_off, eps, oscale, _stream(stream)))
+def qi21_op_rowop_lo(fmt, rows, h, mode, x, y, nparts, pstride, xn, ldxn, xsc, mods, g_off, s_off, eps, oscale,
+                     stream=None):
+    _check(lib().qi21_op_rowop_lo(fmt, rows, h, mode, _p(x), _p(y), nparts, pstride, _p(xn), ldxn, _p(xsc), _p(mods),
+                                  g_off, s_off, eps, oscale, _stream(stream)))
 
 
-def qi21_op_gemm_lo8(epi, M, N, K, A, lda, asc, lds, W, ldw, wsc, out, ldo, gate=None, osc=None, ldos=0, ksplit=1,
-                     oscale=1.0, inscale=1.0, stream=None):
-    _check(lib().qi21_op_gemm_lo8(epi, M, N, K, _p(A), lda, _p(asc), lds, _p(W), ldw, _p(wsc), _p(out), ldo, _p(gate),
-                                  _p(osc), ldos, ksplit, oscale, inscale, _stream(stream)))
+def qi21_op_gemm_lo(fmt, epi, M, N, K, A, lda, asc, lds, W, ldw, wsc, ldws, out, ldo, gate=None, osc=None, ldos=0,
+                    ksplit=1, oscale=1.0, inscale=1.0, stream=None):
+    _check(lib().qi21_op_gemm_lo(fmt, epi, M, N, K, _p(A), lda, _p(asc), lds, _p(W), ldw, _p(wsc), ldws, _p(out), ldo,
+                                 _p(gate), _p(osc), ldos, ksplit, oscale, inscale, _stream(stream)))
 
 
-def qi21_op_plane_lo8(src_dtype, src, rows, cols, dst, ld, group, gstride, goff, stream=None):
-    _check(lib().qi21_op_plane_lo8(src_dtype, _p(src), rows, cols, _p(dst), ld, group, gstride, goff,
-                                   _stream(stream)))
+def qi21_op_plane_lo(fmt, src_dtype, src, rows, cols, dst, ld, group, gstride, goff, stream=None):
+    _check(lib().qi21_op_plane_lo(fmt, src_dtype, _p(src), rows, cols, _p(dst), ld, group, gstride, goff,
+                                  _stream(stream)))
 
 
-def qi21_op_plane8(rows, cols, plane, ld, sc, stream=None):
-    _check(lib().qi21_op_plane8(rows, cols, _p(plane), ld, _p(sc), _stream(stream)))
+def qi21_op_plane_lo_fill(fmt, rows, cols, plane, ld, sc, ldsc=0, stream=None):
+    _check(lib().qi21_op_plane_lo_fill(fmt, rows, cols, _p(plane), ld, _p(sc), ldsc, _stream(stream)))
 
 
 def qi21_op_qkrope(rows, heads, panel, ldp, norm_q, norm_k, cos, sin, eps, kdst=None, ldk=0, stream=None):

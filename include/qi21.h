@@ -82,14 +82,20 @@ typedef void (*qi21_free_fn)(void* ptr, void* ctx);
  *     f16 one, and the residual products run on gfx950's scaled fp8 MFMA
  *     (1.35x the step's GEMM work in MFMA cycles).  Storage error about
  *     2^-16 of the value.  Needs hidden % 256 == 0 and inter % 128 == 0
- *     (EUNSUPPORTED otherwise). */
-enum { QI21_FFN_F16 = 0, QI21_FFN_PAIR = 1, QI21_FFN_LO8 = 2 };
+ *     (EUNSUPPORTED otherwise).
+ *   QI21_FFN_LO4 (3): as LO8 with the residual and the planes' narrow copy
+ *     in fp4 (e2m1) scaled per 32 columns (the MX block), on the scaled fp4
+ *     MFMA at twice the fp8 rate (1.17x the step's GEMM work in MFMA
+ *     cycles).  Storage error about 2^-14 of the value.  Needs hidden and
+ *     inter % 256 == 0.
+ * The residual forms' layouts are described in qi21_ops.h. */
+enum { QI21_FFN_F16 = 0, QI21_FFN_PAIR = 1, QI21_FFN_LO8 = 2, QI21_FFN_LO4 = 3 };
 typedef struct {
   int32_t shift_attn, shift_qkv, shift_ao, shift_ffn, shift_hid;
   int32_t max_programs;
   int32_t profile;
   int32_t gemm_tile; /* -1 = per-shape choice; otherwise a fixed GEMM tile id */
-  int32_t ffn_mode;  /* QI21_FFN_F16 / QI21_FFN_PAIR / QI21_FFN_LO8, see above */
+  int32_t ffn_mode;  /* QI21_FFN_F16 / _PAIR / _LO8 / _LO4, see above */
   qi21_alloc_fn alloc;
   qi21_free_fn free;
   void* alloc_ctx;

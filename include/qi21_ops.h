@@ -20,7 +20,7 @@ extern "C" {
 #endif
 
 enum { QI21_EPI_F16 = 0, QI21_EPI_F32 = 1, QI21_EPI_SWIGLU = 2, QI21_EPI_QKV = 3, QI21_EPI_SWIGLU2 = 4,
-       QI21_EPI_RESID = 7, QI21_EPI_SWIGLU8 = 9 };
+       QI21_EPI_RESID = 7, QI21_EPI_SWIGLU8 = 9, QI21_EPI_SWIGLU4 = 10 };
 
 /* out = A W^T ([QI] lin; the four projection sites of [WG] blocks):
  * A f16 [M][lda] (K contiguous), W f16 [N][K].  Epilogues:
@@ -147,60 +147,78 @@ int qi21_op_rowop(int rows, int h, int mode, float* x, const float* y, void* xn,
 int qi21_op_rowop_parts(int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride, void* xn,
                         int ldxn, const float* mods, int g_off, int s_off, float eps, float oscale, void* stream);
 
-/* The lo8 operand form (QI21_FFN_LO8, qi21.h).  Columns are grouped by
- * 128: group g of a row takes 384 bytes, 128 halves (halves offset 192 g +
- * c % 128) and then 128 fp8 bytes in OCP e4m3 (byte offset 384 g + 256 +
- * c % 128).  Scales are E8M0 bytes b, the factor 2^(b - 127), chosen so
- * that a block's largest |value| / factor lies in [128, 256).
- *   Activation rows: the halves hold hi = f16(v) and the bytes the
- *   residual (v - hi) / factor, one scale per row and 64 columns; the row
- *   represents hi + e4m3 * factor, about 2^-16 of v from v.
- *   Weight rows: the halves hold the weight w in f16 and the bytes an fp8
- *   copy w / factor, one scale per row. */
-/* qi21_op_rowop_parts writing xn in the lo8 form: mode 2 or 3 (bits 0 and
- * 1 as above), h % 128 == 0, xn rows of ldxn halves (ldxn >= 1.5 h, % 4),
- * and one scale per row and 64 columns in xsc [rows][h / 64] (row stride
- * h / 64 bytes).  Otherwise as qi21_op_rowop_parts. */
-int qi21_op_rowop_lo8(int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride, void* xn,
-                      int ldxn, uint8_t* xsc, const float* mods, int g_off, int s_off, float eps, float oscale,
-                      void* stream);
+/* The residual operand forms (QI21_FFN_LO8 and QI21_FFN_LO4, qi21.h): a
+ * float value v is kept as hi = f16(v) plus its residual in a narrow float
+ * times a power-of-two scale.  Scales are E8M0 bytes b, the factor 2^(b -
+ * 127).
+ *   lo8: columns grouped by 128: group g of a row takes 384 bytes, 128
+ *   halves (halves offset 192 g + c % 128) and then 128 OCP e4m3 (fp8)
+ *   bytes (byte offset 384 g + 256 + c % 128).  Scales chosen so that a
+ *   block's largest |value| / factor lies in [128, 256).
+ *   lo4: columns grouped by 256: group g takes 640 bytes, 256 halves
+ *   (halves offset 320 g + c % 256) and then 128 bytes of e2m1 (fp4)
+ *   values, two per byte, column c (even) in the low nibble of byte 640 g +
+ *   512 + (c % 256) / 2.  One scale per 32 columns, the smallest with the
+ *   block's largest |value| / factor <= 6, at scale byte 8 g + 4 (b % 2) +
+ *   b / 2 of the row for the block b = (c % 256) / 32 of group g.
+ *   Activation rows: the halves hold hi = f16(v) and the narrow values the
+ *   residual (v - hi) / factor; lo8 has one scale per row and 64 columns
+ *   (byte c / 64), lo4 one per 32.  The row represents hi + narrow *
+ *   factor, about 2^-16 (lo8) or 2^-14 (lo4) of v from v.
+ *   Weight rows: the halves hold w in f16 and the narrow values a copy
+ *   w / factor; lo8 has one scale per row, lo4 one per 32 columns.
+ * fmt below is QI21_FFN_LO8 or QI21_FFN_LO4. */
 
-/* out = A W^T over operands in the lo8 form ([QI] lin, the FFN sites of
- * [WG] blocks, with the QI21_FFN_LO8 storage of qi21.h): A holds M
+/* qi21_op_rowop_parts writing xn in a residual form: mode 2 or 3 (bits 0
+ * and 1 as above), h % 128 (lo8) / 256 (lo4) == 0, xn rows of ldxn halves
+ * (ldxn >= 1.5 h / 1.25 h, % 4), and the scales in xsc [rows][h / 64]
+ * (lo8) / [rows][h / 32] (lo4).  Otherwise as qi21_op_rowop_parts. */
+int qi21_op_rowop_lo(int fmt, int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride,
+                     void* xn, int ldxn, uint8_t* xsc, const float* mods, int g_off, int s_off, float eps,
+                     float oscale, void* stream);
+
+/* out = A W^T over operands in a residual form ([QI] lin, the FFN sites of
+ * [WG] blocks, with the storage of qi21.h's ffn_mode): A holds M
  * activation rows of lda halves, W N weight rows of ldw halves, each with
- * K columns in the lo8 form (lda, ldw >= 1.5 K, % 8); asc [M][lds] bytes
- * are A's scales per row and 64 columns, wsc [N] W's per row.  Computes,
- * in f32 on f16 and scaled fp8 MFMAs,
- *   acc[m][n] = sum_k hiA[m][k] w[n][k] + sum_k resA[m][k] w8[n][k]
- * with resA and w8 the scaled fp8 values (the residual meets the weight's
- * fp8 copy).  Epilogues:
+ * K columns in the form (lda, ldw >= 1.5 K (lo8) / 1.25 K (lo4), % 8); asc
+ * [M][lds] bytes are A's scales (lds >= K / 64 and even, or K / 32 and a
+ * multiple of 4), wsc W's: [N] for lo8, [N][ldws] for lo4 (ldws >= K /
+ * 32, % 4).  Computes, in f32 on f16 and scaled fp8 / fp4 MFMAs,
+ *   acc[m][n] = sum_k hiA[m][k] w[n][k] + sum_k resA[m][k] wq[n][k]
+ * with resA and wq the scaled narrow values (the residual meets the
+ * weight's narrow copy).  Epilogues:
  *   F32:     out f32 [M][ldo] = acc * oscale; with ksplit > 1 out is
  *            [ksplit][M][N] (ldo == N) of partial products over the column
- *            ranges [p K / ksplit, (p + 1) K / ksplit) (K / 128 % ksplit == 0)
+ *            ranges [p K / ksplit, (p + 1) K / ksplit) (K / 128 (lo8) or
+ *            K / 256 (lo4) a multiple of ksplit)
  *   RESID:   out f32 [M][ldo] += gate[c] * acc * oscale, in place
- *   SWIGLU8: W the interleaved gate/up plane (see SWIGLU); the hidden h =
- *            silu(g * inscale) * (u * inscale) * oscale of N/2 columns to
- *            out as activation rows in the lo8 form (rows of ldo halves,
- *            ldo >= 0.75 N) with scales osc [M][ldos] (ldos >= N / 128)
- * Requires M >= 1, N % 256 == 0, K % 128 == 0, lds >= K / 64 and even,
- * 16-byte aligned A, W, out.  Runs the 256 x 256 4-wave kernel. */
-int qi21_op_gemm_lo8(int epi, int M, int N, int K, const void* A, int lda, const uint8_t* asc, int lds, const void* W,
-                     int ldw, const uint8_t* wsc, void* out, int ldo, const float* gate, uint8_t* osc, int ldos,
-                     int ksplit, float oscale, float inscale, void* stream);
+ *   SWIGLU8 (lo8) / SWIGLU4 (lo4): W the interleaved gate/up plane (see
+ *            SWIGLU); the hidden h = silu(g * inscale) * (u * inscale) *
+ *            oscale of N/2 columns to out as activation rows in the same
+ *            form (rows of ldo halves, ldo >= 0.75 N / 0.625 N) with scales
+ *            osc [M][ldos] (ldos >= N / 128 / N / 64)
+ * Requires M >= 1, N % 256 == 0, K % 128 (lo8) / 256 (lo4) == 0, 16-byte
+ * aligned A, W, out.  Runs the 256 x 256 4-wave kernel. */
+int qi21_op_gemm_lo(int fmt, int epi, int M, int N, int K, const void* A, int lda, const uint8_t* asc, int lds,
+                    const void* W, int ldw, const uint8_t* wsc, int ldws, void* out, int ldo, const float* gate,
+                    uint8_t* osc, int ldos, int ksplit, float oscale, float inscale, void* stream);
 
-/* The f16 part of a lo8 weight plane: source row r of src [rows][cols]
- * (QI21_F32 / BF16 / F16) goes to dst row (r / group) * gstride + goff +
- * r % group (rows of ld halves, ld >= 1.5 cols, % 4), its values at their
- * lo8 positions; the residual bytes are left for qi21_op_plane8.
- * cols % 128 == 0. */
-int qi21_op_plane_lo8(int src_dtype, const void* src, int rows, int cols, void* dst, int ld, int group, int gstride,
-                      int goff, void* stream);
+/* The f16 part of a residual-form weight plane: source row r of src
+ * [rows][cols] (QI21_F32 / BF16 / F16) goes to dst row (r / group) *
+ * gstride + goff + r % group (rows of ld halves, ld >= 1.5 cols (lo8) /
+ * 1.25 cols (lo4), % 4), its values at their positions in the form; the
+ * narrow values are left for qi21_op_plane_lo_fill.  cols % 128 / 256. */
+int qi21_op_plane_lo(int fmt, int src_dtype, const void* src, int rows, int cols, void* dst, int ld, int group,
+                     int gstride, int goff, void* stream);
 
-/* The fp8 part of a lo8 weight plane whose f16 values are set: for each of
- * the rows, e per row such that the row's largest |w| 2^-e lies in [128,
- * 256); byte of column c = e4m3(w_c 2^-e) and sc[r] = e + 127.
- * cols % 128 == 0, ld >= 1.5 cols, % 4. */
-int qi21_op_plane8(int rows, int cols, void* plane, int ld, uint8_t* sc, void* stream);
+/* The narrow part of a residual-form weight plane whose f16 values are
+ * set: lo8, per row the scale e with the row's largest |w| 2^-e in [128,
+ * 256), each byte e4m3(w 2^-e), sc[r] = e + 127 (ldsc unused); lo4, per
+ * row and 32 columns the smallest e with the block's largest |w| 2^-e <=
+ * 6, each nibble e2m1(w 2^-e), scales at sc[r * ldsc + ...] (ldsc >= cols
+ * / 32) in the lo4 order.  Round to nearest even.  cols % 128 / 256 == 0,
+ * ld as above. */
+int qi21_op_plane_lo_fill(int fmt, int rows, int cols, void* plane, int ld, uint8_t* sc, int ldsc, void* stream);
 
 /* Per-head RMSNorm(norm_q | norm_k) then interleaved-pair RoPE on the q
  * (column 0) and k (column heads*128) parts of panel f16 [rows][ldp], in

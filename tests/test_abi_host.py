@@ -105,7 +105,7 @@ def test_model_create_refuses_null_and_block_count():
 def test_model_create_refuses_bad_ffn_mode_before_device_work():
     # the option is checked, and lo8's geometry bounds, before any allocation
     opt = Q.qi21_default_options()
-    opt.ffn_mode = 3
+    opt.ffn_mode = 4
     with pytest.raises(Q.Qi21Error) as e:
         Q.qi21_model_create(_geom(), opt, 2, 1, 1, stream=0)
     assert e.value.code == Q.QI21_EINVAL
@@ -120,9 +120,16 @@ def test_model_create_refuses_bad_ffn_mode_before_device_work():
     with pytest.raises(Q.Qi21Error) as e:
         Q.qi21_model_create(g, opt, 2, 1, 1, stream=0)
     assert e.value.code == Q.QI21_EUNSUPPORTED
+    opt.ffn_mode = Q.QI21_FFN_LO4
+    g = _geom()
+    g.inter = 640  # inter % 256 != 0 (fine for lo8)
+    with pytest.raises(Q.Qi21Error) as e:
+        Q.qi21_model_create(g, opt, 2, 1, 1, stream=0)
+    assert e.value.code == Q.QI21_EUNSUPPORTED
 
 
 def test_op_entry_points_validate_shapes_on_host():
+    L8, L4 = Q.QI21_FFN_LO8, Q.QI21_FFN_LO4
     cases = [
         lambda: Q.qi21_op_gemm(0, 16, 100, 64, 1, 64, 1, 1, 100, stream=0),        # N % 128
         lambda: Q.qi21_op_gemm(0, 16, 128, 60, 1, 64, 1, 1, 128, stream=0),        # K % 64
@@ -160,25 +167,45 @@ def test_op_entry_points_validate_shapes_on_host():
         lambda: Q.qi21_op_rowop(4, 256, 6, 1, 1, 1, 256, 1, 0, 0, 1e-6, 1.0, stream=0),    # pair rows into [rows][h]
         lambda: Q.qi21_op_rowop(4, 256, 2, 1, 1, 1, 258, 1, 0, 0, 1e-6, 1.0, stream=0),
         lambda: Q.qi21_op_rowop_parts(4, 256, 7, 1, 1, 2, 1024, 1, 500, 1, 0, 0, 1e-6, 1.0, stream=0),
-        # the lo8 row op: h % 128, ldxn >= 1.5 h, scales, modes 2 / 3 only
-        lambda: Q.qi21_op_rowop_lo8(4, 192, 2, 1, 1, 1, 0, 1, 288, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
-        lambda: Q.qi21_op_rowop_lo8(4, 256, 2, 1, 1, 1, 0, 1, 380, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
-        lambda: Q.qi21_op_rowop_lo8(4, 256, 2, 1, 1, 1, 0, 1, 384, None, 1, 0, 0, 1e-6, 1.0, stream=0),
-        lambda: Q.qi21_op_rowop_lo8(4, 256, 6, 1, 1, 1, 0, 1, 512, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
-        # the lo8 GEMM: K % 128, N % 256, lda / ldw >= 1.5 K, scale strides, split, epilogue arguments
-        lambda: Q.qi21_op_gemm_lo8(1, 16, 256, 192, 1, 288, 1, 4, 1, 288, 1, 1, 256, stream=0),
-        lambda: Q.qi21_op_gemm_lo8(1, 16, 128, 256, 1, 384, 1, 4, 1, 384, 1, 1, 128, stream=0),
-        lambda: Q.qi21_op_gemm_lo8(1, 16, 256, 256, 1, 256, 1, 4, 1, 384, 1, 1, 256, stream=0),
-        lambda: Q.qi21_op_gemm_lo8(1, 16, 256, 256, 1, 384, 1, 3, 1, 384, 1, 1, 256, stream=0),
-        lambda: Q.qi21_op_gemm_lo8(1, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 1, 256, ksplit=3, stream=0),
-        lambda: Q.qi21_op_gemm_lo8(7, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 1, 256, stream=0),       # no gate
-        lambda: Q.qi21_op_gemm_lo8(9, 16, 512, 256, 1, 384, 1, 4, 1, 384, 1, 1, 384, stream=0),       # no osc
-        lambda: Q.qi21_op_gemm_lo8(0, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 1, 256, stream=0),       # F16
-        lambda: Q.qi21_op_gemm_lo8(7, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 1, 256, gate=1, ksplit=2, stream=0),
-        lambda: Q.qi21_op_plane_lo8(0, 1, 16, 192, 1, 288, 16, 0, 0, stream=0),
-        lambda: Q.qi21_op_plane_lo8(0, 1, 16, 256, 1, 256, 16, 0, 0, stream=0),
-        lambda: Q.qi21_op_plane8(16, 256, 1, 380, 1, stream=0),
-        lambda: Q.qi21_op_plane8(16, 256, 1, 384, None, stream=0),
+        # the residual-form row op: h % 128 (lo8) / 256 (lo4), ldxn >= 1.5 h / 1.25 h, scales,
+        # modes 2 / 3 only, a known format
+        lambda: Q.qi21_op_rowop_lo(L8, 4, 192, 2, 1, 1, 1, 0, 1, 288, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop_lo(L8, 4, 256, 2, 1, 1, 1, 0, 1, 380, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop_lo(L8, 4, 256, 2, 1, 1, 1, 0, 1, 384, None, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop_lo(L8, 4, 256, 6, 1, 1, 1, 0, 1, 512, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop_lo(L4, 4, 384, 2, 1, 1, 1, 0, 1, 480, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop_lo(L4, 4, 512, 2, 1, 1, 1, 0, 1, 636, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
+        lambda: Q.qi21_op_rowop_lo(5, 4, 512, 2, 1, 1, 1, 0, 1, 1024, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
+        # the residual-form GEMM: K % 128 / 256, N % 256, lda / ldw, scale strides, split, epilogue arguments
+        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 256, 192, 1, 288, 1, 4, 1, 288, 1, 0, 1, 256, stream=0),
+        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 128, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 128, stream=0),
+        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 256, 256, 1, 256, 1, 4, 1, 384, 1, 0, 1, 256, stream=0),
+        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 256, 256, 1, 384, 1, 3, 1, 384, 1, 0, 1, 256, stream=0),
+        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 256, ksplit=3, stream=0),
+        lambda: Q.qi21_op_gemm_lo(L8, 7, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 256, stream=0),  # no gate
+        lambda: Q.qi21_op_gemm_lo(L8, 9, 16, 512, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 384, stream=0),  # no osc
+        lambda: Q.qi21_op_gemm_lo(L8, 10, 16, 512, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 384, osc=1, ldos=8,
+                                  stream=0),  # the lo4 SwiGLU on lo8 operands
+        lambda: Q.qi21_op_gemm_lo(L8, 0, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 256, stream=0),  # F16
+        lambda: Q.qi21_op_gemm_lo(L8, 7, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 256, gate=1, ksplit=2,
+                                  stream=0),
+        lambda: Q.qi21_op_gemm_lo(L4, 1, 16, 256, 384, 1, 480, 1, 12, 1, 480, 1, 12, 1, 256, stream=0),  # K % 256
+        lambda: Q.qi21_op_gemm_lo(L4, 1, 16, 256, 512, 1, 632, 1, 16, 1, 640, 1, 16, 1, 256, stream=0),  # lda
+        lambda: Q.qi21_op_gemm_lo(L4, 1, 16, 256, 512, 1, 640, 1, 8, 1, 640, 1, 16, 1, 256, stream=0),   # lds
+        lambda: Q.qi21_op_gemm_lo(L4, 1, 16, 256, 512, 1, 640, 1, 16, 1, 640, 1, 4, 1, 256, stream=0),   # ldws
+        lambda: Q.qi21_op_gemm_lo(L4, 1, 16, 256, 512, 1, 640, 1, 16, 1, 640, 1, 16, 1, 256, ksplit=3, stream=0),
+        lambda: Q.qi21_op_gemm_lo(L4, 9, 16, 1024, 512, 1, 640, 1, 16, 1, 640, 1, 16, 1, 640, osc=1, ldos=8,
+                                  stream=0),  # the lo8 SwiGLU on lo4 operands
+        lambda: Q.qi21_op_gemm_lo(L4, 10, 16, 512, 512, 1, 640, 1, 16, 1, 640, 1, 16, 1, 320, osc=1, ldos=7,
+                                  stream=0),  # ldos < N / 64
+        lambda: Q.qi21_op_plane_lo(L8, 0, 1, 16, 192, 1, 288, 16, 0, 0, stream=0),
+        lambda: Q.qi21_op_plane_lo(L8, 0, 1, 16, 256, 1, 256, 16, 0, 0, stream=0),
+        lambda: Q.qi21_op_plane_lo(L4, 0, 1, 16, 384, 1, 480, 16, 0, 0, stream=0),
+        lambda: Q.qi21_op_plane_lo(L4, 0, 1, 16, 512, 1, 636, 16, 0, 0, stream=0),
+        lambda: Q.qi21_op_plane_lo_fill(L8, 16, 256, 1, 380, 1, 0, stream=0),
+        lambda: Q.qi21_op_plane_lo_fill(L8, 16, 256, 1, 384, None, 0, stream=0),
+        lambda: Q.qi21_op_plane_lo_fill(L4, 16, 512, 1, 640, 1, 8, stream=0),  # ldsc < cols / 32
+        lambda: Q.qi21_op_plane_lo_fill(2 * L4, 16, 512, 1, 640, 1, 16, stream=0),
     ]
     for c in cases:
         with pytest.raises(Q.Qi21Error) as e:

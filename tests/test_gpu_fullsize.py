@@ -10,9 +10,9 @@ pair is compared with the oracle's stored output (written by
 ``tests/golden/make_oracle_golden.py`` from the oracle alone).
 
 End-to-end tolerances.  The benchmark's configuration keeps the FFN input
-and SwiGLU hidden in the lo8 form (QI21_FFN_LO8: f16 plus a scaled fp8
-residual); it, and the f16-pair form (QI21_FFN_PAIR), are held to the 1e-3
-relative L2 bar on v, and every target row compared to 3e-3 relative L2
+and SwiGLU hidden in the lo4 form (QI21_FFN_LO4: f16 plus a scaled fp4
+residual); it, the lo8 form (fp8 residual) and the f16-pair form
+(QI21_FFN_PAIR) are held to the 1e-3 relative L2 bar on v, and every target row compared to 3e-3 relative L2
 over its 64 channels (a row-local fault a few times the bar fails it even
 where the global figure hides it).  With every site in single f16 (the
 pages' design) the error after 32 blocks of these N(0, 0.02) weights is
@@ -218,6 +218,13 @@ def full_model_lo8():
     Q().qi21_model_destroy(m)
 
 
+@pytest.fixture(scope="module")
+def full_model_lo4():
+    m = _full(Q().QI21_FFN_LO4)
+    yield m
+    Q().qi21_model_destroy(m)
+
+
 def _golden(name, p=0, tag=""):
     import glob
     f = glob.glob(os.path.join(GOLD, f"oracle_v_{name}_p{p}{tag}_rows*.npy"))
@@ -245,13 +252,16 @@ def _check_v(got, want, label):
     assert rows.max() < ROW_TOL
 
 
+@pytest.mark.parametrize("mode", ["lo4", "lo8"])
 @pytest.mark.parametrize("name", ["512", "1024", "cond", "ragged", "2048"])
-def test_step_full_size_lo8_against_oracle(full_model_lo8, name):
-    # the configuration bench.py times.  ragged: 4087 target rows behind 37
-    # prefix rows, so the last row tile of every GEMM, the last V^T columns
-    # and the last key tile of attention are partial on the large-pass path
+def test_step_full_size_residual_forms_against_oracle(request, mode, name):
+    # lo4 is the configuration bench.py times.  ragged: 4087 target rows
+    # behind 37 prefix rows, so the last row tile of every GEMM, the last
+    # V^T columns and the last key tile of attention are partial on the
+    # large-pass path
+    m = request.getfixturevalue(f"full_model_{mode}")
     want, stride = _golden(name)
-    _check_v(_step_v(full_model_lo8, CONFIGS[name], 52, stride), want, f"{name} (lo8)")
+    _check_v(_step_v(m, CONFIGS[name], 52, stride), want, f"{name} ({mode})")
 
 
 @pytest.mark.parametrize("name", ["512", "1024", "cond", "ragged"])
@@ -271,9 +281,9 @@ def test_step_full_size_single_f16_within_storage_error(full_model, name):
     assert err < 1.5 * storage
 
 
-@pytest.mark.parametrize("mode", ["lo8", "pair"])
+@pytest.mark.parametrize("mode", ["lo4", "lo8", "pair"])
 def test_cfg_pair_full_size_against_oracle(request, mode):
-    m = request.getfixturevalue("full_model_lo8" if mode == "lo8" else "full_model_pair")
+    m = request.getfixturevalue(f"full_model_{mode}")
     w = CONFIGS["cfg512"]
     wants = [_golden("cfg512", p) for p in range(2)]
     ds = [bench.workload_tensors(w, p) for p in range(2)]

@@ -177,14 +177,14 @@ def test_range_guard_settings(tiny_cpu, shifts):
         q.qi21_model_destroy(m)
 
 
-@pytest.mark.parametrize("mode", ["pair", "lo8"])
+@pytest.mark.parametrize("mode", ["pair", "lo8", "lo4"])
 def test_ffn_mode_option(tiny_cpu, tiny_gpu, mode):
-    """ffn_mode PAIR (FFN input and hidden as f16 pairs) and LO8 (f16 plus
-    a scaled fp8 residual): the result to the bar, on the single step and
-    on a batched CFG pair, and no larger error than single f16"""
+    """ffn_mode PAIR (FFN input and hidden as f16 pairs), LO8 and LO4 (f16
+    plus a scaled fp8 / fp4 residual): the result to the bar, on the single
+    step and on a batched CFG pair, and no larger error than single f16"""
     q = Q()
     opt = q.qi21_default_options()
-    opt.ffn_mode = q.QI21_FFN_PAIR if mode == "pair" else q.QI21_FFN_LO8
+    opt.ffn_mode = {"pair": q.QI21_FFN_PAIR, "lo8": q.QI21_FFN_LO8, "lo4": q.QI21_FFN_LO4}[mode]
     m = bench.build_model(TINY_MODEL, opt)
     try:
         w = CONFIGS["tiny"]
