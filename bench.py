@@ -10,10 +10,11 @@ qkrope, attention, O GEMM, rowop, gate/up GEMM + SwiGLU, down GEMM, rowop]
 prefilled once before the timed region.  Weights are random (seeded,
 bf16, N(0, 0.02)) with the full model's shapes; inputs are synthetic.
 
-The FFN input and the SwiGLU hidden are stored in the lo8 form by default
-(f16 plus a scaled e4m3 residual, ``--ffn lo8``), the configuration whose
-velocity the tests hold to 1e-3 of the oracle; ``--ffn f16`` times the
-pages' single-f16 design and ``--ffn pair`` the f16-pair form.
+The FFN input and the SwiGLU hidden are stored in the lo4 form by default
+(f16 plus an MX-scaled e2m1 residual, ``--ffn lo4``), a configuration
+whose velocity the tests hold to 1e-3 of the oracle, as they do lo8 (an
+e4m3 residual) and pair (f16 pairs); ``--ffn f16`` times the pages'
+single-f16 design, which misses that bar on these weights.
 
 Prints ONE JSON line: s/step (the metric), TFLOP/s and the fraction of the
 f16 MFMA peak (algorithmic FLOP of the method: the residual products of
@@ -228,8 +229,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="1024", choices=sorted(k for k in CONFIGS if k != "tiny"))
-    ap.add_argument("--ffn", default="lo8", choices=("lo8", "pair", "f16"),
-                    help="storage of the FFN input and hidden (lo8: f16 + scaled e4m3 residual; the default)")
+    ap.add_argument("--ffn", default="lo4", choices=("lo4", "lo8", "pair", "f16"),
+                    help="storage of the FFN input and hidden (lo4, the default: f16 + MX-scaled e2m1 residual; "
+                         "lo8: f16 + scaled e4m3 residual)")
     ap.add_argument("--site-steps", type=int, default=3,
                     help="steps of the untimed pass that times every site with HIP events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -253,7 +255,8 @@ def main(argv=None):
     props = torch.cuda.get_device_properties(dev)
     t_build = time.perf_counter()
     opt = Q.qi21_default_options()
-    opt.ffn_mode = {"f16": Q.QI21_FFN_F16, "pair": Q.QI21_FFN_PAIR, "lo8": Q.QI21_FFN_LO8}[args.ffn]
+    opt.ffn_mode = {"f16": Q.QI21_FFN_F16, "pair": Q.QI21_FFN_PAIR, "lo8": Q.QI21_FFN_LO8,
+                    "lo4": Q.QI21_FFN_LO4}[args.ffn]
     m = build_model(spec, opt)
     t_build = time.perf_counter() - t_build
     nprog = len(w.prefixes)
@@ -328,10 +331,11 @@ def main(argv=None):
             sites["all_gemms"] = {"ms_per_step": g_ms / args.site_steps, "tflops": tf, "frac": tf / PEAK_F16_TFLOPS}
         sites["note"] = (f"HIP events around every launch of each site over {args.site_steps} untimed steps after the "
                          "timed region; algorithmic FLOP (lo8 residual products not counted)")
-    # the lo8 form runs its FFN GEMMs over 1.5x their K in MFMA cycles (the
-    # residual k-tiles on the fp8 MFMA at twice the f16 rate): the fraction
-    # of the peak of that instruction mix, for context
-    mix = 1.5 if args.ffn == "lo8" else 2.0 if args.ffn == "pair" else 1.0
+    # the residual forms run their FFN GEMMs over 1.25x (lo4: fp4 MFMA at
+    # four times the f16 rate) or 1.5x (lo8: fp8 at twice) their K in MFMA
+    # cycles, the pair form over 2x: the fraction of the peak of that
+    # instruction mix, for context
+    mix = {"lo4": 1.25, "lo8": 1.5, "pair": 2.0, "f16": 1.0}[args.ffn]
     line = {
         "metric": "denoiser step s/call + TFLOP/s (% f16 MFMA peak) at 1024^2, 32 blocks",
         "value": sec,
@@ -343,7 +347,7 @@ def main(argv=None):
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": (sec / PAGES_STEP_S[args.config]) if (args.config in PAGES_STEP_S and nprog == 1) else None,
-        "dtype": {"lo8": "f16+e4m3", "pair": "f16", "f16": "f16"}[args.ffn],
+        "dtype": {"lo4": "f16+e2m1", "lo8": "f16+e4m3", "pair": "f16", "f16": "f16"}[args.ffn],
         "data": "synthetic (seeded N(0,0.02) bf16 weights of the full 32-block dim-4096 model; N(0,1) rows)",
         "config": {"workload": w.note, "blocks": spec.layers, "dim": spec.dim, "heads": spec.heads,
                    "mlp_hidden": spec.inter, "target_rows": rows_total, "prefix_rows": lp, "programs": nprog,

@@ -251,7 +251,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
             const floatx4 v = lo[p][g] * inv;
             *reinterpret_cast<unsigned*>(brow + lo8_lo_at(c)) = pack_e4m3(v[0], v[1], v[2], v[3]);
           }
-        if (hsel == 0) a.osc[(size_t)row * a.ldos + hc / 64] = (uint8_t)(ex + 127);
+        if (hsel == 0) a.osc[lo8_sc_at(row, hc, a.N / 2)] = (uint8_t)(ex + 127);
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU4) {
@@ -296,7 +296,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
             const floatx4 v = lo[p][g] * inv;
             *reinterpret_cast<uint16_t*>(brow + lo4_lo_at(c)) = (uint16_t)pack_e2m1(v[0], v[1], v[2], v[3]);
           }
-          if (hsel == 0) a.osc[(size_t)row * a.ldos + lo4_sc_at(hc + p * 32)] = (uint8_t)(ex[p] + 127);
+          if (hsel == 0) a.osc[lo4_sc_at(row, hc + p * 32, a.N / 2)] = (uint8_t)(ex[p] + 127);
         }
       }
     }
@@ -707,16 +707,18 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     if constexpr (LO8) {
-      // A scales: rows past M read as zero (so do their A rows)
+      // A scales: the tile's 256-row block of the blocked array (lds
+      // bytes per row; rows past M read whatever the block holds there,
+      // which only their unstored outputs see)
       const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(a.asc + (size_t)m0 * a.lds), 0, min(a.M - m0, DBM) * a.lds, 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.asc + (size_t)m0 * a.lds), 0, DBM * a.lds, 0x00020000);
       // the A scale bytes of the group at unit-local k-tile t (its k-steps
-      // 2 g and 2 g + 1, g the global group)
+      // 2 g and 2 g + 1, g the global group): 32 rows' in 64 bytes
       auto load_asc = [&](int t) {
         const int g = (kt0 + t) / 3;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          asc[i] = (int)__builtin_amdgcn_raw_buffer_load_b16(rs, (wm * WTM + i * 32 + l32) * a.lds + 2 * g, 0, 0);
+          asc[i] = (int)__builtin_amdgcn_raw_buffer_load_b16(rs, g * 512 + (wm * WTM + i * 32 + l32) * 2, 0, 0);
       };
 #pragma unroll
       for (int j = 0; j < TN; ++j) wsc[j] = a.wsc[n0 + wn * WTN + j * 32 + l32];
@@ -770,18 +772,23 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
         step8(1, 1, false, false, 0, 0, ra, rb, 0, 0, 0);
       }
     } else if constexpr (LO4) {
+      // the tile's 256-row blocks of the blocked scale arrays (lds / ldws
+      // bytes per row)
       const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(a.asc + (size_t)m0 * a.lds), 0, min(a.M - m0, DBM) * a.lds, 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.asc + (size_t)m0 * a.lds), 0, DBM * a.lds, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rw =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.wsc + (size_t)n0 * a.ldws), 0, DBN * a.ldws, 0x00020000);
       // the scale dwords of the group at unit-local k-tile t: its fp4
       // k-tile's four k-steps for this lane half, per A row and per W row
+      // (32 rows' dwords of one lane half in 256 bytes)
       auto load_sc = [&](int t) {
-        const int o = ((kt0 + t) / 5) * 8 + 4 * hsel;
+        const int o = ((kt0 + t) / 5) * 2048 + 4 * hsel;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          asc[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, (wm * WTM + i * 32 + l32) * a.lds + o, 0, 0);
+          asc[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, o + (wm * WTM + i * 32 + l32) * 8, 0, 0);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          wsc[j] = *reinterpret_cast<const int*>(a.wsc + (size_t)(n0 + wn * WTN + j * 32 + l32) * a.ldws + o);
+          wsc[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rw, o + (wn * WTN + j * 32 + l32) * 8, 0, 0);
       };
       load_sc(0);
       if (sq == seq0)

@@ -6,15 +6,24 @@
 // lo8: columns grouped by 128; group g of a row takes 384 bytes, the 128
 // halves f16(v) and then the 128 OCP e4m3 (fp8) bytes of the scaled
 // residuals, so a GEMM walks a row in 128-byte k-tiles of two f16 k-tiles
-// and one fp8 k-tile per group.  Activations: one scale per 64 columns.
+// and one fp8 k-tile per group.  Activations: one scale per 64 columns,
+// two per group.
 //
 // lo4: columns grouped by 256; group g takes 640 bytes, the 256 halves
 // and then 128 bytes of e2m1 (fp4) residuals, two per byte (the even
 // column in the low nibble): four f16 k-tiles and one fp4 k-tile per
-// group.  One scale per 32 columns (the MX block), stored per group in the
-// order the fp4 MFMA's lanes take them: byte 8 g + 4 h + s for the block
-// 2 s + h of the group (k-step s of the fp4 k-tile, lane half h), so a
-// lane reads its four k-steps' scales as one dword.
+// group.  One scale per 32 columns (the MX block), eight per group, in the
+// order the fp4 MFMA's lanes take them: byte 4 h + s of the group for the
+// block 2 s + h (k-step s of the fp4 k-tile, lane half h), so a lane reads
+// its four k-steps' scales as one dword.
+//
+// Scale arrays are blocked by 256 rows and, inside a block, ordered group
+// by group: the bytes of rows r .. r + 31 for one group sit next to each
+// other, so the 32 rows a GEMM lane group reads at once come from a few
+// cache lines.  With q scale bytes per group and G groups per row, the
+// byte of row r, group g, position b is
+//   (r / 256) * 256 G q + g * 256 q + (r % 256) * q + b
+// (an array holds whole blocks: round_up(rows, 256) rows).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -41,13 +50,19 @@ __device__ __forceinline__ unsigned pack_e4m3(float a, float b, float c, float d
 }
 
 // lo4 positions: halves offset of column c's f16 value, byte of the pair
-// (c, c + 1) (c even), and the scale byte of c's 32-column block within
-// the row's scale bytes
+// (c, c + 1) (c even)
 __device__ __forceinline__ int lo4_hi_at(int c) { return (c >> 8) * 320 + (c & 255); }
 __device__ __forceinline__ int lo4_lo_at(int c) { return (c >> 8) * 640 + 512 + ((c & 255) >> 1); }
-__device__ __forceinline__ int lo4_sc_at(int c) {
+
+// scale byte of row r, column c in a blocked scale array of rows of w
+// columns (see above): lo8 (q = 2 per 128-column group), lo4 (q = 8 per
+// 256-column group, the block 2 s + h of the group at 4 h + s)
+__device__ __forceinline__ size_t lo8_sc_at(int r, int c, int w) {
+  return (size_t)(r >> 8) * 256 * (w >> 6) + (size_t)(c >> 7) * 512 + (r & 255) * 2 + ((c >> 6) & 1);
+}
+__device__ __forceinline__ size_t lo4_sc_at(int r, int c, int w) {
   const int b = (c & 255) >> 5;
-  return (c >> 8) * 8 + 4 * (b & 1) + (b >> 1);
+  return (size_t)(r >> 8) * 256 * (w >> 5) + (size_t)(c >> 8) * 2048 + (r & 255) * 8 + 4 * (b & 1) + (b >> 1);
 }
 
 // Scale exponent of an fp4 block whose largest magnitude is mx: the

@@ -514,7 +514,6 @@ int run_blocks(qi21_model* m, int rows, const std::vector<Seg>& segs, Prog* pre,
       if (lo) {
         ffn_lo(ga, a.xsc, sx, m->w13s[l], lo4 ? H / 32 : 0);
         ga.osc = a.hsc;
-        ga.ldos = sh;
         HIP_OK(qi21::launch_gemm(lo8 ? qi21::EPI_SWIGLU8 : qi21::EPI_SWIGLU4, ga, 0, s));
       } else {
         ga.kw = H;
@@ -732,8 +731,8 @@ int qi21_model_set_block(qi21_model* m, int layer, int w_dtype, const void* cons
     HIP_OK(qi21::launch_plane8(H, I, m->w2[layer], ld2, m->w2s[layer], s));
   }
   if (lo4) {
-    HIP_OK(qi21::launch_plane4(2 * I, H, m->w13[layer], ld13, m->w13s[layer], H / 32, s));
-    HIP_OK(qi21::launch_plane4(H, I, m->w2[layer], ld2, m->w2s[layer], I / 32, s));
+    HIP_OK(qi21::launch_plane4(2 * I, H, m->w13[layer], ld13, m->w13s[layer], s));
+    HIP_OK(qi21::launch_plane4(H, I, m->w2[layer], ld2, m->w2s[layer], s));
   }
   // the q norm weights carry the softmax's log2(e) / sqrt(128), so every q
   // the block produces is in the base-2 units the attention kernels take
@@ -1248,9 +1247,9 @@ int qi21_op_rowop_lo(int fmt, int rows, int h, int mode, float* x, const float* 
   return op_rowop(rows, h, mode, x, y, nparts, pstride, xn, ldxn, xsc, mods, g_off, s_off, eps, oscale, stream, fmt);
 }
 
-int qi21_op_gemm_lo(int fmt, int epi, int M, int N, int K, const void* A, int lda, const uint8_t* asc, int lds,
-                    const void* W, int ldw, const uint8_t* wsc, int ldws, void* out, int ldo, const float* gate,
-                    uint8_t* osc, int ldos, int ksplit, float oscale, float inscale, void* stream) {
+int qi21_op_gemm_lo(int fmt, int epi, int M, int N, int K, const void* A, int lda, const uint8_t* asc, const void* W,
+                    int ldw, const uint8_t* wsc, void* out, int ldo, const float* gate, uint8_t* osc, int ksplit,
+                    float oscale, float inscale, void* stream) {
   g_err.clear();
   const bool l8 = fmt == QI21_FFN_LO8;
   if (!l8 && fmt != QI21_FFN_LO4) return fail(QI21_EINVAL, "gemm format %d (QI21_FFN_LO8 or QI21_FFN_LO4)", fmt);
@@ -1259,13 +1258,10 @@ int qi21_op_gemm_lo(int fmt, int epi, int M, int N, int K, const void* A, int ld
     return fail(QI21_EINVAL, "residual gemm epilogue %d (F32, RESID or the format's SWIGLU)", epi);
   const int g = l8 ? 128 : 256;                    // columns per group
   const long krow = l8 ? 3L * K / 2 : 5L * K / 4;  // halves per row
-  const int blk = l8 ? 64 : 32;                    // activation scale block
-  if (M < 1 || N < 256 || N % 256 || K < g || K % g || lda % 8 || ldw % 8 || lda < krow || ldw < krow ||
-      lds < K / blk || lds % (l8 ? 2 : 4) || (!l8 && (ldws < K / 32 || ldws % 4)))
+  if (M < 1 || N < 256 || N % 256 || K < g || K % g || lda % 8 || ldw % 8 || lda < krow || ldw < krow)
     return fail(QI21_EINVAL,
-                "residual gemm M %d N %d K %d lda %d ldw %d lds %d ldws %d (need N %% 256, K %% %d, lda and ldw >= %ld "
-                "and %% 8, lds >= K / %d, W scales per 32 columns for lo4)",
-                M, N, K, lda, ldw, lds, ldws, g, krow, blk);
+                "residual gemm M %d N %d K %d lda %d ldw %d (need N %% 256, K %% %d, lda and ldw >= %ld and %% 8)", M, N,
+                K, lda, ldw, g, krow);
   if (!A || !W || !asc || !wsc || !out) return fail(QI21_EINVAL, "residual gemm pointer is NULL");
   if (ksplit < 1 || ksplit > 8 || (K / g) % ksplit || (ksplit > 1 && epi != QI21_EPI_F32))
     return fail(QI21_EINVAL, "residual gemm ksplit %d (1..8, dividing K / %d; F32 only)", ksplit, g);
@@ -1273,19 +1269,17 @@ int qi21_op_gemm_lo(int fmt, int epi, int M, int N, int K, const void* A, int ld
   if (epi == QI21_EPI_F32 && (ldo < N || ldo % 4 || (ksplit > 1 && ldo != N)))
     return fail(QI21_EINVAL, "residual gemm f32 ldo %d (>= N, %% 4; = N when split)", ldo);
   const long hrow = l8 ? 3L * N / 4 : 5L * N / 8;  // halves of an output row of N/2 columns
-  if (epi == sw && (!osc || ldo < hrow || ldo % 4 || ldos < (N / 2) / blk || (N / 2) % g))
-    return fail(QI21_EINVAL, "residual gemm swiglu ldo %d (>= %ld, %% 4), osc, ldos %d (>= %d)", ldo, hrow, ldos,
-                (N / 2) / blk);
+  if (epi == sw && (!osc || ldo < hrow || ldo % 4 || (N / 2) % g))
+    return fail(QI21_EINVAL, "residual gemm swiglu ldo %d (>= %ld, %% 4), osc, N / 2 %% %d", ldo, hrow, g);
   qi21::GemmArgs a = gemm_args(M, N, (int)krow, (const f16*)A, lda, (const f16*)W, out, ldo, oscale, inscale);
   a.ldw = ldw;
   a.lo = l8 ? 8 : 4;
   a.asc = asc;
-  a.lds = lds;
+  a.lds = l8 ? K / 64 : K / 32;
   a.wsc = wsc;
-  a.ldws = l8 ? 0 : ldws;
+  a.ldws = l8 ? 0 : K / 32;
   a.gate = gate;
   a.osc = osc;
-  a.ldos = ldos;
   a.ksplit = ksplit;
   a.pstride = (size_t)M * N;
   HIP_OK(qi21::launch_gemm(epi, a, 0, (hipStream_t)stream));
@@ -1307,18 +1301,18 @@ int qi21_op_plane_lo(int fmt, int src_dtype, const void* src, int rows, int cols
   return QI21_OK;
 }
 
-int qi21_op_plane_lo_fill(int fmt, int rows, int cols, void* plane, int ld, uint8_t* sc, int ldsc, void* stream) {
+int qi21_op_plane_lo_fill(int fmt, int rows, int cols, void* plane, int ld, uint8_t* sc, void* stream) {
   g_err.clear();
   const bool l8 = fmt == QI21_FFN_LO8;
   if (!l8 && fmt != QI21_FFN_LO4) return fail(QI21_EINVAL, "plane format %d", fmt);
   const int g = l8 ? 128 : 256;
   const long need = l8 ? 3L * cols / 2 : 5L * cols / 4;
-  if (rows < 1 || cols < g || cols % g || ld < need || ld % 4 || !plane || !sc || (!l8 && ldsc < cols / 32))
-    return fail(QI21_EINVAL, "residual plane fill rows %d cols %d ld %d ldsc %d", rows, cols, ld, ldsc);
+  if (rows < 1 || cols < g || cols % g || ld < need || ld % 4 || !plane || !sc)
+    return fail(QI21_EINVAL, "residual plane fill rows %d cols %d ld %d", rows, cols, ld);
   if (l8)
     HIP_OK(qi21::launch_plane8(rows, cols, (f16*)plane, ld, sc, (hipStream_t)stream));
   else
-    HIP_OK(qi21::launch_plane4(rows, cols, (f16*)plane, ld, sc, ldsc, (hipStream_t)stream));
+    HIP_OK(qi21::launch_plane4(rows, cols, (f16*)plane, ld, sc, (hipStream_t)stream));
   return QI21_OK;
 }
 

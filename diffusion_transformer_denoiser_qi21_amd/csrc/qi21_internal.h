@@ -35,8 +35,7 @@ enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 
 //   EPI_SWIGLU8 / EPI_SWIGLU4: as EPI_SWIGLU, h written in the lo8 / lo4
 //               row form (lores.h): out row r (ldo halves) holds f16(h) and
 //               the scaled residuals of its N/2 columns, with the scales in
-//               osc[r * ldos + ...] (per 64 columns / per 32 in the lo4
-//               order).  Large-M 4-wave kernel only.
+//               the blocked array osc.  Large-M 4-wave kernel only.
 //   EPI_QKROPE: N = 2H, W = the q then k projection rows; per row and
 //               128-column head: RMSNorm of the accumulators (weights nq for
 //               q heads, nk for k heads, eps in the accumulators' scale),
@@ -57,11 +56,12 @@ enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_SWIGLU2 = 
 // epilogues): A and W rows are in the lo8 / lo4 row form (lores.h), K
 // counting the halves of the whole row (1.5 / 1.25 times the columns), so
 // of every 3 / 5 k-tiles the last holds the residuals of the columns the
-// others hold as halves, multiplied on the scaled fp8 / fp4 MFMA.  Scales:
-// lo8, A row r's residuals of columns [64 g, 64 g + 64) by asc[r * lds +
-// g], W row n's by wsc[n]; lo4, per row and 32 columns in the lo4 order,
-// asc[r * lds + ...] and wsc[n * ldws + ...].  kw = K (no wrap), ldw the
-// W row stride.
+// others hold as halves, multiplied on the scaled fp8 / fp4 MFMA.  Scales
+// (blocked by 256 rows, lores.h): lo8, A's per 64 columns in asc (lds =
+// K / 64 bytes per row), W's one per row in wsc[n]; lo4, A's and W's per
+// 32 columns in asc / wsc (lds = ldws = K / 32).  The arrays hold whole
+// 256-row blocks.  osc (EPI_SWIGLU8 / 4): the hidden's, blocked likewise.
+// kw = K (no wrap), ldw the W row stride.
 // Assumes: N % 128 == 0, K % 64 == 0, kw % 64 == 0, K % kw == 0, M >= 1,
 // 16-byte aligned rows (lda a multiple of 8), for EPI_QKV N/3 % 128 == 0
 // and ld2 >= M.
@@ -74,8 +74,8 @@ struct GemmArgs {
   int lo = 0;
   const uint8_t* asc = nullptr; int lds = 0;
   const uint8_t* wsc = nullptr; int ldws = 0;
-  // EPI_SWIGLU8 output scales
-  uint8_t* osc = nullptr; int ldos = 0;
+  // EPI_SWIGLU8 / EPI_SWIGLU4 output scales
+  uint8_t* osc = nullptr;
   void* out; int ldo;
   f16* out2; int ld2;
   float oscale, inscale;
@@ -128,10 +128,9 @@ hipError_t launch_flash(const FlashArgs* segs, int nseg, hipStream_t s);
 //             xn[r][c] = f16(v), xn[r][h + c] = f16(v - f16(v))
 //   mode & 8: (with & 2, not with & 4) xn rows of 3h bytes in the lo8 row
 //             form (lores.h): f16(v) and e4m3((v - f16(v)) 2^-e), e per 64
-//             columns in xsc[r * (h / 64) + c / 64] (E8M0); h % 128 == 0
+//             columns in the blocked scale array xsc; h % 128 == 0
 //   mode & 16: (with & 2 only) the lo4 row form, rows of 2.5h bytes, e per
-//             32 columns in xsc[r * (h / 32) + ...] in the lo4 order;
-//             h % 256 == 0
+//             32 columns in the blocked array xsc; h % 256 == 0
 // ldxn: xn's row stride in halves (0: h, 2h, 1.5h or 1.25h as the mode implies;
 // otherwise at least that, and a multiple of 4)
 hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16* xn,
@@ -179,9 +178,9 @@ hipError_t launch_plane(int src_dtype, const void* src, int rows, int cols, f16*
                         int gstride, int goff, hipStream_t s, int ldd = 0, int lo = 0);
 // The fp4 part of a lo4 weight plane whose f16 values are set: per row and
 // 32-column block, e with the block's largest |w| 2^-e <= 6 (the smallest
-// such), the residual nibbles e2m1(w 2^-e) and the scale byte e + 127 at
-// sc[r * ldsc + ...] in the lo4 order.  cols % 256 == 0.
-hipError_t launch_plane4(int rows, int cols, f16* plane, int ld, uint8_t* sc, int ldsc, hipStream_t s);
+// such), the residual nibbles e2m1(w 2^-e) and the scale byte e + 127 in
+// the blocked array sc (whole 256-row blocks).  cols % 256 == 0.
+hipError_t launch_plane4(int rows, int cols, f16* plane, int ld, uint8_t* sc, hipStream_t s);
 // The fp8 part of a lo8 weight plane (rows of ld halves in the lo8 row
 // form whose f16 values are set): each row's residual bytes become
 // e4m3(w 2^-e), w the f16 value, e per row such that the row's largest

@@ -40,7 +40,7 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // 16 lanes holding one 64-column block (consecutive lanes, whole groups
 // active or not) share its scale, which the first of them stores
 __device__ __forceinline__ void lo8_store(bool act, int c, float4v r, uint8_t* __restrict__ xb,
-                                          uint8_t* __restrict__ scrow) {
+                                          uint8_t* __restrict__ xsc, int row, int h) {
   const half4 hi = half4{(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
   const float4v lo = r - float4v{(float)hi[0], (float)hi[1], (float)hi[2], (float)hi[3]};  // exact in f32
   float mx = act ? fmaxf(fmaxf(fabsf(lo[0]), fabsf(lo[1])), fmaxf(fabsf(lo[2]), fabsf(lo[3]))) : 0.0f;
@@ -52,14 +52,14 @@ __device__ __forceinline__ void lo8_store(bool act, int c, float4v r, uint8_t* _
     *reinterpret_cast<half4*>(xb + 2 * lo8_hi_at(e0)) = hi;
     const float4v v = lo * __builtin_ldexpf(1.0f, -ex);
     *reinterpret_cast<unsigned*>(xb + lo8_lo_at(e0)) = pack_e4m3(v[0], v[1], v[2], v[3]);
-    if ((c & 15) == 0) scrow[e0 >> 6] = (uint8_t)(ex + 127);
+    if ((c & 15) == 0) xsc[lo8_sc_at(row, e0, h)] = (uint8_t)(ex + 127);
   }
 }
 
 // mode & 16: the same in the lo4 row form, the 8 lanes of a 32-column
 // block sharing its scale
 __device__ __forceinline__ void lo4_store(bool act, int c, float4v r, uint8_t* __restrict__ xb,
-                                          uint8_t* __restrict__ scrow) {
+                                          uint8_t* __restrict__ xsc, int row, int h) {
   const half4 hi = half4{(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
   const float4v lo = r - float4v{(float)hi[0], (float)hi[1], (float)hi[2], (float)hi[3]};  // exact in f32
   float mx = act ? fmaxf(fmaxf(fabsf(lo[0]), fabsf(lo[1])), fmaxf(fabsf(lo[2]), fabsf(lo[3]))) : 0.0f;
@@ -71,7 +71,7 @@ __device__ __forceinline__ void lo4_store(bool act, int c, float4v r, uint8_t* _
     *reinterpret_cast<half4*>(xb + 2 * lo4_hi_at(e0)) = hi;
     const float4v v = lo * __builtin_ldexpf(1.0f, -ex);
     *reinterpret_cast<uint16_t*>(xb + lo4_lo_at(e0)) = (uint16_t)pack_e2m1(v[0], v[1], v[2], v[3]);
-    if ((c & 7) == 0) scrow[lo4_sc_at(e0)] = (uint8_t)(ex + 127);
+    if ((c & 7) == 0) xsc[lo4_sc_at(row, e0, h)] = (uint8_t)(ex + 127);
   }
 }
 
@@ -129,9 +129,9 @@ __global__ __launch_bounds__(256) void rowop_kernel(int rows, int h, float* __re
       float4v r = float4v{0.0f, 0.0f, 0.0f, 0.0f};
       if (act) r = (v[j] - mean) * inv * (1.0f + reinterpret_cast<const float4v*>(mods + s_off)[c]) * oscale;
       if constexpr ((MODE & 8) != 0)
-        lo8_store(act, c, r, xb, xsc + (size_t)row * (h >> 6));
+        lo8_store(act, c, r, xb, xsc, row, h);
       else
-        lo4_store(act, c, r, xb, xsc + (size_t)row * (h >> 5));
+        lo4_store(act, c, r, xb, xsc, row, h);
     }
     return;
   }
@@ -320,9 +320,9 @@ __global__ __launch_bounds__(256) void rowop_wide_kernel(int rows, int h, float*
       float4v r = float4v{0.0f, 0.0f, 0.0f, 0.0f};
       if (act) r = (v[j] - mean) * inv * (1.0f + reinterpret_cast<const float4v*>(mods + s_off)[c]) * oscale;
       if constexpr ((MODE & 8) != 0)
-        lo8_store(act, c, r, xb, xsc + (size_t)row * (h >> 6));
+        lo8_store(act, c, r, xb, xsc, row, h);
       else
-        lo4_store(act, c, r, xb, xsc + (size_t)row * (h >> 5));
+        lo4_store(act, c, r, xb, xsc, row, h);
     }
     return;
   }
@@ -793,13 +793,12 @@ __global__ __launch_bounds__(256) void plane8_kernel(int cols, f16* __restrict__
 
 // One 256-thread block per row of a lo4 weight plane: per 32-column block
 // (8 consecutive threads) the largest |w| of its f16 values, then the
-// block's e2m1 copy w 2^-e and its E8M0 scale in the lo4 order.
+// block's e2m1 copy w 2^-e and its E8M0 scale in the blocked lo4 order.
 __global__ __launch_bounds__(256) void plane4_kernel(int cols, f16* __restrict__ plane, int ld,
-                                                     uint8_t* __restrict__ sc, int ldsc) {
+                                                     uint8_t* __restrict__ sc) {
   const int row = blockIdx.x, t = threadIdx.x;
   f16* pr = plane + (size_t)row * ld;
   uint8_t* pb = reinterpret_cast<uint8_t*>(pr);
-  uint8_t* sr = sc + (size_t)row * ldsc;
   for (int c0 = 0; c0 < cols; c0 += 1024) {
     // (cols % 256 == 0: whole waves are active or not)
     const int c = c0 + 4 * t;
@@ -814,15 +813,15 @@ __global__ __launch_bounds__(256) void plane4_kernel(int cols, f16* __restrict__
       const float inv = __builtin_ldexpf(1.0f, -ex);
       *reinterpret_cast<uint16_t*>(pb + lo4_lo_at(c)) =
           (uint16_t)pack_e2m1((float)w[0] * inv, (float)w[1] * inv, (float)w[2] * inv, (float)w[3] * inv);
-      if ((t & 7) == 0) sr[lo4_sc_at(c)] = (uint8_t)(ex + 127);
+      if ((t & 7) == 0) sc[lo4_sc_at(row, c, cols)] = (uint8_t)(ex + 127);
     }
   }
 }
 
-hipError_t launch_plane4(int rows, int cols, f16* plane, int ld, uint8_t* sc, int ldsc, hipStream_t s) {
+hipError_t launch_plane4(int rows, int cols, f16* plane, int ld, uint8_t* sc, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (cols % 256 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(plane4_kernel, dim3(rows), dim3(256), 0, s, cols, plane, ld, sc, ldsc);
+  hipLaunchKernelGGL(plane4_kernel, dim3(rows), dim3(256), 0, s, cols, plane, ld, sc);
   return hipGetLastError();
 }
 

@@ -84,11 +84,11 @@ _SIGS = {
                                       C.c_int, C.c_int, f32, f32, vp]),
     "qi21_op_rowop_lo": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, vp, C.c_int, C.c_size_t, vp, C.c_int, vp,
                                    vp, C.c_int, C.c_int, f32, f32, vp]),
-    "qi21_op_gemm_lo": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, C.c_int, vp, C.c_int,
-                                  vp, C.c_int, vp, C.c_int, vp, vp, C.c_int, C.c_int, f32, f32, vp]),
+    "qi21_op_gemm_lo": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, vp,
+                                  C.c_int, vp, vp, C.c_int, f32, f32, vp]),
     "qi21_op_plane_lo": (C.c_int, [C.c_int, C.c_int, vp, C.c_int, C.c_int, vp, C.c_int, C.c_int, C.c_int, C.c_int,
                                    vp]),
-    "qi21_op_plane_lo_fill": (C.c_int, [C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, C.c_int, vp]),
+    "qi21_op_plane_lo_fill": (C.c_int, [C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp]),
     "qi21_op_gemm_resid": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, f32,
                                      C.c_int, vp]),
     "qi21_op_qk_gemm": (C.c_int, [C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, C.c_int, vp, vp, vp, f32,
@@ -338,10 +338,10 @@ def qi21_op_rowop_lo(fmt, rows, h, mode, x, y, nparts, pstride, xn, ldxn, xsc, m
                                   g_off, s_off, eps, oscale, _stream(stream)))
 
 
-def qi21_op_gemm_lo(fmt, epi, M, N, K, A, lda, asc, lds, W, ldw, wsc, ldws, out, ldo, gate=None, osc=None, ldos=0,
-                    ksplit=1, oscale=1.0, inscale=1.0, stream=None):
-    _check(lib().qi21_op_gemm_lo(fmt, epi, M, N, K, _p(A), lda, _p(asc), lds, _p(W), ldw, _p(wsc), ldws, _p(out), ldo,
-                                 _p(gate), _p(osc), ldos, ksplit, oscale, inscale, _stream(stream)))
+def qi21_op_gemm_lo(fmt, epi, M, N, K, A, lda, asc, W, ldw, wsc, out, ldo, gate=None, osc=None, ksplit=1,
+                    oscale=1.0, inscale=1.0, stream=None):
+    _check(lib().qi21_op_gemm_lo(fmt, epi, M, N, K, _p(A), lda, _p(asc), _p(W), ldw, _p(wsc), _p(out), ldo, _p(gate),
+                                 _p(osc), ksplit, oscale, inscale, _stream(stream)))
 
 
 def qi21_op_plane_lo(fmt, src_dtype, src, rows, cols, dst, ld, group, gstride, goff, stream=None):
@@ -349,8 +349,8 @@ def qi21_op_plane_lo(fmt, src_dtype, src, rows, cols, dst, ld, group, gstride, g
                                   _stream(stream)))
 
 
-def qi21_op_plane_lo_fill(fmt, rows, cols, plane, ld, sc, ldsc=0, stream=None):
-    _check(lib().qi21_op_plane_lo_fill(fmt, rows, cols, _p(plane), ld, _p(sc), ldsc, _stream(stream)))
+def qi21_op_plane_lo_fill(fmt, rows, cols, plane, ld, sc, stream=None):
+    _check(lib().qi21_op_plane_lo_fill(fmt, rows, cols, _p(plane), ld, _p(sc), _stream(stream)))
 
 
 def qi21_op_qkrope(rows, heads, panel, ldp, norm_q, norm_k, cos, sin, eps, kdst=None, ldk=0, stream=None):

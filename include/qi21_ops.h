@@ -159,20 +159,27 @@ int qi21_op_rowop_parts(int rows, int h, int mode, float* x, const float* y, int
  *   (halves offset 320 g + c % 256) and then 128 bytes of e2m1 (fp4)
  *   values, two per byte, column c (even) in the low nibble of byte 640 g +
  *   512 + (c % 256) / 2.  One scale per 32 columns, the smallest with the
- *   block's largest |value| / factor <= 6, at scale byte 8 g + 4 (b % 2) +
- *   b / 2 of the row for the block b = (c % 256) / 32 of group g.
+ *   block's largest |value| / factor <= 6.
  *   Activation rows: the halves hold hi = f16(v) and the narrow values the
- *   residual (v - hi) / factor; lo8 has one scale per row and 64 columns
- *   (byte c / 64), lo4 one per 32.  The row represents hi + narrow *
- *   factor, about 2^-16 (lo8) or 2^-14 (lo4) of v from v.
+ *   residual (v - hi) / factor; lo8 has one scale per row and 64 columns,
+ *   lo4 one per 32.  The row represents hi + narrow * factor, about 2^-16
+ *   (lo8) or 2^-14 (lo4) of v from v.
  *   Weight rows: the halves hold w in f16 and the narrow values a copy
  *   w / factor; lo8 has one scale per row, lo4 one per 32 columns.
+ * Scale arrays (uint8) are blocked by 256 rows so that a GEMM reads 32
+ * rows' scales from a few cache lines: with q scale bytes per group (lo8
+ * activations 2, lo4 8) and G groups per row, the scale of row r, group g,
+ * position b sits at byte (r / 256) * 256 G q + g * 256 q + (r % 256) * q +
+ * b.  Position b: lo8, the 64-column half (c / 64) % 2; lo4, 4 h + s for
+ * the 32-column block 2 s + h of the group (the order the fp4 MFMA's lanes
+ * read).  An array holds whole blocks: round_up(rows, 256) rows.  lo8
+ * weight scales are one byte per row, sc[r].
  * fmt below is QI21_FFN_LO8 or QI21_FFN_LO4. */
 
 /* qi21_op_rowop_parts writing xn in a residual form: mode 2 or 3 (bits 0
  * and 1 as above), h % 128 (lo8) / 256 (lo4) == 0, xn rows of ldxn halves
- * (ldxn >= 1.5 h / 1.25 h, % 4), and the scales in xsc [rows][h / 64]
- * (lo8) / [rows][h / 32] (lo4).  Otherwise as qi21_op_rowop_parts. */
+ * (ldxn >= 1.5 h / 1.25 h, % 4), and the scales in the blocked array xsc
+ * (h / 64 or h / 32 bytes per row).  Otherwise as qi21_op_rowop_parts. */
 int qi21_op_rowop_lo(int fmt, int rows, int h, int mode, float* x, const float* y, int nparts, size_t pstride,
                      void* xn, int ldxn, uint8_t* xsc, const float* mods, int g_off, int s_off, float eps,
                      float oscale, void* stream);
@@ -181,9 +188,9 @@ int qi21_op_rowop_lo(int fmt, int rows, int h, int mode, float* x, const float* 
  * [WG] blocks, with the storage of qi21.h's ffn_mode): A holds M
  * activation rows of lda halves, W N weight rows of ldw halves, each with
  * K columns in the form (lda, ldw >= 1.5 K (lo8) / 1.25 K (lo4), % 8); asc
- * [M][lds] bytes are A's scales (lds >= K / 64 and even, or K / 32 and a
- * multiple of 4), wsc W's: [N] for lo8, [N][ldws] for lo4 (ldws >= K /
- * 32, % 4).  Computes, in f32 on f16 and scaled fp8 / fp4 MFMAs,
+ * is A's blocked scale array (whole 256-row blocks, K / 64 or K / 32 bytes
+ * per row), wsc W's (lo8: [N]; lo4: blocked, K / 32 bytes per row).
+ * Computes, in f32 on f16 and scaled fp8 / fp4 MFMAs,
  *   acc[m][n] = sum_k hiA[m][k] w[n][k] + sum_k resA[m][k] wq[n][k]
  * with resA and wq the scaled narrow values (the residual meets the
  * weight's narrow copy).  Epilogues:
@@ -196,12 +203,12 @@ int qi21_op_rowop_lo(int fmt, int rows, int h, int mode, float* x, const float* 
  *            SWIGLU); the hidden h = silu(g * inscale) * (u * inscale) *
  *            oscale of N/2 columns to out as activation rows in the same
  *            form (rows of ldo halves, ldo >= 0.75 N / 0.625 N) with scales
- *            osc [M][ldos] (ldos >= N / 128 / N / 64)
+ *            in the blocked array osc
  * Requires M >= 1, N % 256 == 0, K % 128 (lo8) / 256 (lo4) == 0, 16-byte
  * aligned A, W, out.  Runs the 256 x 256 4-wave kernel. */
-int qi21_op_gemm_lo(int fmt, int epi, int M, int N, int K, const void* A, int lda, const uint8_t* asc, int lds,
-                    const void* W, int ldw, const uint8_t* wsc, int ldws, void* out, int ldo, const float* gate,
-                    uint8_t* osc, int ldos, int ksplit, float oscale, float inscale, void* stream);
+int qi21_op_gemm_lo(int fmt, int epi, int M, int N, int K, const void* A, int lda, const uint8_t* asc, const void* W,
+                    int ldw, const uint8_t* wsc, void* out, int ldo, const float* gate, uint8_t* osc, int ksplit,
+                    float oscale, float inscale, void* stream);
 
 /* The f16 part of a residual-form weight plane: source row r of src
  * [rows][cols] (QI21_F32 / BF16 / F16) goes to dst row (r / group) *
@@ -213,12 +220,12 @@ int qi21_op_plane_lo(int fmt, int src_dtype, const void* src, int rows, int cols
 
 /* The narrow part of a residual-form weight plane whose f16 values are
  * set: lo8, per row the scale e with the row's largest |w| 2^-e in [128,
- * 256), each byte e4m3(w 2^-e), sc[r] = e + 127 (ldsc unused); lo4, per
- * row and 32 columns the smallest e with the block's largest |w| 2^-e <=
- * 6, each nibble e2m1(w 2^-e), scales at sc[r * ldsc + ...] (ldsc >= cols
- * / 32) in the lo4 order.  Round to nearest even.  cols % 128 / 256 == 0,
- * ld as above. */
-int qi21_op_plane_lo_fill(int fmt, int rows, int cols, void* plane, int ld, uint8_t* sc, int ldsc, void* stream);
+ * 256), each byte e4m3(w 2^-e), sc[r] = e + 127; lo4, per row and 32
+ * columns the smallest e with the block's largest |w| 2^-e <= 6, each
+ * nibble e2m1(w 2^-e), the scales in the blocked array sc (whole 256-row
+ * blocks, cols / 32 bytes per row).  Round to nearest even.  cols % 128 /
+ * 256 == 0, ld as above. */
+int qi21_op_plane_lo_fill(int fmt, int rows, int cols, void* plane, int ld, uint8_t* sc, void* stream);
 
 /* Per-head RMSNorm(norm_q | norm_k) then interleaved-pair RoPE on the q
  * (column 0) and k (column heads*128) parts of panel f16 [rows][ldp], in

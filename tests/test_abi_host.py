@@ -176,36 +176,31 @@ def test_op_entry_points_validate_shapes_on_host():
         lambda: Q.qi21_op_rowop_lo(L4, 4, 384, 2, 1, 1, 1, 0, 1, 480, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
         lambda: Q.qi21_op_rowop_lo(L4, 4, 512, 2, 1, 1, 1, 0, 1, 636, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
         lambda: Q.qi21_op_rowop_lo(5, 4, 512, 2, 1, 1, 1, 0, 1, 1024, 1, 1, 0, 0, 1e-6, 1.0, stream=0),
-        # the residual-form GEMM: K % 128 / 256, N % 256, lda / ldw, scale strides, split, epilogue arguments
-        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 256, 192, 1, 288, 1, 4, 1, 288, 1, 0, 1, 256, stream=0),
-        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 128, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 128, stream=0),
-        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 256, 256, 1, 256, 1, 4, 1, 384, 1, 0, 1, 256, stream=0),
-        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 256, 256, 1, 384, 1, 3, 1, 384, 1, 0, 1, 256, stream=0),
-        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 256, ksplit=3, stream=0),
-        lambda: Q.qi21_op_gemm_lo(L8, 7, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 256, stream=0),  # no gate
-        lambda: Q.qi21_op_gemm_lo(L8, 9, 16, 512, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 384, stream=0),  # no osc
-        lambda: Q.qi21_op_gemm_lo(L8, 10, 16, 512, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 384, osc=1, ldos=8,
-                                  stream=0),  # the lo4 SwiGLU on lo8 operands
-        lambda: Q.qi21_op_gemm_lo(L8, 0, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 256, stream=0),  # F16
-        lambda: Q.qi21_op_gemm_lo(L8, 7, 16, 256, 256, 1, 384, 1, 4, 1, 384, 1, 0, 1, 256, gate=1, ksplit=2,
-                                  stream=0),
-        lambda: Q.qi21_op_gemm_lo(L4, 1, 16, 256, 384, 1, 480, 1, 12, 1, 480, 1, 12, 1, 256, stream=0),  # K % 256
-        lambda: Q.qi21_op_gemm_lo(L4, 1, 16, 256, 512, 1, 632, 1, 16, 1, 640, 1, 16, 1, 256, stream=0),  # lda
-        lambda: Q.qi21_op_gemm_lo(L4, 1, 16, 256, 512, 1, 640, 1, 8, 1, 640, 1, 16, 1, 256, stream=0),   # lds
-        lambda: Q.qi21_op_gemm_lo(L4, 1, 16, 256, 512, 1, 640, 1, 16, 1, 640, 1, 4, 1, 256, stream=0),   # ldws
-        lambda: Q.qi21_op_gemm_lo(L4, 1, 16, 256, 512, 1, 640, 1, 16, 1, 640, 1, 16, 1, 256, ksplit=3, stream=0),
-        lambda: Q.qi21_op_gemm_lo(L4, 9, 16, 1024, 512, 1, 640, 1, 16, 1, 640, 1, 16, 1, 640, osc=1, ldos=8,
-                                  stream=0),  # the lo8 SwiGLU on lo4 operands
-        lambda: Q.qi21_op_gemm_lo(L4, 10, 16, 512, 512, 1, 640, 1, 16, 1, 640, 1, 16, 1, 320, osc=1, ldos=7,
-                                  stream=0),  # ldos < N / 64
+        # the residual-form GEMM: K % 128 / 256, N % 256, lda / ldw, split, epilogue arguments
+        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 256, 192, 1, 288, 1, 1, 288, 1, 1, 256, stream=0),   # K % 128
+        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 128, 256, 1, 384, 1, 1, 384, 1, 1, 128, stream=0),   # N % 256
+        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 256, 256, 1, 256, 1, 1, 384, 1, 1, 256, stream=0),   # lda < 1.5 K
+        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 256, 256, 1, 384, 1, 1, 380, 1, 1, 256, stream=0),   # ldw
+        lambda: Q.qi21_op_gemm_lo(L8, 1, 16, 256, 256, 1, 384, 1, 1, 384, 1, 1, 256, ksplit=3, stream=0),
+        lambda: Q.qi21_op_gemm_lo(L8, 7, 16, 256, 256, 1, 384, 1, 1, 384, 1, 1, 256, stream=0),   # no gate
+        lambda: Q.qi21_op_gemm_lo(L8, 9, 16, 512, 256, 1, 384, 1, 1, 384, 1, 1, 384, stream=0),   # no osc
+        lambda: Q.qi21_op_gemm_lo(L8, 10, 16, 512, 256, 1, 384, 1, 1, 384, 1, 1, 384, osc=1, stream=0),  # lo4 SwiGLU
+        lambda: Q.qi21_op_gemm_lo(L8, 0, 16, 256, 256, 1, 384, 1, 1, 384, 1, 1, 256, stream=0),   # F16
+        lambda: Q.qi21_op_gemm_lo(L8, 7, 16, 256, 256, 1, 384, 1, 1, 384, 1, 1, 256, gate=1, ksplit=2, stream=0),
+        lambda: Q.qi21_op_gemm_lo(L4, 1, 16, 256, 384, 1, 480, 1, 1, 480, 1, 1, 256, stream=0),   # K % 256
+        lambda: Q.qi21_op_gemm_lo(L4, 1, 16, 256, 512, 1, 632, 1, 1, 640, 1, 1, 256, stream=0),   # lda
+        lambda: Q.qi21_op_gemm_lo(L4, 1, 16, 256, 512, 1, 640, 1, 1, 640, 1, 1, 256, ksplit=3, stream=0),
+        lambda: Q.qi21_op_gemm_lo(L4, 9, 16, 1024, 512, 1, 640, 1, 1, 640, 1, 1, 640, osc=1, stream=0),  # lo8 SwiGLU
+        lambda: Q.qi21_op_gemm_lo(L4, 10, 16, 512, 512, 1, 640, 1, 1, 640, 1, 1, 312, osc=1, stream=0),  # ldo
+        lambda: Q.qi21_op_gemm_lo(L4, 10, 16, 256, 512, 1, 640, 1, 1, 640, 1, 1, 320, osc=1, stream=0),  # N / 2 % 256
         lambda: Q.qi21_op_plane_lo(L8, 0, 1, 16, 192, 1, 288, 16, 0, 0, stream=0),
         lambda: Q.qi21_op_plane_lo(L8, 0, 1, 16, 256, 1, 256, 16, 0, 0, stream=0),
         lambda: Q.qi21_op_plane_lo(L4, 0, 1, 16, 384, 1, 480, 16, 0, 0, stream=0),
         lambda: Q.qi21_op_plane_lo(L4, 0, 1, 16, 512, 1, 636, 16, 0, 0, stream=0),
-        lambda: Q.qi21_op_plane_lo_fill(L8, 16, 256, 1, 380, 1, 0, stream=0),
-        lambda: Q.qi21_op_plane_lo_fill(L8, 16, 256, 1, 384, None, 0, stream=0),
-        lambda: Q.qi21_op_plane_lo_fill(L4, 16, 512, 1, 640, 1, 8, stream=0),  # ldsc < cols / 32
-        lambda: Q.qi21_op_plane_lo_fill(2 * L4, 16, 512, 1, 640, 1, 16, stream=0),
+        lambda: Q.qi21_op_plane_lo_fill(L8, 16, 256, 1, 380, 1, stream=0),
+        lambda: Q.qi21_op_plane_lo_fill(L8, 16, 256, 1, 384, None, stream=0),
+        lambda: Q.qi21_op_plane_lo_fill(L4, 16, 512, 1, 636, 1, stream=0),
+        lambda: Q.qi21_op_plane_lo_fill(2 * L4, 16, 512, 1, 640, 1, stream=0),
     ]
     for c in cases:
         with pytest.raises(Q.Qi21Error) as e:
