@@ -59,11 +59,18 @@ def geom_of(spec):
                        in_ch=spec.in_ch, eps=spec.eps)
 
 
-def build_model(spec, opt=None, device="cuda", time_path=False, txt_in=False):
+def build_model(spec, opt=None, device="cuda", time_path=False, txt_in=False, torch_alloc=True):
     """A qi21 model holding the seeded synthetic weights of ``spec`` (and,
-    with ``time_path`` / ``txt_in``, those of the time path / text front)."""
+    with ``time_path`` / ``txt_in``, those of the time path / text front).
+    With ``torch_alloc`` (and no hook already in ``opt``) the library takes
+    its device memory from torch's caching allocator."""
     import torch
     from diffusion_transformer_denoiser_qi21_amd import qi21 as Q
+
+    if torch_alloc:
+        opt = Q.qi21_default_options() if opt is None else opt
+        if not opt.alloc:
+            Q.DeviceAllocator(device).install(opt)
 
     s = spec.seed
     img_in = inputs.device_tensor(s, TID_IMG_IN, (spec.dim, spec.in_ch), W_SIGMA, bf16=spec.bf16, device=device).float()

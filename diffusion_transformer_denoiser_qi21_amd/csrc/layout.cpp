@@ -16,25 +16,34 @@
 #include <vector>
 
 #include "../../include/qi21.h"
+#include "status.h"
 
 namespace {
-int seg_len(const qi21_seg& s) { return s.kind == 0 ? s.h : s.h * s.w; }
+int64_t seg_len(const qi21_seg& s) { return s.kind == 0 ? (int64_t)s.h : (int64_t)s.h * s.w; }
+
+int refuse(const char* why) {
+  qi21::set_error_text(why);
+  return QI21_EINVAL;
+}
 }  // namespace
 
 extern "C" {
 
 int qi21_layout_sizes(const qi21_seg* segs, int nseg, int32_t* lp, int32_t* n) {
-  if (!segs || nseg < 2) return QI21_EINVAL;
+  qi21::set_error_text("");
+  if (!segs || nseg < 2) return refuse("layout: a prefix run and the target image are needed (segs NULL or nseg < 2)");
   int64_t total = 0;
   for (int i = 0; i < nseg; ++i) {
     const qi21_seg& s = segs[i];
-    if ((s.kind != 0 && s.kind != 1) || s.h < 0 || (s.kind == 1 && s.w < 0)) return QI21_EINVAL;
+    if ((s.kind != 0 && s.kind != 1) || s.h < 0 || (s.kind == 1 && s.w < 0))
+      return refuse("layout: a run has an unknown kind or a negative size");
     total += seg_len(s);
+    if (total > (1 << 24)) return refuse("layout: more than 2^24 rows");
   }
   const qi21_seg& t = segs[nseg - 1];
-  if (t.kind != 1 || t.h <= 0 || t.w <= 0) return QI21_EINVAL;
+  if (t.kind != 1 || t.h <= 0 || t.w <= 0) return refuse("layout: the final run must be a non-empty image");
   const int64_t nt = seg_len(t);
-  if (total - nt <= 0 || total > (1 << 24)) return QI21_EINVAL;
+  if (total - nt <= 0) return refuse("layout: the prefix has no rows");
   if (lp) *lp = (int32_t)(total - nt);
   if (n) *n = (int32_t)nt;
   return QI21_OK;
@@ -43,10 +52,12 @@ int qi21_layout_sizes(const qi21_seg* segs, int nseg, int32_t* lp, int32_t* n) {
 int qi21_layout_tables(const qi21_seg* segs, int nseg, const int32_t* axes, float theta, int64_t* pos,
                        uint32_t* vis, float* cos_p, float* sin_p, float* cos_t, float* sin_t) {
   int32_t lp = 0, n = 0;
-  if (qi21_layout_sizes(segs, nseg, &lp, &n) != QI21_OK || !axes) return QI21_EINVAL;
+  const int rc = qi21_layout_sizes(segs, nseg, &lp, &n);
+  if (rc != QI21_OK) return rc;
+  if (!axes) return refuse("layout tables: axes is NULL");
   int hd = 0;
   for (int a = 0; a < 3; ++a) {
-    if (axes[a] <= 0 || axes[a] % 2) return QI21_EINVAL;
+    if (axes[a] <= 0 || axes[a] % 2) return refuse("layout tables: every axis width must be positive and even");
     hd += axes[a];
   }
   const int half = hd / 2;

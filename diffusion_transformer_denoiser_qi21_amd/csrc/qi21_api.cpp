@@ -25,6 +25,7 @@
 #include "../../include/qi21.h"
 #include "../../include/qi21_ops.h"
 #include "qi21_internal.h"
+#include "status.h"
 
 using qi21::f16;
 
@@ -140,10 +141,14 @@ void* dalloc(qi21_model* m, size_t bytes) {
 
 void dfree(qi21_model* m, void* p, size_t bytes) {
   if (!p) return;
-  if (m->o.free)
+  if (m->o.free) {
+    // hipFree waits for the device; a pool allocator may hand the block out
+    // again at once, so nothing of ours may still be running on it
+    (void)hipDeviceSynchronize();
     m->o.free(p, m->o.alloc_ctx);
-  else
+  } else {
     (void)hipFree(p);
+  }
   m->bytes -= std::min(m->bytes, bytes ? bytes : (size_t)256);
 }
 
@@ -576,6 +581,12 @@ int sync_stream(hipStream_t s) {
 extern "C" {
 
 const char* qi21_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"
+
+void qi21::set_error_text(const char* msg) { g_err = msg; }
+
+extern "C" {
 
 void qi21_default_options(qi21_options* o) {
   if (!o) return;
@@ -1345,7 +1356,7 @@ int qi21_op_final(int rows, int h, const float* x, const float* fs, const float*
 
 int qi21_op_mods(int h, const float* mods, float* mods_dev, void* stream) {
   g_err.clear();
-  if (h < 1 || !mods || !mods_dev) return fail(QI21_EINVAL, "mods h %d", h);
+  if (h < 1 || h > 65536 || !mods || !mods_dev) return fail(QI21_EINVAL, "mods h %d", h);
   HIP_OK(qi21::launch_mods(h, mods, mods_dev, (hipStream_t)stream));
   return QI21_OK;
 }

@@ -164,10 +164,67 @@ def qi21_default_options() -> qi21_options:
     return o
 
 
+class DeviceAllocator:
+    """The ``qi21_options`` alloc/free hook backed by torch's caching allocator.
+
+    The library then takes its planes, activations and prefix caches from
+    the same pool as the caller's tensors instead of calling hipMalloc.
+    ``budget`` (bytes, None = unlimited) makes an allocation return NULL once
+    the live total would pass it, which the library reports as ENOMEM.
+    ``live`` maps each address handed out to its size; ``failed`` counts the
+    refused requests.  Callbacks never raise into C: any error is a NULL.
+    """
+
+    def __init__(self, device=None, budget: Optional[int] = None):
+        import torch
+        idx = None if device is None else torch.device(device).index
+        self.device = torch.cuda.current_device() if idx is None else idx
+        self.budget = budget
+        self.live = {}
+        self.failed = 0
+        self.alloc = ALLOC_FN(self._alloc)
+        self.free = FREE_FN(self._free)
+
+    @property
+    def live_bytes(self) -> int:
+        return sum(self.live.values())
+
+    def _alloc(self, nbytes, ctx):
+        try:
+            if self.budget is not None and self.live_bytes + nbytes > self.budget:
+                self.failed += 1
+                return None
+            import torch
+            p = int(torch.cuda.caching_allocator_alloc(int(nbytes), self.device))
+            self.live[p] = int(nbytes)
+            return p
+        except Exception:
+            self.failed += 1
+            return None
+
+    def _free(self, ptr, ctx):
+        try:
+            if ptr in self.live:
+                del self.live[ptr]
+                import torch
+                torch.cuda.caching_allocator_delete(ptr)
+        except Exception:
+            pass
+
+    def install(self, opt: qi21_options) -> qi21_options:
+        opt.alloc, opt.free, opt.alloc_ctx = self.alloc, self.free, None
+        return opt
+
+
+# options (and with them any allocator callbacks) of each live model
+_MODEL_OPTS = {}
+
+
 def qi21_model_create(geom: qi21_geom, opt: Optional[qi21_options], nblocks: int, img_in, proj_out, stream=None):
     h = vp()
     _check(lib().qi21_model_create(C.byref(geom), C.byref(opt) if opt is not None else None, int(nblocks),
                                    _p(img_in), _p(proj_out), _stream(stream), C.byref(h)))
+    _MODEL_OPTS[h.value] = opt
     return h
 
 
@@ -234,6 +291,7 @@ def qi21_release_key(m, key: int):
 
 def qi21_model_destroy(m):
     lib().qi21_model_destroy(m)
+    _MODEL_OPTS.pop(m.value if isinstance(m, vp) else m, None)
 
 
 def qi21_model_bytes(m) -> int:

@@ -56,8 +56,14 @@ typedef struct {
   float eps;
 } qi21_geom;
 
-/* Device allocator hook (e.g. a framework's caching allocator).  NULL alloc
- * = hipMalloc / hipFree.  alloc returns NULL on failure. */
+/* Device allocator hook (e.g. a framework's caching allocator), in the
+ * place of the device path's scoped allocation ([WG] alloc_scoped).  NULL
+ * alloc = hipMalloc / hipFree; alloc and free are given together or not at
+ * all (EINVAL).  alloc returns NULL on failure, which the calling entry
+ * point reports as ENOMEM after handing back, through free, every block it
+ * took itself (the model's earlier buffers stay).  free is called only
+ * after the device has been synchronised, so the block may be reused at
+ * once.  ctx is alloc_ctx, passed through. */
 typedef void* (*qi21_alloc_fn)(size_t bytes, void* ctx);
 typedef void (*qi21_free_fn)(void* ptr, void* ctx);
 
@@ -105,7 +111,9 @@ typedef struct qi21_model qi21_model;
 
 void qi21_default_options(qi21_options* opt);
 
-/* Create a model of `nblocks` blocks.  img_in: [hidden][64]; proj_out:
+/* Create a model of `nblocks` blocks: the resident weights of the device
+ * path ([WG] module doc and prefill: the f16 weight planes are built once
+ * per model and kept for every program; [QI] Qi21Dit names the tensors).  img_in: [hidden][64]; proj_out:
  * [64][hidden] (both copied to library-owned f32 buffers).  Weight planes
  * of all blocks are allocated here (f16, ~ (4 H^2 + 3 H I) * 2 bytes per
  * block) and filled by qi21_model_set_block.  opt may be NULL (defaults).
@@ -207,7 +215,10 @@ int qi21_release_key(qi21_model* m, uint64_t key);
 /* Free everything the model holds ([WG] release).  NULL is a no-op. */
 void qi21_model_destroy(qi21_model* m);
 
-/* The last error of the calling thread (empty string if none). */
+/* The last error of the calling thread (empty string if none): the text
+ * behind the status code, as the pages' calls return an error value with a
+ * message ([WG] step, prefill, geom_ok; [QI] validate).  The pointer stays
+ * valid until the thread's next qi21 call. */
 const char* qi21_last_error(void);
 
 /* Device bytes the model holds (planes, activations, prefix caches). */

@@ -128,6 +128,59 @@ def test_model_create_refuses_bad_ffn_mode_before_device_work():
     assert e.value.code == Q.QI21_EUNSUPPORTED
 
 
+class _FakePool:
+    """An alloc/free hook that hands out made-up addresses (never touched:
+    qi21_model_create takes all its buffers before any device work) and
+    refuses the request numbered ``fail_at``."""
+
+    def __init__(self, fail_at):
+        self.fail_at, self.n, self.live, self.freed = fail_at, 0, {}, []
+        self.alloc = Q.ALLOC_FN(self._alloc)
+        self.free = Q.FREE_FN(self._free)
+
+    def _alloc(self, nbytes, ctx):
+        self.n += 1
+        if self.n - 1 == self.fail_at:
+            return None
+        p = 0x7f0000000000 + self.n * (1 << 32)
+        self.live[p] = nbytes
+        return p
+
+    def _free(self, ptr, ctx):
+        self.freed.append(ptr)
+        del self.live[ptr]
+
+
+@pytest.mark.parametrize("mode", [Q.QI21_FFN_F16, Q.QI21_FFN_LO4])
+def test_failing_allocator_gives_enomem_and_every_block_back(mode):
+    # per block: qkv, O, gate/up, down planes and the two RMSNorm weights
+    # (+ the two scale arrays of a residual form); then img_in, proj_out and
+    # the device flag
+    per_block = 6 + (2 if mode == Q.QI21_FFN_LO4 else 0)
+    total = 2 * per_block + 3
+    for fail_at in (0, 1, per_block + 2, total - 1):
+        pool = _FakePool(fail_at)
+        opt = Q.qi21_default_options()
+        opt.ffn_mode = mode
+        pool_opt = opt
+        pool_opt.alloc, pool_opt.free = pool.alloc, pool.free
+        with pytest.raises(Q.Qi21Error) as e:
+            Q.qi21_model_create(_geom(), pool_opt, 2, 1, 1, stream=0)
+        assert e.value.code == Q.QI21_ENOMEM, (fail_at, str(e.value))
+        assert "did not fit" in str(e.value)
+        assert pool.n == fail_at + 1  # nothing asked after the refusal
+        assert pool.live == {} and len(pool.freed) == fail_at == len(set(pool.freed))
+
+
+def test_allocator_hooks_come_in_pairs():
+    pool = _FakePool(None)
+    opt = Q.qi21_default_options()
+    opt.alloc = pool.alloc
+    with pytest.raises(Q.Qi21Error) as e:
+        Q.qi21_model_create(_geom(), opt, 2, 1, 1, stream=0)
+    assert e.value.code == Q.QI21_EINVAL and pool.n == 0
+
+
 def test_op_entry_points_validate_shapes_on_host():
     L8, L4 = Q.QI21_FFN_LO8, Q.QI21_FFN_LO4
     cases = [

@@ -258,6 +258,51 @@ def test_batched_step_after_a_refused_nonfinite_step(tiny_gpu, tiny_cpu):
         q.qi21_release_key(tiny_gpu, 21 + p)
 
 
+def test_torch_pool_and_enomem_leave_the_model_usable(tiny_cpu):
+    # every device byte comes from torch's caching allocator through the
+    # alloc/free hook; a refused allocation in prefill gives ENOMEM with the
+    # accounting intact, and the same model then steps to the oracle's v
+    q = Q()
+    pool = q.DeviceAllocator()
+    m = bench.build_model(TINY_MODEL, pool.install(q.qi21_default_options()))
+    try:
+        b0 = q.qi21_model_bytes(m)
+        assert b0 > 0 and pool.live_bytes == b0
+        w = CONFIGS["tiny"]
+        d = bench.workload_tensors(w)
+        pool.budget = b0  # nothing more fits: the activations are refused
+        with pytest.raises(q.Qi21Error) as e:
+            bench.prefill(m, 1, d)
+        assert e.value.code == q.QI21_ENOMEM and pool.failed >= 1
+        assert q.qi21_model_bytes(m) == pool.live_bytes == b0
+        out = torch.zeros(d["n"], 64, device="cuda")
+        with pytest.raises(q.Qi21Error) as e:
+            q.qi21_step(m, 1, d["tok"], d["mods"], d["fs"], out)
+        assert e.value.code == q.QI21_ENOKEY  # the refused program was not kept
+        pool.budget = None
+        bench.prefill(m, 1, d)
+        q.qi21_step(m, 1, d["tok"], d["mods"], d["fs"], out)
+        v1 = out.cpu().numpy()
+        err = rel(v1, oracle_v(tiny_cpu, w))
+        print(f"torch pool: v rel L2 {err:.3e}")
+        assert err < V_TOL
+        # a larger second program needs more activation rows than exist
+        big = Workload("big", TINY_MODEL, 9, (24, 24), ((("text", 40),),))
+        db = bench.workload_tensors(big)
+        pool.budget = pool.live_bytes
+        with pytest.raises(q.Qi21Error) as e:
+            bench.prefill(m, 2, db)
+        assert e.value.code == q.QI21_ENOMEM
+        assert q.qi21_model_bytes(m) == pool.live_bytes
+        pool.budget = None
+        out2 = torch.zeros_like(out)
+        q.qi21_step(m, 1, d["tok"], d["mods"], d["fs"], out2)  # program 1 survived
+        assert np.array_equal(out2.cpu().numpy(), v1)
+    finally:
+        q.qi21_model_destroy(m)
+    assert pool.live == {}
+
+
 def test_error_paths_and_eviction(tiny_gpu):
     q = Q()
     w = CONFIGS["tiny"]
