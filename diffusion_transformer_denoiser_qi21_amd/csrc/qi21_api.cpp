@@ -265,6 +265,18 @@ void free_txt_rows(qi21_model* m) {
   m->txt_cap = 0;
 }
 
+// qi21_txt_in's arguments, checked before any device work
+int txt_in_check(const qi21_model* m, int n, const float* feats, const float* out) {
+  if (!m) return fail(QI21_EINVAL, "model is NULL");
+  if (!m->txt_cin) return fail(QI21_EINVAL, "no txt_in weights (qi21_model_set_txt_in)");
+  if (n < 1 || !feats || !out) return fail(QI21_EINVAL, "txt_in: n %d, feats or out NULL", n);
+  return QI21_OK;
+}
+
+// The text front over n rows with the two intermediates in xn [n][cin] and
+// h [n][H] (f16; only n rows of each are read or written)
+int txt_in_run(qi21_model* m, int n, const float* feats, float* out, f16* xn, f16* h, hipStream_t s);
+
 void free_txt(qi21_model* m) {
   free_txt_rows(m);
   const size_t H = m->g.hidden, c = m->txt_cin;
@@ -359,6 +371,17 @@ qi21::GemmArgs gemm_args(int M, int N, int K, const f16* A, int lda, const f16* 
   a.oscale = oscale;
   a.inscale = inscale;
   return a;
+}
+
+int txt_in_run(qi21_model* m, int n, const float* feats, float* out, f16* xn, f16* h, hipStream_t s) {
+  const int H = m->g.hidden, c = m->txt_cin;
+  HIP_OK(qi21::launch_txtnorm(n, c, feats, m->txt_norm, m->g.eps, xn, s));
+  const int tile = m->o.gemm_tile;
+  qi21::GemmArgs g1 = gemm_args(n, H, c, xn, c, m->txt_w1, h, H, 1.0f);
+  HIP_OK(qi21::launch_gemm(qi21::EPI_GELU, g1, tile, s));
+  qi21::GemmArgs g2 = gemm_args(n, H, H, h, H, m->txt_w2, out, H, 1.0f);
+  HIP_OK(qi21::launch_gemm(qi21::EPI_F32, g2, tile, s));
+  return QI21_OK;
 }
 
 // One segment of the rows of a pass (one program's rows in a batch).
@@ -585,6 +608,22 @@ const char* qi21_last_error(void) { return g_err.c_str(); }
 }  // extern "C"
 
 void qi21::set_error_text(const char* msg) { g_err = msg; }
+
+int qi21::txt_in_scratch(qi21_model* m, int n, const float* feats, float* out, void* scratch, size_t bytes,
+                         void* stream) {
+  g_err.clear();
+  int rc = txt_in_check(m, n, feats, out);
+  if (rc) return rc;
+  const size_t H = m->g.hidden, c = m->txt_cin;
+  const size_t xn_bytes = round_up((size_t)n * c * 2, 256), need = xn_bytes + (size_t)n * H * 2;
+  if (!scratch) return fail(QI21_EINVAL, "txt_in: no scratch");
+  if (need > bytes)
+    return fail(QI21_EINVAL, "txt_in without allocation: %d rows need %zu scratch bytes, the limit is %zu (%zu rows)", n,
+                need, bytes, bytes / ((c + H) * 2 + 256));
+  f16* xn = (f16*)scratch;
+  f16* h = (f16*)((char*)scratch + xn_bytes);
+  return txt_in_run(m, n, feats, out, xn, h, (hipStream_t)stream);
+}
 
 extern "C" {
 
@@ -1010,9 +1049,8 @@ int qi21_model_set_txt_in(qi21_model* m, int context_in, int w_dtype, const floa
 
 int qi21_txt_in(qi21_model* m, int n, const float* feats, float* out, void* stream) {
   g_err.clear();
-  if (!m) return fail(QI21_EINVAL, "model is NULL");
-  if (!m->txt_cin) return fail(QI21_EINVAL, "no txt_in weights (qi21_model_set_txt_in)");
-  if (n < 1 || !feats || !out) return fail(QI21_EINVAL, "txt_in: n %d, feats or out NULL", n);
+  int rc = txt_in_check(m, n, feats, out);
+  if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   const int H = m->g.hidden, c = m->txt_cin;
   if (m->txt_cap < n) {
@@ -1027,13 +1065,7 @@ int qi21_txt_in(qi21_model* m, int n, const float* feats, float* out, void* stre
     }
     m->txt_cap = cap;
   }
-  HIP_OK(qi21::launch_txtnorm(n, c, feats, m->txt_norm, m->g.eps, m->txt_xn, s));
-  const int tile = m->o.gemm_tile;
-  qi21::GemmArgs g1 = gemm_args(n, H, c, m->txt_xn, c, m->txt_w1, m->txt_h, H, 1.0f);
-  HIP_OK(qi21::launch_gemm(qi21::EPI_GELU, g1, tile, s));
-  qi21::GemmArgs g2 = gemm_args(n, H, H, m->txt_h, H, m->txt_w2, out, H, 1.0f);
-  HIP_OK(qi21::launch_gemm(qi21::EPI_F32, g2, tile, s));
-  return QI21_OK;
+  return txt_in_run(m, n, feats, out, m->txt_xn, m->txt_h, s);
 }
 
 int qi21_release_key(qi21_model* m, uint64_t key) {

@@ -64,6 +64,8 @@ _SIGS = {
     "qi21_model_set_time": (C.c_int, [vp, C.c_int, vp, vp, vp, vp, vp]),
     "qi21_model_set_txt_in": (C.c_int, [vp, C.c_int, C.c_int, vp, vp, vp, vp]),
     "qi21_txt_in": (C.c_int, [vp, C.c_int, vp, vp, vp]),
+    "qi21_txt_in_noalloc": (C.c_int, [vp, C.c_int, vp, vp, vp]),
+    "qi21_txt_in_noalloc_bytes": (C.c_size_t, []),
     "qi21_time_mods": (C.c_int, [vp, f32, vp, vp, vp]),
     "qi21_step_t": (C.c_int, [vp, u64, vp, f32, vp, vp]),
     "qi21_sample": (C.c_int, [vp, u64, vp, C.c_int, C.POINTER(f32), vp]),
@@ -269,6 +271,14 @@ def qi21_model_set_txt_in(m, context_in: int, w_dtype: Optional[int], txt_norm, 
 
 def qi21_txt_in(m, n: int, feats, out, stream=None):
     _check(lib().qi21_txt_in(m, n, _p(feats), _p(out), _stream(stream)))
+
+
+def qi21_txt_in_noalloc(m, n: int, feats, out, stream=None):
+    _check(lib().qi21_txt_in_noalloc(m, int(n), _p(feats), _p(out), _stream(stream)))
+
+
+def qi21_txt_in_noalloc_bytes() -> int:
+    return int(lib().qi21_txt_in_noalloc_bytes())
 
 
 def qi21_time_mods(m, t: float, mods, fs, stream=None):

@@ -179,6 +179,24 @@ int qi21_model_set_txt_in(qi21_model* m, int context_in, int w_dtype, const floa
  * stream is. */
 int qi21_txt_in(qi21_model* m, int n, const float* feats, float* out, void* stream);
 
+/* qi21_txt_in for callers that cannot allocate device memory during the
+ * call (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and the same result, with the two
+ * intermediates (normalised rows [n][context_in] and GELU hidden [n][H],
+ * f16) in a scratch array of qi21_txt_in_noalloc_bytes() bytes (32 MiB)
+ * that the library holds on each GPU it runs on until the process ends.
+ * Rows fit while round_up(2 n context_in, 256) + 2 n H is within that size
+ * (about 2500 rows at context_in 3584, H 3072); more gives EINVAL before
+ * any device work.  The model (with its txt_in weights) must already
+ * exist; the call allocates nothing and does not synchronise.  Every call
+ * on one GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller.  Errors: EINVAL, EDEVICE. */
+int qi21_txt_in_noalloc(qi21_model* m, int n, const float* feats, float* out, void* stream);
+
+/* Size in bytes of qi21_txt_in_noalloc's scratch array. */
+size_t qi21_txt_in_noalloc_bytes(void);
+
 /* Time-path weights ([QI] Qi21Dit: time_text_embed.timestep_embedder
  * linear_1 [H][256] and linear_2 [H][H], modulation [4H][H], norm_out
  * [H][H]; row-major [out][in], bias-free), element type w_dtype, kept as f32
