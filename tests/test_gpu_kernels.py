@@ -3,7 +3,10 @@
 Every kernel is called through the C ABI (``qi21_op_*``) on seeded inputs
 and compared element by element with the oracle's function on the same
 values: f32 outputs to 1e-5 relative L2, f16 outputs (one rounding to
-binary16) to 2e-3.  Sizes span several tiles with a ragged tail.
+binary16) to 2e-3.  Besides the whole tensor's relative L2, every row's
+own relative L2 must stay within ROW_FACTOR times the same bound, so that
+an error confined to a tail tile, a mask edge or one row cannot hide in
+the global figure.  Sizes span several tiles with a ragged tail.
 """
 import math
 
@@ -12,6 +15,7 @@ import pytest
 
 import inputs
 from oracle import qi21_oracle as O
+from parity import ROW_FACTOR, assert_close, rel, rowrel  # noqa: F401
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -23,12 +27,6 @@ F32_TOL = 1e-5
 def Q():
     from diffusion_transformer_denoiser_qi21_amd import qi21
     return qi21
-
-
-def rel(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
 def f16_host(seed, tid, shape, sigma):
@@ -70,7 +68,7 @@ def test_gemm_epilogues(epi, M, tile):
                        oscale=oscale, tile=tile)
         sync()
         want = O.lin(A, W) * np.float32(oscale)
-        assert rel(out.float().cpu().numpy(), want) < (F16_TOL if epi == "f16" else F32_TOL)
+        assert_close(out.float().cpu().numpy(), want, (F16_TOL if epi == "f16" else F32_TOL))
     elif epi == "swiglu":
         G, U = W[: N // 2], W[N // 2:]
         w13 = torch.empty(N, K, device="cuda", dtype=torch.float16)
@@ -82,7 +80,7 @@ def test_gemm_epilogues(epi, M, tile):
         g = O.lin(A, G) * np.float32(inscale)
         u = O.lin(A, U) * np.float32(inscale)
         want = O.silu(g) * u * np.float32(oscale)
-        assert rel(out.float().cpu().numpy(), want) < F16_TOL
+        assert_close(out.float().cpu().numpy(), want, F16_TOL)
     else:
         h = N // 3
         ld2 = ((M + 63) // 64) * 64
@@ -91,10 +89,10 @@ def test_gemm_epilogues(epi, M, tile):
         q.qi21_op_gemm(q.QI21_EPI_QKV, M, N, K, dA, K, dW, out, 2 * h, vt, ld2, oscale=oscale, tile=tile)
         sync()
         want = O.lin(A, W) * np.float32(oscale)
-        assert rel(out.float().cpu().numpy(), want[:, :2 * h]) < F16_TOL
+        assert_close(out.float().cpu().numpy(), want[:, :2 * h], F16_TOL)
         vtn = vt.float().cpu().numpy()
         cols = vt_pos(np.arange(M))
-        assert rel(vtn[:, cols], want[:, 2 * h:].T) < F16_TOL
+        assert_close(vtn[:, cols], want[:, 2 * h:].T, F16_TOL)
         rest = np.setdiff1d(np.arange(ld2), cols)
         assert np.all(vtn[:, rest] == 0)  # nothing written for rows past M
 
@@ -137,7 +135,7 @@ def test_gemm_pair_operand(epi, M, tile):
         q.qi21_op_gemm_pair(q.QI21_EPI_F32, M, N, K, dA, 2 * K, dW, out, N, oscale=oscale, tile=tile)
         sync()
         want = A64 @ W64.T * oscale
-        assert rel(out.cpu().numpy(), want) < PAIR_TOL
+        assert_close(out.cpu().numpy(), want, PAIR_TOL)
         single = O.lin(hi.astype(np.float32), W) * np.float32(oscale)
         assert rel(single, want) > 10 * PAIR_TOL  # the lo half matters at this tolerance
         return
@@ -153,7 +151,7 @@ def test_gemm_pair_operand(epi, M, tile):
         q.qi21_op_gemm_pair(q.QI21_EPI_SWIGLU, M, N, K, dA, 2 * K, w13, out, N // 2, oscale=oscale, inscale=inscale,
                             tile=tile)
         sync()
-        assert rel(out.float().cpu().numpy(), want) < F16_TOL
+        assert_close(out.float().cpu().numpy(), want, F16_TOL)
     else:
         out = torch.zeros(M, N, device="cuda", dtype=torch.float16)
         q.qi21_op_gemm_pair(q.QI21_EPI_SWIGLU2, M, N, K, dA, 2 * K, w13, out, N, oscale=oscale, inscale=inscale,
@@ -162,7 +160,7 @@ def test_gemm_pair_operand(epi, M, tile):
         o = out.cpu().numpy()
         ohi, olo = o[:, : N // 2], o[:, N // 2:]
         _check_pair(ohi, olo)
-        assert rel(ohi.astype(np.float64) + olo.astype(np.float64), want) < PAIR_TOL
+        assert_close(ohi.astype(np.float64) + olo.astype(np.float64), want, PAIR_TOL)
 
 
 @pytest.mark.parametrize("M", [77, 1600])
@@ -185,7 +183,7 @@ def test_gemm_swiglu_pair_output(M):
     want = g / (1 + np.exp(-g)) * u
     o = out.cpu().numpy()
     _check_pair(o[:, : N // 2], o[:, N // 2:])
-    assert rel(o[:, : N // 2].astype(np.float64) + o[:, N // 2:], want) < PAIR_TOL
+    assert_close(o[:, : N // 2].astype(np.float64) + o[:, N // 2:], want, PAIR_TOL)
 
 
 def test_gemm_plane_conversion_exact():
@@ -260,7 +258,7 @@ def test_flash_parity(case):
     sync()
     visible = vis if vis is not None else np.full(nq, m, np.int64)
     want = O.attention(qa, k, v, visible, heads, hd) * np.float32(oscale)
-    assert rel(out.float().cpu().numpy(), want) < F16_TOL
+    assert_close(out.float().cpu().numpy(), want, F16_TOL)
 
 
 # 32 heads; on 256 CUs 96 queries run as key-split blocks, 2048 as 4-wave
@@ -301,7 +299,7 @@ def test_flash_lazy_rescale_paths(order, nq):
     assert np.isfinite(got).all()
     visible = vis if vis is not None else np.full(nq, n1, np.int64)
     want = O.attention(qe, k, v, visible, heads, hd)
-    assert rel(got, want) < F16_TOL
+    assert_close(got, want, F16_TOL)
 
 
 # ───────────────────────────── row kernels ─────────────────────────────
@@ -322,11 +320,11 @@ def test_rowop_pair_output(mode, rows, h):
     q.qi21_op_rowop(rows, h, mode, dx, dy, xn, xn.shape[1], dm, g_off, s_off, eps, oscale)
     sync()
     xe = O.gated_add(x, y, mods[g_off:g_off + h]) if mode & 1 else x
-    assert rel(dx.cpu().numpy(), xe) < 1e-6
+    assert_close(dx.cpu().numpy(), xe, 1e-6)
     want = O.norm_mod(xe, mods[s_off:s_off + h], eps, dt=np.float64) * oscale
     o = xn.cpu().numpy()
     _check_pair(o[:, :h], o[:, h:])
-    assert rel(o[:, :h].astype(np.float64) + o[:, h:], want) < 2e-6
+    assert_close(o[:, :h].astype(np.float64) + o[:, h:], want, 2e-6)
 
 
 
@@ -344,10 +342,10 @@ def test_rowop_modes(mode, rows, h):
     q.qi21_op_rowop(rows, h, mode, dx, dy, xn, xn.shape[1], dm, g_off, s_off, eps, oscale)
     sync()
     xe = O.gated_add(x, y, mods[g_off:g_off + h]) if mode & 1 else x
-    assert rel(dx.cpu().numpy(), xe) < 1e-6
+    assert_close(dx.cpu().numpy(), xe, 1e-6)
     if mode & 2:
         want = O.norm_mod(xe, mods[s_off:s_off + h], eps) * np.float32(oscale)
-        assert rel(xn.float().cpu().numpy(), want) < F16_TOL
+        assert_close(xn.float().cpu().numpy(), want, F16_TOL)
     else:
         assert torch.all(xn == 0)
 
@@ -384,15 +382,15 @@ def test_rowop_row_forms(rows, h, mode):
     q.qi21_op_rowop(rows, h, mode, dx, dy, xn, xn.shape[1], dm, g_off, s_off, eps, oscale)
     sync()
     xe = O.gated_add(x, y, mods[g_off:g_off + h]) if mode & 1 else x
-    assert rel(dx.cpu().numpy(), xe) < 1e-6
+    assert_close(dx.cpu().numpy(), xe, 1e-6)
     if mode & 2:
         want = O.norm_mod(xe, mods[s_off:s_off + h], eps, dt=np.float64) * oscale
         o = xn.float().cpu().numpy()
         if mode & 4:
             _check_pair(xn[:, :h].cpu().numpy(), xn[:, h:].cpu().numpy())
-            assert rel(o[:, :h].astype(np.float64) + o[:, h:], want) < 2e-6
+            assert_close(o[:, :h].astype(np.float64) + o[:, h:], want, 2e-6)
         else:
-            assert rel(o, want) < F16_TOL
+            assert_close(o, want, F16_TOL)
     else:
         assert torch.all(xn == 0)
 
@@ -418,12 +416,12 @@ def test_qkrope(rows, kdst):
     got = dp.float().cpu().numpy()
     wq_ = O.qk_norm_rope(panel[:, :H], wq, c, s, heads, hd, eps)
     wk_ = O.qk_norm_rope(panel[:, H:2 * H], wk, c, s, heads, hd, eps)
-    assert rel(got[:, :H], wq_) < F16_TOL
+    assert_close(got[:, :H], wq_, F16_TOL)
     if kdst:
-        assert rel(kd.float().cpu().numpy(), wk_) < F16_TOL
+        assert_close(kd.float().cpu().numpy(), wk_, F16_TOL)
         assert np.array_equal(got[:, H:], panel[:, H:])  # k untouched in the panel
     else:
-        assert rel(got[:, H:2 * H], wk_) < F16_TOL
+        assert_close(got[:, H:2 * H], wk_, F16_TOL)
         assert np.array_equal(got[:, 2 * H:], panel[:, 2 * H:])
 
 
@@ -450,7 +448,7 @@ def test_gemm_gated_residual(M, tile, pair):
                          dev(gate), 0.5, tile)
     sync()
     want = x.astype(np.float64) + gate.astype(np.float64) * prod * 0.5
-    assert rel(dx.cpu().numpy(), want) < (PAIR_TOL if pair else F32_TOL * 10)
+    assert_close(dx.cpu().numpy(), want, (PAIR_TOL if pair else F32_TOL * 10))
 
 
 @pytest.mark.parametrize("tile", [0, 1, 2])
@@ -466,7 +464,7 @@ def test_gemm_k_depths(K, tile):
     out = torch.zeros(M, N, device="cuda", dtype=torch.float32)
     q.qi21_op_gemm(q.QI21_EPI_F32, M, N, K, dev(A, torch.float16), K, dev(W, torch.float16), out, N, tile=tile)
     sync()
-    assert rel(out.cpu().numpy(), O.lin(A, W)) < F32_TOL * 10
+    assert_close(out.cpu().numpy(), O.lin(A, W), F32_TOL * 10)
     A32 = inputs.host_array(13, 3, (M, K), 1.0)
     hi, lo = _pair(A32)
     Ap = np.concatenate([hi, lo], axis=1)
@@ -477,7 +475,7 @@ def test_gemm_k_depths(K, tile):
                          tile)
     sync()
     want = A32.astype(np.float64) @ W.astype(np.float64).T
-    assert rel(dx.cpu().numpy(), want) < PAIR_TOL
+    assert_close(dx.cpu().numpy(), want, PAIR_TOL)
 
 
 @pytest.mark.parametrize("tile", [0, 2])
@@ -498,8 +496,8 @@ def test_gemm_split_partials(M, ksplit, K, tile):
     got = part.cpu().numpy()
     for p in range(ksplit):
         want = O.lin(A[:, p * ks:(p + 1) * ks], W[:, p * ks:(p + 1) * ks]) * np.float32(0.5)
-        assert rel(got[p], want) < F32_TOL * 10
-    assert rel(got.sum(axis=0), O.lin(A, W) * np.float32(0.5)) < F32_TOL * 10
+        assert_close(got[p], want, F32_TOL * 10)
+    assert_close(got.sum(axis=0), O.lin(A, W) * np.float32(0.5), F32_TOL * 10)
     if K % (128 * ksplit) == 0:
         kw = K // 2
         Wp = W[:, :kw]
@@ -507,7 +505,7 @@ def test_gemm_split_partials(M, ksplit, K, tile):
         q.qi21_op_gemm_split(M, N, K, kw, dev(A, torch.float16), K, dev(Wp, torch.float16), part, ksplit, 1.0, tile)
         sync()
         want = A[:, :kw].astype(np.float64) @ Wp.astype(np.float64).T + A[:, kw:].astype(np.float64) @ Wp.astype(np.float64).T
-        assert rel(part.cpu().numpy().sum(axis=0), want) < F32_TOL * 10
+        assert_close(part.cpu().numpy().sum(axis=0), want, F32_TOL * 10)
 
 
 @pytest.mark.parametrize("nparts", [1, 2, 3, 4])
@@ -528,15 +526,15 @@ def test_rowop_adds_partial_planes(mode, nparts):
     for p in range(1, nparts):
         ysum = ysum + y[p, :rows]
     xw = x + mods[g_off:g_off + h] * ysum
-    assert rel(dx.cpu().numpy(), xw) < F32_TOL
+    assert_close(dx.cpu().numpy(), xw, F32_TOL)
     if mode & 2:
         v = O.layer_norm(xw, eps) * (1.0 + mods[s_off:s_off + h]) * np.float32(oscale)
         got = xn.float().cpu().numpy()
         if mode & 4:
             got = got[:, :h] + got[:, h:]
-            assert rel(got, v) < F32_TOL
+            assert_close(got, v, F32_TOL)
         else:
-            assert rel(got, v) < F16_TOL
+            assert_close(got, v, F16_TOL)
 
 
 @pytest.mark.parametrize("tile", [0, 2])
@@ -566,8 +564,8 @@ def test_qk_gemm_fused_norm_rope(M, tile):
     want_q = O.qk_norm_rope(O.lin(A, W[:H]), wq, c, s, heads, hd, eps)
     want_k = O.qk_norm_rope(O.lin(A, W[H:]), wk, c, s, heads, hd, eps)
     got_q = qo.float().cpu().numpy()
-    assert rel(got_q[:, :H], want_q) < F16_TOL
-    assert rel(ko.float().cpu().numpy(), want_k) < F16_TOL
+    assert_close(got_q[:, :H], want_q, F16_TOL)
+    assert_close(ko.float().cpu().numpy(), want_k, F16_TOL)
     assert np.all(got_q[:, H:] == 0)  # nothing past the q heads
 
 
@@ -588,7 +586,7 @@ def test_vt_gemm_key_order_and_bound(nkeys, tile):
     got = out.float().cpu().numpy()
     want = (O.lin(X[:nkeys], Wv) * np.float32(0.5)).T
     cols = vt_pos(np.arange(nkeys))
-    assert rel(got[:, cols], want) < F16_TOL
+    assert_close(got[:, cols], want, F16_TOL)
     rest = np.setdiff1d(np.arange(ldo), cols)
     assert np.all(got[:, rest] == 0)
 
@@ -602,7 +600,7 @@ def test_embed(rows, h):
     x = torch.zeros(rows, h, device="cuda")
     q.qi21_op_embed(rows, h, dev(tok), dev(w), x)
     sync()
-    assert rel(x.cpu().numpy(), O.embed_image(tok, w)) < F32_TOL
+    assert_close(x.cpu().numpy(), O.embed_image(tok, w), F32_TOL)
 
 
 @pytest.mark.parametrize("h", [256, 4096])
@@ -620,7 +618,7 @@ def test_final_and_nonfinite_flag(rows, h, offset):
     q.qi21_op_final(rows, h, dev(x), dev(fs), dev(po), 1e-6, out, flag)
     sync()
     want = O.lin(O.layer_norm(x, 1e-6) * fs, po)  # LN(x) * (1 + final_scale), fs = 1 + final_scale
-    assert rel(out.cpu().numpy(), want) < F32_TOL
+    assert_close(out.cpu().numpy(), want, F32_TOL)
     assert int(flag.item()) == 0
     x[rows // 2, 3] = np.inf
     q.qi21_op_final(rows, h, dev(x), dev(fs), dev(po), 1e-6, out, flag)

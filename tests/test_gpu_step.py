@@ -17,6 +17,7 @@ from inputs import CONFIGS
 from inputs.configs import TINY_MODEL, Workload
 from oracle import SynthModel, workload_inputs
 from oracle import qi21_oracle as O
+from parity import ROW_FACTOR, assert_close, rel, rowrel
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -28,9 +29,9 @@ def Q():
     return qi21
 
 
-def rel(a, b):
-    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
-    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+def rel_rows(a, b):
+    """The whole tensor's relative L2 and the largest one row's own"""
+    return rel(a, b), rowrel(a, b)
 
 
 @pytest.fixture(scope="module")
@@ -64,9 +65,9 @@ def test_tiny_prefill_step_parity(tiny_gpu, tiny_cpu):
     w = CONFIGS["tiny"]
     v, _ = gpu_v(tiny_gpu, w)
     want = oracle_v(tiny_cpu, w)
-    err = rel(v, want)
+    err, row = rel_rows(v, want)
     print(f"tiny v rel L2 {err:.3e}")
-    assert err < V_TOL
+    assert err < V_TOL and row < ROW_FACTOR * V_TOL
 
 
 @pytest.mark.parametrize("segs,target", [
@@ -78,9 +79,9 @@ def test_condition_prefix_parity(tiny_gpu, tiny_cpu, segs, target):
     w = Workload("t", TINY_MODEL, 33, target, (tuple(segs),))
     v, _ = gpu_v(tiny_gpu, w, key=2)
     want = oracle_v(tiny_cpu, w)
-    err = rel(v, want)
+    err, row = rel_rows(v, want)
     print(f"{segs} -> {target}: v rel L2 {err:.3e}")
-    assert err < V_TOL
+    assert err < V_TOL and row < ROW_FACTOR * V_TOL
 
 
 def test_cfg_pair_unequal_prefixes_batched(tiny_gpu, tiny_cpu):
@@ -98,13 +99,13 @@ def test_cfg_pair_unequal_prefixes_batched(tiny_gpu, tiny_cpu):
         lay = O.Layout(w.layout(p))
         pre = O.prefill(tiny_cpu, d["x_prefix"], lay)
         want = O.step(tiny_cpu, pre, d["tok"], d["mods"], d["final_scale"])
-        err = rel(outs[p].cpu().numpy(), want)
+        err, row = rel_rows(outs[p].cpu().numpy(), want)
         print(f"cfg prefix {p}: v rel L2 {err:.3e}")
-        assert err < V_TOL
+        assert err < V_TOL and row < ROW_FACTOR * V_TOL
     # batched == one program at a time
     single = torch.zeros_like(outs[1])
     q.qi21_step(tiny_gpu, 11, ds[1]["tok"], ds[1]["mods"], ds[1]["fs"], single)
-    assert rel(single.cpu().numpy(), outs[1].cpu().numpy()) < 1e-6
+    assert_close(single.cpu().numpy(), outs[1].cpu().numpy(), 1e-6, row_tol=2e-5)  # summation order, as below
 
 
 @pytest.fixture(scope="module")
@@ -144,12 +145,12 @@ def test_cfg_pair_shared_attention_launch(wide_gpu, wide_cpu, target):
     for p in range(2):
         got = outs[p].cpu().numpy()
         assert np.isfinite(got).all()
-        err = rel(got, oracle_v(wide_cpu, w, p))
+        err, row = rel_rows(got, oracle_v(wide_cpu, w, p))
         single = torch.zeros_like(outs[p])
         q.qi21_step(wide_gpu, 20 + p, ds[p]["tok"], ds[p]["mods"], ds[p]["fs"], single)
         print(f"{target} program {p}: v rel L2 {err:.3e} (alone vs batched "
               f"{rel(single.cpu().numpy(), got):.3e})")
-        assert err < V_TOL
+        assert err < V_TOL and row < ROW_FACTOR * V_TOL
 
 
 def test_step_is_deterministic(tiny_gpu):
@@ -172,7 +173,7 @@ def test_range_guard_settings(tiny_cpu, shifts):
     try:
         w = CONFIGS["tiny"]
         v, _ = gpu_v(m, w)
-        assert rel(v, oracle_v(tiny_cpu, w)) < V_TOL
+        assert_close(v, oracle_v(tiny_cpu, w), V_TOL)
     finally:
         q.qi21_model_destroy(m)
 
@@ -190,16 +191,20 @@ def test_ffn_mode_option(tiny_cpu, tiny_gpu, mode):
         w = CONFIGS["tiny"]
         v, _ = gpu_v(m, w)
         want = oracle_v(tiny_cpu, w)
-        err = rel(v, want)
+        err, row = rel_rows(v, want)
         base = rel(gpu_v(tiny_gpu, w, key=5)[0], want)
         print(f"tiny v rel L2 ffn_mode {mode} {err:.3e}, single f16 {base:.3e}")
-        assert err < V_TOL and err < base
+        assert err < V_TOL and row < ROW_FACTOR * V_TOL and err < base
         ds = [bench.workload_tensors(w) for _ in range(2)]
         bench.prefill(m, 2, ds[0])
         outs = [torch.zeros(ds[0]["n"], 64, device="cuda") for _ in range(2)]
         q.qi21_step_batch(m, [1, 2], [d["tok"] for d in ds], ds[0]["mods"], ds[0]["fs"], outs)
+        # batched and single passes sum in different orders; where that moves
+        # an f32 value across an f16 rounding boundary at a storage site, one
+        # element of a row moves by 2^-11 of itself, so a row's figure may
+        # reach several times the whole tensor's
         for o in outs:
-            assert rel(o.cpu().numpy(), v) < 1e-6
+            assert_close(o.cpu().numpy(), v, 1e-6, row_tol=2e-5)
     finally:
         q.qi21_model_destroy(m)
 
@@ -253,7 +258,7 @@ def test_batched_step_after_a_refused_nonfinite_step(tiny_gpu, tiny_cpu):
         want = O.step(tiny_cpu, pre, d["tok"], d["mods"], d["final_scale"])
         got = outs[p].cpu().numpy()
         assert np.isfinite(got).all()
-        assert rel(got, want) < V_TOL
+        assert_close(got, want, V_TOL)
     for p in range(2):
         q.qi21_release_key(tiny_gpu, 21 + p)
 
@@ -283,9 +288,9 @@ def test_torch_pool_and_enomem_leave_the_model_usable(tiny_cpu):
         bench.prefill(m, 1, d)
         q.qi21_step(m, 1, d["tok"], d["mods"], d["fs"], out)
         v1 = out.cpu().numpy()
-        err = rel(v1, oracle_v(tiny_cpu, w))
+        err, row = rel_rows(v1, oracle_v(tiny_cpu, w))
         print(f"torch pool: v rel L2 {err:.3e}")
-        assert err < V_TOL
+        assert err < V_TOL and row < ROW_FACTOR * V_TOL
         # a larger second program needs more activation rows than exist
         big = Workload("big", TINY_MODEL, 9, (24, 24), ((("text", 40),),))
         db = bench.workload_tensors(big)
@@ -357,8 +362,8 @@ def test_time_mods_match_oracle(tiny_time, tiny_cpu, t):
     q.qi21_time_mods(tiny_time, t, mods, fs)
     torch.cuda.synchronize()
     want_m, want_f = O.time_mods(tiny_cpu.time(), t)
-    assert rel(mods.cpu().numpy(), want_m) < 1e-5
-    assert rel(fs.cpu().numpy(), 1.0 + want_f) < 1e-6
+    assert_close(mods.cpu().numpy(), want_m, 1e-5)
+    assert_close(fs.cpu().numpy(), 1.0 + want_f, 1e-6)
 
 
 def test_step_t_against_oracle(tiny_time, tiny_cpu):
@@ -370,9 +375,9 @@ def test_step_t_against_oracle(tiny_time, tiny_cpu):
     dd = workload_inputs(w)
     pre = O.prefill(tiny_cpu, dd["x_prefix"], O.Layout(w.layout()))
     mods, fsc = O.time_mods(tiny_cpu.time(), 0.55)
-    err = rel(out.cpu().numpy(), O.step(tiny_cpu, pre, dd["tok"], mods, fsc))
+    err, row = rel_rows(out.cpu().numpy(), O.step(tiny_cpu, pre, dd["tok"], mods, fsc))
     print(f"step_t v rel L2 {err:.3e}")
-    assert err < V_TOL
+    assert err < V_TOL and row < ROW_FACTOR * V_TOL
 
 
 def test_sampler_against_oracle(tiny_time, tiny_cpu):
@@ -385,9 +390,9 @@ def test_sampler_against_oracle(tiny_time, tiny_cpu):
     dd = workload_inputs(w)
     pre = O.prefill(tiny_cpu, dd["x_prefix"], O.Layout(w.layout()))
     want = O.sample(tiny_cpu, pre, dd["tok"], times)
-    err = rel(x.cpu().numpy(), want)
+    err, row = rel_rows(x.cpu().numpy(), want)
     print(f"3-step sample rel L2 {err:.3e}")
-    assert err < V_TOL
+    assert err < V_TOL and row < ROW_FACTOR * V_TOL
     # no time elapses, x unchanged; zero steps are a no-op
     y = d["tok"].clone()
     Q().qi21_sample(tiny_time, 8, y, [0.4, 0.4])
@@ -433,9 +438,9 @@ def test_txt_in_matches_oracle(tiny_txt, tiny_cpu, n):
     torch.cuda.synchronize()
     t = tiny_cpu.txt()
     want = O.embed_text(f, t["txt_norm"], t["txt_in1"], t["txt_in2"], TINY_MODEL.eps)
-    err = rel(out.cpu().numpy(), want)
+    err, row = rel_rows(out.cpu().numpy(), want)
     print(f"txt_in n {n}: rel L2 {err:.3e}")
-    assert err < 2e-3  # the normalised features and the GELU output are f16
+    assert err < 2e-3 and row < ROW_FACTOR * 2e-3  # the normalised features and the GELU output are f16
 
 
 def test_txt_in_feeds_prefill(tiny_txt, tiny_cpu):
@@ -452,9 +457,9 @@ def test_txt_in_feeds_prefill(tiny_txt, tiny_cpu):
     xp = O.embed_text(f, t["txt_norm"], t["txt_in1"], t["txt_in2"], TINY_MODEL.eps)
     pre = O.prefill(tiny_cpu, xp, O.Layout(w.layout()))
     want = O.step(tiny_cpu, pre, dd["tok"], dd["mods"], dd["final_scale"])
-    err = rel(out.cpu().numpy(), want)
+    err, row = rel_rows(out.cpu().numpy(), want)
     print(f"txt_in prefix -> step: v rel L2 {err:.3e}")
-    assert err < V_TOL
+    assert err < V_TOL and row < ROW_FACTOR * V_TOL
 
 
 def test_txt_in_requires_weights(tiny_gpu):
