@@ -198,18 +198,20 @@ def cpu_baseline(w, min_s=10.0):
                       f"x{spec.layers / blocks_done:.2f}"}
 
 
-def recorded_traffic(config: str):
+def recorded_traffic(config: str, ffn: str):
     """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 counter record, or None if none matches this workload or the
-    kernel's source changed since the counters were taken."""
+    rocprofv3 counter record of this FFN form, or None if none matches this
+    workload or any source of the kernel changed since the counters were
+    taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "gate_up_gemm_1024_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"gate_up_gemm_1024_{ffn}_traffic.json")
     if config != "1024" or not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, rec["kernel_source"])
-    if hashlib.sha1(open(src, "rb").read()).hexdigest() != rec["kernel_source_sha1"]:
-        return None
+    srcs = rec.get("kernel_sources") or {rec["kernel_source"]: rec["kernel_source_sha1"]}
+    for src, sha in srcs.items():
+        if hashlib.sha1(open(os.path.join(ROOT, src), "rb").read()).hexdigest() != sha:
+            return None
     return rec["traffic_bytes_per_launch"]
 
 
@@ -337,7 +339,7 @@ def main(argv=None):
             tf = g_fl / (g_ms / 1e3) / 1e12
             sites["all_gemms"] = {"ms_per_step": g_ms / args.site_steps, "tflops": tf, "frac": tf / PEAK_F16_TFLOPS}
         sites["note"] = (f"HIP events around every launch of each site over {args.site_steps} untimed steps after the "
-                         "timed region; algorithmic FLOP (lo8 residual products not counted)")
+                         "timed region; algorithmic FLOP (the residual forms' extra products not counted)")
     # the residual forms run their FFN GEMMs over 1.25x (lo4: fp4 MFMA at
     # four times the f16 rate) or 1.5x (lo8: fp8 at twice) their K in MFMA
     # cycles, the pair form over 2x: the fraction of the peak of that
@@ -364,7 +366,7 @@ def main(argv=None):
         "step_tflop": flops / 1e12,
         "roofline": {"bound": "mfma", "kernel": "gate/up GEMM + SwiGLU", "achieved": w13_tf,
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": w13_tf / PEAK_F16_TFLOPS,
-                     "traffic": recorded_traffic(args.config), "launch_ms": w13_launch_ms,
+                     "traffic": recorded_traffic(args.config, args.ffn), "launch_ms": w13_launch_ms,
                      "launches": int(n_cls[4]), "algorithmic_flop": w13_flop,
                      "mfma_mix_frac": w13_tf * mix / PEAK_F16_TFLOPS},
         "sites": sites,

@@ -18,22 +18,29 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert line and "one GPU" in json.loads(line[0])["error"]
 
 
-def test_traffic_record_matches_only_its_workload_and_source():
-    rec = json.load(open(os.path.join(ROOT, "profiles", "gate_up_gemm_1024_traffic.json")))
-    got = bench.recorded_traffic("1024")
-    # the record is either current (its value) or stale (None): never another number
-    assert got in (None, rec["traffic_bytes_per_launch"])
-    assert bench.recorded_traffic("2048") is None
-    assert bench.recorded_traffic("512") is None
+def test_traffic_record_matches_only_its_workload_form_and_sources():
+    for ffn in ("lo4", "f16"):
+        rec = json.load(open(os.path.join(ROOT, "profiles", f"gate_up_gemm_1024_{ffn}_traffic.json")))
+        got = bench.recorded_traffic("1024", ffn)
+        # the record is either current (its value) or stale (None): never another number
+        assert got in (None, rec["traffic_bytes_per_launch"])
+        assert bench.recorded_traffic("2048", ffn) is None
+        assert bench.recorded_traffic("512", ffn) is None
+    assert bench.recorded_traffic("1024", "pair") is None  # no record for that form
 
 
-def test_traffic_record_is_dropped_when_the_kernel_source_changes(tmp_path, monkeypatch):
-    rec = json.load(open(os.path.join(ROOT, "profiles", "gate_up_gemm_1024_traffic.json")))
+def test_traffic_record_is_dropped_when_a_kernel_source_changes(tmp_path, monkeypatch):
+    rec = json.load(open(os.path.join(ROOT, "profiles", "gate_up_gemm_1024_lo4_traffic.json")))
     fake = tmp_path / "profiles"
     fake.mkdir()
-    src = tmp_path / "k.hip"
-    src.write_text("// not the recorded source\\n")
-    rec = dict(rec, kernel_source="k.hip")
-    (fake / "gate_up_gemm_1024_traffic.json").write_text(json.dumps(rec))
+    srcs = {}
+    for name, sha in rec["kernel_sources"].items():
+        f = tmp_path / os.path.basename(name)
+        f.write_bytes(open(os.path.join(ROOT, name), "rb").read())
+        srcs[os.path.basename(name)] = sha
+    (fake / "gate_up_gemm_1024_lo4_traffic.json").write_text(json.dumps(dict(rec, kernel_sources=srcs)))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.recorded_traffic("1024") is None
+    current = bench.recorded_traffic("1024", "lo4")
+    (tmp_path / "lores.h").write_text("// not the recorded source\n")  # one of the sources changes
+    assert bench.recorded_traffic("1024", "lo4") is None
+    assert current in (None, rec["traffic_bytes_per_launch"])
