@@ -43,6 +43,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -283,19 +284,39 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[p]), __float_as_uint(mx[p]), false, false);
         ex[p] = lo4_exp(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
       }
-      if (row < a.M) {
-        f16* orow = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo;
-        uint8_t* brow = reinterpret_cast<uint8_t*>(orow);
+      // Lane l (hsel 0) holds columns 8g .. 8g + 3 of each 32-column block and
+      // lane l + 32 columns 8g + 4 .. 8g + 7.  One lane-half swap per register
+      // makes the runs contiguous: the lower lane then stores columns 16k ..
+      // 16k + 7 and the upper 16k + 8 .. 16k + 15 of the f16 part (k = 0, 1;
+      // 16 bytes each), and the lower lane the codes of columns 0 .. 15, the
+      // upper those of 16 .. 31 (8 bytes each).  The permlane runs in every
+      // lane; rows past M only skip the stores.
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const float inv = __builtin_ldexpf(1.0f, -ex[p]);
+      for (int p = 0; p < 2; ++p) {
+        const float inv = __builtin_ldexpf(1.0f, -ex[p]);
+        unsigned q[4];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int c = hc + p * 32 + 8 * g + 4 * hsel;
-            *reinterpret_cast<half4*>(orow + lo4_hi_at(c)) = hi[p][g];
-            const floatx4 v = lo[p][g] * inv;
-            *reinterpret_cast<uint16_t*>(brow + lo4_lo_at(c)) = (uint16_t)pack_e2m1(v[0], v[1], v[2], v[3]);
-          }
+        for (int g = 0; g < 4; ++g) {
+          const floatx4 v = lo[p][g] * inv;
+          q[g] = pack_e2m1(v[0], v[1], v[2], v[3]) & 0xffffu;
+        }
+        const auto cs = __builtin_amdgcn_permlane32_swap(q[0] | (q[1] << 16), q[2] | (q[3] << 16), false, false);
+        const u32x2 codes = {(cs[0] & 0xffffu) | (cs[1] << 16), (cs[0] >> 16) | (cs[1] & 0xffff0000u)};
+        u32x4 hv[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const u32x2 x = __builtin_bit_cast(u32x2, hi[p][2 * k]), y = __builtin_bit_cast(u32x2, hi[p][2 * k + 1]);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
+          hv[k] = u32x4{s0[0], s1[0], s0[1], s1[1]};
+        }
+        if (row < a.M) {
+          f16* orow = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo;
+          uint8_t* brow = reinterpret_cast<uint8_t*>(orow);
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+            *reinterpret_cast<u32x4*>(orow + lo4_hi_at(hc + p * 32 + 16 * k + 8 * hsel)) = hv[k];
+          *reinterpret_cast<u32x2*>(brow + lo4_lo_at(hc + p * 32) + 8 * hsel) = codes;
           if (hsel == 0) a.osc[lo4_sc_at(row, hc + p * 32, a.N / 2)] = (uint8_t)(ex[p] + 127);
         }
       }
