@@ -84,6 +84,29 @@ __device__ __forceinline__ void tile_of(int M, int N, int BM, int BN, int& tm, i
 // of every 16 into one 16-byte chunk (the attention kernel's P V operand).
 __device__ __forceinline__ int vt_pos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// The 32 columns of a row that a 32 x 32 accumulator tile gives two lanes:
+// lane l (hsel 0) holds the 4-column chunks 0, 2, 4, 6 (in its g = 0..3
+// parts) and lane l + 32 the chunks 1, 3, 5, 7.  One lane-half swap per
+// register makes the runs contiguous.  pair_halves: chunks of 4 halves; the
+// lower lane returns columns 0..7 and 16..23, the upper 8..15 and 24..31
+// (vector k goes to column 16 k + 8 hsel).  pair_words: chunks of 4 bytes;
+// the lower lane returns the bytes of columns 0..15, the upper those of
+// 16..31 (at byte 16 hsel).  Every lane must take part.
+__device__ __forceinline__ void pair_halves(const half4 (&h)[4], u32x4 (&out)[2]) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const u32x2 x = __builtin_bit_cast(u32x2, h[2 * k]), y = __builtin_bit_cast(u32x2, h[2 * k + 1]);
+    const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
+    out[k] = u32x4{s0[0], s1[0], s0[1], s1[1]};
+  }
+}
+__device__ __forceinline__ u32x4 pair_words(const unsigned (&q)[4]) {
+  const auto s0 = __builtin_amdgcn_permlane32_swap(q[0], q[2], false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(q[1], q[3], false, false);
+  return u32x4{s0[0], s0[1], s1[0], s1[1]};
+}
+
 // Epilogue of a wave whose output rows [r0, r0 + 32 TM) and columns
 // [c0, c0 + 32 TN) were accumulated with the W fragment as the MFMA's A
 // operand (C^T = W A^T): the 32x32 accumulator layout (lane l holds
@@ -114,7 +137,35 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
           }
       }
     }
-  } else if constexpr (EPI == EPI_F32 || EPI == EPI_F16 || EPI == EPI_GELU) {
+  } else if constexpr (EPI == EPI_F16 || EPI == EPI_GELU) {
+    // f16 rows: 16-byte stores through the lane-half swap
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = r0 + i * 32 + l32;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        half4 h[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          floatx4 v = floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e] * a.inscale);
+          }
+          v = v * a.oscale;
+          h[g] = half4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+        }
+        u32x4 hv[2];
+        pair_halves(h, hv);
+        if (row < a.M) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+            *reinterpret_cast<u32x4*>(reinterpret_cast<f16*>(a.out) + obase + (size_t)row * a.ldo + c0 + j * 32 +
+                                      16 * k + 8 * hsel) = hv[k];
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_F32) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int row = r0 + i * 32 + l32;
@@ -124,17 +175,9 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const size_t o = obase + (size_t)row * a.ldo + c0 + j * 32 + 8 * g + 4 * hsel;
-            floatx4 v = floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-            if constexpr (EPI == EPI_GELU) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e] * a.inscale);
-            }
-            v = v * a.oscale;
-            if constexpr (EPI == EPI_F32)
-              *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(a.out) + o) = v;
-            else
-              *reinterpret_cast<half4*>(reinterpret_cast<f16*>(a.out) + o) =
-                  half4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+            const floatx4 v =
+                floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]} * a.oscale;
+            *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(a.out) + o) = v;
           }
       }
     }
@@ -160,23 +203,31 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
         ss = __uint_as_float(r[0]) + __uint_as_float(r[1]);
       }
       const float inv = rsqrtf(ss * (1.0f / 128.0f) + a.eps);
-      if (row < a.M) {
-        // the row's packed table: cos and sin of the lane's two pairs in one 16-byte load
-        const float* tr = a.rope + (size_t)row * 128;
+      // the row's packed table: cos and sin of the lane's two pairs in one
+      // 16-byte load (rows past M read the last row; their results are not
+      // stored, but every lane takes part in the swaps)
+      const float* tr = a.rope + (size_t)min(row, a.M - 1) * 128;
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j) {
+        half4 h[4];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d = j * 32 + 8 * g + 4 * hsel;  // dims d .. d+3: pairs d/2, d/2 + 1
-            const floatx4 w = *reinterpret_cast<const floatx4*>(nw + d);
-            const floatx4 t = *reinterpret_cast<const floatx4*>(tr + d);  // cos d/2, d/2+1, sin d/2, d/2+1
-            const floatx2 cs = floatx2{t[0], t[1]}, sn = floatx2{t[2], t[3]};
-            const float a0 = (acc[i][j][4 * g] * inv) * w[0], b0 = (acc[i][j][4 * g + 1] * inv) * w[1];
-            const float a1 = (acc[i][j][4 * g + 2] * inv) * w[2], b1 = (acc[i][j][4 * g + 3] * inv) * w[3];
-            *reinterpret_cast<half4*>(dst + (size_t)row * ld + d) =
-                half4{(f16)(a0 * cs[0] - b0 * sn[0]), (f16)(a0 * sn[0] + b0 * cs[0]), (f16)(a1 * cs[1] - b1 * sn[1]),
-                      (f16)(a1 * sn[1] + b1 * cs[1])};
-          }
+        for (int g = 0; g < 4; ++g) {
+          const int d = j * 32 + 8 * g + 4 * hsel;  // dims d .. d+3: pairs d/2, d/2 + 1
+          const floatx4 w = *reinterpret_cast<const floatx4*>(nw + d);
+          const floatx4 t = *reinterpret_cast<const floatx4*>(tr + d);  // cos d/2, d/2+1, sin d/2, d/2+1
+          const floatx2 cs = floatx2{t[0], t[1]}, sn = floatx2{t[2], t[3]};
+          const float a0 = (acc[i][j][4 * g] * inv) * w[0], b0 = (acc[i][j][4 * g + 1] * inv) * w[1];
+          const float a1 = (acc[i][j][4 * g + 2] * inv) * w[2], b1 = (acc[i][j][4 * g + 3] * inv) * w[3];
+          h[g] = half4{(f16)(a0 * cs[0] - b0 * sn[0]), (f16)(a0 * sn[0] + b0 * cs[0]), (f16)(a1 * cs[1] - b1 * sn[1]),
+                       (f16)(a1 * sn[1] + b1 * cs[1])};
+        }
+        u32x4 hv[2];
+        pair_halves(h, hv);
+        if (row < a.M) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+            *reinterpret_cast<u32x4*>(dst + (size_t)row * ld + j * 32 + 16 * k + 8 * hsel) = hv[k];
+        }
       }
     }
   } else if constexpr (EPI == EPI_VT) {
@@ -192,21 +243,25 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
       const int row = r0 + i * 32 + l32;
       if (row < a.M) {
         f16* orow = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo;
+        // keys base + 4 hsel .. + 3 (chunk 2m) and base + 8 + 4 hsel .. + 3
+        // (chunk 2m + 1) land at positions base + 8 hsel .. + 7: one 16-byte
+        // store.  A group of 16 keys is below cz whole or not at all, and the
+        // host guarantees nvalid <= cz.
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int c = c0 + j * 32 + 8 * g + 4 * hsel;
-            half4 v;
+          for (int m = 0; m < 2; ++m) {
+            const int base = c0 + j * 32 + 16 * m;
+            if (base < cz) {
+              half8 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (f16)(acc[i][j][4 * g + e] * a.oscale);
-            if (c + 3 < a.nvalid) {
-              *reinterpret_cast<half4*>(orow + vt_pos(c)) = v;
-            } else if (c < cz) {
+              for (int h = 0; h < 2; ++h) {
+                const int c = base + 8 * h + 4 * hsel;
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (c + e >= a.nvalid) v[e] = (f16)0.0f;
-              *reinterpret_cast<half4*>(orow + vt_pos(c)) = v;
+                for (int e = 0; e < 4; ++e)
+                  v[4 * h + e] = c + e < a.nvalid ? (f16)(acc[i][j][4 * (2 * m + h) + e] * a.oscale) : (f16)0.0f;
+              }
+              *reinterpret_cast<half8*>(orow + base + 8 * hsel) = v;
             }
           }
       }
@@ -240,20 +295,29 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
       }
       const int ex = lo8_exp(mx);
       const float inv = __builtin_ldexpf(1.0f, -ex);
-      if (row < a.M) {
-        f16* orow = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo;
-        uint8_t* brow = reinterpret_cast<uint8_t*>(orow);
+      // contiguous runs through the lane-half swap (every lane takes part;
+      // rows past M skip the stores)
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
+      for (int p = 0; p < 2; ++p) {
+        unsigned q[4];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int c = hc + p * 32 + 8 * g + 4 * hsel;
-            *reinterpret_cast<half4*>(orow + lo8_hi_at(c)) = hi[p][g];
-            const floatx4 v = lo[p][g] * inv;
-            *reinterpret_cast<unsigned*>(brow + lo8_lo_at(c)) = pack_e4m3(v[0], v[1], v[2], v[3]);
-          }
-        if (hsel == 0) a.osc[lo8_sc_at(row, hc, a.N / 2)] = (uint8_t)(ex + 127);
+        for (int g = 0; g < 4; ++g) {
+          const floatx4 v = lo[p][g] * inv;
+          q[g] = pack_e4m3(v[0], v[1], v[2], v[3]);
+        }
+        const u32x4 codes = pair_words(q);
+        u32x4 hv[2];
+        pair_halves(hi[p], hv);
+        if (row < a.M) {
+          f16* orow = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo;
+          uint8_t* brow = reinterpret_cast<uint8_t*>(orow);
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+            *reinterpret_cast<u32x4*>(orow + lo8_hi_at(hc + p * 32 + 16 * k + 8 * hsel)) = hv[k];
+          *reinterpret_cast<u32x4*>(brow + lo8_lo_at(hc + p * 32) + 16 * hsel) = codes;
+        }
       }
+      if (row < a.M && hsel == 0) a.osc[lo8_sc_at(row, hc, a.N / 2)] = (uint8_t)(ex + 127);
     }
   } else if constexpr (EPI == EPI_SWIGLU4) {
     // the wave's 4 column tiles are 64 hidden columns, two 32-column scale
@@ -303,13 +367,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
         const auto cs = __builtin_amdgcn_permlane32_swap(q[0] | (q[1] << 16), q[2] | (q[3] << 16), false, false);
         const u32x2 codes = {(cs[0] & 0xffffu) | (cs[1] << 16), (cs[0] >> 16) | (cs[1] & 0xffff0000u)};
         u32x4 hv[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const u32x2 x = __builtin_bit_cast(u32x2, hi[p][2 * k]), y = __builtin_bit_cast(u32x2, hi[p][2 * k + 1]);
-          const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
-          hv[k] = u32x4{s0[0], s1[0], s0[1], s1[1]};
-        }
+        pair_halves(hi[p], hv);
         if (row < a.M) {
           f16* orow = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo;
           uint8_t* brow = reinterpret_cast<uint8_t*>(orow);
@@ -326,23 +384,30 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& a, floatx16 (&acc)
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int row = r0 + i * 32 + l32;
-      if (row < a.M) {
 #pragma unroll
-        for (int p = 0; p < TN / 2; ++p)
+      for (int p = 0; p < TN / 2; ++p) {
+        half4 hi[4], lo[4];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            half4 hi, lo;
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float h = silu_f(acc[i][2 * p][4 * g + e] * a.inscale) * (acc[i][2 * p + 1][4 * g + e] * a.inscale) *
-                              a.oscale;
-              hi[e] = (f16)h;
-              lo[e] = (f16)(h - (float)hi[e]);  // exact in f32
-            }
-            f16* op = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo + c0 / 2 + p * 32 + 8 * g + 4 * hsel;
-            *reinterpret_cast<half4*>(op) = hi;
-            if constexpr (EPI == EPI_SWIGLU2) *reinterpret_cast<half4*>(op + a.N / 2) = lo;
+          for (int e = 0; e < 4; ++e) {
+            const float h = silu_f(acc[i][2 * p][4 * g + e] * a.inscale) * (acc[i][2 * p + 1][4 * g + e] * a.inscale) *
+                            a.oscale;
+            hi[g][e] = (f16)h;
+            lo[g][e] = (f16)(h - (float)hi[g][e]);  // exact in f32
           }
+        // contiguous runs through the lane-half swap (every lane takes part)
+        u32x4 hv[2], lv[2];
+        pair_halves(hi, hv);
+        if constexpr (EPI == EPI_SWIGLU2) pair_halves(lo, lv);
+        if (row < a.M) {
+          f16* op = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo + c0 / 2 + p * 32 + 8 * hsel;
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            *reinterpret_cast<u32x4*>(op + 16 * k) = hv[k];
+            if constexpr (EPI == EPI_SWIGLU2) *reinterpret_cast<u32x4*>(op + a.N / 2 + 16 * k) = lv[k];
+          }
+        }
       }
     }
   }
