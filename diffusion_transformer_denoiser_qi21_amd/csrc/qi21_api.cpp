@@ -1111,6 +1111,9 @@ int op_gemm(int epi, int M, int N, int K, int ka, const void* A, int lda, const 
   if (!A || !W || !out) return fail(QI21_EINVAL, "gemm pointer is NULL");
   const int ocols = epi == QI21_EPI_SWIGLU ? N / 2 : epi == QI21_EPI_QKV ? 2 * N / 3 : N;
   if (ldo < ocols) return fail(QI21_EINVAL, "ldo %d < %d output columns", ldo, ocols);
+  // f16 rows of the row-layout epilogues are written in 16-byte vectors
+  if (epi != QI21_EPI_F32 && epi != QI21_EPI_QKV && ldo % 8)
+    return fail(QI21_EINVAL, "ldo %d: f16 output rows need ldo %% 8 == 0", ldo);
   if (epi == QI21_EPI_QKV && ((N / 3) % 128 || N % 3 || !out2 || ld2 % 4 || ld2 < M))
     return fail(QI21_EINVAL, "qkv epilogue needs N/3 %% 128 == 0, out2, ld2 %% 4 == 0, ld2 >= M");
   if (tile < -1 || tile > 2 || (tile != 1 && tile != -1 && N % 256)) return fail(QI21_EINVAL, "tile %d for N %d", tile, N);
@@ -1179,7 +1182,7 @@ int qi21_op_rope_pack(int n, const float* cos, const float* sin, float* out, voi
 int qi21_op_qk_gemm(int M, int H, const void* A, int lda, const void* W, void* q_out, int ldq, void* k_out, int ldk,
                     const float* norm_q, const float* norm_k, const float* rope, float eps, int tile, void* stream) {
   g_err.clear();
-  if (M < 1 || H < 128 || H % 128 || lda % 8 || lda < H || ldq % 4 || ldk % 4 || ldq < H || ldk < H)
+  if (M < 1 || H < 128 || H % 128 || lda % 8 || lda < H || ldq % 8 || ldk % 8 || ldq < H || ldk < H)
     return fail(QI21_EINVAL, "qk gemm M %d H %d lda %d ldq %d ldk %d", M, H, lda, ldq, ldk);
   if (!A || !W || !q_out || !k_out || !norm_q || !norm_k || !rope) return fail(QI21_EINVAL, "qk gemm pointer NULL");
   if (tile == -1) tile = 0;
@@ -1198,7 +1201,7 @@ int qi21_op_qk_gemm(int M, int H, const void* A, int lda, const void* W, void* q
 int qi21_op_vt_gemm(int H, int nkeys, int K, const void* Wv, int lda, const void* X, void* out, int ldo, float oscale,
                     int tile, void* stream) {
   g_err.clear();
-  if (H < 1 || nkeys < 1 || K < 64 || K % 64 || lda % 8 || lda < K || ldo % 4 || (size_t)ldo < round_up(nkeys, 16))
+  if (H < 1 || nkeys < 1 || K < 64 || K % 64 || lda % 8 || lda < K || ldo % 8 || (size_t)ldo < round_up(nkeys, 16))
     return fail(QI21_EINVAL, "vt gemm H %d nkeys %d K %d lda %d ldo %d", H, nkeys, K, lda, ldo);
   if (!Wv || !X || !out) return fail(QI21_EINVAL, "vt gemm pointer NULL");
   if (tile == -1) tile = 0;
@@ -1312,8 +1315,8 @@ int qi21_op_gemm_lo(int fmt, int epi, int M, int N, int K, const void* A, int ld
   if (epi == QI21_EPI_F32 && (ldo < N || ldo % 4 || (ksplit > 1 && ldo != N)))
     return fail(QI21_EINVAL, "residual gemm f32 ldo %d (>= N, %% 4; = N when split)", ldo);
   const long hrow = l8 ? 3L * N / 4 : 5L * N / 8;  // halves of an output row of N/2 columns
-  if (epi == sw && (!osc || ldo < hrow || ldo % 4 || (N / 2) % g))
-    return fail(QI21_EINVAL, "residual gemm swiglu ldo %d (>= %ld, %% 4), osc, N / 2 %% %d", ldo, hrow, g);
+  if (epi == sw && (!osc || ldo < hrow || ldo % 8 || (N / 2) % g))
+    return fail(QI21_EINVAL, "residual gemm swiglu ldo %d (>= %ld, %% 8), osc, N / 2 %% %d", ldo, hrow, g);
   qi21::GemmArgs a = gemm_args(M, N, (int)krow, (const f16*)A, lda, (const f16*)W, out, ldo, oscale, inscale);
   a.ldw = ldw;
   a.lo = l8 ? 8 : 4;

@@ -37,8 +37,9 @@ enum { QI21_EPI_F16 = 0, QI21_EPI_F32 = 1, QI21_EPI_SWIGLU = 2, QI21_EPI_QKV = 3
  *           out[r][c] = f16(h), out[r][N/2 + c] = f16(h - f16(h)); ldo >= N
  *           (the hidden of the QI21_FFN_PAIR option, qi21.h)
  * Requires M >= 1, N % 128 == 0, K % 64 == 0, lda % 8 == 0, lda >= K,
- * ldo >= output columns, ldo % 4 == 0, 16-byte aligned A, W and out, for
- * QKV (N/3) % 128 == 0, ld2 % 4 == 0, ld2 >= M.
+ * ldo >= output columns, ldo % 8 == 0 for f16 outputs (rows are written in
+ * 16-byte vectors) and % 4 for F32 and QKV, 16-byte aligned A, W and out,
+ * for QKV (N/3) % 128 == 0, ld2 % 4 == 0, ld2 >= M.
  * tile: -1 automatic, 0 = 256x256 with 4 waves, 2 = 256x256 with 8 waves
  * (both need N % 256 == 0), 1 = 128x128. */
 int qi21_op_gemm(int epi, int M, int N, int K, const void* A, int lda, const void* W, void* out, int ldo,
@@ -83,7 +84,7 @@ int qi21_op_gemm_split(int M, int N, int K, int kw, const void* A, int lda, cons
  * packed table rope f32 [M][128] that qi21_op_rope_pack writes; q heads go
  * to q_out f16 [M][ldq], k heads to k_out f16 [M][ldk], both at column
  * head*128.  Requires M >= 1, H % 128 == 0, lda % 8 == 0, lda >= H, ldq,
- * ldk >= H and % 4 == 0, 16-byte aligned pointers.  tile: -1 or 0 (4
+ * ldk >= H and % 8 == 0, 16-byte aligned pointers.  tile: -1 or 0 (4
  * waves), 2 (8 waves). */
 int qi21_op_qk_gemm(int M, int H, const void* A, int lda, const void* W, void* q_out, int ldq, void* k_out, int ldk,
                     const float* norm_q, const float* norm_k, const float* rope, float eps, int tile, void* stream);
@@ -102,7 +103,7 @@ int qi21_op_rope_pack(int n, const float* cos, const float* sin, float* out, voi
  * [H][lda], X f16 rows of K columns (row stride K); X must hold
  * round_up(nkeys, 256) readable rows (the kernel reads whole 256-row
  * tiles, and rows past nkeys only feed unwritten columns).  Requires
- * K % 64 == 0, lda % 8 == 0, lda >= K, ldo % 4 == 0, ldo >=
+ * K % 64 == 0, lda % 8 == 0, lda >= K, ldo % 8 == 0, ldo >=
  * round_up(nkeys, 16).  tile: -1 or 0 (4 waves), 2 (8 waves). */
 int qi21_op_vt_gemm(int H, int nkeys, int K, const void* Wv, int lda, const void* X, void* out, int ldo, float oscale,
                     int tile, void* stream);
@@ -202,8 +203,8 @@ int qi21_op_rowop_lo(int fmt, int rows, int h, int mode, float* x, const float* 
  *   SWIGLU8 (lo8) / SWIGLU4 (lo4): W the interleaved gate/up plane (see
  *            SWIGLU); the hidden h = silu(g * inscale) * (u * inscale) *
  *            oscale of N/2 columns to out as activation rows in the same
- *            form (rows of ldo halves, ldo >= 0.75 N / 0.625 N) with scales
- *            in the blocked array osc
+ *            form (rows of ldo halves, ldo >= 0.75 N / 0.625 N and % 8,
+ *            written in 16-byte vectors) with scales in the blocked array osc
  * Requires M >= 1, N % 256 == 0, K % 128 (lo8) / 256 (lo4) == 0, 16-byte
  * aligned A, W, out.  Runs the 256 x 256 4-wave kernel. */
 int qi21_op_gemm_lo(int fmt, int epi, int M, int N, int K, const void* A, int lda, const uint8_t* asc, const void* W,

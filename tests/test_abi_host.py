@@ -196,6 +196,11 @@ def test_op_entry_points_validate_shapes_on_host():
         lambda: Q.qi21_op_rowop(4, 256, 5, 1, 1, 1, 512, 1, 0, 0, 1e-6, 1.0, stream=0),
         lambda: Q.qi21_op_rowop(4, 256, 8, 1, 1, 1, 256, 1, 0, 0, 1e-6, 1.0, stream=0),
         lambda: Q.qi21_op_gemm(5, 16, 128, 64, 1, 64, 1, 1, 128, stream=0),           # no such epilogue
+        # f16 output rows are written in 16-byte vectors: ldo % 8
+        lambda: Q.qi21_op_gemm(0, 16, 128, 64, 1, 64, 1, 1, 132, stream=0),
+        lambda: Q.qi21_op_gemm(2, 16, 256, 64, 1, 64, 1, 1, 132, stream=0),
+        lambda: Q.qi21_op_qk_gemm(16, 256, 1, 256, 1, 1, 260, 1, 256, 1, 1, 1, 1e-6, stream=0),
+        lambda: Q.qi21_op_vt_gemm(256, 100, 256, 1, 256, 1, 1, 116, stream=0),
         lambda: Q.qi21_op_gemm(4, 16, 128, 64, 1, 64, 1, 1, 64, stream=0),            # swiglu2 needs ldo >= N
         lambda: Q.qi21_op_gemm_pair(1, 16, 128, 64, 1, 100, 1, 1, 128, stream=0),     # lda < 2K
         lambda: Q.qi21_op_gemm_pair(3, 16, 384, 64, 1, 128, 1, 1, 384, stream=0),     # no qkv pair epilogue
