@@ -601,6 +601,13 @@ struct FinalSlice {
 };
 }  // namespace
 
+// v = (LN(x) fs) proj_out^T for 16 rows per block in one pass over x.  With
+// s the row's first element, LN(x)_c fs_c = inv (x_c - mean) fs_c, so
+//   v_o = inv (sum_c (x_c - s) fs_c w_oc - (mean - s) sum_c fs_c w_oc).
+// Wave w streams columns [w h / 16, (w + 1) h / 16) of all 16 rows: the
+// 16x16x4 f32 MFMAs take (x - s) fs against proj_out, and the same loads
+// give each row's sums of (x - s) and (x - s)^2 (the shift keeps the
+// variance sum well conditioned) and each output's sum_c fs_c w_oc.
 // (amdgpu_waves_per_eu: the scheduler may keep 128 registers per lane, so the
 // loads run ahead instead of being moved next to their use)
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void final_kernel(int rows, int h, const float* __restrict__ x,
@@ -608,43 +615,15 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
                                                      float eps, float* __restrict__ out, int* __restrict__ flag) {
   constexpr int NWV = 16;
   __shared__ float part[NWV][16][64];
-  __shared__ float mean_s[16], inv_s[16];
+  __shared__ float bpart[NWV][64];
+  __shared__ float s1p[NWV][16], s2p[NWV][16];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int r0 = blockIdx.x * 16;
-  {
-    const float* xrow = x + (size_t)min(r0 + wave, rows - 1) * h;
-    const float4v* xr = reinterpret_cast<const float4v*>(xrow);
-    const float shift = xrow[0];
-    float s1 = 0.0f, s2 = 0.0f;
-    // four loads in flight per lane (h / 4 is a multiple of 64, so the
-    // bound is the same for the whole wave; lanes past it add zeros)
-    for (int c0 = 0; c0 < (h >> 2); c0 += 256) {
-      float4v v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = c0 + 64 * j + lane;
-        v[j] = c < (h >> 2) ? xr[c] : float4v{shift, shift, shift, shift};
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4v d = v[j] - shift;
-        s1 += (d[0] + d[1]) + (d[2] + d[3]);
-        s2 += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
-      }
-    }
-    const float m1 = wave_sum(s1) / (float)h;
-    const float var = fmaxf(wave_sum(s2) / (float)h - m1 * m1, 0.0f);
-    if (lane == 0) {
-      mean_s[wave] = shift + m1;
-      inv_s[wave] = rsqrtf(var + eps);
-    }
-  }
-  __syncthreads();
   const int rl = lane & 15, q = lane >> 4;
-  const float mean = mean_s[rl], inv = inv_s[rl];
+  // rows of the block past the end read as zeros (and are not stored)
+  const float shift = r0 + rl < rows ? x[(size_t)(r0 + rl) * h] : 0.0f;
   // Buffer loads (an intrinsic, not a plain load, so the compiler does not
   // fold the two buffers' loads back into one load next to the MFMAs).
-  // Rows of the block past the end read as zeros and are not stored.
   const auto rx = __builtin_amdgcn_make_buffer_rsrc((void*)(x + (size_t)r0 * h), 0, min(rows - r0, 16) * h * 4,
                                                     0x00020000);
   const auto rf = __builtin_amdgcn_make_buffer_rsrc((void*)fs, 0, h * 4, 0x00020000);
@@ -661,15 +640,28 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) sl.w[nb] = ld(rw, wo + nb * wnb + c);
   };
+  // lane (rl, q) of a slice: row rl, columns 4q .. 4q + 3 (MFMA A row rl,
+  // k = q) and, for output 16 nb + rl, the same columns of proj_out (B k =
+  // q, column rl)
   floatx4 acc[4];
+  float bsum[4], s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) acc[nb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int nb = 0; nb < 4; ++nb) {
+    acc[nb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    bsum[nb] = 0.0f;
+  }
   auto mma = [&](const FinalSlice& sl) {
-    const float4v av = (sl.x - mean) * inv * sl.f;
+    const float4v d = sl.x - shift;
+    s1 += (d[0] + d[1]) + (d[2] + d[3]);
+    s2 += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
+    const float4v av = d * sl.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], sl.w[nb][j], acc[nb], 0, 0, 0);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      bsum[nb] += (sl.f[0] * sl.w[nb][0] + sl.f[1] * sl.w[nb][1]) + (sl.f[2] * sl.w[nb][2] + sl.f[3] * sl.w[nb][3]);
   };
   // two slices in flight: each buffer is refilled right after its MFMAs
   // (cq is a multiple of 16; an odd count of slices skips the last sb)
@@ -684,6 +676,20 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
       fetch(c0 + 48, sb);
     }
   }
+  // the four lanes of a row (q = 0..3) hold its four column classes
+#pragma unroll
+  for (int o = 16; o < 64; o <<= 1) {
+    s1 += __shfl_xor(s1, o);
+    s2 += __shfl_xor(s2, o);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) bsum[nb] += __shfl_xor(bsum[nb], o);
+  }
+  if (q == 0) {
+    s1p[wave][rl] = s1;
+    s2p[wave][rl] = s2;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) bpart[wave][16 * nb + rl] = bsum[nb];
+  }
   // lane l holds rows 4q .. 4q+3 of column l % 16 of each 16-column block
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
@@ -691,9 +697,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
     for (int i = 0; i < 4; ++i) part[wave][4 * q + i][nb * 16 + rl] = acc[nb][i];
   __syncthreads();
   const int r = t >> 6, o = t & 63;  // one output per thread
-  float v = 0.0f;
+  float a = 0.0f, b = 0.0f, m1 = 0.0f, m2 = 0.0f;
 #pragma unroll
-  for (int k = 0; k < NWV; ++k) v += part[k][r][o];
+  for (int k = 0; k < NWV; ++k) {
+    a += part[k][r][o];
+    b += bpart[k][o];
+    m1 += s1p[k][r];
+    m2 += s2p[k][r];
+  }
+  m1 /= (float)h;  // mean - shift
+  const float var = fmaxf(m2 / (float)h - m1 * m1, 0.0f);
+  const float v = rsqrtf(var + eps) * (a - m1 * b);
   if (r0 + r < rows) {
     out[(size_t)(r0 + r) * 64 + o] = v;
     if (!__builtin_isfinite(v)) atomicOr(flag, 1);
