@@ -1,24 +1,24 @@
 // MFMA GEMM of the denoiser's four projection sites (qkv, O, gate/up, down).
 //
-// C[M][N] = A[M][K] * W[N][K]^T with f16 operands and f32 accumulation,
-// the contraction done by v_mfma_f32_32x32x16_f16 (gfx950).  Both operands
-// are K-contiguous in HBM (activations row-major, weight planes [out][in]),
-// which is exactly the layout the MFMA A and B fragments want, so no
-// operand is ever transposed.
+// C[M][N] = A[M][K] * W[N][K]^T with f16 operands and f32 accumulation.
+// Both operands are K-contiguous in HBM (activations row-major, weight
+// planes [out][in]), which is exactly the layout the MFMA A and B
+// fragments want, so no operand is ever transposed.
 //
-// Two kernels share the epilogues:
+// Three kernels share the tile walk, the LDS layout and the loads:
 //
-// * gemm_dma_kernel, the large-M kernel: block tile 256 x 256 x 64, 8 waves
-//   of 128 x 64 (two per SIMD; a 4-wave form of 128 x 128 is kept), 2 LDS
-//   stages filled by buffer loads that write straight into LDS (no register
-//   staging).  Each load reads 8 whole 128-byte rows, which the L2 -> CU
-//   path serves about 1.4x faster than 16 half rows.  A-rows past M come
-//   back as zeros from the buffer resource's range check.  The main loop is
-//   branch-free and its schedule is pinned: each MFMA is paired with at most
-//   one LDS fragment read and one LDS-bound buffer load.  One barrier per
-//   k-tile, after its third k-step's fragment reads: the next k-tile is then
-//   resident and this stage may be refilled; the refill is spread over the
-//   fourth k-step and the first k-step of the next k-tile.
+// * gemm16_kernel, the large-M kernel of the step: block tile 256 x 256 x
+//   64, 4 waves of 128 x 128 on v_mfma_f32_16x16x32_f16 (lo4: plus the
+//   scaled fp4 MFMA), 2 LDS stages filled by buffer loads that write
+//   straight into LDS (no register staging).  Each load reads 8 whole
+//   128-byte rows, which the L2 -> CU path serves about 1.4x faster than
+//   16 half rows.  A-rows past M come back as zeros from the buffer
+//   resource's range check.  The main loop is branch-free and its
+//   schedule is pinned; one barrier per k-tile, after which all loads of
+//   the k-tile two ahead go out.
+// * gemm_dma_kernel, the same tile on v_mfma_f32_32x32x16_f16: the lo8 form,
+//   the qkv split, the 8-wave form (128 x 64 per wave) and work units with
+//   an odd number of k-tiles.
 // * gemm_rs_kernel, the small-M / narrow-N kernel: block tile BM x BN x 64,
 //   global -> registers -> LDS, double-buffered.
 //
@@ -972,6 +972,540 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_dma_kernel(GemmArgs a) {
   __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));  // no LDS-bound load outlives the block
 }
 
+// ───────────────────── large-M kernel, 16 x 16 x 32 MFMAs ─────────────────────
+namespace {
+
+// Row layout of a 16 x 16 accumulator tile of C^T = W A^T (the W fragment
+// as the MFMA's A operand): lane l holds output row l % 16 of the tile and
+// its 4 consecutive output columns 4 (l / 16) .. + 3 in registers 0..3.
+// Two tiles j0 (even) and j0 + 1 merge through one v_permlane16_swap per
+// register into runs of 8 columns: lane group g = l / 16 then holds
+// columns m16_col(g) .. + 7 of the 32 the pair covers.  Every lane must
+// take part.
+__device__ __forceinline__ int m16_col(int g) { return 16 * (g & 1) + 8 * (g >> 1); }
+__device__ __forceinline__ u32x4 merge16(const half4& x, const half4& y) {
+  const u32x2 xv = __builtin_bit_cast(u32x2, x), yv = __builtin_bit_cast(u32x2, y);
+  const auto s0 = __builtin_amdgcn_permlane16_swap(xv[0], yv[0], false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(xv[1], yv[1], false, false);
+  return u32x4{s0[0], s1[0], s0[1], s1[1]};
+}
+__device__ __forceinline__ half4 to_half4(const floatx4& v) { return half4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]}; }
+// sum / max of a value over the four lane groups that share an output row
+__device__ __forceinline__ float row_sum16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float row_max16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Epilogue of a wave whose output rows [r0, r0 + 128) and columns [c0, c0 +
+// 128) sit in 8 x 8 tiles of 16 x 16 (tile (i, j): rows r0 + 16 i .., columns
+// c0 + 16 j ..): lane l holds row r0 + 16 i + l % 16 and columns c0 + 16 j +
+// 4 g .. + 3, g = l / 16.
+template <int EPI>
+__device__ __forceinline__ void epilogue16(const GemmArgs& a, floatx4 (&acc)[8][8], int r0, int c0, int lane,
+                                           size_t obase) {
+  // lane indices opaque here: address arithmetic derived from them stays in
+  // the epilogue instead of being hoisted out of the tile loop, where its
+  // registers would compete with the main loop's
+  int l16 = lane & 15, g = lane >> 4;
+  asm volatile("" : "+v"(l16), "+v"(g));
+  if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = r0 + 16 * i + l16;
+      if (row < a.M) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = c0 + 16 * j + 4 * g;
+          floatx4* xp = reinterpret_cast<floatx4*>(reinterpret_cast<float*>(a.out) + (size_t)row * a.ldo + c);
+          const floatx4 gt = *reinterpret_cast<const floatx4*>(a.gate + c);
+          floatx4 x = *xp;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(gt[e], acc[i][j][e] * a.oscale, x[e]);
+          *xp = x;
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_F32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = r0 + 16 * i + l16;
+      if (row < a.M) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(a.out) + obase + (size_t)row * a.ldo + c0 + 16 * j +
+                                      4 * g) = acc[i][j] * a.oscale;
+      }
+    }
+  } else if constexpr (EPI == EPI_F16 || EPI == EPI_GELU) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = r0 + 16 * i + l16;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        floatx4 v[2] = {acc[i][2 * p], acc[i][2 * p + 1]};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[u][e] = gelu_f(v[u][e] * a.inscale);
+          }
+          v[u] = v[u] * a.oscale;
+        }
+        const u32x4 o = merge16(to_half4(v[0]), to_half4(v[1]));
+        if (row < a.M)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<f16*>(a.out) + obase + (size_t)row * a.ldo + c0 + 32 * p +
+                                    m16_col(g)) = o;
+      }
+    }
+  } else if constexpr (EPI == EPI_QKROPE) {
+    // the wave's 128 columns are one head (c0 % 128 == 0); a row's 128
+    // accumulators sit in its four lane groups
+    const int H = a.N / 2;
+    const bool isk = c0 >= H;
+    const float* nw = isk ? a.nk : a.nq;
+    f16* dst = isk ? a.kout + (c0 - H) : reinterpret_cast<f16*>(a.out) + c0;
+    const int ld = isk ? a.ldk : a.ldo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = r0 + 16 * i + l16;
+      float ss = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(acc[i][j][e], acc[i][j][e], ss);
+      const float inv = rsqrtf(row_sum16(ss) * (1.0f / 128.0f) + a.eps);
+      // the row's packed table: cos and sin of the lane's two pairs in one
+      // 16-byte load (rows past M read the last row; their results are not
+      // stored, but every lane takes part in the swaps)
+      const float* tr = a.rope + (size_t)min(row, a.M - 1) * 128;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        half4 h[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = 2 * p + u;
+          const int d = 16 * j + 4 * g;  // dims d .. d+3: pairs d/2, d/2 + 1
+          const floatx4 w = *reinterpret_cast<const floatx4*>(nw + d);
+          const floatx4 t = *reinterpret_cast<const floatx4*>(tr + d);  // cos d/2, d/2+1, sin d/2, d/2+1
+          const float a0 = (acc[i][j][0] * inv) * w[0], b0 = (acc[i][j][1] * inv) * w[1];
+          const float a1 = (acc[i][j][2] * inv) * w[2], b1 = (acc[i][j][3] * inv) * w[3];
+          h[u] = half4{(f16)(a0 * t[0] - b0 * t[2]), (f16)(a0 * t[2] + b0 * t[0]), (f16)(a1 * t[1] - b1 * t[3]),
+                       (f16)(a1 * t[3] + b1 * t[1])};
+        }
+        const u32x4 o = merge16(h[0], h[1]);
+        if (row < a.M) *reinterpret_cast<u32x4*>(dst + (size_t)row * ld + 32 * p + m16_col(g)) = o;
+      }
+    }
+  } else if constexpr (EPI == EPI_VT) {
+    // output rows are V dims, columns are keys: key c goes to vt_pos(c),
+    // which swaps bits 2 and 3, so the lane groups g = 0, 2 of a 16-key tile
+    // fill positions 0..7 and g = 1, 3 positions 8..15.  Tiles 2p and 2p + 1
+    // merge through v_permlane32_swap: lane group g then holds positions
+    // 16 (g >> 1) + 8 (g & 1) .. + 7 of the pair's 32.  Columns from nvalid
+    // up to the leading dimension (whole groups of 16) get zeros: the
+    // attention kernel reads whole 64-key tiles and multiplies the columns
+    // past the keys by P = 0, which must not meet a stale non-finite value.
+    const int cz = a.ldo & ~15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = r0 + 16 * i + l16;
+      f16* orow = reinterpret_cast<f16*>(a.out) + (size_t)min(row, a.M - 1) * a.ldo;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        u32x2 x[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int c = c0 + 32 * p + 16 * u + 4 * g;
+          half4 h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = c + e < a.nvalid ? (f16)(acc[i][2 * p + u][e] * a.oscale) : (f16)0.0f;
+          x[u] = __builtin_bit_cast(u32x2, h);
+        }
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x[0][0], x[1][0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x[0][1], x[1][1], false, false);
+        const int base = c0 + 32 * p + 16 * (g >> 1);  // this lane's 16-key group
+        // a group of 16 keys is below cz whole or not at all, and the host
+        // guarantees nvalid <= cz
+        if (row < a.M && base < cz)
+          *reinterpret_cast<u32x4*>(orow + base + 8 * (g & 1)) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU4) {
+    // the wave's 128 W rows are two groups p of 32 gate rows (tiles 4p,
+    // 4p + 1) and the matching 32 up rows (4p + 2, 4p + 3): 64 hidden
+    // columns, one 32-column scale block per group and row
+    const int hc = c0 / 2;  // first hidden column of the wave
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = r0 + 16 * i + l16;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        half4 hi[2];
+        floatx4 lo[2];
+        float mx = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float h = silu_f(acc[i][4 * p + u][e] * a.inscale) * (acc[i][4 * p + 2 + u][e] * a.inscale) * a.oscale;
+            hi[u][e] = (f16)h;
+            lo[u][e] = h - (float)hi[u][e];  // exact in f32
+            mx = fmaxf(mx, fabsf(lo[u][e]));
+          }
+        const int ex = lo4_exp(row_max16(mx));
+        const float inv = __builtin_ldexpf(1.0f, -ex);
+        unsigned q[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const floatx4 v = lo[u] * inv;
+          q[u] = pack_e2m1(v[0], v[1], v[2], v[3]);
+        }
+        // the codes of the lane's 8 columns, like the halves: one swap
+        const auto cs = __builtin_amdgcn_permlane16_swap(q[0], q[1], false, false);
+        const unsigned codes = (cs[0] & 0xffffu) | (cs[1] << 16);
+        const u32x4 hv = merge16(hi[0], hi[1]);
+        if (row < a.M) {
+          f16* orow = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo;
+          uint8_t* brow = reinterpret_cast<uint8_t*>(orow);
+          const int c = hc + 32 * p + m16_col(g);
+          *reinterpret_cast<u32x4*>(orow + lo4_hi_at(c)) = hv;
+          *reinterpret_cast<unsigned*>(brow + lo4_lo_at(c)) = codes;
+          if (g == 0) a.osc[lo4_sc_at(row, hc + 32 * p, a.N / 2)] = (uint8_t)(ex + 127);
+        }
+      }
+      // one row slice at a time: hoisting every slice's accumulator reads
+      // would crowd the registers the main loop needs
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {  // EPI_SWIGLU, EPI_SWIGLU2: gate / up groups as for EPI_SWIGLU4
+    static_assert(EPI == EPI_SWIGLU || EPI == EPI_SWIGLU2, "row-layout epilogue");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = r0 + 16 * i + l16;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        half4 hi[2], lo[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float h = silu_f(acc[i][4 * p + u][e] * a.inscale) * (acc[i][4 * p + 2 + u][e] * a.inscale) * a.oscale;
+            hi[u][e] = (f16)h;
+            lo[u][e] = (f16)(h - (float)hi[u][e]);  // exact in f32
+          }
+        const u32x4 hv = merge16(hi[0], hi[1]);
+        u32x4 lv = u32x4{0, 0, 0, 0};
+        if constexpr (EPI == EPI_SWIGLU2) lv = merge16(lo[0], lo[1]);
+        if (row < a.M) {
+          f16* op = reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo + c0 / 2 + 32 * p + m16_col(g);
+          *reinterpret_cast<u32x4*>(op) = hv;
+          if constexpr (EPI == EPI_SWIGLU2) *reinterpret_cast<u32x4*>(op + a.N / 2) = lv;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// The 4-wave 256 x 256 x 64 kernel on v_mfma_f32_16x16x32_f16: each wave
+// computes 128 x 128 as 8 x 8 tiles of 16 x 16 (256 accumulators).  Loads,
+// LDS layout, tile order and the persistent walk are those of
+// gemm_dma_kernel; what differs:
+//
+// * A k-tile is two k-steps of 32.  A lane's fragment of k-step s is the
+//   16-byte chunk 4 s + l / 16 of its row, rows l % 16 of each 16-row
+//   slice.  B (W) fragments are double-buffered; an A fragment is
+//   refilled in place once its 8 MFMAs are issued (96 registers).
+// * All 16 loads of k-tile t + 2 go out in the k-step right after the
+//   barrier of k-tile t, so each has a whole k-tile to land.
+// * Stage indices are compile-time constants: k-tiles run in pairs (lo4:
+//   groups of five in pairs), so a unit needs an even number of k-tiles
+//   (lo4: of groups), and no fragment address is computed in the loop.
+// * LO4: a group of four f16 k-tiles and one e2m1 k-tile per 256 columns.
+//   An e2m1 k-tile's k-step s is one v_mfma_scale_f32_16x16x128_f8f6f4 per
+//   tile (fp4 operands, same chunks as f16); lane group g takes scale
+//   block g of the k-step (block 4 s + g of the group), which sits at byte
+//   (g >> 1) + 2 s of the scale dword at 4 (g & 1).
+//
+// LSP / LOFF: a load after every LSP-th MFMA from the LOFF-th; BPOS: the
+// MFMA of a row of 8 after which the next B fragment is read.  These fix
+// the instruction order; the register allocator keeps the accumulators in
+// AGPRs only for some of them (checked on the built code).
+template <int EPI, int LO, int LSP, int LOFF, int BPOS>
+__global__ __launch_bounds__(256, 1) void gemm16_kernel(GemmArgs a) {
+  constexpr bool LO4 = LO == 4;
+  constexpr int NL = 8, NQ = 16, TM = 8, TN = 8, MM = 64;
+  extern __shared__ __attribute__((aligned(16))) f16 smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int K = a.K;
+  const int KT = K / DBK / a.ksplit;  // k-tiles per work unit (LO4: a multiple of 5)
+  const int ldw = a.ldw ? a.ldw : a.kw;
+  const int tiles_n = a.N / DBN, tiles_m = (a.M + DBM - 1) / DBM;
+  const int ntiles = tiles_n * tiles_m, nunits = ntiles * a.ksplit;
+  int seq0, seq_end, seq_step;
+  {
+    const int nblk = gridDim.x, b = blockIdx.x;
+    if (nblk < nunits && (nblk & 7) == 0) {
+      const int per_xcd = nblk >> 3, x = b & 7, li = b >> 3;
+      const int chunk = (nunits + 7) >> 3;
+      seq0 = x * chunk + li;
+      seq_end = min(nunits, (x + 1) * chunk);
+      seq_step = per_xcd;
+    } else {
+      seq0 = b;
+      seq_end = b + 1;
+      seq_step = 1;
+    }
+  }
+  auto tile_rc = [&](int sq, int& tm, int& tn, int& kt0) __attribute__((always_inline)) {
+    kt0 = (sq / ntiles) * KT;
+    sq %= ntiles;
+    constexpr int G = 4;
+    if (tiles_m % G == 0) {
+      const int per = G * tiles_n;
+      const int gg = sq / per, w = sq - gg * per;
+      tm = gg * G + w % G;
+      tn = w / G;
+    } else {
+      tm = sq / tiles_n;
+      tn = sq - tm * tiles_n;
+    }
+  };
+  int voa[8], vob[8];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int p = (wave * NL + i) * 64 + lane;
+    const int r = p >> 3, c = (p & 7) ^ dswz(r);
+    voa[i] = (r * a.lda + 8 * c) * 2 - (i & 3) * 1024;
+    vob[i] = (r * ldw + 8 * c) * 2 - (i & 3) * 1024;
+  }
+  auto rsrc_a = [&](int m0) __attribute__((always_inline)) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(a.A + (size_t)m0 * a.lda), 0,
+                                             (min(a.M - m0, DBM) - 1) * a.lda * 2 + K * 2, 0x00020000);
+  };
+  auto rsrc_b = [&](int n0) __attribute__((always_inline)) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (size_t)n0 * ldw), 0, DBN * ldw * 2, 0x00020000);
+  };
+  const int KTW = a.kw / DBK;
+  int kt0 = 0;
+  // load q of unit-local k-tile t into stage st (as in gemm_dma_kernel)
+  auto load1 = [&](__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int st, int t, int q) __attribute__((always_inline)) {
+    const bool w = q >= NL;
+    const int i = w ? q - NL : q;
+    f16* base = smem + st * DSTAGE + (w ? DBM * DBK : 0) + (wave * NL + (i & ~3)) * 64 * 8;
+    const __amdgpu_buffer_rsrc_t r = w ? rb : ra;
+    const int vo = w ? vob[i] : voa[i];
+    const int tg = kt0 + t;
+    const int so = (w && tg >= KTW ? tg - KTW : tg) * DBK * 2;
+    switch (i & 3) {
+      case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base, 16, vo, so, 0, 0); break;
+      case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base, 16, vo, so, 1024, 0); break;
+      case 2: __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base, 16, vo, so, 2048, 0); break;
+      default: __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base, 16, vo, so, 3072, 0); break;
+    }
+  };
+  floatx4 acc[TM][TN];
+  half8 af[TM], bf[2][TN];
+  // this lane's row offsets (halves) in a stage for k-steps 0 and 1: row
+  // l16 of each 16-row slice (whose swizzle is that of l16), chunk 4 s + g4
+  const int sw = dswz(l16);
+  const int ro0 = l16 * DBK + ((g4 ^ sw) * 8);
+  const int ro1 = l16 * DBK + (((4 + g4) ^ sw) * 8);
+  auto readA = [&](int st, int kq, int i) __attribute__((always_inline)) {
+    const f16* sa = smem + st * DSTAGE + (kq ? ro1 : ro0);
+    af[i] = *reinterpret_cast<const half8*>(sa + (wm * 128 + i * 16) * DBK);
+  };
+  auto readB = [&](int st, int kq, int b, int j) __attribute__((always_inline)) {
+    const f16* sa = smem + st * DSTAGE + (kq ? ro1 : ro0);
+    bf[b][j] = *reinterpret_cast<const half8*>(sa + DBM * DBK + (wn * 128 + j * 16) * DBK);
+  };
+  // scale dwords of a group (LO4): per A row and per W row of the lane,
+  // shifted so that bytes 0 and 2 are k-steps 0 and 1
+  int asc[TM], wsc[TN];
+  auto mfma1 = [&](bool fp4, int b, int k) __attribute__((always_inline)) {
+    const int i = k / TN, j = k % TN;
+    if (!fp4) {
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[b][j], af[i], acc[i][j], 0, 0, 0);
+    } else {
+      const i32x8 wv = __builtin_bit_cast(i32x8, __builtin_shufflevector(__builtin_bit_cast(u32x4, bf[b][j]),
+                                                                         u32x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7));
+      const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(__builtin_bit_cast(u32x4, af[i]),
+                                                                         u32x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7));
+      if (b == 0)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, av, acc[i][j], 4, 4, 0, wsc[j], 0, asc[i]);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, av, acc[i][j], 4, 4, 2, wsc[j], 2, asc[i]);
+    }
+  };
+  // One k-step: the MFMAs of k-step b (B buffer b); when rd, the fragments
+  // of k-step rkq of stage rst (B into buffer b ^ 1 after MFMA 8 j + BPOS,
+  // A i in place after MFMA 8 i + 7); when ld, the loads of k-tile tl into
+  // stage lst.
+  auto step = [&](bool fp4, int b, bool rd, int rst, int rkq, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                  bool ld, int lst, int tl) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < MM; ++k) {
+      mfma1(fp4, b, k);
+      if (ld && k % LSP == LOFF && k / LSP < NQ) load1(ra, rb, lst, tl, k / LSP);
+      if (rd && k % 8 == BPOS) readB(rst, rkq, b ^ 1, k / 8);
+      if (rd && k % 8 == 7) readA(rst, rkq, k / 8);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // The accumulators held in AGPRs at a loop head: without this the
+  // register allocator may give the loop-carried values VGPR homes and
+  // copy all 256 through VGPRs every iteration (the MFMAs read and write
+  // AGPRs directly, so pinning costs nothing).
+  auto pin_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) asm volatile("" : "+a"(acc[i][j]));
+  };
+  auto sync_tile = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // k-tile t of stage s: k-step 0 (reads k-step 1), barrier, k-step 1
+  // (reads k-step 0 of the next k-tile when rdn; loads k-tile t + 2 into
+  // stage s when ld)
+  auto ktile = [&](bool fp4, int s, int t, bool rdn, bool ld, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb) __attribute__((always_inline)) {
+    step(fp4, 0, true, s, 1, ra, rb, false, 0, 0);
+    sync_tile();
+    step(fp4, 1, rdn, s ^ 1, 0, ra, rb, ld, s, t + 2);
+  };
+  // k-tiles 0 and 1 of the unit at (tm, tn, kt0)
+  auto prologue = [&](int tm, int tn) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t ra = rsrc_a(tm * DBM), rb = rsrc_b(tn * DBN);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) load1(ra, rb, 0, 0, q);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) load1(ra, rb, 1, 1, q);
+  };
+
+  int tm, tn;
+  tile_rc(seq0, tm, tn, kt0);
+  prologue(tm, tn);
+  for (int sq = seq0; sq < seq_end; sq += seq_step) {
+    const int m0 = tm * DBM, n0 = tn * DBN;
+    const size_t obase = (size_t)(kt0 / KT) * a.pstride;  // partial plane of a split unit
+    const __amdgpu_buffer_rsrc_t ra = rsrc_a(m0), rb = rsrc_b(n0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    // the unit's last k-step, after the next unit's prologue
+    auto finish = [&](bool fp4) __attribute__((always_inline)) {
+      const int nsq = sq + seq_step;
+      if (nsq < seq_end) {
+        tile_rc(nsq, tm, tn, kt0);
+        prologue(tm, tn);
+      }
+      step(fp4, 1, false, 0, 0, ra, rb, false, 0, 0);
+    };
+    if constexpr (LO4) {
+      // the tile's 256-row blocks of the blocked scale arrays
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.asc + (size_t)m0 * a.lds), 0, DBM * a.lds, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rw =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.wsc + (size_t)n0 * a.ldws), 0, DBN * a.ldws, 0x00020000);
+      const int sh = 8 * (g4 >> 1);
+      auto load_sc = [&](int t) __attribute__((always_inline)) {  // the group of unit-local k-tile t
+        const int o = ((kt0 + t) / 5) * 2048 + 4 * (g4 & 1);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) asc[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, o + (wm * 128 + i * 16 + l16) * 8, 0, 0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) wsc[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rw, o + (wn * 128 + j * 16 + l16) * 8, 0, 0);
+      };
+      auto shift_sc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) asc[i] = (int)((unsigned)asc[i] >> sh);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) wsc[j] = (int)((unsigned)wsc[j] >> sh);
+      };
+      load_sc(0);
+      // k-tile 0 landed (with the first unit, k-tile 1 and the scales may
+      // still be in flight; after an epilogue, its stores share the counter)
+      if (sq == seq0)
+        __builtin_amdgcn_s_waitcnt(wait_imm(NQ + TM + TN, 15));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int r = 0; r < 8; ++r) { readA(0, 0, r); readB(0, 0, 0, r); }
+      __builtin_amdgcn_sched_barrier(0);
+      // The fp4 k-tile t + 4 of a group from stage s (k-step 0 after the
+      // scales of the group, landed four barriers ago, are shifted into
+      // place).  nx: a group follows (read its first fragments, load its
+      // second k-tile, then fetch its scales).
+      auto fp4_tile = [&](int s, int t, bool nx) __attribute__((always_inline)) {
+        shift_sc();
+        step(true, 0, true, s, 1, ra, rb, false, 0, 0);
+        sync_tile();
+        if (nx) {
+          step(true, 1, true, s ^ 1, 0, ra, rb, true, s, t + 6);
+          load_sc(t + 5);
+        } else {
+          finish(true);
+        }
+      };
+      // a group from stage s: f16 k-tiles t .. t + 3, the fp4 k-tile t + 4
+      auto group = [&](int s, int t, bool nx) __attribute__((always_inline)) {
+        ktile(false, s, t, true, true, ra, rb);
+        ktile(false, s ^ 1, t + 1, true, true, ra, rb);
+        ktile(false, s, t + 2, true, true, ra, rb);
+        ktile(false, s ^ 1, t + 3, true, nx, ra, rb);
+        fp4_tile(s, t, nx);
+      };
+      // groups in pairs (an even number of groups); the last ends with the
+      // unit's last k-step
+      for (int t = 0; t < KT - 10; t += 10) {
+        pin_acc();
+        group(0, t, true);
+        group(1, t + 5, true);
+      }
+      group(0, KT - 10, true);
+      group(1, KT - 5, false);
+    } else {
+      // k-tile 0 landed.  After an epilogue its stores share the vector
+      // memory counter with these loads, so wait for all of them.
+      if (sq == seq0)
+        __builtin_amdgcn_s_waitcnt(wait_imm(NQ, 15));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int r = 0; r < 8; ++r) { readA(0, 0, r); readB(0, 0, 0, r); }
+      __builtin_amdgcn_sched_barrier(0);
+      // k-tiles in pairs (an even number of them)
+      for (int t = 0; t < KT - 2; t += 2) {
+        pin_acc();
+        ktile(false, 0, t, true, true, ra, rb);
+        ktile(false, 1, t + 1, true, true, ra, rb);
+      }
+      ktile(false, 0, KT - 2, true, false, ra, rb);
+      step(false, 0, true, 1, 1, ra, rb, false, 0, 0);
+      sync_tile();
+      finish(false);
+    }
+    epilogue16<EPI>(a, acc, m0 + wm * 128, n0 + wn * 128, lane, obase);
+  }
+  __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));  // no LDS-bound load outlives the block
+}
+
 // ───────────────────── small-M kernel: register-staged, BM x BN x 64 ─────────────────────
 namespace {
 __device__ __forceinline__ int swz8(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
@@ -1071,8 +1605,40 @@ __global__ __launch_bounds__(256) void gemm_rs_kernel(GemmArgs a) {
 
 namespace {
 
+// the 16 x 16 x 32 kernel with the instruction order that keeps its
+// accumulators in AGPRs (LSP = 4, LOFF = 1, BPOS = 1)
+template <int EPI, int LO>
+hipError_t launch16(const GemmArgs& a, hipStream_t s) {
+  constexpr size_t lds = (size_t)DNS * DSTAGE * 2;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm16_kernel<EPI, LO, 4, 1, 1>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int tiles = ((a.M + DBM - 1) / DBM) * (a.N / DBN) * a.ksplit;
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+      cus = 256;
+    cus &= ~7;
+  }
+  const int blocks = tiles > cus ? cus : tiles;
+  hipLaunchKernelGGL((gemm16_kernel<EPI, LO, 4, 1, 1>), dim3(blocks), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+// 4-wave launches of the f16 and lo4 forms run the 16 x 16 x 32 kernel
+// when a work unit has an even number of k-tiles (lo4: of groups); lo8,
+// the qkv split, the 8-wave form and the other counts the 32 x 32 x 16 one
 template <int EPI, int NW, int LO = 0>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
+  if constexpr (NW == 4 && LO != 8 && EPI != EPI_QKV && EPI != EPI_SWIGLU8) {
+    const int kt = a.K / DBK / a.ksplit;  // k-tiles per unit
+    if (LO == 4 ? kt % 10 == 0 : (kt % 2 == 0 && kt >= 2)) return launch16<EPI, LO>(a, s);
+  }
   constexpr size_t lds = (size_t)DNS * DSTAGE * 2;
   static bool attr = false;
   if (!attr) {
