@@ -230,6 +230,48 @@ def copy_calibration(gib: int = 1, reps: int = 5) -> int:
     return 0
 
 
+def gemm_vs_hipblaslt(reps: int = 12) -> int:
+    """The 256 x 256 GEMM of the step's large sites against hipBLASLt
+    (torch.matmul) on the same f16 operands, f16 out: one JSON line per
+    shape with both medians (HIP events, interleaved) and the largest
+    elementwise difference.  Context for the GEMM roofline, not a step."""
+    import torch
+    from diffusion_transformer_denoiser_qi21_amd import qi21 as Q
+
+    torch.manual_seed(0)
+    M, H, I = 4096, 4096, 12288
+    for name, N, K in (("gate/up", 2 * I, H), ("down", H, I), ("O", H, H), ("N 24576, K 12288", 2 * I, I)):
+        A = torch.randn(M, K, device="cuda").half()
+        W = (torch.randn(N, K, device="cuda") * 0.02).half()
+        ref = torch.empty(M, N, device="cuda", dtype=torch.half)
+        out = torch.empty(M, N, device="cuda", dtype=torch.half)
+        fns = {"hipblaslt": lambda: torch.matmul(A, W.t(), out=ref),
+               "qi21": lambda: Q.qi21_op_gemm(Q.QI21_EPI_F16, M, N, K, A, K, W, out, N, tile=0)}
+        for f in fns.values():
+            for _ in range(3):
+                f()
+        torch.cuda.synchronize()
+        diff = (out.float() - ref.float()).abs().max().item()
+        ts = {k: [] for k in fns}
+        for _ in range(reps):
+            for k, f in fns.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(4):
+                    f()
+                e1.record()
+                torch.cuda.synchronize()
+                ts[k].append(e0.elapsed_time(e1) / 4)
+        flop = 2.0 * M * N * K
+        row = {"shape": name, "M": M, "N": N, "K": K, "max_abs_diff": diff}
+        for k, v in ts.items():
+            med = sorted(v)[len(v) // 2]
+            row[k] = {"median_us": round(med * 1e3, 1), "tflops": round(flop / med / 1e9, 1),
+                      "frac": round(flop / med / 1e9 / PEAK_F16_TFLOPS, 4)}
+        print(json.dumps(row), flush=True)
+    return 0
+
+
 # ───────────────────────────── main ─────────────────────────────
 
 def main(argv=None):
@@ -246,9 +288,13 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (the scale for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--gemm-vs-hipblaslt", action="store_true",
+                    help="only time the large-site GEMM against hipBLASLt (torch.matmul) at the step's shapes")
     args = ap.parse_args(argv)
     if args.copy_calibration:
         return copy_calibration()
+    if args.gemm_vs_hipblaslt:
+        return gemm_vs_hipblaslt()
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU; --gpus above 1 is not supported "
                                    "(a step sharded by target rows over several GPUs is not built)"}))

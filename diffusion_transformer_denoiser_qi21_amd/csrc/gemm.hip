@@ -1364,10 +1364,11 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // The accumulators held in AGPRs at a loop head: without this the
-  // register allocator may give the loop-carried values VGPR homes and
-  // copy all 256 through VGPRs every iteration (the MFMAs read and write
-  // AGPRs directly, so pinning costs nothing).
+  // The accumulators held in AGPRs, at every k-tile and loop head: without
+  // this the register allocator may give the loop-carried values VGPR
+  // homes, or park some in VGPRs where registers run short, and copy them
+  // back and forth (the MFMAs read and write AGPRs directly, so pinning
+  // costs nothing).
   auto pin_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -1383,17 +1384,43 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(GemmArgs a) {
   // (reads k-step 0 of the next k-tile when rdn; loads k-tile t + 2 into
   // stage s when ld)
   auto ktile = [&](bool fp4, int s, int t, bool rdn, bool ld, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb) __attribute__((always_inline)) {
+    pin_acc();
     step(fp4, 0, true, s, 1, ra, rb, false, 0, 0);
     sync_tile();
     step(fp4, 1, rdn, s ^ 1, 0, ra, rb, ld, s, t + 2);
   };
-  // k-tiles 0 and 1 of the unit at (tm, tn, kt0)
+  // LO4 scales pass through LDS: two 4 KB buffers after the stages, each
+  // one group's A-row scale bytes of the tile (2 KB) and W-row ones (2 KB).
+  // Wave w moves 1 KB of a group (A scales for w < 2, W scales above, half
+  // w & 1) with one LDS-direct load, right after a barrier like the
+  // k-tile loads; a lane reads its 16 dwords at the group's fp4 k-tile.
+  constexpr int SCH = DNS * DSTAGE;  // halves offset of the scale buffers
+  auto load_sc = [&](int m0_, int n0_, int sb, int grp) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r =
+        wave >= 2 ? __builtin_amdgcn_make_buffer_rsrc((void*)(a.wsc + (size_t)n0_ * a.ldws), 0, DBN * a.ldws, 0x00020000)
+                  : __builtin_amdgcn_make_buffer_rsrc((void*)(a.asc + (size_t)m0_ * a.lds), 0, DBM * a.lds, 0x00020000);
+    f16* base = smem + SCH + sb * 2048 + wave * 512;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base, 16, lane * 16, grp * 2048 + (wave & 1) * 1024, 0, 0);
+  };
+  // this lane's scale dwords of buffer sb, shifted so that bytes 0 and 2
+  // are k-steps 0 and 1
+  const int sh = 8 * (g4 >> 1);
+  auto read_sc = [&](int sb) __attribute__((always_inline)) {
+    const unsigned* sp = reinterpret_cast<const unsigned*>(smem + SCH + sb * 2048) + (g4 & 1);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) asc[i] = (int)(sp[(wm * 128 + i * 16 + l16) * 2] >> sh);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) wsc[j] = (int)(sp[512 + (wn * 128 + j * 16 + l16) * 2] >> sh);
+  };
+  // k-tiles 0 and 1 of the unit at (tm, tn, kt0) (LO4: and its first
+  // group's scales, into buffer 0)
   auto prologue = [&](int tm, int tn) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t ra = rsrc_a(tm * DBM), rb = rsrc_b(tn * DBN);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) load1(ra, rb, 0, 0, q);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) load1(ra, rb, 1, 1, q);
+    if constexpr (LO4) load_sc(tm * DBM, tn * DBN, 0, kt0 / 5);
   };
 
   int tm, tn;
@@ -1417,58 +1444,39 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(GemmArgs a) {
       step(fp4, 1, false, 0, 0, ra, rb, false, 0, 0);
     };
     if constexpr (LO4) {
-      // the tile's 256-row blocks of the blocked scale arrays
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(a.asc + (size_t)m0 * a.lds), 0, DBM * a.lds, 0x00020000);
-      const __amdgpu_buffer_rsrc_t rw =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(a.wsc + (size_t)n0 * a.ldws), 0, DBN * a.ldws, 0x00020000);
-      const int sh = 8 * (g4 >> 1);
-      auto load_sc = [&](int t) __attribute__((always_inline)) {  // the group of unit-local k-tile t
-        const int o = ((kt0 + t) / 5) * 2048 + 4 * (g4 & 1);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) asc[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, o + (wm * 128 + i * 16 + l16) * 8, 0, 0);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) wsc[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rw, o + (wn * 128 + j * 16 + l16) * 8, 0, 0);
-      };
-      auto shift_sc = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) asc[i] = (int)((unsigned)asc[i] >> sh);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) wsc[j] = (int)((unsigned)wsc[j] >> sh);
-      };
-      load_sc(0);
-      // k-tile 0 landed (with the first unit, k-tile 1 and the scales may
-      // still be in flight; after an epilogue, its stores share the counter)
+      // k-tile 0 landed (with the first unit, the later loads of the
+      // prologue, k-tile 1 and the scales, may still be in flight; after an
+      // epilogue, its stores share the counter)
       if (sq == seq0)
-        __builtin_amdgcn_s_waitcnt(wait_imm(NQ + TM + TN, 15));
+        __builtin_amdgcn_s_waitcnt(wait_imm(NQ + 1, 15));
       else
         __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
       __builtin_amdgcn_s_barrier();
 #pragma unroll
       for (int r = 0; r < 8; ++r) { readA(0, 0, r); readB(0, 0, 0, r); }
       __builtin_amdgcn_sched_barrier(0);
-      // The fp4 k-tile t + 4 of a group from stage s (k-step 0 after the
-      // scales of the group, landed four barriers ago, are shifted into
-      // place).  nx: a group follows (read its first fragments, load its
-      // second k-tile, then fetch its scales).
-      auto fp4_tile = [&](int s, int t, bool nx) __attribute__((always_inline)) {
-        shift_sc();
+      // The fp4 k-tile t + 4 of a group from stage s whose scales sit in
+      // buffer sb.  nx: a group follows (right after the barrier, its
+      // scales go out into the other buffer; then read its first
+      // fragments and load its second k-tile).
+      auto fp4_tile = [&](int s, int sb, int t, bool nx) __attribute__((always_inline)) {
+        pin_acc();
+        read_sc(sb);
         step(true, 0, true, s, 1, ra, rb, false, 0, 0);
         sync_tile();
         if (nx) {
+          load_sc(m0, n0, sb ^ 1, (kt0 + t + 5) / 5);
           step(true, 1, true, s ^ 1, 0, ra, rb, true, s, t + 6);
-          load_sc(t + 5);
         } else {
           finish(true);
         }
       };
-      // a group from stage s: f16 k-tiles t .. t + 3, the fp4 k-tile t + 4
       auto group = [&](int s, int t, bool nx) __attribute__((always_inline)) {
         ktile(false, s, t, true, true, ra, rb);
         ktile(false, s ^ 1, t + 1, true, true, ra, rb);
         ktile(false, s, t + 2, true, true, ra, rb);
         ktile(false, s ^ 1, t + 3, true, nx, ra, rb);
-        fp4_tile(s, t, nx);
+        fp4_tile(s, s, t, nx);  // groups alternate stages and scale buffers alike
       };
       // groups in pairs (an even number of groups); the last ends with the
       // unit's last k-step
@@ -1609,7 +1617,7 @@ namespace {
 // accumulators in AGPRs (LSP = 4, LOFF = 1, BPOS = 1)
 template <int EPI, int LO>
 hipError_t launch16(const GemmArgs& a, hipStream_t s) {
-  constexpr size_t lds = (size_t)DNS * DSTAGE * 2;
+  constexpr size_t lds = (size_t)DNS * DSTAGE * 2 + (LO == 4 ? 8192 : 0);  // + the lo4 scale buffers
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm16_kernel<EPI, LO, 4, 1, 1>),

@@ -12,10 +12,13 @@
 // lo4: columns grouped by 256; group g takes 640 bytes, the 256 halves
 // and then 128 bytes of e2m1 (fp4) residuals, two per byte (the even
 // column in the low nibble): four f16 k-tiles and one fp4 k-tile per
-// group.  One scale per 32 columns (the MX block), eight per group, in the
-// order the fp4 MFMA's lanes take them: byte 4 h + s of the group for the
-// block 2 s + h (k-step s of the fp4 k-tile, lane half h), so a lane reads
-// its four k-steps' scales as one dword.
+// group.  One scale per 32 columns (the MX block), eight per group: byte
+// 4 h + s of the group for the block 2 s + h.  That is the order in which
+// the lanes of a 32 x 32 x 64 fp4 MFMA take them (k-step s of the fp4
+// k-tile, lane half h): a lane reads its four k-steps' scales as one
+// dword.  The 16 x 16 x 128 fp4 MFMA's lane group g (of four) takes
+// block g in k-step 0 and block 4 + g in k-step 1: bytes g / 2 and
+// g / 2 + 2 of the dword at 4 (g % 2).
 //
 // Scale arrays are blocked by 256 rows and, inside a block, ordered group
 // by group: the bytes of rows r .. r + 31 for one group sit next to each
