@@ -19,14 +19,14 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 def test_traffic_record_matches_only_its_workload_form_and_sources():
-    for ffn in ("lo4", "f16"):
-        rec = json.load(open(os.path.join(ROOT, "profiles", f"gate_up_gemm_1024_{ffn}_traffic.json")))
-        got = bench.recorded_traffic("1024", ffn)
-        # the record is either current (its value) or stale (None): never another number
-        assert got in (None, rec["traffic_bytes_per_launch"])
-        assert bench.recorded_traffic("2048", ffn) is None
-        assert bench.recorded_traffic("512", ffn) is None
-    assert bench.recorded_traffic("1024", "pair") is None  # no record for that form
+    rec = json.load(open(os.path.join(ROOT, "profiles", "gate_up_gemm_1024_lo4_traffic.json")))
+    got = bench.recorded_traffic("1024", "lo4")
+    # the record is either current (its value) or stale (None): never another number
+    assert got in (None, rec["traffic_bytes_per_launch"])
+    assert bench.recorded_traffic("2048", "lo4") is None
+    assert bench.recorded_traffic("512", "lo4") is None
+    for ffn in ("f16", "lo8", "pair"):  # no record for these forms
+        assert bench.recorded_traffic("1024", ffn) is None
 
 
 def test_traffic_record_is_dropped_when_a_kernel_source_changes(tmp_path, monkeypatch):
