@@ -1380,15 +1380,6 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(GemmArgs a) {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // k-tile t of stage s: k-step 0 (reads k-step 1), barrier, k-step 1
-  // (reads k-step 0 of the next k-tile when rdn; loads k-tile t + 2 into
-  // stage s when ld)
-  auto ktile = [&](bool fp4, int s, int t, bool rdn, bool ld, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb) __attribute__((always_inline)) {
-    pin_acc();
-    step(fp4, 0, true, s, 1, ra, rb, false, 0, 0);
-    sync_tile();
-    step(fp4, 1, rdn, s ^ 1, 0, ra, rb, ld, s, t + 2);
-  };
   // LO4 scales pass through LDS: two 4 KB buffers after the stages, each
   // one group's A-row scale bytes of the tile (2 KB) and W-row ones (2 KB).
   // Wave w moves 1 KB of a group (A scales for w < 2, W scales above, half
@@ -1402,15 +1393,35 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(GemmArgs a) {
     f16* base = smem + SCH + sb * 2048 + wave * 512;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, base, 16, lane * 16, grp * 2048 + (wave & 1) * 1024, 0, 0);
   };
-  // this lane's scale dwords of buffer sb, shifted so that bytes 0 and 2
-  // are k-steps 0 and 1
+  // this lane's scale dwords of buffer sb; shift_sc then moves bytes so
+  // that bytes 0 and 2 are k-steps 0 and 1
   const int sh = 8 * (g4 >> 1);
   auto read_sc = [&](int sb) __attribute__((always_inline)) {
     const unsigned* sp = reinterpret_cast<const unsigned*>(smem + SCH + sb * 2048) + (g4 & 1);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) asc[i] = (int)(sp[(wm * 128 + i * 16 + l16) * 2] >> sh);
+    for (int i = 0; i < TM; ++i) asc[i] = (int)sp[(wm * 128 + i * 16 + l16) * 2];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) wsc[j] = (int)(sp[512 + (wn * 128 + j * 16 + l16) * 2] >> sh);
+    for (int j = 0; j < TN; ++j) wsc[j] = (int)sp[512 + (wn * 128 + j * 16 + l16) * 2];
+  };
+  auto shift_sc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) asc[i] = (int)((unsigned)asc[i] >> sh);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) wsc[j] = (int)((unsigned)wsc[j] >> sh);
+  };
+  // k-tile t of stage s: k-step 0 (reads k-step 1), barrier, k-step 1
+  // (reads k-step 0 of the next k-tile when rdn; loads k-tile t + 2 into
+  // stage s when ld)
+  // (rsc: after the barrier, also read the scale dwords of buffer sb, for
+  // the fp4 k-tile that follows)
+  auto ktile = [&](bool fp4, int s, int t, bool rdn, bool ld, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                   bool rsc = false, int sb = 0) __attribute__((always_inline)) {
+    pin_acc();
+    step(fp4, 0, true, s, 1, ra, rb, false, 0, 0);
+    sync_tile();
+    if constexpr (LO4)
+      if (rsc) read_sc(sb);
+    step(fp4, 1, rdn, s ^ 1, 0, ra, rb, ld, s, t + 2);
   };
   // k-tiles 0 and 1 of the unit at (tm, tn, kt0) (LO4: and its first
   // group's scales, into buffer 0)
@@ -1456,12 +1467,12 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(GemmArgs a) {
       for (int r = 0; r < 8; ++r) { readA(0, 0, r); readB(0, 0, 0, r); }
       __builtin_amdgcn_sched_barrier(0);
       // The fp4 k-tile t + 4 of a group from stage s whose scales sit in
-      // buffer sb.  nx: a group follows (right after the barrier, its
+      // buffer sb (their dwords were read one k-step before).  nx: a group follows (right after the barrier, its
       // scales go out into the other buffer; then read its first
       // fragments and load its second k-tile).
       auto fp4_tile = [&](int s, int sb, int t, bool nx) __attribute__((always_inline)) {
         pin_acc();
-        read_sc(sb);
+        shift_sc();
         step(true, 0, true, s, 1, ra, rb, false, 0, 0);
         sync_tile();
         if (nx) {
@@ -1475,7 +1486,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(GemmArgs a) {
         ktile(false, s, t, true, true, ra, rb);
         ktile(false, s ^ 1, t + 1, true, true, ra, rb);
         ktile(false, s, t + 2, true, true, ra, rb);
-        ktile(false, s ^ 1, t + 3, true, nx, ra, rb);
+        ktile(false, s ^ 1, t + 3, true, nx, ra, rb, true, s);  // + the fp4 k-tile's scale dwords
         fp4_tile(s, s, t, nx);  // groups alternate stages and scale buffers alike
       };
       // groups in pairs (an even number of groups); the last ends with the
