@@ -408,14 +408,19 @@ def _random_rows(fmt, rng, rows, cols, hi_sigma, act, sc_lo, sc_hi):
     return lo4_join(hi, nib), arr, hi.astype(np.float64), e2m1_decode(nib) * 2.0 ** f
 
 
+@pytest.mark.parametrize("even", [False, True])
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [1, 77, 300, 1040])
 @pytest.mark.parametrize("epi", ["f32", "resid", "split", "swiglu"])
-def test_gemm_lo_epilogues(fmt, epi, M):
+def test_gemm_lo_epilogues(fmt, epi, M, even):
+    """even: an even number of column groups per work unit, which lo4 runs
+    on the 16 x 16 x 32 kernel; odd counts take the 32 x 32 x 16 one."""
     q = Q()
-    rng = np.random.default_rng(1000 + M + (7 if fmt == "lo4" else 0))
+    rng = np.random.default_rng(1000 + M + (7 if fmt == "lo4" else 0) + (3 if even else 0))
     g = 128 if fmt == "lo8" else 256
-    N, K = (512 if fmt == "lo8" else 1024, 2 * g) if epi == "swiglu" else (256, 3 * g)
+    ng, ks = ((2 if even else 3), 1) if epi == "swiglu" else ((4, 2) if even else (3, 3)) if epi == "split" else \
+        ((4 if even else 3), 1)
+    N, K = (512 if fmt == "lo8" else 1024, ng * g) if epi == "swiglu" else (256, ng * g)
     kr = 3 * K // 2 if fmt == "lo8" else 5 * K // 4  # halves per row
     abuf, asc, a_h, a_l = _random_rows(fmt, rng, M, K, 1.0, True, 108, 116)
     wbuf, wsc, w_h, w_l = _random_rows(fmt, rng, N, K, 0.05, False, 110, 116)
@@ -425,12 +430,11 @@ def test_gemm_lo_epilogues(fmt, epi, M):
     oscale = 0.5
     f = fmt_id(fmt)
     if epi in ("f32", "split"):
-        ks = 3 if epi == "split" else 1
         out = torch.full((ks, M, N), float("nan"), device="cuda")
         q.qi21_op_gemm_lo(f, q.QI21_EPI_F32, M, N, K, A, kr, da, W, kr, dw, out, N, ksplit=ks, oscale=oscale)
         sync()
         o = out.cpu().numpy().astype(np.float64)
-        for p in range(ks):  # each plane its own third of the columns
+        for p in range(ks):  # each plane its own share of the columns
             c = slice(p * K // ks, (p + 1) * K // ks)
             want_p = (a_h[:, c] @ w_h[:, c].T + a_l[:, c] @ w_l[:, c].T) * oscale
             assert np.abs(o[p] - want_p).max() <= 1e-5 * np.abs(want_p).max()
