@@ -17,8 +17,8 @@
 //   schedule is pinned; one barrier per k-tile, after which all loads of
 //   the k-tile two ahead go out.
 // * gemm_dma_kernel, the same tile on v_mfma_f32_32x32x16_f16: the lo8 form,
-//   the qkv split, the 8-wave form (128 x 64 per wave) and work units with
-//   an odd number of k-tiles.
+//   the 8-wave form (128 x 64 per wave) and work units with an odd number
+//   of k-tiles.
 // * gemm_rs_kernel, the small-M / narrow-N kernel: block tile BM x BN x 64,
 //   global -> registers -> LDS, double-buffered.
 //
@@ -1004,6 +1004,26 @@ __device__ __forceinline__ float row_max16(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// 4 x 4 transpose of f16 values inside each quad of lanes: lane r (= lane
+// % 4) of a quad holds x[r][0..3] packed two to a dword (the first in the
+// low half) and gets x[0..3][r] back in the same packing.  Two exchanges:
+// lanes r and r ^ 2 swap the column pair the other keeps, then lanes r and
+// r ^ 1 the column the other keeps.  Every lane must take part.
+__device__ __forceinline__ u32x2 quad_t16(u32x2 v, int r) {
+  constexpr unsigned LO = 0x05040100u, HI = 0x07060302u;  // perm selectors: low / high halves of (src1, src0)
+  const bool low2 = r < 2, odd = r & 1;
+  // lanes 0, 1 keep columns 0, 1 and lanes 2, 3 columns 2, 3
+  const unsigned got1 = (unsigned)__builtin_amdgcn_mov_dpp((int)(low2 ? v[1] : v[0]), 0x4e, 0xf, 0xf, false);
+  const unsigned ra = low2 ? v[0] : got1;  // row r % 2 of the kept columns
+  const unsigned rb = low2 ? got1 : v[1];  // row r % 2 + 2
+  // even lanes keep the first of their two columns, odd lanes the second
+  const unsigned keep = __builtin_amdgcn_perm(rb, ra, odd ? HI : LO);
+  const unsigned got2 = (unsigned)__builtin_amdgcn_mov_dpp((int)__builtin_amdgcn_perm(rb, ra, odd ? LO : HI), 0xb1, 0xf,
+                                                           0xf, false);
+  const unsigned r02 = odd ? got2 : keep, r13 = odd ? keep : got2;  // rows 0, 2 and rows 1, 3 of column r
+  return u32x2{__builtin_amdgcn_perm(r13, r02, LO), __builtin_amdgcn_perm(r13, r02, HI)};
+}
+
 // Epilogue of a wave whose output rows [r0, r0 + 128) and columns [c0, c0 +
 // 128) sit in 8 x 8 tiles of 16 x 16 (tile (i, j): rows r0 + 16 i .., columns
 // c0 + 16 j ..): lane l holds row r0 + 16 i + l % 16 and columns c0 + 16 j +
@@ -1015,6 +1035,15 @@ __device__ __forceinline__ void epilogue16(const GemmArgs& a, floatx4 (&acc)[8][
   // the epilogue instead of being hoisted out of the tile loop, where its
   // registers would compete with the main loop's
   int l16 = lane & 15, g = lane >> 4;
+  if constexpr (EPI == EPI_QKV) {
+    // and taken afresh (the count of the lanes below this one, in an asm
+    // statement that cannot move out of the tile loop), so that no lane
+    // index computed before the loop has to live through it
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    l16 = ln & 15;
+    g = ln >> 4;
+  }
   asm volatile("" : "+v"(l16), "+v"(g));
   if constexpr (EPI == EPI_RESID) {
 #pragma unroll
@@ -1063,6 +1092,44 @@ __device__ __forceinline__ void epilogue16(const GemmArgs& a, floatx4 (&acc)[8][
         if (row < a.M)
           *reinterpret_cast<u32x4*>(reinterpret_cast<f16*>(a.out) + obase + (size_t)row * a.ldo + c0 + 32 * p +
                                     m16_col(g)) = o;
+      }
+    }
+  } else if constexpr (EPI == EPI_QKV) {
+    // q | k columns (c0 < 2H) to out as f16; v columns transposed into out2
+    // (V^T: one row per v column, key c at vt_pos(c)).  A lane holds one key
+    // and 4 consecutive v columns of a tile; the 4 x 4 transpose inside each
+    // quad (keys 4a .. 4a + 3 of the tile) gives lane 4a + r the 4 keys of
+    // column 4g + r, which vt_pos keeps contiguous: one 8-byte store.  Keys
+    // from M up to the leading dimension (whole groups of 16) get zeros.
+    const int two_h = (a.N / 3) * 2;
+    if (c0 < two_h) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = r0 + 16 * i + l16;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const u32x4 o = merge16(to_half4(acc[i][2 * p] * a.oscale), to_half4(acc[i][2 * p + 1] * a.oscale));
+          if (row < a.M)
+            *reinterpret_cast<u32x4*>(reinterpret_cast<f16*>(a.out) + (size_t)row * a.ldo + c0 + 32 * p + m16_col(g)) = o;
+        }
+      }
+    } else {
+      const int r = l16 & 3, rz = a.ld2 & ~15;
+      const bool tail = r0 + 128 > a.M;  // the wave holds rows past M
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int key = r0 + 16 * i + (l16 & ~3);  // the quad's first key
+        const bool zero = tail && r0 + 16 * i + l16 >= a.M;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          u32x2 v = __builtin_bit_cast(u32x2, to_half4(acc[i][j] * a.oscale));
+          if (zero) v = u32x2{0u, 0u};
+          v = quad_t16(v, r);
+          if (key < rz)
+            *reinterpret_cast<u32x2*>(a.out2 + (size_t)(c0 - two_h + 16 * j + 4 * g + r) * a.ld2 + vt_pos(key)) = v;
+        }
+        // one row slice at a time (as in the SwiGLU epilogue)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   } else if constexpr (EPI == EPI_QKROPE) {
@@ -1651,10 +1718,10 @@ hipError_t launch16(const GemmArgs& a, hipStream_t s) {
 
 // 4-wave launches of the f16 and lo4 forms run the 16 x 16 x 32 kernel
 // when a work unit has an even number of k-tiles (lo4: of groups); lo8,
-// the qkv split, the 8-wave form and the other counts the 32 x 32 x 16 one
+// the 8-wave form and the other counts the 32 x 32 x 16 one
 template <int EPI, int NW, int LO = 0>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
-  if constexpr (NW == 4 && LO != 8 && EPI != EPI_QKV && EPI != EPI_SWIGLU8) {
+  if constexpr (NW == 4 && LO != 8 && EPI != EPI_SWIGLU8) {
     const int kt = a.K / DBK / a.ksplit;  // k-tiles per unit
     if (LO == 4 ? kt % 10 == 0 : (kt % 2 == 0 && kt >= 2)) return launch16<EPI, LO>(a, s);
   }

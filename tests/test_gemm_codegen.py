@@ -68,5 +68,6 @@ def test_gemm16_main_loops_keep_accumulators_in_agprs(gemm_asm):
         for c in mfma_loops:
             moves = sum(v for k, v in c.items() if k.startswith("v_accvgpr"))
             assert moves == 0, f"{name}: {moves} accumulator copies in the main loop"
-    # the f16 forms of every row epilogue, and the lo4 forms of the FFN sites
-    assert seen >= 11, seen
+    # the f16 forms of every epilogue but the 8-wave lo8 SwiGLU, and the lo4
+    # forms of the FFN sites
+    assert seen >= 12, seen
