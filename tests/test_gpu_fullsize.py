@@ -301,7 +301,7 @@ def test_step_full_size_residual_forms_against_oracle(request, mode, name):
     _check_v(_step_v(m, CONFIGS[name], 52, stride), want, f"{name} ({mode})")
 
 
-@pytest.mark.parametrize("name", ["512", "1024", "cond", "ragged"])
+@pytest.mark.parametrize("name", ["512", "1024", "cond", "ragged", "2048"])
 def test_step_full_size_pair_against_oracle(full_model_pair, name):
     want, stride = _golden(name)
     _check_v(_step_v(full_model_pair, CONFIGS[name], 50, stride), want, f"{name} (pair)")
