@@ -19,7 +19,8 @@ single-f16 design, which misses that bar on these weights.
 Prints ONE JSON line: s/step (the metric), TFLOP/s and the fraction of the
 f16 MFMA peak (algorithmic FLOP of the method: the residual products of
 the lo8 form are not counted), the dominant kernel's roofline (gate/up
-GEMM, timed with HIP events on the launch stream inside the timed region),
+GEMM, timed with HIP events on the launch stream inside the timed region,
+around a sample of its launches: one in every ``--event-every``),
 every site's MFMA fraction from a separate profiled pass after the timed
 region, and the CPU oracle's time on a bounded sample of the same
 workload.
@@ -285,6 +286,10 @@ def main(argv=None):
                          "lo8: f16 + scaled e4m3 residual)")
     ap.add_argument("--site-steps", type=int, default=3,
                     help="steps of the untimed pass that times every site with HIP events")
+    ap.add_argument("--event-every", type=int, default=7,
+                    help="in the timed region, bracket one gate/up launch in this many with HIP events (an event "
+                         "pair delays the launches around it by a few microseconds; 7 is coprime to the 32 "
+                         "blocks, so the sample walks every block)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (the scale for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -335,9 +340,11 @@ def main(argv=None):
     for _ in range(args.warmup):
         one_step()
     Q.qi21_profile_read(m)
-    # the timed region: the dominant kernel (gate/up GEMM) is bracketed by
-    # HIP events on the launch stream inside the library
+    # the timed region: a sample of the dominant kernel's (gate/up GEMM)
+    # launches is bracketed by HIP events on the launch stream inside the
+    # library
     Q.qi21_set_profile(m, 1 << 4)
+    Q.qi21_set_profile_every(m, args.event_every)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -349,6 +356,7 @@ def main(argv=None):
     site_ms, site_n = None, None
     if args.site_steps > 0:
         Q.qi21_set_profile(m, (1 << 0) | (1 << 2) | (1 << 3) | (1 << 4) | (1 << 5))
+        Q.qi21_set_profile_every(m, 1)
         for _ in range(args.site_steps):
             one_step()
         torch.cuda.synchronize()
@@ -413,7 +421,8 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "kernel": "gate/up GEMM + SwiGLU", "achieved": w13_tf,
                      "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": w13_tf / PEAK_F16_TFLOPS,
                      "traffic": recorded_traffic(args.config, args.ffn), "launch_ms": w13_launch_ms,
-                     "launches": int(n_cls[4]), "algorithmic_flop": w13_flop,
+                     "launches": int(n_cls[4]), "launches_sampled_one_in": args.event_every,
+                     "algorithmic_flop": w13_flop,
                      "mfma_mix_frac": w13_tf * mix / PEAK_F16_TFLOPS},
         "sites": sites,
         "device": props.name,

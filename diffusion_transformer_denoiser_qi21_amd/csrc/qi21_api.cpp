@@ -87,6 +87,8 @@ struct Prof {
   size_t used[NCLASS] = {};
   double ms[NCLASS] = {};
   int64_t n[NCLASS] = {};
+  int every = 1;                // bracket one launch of a class in every `every`
+  int64_t seen[NCLASS] = {};    // launches of each profiled class so far
 };
 
 }  // namespace
@@ -303,6 +305,7 @@ struct Scope {
   Scope(qi21_model* m_, int c, hipStream_t s_) : m(m_), cls(c), s(s_) {
     if (!((m->o.profile >> cls) & 1)) return;
     Prof& P = m->prof;
+    if (P.seen[cls]++ % P.every) return;
     const size_t i = P.used[cls] * 2;
     while (P.ev[cls].size() < i + 2) {
       hipEvent_t e;
@@ -1084,6 +1087,14 @@ int qi21_release_key(qi21_model* m, uint64_t key) {
 int qi21_set_profile(qi21_model* m, int class_mask) {
   if (!m) return fail(QI21_EINVAL, "model is NULL");
   m->o.profile = class_mask;
+  return QI21_OK;
+}
+
+int qi21_set_profile_every(qi21_model* m, int every) {
+  if (!m) return fail(QI21_EINVAL, "model is NULL");
+  if (every < 1) return fail(QI21_EINVAL, "profile sampling every %d (>= 1)", every);
+  m->prof.every = every;
+  for (int64_t& c : m->prof.seen) c = 0;
   return QI21_OK;
 }
 

@@ -74,6 +74,7 @@ _SIGS = {
     "qi21_model_bytes": (C.c_size_t, [vp]),
     "qi21_profile_read": (C.c_int, [vp, C.POINTER(C.c_double), C.POINTER(i64)]),
     "qi21_set_profile": (C.c_int, [vp, C.c_int]),
+    "qi21_set_profile_every": (C.c_int, [vp, C.c_int]),
     "qi21_layout_sizes": (C.c_int, [C.POINTER(qi21_seg), C.c_int, C.POINTER(i32), C.POINTER(i32)]),
     "qi21_layout_tables": (C.c_int, [C.POINTER(qi21_seg), C.c_int, C.POINTER(i32), f32, vp, vp, vp, vp, vp, vp]),
     "qi21_op_gemm": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, vp, C.c_int, vp, vp, C.c_int, vp, C.c_int, f32, f32,
@@ -310,6 +311,10 @@ def qi21_model_bytes(m) -> int:
 
 def qi21_set_profile(m, class_mask: int):
     _check(lib().qi21_set_profile(m, int(class_mask)))
+
+
+def qi21_set_profile_every(m, every: int):
+    _check(lib().qi21_set_profile_every(m, int(every)))
 
 
 def qi21_profile_read(m):

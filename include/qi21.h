@@ -245,6 +245,14 @@ size_t qi21_model_bytes(const qi21_model* m);
 /* Change the profiled class mask of a model (as opt.profile). */
 int qi21_set_profile(qi21_model* m, int class_mask);
 
+/* Bracket only one launch in every `every` of each profiled class (every
+ * >= 1; 1, the default, brackets all), counted from this call: an event
+ * pair on the stream delays the launches around it by a few microseconds,
+ * so a sample keeps that cost off most launches.  EINVAL for a NULL model
+ * or every < 1.  Not from the pages: a measurement aid, like
+ * qi21_set_profile. */
+int qi21_set_profile_every(qi21_model* m, int every);
+
 /* Profiling (opt.profile != 0): per-class device milliseconds summed over
  * the steps since the last read, and the number of launches of each
  * class; classes: 0 qkv GEMM, 1 qkrope, 2 flash, 3 O GEMM, 4 gate/up GEMM,

@@ -210,6 +210,35 @@ def test_step_is_deterministic(tiny_gpu):
     assert torch.equal(a, b)
 
 
+def test_profile_sampling_counts_and_leaves_v_alone(tiny_gpu):
+    """Events around one launch in `every` of a profiled class: the launch
+    counts follow, and v is bit-identical with and without the events."""
+    q = Q()
+    w = CONFIGS["tiny"]
+    d = bench.workload_tensors(w)
+    bench.prefill(tiny_gpu, 4, d)
+    ref = torch.zeros(d["n"], 64, device="cuda")
+    q.qi21_step(tiny_gpu, 4, d["tok"], d["mods"], d["fs"], ref)
+    blocks = TINY_MODEL.layers
+    with pytest.raises(RuntimeError):
+        q.qi21_set_profile_every(tiny_gpu, 0)
+    q.qi21_profile_read(tiny_gpu)
+    q.qi21_set_profile(tiny_gpu, (1 << 4) | (1 << 5))
+    for every, steps in ((1, 2), (3, 5)):
+        q.qi21_set_profile_every(tiny_gpu, every)
+        for _ in range(steps):
+            out = torch.zeros(d["n"], 64, device="cuda")
+            q.qi21_step(tiny_gpu, 4, d["tok"], d["mods"], d["fs"], out)
+            assert torch.equal(out, ref)
+        torch.cuda.synchronize()
+        ms, n = q.qi21_profile_read(tiny_gpu)
+        want = -(-steps * blocks // every)  # launches 0, every, 2 every, ... of steps * blocks
+        assert n[4] == want and n[5] == want, (every, n)
+        assert ms[4] > 0 and ms[5] > 0
+    q.qi21_set_profile(tiny_gpu, 0)
+    q.qi21_set_profile_every(tiny_gpu, 1)
+
+
 @pytest.mark.parametrize("shifts", [(0, 0, 0, 0, 0), (4, 8, 2, 4, 10)])
 def test_range_guard_settings(tiny_cpu, shifts):
     q = Q()
