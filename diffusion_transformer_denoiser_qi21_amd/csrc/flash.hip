@@ -351,18 +351,26 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_kernel(FlashArgs a0, Fl
 
   const float ltot = pair_sum(lsum);
   const float inv = ltot > 0.0f ? a.oscale / ltot : 0.0f;
-  if (live) {
-    f16* op = a.out + (size_t)myq * a.ldo + head * 128 + 4 * hs;
+  // Lane l holds dims 32 d + 8 g + 4 hs .. + 3 of its query, lane l ^ 32
+  // the other 4 of each 8; one v_permlane32_swap per register of a pair of
+  // g gives lane hs the 8 dims of g = 2 k + hs: one 16-byte store each.
+  f16* op = a.out + (size_t)myq * a.ldo + head * 128;
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
+  for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+    for (int k = 0; k < 2; ++k) {
+      u32x2 x[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
         half4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (f16)(o[d][4 * g + e] * inv);
-        *reinterpret_cast<half4*>(op + 32 * d + 8 * g) = v;
+        for (int e = 0; e < 4; ++e) v[e] = (f16)(o[d][4 * (2 * k + u) + e] * inv);
+        x[u] = __builtin_bit_cast(u32x2, v);
       }
-  }
+      const auto s0 = __builtin_amdgcn_permlane32_swap(x[0][0], x[1][0], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(x[0][1], x[1][1], false, false);
+      if (live) *reinterpret_cast<u32x4*>(op + 32 * d + 8 * (2 * k + hs)) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+    }
 }
 
 // The key-split form for grids too small to give each SIMD two waves
@@ -587,19 +595,27 @@ __global__ __launch_bounds__(512, 1) void flash_split_kernel(FlashArgs a0, Flash
     const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
     const float ltot = pair_sum(lsum * a0 + l1 * a1);
     const float inv = ltot > 0.0f ? a.oscale / ltot : 0.0f;
-    if (live) {
-      f16* op = a.out + (size_t)myq * a.ldo + head * 128 + 4 * hs;
+    // 16-byte stores of 8 dims per lane, as in flash_kernel (group 0 is
+    // whole waves, so every lane takes part in the swaps)
+    f16* op = a.out + (size_t)myq * a.ldo + head * 128;
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
+    for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+      for (int k = 0; k < 2; ++k) {
+        u32x2 x[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int g = 2 * k + u;
           half4 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             v[e] = (f16)((o[d][4 * g + e] * a0 + xo[d * 16 + 4 * g + e] * a1) * inv);
-          *reinterpret_cast<half4*>(op + 32 * d + 8 * g) = v;
+          x[u] = __builtin_bit_cast(u32x2, v);
         }
-    }
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x[0][0], x[1][0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x[0][1], x[1][1], false, false);
+        if (live) *reinterpret_cast<u32x4*>(op + 32 * d + 8 * (2 * k + hs)) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+      }
   }
 }
 
