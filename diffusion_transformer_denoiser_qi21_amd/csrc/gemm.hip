@@ -1210,6 +1210,10 @@ __device__ __forceinline__ void epilogue16(const GemmArgs& a, floatx4 (&acc)[8][
     // 4p + 1) and the matching 32 up rows (4p + 2, 4p + 3): 64 hidden
     // columns, one 32-column scale block per group and row
     const int hc = c0 / 2;  // first hidden column of the wave
+    // silu(g s) (u s) o = (g u) (s^2 o) / (1 + 2^(g (-s log2 e))): s and o
+    // are powers of two, so both factors are exact scalings of the
+    // constants and the exponent argument is that of exp(-g s)
+    const float ke = a.inscale * -1.44269504088896341f, kp = a.inscale * a.inscale * a.oscale;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = r0 + 16 * i + l16;
@@ -1222,7 +1226,8 @@ __device__ __forceinline__ void epilogue16(const GemmArgs& a, floatx4 (&acc)[8][
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float h = silu_f(acc[i][4 * p + u][e] * a.inscale) * (acc[i][4 * p + 2 + u][e] * a.inscale) * a.oscale;
+            const float gv = acc[i][4 * p + u][e], uv = acc[i][4 * p + 2 + u][e];
+            const float h = (gv * uv) * kp * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gv * ke));
             hi[u][e] = (f16)h;
             lo[u][e] = h - (float)hi[u][e];  // exact in f32
             mx = fmaxf(mx, fabsf(lo[u][e]));
