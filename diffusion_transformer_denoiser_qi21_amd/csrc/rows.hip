@@ -162,11 +162,12 @@ __global__ __launch_bounds__(256) void rowop_kernel(int rows, int h, float* __re
 // both rows' loads go out before either row's reductions, and the two
 // rows' reductions share their barriers.  Same arithmetic, in the same
 // order, as rowop_wide_kernel.  An odd last row is loaded twice and
-// written once.
-template <int NJ>
+// written once.  LO4: xn in the lo4 row form (mode 2 | 16), as
+// rowop_wide_kernel writes it.
+template <int NJ, bool LO4>
 __global__ __launch_bounds__(256) void rownorm2_kernel(int rows, int h, const float* __restrict__ x,
                                                        f16* __restrict__ xn, int ldxn, const float* __restrict__ mods,
-                                                       int s_off, float eps, float oscale) {
+                                                       int s_off, float eps, float oscale, uint8_t* __restrict__ xsc) {
   __shared__ float red[2][4];
   const int t = threadIdx.x, w = t >> 6;
   const int r0 = blockIdx.x * 2;
@@ -219,14 +220,26 @@ __global__ __launch_bounds__(256) void rownorm2_kernel(int rows, int h, const fl
   for (int k = 0; k < 2; ++k) {
     if (k == 1 && !two) break;
     const float inv = rsqrtf((red[k][0] + red[k][1] + red[k][2] + red[k][3]) / (float)h + eps);
-    half4* xo = reinterpret_cast<half4*>(xn + (size_t)(r0 + k) * ldxn);
+    if constexpr (LO4) {
+      uint8_t* xb = reinterpret_cast<uint8_t*>(xn + (size_t)(r0 + k) * ldxn);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int c = t + 256 * j;
-      if (c < nc) {
-        const float4v sc = reinterpret_cast<const float4v*>(mods + s_off)[c];
-        const float4v r = (v[k][j] - mean[k]) * inv * (1.0f + sc) * oscale;
-        xo[c] = half4{(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
+      for (int j = 0; j < NJ; ++j) {
+        const int c = t + 256 * j;
+        const bool act = c < nc;
+        float4v r = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+        if (act) r = (v[k][j] - mean[k]) * inv * (1.0f + reinterpret_cast<const float4v*>(mods + s_off)[c]) * oscale;
+        lo4_store(act, c, r, xb, xsc, r0 + k, h);
+      }
+    } else {
+      half4* xo = reinterpret_cast<half4*>(xn + (size_t)(r0 + k) * ldxn);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = t + 256 * j;
+        if (c < nc) {
+          const float4v sc = reinterpret_cast<const float4v*>(mods + s_off)[c];
+          const float4v r = (v[k][j] - mean[k]) * inv * (1.0f + sc) * oscale;
+          xo[c] = half4{(f16)r[0], (f16)r[1], (f16)r[2], (f16)r[3]};
+        }
       }
     }
   }
@@ -423,8 +436,13 @@ hipError_t launch_rowop(int rows, int h, int mode, float* x, const float* y, f16
     // the LayerNorm passes of long steps: two rows per block (4096 rows: 17.0
     // against 19.5 us; even at 16384 rows, 0.3 us slower at 1024)
     if (mode == 2 && rows > 2048) {
-      hipLaunchKernelGGL(rownorm2_kernel<4>, dim3((rows + 1) / 2), dim3(256), 0, s, rows, h, x, xn, ldxn, mods, s_off,
-                         eps, oscale);
+      hipLaunchKernelGGL((rownorm2_kernel<4, false>), dim3((rows + 1) / 2), dim3(256), 0, s, rows, h, x, xn, ldxn, mods,
+                         s_off, eps, oscale, xsc);
+      return hipGetLastError();
+    }
+    if (mode == (2 | 16) && rows > 2048) {
+      hipLaunchKernelGGL((rownorm2_kernel<4, true>), dim3((rows + 1) / 2), dim3(256), 0, s, rows, h, x, xn, ldxn, mods,
+                         s_off, eps, oscale, xsc);
       return hipGetLastError();
     }
     return launch_rowop_wide<4>(QI21_LAUNCH_ARGS);
