@@ -97,6 +97,32 @@ def test_gemm_epilogues(epi, M, tile):
         assert np.all(vtn[:, rest] == 0)  # nothing written for rows past M
 
 
+@pytest.mark.parametrize("M,ld2", [(300, 308), (77, 84), (256, 260), (1040, 1044)])
+def test_qkv_vt_leading_dimension_tail(M, ld2):
+    """The qkv split's V^T with a leading dimension that is not a whole
+    number of 16-key groups, on the 256 x 256 tile (tile 0): keys below M
+    hold v, keys from M up to the last whole group of 16 below ld2 hold
+    zeros, and the columns past that group are not written."""
+    q = Q()
+    N, K = 768, 512
+    h = N // 3
+    A = f16_host(3, 1, (M, K), 1.0)
+    W = f16_host(3, 2, (N, K), 0.05)
+    out = torch.zeros(M, 2 * h, device="cuda", dtype=torch.float16)
+    vt = torch.full((h, ld2), 7.0, device="cuda", dtype=torch.float16)
+    q.qi21_op_gemm(q.QI21_EPI_QKV, M, N, K, dev(A, torch.float16), K, dev(W, torch.float16), out, 2 * h, vt, ld2,
+                   oscale=0.5, tile=0)
+    sync()
+    want = O.lin(A, W) * np.float32(0.5)
+    assert_close(out.float().cpu().numpy(), want[:, :2 * h], F16_TOL)
+    vtn = vt.float().cpu().numpy()
+    assert_close(vtn[:, vt_pos(np.arange(M))], want[:, 2 * h:].T, F16_TOL)
+    rz = ld2 & ~15
+    pad = np.setdiff1d(np.arange(rz), vt_pos(np.arange(M)))
+    assert np.all(vtn[:, pad] == 0)
+    assert np.all(vtn[:, rz:] == 7.0)
+
+
 def _pair(a32):
     """an f32 array as the f16 pair (hi, lo) = (f16(a), f16(a - hi))"""
     hi = a32.astype(np.float16)
